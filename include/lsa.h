@@ -1,0 +1,231 @@
+/*
+ * lsa.h -- C ABI of the Latent Sparse Attention (LSA) indexing + sparse
+ * attention library for AMD Instinct MI355X (gfx950).
+ *
+ * Page citations use these short names (the pages are public web pages on
+ * the paper "Latent Sparse Attention: Towards Subquadratic Ultra-Long Context
+ * Attention"):
+ *   [summary]  "Latent Sparse Attention: Towards Subquadratic Ultra-Long
+ *              Context Attention" (paper summary page)
+ *   [catalog]  "Latent Sparse Attention (LSA): A Card-Catalog Approach to
+ *              Subquadratic Ultra-Long Context Attention" (forum post)
+ *   [72x]      "Latent Sparse Attention: 72x in One Layer, 9x for the Whole
+ *              Model at 10M Tokens" (blog post)
+ *   [visual]   "Latent Sparse Attention at 10M tokens -- Hierarchical key
+ *              clusters" (explainer)
+ *
+ * Conventions shared by every entry point
+ *   - Ownership: the caller owns every device buffer (cache storage,
+ *     workspaces, inputs, outputs).  The library never allocates device
+ *     memory; it only allocates the small host-side lsa_cache handle.
+ *   - Execution: every call that takes a `stream` enqueues its kernels on that
+ *     HIP stream (a hipStream_t passed as void*, NULL = default stream) and
+ *     returns without synchronising.  Outputs are valid once the stream has
+ *     reached that point.
+ *   - Errors: calls return LSA_OK (0) or a negative lsa_status.  All
+ *     arguments are validated on the host before anything is enqueued; a
+ *     rejected call changes nothing.  A launch failure returns LSA_ERR_HIP.
+ *   - Layout: row-major, contiguous.  Key positions are int32 (< 2^31).
+ *     Index lists are ascending and padded with -1.
+ *   - Concurrency: calls on the same cache must not overlap; separate caches
+ *     are independent.
+ *   - Supported shapes: d_latent 64, n_pool 4, block 512, 64 buckets per
+ *     block, bucket cap 16 keys, head_dim 128, Hq % Hkv == 0,
+ *     Hq / Hkv <= 16, 0 <= k <= 8192, 0 <= n_sink, 1 <= window <= 8192.
+ *     Anything else returns LSA_ERR_UNSUPPORTED.
+ */
+#ifndef LSA_H
+#define LSA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LSA_OK = 0,
+  LSA_ERR_ARG = -1,         /* null pointer, negative size, inconsistent arguments */
+  LSA_ERR_UNSUPPORTED = -2, /* parameter value outside the supported shapes */
+  LSA_ERR_WORKSPACE = -3,   /* workspace smaller than the matching *_workspace_bytes */
+  LSA_ERR_CAPACITY = -4,    /* cache storage too small / appending past max_tokens */
+  LSA_ERR_HIP = -5,         /* a HIP launch or API call failed */
+  LSA_ERR_STATE = -6        /* e.g. a tree query on a cache built without a tree */
+} lsa_status;
+
+enum { LSA_F32 = 0, LSA_BF16 = 1 };  /* element types */
+enum { LSA_FLAT = 0, LSA_TREE = 1 }; /* search modes */
+
+/*
+ * Method parameters.  [catalog "Key points"]: 64-d latent keys, pooled by 4,
+ * 512-key cluster blocks, buckets of about 8 and at most 16 keys.
+ * [72x "The same steps in general"]: k far keys, 4 sinks, a 512-key window.
+ */
+typedef struct {
+  int32_t d_latent;        /* latent dimension: 64 */
+  int32_t n_pool;          /* unit keys summed per pooled key: 4 */
+  int32_t block_keys;      /* keys per cluster block: 512 */
+  int32_t n_buckets;       /* buckets per full block: 64 */
+  int32_t bucket_cap_keys; /* max keys per bucket: 16 */
+  int32_t k;               /* far keys per query, 0..8192 */
+  int32_t n_sink;          /* leading keys always read (clipped to the query) */
+  int32_t window;          /* recent keys always read, query included */
+  int32_t mode;            /* LSA_FLAT or LSA_TREE (cache: build a tree too) */
+  int32_t beam;            /* tree beam width, 1..64 */
+  int32_t leaf_level;      /* tree: level where the beam stops; -1 = smallest l
+                              with beam * 2^l >= ceil(k/4) + 65 */
+  int32_t index_dtype;     /* stored centroids and normalised queries: LSA_F32 | LSA_BF16 */
+  int32_t exact_select;    /* 0: sampled threshold + exact fallback; 1: always exact */
+} lsa_params;
+
+/* Fills *p with the defaults above (k = 2048, flat, bf16). */
+void lsa_default_params(lsa_params* p);
+
+/* Human-readable name of a status code (static storage). */
+const char* lsa_status_string(int status);
+
+/* LSA_OK if *p is within the supported shapes. */
+int lsa_check_params(const lsa_params* p);
+
+/* Index list length n_sink + window + k (or a negative status). */
+int32_t lsa_list_len(const lsa_params* p);
+
+/* Buckets kept per query before expansion: ceil(k / n_pool) + n_buckets + 1.
+ * This many always suffice: each bucket that avoids the sinks and the window
+ * gives at least n_pool keys, and at most n_buckets + 1 buckets touch them. */
+int32_t lsa_top_buckets(const lsa_params* p);
+
+/* ---------------------------------------------------------------- cache --
+ * The bucket cache [catalog "Summary", "Key points"], [visual "How the
+ * hierarchy is built"]: per full 512-key block, 64 buckets, each a unit
+ * centroid (index_dtype, 64 values) and a member table (4 bytes: the
+ * block-local pooled indices of its members, ascending, 0xFF = unused); in
+ * tree mode also the tree levels above the buckets.  Buckets are numbered
+ * 64 * block + rank of their smallest pooled index.  Keys of the trailing
+ * partial block are staged in the cache until the block is full. */
+typedef struct lsa_cache lsa_cache;
+
+/* Device bytes needed for a cache that can hold max_tokens keys. */
+int64_t lsa_cache_bytes(const lsa_params* p, int64_t max_tokens);
+
+/* Creates a host handle over caller-owned device memory `cache_mem` of
+ * `bytes` bytes (>= lsa_cache_bytes).  The cache starts empty.  Structural
+ * parameters (d_latent .. bucket_cap_keys, index_dtype, mode) are fixed here. */
+int lsa_cache_init(const lsa_params* p, int64_t max_tokens, void* cache_mem, int64_t bytes,
+                   lsa_cache** out);
+
+/* Frees the host handle only; the device memory stays the caller's. */
+int lsa_cache_release(lsa_cache* c);
+
+/* Number of keys appended so far. */
+int64_t lsa_cache_tokens(const lsa_cache* c);
+
+/* Device addresses and sizes inside a cache, for reading it back. */
+typedef struct {
+  int64_t n_tokens;        /* keys appended */
+  int64_t n_blocks;        /* full (clustered) blocks */
+  int64_t n_buckets;       /* 64 * n_blocks */
+  void* centroids;         /* [max_buckets, 64] index_dtype */
+  uint32_t* members;       /* [max_buckets] packed pooled indices */
+  float* staging;          /* [block_keys, 64] fp32 keys of the partial block */
+  int32_t tree_height;     /* levels above the buckets (0 without a tree) */
+  int64_t level_nodes[32]; /* nodes per level, level 0 = buckets */
+  void* level_centroids[32];  /* level >= 1: [n, 64] index_dtype */
+  int32_t* level_child[32];   /* level >= 1: [n, 2] child indices, -1 = none */
+  int32_t* level_min_block[32]; /* level >= 1: [n] smallest block below */
+} lsa_cache_view;
+
+int lsa_cache_get_view(const lsa_cache* c, lsa_cache_view* out);
+
+/* ------------------------------------------------------- cache builder --
+ * build_bucket_cache appends n_new latent keys (device fp32 [n_new, 64]) to
+ * the cache and clusters every block that becomes full: keys are
+ * L2-normalised, every 4 consecutive unit keys are summed into a pooled key,
+ * and the 128 pooled keys of the block are merged bottom-up by Ward's method
+ * into 64 buckets of at most 4 pooled keys (16 keys) [catalog "Key points"],
+ * [72x "The same steps in general"], [visual "How the hierarchy is built"].
+ * Greedy global-minimum merging among feasible pairs, ties to the smallest
+ * pair of cluster ids, normalisation and Ward costs in fp64.  Centroids are
+ * the unit vector of the sum of the members' pooled keys, rounded to
+ * index_dtype (nearest even).  In tree mode the tree levels above the new
+ * buckets are rebuilt.  Blocks never change once clustered.
+ * No workspace is needed.  Returns LSA_ERR_CAPACITY past max_tokens. */
+int build_bucket_cache(lsa_cache* c, const float* latent_keys, int64_t n_new, void* stream);
+
+/* ------------------------------------------------------------- indexer --
+ * Workspace for lsa_index_prefill with up to max_queries queries, or for
+ * lsa_index_decode with a batch of max_queries sequences. */
+int64_t lsa_index_workspace_bytes(const lsa_params* p, int64_t max_queries);
+
+/*
+ * lsa_index_prefill: index lists for the Tq queries at positions
+ * q_start .. q_start+Tq-1 of the sequence whose keys are in `c`.
+ *   latent_q  device fp32 [Tq, 64]
+ *   idx       device int32 [Tq, L] with L = lsa_list_len(p): ascending key
+ *             positions, -1 padded
+ *   count     device int32 [Tq]: valid entries of each row
+ *   ranked    optional device int32 [Tq, lsa_top_buckets(p)]: the buckets
+ *             kept before expansion, best first (-1 padded); may be NULL
+ * Steps [visual "What one query actually does"], [72x "The same steps in
+ * general"]: the query is normalised (fp64) and rounded to index_dtype; in
+ * flat mode every eligible bucket (block < position / 512, i.e. complete
+ * earlier blocks) is scored, in tree mode a beam search descends the tree
+ * [catalog "Key points"]; buckets are ranked by (score desc, bucket asc),
+ * opened best-first taking member keys (ascending) that are not sinks or
+ * window keys until k far keys are collected; the list is the sorted union
+ * of sinks, far keys and window.  One list per query, shared by all heads.
+ * The cache may hold keys past the queries (the block mask ignores them),
+ * but it must hold every block that is complete before the last query:
+ * (q_start + Tq - 1) / 512 <= number of full blocks, else LSA_ERR_STATE.
+ */
+int lsa_index_prefill(const lsa_cache* c, const float* latent_q, int64_t q_start, int64_t Tq,
+                      const lsa_params* p, int32_t* idx, int32_t* count, int32_t* ranked,
+                      void* workspace, int64_t ws_bytes, void* stream);
+
+/*
+ * lsa_index_decode: one decode step for B independent sequences.
+ *   caches        host array [B] of handles (distinct caches)
+ *   latent_q      device fp32 [B, 64]: the new query of each sequence
+ *   latent_k_new  device fp32 [B, 64]: the new key of each sequence
+ * For sequence b with p = lsa_cache_tokens(caches[b]) the new key becomes
+ * position p; if it completes a block ((p+1) % 512 == 0) that block is
+ * clustered (and the tree updated) [visual "How the hierarchy is built"];
+ * then the index list of the query at position p is written to idx[b] /
+ * count[b] exactly as lsa_index_prefill would.  The caller appends the
+ * matching K/V rows to its own KV cache.  B <= 64.
+ */
+int lsa_index_decode(lsa_cache* const* caches, int32_t B, const float* latent_q,
+                     const float* latent_k_new, const lsa_params* p, int32_t* idx,
+                     int32_t* count, void* workspace, int64_t ws_bytes, void* stream);
+
+/* ----------------------------------------------------- sparse attention --
+ * Workspace for lsa_sparse_attention (split partials; 0 when splits == 1). */
+int64_t lsa_attention_workspace_bytes(int32_t B, int64_t Tq, int32_t Hq, int32_t D,
+                                      int32_t splits);
+
+/*
+ * lsa_sparse_attention [visual "Intro", "What one query actually does"]:
+ * ordinary softmax attention of every query head over the keys listed for
+ * its query; head h reads KV head h * Hkv / Hq (GQA), all heads of a query
+ * share its list.
+ *   q        [B, Tq, Hq, D]      dtype
+ *   k_cache  [B, Tmax, Hkv, D]   dtype
+ *   v_cache  [B, Tmax, Hkv, D]   dtype
+ *   idx      [B, Tq, L_max] int32 key positions (< Tmax), count [B, Tq]
+ *   out      [B, Tq, Hq, D]      dtype
+ * dtype LSA_BF16 (fp32 accumulation, fp32 softmax) or LSA_F32.
+ * scale multiplies q.k (pass 1/sqrt(D)).  splits >= 1 splits each list into
+ * that many parts whose partial softmax states are combined afterwards
+ * (decode); needs lsa_attention_workspace_bytes of workspace.
+ * A row with count 0 produces zeros.
+ */
+int lsa_sparse_attention(const void* q, const void* k_cache, const void* v_cache, int32_t B,
+                         int64_t Tq, int64_t Tmax, int32_t Hq, int32_t Hkv, int32_t D,
+                         const int32_t* idx, const int32_t* count, int32_t L_max, float scale,
+                         int32_t dtype, int32_t splits, void* out, void* workspace,
+                         int64_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LSA_H */

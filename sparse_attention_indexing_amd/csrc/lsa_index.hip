@@ -1,0 +1,754 @@
+// Indexer: query normalisation, bucket scoring with the causal block mask,
+// exact top-B bucket selection, tree beam search, best-first expansion with
+// sinks and window.
+//
+// [visual "What one query actually does"]: the query is normalised and scored
+// against bucket centroids (flat: every centroid of earlier complete blocks;
+// tree: beam search level by level), the chosen buckets are opened best
+// first until k far keys are collected, the first few tokens and a one-block
+// recent window are always added, and one list is shared by all heads.
+// [72x "The same steps in general"]: keys of an opened bucket that are
+// already sinks or window keys are skipped and the next key takes their
+// place; the list is returned sorted.
+//
+// Flat prefill selection is exact without materialising the
+// (queries x buckets) score matrix:
+//   1. k_thresh: bf16 MFMA scores on a 1/16 sample of bucket tiles, a per-query
+//      histogram, and a threshold tau whose expected pass count is ~2x the
+//      number of buckets kept (B);
+//   2. k_score_filter: every eligible score on MFMA; scores >= tau are
+//      appended (score, bucket) to a per-query candidate list;
+//   3. k_exact_select: queries whose list holds fewer than B or more than
+//      `cap` candidates are redone exactly (radix select on recomputed
+//      scores, ties to the lower bucket);
+//   4. k_select_expand: sort candidates by (score desc, bucket asc), keep B,
+//      expand, sort the far keys, write sinks | far | window.
+// Every bucket with a score >= the B-th best score is a candidate, so the
+// kept set equals the exact top-B whenever step 2 did not overflow.
+#include "lsa_internal.h"
+
+namespace lsa {
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+
+constexpr int kTile = 32;             // buckets per MFMA tile
+constexpr int kSegTiles = 256;        // tiles per score_filter workgroup (8,192 buckets)
+constexpr int kQueriesPerWg = 128;    // 4 waves x 32 queries
+constexpr int kBins = 256;            // threshold histogram bins over [-1, 1]
+
+__device__ __forceinline__ uint32_t f32_orderable(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ int64_t qpos(const IndexCtx& c, int64_t i) {
+  return c.per_seq ? c.pos[i] : c.q_start + i;
+}
+__device__ __forceinline__ const void* qcent(const IndexCtx& c, int64_t i) {
+  return c.per_seq ? c.cent[i] : c.cent[0];
+}
+__device__ __forceinline__ const uint32_t* qmem(const IndexCtx& c, int64_t i) {
+  return c.per_seq ? c.members[i] : c.members[0];
+}
+// buckets of complete blocks before the query's own block
+__device__ __forceinline__ int64_t n_eligible(int64_t p) { return (int64_t)kBuckets * (p / kBlock); }
+
+// Query held by column `col` of wave `wave` in query tile `qt` of an MFMA
+// kernel.  Prefill: 32 queries per wave sharing one cache.  Decode: one query
+// per wave (column 0), because every sequence has its own centroids.
+__device__ __forceinline__ int64_t mfma_query(const IndexCtx& c, int64_t qt, int wave, int col) {
+  if (c.per_seq) return col == 0 ? qt * 4 + wave : -1;
+  return qt * kQueriesPerWg + 32 * wave + col;
+}
+
+// ------------------------------------------------------------------ qnorm
+// 16 lanes per query, 4 dims each; fp64 norm, rounded to the index dtype.
+template <int DT>
+__global__ __launch_bounds__(256) void k_qnorm(const float* __restrict__ y, int64_t n,
+                                               void* __restrict__ yhat) {
+  const int64_t i = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int l = threadIdx.x & 15;
+  float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (i < n) x = reinterpret_cast<const float4*>(y + i * kLatent)[l];
+  double ss = (double)x.x * x.x;
+  ss = __builtin_fma((double)x.y, (double)x.y, ss);
+  ss = __builtin_fma((double)x.z, (double)x.z, ss);
+  ss = __builtin_fma((double)x.w, (double)x.w, ss);
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) ss += __shfl_xor(ss, off, 64);
+  if (i >= n) return;
+  const double nr = __builtin_sqrt(ss);
+  const bool zero = nr < 1e-30;
+  const double v0 = zero ? 0.0 : x.x / nr, v1 = zero ? 0.0 : x.y / nr;
+  const double v2 = zero ? 0.0 : x.z / nr, v3 = zero ? 0.0 : x.w / nr;
+  if (DT == LSA_BF16) {
+    uint2 w;
+    w.x = (uint32_t)f64_to_bf16_rne(v0) | ((uint32_t)f64_to_bf16_rne(v1) << 16);
+    w.y = (uint32_t)f64_to_bf16_rne(v2) | ((uint32_t)f64_to_bf16_rne(v3) << 16);
+    reinterpret_cast<uint2*>(yhat)[i * 16 + l] = w;
+  } else {
+    reinterpret_cast<float4*>(yhat)[i * 16 + l] = make_float4((float)v0, (float)v1, (float)v2, (float)v3);
+  }
+}
+
+// ------------------------------------------------------------------ MFMA tile
+// One wave scores 32 bucket rows (A) against 32 queries (B) with a 64-deep
+// reduction.  Lane l holds row / column l % 32 and the 32 dims of half l / 32;
+// A and B use the same dim order inside each MFMA, so the result is the full
+// dot product.  Output: lane l, register r -> bucket row 8*(r/4) + 4*(l/32)
+// + r%4 of the tile, query column l % 32.
+struct QFrag {
+  bf16x8 b[4];    // bf16: 4 MFMAs x 8 values
+  float f[32];    // fp32: 32 MFMAs x 1 value
+};
+
+template <int DT>
+__device__ __forceinline__ void load_qfrag(QFrag& q, const void* yhat, int64_t qi, bool valid,
+                                           int half) {
+  if (DT == LSA_BF16) {
+    const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(yhat) +
+                                                      qi * kLatent + 32 * half);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint4 u = valid ? src[j] : make_uint4(0, 0, 0, 0);
+      q.b[j] = __builtin_bit_cast(bf16x8, u);
+    }
+  } else {
+    const float* src = reinterpret_cast<const float*>(yhat) + qi * kLatent + 32 * half;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) q.f[j] = valid ? src[j] : 0.f;
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ f32x16 score_tile(const void* cent, int64_t row, int half,
+                                             const QFrag& q) {
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  if (DT == LSA_BF16) {
+    const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(cent) +
+                                                      row * kLatent + 32 * half);
+    uint4 a[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a[j] = src[j];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[j]), q.b[j], acc,
+                                                    0, 0, 0);
+  } else {
+    const float4* src = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(cent) +
+                                                        row * kLatent + 32 * half);
+    float a[32];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float4 v = src[j];
+      a[4 * j] = v.x; a[4 * j + 1] = v.y; a[4 * j + 2] = v.z; a[4 * j + 3] = v.w;
+    }
+#pragma unroll
+    for (int j = 0; j < 32; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[j], q.f[j], acc, 0, 0, 0);
+  }
+  return acc;
+}
+
+__device__ __forceinline__ int tile_row(int r, int lane) {
+  return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+}
+
+// ------------------------------------------------------------------ thresh
+// Histogram of sampled scores per query -> tau.  Workgroup = 128 queries.
+template <int DT>
+__global__ __launch_bounds__(256) void k_thresh(IndexCtx ctx, IndexWs ws) {
+  __shared__ uint32_t hist[kQueriesPerWg][kBins];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < kQueriesPerWg * kBins; i += 256) (&hist[0][0])[i] = 0;
+  const int col = lane & 31, half = lane >> 5;
+  const int64_t qi = mfma_query(ctx, blockIdx.x, wave, col);
+  const bool valid = qi >= 0 && qi < ctx.n;
+  const int64_t ne = valid ? n_eligible(qpos(ctx, qi)) : 0;
+  QFrag qf;
+  load_qfrag<DT>(qf, ws.yhat, valid ? qi : 0, valid, half);
+  // loop bound: the wave's largest eligible count
+  int64_t wmax = ne;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    int64_t o = __shfl_xor(wmax, off, 64);
+    wmax = o > wmax ? o : wmax;
+  }
+  const int64_t wq = mfma_query(ctx, blockIdx.x, wave, 0);
+  const void* cent = qcent(ctx, wq < ctx.n ? wq : 0);
+  __syncthreads();
+  const int64_t n_tiles = wmax / kTile;
+  for (int64_t t = 0; t < n_tiles; t += kSampleStride) {
+    f32x16 acc = score_tile<DT>(cent, t * kTile + col, half, qf);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t g = t * kTile + tile_row(r, lane);
+      if (g < ne) {
+        int bin = (int)__builtin_floorf((acc[r] + 1.0f) * (kBins / 2));
+        bin = bin < 0 ? 0 : (bin >= kBins ? kBins - 1 : bin);
+        atomicAdd(&hist[32 * wave + col][bin], 1u);
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < kQueriesPerWg) {
+    const int64_t qj = mfma_query(ctx, blockIdx.x, tid >> 5, tid & 31);
+    if (qj >= 0 && qj < ctx.n) {
+      const int64_t nej = n_eligible(qpos(ctx, qj));
+      float tau = -3.0e38f;
+      if (nej > ctx.cap) {
+        const int64_t ntl = nej / kTile;
+        const int64_t nsamp = (ntl + kSampleStride - 1) / kSampleStride;
+        const int64_t want = (2 * (int64_t)ctx.top_b * nsamp + ntl - 1) / ntl;
+        int64_t cum = 0;
+        for (int b = kBins - 1; b >= 0; --b) {
+          cum += hist[tid][b];
+          if (cum >= want) { tau = (float)b / (kBins / 2) - 1.0f; break; }
+        }
+      }
+      ws.tau[qj] = tau;
+      ws.cand_cnt[qj] = 0;
+      ws.status[qj] = 0;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ score + filter
+// grid.x = bucket segments of 8,192, grid.y = query tiles of 128.
+template <int DT>
+__global__ __launch_bounds__(256) void k_score_filter(IndexCtx ctx, IndexWs ws, int seg_tiles) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const int64_t qi = mfma_query(ctx, blockIdx.y, wave, col);
+  const bool valid = qi >= 0 && qi < ctx.n;
+  const int64_t ne = valid ? n_eligible(qpos(ctx, qi)) : 0;
+  int64_t wmax = ne;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    int64_t o = __shfl_xor(wmax, off, 64);
+    wmax = o > wmax ? o : wmax;
+  }
+  const int64_t t0 = (int64_t)blockIdx.x * seg_tiles;
+  int64_t t1 = wmax / kTile;
+  if (t1 > t0 + seg_tiles) t1 = t0 + seg_tiles;
+  if (t0 >= t1) return;
+  QFrag qf;
+  load_qfrag<DT>(qf, ws.yhat, valid ? qi : 0, valid, half);
+  const float tau = valid ? ws.tau[qi] : 3.0e38f;
+  const int64_t wq = mfma_query(ctx, blockIdx.y, wave, 0);
+  const void* cent = qcent(ctx, wq < ctx.n ? wq : 0);
+  uint2* cand = ws.cand + (valid ? qi : 0) * (int64_t)ctx.cap;
+  for (int64_t t = t0; t < t1; ++t) {
+    f32x16 acc = score_tile<DT>(cent, t * kTile + col, half, qf);
+    float m = acc[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) m = fmaxf(m, acc[r]);
+    if (__ballot(m >= tau) == 0) continue;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t g = t * kTile + tile_row(r, lane);
+      if (acc[r] >= tau && g < ne) {
+        const int slot = atomicAdd(&ws.cand_cnt[qi], 1);
+        if (slot < ctx.cap) cand[slot] = make_uint2(__float_as_uint(acc[r]), (uint32_t)g);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ exact select
+// Scalar (VALU) score of bucket g, same inputs as the MFMA path.
+template <int DT>
+__device__ __forceinline__ float vscore(const void* cent, int64_t g, const float* yq) {
+  float s = 0.f;
+  if (DT == LSA_BF16) {
+    const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(cent) + g * kLatent);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      uint4 u = src[j];
+      uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s = __builtin_fmaf(bf16_to_f32((uint16_t)(w[e] & 0xffff)), yq[8 * j + 2 * e], s);
+        s = __builtin_fmaf(bf16_to_f32((uint16_t)(w[e] >> 16)), yq[8 * j + 2 * e + 1], s);
+      }
+    }
+  } else {
+    const float4* src = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(cent) + g * kLatent);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      float4 v = src[j];
+      s = __builtin_fmaf(v.x, yq[4 * j], s);
+      s = __builtin_fmaf(v.y, yq[4 * j + 1], s);
+      s = __builtin_fmaf(v.z, yq[4 * j + 2], s);
+      s = __builtin_fmaf(v.w, yq[4 * j + 3], s);
+    }
+  }
+  return s;
+}
+
+template <int DT>
+__device__ __forceinline__ void load_yq(float* yq, const void* yhat, int64_t qi) {
+  if (DT == LSA_BF16) {
+    const uint16_t* src = reinterpret_cast<const uint16_t*>(yhat) + qi * kLatent;
+#pragma unroll
+    for (int d = 0; d < kLatent; ++d) yq[d] = bf16_to_f32(src[d]);
+  } else {
+    const float* src = reinterpret_cast<const float*>(yhat) + qi * kLatent;
+#pragma unroll
+    for (int d = 0; d < kLatent; ++d) yq[d] = src[d];
+  }
+}
+
+// 256-thread exclusive prefix sum; returns the exclusive value, *total = sum.
+__device__ __forceinline__ int block_scan_excl(int v, int* wsum, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    if (w < wave) base += wsum[w];
+    tot += wsum[w];
+  }
+  __syncthreads();
+  *total = tot;
+  return base + x - v;
+}
+
+// One workgroup per query.  Re-does queries whose candidate list is unusable
+// (or every query when `force`): exact B-th largest score by 4 radix passes
+// of 8 bits over the order-preserving integer image of the fp32 score, then
+// emits every bucket above it and, among buckets equal to it, the lowest.
+template <int DT>
+__global__ __launch_bounds__(256) void k_exact_select(IndexCtx ctx, IndexWs ws, int force) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t s_prefix, s_want;
+  __shared__ int wsum[4];
+  __shared__ int s_out;
+  const int tid = threadIdx.x;
+  const int64_t qi = blockIdx.x;
+  if (qi >= ctx.n) return;
+  const int64_t ne = n_eligible(qpos(ctx, qi));
+  const int64_t beff = ne < ctx.top_b ? ne : ctx.top_b;
+  const int cnt = ws.cand_cnt[qi];
+  if (!force && cnt >= beff && cnt <= ctx.cap) return;
+  const void* cent = qcent(ctx, qi);
+  float yq[kLatent];
+  load_yq<DT>(yq, ws.yhat, qi);
+  uint32_t prefix = 0, mask = 0;
+  uint32_t want = (uint32_t)beff;
+  if (tid == 0) { s_out = 0; }
+  if (beff > 0) {
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      hist[tid] = 0;
+      __syncthreads();
+      for (int64_t g = tid; g < ne; g += 256) {
+        const uint32_t key = f32_orderable(vscore<DT>(cent, g, yq));
+        if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      if (tid == 0) {
+        uint32_t cum = 0;
+        for (int b = 255; b >= 0; --b) {
+          if (cum + hist[b] >= want) {
+            s_prefix = prefix | ((uint32_t)b << shift);
+            s_want = want - cum;
+            break;
+          }
+          cum += hist[b];
+        }
+      }
+      __syncthreads();
+      prefix = s_prefix;
+      want = s_want;
+      mask |= 255u << shift;
+      __syncthreads();
+    }
+    // emit: everything above the threshold key, and the `want` lowest buckets equal to it
+    uint2* cand = ws.cand + qi * (int64_t)ctx.cap;
+    int eq_base = 0;
+    for (int64_t g0 = 0; g0 < ne; g0 += 256) {
+      const int64_t g = g0 + tid;
+      float s = 0.f;
+      uint32_t key = 0;
+      if (g < ne) { s = vscore<DT>(cent, g, yq); key = f32_orderable(s); }
+      const int gt = (g < ne) && key > prefix;
+      const int eq = (g < ne) && key == prefix;
+      int eq_tot;
+      const int eq_rank = eq_base + block_scan_excl(eq, wsum, &eq_tot);
+      if (gt || (eq && eq_rank < (int)want)) {
+        const int slot = atomicAdd(&s_out, 1);
+        if (slot < ctx.cap) cand[slot] = make_uint2(__float_as_uint(s), (uint32_t)g);
+      }
+      eq_base += eq_tot;
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    ws.cand_cnt[qi] = (int)beff;
+    ws.status[qi] = 1;
+  }
+}
+
+// ------------------------------------------------------------------ tree search
+// One wave per query.  Beam descent from the root, keeping the best `beam`
+// eligible children (score desc, node asc) on every level down to lstar; then
+// every eligible bucket under the final beam becomes a candidate.
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  const uint32_t lo = __shfl_xor((uint32_t)v, m, 64);
+  const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Sort 128 keys held two per lane (element lane and lane + 64) in descending order.
+__device__ __forceinline__ void wave_bitonic128_desc(uint64_t& e0, uint64_t& e1) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int k = 2; k <= 128; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j == 64) {  // k == 128: pairs (lane, lane + 64), lower index takes the max
+        const uint64_t a = e0, b = e1;
+        e0 = a > b ? a : b;
+        e1 = a > b ? b : a;
+      } else {
+        const uint64_t o0 = shfl_xor_u64(e0, j), o1 = shfl_xor_u64(e1, j);
+        const bool lower = (lane & j) == 0;
+        const bool d0 = (lane & k) == 0, d1 = ((lane + 64) & k) == 0;
+        e0 = (lower == d0) ? (e0 > o0 ? e0 : o0) : (e0 > o0 ? o0 : e0);
+        e1 = (lower == d1) ? (e1 > o1 ? e1 : o1) : (e1 > o1 ? o1 : e1);
+      }
+    }
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__(64) void k_tree_search(IndexCtx ctx, TreeCtx tc, IndexWs ws) {
+  extern __shared__ int32_t tsm[];
+  int32_t* bufA = tsm;
+  int32_t* bufB = tsm + ctx.cap;
+  __shared__ int32_t beam[kMaxBeam];
+  __shared__ int s_nbeam;
+  const int lane = threadIdx.x;
+  const int64_t qi = blockIdx.x;
+  if (qi >= ctx.n) return;
+  const int64_t p = qpos(ctx, qi);
+  const int64_t qb = p / kBlock;
+  const int64_t ne = n_eligible(p);
+  if (lane == 0) { ws.status[qi] = 0; }
+  if (ne == 0) {
+    if (lane == 0) ws.cand_cnt[qi] = 0;
+    return;
+  }
+  float yq[kLatent];
+  load_yq<DT>(yq, ws.yhat, qi);
+  if (lane == 0) { beam[0] = 0; s_nbeam = 1; }
+  __builtin_amdgcn_wave_barrier();
+  __syncthreads();
+  int nbeam = 1;
+  for (int lvl = tc.height - 1; lvl >= tc.lstar; --lvl) {
+    uint64_t e[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      e[h] = 0;
+      const int j = lane;  // beam slot
+      if (j < nbeam) {
+        const int32_t c = tc.child[lvl + 1][2 * beam[j] + h];
+        if (c >= 0) {
+          const int64_t mb = lvl == 0 ? (int64_t)c / kBuckets : (int64_t)tc.minb[lvl][c];
+          if (mb < qb) {
+            const float s = vscore<DT>(tc.cent[lvl], c, yq);
+            e[h] = ((uint64_t)f32_orderable(s) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)c);
+          }
+        }
+      }
+    }
+    // valid entries are nonzero (orderable keys of finite scores have the top bit set or are > 0)
+    wave_bitonic128_desc(e[0], e[1]);
+    const int nvalid = __popcll(__ballot(e[0] != 0)) + __popcll(__ballot(e[1] != 0));
+    const int keep = nvalid < tc.beam ? nvalid : tc.beam;
+    __syncthreads();
+    if (lane < keep) beam[lane] = (int32_t)(0xFFFFFFFFu - (uint32_t)(e[0] & 0xFFFFFFFFu));
+    if (lane + 64 < keep) beam[lane + 64] = (int32_t)(0xFFFFFFFFu - (uint32_t)(e[1] & 0xFFFFFFFFu));
+    nbeam = keep;
+    __syncthreads();
+  }
+  // expand the final beam down to the buckets
+  int n = nbeam;
+  for (int j = lane; j < n; j += 64) bufA[j] = beam[j];
+  __syncthreads();
+  int32_t* cur = bufA;
+  int32_t* nxt = bufB;
+  for (int lvl = tc.lstar; lvl >= 1; --lvl) {
+    int base = 0;
+    for (int j0 = 0; j0 < n; j0 += 32) {
+      const int j = j0 + (lane >> 1);
+      int32_t c = -1;
+      if (j < n) c = tc.child[lvl][2 * cur[j] + (lane & 1)];
+      const uint64_t bal = __ballot(c >= 0);
+      const int pos = base + __popcll(bal & ((1ull << lane) - 1ull));
+      if (c >= 0 && pos < ctx.cap) nxt[pos] = c;
+      base += __popcll(bal);
+    }
+    n = base < ctx.cap ? base : ctx.cap;
+    __syncthreads();
+    int32_t* t = cur; cur = nxt; nxt = t;
+  }
+  // score eligible buckets and write the candidate list
+  uint2* cand = ws.cand + qi * (int64_t)ctx.cap;
+  int out = 0;
+  for (int j0 = 0; j0 < n; j0 += 64) {
+    const int j = j0 + lane;
+    int32_t g = j < n ? cur[j] : -1;
+    const bool ok = g >= 0 && (int64_t)g < ne;
+    float s = 0.f;
+    if (ok) s = vscore<DT>(tc.cent[0], g, yq);
+    const uint64_t bal = __ballot(ok);
+    const int pos = out + __popcll(bal & ((1ull << lane) - 1ull));
+    if (ok) cand[pos] = make_uint2(__float_as_uint(s), (uint32_t)g);
+    out += __popcll(bal);
+  }
+  if (lane == 0) ws.cand_cnt[qi] = out;
+}
+
+// ------------------------------------------------------------------ select + expand
+__device__ void bitonic_sort_u64_desc(uint64_t* a, int n2) {
+  for (int k = 2; k <= n2; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < n2; i += 256) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const uint64_t x = a[i], y = a[ixj];
+          const bool desc = (i & k) == 0;
+          if (desc ? (x < y) : (x > y)) { a[i] = y; a[ixj] = x; }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+__device__ void bitonic_sort_i32_asc(int32_t* a, int n2) {
+  for (int k = 2; k <= n2; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < n2; i += 256) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const int32_t x = a[i], y = a[ixj];
+          const bool asc = (i & k) == 0;
+          if (asc ? (x > y) : (x < y)) { a[i] = y; a[ixj] = x; }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+__device__ __forceinline__ int pow2_ceil(int x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+// One workgroup per query.
+__global__ __launch_bounds__(256) void k_select_expand(IndexCtx ctx, IndexWs ws, int32_t* idx,
+                                                       int32_t* count, int32_t* ranked) {
+  extern __shared__ uint64_t sm[];
+  const int cap = ctx.cap;
+  uint64_t* keys = sm;                                        // [cap]
+  int32_t* far = reinterpret_cast<int32_t*>(keys + cap);      // [pow2(k)]
+  int32_t* excl = far + pow2_ceil(ctx.k > 1 ? ctx.k : 1);     // [top_b]
+  __shared__ int wsum[4];
+  const int tid = threadIdx.x;
+  const int64_t qi = blockIdx.x;
+  if (qi >= ctx.n) return;
+  const int64_t p = qpos(ctx, qi);
+  const uint32_t* mem = qmem(ctx, qi);
+  int c = ws.cand_cnt[qi];
+  c = c < cap ? c : cap;
+  const int n2 = pow2_ceil(c > 1 ? c : 1);
+  const uint2* cand = ws.cand + qi * (int64_t)cap;
+  for (int i = tid; i < n2; i += 256) {
+    uint64_t key = 0;
+    if (i < c) {
+      const uint2 e = cand[i];
+      key = ((uint64_t)f32_orderable(__uint_as_float(e.x)) << 32) | (uint32_t)(0xFFFFFFFFu - e.y);
+    }
+    keys[i] = key;
+  }
+  __syncthreads();
+  bitonic_sort_u64_desc(keys, n2);
+  const int nb = c < ctx.top_b ? c : ctx.top_b;
+  if (ranked) {
+    for (int i = tid; i < ctx.top_b; i += 256)
+      ranked[qi * ctx.top_b + i] = i < nb ? (int32_t)(0xFFFFFFFFu - (uint32_t)(keys[i] & 0xFFFFFFFFu)) : -1;
+  }
+  // near set: sinks [0, s_end) and window [w_start, p]
+  const int64_t s_end = p + 1 < ctx.n_sink ? p + 1 : ctx.n_sink;
+  const int64_t w_start = p - ctx.window + 1 > 0 ? p - ctx.window + 1 : 0;
+  // keys each kept bucket contributes (members not in the near set)
+  int total = 0;
+  for (int i0 = 0; i0 < nb; i0 += 256) {
+    const int i = i0 + tid;
+    int ci = 0;
+    if (i < nb) {
+      const uint32_t g = 0xFFFFFFFFu - (uint32_t)(keys[i] & 0xFFFFFFFFu);
+      const uint32_t m = mem[g];
+      const int64_t kb = (int64_t)(g / kBuckets) * kBlock;
+#pragma unroll
+      for (int e = 0; e < kCapItems; ++e) {
+        const uint32_t j = (m >> (8 * e)) & 0xFFu;
+        if (j != 0xFFu) {
+#pragma unroll
+          for (int u = 0; u < kPool; ++u) {
+            const int64_t key = kb + kPool * j + u;
+            ci += !(key < s_end || key >= w_start);
+          }
+        }
+      }
+    }
+    int tot;
+    const int ex = block_scan_excl(ci, wsum, &tot);
+    if (i < nb) excl[i] = total + ex;
+    total += tot;
+  }
+  __syncthreads();
+  const int n_far = total < ctx.k ? total : ctx.k;
+  for (int i = tid; i < nb; i += 256) {
+    int o = excl[i];
+    if (o >= n_far) continue;
+    const uint32_t g = 0xFFFFFFFFu - (uint32_t)(keys[i] & 0xFFFFFFFFu);
+    const uint32_t m = mem[g];
+    const int64_t kb = (int64_t)(g / kBuckets) * kBlock;
+    for (int e = 0; e < kCapItems && o < n_far; ++e) {
+      const uint32_t j = (m >> (8 * e)) & 0xFFu;
+      if (j == 0xFFu) break;
+      for (int u = 0; u < kPool && o < n_far; ++u) {
+        const int64_t key = kb + kPool * j + u;
+        if (!(key < s_end || key >= w_start)) far[o++] = (int32_t)key;
+      }
+    }
+  }
+  __syncthreads();
+  const int f2 = pow2_ceil(n_far > 1 ? n_far : 1);
+  for (int i = n_far + tid; i < f2; i += 256) far[i] = 0x7fffffff;
+  __syncthreads();
+  bitonic_sort_i32_asc(far, f2);
+  // sinks | far | window, -1 padded
+  int32_t* out = idx + qi * (int64_t)ctx.list_len;
+  int cnt;
+  if (w_start <= s_end) {
+    cnt = (int)(p + 1);
+    for (int i = tid; i < ctx.list_len; i += 256) out[i] = i < cnt ? i : -1;
+  } else {
+    const int ns = (int)s_end, nw = (int)(p - w_start + 1);
+    cnt = ns + n_far + nw;
+    for (int i = tid; i < ctx.list_len; i += 256) {
+      int32_t v = -1;
+      if (i < ns) v = i;
+      else if (i < ns + n_far) v = far[i - ns];
+      else if (i < cnt) v = (int32_t)(w_start + (i - ns - n_far));
+      out[i] = v;
+    }
+  }
+  if (tid == 0) count[qi] = cnt;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ launchers
+
+hipError_t launch_qnorm(const float* y, int64_t n, void* yhat, int dtype, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  dim3 grid((unsigned)((n + 15) / 16));
+  if (dtype == LSA_BF16) hipLaunchKernelGGL(k_qnorm<LSA_BF16>, grid, dim3(256), 0, s, y, n, yhat);
+  else hipLaunchKernelGGL(k_qnorm<LSA_F32>, grid, dim3(256), 0, s, y, n, yhat);
+  return hipGetLastError();
+}
+
+static int64_t query_tiles(const IndexCtx& ctx) {
+  return ctx.per_seq ? (ctx.n + 3) / 4 : (ctx.n + kQueriesPerWg - 1) / kQueriesPerWg;
+}
+
+hipError_t launch_thresh(const IndexCtx& ctx, const IndexWs& ws, int dtype, hipStream_t s) {
+  if (ctx.n <= 0) return hipSuccess;
+  dim3 grid((unsigned)query_tiles(ctx));
+  if (dtype == LSA_BF16) hipLaunchKernelGGL(k_thresh<LSA_BF16>, grid, dim3(256), 0, s, ctx, ws);
+  else hipLaunchKernelGGL(k_thresh<LSA_F32>, grid, dim3(256), 0, s, ctx, ws);
+  return hipGetLastError();
+}
+
+hipError_t launch_score_filter(const IndexCtx& ctx, const IndexWs& ws, int dtype,
+                               int64_t max_tiles, hipStream_t s) {
+  if (ctx.n <= 0 || max_tiles <= 0) return hipSuccess;
+  // decode has few queries: shorter segments give enough workgroups to stream HBM
+  const int seg = ctx.per_seq ? 32 : kSegTiles;
+  dim3 grid((unsigned)((max_tiles + seg - 1) / seg), (unsigned)query_tiles(ctx));
+  if (dtype == LSA_BF16) hipLaunchKernelGGL(k_score_filter<LSA_BF16>, grid, dim3(256), 0, s, ctx, ws, seg);
+  else hipLaunchKernelGGL(k_score_filter<LSA_F32>, grid, dim3(256), 0, s, ctx, ws, seg);
+  return hipGetLastError();
+}
+
+hipError_t launch_exact_select(const IndexCtx& ctx, const IndexWs& ws, int dtype, int force,
+                               hipStream_t s) {
+  if (ctx.n <= 0) return hipSuccess;
+  dim3 grid((unsigned)ctx.n);
+  if (dtype == LSA_BF16) hipLaunchKernelGGL(k_exact_select<LSA_BF16>, grid, dim3(256), 0, s, ctx, ws, force);
+  else hipLaunchKernelGGL(k_exact_select<LSA_F32>, grid, dim3(256), 0, s, ctx, ws, force);
+  return hipGetLastError();
+}
+
+static void allow_large_lds(const void* fn);
+
+hipError_t launch_tree_search(const IndexCtx& ctx, const TreeCtx& tc, const IndexWs& ws,
+                              int dtype, hipStream_t s) {
+  if (ctx.n <= 0) return hipSuccess;
+  static bool once = false;
+  if (!once) {
+    allow_large_lds(reinterpret_cast<const void*>(k_tree_search<LSA_BF16>));
+    allow_large_lds(reinterpret_cast<const void*>(k_tree_search<LSA_F32>));
+    once = true;
+  }
+  const size_t smem = (size_t)2 * ctx.cap * sizeof(int32_t);
+  dim3 grid((unsigned)ctx.n);
+  if (dtype == LSA_BF16) hipLaunchKernelGGL(k_tree_search<LSA_BF16>, grid, dim3(64), smem, s, ctx, tc, ws);
+  else hipLaunchKernelGGL(k_tree_search<LSA_F32>, grid, dim3(64), smem, s, ctx, tc, ws);
+  return hipGetLastError();
+}
+
+// Kernels whose dynamic LDS grows with k may need more than the default 64 KiB.
+// The request is advisory: an error from it is consumed so that it cannot be
+// mistaken for a launch failure by the next hipGetLastError.
+static void allow_large_lds(const void* fn) {
+  (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
+  (void)hipGetLastError();
+}
+
+static int pow2_ceil_host(int x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+hipError_t launch_select_expand(const IndexCtx& ctx, const IndexWs& ws, int32_t* idx,
+                                int32_t* count, int32_t* ranked, hipStream_t s) {
+  if (ctx.n <= 0) return hipSuccess;
+  const size_t smem = (size_t)ctx.cap * 8 + (size_t)pow2_ceil_host(ctx.k > 1 ? ctx.k : 1) * 4 +
+                      (size_t)ctx.top_b * 4;
+  static bool once = false;
+  if (!once) { allow_large_lds(reinterpret_cast<const void*>(k_select_expand)); once = true; }
+  hipLaunchKernelGGL(k_select_expand, dim3((unsigned)ctx.n), dim3(256), smem, s, ctx, ws, idx,
+                     count, ranked);
+  return hipGetLastError();
+}
+
+}  // namespace lsa

@@ -1,0 +1,155 @@
+// Internal declarations of the LSA library (device helpers, launchers).
+// gfx950 only: 64-wide wavefronts, 160 KiB LDS per CU, bf16 MFMA.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/lsa.h"
+
+namespace lsa {
+
+constexpr int kLatent = 64;        // latent dimension
+constexpr int kPool = 4;           // keys per pooled key
+constexpr int kBlock = 512;        // keys per cluster block
+constexpr int kItems = kBlock / kPool;  // pooled keys per block: 128
+constexpr int kBuckets = 64;       // buckets per block
+constexpr int kCapItems = 4;       // 16 keys = 4 pooled keys
+constexpr int kTreeGroup = 128;    // tree: nodes paired inside groups of 128
+constexpr int kMaxLevels = 32;
+constexpr int kMaxK = 8192;
+constexpr int kMaxWindow = 8192;
+constexpr int kHeadDim = 128;
+constexpr int kMaxSeq = 32;        // sequences per batched decode launch
+constexpr int kMaxBeam = 64;
+constexpr int kSampleStride = 16;  // threshold sample: every 16th tile of 32 buckets
+
+// ---------------------------------------------------------------- numerics
+
+// fp64 -> bfloat16 bits, round to nearest even (8 significant bits).
+__host__ __device__ inline uint16_t f64_to_bf16_rne(double x) {
+  union { double d; uint64_t u; } v;
+  v.d = x;
+  const uint64_t sign = v.u & 0x8000000000000000ull;
+  const uint64_t mag = v.u & 0x7fffffffffffffffull;
+  const int e = (int)(mag >> 52) - 1023;
+  if (mag == 0) return (uint16_t)(sign >> 48);
+  if (e >= -126) {
+    // normal bf16 range: drop 45 of the 52 fraction bits with nearest-even
+    const uint64_t lsb = (mag >> 45) & 1ull;
+    uint64_t r = mag + 0x0FFFFFFFFFFFull + lsb;
+    r &= ~((1ull << 45) - 1ull);
+    const int er = (int)(r >> 52) - 1023;
+    if (er > 127) return (uint16_t)((sign >> 48) | 0x7f80u);  // overflow -> inf
+    const uint32_t frac = (uint32_t)((r >> 45) & 0x7f);
+    return (uint16_t)((sign >> 48) | ((uint32_t)(er + 127) << 7) | frac);
+  }
+  // subnormal bf16: quantum 2^-133
+  double q = __builtin_rint(__builtin_ldexp(__builtin_fabs(x), 133));
+  uint32_t m = (uint32_t)q;  // <= 128 (128 rounds up to the smallest normal)
+  return (uint16_t)((sign >> 48) | m);
+}
+
+__host__ __device__ inline float bf16_to_f32(uint16_t b) {
+  union { uint32_t u; float f; } v;
+  v.u = ((uint32_t)b) << 16;
+  return v.f;
+}
+
+// fp32 -> bfloat16 bits, nearest even (finite inputs).
+__host__ __device__ inline uint16_t f32_to_bf16_rne(float f) {
+  union { float f; uint32_t u; } v;
+  v.f = f;
+  const uint32_t lsb = (v.u >> 16) & 1u;
+  return (uint16_t)((v.u + 0x7fffu + lsb) >> 16);
+}
+
+// ---------------------------------------------------------------- cache state
+
+struct CacheLayout {
+  int64_t max_blocks;
+  int64_t off_staging, off_cent, off_members;
+  int64_t lvl_cap[kMaxLevels];
+  int64_t off_lvl_cent[kMaxLevels], off_lvl_child[kMaxLevels], off_lvl_minb[kMaxLevels];
+  int n_levels;  // highest level with storage
+  int64_t total;
+};
+
+struct CacheState {
+  lsa_params prm;
+  int64_t max_tokens;
+  int64_t n_tokens;
+  int64_t n_blocks;
+  char* base;
+  int64_t bytes;
+  CacheLayout lay;
+  int tree;                // 1 if a tree is maintained
+  int height;              // current levels above the buckets
+  int64_t level_n[kMaxLevels];
+};
+
+inline size_t idx_elem_bytes(int dtype) { return dtype == LSA_BF16 ? 2 : 4; }
+
+// ---------------------------------------------------------------- indexer context
+
+// Describes the queries of one indexer launch.  Prefill: one cache, query i
+// at position q_start + i.  Decode: query i belongs to sequence i (own cache,
+// position pos[i]).
+struct IndexCtx {
+  int64_t n;
+  int64_t q_start;
+  int32_t per_seq;
+  int32_t k, n_sink, window;
+  int32_t top_b;          // buckets kept before expansion
+  int32_t cap;            // candidate slots per query
+  int32_t list_len;
+  const void* cent[kMaxSeq];
+  const uint32_t* members[kMaxSeq];
+  int64_t pos[kMaxSeq];
+};
+
+struct TreeCtx {
+  int height;
+  int lstar;
+  int beam;
+  const void* cent[kMaxLevels];       // level 0 = buckets
+  const int32_t* child[kMaxLevels];   // level >= 1
+  const int32_t* minb[kMaxLevels];    // level >= 1
+};
+
+struct IndexWs {
+  void* yhat;          // [n, 64] index dtype
+  float* tau;          // [n]
+  int32_t* cand_cnt;   // [n]
+  uint2* cand;         // [n, cap] (score bits, bucket)
+  int32_t* status;     // [n] 1 if the exact path was used
+};
+
+// ---------------------------------------------------------------- launchers
+// All launchers enqueue on `s` and return hipSuccess or the launch error.
+
+hipError_t launch_ward_blocks(const float* keys, int64_t first_block, int64_t n_blocks,
+                              void* cent, uint32_t* members, int dtype, hipStream_t s);
+hipError_t launch_tree_groups(const void* child_cent, const int32_t* child_minb,
+                              int64_t n_child, int64_t g0, int64_t g1, void* cent,
+                              int32_t* child, int32_t* minb, int dtype, int child_is_bucket,
+                              hipStream_t s);
+hipError_t launch_copy_rows(float* dst, const float* src, int64_t n, hipStream_t s);
+
+hipError_t launch_qnorm(const float* y, int64_t n, void* yhat, int dtype, hipStream_t s);
+hipError_t launch_thresh(const IndexCtx& ctx, const IndexWs& ws, int dtype, hipStream_t s);
+hipError_t launch_score_filter(const IndexCtx& ctx, const IndexWs& ws, int dtype,
+                               int64_t max_tiles, hipStream_t s);
+hipError_t launch_exact_select(const IndexCtx& ctx, const IndexWs& ws, int dtype, int force,
+                               hipStream_t s);
+hipError_t launch_tree_search(const IndexCtx& ctx, const TreeCtx& tc, const IndexWs& ws,
+                              int dtype, hipStream_t s);
+hipError_t launch_select_expand(const IndexCtx& ctx, const IndexWs& ws, int32_t* idx,
+                                int32_t* count, int32_t* ranked, hipStream_t s);
+
+hipError_t launch_attention(const void* q, const void* k, const void* v, int32_t B, int64_t Tq,
+                            int64_t Tmax, int32_t Hq, int32_t Hkv, const int32_t* idx,
+                            const int32_t* count, int32_t L_max, float scale, int dtype,
+                            int32_t splits, void* out, float* ws, hipStream_t s);
+
+}  // namespace lsa

@@ -1,0 +1,123 @@
+"""The C-ABI library loads, exports every entry point the header declares, and
+rejects bad arguments on the host before anything reaches a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_attention_indexing_amd as lsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lsa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(lsa.LIB_PATH), reason="liblsa.so not built")
+
+FAKE_DEV = ctypes.c_void_p(1 << 20)   # aligned address; init only records it
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\**\s+([a-z_0-9]+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert "build_bucket_cache" in names and "lsa_sparse_attention" in names
+    assert len(names) >= 16
+    L = ctypes.CDLL(lsa.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def _p(**kw):
+    return lsa.Params(**kw)
+
+
+def test_params_validation():
+    L = lsa.lib()
+    assert L.lsa_check_params(ctypes.byref(_p().c())) == 0
+    for bad in [dict(d_latent=32), dict(n_pool=8), dict(block_keys=256), dict(n_buckets=32),
+                dict(bucket_cap_keys=8), dict(k=-1), dict(k=9000), dict(window=0),
+                dict(beam=65), dict(index_dtype=7), dict(mode=3), dict(exact_select=2)]:
+        assert L.lsa_check_params(ctypes.byref(_p(**bad).c())) == -2, bad
+    assert L.lsa_check_params(None) == -1
+    d = lsa._Params()
+    L.lsa_default_params(ctypes.byref(d))
+    assert (d.d_latent, d.n_pool, d.block_keys, d.n_buckets, d.bucket_cap_keys) == (64, 4, 512, 64, 16)
+    assert (d.k, d.n_sink, d.window) == (2048, 4, 512)
+
+
+def test_sizes():
+    assert lsa.list_len(_p(k=2048)) == 4 + 512 + 2048
+    assert lsa.list_len(_p(k=4096)) == 4612
+    assert lsa.top_buckets(_p(k=2048)) == 512 + 65
+    assert lsa.top_buckets(_p(k=4096)) == 1089
+    L = lsa.lib()
+    flat = L.lsa_cache_bytes(ctypes.byref(_p().c()), 1 << 20)
+    tree = L.lsa_cache_bytes(ctypes.byref(_p(mode=lsa.LSA_TREE).c()), 1 << 20)
+    nb = (1 << 20) // 512 * 64
+    assert flat >= nb * (128 + 4)
+    assert tree > flat + (nb - 1) * 128
+    # bf16 centroids + 4-byte member tables: 16.5 bytes per token
+    assert flat / (1 << 20) < 17.0
+    assert L.lsa_cache_bytes(ctypes.byref(_p().c()), -1) == -1
+    assert L.lsa_index_workspace_bytes(ctypes.byref(_p().c()), 100) > 100 * 2048 * 8
+
+
+def test_cache_init_and_host_errors():
+    L = lsa.lib()
+    p = _p()
+    need = L.lsa_cache_bytes(ctypes.byref(p.c()), 4096)
+    h = ctypes.c_void_p()
+    assert L.lsa_cache_init(ctypes.byref(p.c()), 4096, FAKE_DEV, need - 1, ctypes.byref(h)) == -4
+    assert L.lsa_cache_init(ctypes.byref(p.c()), 4096, None, need, ctypes.byref(h)) == -1
+    assert L.lsa_cache_init(ctypes.byref(p.c()), 4096, ctypes.c_void_p((1 << 20) + 8), need,
+                            ctypes.byref(h)) == -1
+    assert L.lsa_cache_init(ctypes.byref(p.c()), 4096, FAKE_DEV, need, ctypes.byref(h)) == 0
+    try:
+        assert L.lsa_cache_tokens(h) == 0
+        # nothing to do / over capacity / null keys: all decided on the host
+        assert L.build_bucket_cache(h, None, 0, None) == 0
+        assert L.build_bucket_cache(h, FAKE_DEV, 5000, None) == -4
+        assert L.build_bucket_cache(h, None, 10, None) == -1
+        assert L.build_bucket_cache(h, FAKE_DEV, -1, None) == -1
+        ws = L.lsa_index_workspace_bytes(ctypes.byref(p.c()), 8)
+        # queries past the clustered blocks
+        assert L.lsa_index_prefill(h, FAKE_DEV, 1000, 8, ctypes.byref(p.c()), FAKE_DEV, FAKE_DEV,
+                                   None, FAKE_DEV, ws, None) == -6
+        # workspace too small
+        assert L.lsa_index_prefill(h, FAKE_DEV, 0, 8, ctypes.byref(p.c()), FAKE_DEV, FAKE_DEV,
+                                   None, FAKE_DEV, ws - 1, None) == -3
+        # tree query on a flat cache; dtype mismatch
+        assert L.lsa_index_prefill(h, FAKE_DEV, 0, 8, ctypes.byref(_p(mode=1).c()), FAKE_DEV,
+                                   FAKE_DEV, None, FAKE_DEV, ws, None) == -6
+        assert L.lsa_index_prefill(h, FAKE_DEV, 0, 8, ctypes.byref(_p(index_dtype=0).c()),
+                                   FAKE_DEV, FAKE_DEV, None, FAKE_DEV, 1 << 30, None) == -1
+        arr = (ctypes.c_void_p * 2)(h, h)
+        assert L.lsa_index_decode(arr, 2, FAKE_DEV, FAKE_DEV, ctypes.byref(p.c()), FAKE_DEV,
+                                  FAKE_DEV, FAKE_DEV, 1 << 30, None) == -1   # same cache twice
+        assert L.lsa_index_decode(arr, 65, FAKE_DEV, FAKE_DEV, ctypes.byref(p.c()), FAKE_DEV,
+                                  FAKE_DEV, FAKE_DEV, 1 << 30, None) == -1
+        assert L.lsa_cache_tokens(h) == 0     # rejected calls changed nothing
+    finally:
+        assert L.lsa_cache_release(h) == 0
+
+
+def test_attention_host_errors():
+    L = lsa.lib()
+    f = ctypes.c_float(0.1)
+    args = lambda D=128, Hq=32, Hkv=4, dt=1, splits=1, ws=0: (
+        FAKE_DEV, FAKE_DEV, FAKE_DEV, 1, 16, 1024, Hq, Hkv, D, FAKE_DEV, FAKE_DEV, 100, f, dt,
+        splits, FAKE_DEV, None, ws, None)
+    assert L.lsa_sparse_attention(*args(D=64)) == -2
+    assert L.lsa_sparse_attention(*args(Hq=30)) == -2
+    assert L.lsa_sparse_attention(*args(Hq=64, Hkv=2)) == -2
+    assert L.lsa_sparse_attention(*args(dt=5)) == -2
+    assert L.lsa_sparse_attention(*args(splits=0)) == -1
+    assert L.lsa_sparse_attention(*args(splits=4)) == -3
+    assert L.lsa_attention_workspace_bytes(1, 16, 32, 128, 1) == 0
+    assert L.lsa_attention_workspace_bytes(1, 16, 32, 128, 4) == 16 * 4 * 32 * 130 * 4
+    assert L.lsa_status_string(-3) == b"workspace too small"

@@ -1,0 +1,258 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.  Bucket partitions and index lists must match exactly
+outside near ties (decision gaps below 1e-5, reported); attention within
+1e-4 (fp32) / 2e-2 (bf16) max-abs."""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import lsa_synth as S
+import sparse_attention_indexing_amd as lsa
+from oracle import lsa_oracle as O
+from parity_util import (bf16_tensor, cache_to_host, check_list_invariants, compare_cache,
+                         compare_lists, gpu_cache, oracle_params)
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    lsa.lib()
+
+
+def _c1(T=4096, dtype=lsa.LSA_F32, k=256):
+    w = S.WORKLOADS[1]
+    X, Y, _ = S.latent_inputs(w, T=T, query_rows=(0, T))
+    p = lsa.Params(k=k, index_dtype=dtype)
+    return w, X, Y, p
+
+
+# ---------------------------------------------------------------- inputs
+
+def test_device_generator_matches_host():
+    say("case: synth device vs host")
+    w = S.WORKLOADS[2]
+    rows, width = 300, 512
+    for tensor, dt in (("k", "bf16"), ("q", "f32")):
+        ww = S.Workload(**{**w.__dict__, "dtype": dt})
+        host, bits = S.normal_rows(ww, tensor, np.arange(rows), width, row_offset=1000)
+        out = torch.empty(rows * width, dtype=torch.bfloat16 if dt == "bf16" else torch.float32,
+                          device="cuda")
+        S.device_fill_normal(out.data_ptr(), rows * width, S.philox_key(ww.cfg, tensor),
+                             1000 * width, dt == "bf16")
+        torch.cuda.synchronize()
+        dev = out.float().cpu().numpy().reshape(rows, width)
+        assert np.array_equal(dev, host), f"{tensor}: {np.sum(dev != host)} elements differ"
+
+
+# ---------------------------------------------------------------- builder
+
+@pytest.mark.parametrize("dtype", [lsa.LSA_F32, lsa.LSA_BF16])
+def test_build_matches_oracle(dtype):
+    say(f"case: build T=4096 dtype={dtype}")
+    w, X, Y, p = _c1(dtype=dtype)
+    c = gpu_cache(X, p)
+    oc = O.build_cache(X, oracle_params(p))
+    rep = compare_cache(cache_to_host(c), oc, X)
+    say("build", rep)
+
+
+def test_build_incremental_appends():
+    say("case: build incremental")
+    w, X, Y, p = _c1(T=16 * 512 + 300, dtype=lsa.LSA_BF16)
+    c = gpu_cache(X, p, chunks=[700, 1, 5000, 11, 512, X.shape[0] - 6224])
+    assert c.n_tokens == X.shape[0]
+    oc = O.build_cache(X, oracle_params(p))
+    compare_cache(cache_to_host(c), oc, X)
+
+
+# ---------------------------------------------------------------- indexer
+
+def test_index_c1_all_queries():
+    say("case: index T=4096 f32 all queries")
+    w, X, Y, p = _c1()
+    c = gpu_cache(X, p)
+    idx, cnt = lsa.index_prefill(c, torch.from_numpy(Y).cuda(), 0, p)
+    torch.cuda.synchronize()
+    oc = O.build_cache(X, oracle_params(p))
+    rep = compare_lists(idx.cpu().numpy(), cnt.cpu().numpy(), range(4096), Y, oc)
+    say("index", rep)
+
+
+@pytest.mark.parametrize("k,exact", [(256, 0), (2048, 0), (256, 1)])
+def test_index_sampled_threshold(k, exact):
+    """T=32768: most queries have more eligible buckets than candidate slots,
+    so the sampled threshold + filter path (or the exact path) decides."""
+    say(f"case: index T=32768 bf16 k={k} exact={exact}")
+    w = S.WORKLOADS[2]
+    T = 32768
+    X, Y, _ = S.latent_inputs(w, T=T, query_rows=(0, T))
+    p = lsa.Params(k=k, index_dtype=lsa.LSA_BF16, exact_select=exact)
+    c = gpu_cache(X, p)
+    idx, cnt = lsa.index_prefill(c, torch.from_numpy(Y).cuda(), 0, p)
+    torch.cuda.synchronize()
+    oc = O.build_cache(X, oracle_params(p))
+    pos = np.unique(np.concatenate([np.arange(0, T, 61), np.arange(T - 64, T), [511, 512, 513]]))
+    rep = compare_lists(idx.cpu().numpy()[pos], cnt.cpu().numpy()[pos], pos, Y[pos], oc)
+    say("index", rep)
+
+
+def test_index_last_chunk_and_determinism():
+    say("case: index last chunk, twice")
+    w = S.WORKLOADS[2]
+    T, Tq = 20000, 3000
+    X, Y, _ = S.latent_inputs(w, T=T, query_rows=(T - Tq, T))
+    p = lsa.Params(k=512, index_dtype=lsa.LSA_BF16)
+    c = gpu_cache(X, p)
+    Yd = torch.from_numpy(Y).cuda()
+    a = lsa.index_prefill(c, Yd, T - Tq, p)
+    b = lsa.index_prefill(c, Yd, T - Tq, p)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    oc = O.build_cache(X, oracle_params(p))
+    rows = np.arange(0, Tq, 37)
+    compare_lists(a[0].cpu().numpy()[rows], a[1].cpu().numpy()[rows], T - Tq + rows, Y[rows], oc)
+
+
+# ---------------------------------------------------------------- attention
+
+def _qkv_host(w, T, Tq_rows):
+    q, qb = S.normal_rows(w, "q", Tq_rows, w.Hq * w.D)
+    k, kb = S.normal_rows(w, "k", np.arange(T), w.Hkv * w.D)
+    v, vb = S.normal_rows(w, "v", np.arange(T), w.Hkv * w.D)
+    return (q.reshape(-1, w.Hq, w.D), k.reshape(T, w.Hkv, w.D), v.reshape(T, w.Hkv, w.D),
+            qb, kb, vb)
+
+
+def test_attention_f32_on_oracle_lists():
+    say("case: attention f32 T=4096")
+    w, X, Y, p = _c1()
+    oc = O.build_cache(X, oracle_params(p))
+    rows = np.arange(0, 4096, 16)
+    q, k, v, *_ = _qkv_host(w, 4096, rows)
+    L = lsa.list_len(p)
+    res = [O.index_query(Y[r], int(r), oc) for r in rows]
+    idx = np.stack([r.idx for r in res]).astype(np.int32)
+    cnt = np.array([r.count for r in res], np.int32)
+    out = lsa.sparse_attention(torch.from_numpy(q).cuda(), torch.from_numpy(k).cuda(),
+                               torch.from_numpy(v).cuda(), torch.from_numpy(idx).cuda(),
+                               torch.from_numpy(cnt).cuda())
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    err = max(np.abs(out[i] - O.attention_query(q[i], k, v, idx[i], cnt[i])).max()
+              for i in range(len(rows)))
+    say("attention f32 max abs err", err)
+    assert err <= 1e-4
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+def test_attention_bf16_on_oracle_lists(splits):
+    say(f"case: attention bf16 splits={splits}")
+    w = S.WORKLOADS[2]
+    T = 8192
+    X, Y, _ = S.latent_inputs(w, T=T, query_rows=(0, T))
+    p = lsa.Params(k=2048, index_dtype=lsa.LSA_BF16)
+    oc = O.build_cache(X, oracle_params(p))
+    rows = np.concatenate([[0, 1, 5, 600], np.arange(2000, T, 397), [T - 1]])
+    q, k, v, qb, kb, vb = _qkv_host(w, T, rows)
+    res = [O.index_query(Y[r], int(r), oc) for r in rows]
+    idx = np.stack([r.idx for r in res]).astype(np.int32)
+    cnt = np.array([r.count for r in res], np.int32)
+    out = lsa.sparse_attention(bf16_tensor(qb).cuda().view(len(rows), w.Hq, w.D),
+                               bf16_tensor(kb).cuda().view(T, w.Hkv, w.D),
+                               bf16_tensor(vb).cuda().view(T, w.Hkv, w.D),
+                               torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda(),
+                               splits=splits)
+    torch.cuda.synchronize()
+    out = out.float().cpu().numpy()
+    err = max(np.abs(out[i] - O.attention_query(q[i], k, v, idx[i], cnt[i])).max()
+              for i in range(len(rows)))
+    say("attention bf16 max abs err", err)
+    assert err <= 2e-2
+
+
+def test_end_to_end_c1():
+    """GPU lists feed GPU attention; compared with the oracle's own lists and
+    attention wherever the query is not a near tie."""
+    say("case: end-to-end T=4096 f32")
+    w, X, Y, p = _c1()
+    c = gpu_cache(X, p)
+    idx, cnt = lsa.index_prefill(c, torch.from_numpy(Y).cuda(), 0, p)
+    q, k, v, *_ = _qkv_host(w, 4096, np.arange(4096))
+    out = lsa.sparse_attention(torch.from_numpy(q).cuda(), torch.from_numpy(k).cuda(),
+                               torch.from_numpy(v).cuda(), idx, cnt)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    oc = O.build_cache(X, oracle_params(p))
+    err = 0.0
+    for t in range(0, 4096, 13):
+        r = O.index_query(Y[t], t, oc)
+        if r.exempt:
+            continue
+        err = max(err, np.abs(out[t] - O.attention_query(q[t], k, v, r.idx, r.count)).max())
+    say("end-to-end max abs err", err)
+    assert err <= 1e-4
+
+
+# ---------------------------------------------------------------- tree
+
+def test_tree_build_and_search():
+    say("case: tree T=65536")
+    w = S.WORKLOADS[4]
+    T = 65536
+    X, Y, _ = S.latent_inputs(w, T=T, query_rows=(T - 2048, T))
+    p = lsa.Params(k=256, index_dtype=lsa.LSA_BF16, mode=lsa.LSA_TREE, beam=64)
+    c = gpu_cache(X, p, chunks=[30000, 512, T - 30512])
+    g = cache_to_host(c)
+    oc = O.build_cache(X, oracle_params(p))
+    compare_cache(g, oc, X)
+    ot = O.build_tree(oc)
+    assert len(g["levels"]) == ot.height
+    if min(ot.group_min_gap) > 1e-9:
+        for l, lv in enumerate(g["levels"], start=1):
+            assert np.array_equal(lv["child"], ot.levels[l]["child"]), f"level {l} children"
+            assert np.array_equal(lv["min_block"], ot.levels[l]["min_block"]), f"level {l} min_block"
+            assert np.array_equal(lv["cent"], ot.levels[l]["cent"]), f"level {l} centroids"
+    idx, cnt = lsa.index_prefill(c, torch.from_numpy(Y).cuda(), T - 2048, p)
+    torch.cuda.synchronize()
+    rows = np.arange(0, 2048, 29)
+    rep = compare_lists(idx.cpu().numpy()[rows], cnt.cpu().numpy()[rows], T - 2048 + rows, Y[rows],
+                        oc, mode="tree", tree=ot)
+    say("tree index", rep)
+
+
+# ---------------------------------------------------------------- decode
+
+@pytest.mark.parametrize("mode", [lsa.LSA_FLAT, lsa.LSA_TREE])
+def test_decode_steps(mode):
+    say(f"case: decode mode={mode}")
+    w = S.WORKLOADS[3]
+    lens = [4 * 512 + 509, 3000, 1500]       # the first sequence fills a block on step 3
+    p = lsa.Params(k=256, index_dtype=lsa.LSA_BF16, mode=mode)
+    seqs = [S.latent_inputs(w, seq=b, T=n + 4, query_rows=(0, n + 4)) for b, n in enumerate(lens)]
+    caches = [gpu_cache(X[:n], p, max_tokens=n + 4) for (X, Y, _), n in zip(seqs, lens)]
+    for step in range(4):
+        q = torch.from_numpy(np.stack([Y[n + step] for (X, Y, _), n in zip(seqs, lens)])).cuda()
+        kn = torch.from_numpy(np.stack([X[n + step] for (X, Y, _), n in zip(seqs, lens)])).cuda()
+        idx, cnt = lsa.index_decode(caches, q, kn, p)
+        torch.cuda.synchronize()
+        for b, ((X, Y, _), n) in enumerate(zip(seqs, lens)):
+            pos = n + step
+            oc = O.build_cache(X[:pos + 1], oracle_params(p))
+            tree = O.build_tree(oc) if mode == lsa.LSA_TREE else None
+            compare_lists(idx.cpu().numpy()[b:b + 1], cnt.cpu().numpy()[b:b + 1], [pos], Y[pos:pos + 1],
+                          oc, "tree" if tree else "flat", tree)
+    # the block completed by decode is clustered like the oracle's
+    X, Y, _ = seqs[0]
+    oc = O.build_cache(X[:lens[0] + 4], oracle_params(p))
+    compare_cache(cache_to_host(caches[0]), oc, X)
