@@ -22,7 +22,7 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 constexpr int kKT = 32;          // keys per tile
 constexpr int kVStride = 136;    // LDS row stride (bf16) of the staged V tile
 constexpr int kPStride = 40;     // LDS row stride (bf16) of P
-constexpr int kMaxWaves = 8;
+constexpr int kMaxWaves = 4;
 
 __device__ __forceinline__ void wave_fence() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -45,7 +45,35 @@ struct AttnArgs {
 
 constexpr int kWaveLds = kKT * kVStride + 16 * kPStride;  // bf16 elements per wave
 
-__global__ __launch_bounds__(64 * kMaxWaves) void k_attn_bf16(AttnArgs a) {
+// K fragment of one key row for 16x16x32 MFMAs: dims [32u, 32u + 32) (64 B)
+__device__ __forceinline__ void load_krow(uint4* w, const uint16_t* base, int u) {
+  const uint4* src = reinterpret_cast<const uint4*>(base + 32 * u);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) w[j] = src[j];
+}
+// half a V row: dims [64h, 64h + 64) (128 B), kept in eight named registers
+struct VHalf {
+  uint4 r0, r1, r2, r3, r4, r5, r6, r7;
+};
+__device__ __forceinline__ VHalf load_vhalf(const uint16_t* base, int h) {
+  const uint4* src = reinterpret_cast<const uint4*>(base + 64 * h);
+  VHalf v;
+  v.r0 = src[0]; v.r1 = src[1]; v.r2 = src[2]; v.r3 = src[3];
+  v.r4 = src[4]; v.r5 = src[5]; v.r6 = src[6]; v.r7 = src[7];
+  return v;
+}
+__device__ __forceinline__ void store_vhalf(uint16_t* dst, const VHalf& v) {
+  uint4* d = reinterpret_cast<uint4*>(dst);
+  d[0] = v.r0; d[1] = v.r1; d[2] = v.r2; d[3] = v.r3;
+  d[4] = v.r4; d[5] = v.r5; d[6] = v.r6; d[7] = v.r7;
+}
+
+// One workgroup per (query row, split); wave w handles KV heads w, w + nwaves, ...
+// The row's index list is staged in LDS once.  Gathers are software
+// pipelined: the K and V rows of tile t+1 are requested right after the QK^T
+// products of tile t, so their latency overlaps the softmax and PV of tile t.
+// Positions outside [0, Tmax) are skipped (masked to zero weight).
+__global__ __launch_bounds__(64 * kMaxWaves, 3) void k_attn_bf16(AttnArgs a) {
   extern __shared__ uint16_t attn_lds[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nwaves = blockDim.x >> 6;
@@ -57,10 +85,20 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_attn_bf16(AttnArgs a) {
   const int per = (cnt + a.splits - 1) / a.splits;
   const int k0 = split * per;
   const int k1 = (k0 + per) < cnt ? (k0 + per) : cnt;
-  const int32_t* lst = a.idx + row * (int64_t)a.L;
+  const int n = k1 > k0 ? k1 - k0 : 0;
+  const int32_t* lst = a.idx + row * (int64_t)a.L + k0;
+  int32_t* lst_s = reinterpret_cast<int32_t*>(attn_lds + nwaves * kWaveLds);
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const int32_t v = lst[i];
+    lst_s[i] = (v >= 0 && v < a.Tmax) ? v : -1;
+  }
+  __syncthreads();
   const int r16 = lane & 15, u = lane >> 4;
+  const int kk = lane >> 1, hv = lane & 1;       // V staging: key kk, dims half hv
   uint16_t* vs = attn_lds + wave * kWaveLds;
   uint16_t* ps = vs + kKT * kVStride;
+  const uint16_t* kbase = a.k + b * a.Tmax * a.Hkv * kHeadDim;
+  const uint16_t* vbase = a.v + b * a.Tmax * a.Hkv * kHeadDim;
 
   for (int kvh = wave; kvh < a.Hkv; kvh += nwaves) {
     // Q fragment: head row r16 of the group, dims [32u + 8j, +8)
@@ -81,49 +119,41 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_attn_bf16(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) { m[i] = -__builtin_inff(); l[i] = 0.f; }
 
-    for (int t0 = k0; t0 < k1; t0 += kKT) {
-      // ---- S = Q K^T for keys t0 + r16 (tile A) and t0 + 16 + r16 (tile B)
-      const int ia = t0 + r16, ib = t0 + 16 + r16;
-      int32_t pa = ia < k1 ? lst[ia] : -1;
-      int32_t pb = ib < k1 ? lst[ib] : -1;
-      pa = pa < a.Tmax ? pa : -1;   // positions outside the KV cache are skipped
-      pb = pb < a.Tmax ? pb : -1;
+    auto pos_at = [&](int i) -> int32_t { return i < n ? lst_s[i] : -1; };
+    auto row_of = [&](const uint16_t* base, int32_t p) {
+      return base + ((int64_t)(p >= 0 ? p : 0) * a.Hkv + kvh) * kHeadDim;
+    };
+    int32_t pa = pos_at(r16), pb = pos_at(16 + r16), pv = pos_at(kk);
+    uint4 wa[4], wb[4];
+    load_krow(wa, row_of(kbase, pa), u);
+    load_krow(wb, row_of(kbase, pb), u);
+    VHalf vr = load_vhalf(row_of(vbase, pv), hv);
+    for (int t = 0; t < n; t += kKT) {
+      // stage this tile's V rows (registers -> LDS)
+      store_vhalf(vs + kk * kVStride + 64 * hv, vr);
+      // S = Q K^T for keys t + r16 (A) and t + 16 + r16 (B)
       f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
-      {
-        const uint4* ka = reinterpret_cast<const uint4*>(
-            a.k + ((b * a.Tmax + (pa >= 0 ? pa : 0)) * a.Hkv + kvh) * kHeadDim + 32 * u);
-        const uint4* kb = reinterpret_cast<const uint4*>(
-            a.k + ((b * a.Tmax + (pb >= 0 ? pb : 0)) * a.Hkv + kvh) * kHeadDim + 32 * u);
-        uint4 wa[4], wb[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          wa[j] = pa >= 0 ? ka[j] : make_uint4(0, 0, 0, 0);
-          wb[j] = pb >= 0 ? kb[j] : make_uint4(0, 0, 0, 0);
-        }
-        // stage the V tile while the K products run: lane -> key lane/2, dims half lane&1
-        {
-          const int kk = lane >> 1, hv = lane & 1;
-          const int iv = t0 + kk;
-          int32_t pv = iv < k1 ? lst[iv] : -1;
-          pv = pv < a.Tmax ? pv : -1;
-          const uint4* vsrc = reinterpret_cast<const uint4*>(
-              a.v + ((b * a.Tmax + (pv >= 0 ? pv : 0)) * a.Hkv + kvh) * kHeadDim + 64 * hv);
-          uint4* vdst = reinterpret_cast<uint4*>(vs + kk * kVStride + 64 * hv);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) vdst[j] = pv >= 0 ? vsrc[j] : make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[j], __builtin_bit_cast(bf16x8, wa[j]), sa, 0, 0, 0);
-          sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[j], __builtin_bit_cast(bf16x8, wb[j]), sb, 0, 0, 0);
-        }
+      for (int j = 0; j < 4; ++j) {
+        sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[j], __builtin_bit_cast(bf16x8, wa[j]), sa, 0, 0, 0);
+        sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[j], __builtin_bit_cast(bf16x8, wb[j]), sb, 0, 0, 0);
       }
-      // ---- online softmax; lane holds rows 4u + i for key column r16
+      const bool va = pa >= 0, vb = pb >= 0;
+      // request the next tile now
+      if (t + kKT < n) {
+        pa = pos_at(t + kKT + r16);
+        pb = pos_at(t + kKT + 16 + r16);
+        pv = pos_at(t + kKT + kk);
+        load_krow(wa, row_of(kbase, pa), u);
+        load_krow(wb, row_of(kbase, pb), u);
+        vr = load_vhalf(row_of(vbase, pv), hv);
+      }
+      // online softmax; lane holds rows 4u + i for key column r16
       float pA[4], pB[4], alpha[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float xa = pa >= 0 ? sa[i] * a.scale : -__builtin_inff();
-        const float xb = pb >= 0 ? sb[i] * a.scale : -__builtin_inff();
+        const float xa = va ? sa[i] * a.scale : -__builtin_inff();
+        const float xb = vb ? sb[i] * a.scale : -__builtin_inff();
         float mx = fmaxf(xa, xb);
 #pragma unroll
         for (int off = 1; off < 16; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
@@ -142,14 +172,14 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_attn_bf16(AttnArgs a) {
       for (int j = 0; j < 8; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[j][i] *= alpha[i];
-      // ---- P (bf16) to LDS as [head row][key]
+      // P (bf16) to LDS as [head row][key]
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         ps[(4 * u + i) * kPStride + r16] = f32_to_bf16_rne(pA[i]);
         ps[(4 * u + i) * kPStride + 16 + r16] = f32_to_bf16_rne(pB[i]);
       }
       wave_fence();
-      // ---- O += P V: A = P rows r16, keys [8u, +8); B = V keys [8u, +8), dim 16j + r16
+      // O += P V: A = P rows r16, keys [8u, +8); B = V keys [8u, +8), dim 16j + r16
       const bf16x8 pf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(ps + r16 * kPStride + 8 * u));
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -165,7 +195,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_attn_bf16(AttnArgs a) {
       }
       wave_fence();
     }
-    // ---- write: rows 4u + i < G, dims 16j + r16
+    // write: rows 4u + i < G, dims 16j + r16
     if (a.splits == 1) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -332,13 +362,13 @@ hipError_t launch_attention(const void* q, const void* k, const void* v, int32_t
     static bool attr_set = false;
     if (!attr_set) {
       (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_attn_bf16),
-                                hipFuncAttributeMaxDynamicSharedMemorySize,
-                                kMaxWaves * kWaveLds * (int)sizeof(uint16_t));
+                                hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
       (void)hipGetLastError();  // advisory; never report it as a launch failure
       attr_set = true;
     }
-    hipLaunchKernelGGL(k_attn_bf16, dim3((unsigned)rows, (unsigned)splits), dim3(64 * nw),
-                       (size_t)nw * kWaveLds * sizeof(uint16_t), s, a);
+    const int per = (L_max + splits - 1) / splits;
+    const size_t smem = (size_t)nw * kWaveLds * sizeof(uint16_t) + (size_t)per * sizeof(int32_t);
+    hipLaunchKernelGGL(k_attn_bf16, dim3((unsigned)rows, (unsigned)splits), dim3(64 * nw), smem, s, a);
   } else {
     AttnArgsF32 a;
     a.q = (const float*)q; a.k = (const float*)k; a.v = (const float*)v;

@@ -521,53 +521,141 @@ __global__ __launch_bounds__(64) void k_tree_search(IndexCtx ctx, TreeCtx tc, In
 }
 
 // ------------------------------------------------------------------ select + expand
-__device__ void bitonic_sort_u64_desc(uint64_t* a, int n2) {
-  for (int k = 2; k <= n2; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < n2; i += 256) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const uint64_t x = a[i], y = a[ixj];
-          const bool desc = (i & k) == 0;
-          if (desc ? (x < y) : (x > y)) { a[i] = y; a[ixj] = x; }
-        }
-      }
-      __syncthreads();
-    }
+// Lanes of the wave whose 8-bit digit equals this lane's (among `active`).
+__device__ __forceinline__ uint64_t match_digit(uint32_t d, uint64_t active) {
+  uint64_t peers = active;
+#pragma unroll
+  for (int bit = 0; bit < 8; ++bit) {
+    const uint64_t m = __ballot((d >> bit) & 1u);
+    peers &= ((d >> bit) & 1u) ? m : ~m;
   }
+  return peers;
 }
 
-__device__ void bitonic_sort_i32_asc(int32_t* a, int n2) {
-  for (int k = 2; k <= n2; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < n2; i += 256) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const int32_t x = a[i], y = a[ixj];
-          const bool asc = (i & k) == 0;
-          if (asc ? (x > y) : (x < y)) { a[i] = y; a[ixj] = x; }
-        }
-      }
-      __syncthreads();
+// Stable LSD radix sort (8-bit digits) of n non-negative int32 keys in LDS,
+// ascending.  Wave w owns the contiguous chunk [w*ch, (w+1)*ch); `tmp` is a
+// second buffer of n ints, `cnt` 4 x 256 counters.  Returns the buffer that
+// holds the result.
+__device__ int32_t* radix_sort_i32(int32_t* keys, int32_t* tmp, int n, int max_key,
+                                   uint32_t (*cnt)[256]) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ch = (n + 3) / 4;
+  const int c0 = wave * ch;
+  const int c1 = (c0 + ch) < n ? (c0 + ch) : n;
+  int bits = 0;
+  while (bits < 31 && (max_key >> bits) != 0) bits += 8;
+  for (int shift = 0; shift < bits; shift += 8) {
+    for (int i = tid; i < 4 * 256; i += 256) (&cnt[0][0])[i] = 0;
+    __syncthreads();
+    for (int e = c0 + lane; e < c1; e += 64) atomicAdd(&cnt[wave][(keys[e] >> shift) & 255], 1u);
+    __syncthreads();
+    {
+      // digit-major, wave-minor exclusive offsets
+      const int d = tid;
+      uint32_t tot = 0, pre[4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) { pre[w] = tot; tot += cnt[w][d]; }
+      __shared__ int wsum_r[4];
+      int tmp_tot;
+      const int start = block_scan_excl((int)tot, wsum_r, &tmp_tot);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) cnt[w][d] = (uint32_t)start + pre[w];
     }
+    __syncthreads();
+    for (int e0 = c0; e0 < c1; e0 += 64) {
+      const int e = e0 + lane;
+      const bool ok = e < c1;
+      const uint64_t active = __ballot(ok);
+      const int32_t key = ok ? keys[e] : 0;
+      const uint32_t d = ((uint32_t)key >> shift) & 255u;
+      const uint64_t peers = match_digit(d, active);
+      if (ok) {
+        const int rank = __popcll(peers & ((1ull << lane) - 1ull));
+        const uint32_t base = cnt[wave][d];
+        tmp[base + rank] = key;
+        if (rank == 0) cnt[wave][d] = base + (uint32_t)__popcll(peers);
+      }
+    }
+    __syncthreads();
+    int32_t* t = keys; keys = tmp; tmp = t;
   }
+  return keys;
 }
 
-__device__ __forceinline__ int pow2_ceil(int x) {
-  int p = 1;
-  while (p < x) p <<= 1;
-  return p;
+// Weighted radix select over items i < c that pass `filt`, ordered by a
+// 32-bit key descending: finds the key K at which the running weight (from
+// the largest key down) reaches `want`.  On return `want` is the weight
+// still needed from the items whose key equals K.  Requires the total weight
+// of the passing items to be >= want.
+template <class KeyF, class FiltF>
+__device__ uint32_t weighted_select(int c, KeyF key, FiltF filt, const uint8_t* w, uint32_t& want,
+                                    uint32_t (*hist)[256], uint32_t* s_prefix, uint32_t* s_want) {
+  const int tid = threadIdx.x;
+  uint32_t prefix = 0, mask = 0;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    hist[0][tid] = 0;
+    __syncthreads();
+    for (int i = tid; i < c; i += 256) {
+      const uint32_t kv = key(i);
+      if ((kv & mask) == prefix && w[i] && filt(i)) atomicAdd(&hist[0][(kv >> shift) & 255u], (uint32_t)w[i]);
+    }
+    __syncthreads();
+    if (tid < 64) {
+      // lane l owns digits 4l .. 4l+3; weight of higher digits by a suffix scan
+      const int l = tid;
+      const uint32_t h0 = hist[0][4 * l], h1 = hist[0][4 * l + 1];
+      const uint32_t h2 = hist[0][4 * l + 2], h3 = hist[0][4 * l + 3];
+      const uint32_t lsum = h0 + h1 + h2 + h3;
+      uint32_t x = lsum;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_down(x, off, 64);
+        if (l + off < 64) x += y;
+      }
+      const uint32_t above = x - lsum;   // weight of digits > 4l + 3
+      const uint32_t c3 = above + h3, c2 = c3 + h2, c1 = c2 + h1, c0 = c1 + h0;
+      int dig = -1;
+      uint32_t before = 0;
+      if (above < want && c3 >= want) { dig = 4 * l + 3; before = above; }
+      else if (c3 < want && c2 >= want) { dig = 4 * l + 2; before = c3; }
+      else if (c2 < want && c1 >= want) { dig = 4 * l + 1; before = c2; }
+      else if (c1 < want && c0 >= want) { dig = 4 * l; before = c1; }
+      if (dig >= 0) {
+        *s_prefix = prefix | ((uint32_t)dig << shift);
+        *s_want = want - before;
+      }
+    }
+    __syncthreads();
+    prefix = *s_prefix;
+    want = *s_want;
+    mask |= 255u << shift;
+    __syncthreads();
+  }
+  return prefix;
 }
 
-// One workgroup per query.
+// One workgroup per query.  The walk over buckets ranked by (score desc,
+// bucket asc) stops at the bucket where the running count of far keys
+// reaches k.  That bucket is found without sorting: a radix select on the
+// fp32 scores weighted by each bucket's far-key contribution gives the score
+// S* at which the running sum crosses k; buckets above S* are taken whole,
+// buckets tied at S* are walked in bucket order, the crossing one is cut.
+// Every candidate list holds the exact top-B (or every eligible bucket), so
+// the crossing lies inside it.  The far keys are then radix-sorted.
 __global__ __launch_bounds__(256) void k_select_expand(IndexCtx ctx, IndexWs ws, int32_t* idx,
                                                        int32_t* count, int32_t* ranked) {
   extern __shared__ uint64_t sm[];
   const int cap = ctx.cap;
-  uint64_t* keys = sm;                                        // [cap]
-  int32_t* far = reinterpret_cast<int32_t*>(keys + cap);      // [pow2(k)]
-  int32_t* excl = far + pow2_ceil(ctx.k > 1 ? ctx.k : 1);     // [top_b]
+  const int kf = ctx.k > 1 ? ctx.k : 1;
+  uint32_t* skey = reinterpret_cast<uint32_t*>(sm);           // [cap] orderable scores
+  uint32_t* sbkt = skey + cap;                                // [cap] bucket ids
+  uint8_t* contrib = reinterpret_cast<uint8_t*>(sbkt + cap);  // [cap]
+  int32_t* far = reinterpret_cast<int32_t*>(contrib + cap);   // [kf]
+  int32_t* far2 = far + kf;                                   // [kf]
+  __shared__ uint32_t hist[4][256];
   __shared__ int wsum[4];
+  __shared__ uint32_t s_prefix, s_want;
+  __shared__ int s_total, s_trunc_m;
   const int tid = threadIdx.x;
   const int64_t qi = blockIdx.x;
   if (qi >= ctx.n) return;
@@ -575,74 +663,97 @@ __global__ __launch_bounds__(256) void k_select_expand(IndexCtx ctx, IndexWs ws,
   const uint32_t* mem = qmem(ctx, qi);
   int c = ws.cand_cnt[qi];
   c = c < cap ? c : cap;
-  const int n2 = pow2_ceil(c > 1 ? c : 1);
   const uint2* cand = ws.cand + qi * (int64_t)cap;
-  for (int i = tid; i < n2; i += 256) {
-    uint64_t key = 0;
-    if (i < c) {
-      const uint2 e = cand[i];
-      key = ((uint64_t)f32_orderable(__uint_as_float(e.x)) << 32) | (uint32_t)(0xFFFFFFFFu - e.y);
-    }
-    keys[i] = key;
-  }
-  __syncthreads();
-  bitonic_sort_u64_desc(keys, n2);
-  const int nb = c < ctx.top_b ? c : ctx.top_b;
-  if (ranked) {
-    for (int i = tid; i < ctx.top_b; i += 256)
-      ranked[qi * ctx.top_b + i] = i < nb ? (int32_t)(0xFFFFFFFFu - (uint32_t)(keys[i] & 0xFFFFFFFFu)) : -1;
-  }
-  // near set: sinks [0, s_end) and window [w_start, p]
   const int64_t s_end = p + 1 < ctx.n_sink ? p + 1 : ctx.n_sink;
   const int64_t w_start = p - ctx.window + 1 > 0 ? p - ctx.window + 1 : 0;
-  // keys each kept bucket contributes (members not in the near set)
-  int total = 0;
-  for (int i0 = 0; i0 < nb; i0 += 256) {
-    const int i = i0 + tid;
+  // candidates and their far-key contributions (members outside the near set)
+  int my_w = 0;
+  for (int i = tid; i < c; i += 256) {
+    const uint2 e = cand[i];
+    const uint32_t g = e.y;
+    const uint32_t m = mem[g];
+    const int64_t kb = (int64_t)(g / kBuckets) * kBlock;
     int ci = 0;
-    if (i < nb) {
-      const uint32_t g = 0xFFFFFFFFu - (uint32_t)(keys[i] & 0xFFFFFFFFu);
-      const uint32_t m = mem[g];
-      const int64_t kb = (int64_t)(g / kBuckets) * kBlock;
 #pragma unroll
-      for (int e = 0; e < kCapItems; ++e) {
-        const uint32_t j = (m >> (8 * e)) & 0xFFu;
-        if (j != 0xFFu) {
+    for (int q = 0; q < kCapItems; ++q) {
+      const uint32_t j = (m >> (8 * q)) & 0xFFu;
+      if (j != 0xFFu) {
 #pragma unroll
-          for (int u = 0; u < kPool; ++u) {
-            const int64_t key = kb + kPool * j + u;
-            ci += !(key < s_end || key >= w_start);
-          }
+        for (int u = 0; u < kPool; ++u) {
+          const int64_t key = kb + kPool * j + u;
+          ci += !(key < s_end || key >= w_start);
         }
       }
     }
-    int tot;
-    const int ex = block_scan_excl(ci, wsum, &tot);
-    if (i < nb) excl[i] = total + ex;
-    total += tot;
+    skey[i] = f32_orderable(__uint_as_float(e.x));
+    sbkt[i] = g;
+    contrib[i] = (uint8_t)ci;
+    my_w += ci;
   }
-  __syncthreads();
-  const int n_far = total < ctx.k ? total : ctx.k;
-  for (int i = tid; i < nb; i += 256) {
-    int o = excl[i];
-    if (o >= n_far) continue;
-    const uint32_t g = 0xFFFFFFFFu - (uint32_t)(keys[i] & 0xFFFFFFFFu);
-    const uint32_t m = mem[g];
-    const int64_t kb = (int64_t)(g / kBuckets) * kBlock;
-    for (int e = 0; e < kCapItems && o < n_far; ++e) {
-      const uint32_t j = (m >> (8 * e)) & 0xFFu;
-      if (j == 0xFFu) break;
-      for (int u = 0; u < kPool && o < n_far; ++u) {
-        const int64_t key = kb + kPool * j + u;
-        if (!(key < s_end || key >= w_start)) far[o++] = (int32_t)key;
-      }
+  if (tid == 0) { s_trunc_m = 0; s_total = 0; }
+  int total;
+  (void)block_scan_excl(my_w, wsum, &total);   // also orders the LDS writes above
+  // optional output: the kept buckets best first (O(c^2) ranking; for tests)
+  if (ranked) {
+    const int nb = c < ctx.top_b ? c : ctx.top_b;
+    for (int r = nb + tid; r < ctx.top_b; r += 256) ranked[qi * ctx.top_b + r] = -1;
+    for (int i = tid; i < c; i += 256) {
+      int ahead = 0;
+      for (int j = 0; j < c; ++j)
+        ahead += skey[j] > skey[i] || (skey[j] == skey[i] && sbkt[j] < sbkt[i]);
+      if (ahead < nb) ranked[qi * ctx.top_b + ahead] = (int32_t)sbkt[i];
     }
   }
+  // ---- weighted radix select: score S* where the running far-key count reaches k,
+  // then the bucket g* among the buckets tied at S* (lowest bucket first)
+  const int k = ctx.k;
+  uint32_t prefix = 0, gstar_key = 0, want = (uint32_t)k;
+  const bool cut = k > 0 && total >= k;
+  if (cut) {
+    prefix = weighted_select(c, [&](int i) { return skey[i]; }, [&](int) { return true; },
+                             contrib, want, hist, &s_prefix, &s_want);
+    const uint32_t sstar = prefix;
+    gstar_key = weighted_select(c, [&](int i) { return 0xFFFFFFFFu - sbkt[i]; },
+                                [&](int i) { return skey[i] == sstar; }, contrib, want, hist,
+                                &s_prefix, &s_want);
+    if (tid == 0) s_trunc_m = (int)want;
+  }
   __syncthreads();
-  const int f2 = pow2_ceil(n_far > 1 ? n_far : 1);
-  for (int i = n_far + tid; i < f2; i += 256) far[i] = 0x7fffffff;
-  __syncthreads();
-  bitonic_sort_i32_asc(far, f2);
+  // ---- emit far keys: whole buckets above S* (every bucket without a cut),
+  // the cut bucket's first members
+  const int trunc_m = s_trunc_m;
+  const uint32_t gstar = 0xFFFFFFFFu - gstar_key;
+  const int n_far = cut ? k : total;
+  for (int i0 = 0; i0 < c; i0 += 256) {
+    const int i = i0 + tid;
+    int take = 0;
+    if (i < c) {
+      if (!cut || skey[i] > prefix || (skey[i] == prefix && sbkt[i] < gstar)) take = contrib[i];
+      else if (skey[i] == prefix && sbkt[i] == gstar) take = trunc_m;
+    }
+    int chunk_tot;
+    const int o0 = block_scan_excl(take, wsum, &chunk_tot);
+    const int base = s_total;
+    if (take > 0) {
+      int o = base + o0;
+      const uint32_t g = sbkt[i];
+      const uint32_t m = mem[g];
+      const int64_t kb = (int64_t)(g / kBuckets) * kBlock;
+      int left = take;
+      for (int q = 0; q < kCapItems && left > 0; ++q) {
+        const uint32_t j = (m >> (8 * q)) & 0xFFu;
+        if (j == 0xFFu) break;
+        for (int u = 0; u < kPool && left > 0; ++u) {
+          const int64_t key = kb + kPool * j + u;
+          if (!(key < s_end || key >= w_start)) { far[o++] = (int32_t)key; --left; }
+        }
+      }
+    }
+    __syncthreads();
+    if (tid == 0) s_total = base + chunk_tot;
+    __syncthreads();
+  }
+  const int32_t* sorted_far = radix_sort_i32(far, far2, n_far, (int)(p > 0 ? p : 0), hist);
   // sinks | far | window, -1 padded
   int32_t* out = idx + qi * (int64_t)ctx.list_len;
   int cnt;
@@ -655,7 +766,7 @@ __global__ __launch_bounds__(256) void k_select_expand(IndexCtx ctx, IndexWs ws,
     for (int i = tid; i < ctx.list_len; i += 256) {
       int32_t v = -1;
       if (i < ns) v = i;
-      else if (i < ns + n_far) v = far[i - ns];
+      else if (i < ns + n_far) v = sorted_far[i - ns];
       else if (i < cnt) v = (int32_t)(w_start + (i - ns - n_far));
       out[i] = v;
     }
@@ -742,8 +853,7 @@ static int pow2_ceil_host(int x) {
 hipError_t launch_select_expand(const IndexCtx& ctx, const IndexWs& ws, int32_t* idx,
                                 int32_t* count, int32_t* ranked, hipStream_t s) {
   if (ctx.n <= 0) return hipSuccess;
-  const size_t smem = (size_t)ctx.cap * 8 + (size_t)pow2_ceil_host(ctx.k > 1 ? ctx.k : 1) * 4 +
-                      (size_t)ctx.top_b * 4;
+  const size_t smem = (size_t)ctx.cap * 9 + (size_t)(ctx.k > 1 ? ctx.k : 1) * 8;
   static bool once = false;
   if (!once) { allow_large_lds(reinterpret_cast<const void*>(k_select_expand)); once = true; }
   hipLaunchKernelGGL(k_select_expand, dim3((unsigned)ctx.n), dim3(256), smem, s, ctx, ws, idx,
