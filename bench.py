@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--mode", default="flat", choices=["flat", "tree"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration)")
     return ap.parse_args()
 
 
@@ -153,6 +155,12 @@ def main():
             times.append((e0, e1, e2, e3))
         return c
 
+    if args.calib_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()

@@ -20,8 +20,8 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
 constexpr int kKT = 32;          // keys per tile
-constexpr int kVStride = 136;    // LDS row stride (bf16) of the staged V tile
-constexpr int kPStride = 40;     // LDS row stride (bf16) of P
+constexpr int kVStride = 136;    // LDS row stride (bf16) of the staged V tile [key][dim]
+constexpr int kPStride = 16;     // LDS row stride (bf16) of P stored as [key][head]
 constexpr int kMaxWaves = 4;
 
 __device__ __forceinline__ void wave_fence() {
@@ -41,9 +41,42 @@ struct AttnArgs {
   int64_t Tq, Tmax;
   int32_t Hq, Hkv, G, L, splits;
   float scale;
+  float scale_log2;     // scale * log2(e): softmax in base 2
 };
 
-constexpr int kWaveLds = kKT * kVStride + 16 * kPStride;  // bf16 elements per wave
+constexpr int kWaveLds = kKT * kVStride + kKT * kPStride;  // bf16 elements per wave
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+
+// Transposing LDS read (gfx950): within each 16-lane group, lane l receives
+// element (l & 3) of the 8-byte words read by lanes (l >> 2) + 4j, j = 0..3.
+// With lane s of the group pointing at row r0 + (s >> 2), column c0 + 4 (s & 3)
+// of a row-major 16-bit matrix, lane l gets column c0 + l of rows r0 .. r0+3.
+__device__ __forceinline__ uint2 ds_read_tr16(const uint16_t* p) {
+  v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p));
+  return __builtin_bit_cast(uint2, r);
+}
+
+// Reductions over the 16 lanes of a DPP row (quad swaps, half mirror, mirror).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));    // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f<0x141>(v));   // row_half_mirror
+  v = fmaxf(v, dpp_f<0x140>(v));   // row_mirror
+  return v;
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x141>(v);
+  v += dpp_f<0x140>(v);
+  return v;
+}
 
 // K fragment of one key row for 16x16x32 MFMAs: dims [32u, 32u + 32) (64 B)
 __device__ __forceinline__ void load_krow(uint4* w, const uint16_t* base, int u) {
@@ -77,7 +110,12 @@ __global__ __launch_bounds__(64 * kMaxWaves, 3) void k_attn_bf16(AttnArgs a) {
   extern __shared__ uint16_t attn_lds[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nwaves = blockDim.x >> 6;
-  const int64_t row = blockIdx.x;
+  // Workgroups are dealt to the 8 XCDs round-robin; give each XCD a contiguous
+  // range of rows so neighbouring queries (shared window, similar buckets)
+  // meet in the same L2.
+  const int64_t per_xcd = (a.rows + 7) / 8;
+  const int64_t row = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (row >= a.rows) return;
   const int split = blockIdx.y;
   const int64_t b = row / a.Tq;
   int cnt = a.count[row];
@@ -148,49 +186,55 @@ __global__ __launch_bounds__(64 * kMaxWaves, 3) void k_attn_bf16(AttnArgs a) {
         load_krow(wb, row_of(kbase, pb), u);
         vr = load_vhalf(row_of(vbase, pv), hv);
       }
-      // online softmax; lane holds rows 4u + i for key column r16
+      // online softmax (base 2); lane holds rows 4u + i for key column r16
       float pA[4], pB[4], alpha[4];
+      bool grew = false;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float xa = va ? sa[i] * a.scale : -__builtin_inff();
-        const float xb = vb ? sb[i] * a.scale : -__builtin_inff();
-        float mx = fmaxf(xa, xb);
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+        const float xa = va ? sa[i] * a.scale_log2 : -__builtin_inff();
+        const float xb = vb ? sb[i] * a.scale_log2 : -__builtin_inff();
+        const float mx = row16_max(fmaxf(xa, xb));
         const float mn = fmaxf(m[i], mx);
         const bool empty = mn == -__builtin_inff();
-        alpha[i] = empty ? 1.f : __expf(m[i] - mn);
-        pA[i] = empty ? 0.f : __expf(xa - mn);
-        pB[i] = empty ? 0.f : __expf(xb - mn);
-        float rs = pA[i] + pB[i];
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) rs += __shfl_xor(rs, off, 64);
-        l[i] = l[i] * alpha[i] + rs;
+        grew |= mn > m[i];
+        alpha[i] = empty ? 1.f : __builtin_amdgcn_exp2f(m[i] - mn);
+        pA[i] = empty ? 0.f : __builtin_amdgcn_exp2f(xa - mn);
+        pB[i] = empty ? 0.f : __builtin_amdgcn_exp2f(xb - mn);
+        l[i] = l[i] * alpha[i] + row16_sum(pA[i] + pB[i]);
         m[i] = mn;
       }
+      if (__ballot(grew)) {   // rescale only when some row maximum moved
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < 8; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o[j][i] *= alpha[i];
-      // P (bf16) to LDS as [head row][key]
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ps[(4 * u + i) * kPStride + r16] = f32_to_bf16_rne(pA[i]);
-        ps[(4 * u + i) * kPStride + 16 + r16] = f32_to_bf16_rne(pB[i]);
+          for (int i = 0; i < 4; ++i) o[j][i] *= alpha[i];
+      }
+      // P (bf16) to LDS as [key][head]: 8 contiguous bytes per key and lane
+      {
+        uint2 wa2, wb2;
+        wa2.x = (uint32_t)f32_to_bf16_rne(pA[0]) | ((uint32_t)f32_to_bf16_rne(pA[1]) << 16);
+        wa2.y = (uint32_t)f32_to_bf16_rne(pA[2]) | ((uint32_t)f32_to_bf16_rne(pA[3]) << 16);
+        wb2.x = (uint32_t)f32_to_bf16_rne(pB[0]) | ((uint32_t)f32_to_bf16_rne(pB[1]) << 16);
+        wb2.y = (uint32_t)f32_to_bf16_rne(pB[2]) | ((uint32_t)f32_to_bf16_rne(pB[3]) << 16);
+        *reinterpret_cast<uint2*>(ps + r16 * kPStride + 4 * u) = wa2;
+        *reinterpret_cast<uint2*>(ps + (16 + r16) * kPStride + 4 * u) = wb2;
       }
       wave_fence();
-      // O += P V: A = P rows r16, keys [8u, +8); B = V keys [8u, +8), dim 16j + r16
-      const bf16x8 pf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(ps + r16 * kPStride + 8 * u));
+      // O += P V.  A = P: lane row r16 = head, keys [8u, +8); B = V: column
+      // 16j + r16 = dim, keys [8u, +8).  Both come from transposing reads:
+      // source lane s of a group points at key 8u + (s >> 2) (+4), column 4 (s & 3).
+      const int sk = 8 * u + (r16 >> 2), sc = 4 * (r16 & 3);
+      bf16x8 pf;
+      {
+        const uint2 lo = ds_read_tr16(ps + sk * kPStride + sc);
+        const uint2 hi = ds_read_tr16(ps + (sk + 4) * kPStride + sc);
+        pf = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+      }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        uint32_t w[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t lo = vs[(8 * u + 2 * e) * kVStride + 16 * j + r16];
-          const uint32_t hi = vs[(8 * u + 2 * e + 1) * kVStride + 16 * j + r16];
-          w[e] = lo | (hi << 16);
-        }
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+        const uint2 lo = ds_read_tr16(vs + sk * kVStride + 16 * j + sc);
+        const uint2 hi = ds_read_tr16(vs + (sk + 4) * kVStride + 16 * j + sc);
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
         o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf, vf, o[j], 0, 0, 0);
       }
       wave_fence();
@@ -220,8 +264,193 @@ __global__ __launch_bounds__(64 * kMaxWaves, 3) void k_attn_bf16(AttnArgs a) {
           float* orow = ob + (slot * a.Hq + h) * kHeadDim;
 #pragma unroll
           for (int j = 0; j < 8; ++j) orow[16 * j + r16] = o[j][i];
-          if (r16 == 0) { mb[slot * a.Hq + h] = m[i]; lb[slot * a.Hq + h] = l[i]; }
+          // running max back to natural-log units for the combine step
+          if (r16 == 0) { mb[slot * a.Hq + h] = m[i] * 0.6931471805599453f; lb[slot * a.Hq + h] = l[i]; }
         }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Four-KV-head path (Hkv = 4, the shape of the 128K .. 10M workloads).  A
+// token's K (and V) rows for all four KV heads are 1 KiB contiguous, so the
+// workgroup streams each tile of 16 tokens with one 64-lane 16-byte load per
+// token and tensor, straight from global memory into LDS
+// (global_load_lds_dwordx4: lane i writes bytes [16 i, 16 i + 16) of the
+// row).  Two LDS stages: tile t+1 is in flight while tile t is computed.
+// Wave w then computes KV head w: S = Q K^T on 16x16x32 MFMAs (B from LDS,
+// 64 contiguous bytes per lane), online softmax with DPP row reductions, and
+// O += P V on 16x16x16 MFMAs whose A (P) and B (V) operands come from
+// transposing LDS reads.  Rows are padded (K: 1040 B, V: 1056 B) so that the
+// 16 lanes of a group hit distinct banks.
+constexpr int kT3 = 16;                 // tokens per tile
+constexpr int kKRow3 = 1040;            // bytes per token row of K in LDS
+constexpr int kVRow3 = 1056;            // bytes per token row of V in LDS
+constexpr int kStage3 = kT3 * (kKRow3 + kVRow3);   // bytes per stage
+constexpr int kP3 = kT3 * 16 * 2;       // P tile [16 keys][16 heads] bf16, per wave
+constexpr int kLds3 = 2 * kStage3 + 4 * kP3;
+
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void g2lds16(const void* g, char* lds_row) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_row, 16, 0, 0);
+}
+
+__global__ __launch_bounds__(256, 2) void k_attn_bf16_h4(AttnArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char lds3[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t per_xcd = (a.rows + 7) / 8;
+  const int64_t row = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (row >= a.rows) return;
+  const int split = blockIdx.y;
+  const int64_t b = row / a.Tq;
+  int cnt = a.count[row];
+  cnt = cnt < 0 ? 0 : (cnt > a.L ? a.L : cnt);
+  const int per = (cnt + a.splits - 1) / a.splits;
+  const int k0 = split * per;
+  const int k1 = (k0 + per) < cnt ? (k0 + per) : cnt;
+  const int n = k1 > k0 ? k1 - k0 : 0;
+  const int32_t* lst = a.idx + row * (int64_t)a.L + k0;
+  const char* kbase = reinterpret_cast<const char*>(a.k + b * a.Tmax * 4 * kHeadDim);
+  const char* vbase = reinterpret_cast<const char*>(a.v + b * a.Tmax * 4 * kHeadDim);
+  uint16_t* ps = reinterpret_cast<uint16_t*>(lds3 + 2 * kStage3 + wave * kP3);
+  const int r16 = lane & 15, u = lane >> 4;
+  const int kvh = wave;
+
+  // zero the V rows once: skipped (invalid) tokens must never feed NaN garbage
+  for (int i = threadIdx.x; i < 2 * kT3 * kVRow3 / 16; i += 256) {
+    const int st = i / (kT3 * kVRow3 / 16), r = i % (kT3 * kVRow3 / 16);
+    reinterpret_cast<uint4*>(lds3 + st * kStage3 + kT3 * kKRow3)[r] = make_uint4(0, 0, 0, 0);
+  }
+  __syncthreads();
+
+  // positions of a tile: lane l < 16 holds key t + l (-1 past the end or outside the cache)
+  auto load_pos = [&](int t) -> int32_t {
+    int32_t p = (lane < kT3 && t + lane < n) ? lst[t + lane] : -1;
+    return (p >= 0 && p < a.Tmax) ? p : -1;
+  };
+  // wave w loads tokens 4w .. 4w+3 of a tile (K and V rows, 1 KiB each)
+  auto issue = [&](int st, int32_t pl) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int tok = 4 * wave + j;
+      const int32_t p = __builtin_amdgcn_readfirstlane(__shfl(pl, tok, 64));
+      if (p >= 0) {
+        char* sb = lds3 + st * kStage3;
+        g2lds16(kbase + (int64_t)p * 1024 + 16 * lane, sb + tok * kKRow3);
+        g2lds16(vbase + (int64_t)p * 1024 + 16 * lane, sb + kT3 * kKRow3 + tok * kVRow3);
+      }
+    }
+  };
+
+  bf16x8 qf[4];
+  {
+    const bool ok = r16 < a.G;
+    const uint16_t* qrow = a.q + (row * a.Hq + (int64_t)kvh * a.G + (ok ? r16 : 0)) * kHeadDim + 32 * u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint4 w = ok ? reinterpret_cast<const uint4*>(qrow)[j] : make_uint4(0, 0, 0, 0);
+      qf[j] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+  f32x4 o[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { m[i] = -__builtin_inff(); l[i] = 0.f; }
+
+  int32_t pl_cur = load_pos(0), pl_nxt = load_pos(kT3);
+  if (n > 0) issue(0, pl_cur);
+  int st = 0;
+  for (int t = 0; t < n; t += kT3, st ^= 1) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's loads of tile t landed
+    __syncthreads();                      // everyone's loads landed; stage st^1 is free
+    int32_t pl_nn = -1;
+    if (t + kT3 < n) {
+      issue(st ^ 1, pl_nxt);
+      pl_nn = load_pos(t + 2 * kT3);
+    }
+    const char* kst = lds3 + st * kStage3;
+    const char* vst = kst + kT3 * kKRow3;
+    // S = Q K^T: key column r16, dims [32u + 8j, +8) from K row r16, head kvh
+    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+    {
+      const uint4* kr = reinterpret_cast<const uint4*>(kst + r16 * kKRow3 + kvh * 256 + 64 * u);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[j], __builtin_bit_cast(bf16x8, kr[j]), sacc, 0, 0, 0);
+    }
+    const bool valid = __shfl(pl_cur, r16, 64) >= 0;
+    float pv[4], alpha[4];
+    bool grew = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float x = valid ? sacc[i] * a.scale_log2 : -__builtin_inff();
+      const float mx = row16_max(x);
+      const float mn = fmaxf(m[i], mx);
+      const bool empty = mn == -__builtin_inff();
+      grew |= mn > m[i];
+      alpha[i] = empty ? 1.f : __builtin_amdgcn_exp2f(m[i] - mn);
+      pv[i] = empty ? 0.f : __builtin_amdgcn_exp2f(x - mn);
+      l[i] = l[i] * alpha[i] + row16_sum(pv[i]);
+      m[i] = mn;
+    }
+    if (__ballot(grew)) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[j][i] *= alpha[i];
+    }
+    {
+      uint2 w2;
+      w2.x = (uint32_t)f32_to_bf16_rne(pv[0]) | ((uint32_t)f32_to_bf16_rne(pv[1]) << 16);
+      w2.y = (uint32_t)f32_to_bf16_rne(pv[2]) | ((uint32_t)f32_to_bf16_rne(pv[3]) << 16);
+      *reinterpret_cast<uint2*>(ps + r16 * 16 + 4 * u) = w2;   // P[key r16][heads 4u..4u+3]
+    }
+    wave_fence();
+    // O += P V with 16x16x16 MFMAs: A = P (head r16, keys 4u..4u+3), B = V
+    // (dim 16j + r16, keys 4u..4u+3); source lane s points at key 4u + (s >> 2)
+    const int sk = 4 * u + (r16 >> 2), sc = 4 * (r16 & 3);
+    const v4s_t pa4 = __builtin_bit_cast(v4s_t, ds_read_tr16(ps + sk * 16 + sc));
+    const uint16_t* vrow = reinterpret_cast<const uint16_t*>(vst + sk * kVRow3 + kvh * 256) + sc;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const v4s_t vb4 = __builtin_bit_cast(v4s_t, ds_read_tr16(vrow + 16 * j));
+      o[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa4, vb4, o[j], 0, 0, 0);
+    }
+    wave_fence();
+    pl_cur = pl_nxt;
+    pl_nxt = pl_nn;
+  }
+  // write: rows 4u + i < G, dims 16j + r16
+  if (a.splits == 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int hr = 4 * u + i;
+      if (hr < a.G) {
+        const float inv = l[i] > 0.f ? 1.f / l[i] : 0.f;
+        uint16_t* orow = a.out + (row * a.Hq + (int64_t)kvh * a.G + hr) * kHeadDim;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) orow[16 * j + r16] = f32_to_bf16_rne(o[j][i] * inv);
+      }
+    }
+  } else {
+    const int64_t slot = row * a.splits + split;
+    float* ob = a.ws;
+    float* mb = a.ws + a.rows * a.splits * a.Hq * kHeadDim;
+    float* lb = mb + a.rows * a.splits * a.Hq;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int hr = 4 * u + i;
+      if (hr < a.G) {
+        const int64_t h = (int64_t)kvh * a.G + hr;
+        float* orow = ob + (slot * a.Hq + h) * kHeadDim;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) orow[16 * j + r16] = o[j][i];
+        if (r16 == 0) { mb[slot * a.Hq + h] = m[i] * 0.6931471805599453f; lb[slot * a.Hq + h] = l[i]; }
       }
     }
   }
@@ -358,6 +587,24 @@ hipError_t launch_attention(const void* q, const void* k, const void* v, int32_t
     a.idx = idx; a.count = count; a.out = (uint16_t*)out; a.ws = ws;
     a.rows = rows; a.Tq = Tq; a.Tmax = Tmax; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv;
     a.L = L_max; a.splits = splits; a.scale = scale;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    if (Hkv == 4) {
+      static bool attr3 = false;
+      if (!attr3) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_attn_bf16_h4),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, kLds3);
+        (void)hipGetLastError();
+        attr3 = true;
+      }
+      const int64_t grid = (rows + 7) / 8 * 8;
+      hipLaunchKernelGGL(k_attn_bf16_h4, dim3((unsigned)grid, (unsigned)splits), dim3(256),
+                         (size_t)kLds3, s, a);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess || splits == 1) return e;
+      hipLaunchKernelGGL(k_attn_combine<LSA_BF16>, dim3((unsigned)(rows * Hq)), dim3(kHeadDim), 0,
+                         s, ws, out, rows, Hq, splits);
+      return hipGetLastError();
+    }
     const int nw = Hkv < kMaxWaves ? Hkv : kMaxWaves;
     static bool attr_set = false;
     if (!attr_set) {
@@ -368,7 +615,8 @@ hipError_t launch_attention(const void* q, const void* k, const void* v, int32_t
     }
     const int per = (L_max + splits - 1) / splits;
     const size_t smem = (size_t)nw * kWaveLds * sizeof(uint16_t) + (size_t)per * sizeof(int32_t);
-    hipLaunchKernelGGL(k_attn_bf16, dim3((unsigned)rows, (unsigned)splits), dim3(64 * nw), smem, s, a);
+    const int64_t grid = (rows + 7) / 8 * 8;
+    hipLaunchKernelGGL(k_attn_bf16, dim3((unsigned)grid, (unsigned)splits), dim3(64 * nw), smem, s, a);
   } else {
     AttnArgsF32 a;
     a.q = (const float*)q; a.k = (const float*)k; a.v = (const float*)v;
