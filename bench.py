@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--decode", action="store_true",
+                    help="time decode steps (cfg 3: 16 sequences at 1M; cfg 5: one at 10M)")
+    ap.add_argument("--splits", type=int, default=16, help="decode attention splits")
     return ap.parse_args()
 
 
@@ -88,6 +91,111 @@ def cpu_baseline(w, X, Y, budget_s: float):
                        f"{w.Tq} queries; one thread")
 
 
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    when there is none or the kernel source changed since it was taken."""
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(root, "profiles", f"{kernel}.{workload}.traffic.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(("#", "|", " ")):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    try:
+        src = open(os.path.join(root, fields["kernel_source"]), "rb").read()
+        if hashlib.sha256(src).hexdigest()[:16] != fields["kernel_source_sha256_16"]:
+            return None
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, OSError, ValueError):
+        return None
+
+
+def bench_decode(args, w, dev):
+    """Batched decode: every sequence holds T cached tokens; each step appends one
+    key per sequence (clustering a block when it fills), builds the index lists
+    and runs split attention.  512 consecutive steps: 511 steady steps and one
+    block-completing step."""
+    import torch
+
+    import lsa_synth as S
+    import sparse_attention_indexing_amd as lsa
+    B = w.batch if args.cfg == 3 else 1
+    T, n_steps = w.T, 512
+    Tmax = T + n_steps
+    mode = lsa.LSA_TREE if args.mode == "tree" else lsa.LSA_FLAT
+    p = lsa.Params(k=w.k, n_sink=w.n_sink, window=w.window, mode=mode, beam=w.beam)
+    L = lsa.list_len(p)
+    caches, keys_new, queries = [], [], []
+    t_gen = time.perf_counter()
+    for b in range(B):
+        X, Y, _ = S.latent_inputs(w, seq=b, T=Tmax, query_rows=(T, Tmax))
+        c = lsa.BucketCache(p, Tmax)
+        c.build(torch.from_numpy(X[:T]).to(dev))
+        caches.append(c)
+        keys_new.append(X[T:Tmax])
+        queries.append(Y)
+        del X
+    torch.cuda.synchronize()
+    log(f"{B} caches of {T} tokens built ({time.perf_counter() - t_gen:.1f}s with input generation)")
+    kn = torch.from_numpy(np.stack(keys_new, axis=1).copy()).to(dev)      # [steps, B, 64]
+    qn = torch.from_numpy(np.stack(queries, axis=1).copy()).to(dev)
+    tdt = torch.bfloat16
+    Kc = torch.empty((B, Tmax, w.Hkv, w.D), dtype=tdt, device=dev)
+    Vc = torch.empty_like(Kc)
+    Qd = torch.empty((n_steps, B, 1, w.Hq, w.D), dtype=tdt, device=dev)
+    cs = torch.cuda.current_stream().cuda_stream
+    for b in range(B):
+        S.device_fill_normal(Kc[b].data_ptr(), Kc[b].numel(), S.philox_key(w.cfg, "k", b), 0, True, cs)
+        S.device_fill_normal(Vc[b].data_ptr(), Vc[b].numel(), S.philox_key(w.cfg, "v", b), 0, True, cs)
+    qsrc = torch.empty((n_steps, w.Hq * w.D), dtype=tdt, device=dev)
+    for b in range(B):
+        S.device_fill_normal(qsrc.data_ptr(), qsrc.numel(), S.philox_key(w.cfg, "q", b),
+                             T * w.Hq * w.D, True, cs)
+        Qd[:, b, 0] = qsrc.view(n_steps, w.Hq, w.D)
+    idx = torch.empty((B, L), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B,), dtype=torch.int32, device=dev)
+    ws = torch.empty(lsa.index_workspace_bytes(p, B), dtype=torch.uint8, device=dev)
+    wsa = torch.empty(max(lsa.lib().lsa_attention_workspace_bytes(B, 1, w.Hq, w.D, args.splits), 1),
+                      dtype=torch.uint8, device=dev)
+    out = torch.empty((B, 1, w.Hq, w.D), dtype=tdt, device=dev)
+    torch.cuda.synchronize()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    marks = []
+    for s_ in range(n_steps):
+        e0, e1, e2 = ev(), ev(), ev()
+        e0.record()
+        lsa.index_decode(caches, qn[s_], kn[s_], p, workspace=ws, out=(idx, cnt))
+        e1.record()
+        lsa.sparse_attention(Qd[s_], Kc, Vc, idx.view(B, 1, L), cnt.view(B, 1), splits=args.splits,
+                             out=out, workspace=wsa)
+        e2.record()
+        marks.append((e0, e1, e2))
+    torch.cuda.synchronize()
+    tim = np.array([[a.elapsed_time(b_), b_.elapsed_time(c_)] for a, b_, c_ in marks]) * 1e3
+    fire = [i for i in range(n_steps) if (T + i + 1) % 512 == 0]
+    steady = [i for i in range(8, n_steps) if i not in fire]
+    st = tim[steady]
+    tot_steady = float(np.median(st.sum(axis=1)))
+    res = {
+        "metric": f"decode us/token ({args.mode})", "value": round(tot_steady, 2), "unit": "us/token",
+        "n_gpus": 1, "steps": len(steady), "warmup": 8, "ms_per_step": round(tot_steady / 1e3, 5),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name if args.cfg == 3 else "decode_t10m_b1_bf16", "T": T,
+                   "batch": B, "k": w.k, "mode": args.mode, "attention_splits": args.splits,
+                   "parallelism": "none"},
+        "stages_us": {"index_decode": round(float(np.median(st[:, 0])), 2),
+                      "attention": round(float(np.median(st[:, 1])), 2)},
+        "firing_step_us": {"index_decode": round(float(tim[fire[0], 0]), 2),
+                           "attention": round(float(tim[fire[0], 1]), 2)} if fire else None,
+        "per_sequence_step_us": round(tot_steady / B, 3),
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -100,10 +208,12 @@ def main():
     import sparse_attention_indexing_amd as lsa
 
     w = S.WORKLOADS[args.cfg]
-    if w.batch != 1:
-        raise SystemExit("bench.py times prefill workloads (cfg 1, 2, 4, 5)")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.decode:
+        return bench_decode(args, w, dev)
+    if w.batch != 1:
+        raise SystemExit("prefill timing needs a single-sequence workload (cfg 1, 2, 4, 5)")
     t_gen = time.perf_counter()
     X, Y, _ = S.latent_inputs(w)
     Xd = torch.from_numpy(X).to(dev)
@@ -141,11 +251,30 @@ def main():
 
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
+    full_prefill = w.q_start == 0
+    prebuilt = None
+    build_once_ms = None
+    if not full_prefill:
+        # last prefill chunk of a long context: the cache of every full block
+        # exists before the chunk; building it is timed once, separately
+        prebuilt = _Cache()
+        b0, b1 = ev(), ev()
+        b0.record()
+        prebuilt.build(Xd)
+        b1.record()
+        torch.cuda.synchronize()
+        build_once_ms = b0.elapsed_time(b1)
+        log(f"cache for {w.T // 512} blocks built in {build_once_ms:.2f} ms")
+
     def step(times=None):
         e0, e1, e2, e3 = ev(), ev(), ev(), ev()
-        c = _Cache()
-        e0.record()
-        c.build(Xd)
+        if full_prefill:
+            c = _Cache()
+            e0.record()
+            c.build(Xd)
+        else:
+            c = prebuilt
+            e0.record()
         e1.record()
         lsa.index_prefill(c, Yd, w.q_start, p, workspace=ws, out=(idx, cnt))
         e2.record()
@@ -187,13 +316,18 @@ def main():
     # algorithmic FLOPs of flat scoring: 2 * 64 per eligible (query, bucket) pair
     pos = np.arange(w.q_start, w.T, dtype=np.int64)
     pairs = int((64 * (pos // 512)).sum())
+    kname = ("k_attn_bf16_h4" if w.Hkv == 4 else "k_attn_bf16") if w.dtype == "bf16" else "k_attn_f32"
+    traffic = measured_traffic(kname, w.name)
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
-                    kernel="k_attn_bf16" if w.dtype == "bf16" else "k_attn_f32",
-                    algorithmic_bytes=attn_bytes, kernel_ms=round(float(t_attn), 4))
+                    frac=round(achieved / HBM_PEAK_GBS, 4),
+                    traffic=None if traffic is None else round(traffic),
+                    kernel=kname, algorithmic_bytes=attn_bytes, kernel_ms=round(float(t_attn), 4))
+    if traffic is not None:
+        roofline["traffic_gbs"] = round(traffic / (t_attn * 1e-3) / 1e9, 1)
+        roofline["traffic_frac"] = round(traffic / (t_attn * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
     value = w.Tq / (ms_step * 1e-3)
     res = {
-        "metric": "prefill query tok/s per layer", "value": round(value, 1),
+        "metric": f"prefill query tok/s per layer ({args.mode})", "value": round(value, 1),
         "unit": "query tok/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
@@ -202,10 +336,14 @@ def main():
                    "window": w.window, "latent_components": w.n_comp, "parallelism": "none"},
         "stages_ms": {"build": round(float(t_build), 4), "index": round(float(t_index), 4),
                       "attention": round(float(t_attn), 4)},
+        "step": ("build + index + attention" if full_prefill else
+                 "index + attention for the last chunk (cache built before timing)"),
         "scoring": {"pairs": pairs, "algorithmic_tflop": round(pairs * 128 / 1e12, 4)},
         "roofline": roofline,
     }
-    if not args.no_cpu_baseline:
+    if build_once_ms is not None:
+        res["cache_build_ms"] = round(build_once_ms, 3)
+    if not args.no_cpu_baseline and w.T <= 1 << 17:
         log("timing the CPU oracle on a sample ...")
         cb = cpu_baseline(w, X, Y, args.cpu_seconds)
         res["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}

@@ -37,10 +37,8 @@ __device__ __forceinline__ uint16_t to_bf16(double x) {
   return (uint16_t)(__float_as_uint(f) >> 16);
 }
 
-__global__ void k_fill_normal(void* out, int64_t n, int64_t off, uint32_t k0, uint32_t k1,
-                              int is_bf16) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n) return;
+__device__ __forceinline__ void fill_one(void* out, int64_t i, int64_t off, uint32_t k0, uint32_t k1,
+                                         int is_bf16) {
   const uint64_t e = (uint64_t)(off + i);
   const uint64_t m = e >> 2;
   const int slot = (int)(e & 3);
@@ -57,12 +55,22 @@ __global__ void k_fill_normal(void* out, int64_t n, int64_t off, uint32_t k0, ui
   else reinterpret_cast<float*>(out)[i] = (float)z;
 }
 
+// Grid-stride loop: a dispatch's total work-item count must stay below 2^32,
+// and the 10M-token K/V tensors have 5.12e9 elements.
+__global__ void k_fill_normal(void* out, int64_t n, int64_t off, uint32_t k0, uint32_t k1,
+                              int is_bf16) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+    fill_one(out, i, off, k0, k1, is_bf16);
+}
+
 }  // namespace
 
 extern "C" int synth_fill_normal(void* ptr, int64_t n, int64_t elem_offset, uint32_t k0,
                                  uint32_t k1, int is_bf16, void* stream) {
   if (n <= 0) return 0;
-  const int64_t blocks = (n + 255) / 256;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 262144) blocks = 262144;
   hipLaunchKernelGGL(k_fill_normal, dim3((unsigned)blocks), dim3(256), 0,
                      reinterpret_cast<hipStream_t>(stream), ptr, n, elem_offset, k0, k1, is_bf16);
   return (int)hipGetLastError();

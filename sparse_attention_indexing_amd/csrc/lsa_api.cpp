@@ -173,7 +173,7 @@ int append_keys(CacheState& c, const float* keys, int64_t n, hipStream_t s) {
 }
 
 struct WsLayout {
-  int64_t off_yhat, off_tau, off_cnt, off_status, off_cand, total;
+  int64_t off_yhat, off_tau, off_cnt, off_status, off_hist, off_cand, total;
 };
 
 WsLayout index_ws_layout(const lsa_params* p, int64_t nq) {
@@ -187,6 +187,8 @@ WsLayout index_ws_layout(const lsa_params* p, int64_t nq) {
   off = align_up(off + nq * 4);
   w.off_status = off;
   off = align_up(off + nq * 4);
+  w.off_hist = off;
+  off = align_up(off + nq * 256 * 4);
   w.off_cand = off;
   off = align_up(off + nq * (int64_t)cand_cap(p) * 8);
   w.total = off;
@@ -201,6 +203,7 @@ IndexWs make_ws(void* base, const WsLayout& w) {
   ws.cand_cnt = reinterpret_cast<int32_t*>(b + w.off_cnt);
   ws.status = reinterpret_cast<int32_t*>(b + w.off_status);
   ws.cand = reinterpret_cast<uint2*>(b + w.off_cand);
+  ws.hist = reinterpret_cast<uint32_t*>(b + w.off_hist);
   return ws;
 }
 
@@ -417,7 +420,7 @@ int lsa_index_prefill(const lsa_cache* c, const float* latent_q, int64_t q_start
   ctx.per_seq = 0;
   ctx.cent[0] = lvl_cent(st, 0);
   ctx.members[0] = reinterpret_cast<const uint32_t*>(st.base + st.lay.off_members);
-  hipError_t e = launch_qnorm(latent_q, Tq, ws.yhat, p->index_dtype, s);
+  hipError_t e = launch_qnorm(latent_q, Tq, ws.yhat, p->index_dtype, nullptr, s);
   if (e != hipSuccess) return LSA_ERR_HIP;
   const int64_t max_elig = (last / kBlock) * kBuckets;
   TreeCtx tc;
@@ -456,7 +459,7 @@ int lsa_index_decode(lsa_cache* const* caches, int32_t B, const float* latent_q,
     if (rc) return rc;
   }
   IndexWs ws = make_ws(workspace, wl);
-  hipError_t e = launch_qnorm(latent_q, B, ws.yhat, p->index_dtype, s);
+  hipError_t e = launch_qnorm(latent_q, B, ws.yhat, p->index_dtype, ws.hist, s);
   if (e != hipSuccess) return LSA_ERR_HIP;
   const int L = p->n_sink + p->window + p->k;
   if (tree) {
@@ -471,6 +474,7 @@ int lsa_index_decode(lsa_cache* const* caches, int32_t B, const float* latent_q,
       IndexWs wsb = ws;
       wsb.yhat = reinterpret_cast<char*>(ws.yhat) + (int64_t)b * kLatent * idx_elem_bytes(p->index_dtype);
       wsb.tau += b; wsb.cand_cnt += b; wsb.status += b;
+      wsb.hist += (int64_t)b * 256;
       wsb.cand += (int64_t)b * ctx.cap;
       const int64_t max_elig = (ctx.pos[0] / kBlock) * kBuckets;
       TreeCtx tc;
@@ -500,6 +504,7 @@ int lsa_index_decode(lsa_cache* const* caches, int32_t B, const float* latent_q,
     IndexWs wsb = ws;
     wsb.yhat = reinterpret_cast<char*>(ws.yhat) + (int64_t)b0 * kLatent * idx_elem_bytes(p->index_dtype);
     wsb.tau += b0; wsb.cand_cnt += b0; wsb.status += b0;
+    wsb.hist += (int64_t)b0 * 256;
     wsb.cand += (int64_t)b0 * ctx.cap;
     rc = run_selection(ctx, wsb, p, nullptr, max_elig, idx + (int64_t)b0 * L, count + b0, nullptr, s);
     if (rc) return rc;

@@ -67,9 +67,13 @@ __device__ __forceinline__ int64_t mfma_query(const IndexCtx& c, int64_t qt, int
 // 16 lanes per query, 4 dims each; fp64 norm, rounded to the index dtype.
 template <int DT>
 __global__ __launch_bounds__(256) void k_qnorm(const float* __restrict__ y, int64_t n,
-                                               void* __restrict__ yhat) {
+                                               void* __restrict__ yhat, uint32_t* hist) {
   const int64_t i = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
   const int l = threadIdx.x & 15;
+  if (hist && i < n) {       // clear this query's histogram (decode threshold)
+#pragma unroll
+    for (int b = 0; b < 16; ++b) hist[i * 256 + 16 * l + b] = 0u;
+  }
   float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
   if (i < n) x = reinterpret_cast<const float4*>(y + i * kLatent)[l];
   double ss = (double)x.x * x.x;
@@ -214,6 +218,69 @@ __global__ __launch_bounds__(256) void k_thresh(IndexCtx ctx, IndexWs ws) {
       ws.status[qj] = 0;
     }
   }
+}
+
+// Decode: the sampled histogram of one query is spread over many workgroups
+// (grid.x = sample segments, grid.y = query tiles of 4, one query per wave)
+// and accumulated in global memory; k_thresh_tau turns it into tau.
+constexpr int kHistSegTiles = 8;   // sampled tiles per workgroup
+
+template <int DT>
+__global__ __launch_bounds__(256) void k_thresh_hist(IndexCtx ctx, IndexWs ws) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const int64_t qi = mfma_query(ctx, blockIdx.y, wave, col);
+  const bool valid = qi >= 0 && qi < ctx.n;
+  const int64_t ne = valid ? n_eligible(qpos(ctx, qi)) : 0;
+  int64_t wmax = ne;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    int64_t o = __shfl_xor(wmax, off, 64);
+    wmax = o > wmax ? o : wmax;
+  }
+  const int64_t n_tiles = wmax / kTile;
+  const int64_t s0 = (int64_t)blockIdx.x * kHistSegTiles * kSampleStride;
+  if (s0 >= n_tiles || ne <= ctx.cap) {
+    if (__ballot(s0 < n_tiles && ne > ctx.cap) == 0) return;
+  }
+  QFrag qf;
+  load_qfrag<DT>(qf, ws.yhat, valid ? qi : 0, valid, half);
+  const int64_t wq = mfma_query(ctx, blockIdx.y, wave, 0);
+  const void* cent = qcent(ctx, wq < ctx.n ? wq : 0);
+  uint32_t* h = ws.hist + (valid ? qi : 0) * 256;
+  for (int64_t t = s0; t < n_tiles && t < s0 + kHistSegTiles * kSampleStride; t += kSampleStride) {
+    f32x16 acc = score_tile<DT>(cent, t * kTile + col, half, qf);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t g = t * kTile + tile_row(r, lane);
+      if (g < ne && ne > ctx.cap) {
+        int bin = (int)__builtin_floorf((acc[r] + 1.0f) * (kBins / 2));
+        bin = bin < 0 ? 0 : (bin >= kBins ? kBins - 1 : bin);
+        atomicAdd(&h[bin], 1u);
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(64) void k_thresh_tau(IndexCtx ctx, IndexWs ws) {
+  const int64_t qj = (int64_t)blockIdx.x * 64 + threadIdx.x;
+  if (qj >= ctx.n) return;
+  const int64_t nej = n_eligible(qpos(ctx, qj));
+  float tau = -3.0e38f;
+  if (nej > ctx.cap) {
+    const int64_t ntl = nej / kTile;
+    const int64_t nsamp = (ntl + kSampleStride - 1) / kSampleStride;
+    const int64_t want = (2 * (int64_t)ctx.top_b * nsamp + ntl - 1) / ntl;
+    const uint32_t* h = ws.hist + qj * 256;
+    int64_t cum = 0;
+    for (int b = kBins - 1; b >= 0; --b) {
+      cum += h[b];
+      if (cum >= want) { tau = (float)b / (kBins / 2) - 1.0f; break; }
+    }
+  }
+  ws.tau[qj] = tau;
+  ws.cand_cnt[qj] = 0;
+  ws.status[qj] = 0;
 }
 
 // ------------------------------------------------------------------ score + filter
@@ -778,11 +845,12 @@ __global__ __launch_bounds__(256) void k_select_expand(IndexCtx ctx, IndexWs ws,
 
 // ------------------------------------------------------------------ launchers
 
-hipError_t launch_qnorm(const float* y, int64_t n, void* yhat, int dtype, hipStream_t s) {
+hipError_t launch_qnorm(const float* y, int64_t n, void* yhat, int dtype, uint32_t* hist,
+                        hipStream_t s) {
   if (n <= 0) return hipSuccess;
   dim3 grid((unsigned)((n + 15) / 16));
-  if (dtype == LSA_BF16) hipLaunchKernelGGL(k_qnorm<LSA_BF16>, grid, dim3(256), 0, s, y, n, yhat);
-  else hipLaunchKernelGGL(k_qnorm<LSA_F32>, grid, dim3(256), 0, s, y, n, yhat);
+  if (dtype == LSA_BF16) hipLaunchKernelGGL(k_qnorm<LSA_BF16>, grid, dim3(256), 0, s, y, n, yhat, hist);
+  else hipLaunchKernelGGL(k_qnorm<LSA_F32>, grid, dim3(256), 0, s, y, n, yhat, hist);
   return hipGetLastError();
 }
 
@@ -792,6 +860,25 @@ static int64_t query_tiles(const IndexCtx& ctx) {
 
 hipError_t launch_thresh(const IndexCtx& ctx, const IndexWs& ws, int dtype, hipStream_t s) {
   if (ctx.n <= 0) return hipSuccess;
+  if (ctx.per_seq) {
+    // decode: many workgroups per query, global histogram, then tau
+    int64_t max_tiles = 0;
+    for (int64_t i = 0; i < ctx.n; ++i) {
+      const int64_t t = (ctx.pos[i] / kBlock) * kBuckets / kTile;
+      max_tiles = t > max_tiles ? t : max_tiles;
+    }
+    const int64_t per_wg = (int64_t)kHistSegTiles * kSampleStride;
+    const int64_t gx = (max_tiles + per_wg - 1) / per_wg;
+    if (gx > 0) {
+      dim3 grid((unsigned)gx, (unsigned)query_tiles(ctx));
+      if (dtype == LSA_BF16) hipLaunchKernelGGL(k_thresh_hist<LSA_BF16>, grid, dim3(256), 0, s, ctx, ws);
+      else hipLaunchKernelGGL(k_thresh_hist<LSA_F32>, grid, dim3(256), 0, s, ctx, ws);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(k_thresh_tau, dim3((unsigned)((ctx.n + 63) / 64)), dim3(64), 0, s, ctx, ws);
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)query_tiles(ctx));
   if (dtype == LSA_BF16) hipLaunchKernelGGL(k_thresh<LSA_BF16>, grid, dim3(256), 0, s, ctx, ws);
   else hipLaunchKernelGGL(k_thresh<LSA_F32>, grid, dim3(256), 0, s, ctx, ws);

@@ -123,6 +123,7 @@ struct IndexWs {
   int32_t* cand_cnt;   // [n]
   uint2* cand;         // [n, cap] (score bits, bucket)
   int32_t* status;     // [n] 1 if the exact path was used
+  uint32_t* hist;      // [n, 256] sampled-score histogram (decode)
 };
 
 // ---------------------------------------------------------------- launchers
@@ -136,7 +137,8 @@ hipError_t launch_tree_groups(const void* child_cent, const int32_t* child_minb,
                               hipStream_t s);
 hipError_t launch_copy_rows(float* dst, const float* src, int64_t n, hipStream_t s);
 
-hipError_t launch_qnorm(const float* y, int64_t n, void* yhat, int dtype, hipStream_t s);
+hipError_t launch_qnorm(const float* y, int64_t n, void* yhat, int dtype, uint32_t* hist,
+                        hipStream_t s);
 hipError_t launch_thresh(const IndexCtx& ctx, const IndexWs& ws, int dtype, hipStream_t s);
 hipError_t launch_score_filter(const IndexCtx& ctx, const IndexWs& ws, int dtype,
                                int64_t max_tiles, hipStream_t s);

@@ -2,6 +2,9 @@
 seeded inputs and compare them (the oracle never sees a GPU result)."""
 from __future__ import annotations
 
+import multiprocessing as mp
+import os
+
 import numpy as np
 import torch
 
@@ -107,3 +110,66 @@ def compare_lists(idx: np.ndarray, cnt: np.ndarray, positions, ys, oc: O.BucketC
 
 def bf16_tensor(bits: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16)
+
+
+# ---------------------------------------------------------------- parallel oracle build
+_PX = None
+_PPRM = None
+
+
+def _build_part(blocks):
+    c = O.build_cache(_PX, _PPRM, blocks=blocks)
+    M = _PPRM.n_buckets
+    sel = np.concatenate([np.arange(b * M, (b + 1) * M) for b in blocks])
+    return (blocks, c.centroids[sel], [c.members[g] for g in sel], [c.pooled[g] for g in sel],
+            c.block_min_gap[blocks], c.block_ess[blocks])
+
+
+def oracle_cache_parallel(X: np.ndarray, prm: O.Params, procs: int = 8) -> O.BucketCache:
+    """The oracle's build_cache over all full blocks, blocks split across forked
+    worker processes (numpy only; no GPU use in the workers)."""
+    global _PX, _PPRM
+    nb = X.shape[0] // prm.block
+    if nb <= 64:
+        return O.build_cache(X, prm)
+    _PX, _PPRM = X, prm
+    chunks = [c for c in np.array_split(np.arange(nb), procs * 8) if len(c)]
+    with mp.get_context("fork").Pool(procs) as pool:
+        parts = pool.map(_build_part, chunks)
+    M = prm.n_buckets
+    cent = np.full((nb * M, prm.d_latent), np.nan)
+    members, pooled = [None] * (nb * M), [None] * (nb * M)
+    gaps, ess = np.full(nb, np.inf), np.zeros(nb)
+    for blocks, ce, me, po, ga, es in parts:
+        sel = np.concatenate([np.arange(b * M, (b + 1) * M) for b in blocks])
+        cent[sel] = ce
+        for g, m, q in zip(sel, me, po):
+            members[g], pooled[g] = m, q
+        gaps[blocks], ess[blocks] = ga, es
+    _PX = None
+    return O.BucketCache(prm, nb, cent, members, pooled, gaps, ess)
+
+
+def device_normal(w, tensor: str, shape, seq: int = 0, row0: int = 0):
+    """A Q/K/V tensor generated on the GPU (same Philox definition as the host rows)."""
+    import torch
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    t = torch.empty(shape, dtype=dt, device="cuda")
+    width = int(np.prod(shape[1:]))
+    S.device_fill_normal(t.data_ptr(), t.numel(), S.philox_key(w.cfg, tensor, seq), row0 * width,
+                         w.dtype == "bf16", torch.cuda.current_stream().cuda_stream)
+    return t
+
+
+def host_rows(w, tensor: str, rows, width: int, seq: int = 0):
+    """Rows of a Q/K/V tensor from the host generator, as float64."""
+    vals, _ = S.normal_rows(w, tensor, np.asarray(rows), width, seq)
+    return vals.astype(np.float64)
+
+
+def attention_from_rows(w, q_row: np.ndarray, idx: np.ndarray, count: int, seq: int = 0):
+    """Oracle attention of one query whose K/V rows come from the host generator."""
+    sel = np.asarray(idx[:count], np.int64)
+    k = host_rows(w, "k", sel, w.Hkv * w.D, seq).reshape(-1, w.Hkv, w.D)
+    v = host_rows(w, "v", sel, w.Hkv * w.D, seq).reshape(-1, w.Hkv, w.D)
+    return O.attention_query(q_row.reshape(w.Hq, w.D), k, v, np.arange(len(sel)), len(sel))

@@ -1,0 +1,167 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times.  The oracle builds every block (in forked worker processes)
+and recomputes sampled queries one by one; Q/K/V rows it needs come from the
+host generator while the GPU gets the same tensors from the device generator."""
+import sys
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import lsa_synth as S
+import sparse_attention_indexing_amd as lsa
+from oracle import lsa_oracle as O
+from parity_util import (attention_from_rows, cache_to_host, compare_cache, compare_lists,
+                         device_normal, gpu_cache, host_rows, oracle_cache_parallel,
+                         oracle_params)
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    lsa.lib()
+
+
+def _attn_check(w, q_dev_rows, out, idx, cnt, rows, seq=0, label=""):
+    err = 0.0
+    for i, r in enumerate(rows):
+        ref = attention_from_rows(w, q_dev_rows[i], idx[r], int(cnt[r]), seq)
+        err = max(err, float(np.abs(out[r].astype(np.float64) - ref).max()))
+    say(f"{label} attention max abs err {err:.3g} over {len(rows)} queries")
+    assert err <= 2e-2
+
+
+def test_prefill_128k_full_size():
+    say("case: prefill T=131072 flat (benchmark workload)")
+    w = S.WORKLOADS[2]
+    X, Y, _ = S.latent_inputs(w)
+    p = lsa.Params(k=w.k)
+    c = gpu_cache(X, p)
+    Yd = torch.from_numpy(Y).cuda()
+    idx, cnt = lsa.index_prefill(c, Yd, w.q_start, p)
+    Q = device_normal(w, "q", (w.Tq, w.Hq, w.D))
+    K = device_normal(w, "k", (w.T, w.Hkv, w.D))
+    V = device_normal(w, "v", (w.T, w.Hkv, w.D))
+    out = lsa.sparse_attention(Q, K, V, idx, cnt)
+    torch.cuda.synchronize()
+    oc = oracle_cache_parallel(X, oracle_params(p))
+    say("build", compare_cache(cache_to_host(c), oc, X))
+    idx_h, cnt_h = idx.cpu().numpy(), cnt.cpu().numpy()
+    rows = np.unique(np.concatenate([np.linspace(0, w.Tq - 1, 96).astype(int), np.arange(w.Tq - 16, w.Tq)]))
+    say("index", compare_lists(idx_h[rows], cnt_h[rows], rows, Y[rows], oc))
+    arows = rows[::8]
+    q_rows = host_rows(w, "q", arows, w.Hq * w.D)
+    _attn_check(w, q_rows, out.float().cpu().numpy(), idx_h, cnt_h, arows, label="prefill 128K")
+
+
+def test_prefill_1m_tree_and_flat():
+    say("case: T=1M last 8192 queries, tree (beam 64) and flat")
+    w = S.WORKLOADS[4]
+    X, Y, _ = S.latent_inputs(w)
+    pt = lsa.Params(k=w.k, mode=lsa.LSA_TREE, beam=w.beam)
+    pf = lsa.Params(k=w.k, mode=lsa.LSA_FLAT)
+    c = gpu_cache(X, pt)
+    Yd = torch.from_numpy(Y).cuda()
+    it, ct = lsa.index_prefill(c, Yd, w.q_start, pt)
+    i_f, c_f = lsa.index_prefill(c, Yd, w.q_start, pf)
+    torch.cuda.synchronize()
+    t0 = time.time()
+    oc = oracle_cache_parallel(X, oracle_params(pt))
+    g = cache_to_host(c)
+    say("build", compare_cache(g, oc, X), f"{time.time() - t0:.1f}s")
+    ot = O.build_tree(oc)
+    assert len(g["levels"]) == ot.height == 17
+    if min(ot.group_min_gap) > 1e-12:
+        for l, lv in enumerate(g["levels"], start=1):
+            assert np.array_equal(lv["child"], ot.levels[l]["child"]), f"level {l} children"
+            assert np.array_equal(lv["min_block"], ot.levels[l]["min_block"]), f"level {l}"
+            assert np.array_equal(lv["cent"], ot.levels[l]["cent"]), f"level {l} centroids"
+    rows = np.linspace(0, w.Tq - 1, 24).astype(int)
+    it_h, ct_h, if_h, cf_h = it.cpu().numpy(), ct.cpu().numpy(), i_f.cpu().numpy(), c_f.cpu().numpy()
+    say("tree index", compare_lists(it_h[rows], ct_h[rows], w.q_start + rows, Y[rows], oc, "tree", ot))
+    say("flat index", compare_lists(if_h[rows], cf_h[rows], w.q_start + rows, Y[rows], oc))
+    # tree vs flat: share of the flat far keys the tree also finds (all queries)
+    near = 4 + 512
+    rec = []
+    for r in range(0, w.Tq, 64):
+        a = set(if_h[r, :cf_h[r]].tolist())
+        b = set(it_h[r, :ct_h[r]].tolist())
+        rec.append((len(a & b) - near) / max(1, len(a) - near))
+    say(f"tree/flat far-key recall: mean {np.mean(rec):.3f} min {np.min(rec):.3f}")
+
+
+def test_decode_1m_steady_and_firing():
+    """Two sequences of the 16-sequence decode workload: one whose new key
+    completes a block (the block is clustered in the step), one steady."""
+    say("case: decode T=1M, block-completing and steady sequences")
+    w = S.WORKLOADS[3]
+    lens = [w.T - 1, w.T]
+    p = lsa.Params(k=w.k)
+    seqs = [S.latent_inputs(w, seq=b, T=n + 1, query_rows=(n, n + 1)) for b, n in enumerate(lens)]
+    caches = [gpu_cache(X[:n], p, max_tokens=n + 1) for (X, Y, _), n in zip(seqs, lens)]
+    q = torch.from_numpy(np.stack([Y[0] for (X, Y, _) in seqs])).cuda()
+    kn = torch.from_numpy(np.stack([X[n] for (X, Y, _), n in zip(seqs, lens)])).cuda()
+    idx, cnt = lsa.index_decode(caches, q, kn, p)
+    Tmax = max(lens) + 1
+    K = torch.stack([device_normal(w, "k", (Tmax, w.Hkv, w.D), seq=b) for b in range(2)])
+    V = torch.stack([device_normal(w, "v", (Tmax, w.Hkv, w.D), seq=b) for b in range(2)])
+    Q = torch.stack([device_normal(w, "q", (1, w.Hq, w.D), seq=b, row0=n) for b, n in enumerate(lens)])
+    out = lsa.sparse_attention(Q, K, V, idx.view(2, 1, -1), cnt.view(2, 1), splits=16)
+    torch.cuda.synchronize()
+    idx_h, cnt_h, out_h = idx.cpu().numpy(), cnt.cpu().numpy(), out.float().cpu().numpy()
+    for b, ((X, Y, _), n) in enumerate(zip(seqs, lens)):
+        oc = oracle_cache_parallel(X[:n + 1], oracle_params(p))
+        say(f"seq {b}", compare_lists(idx_h[b:b + 1], cnt_h[b:b + 1], [n], Y[0:1], oc))
+        if b == 0:  # the block completed by this step matches the oracle's clustering
+            g = cache_to_host(caches[0])
+            assert g["n_blocks"] == (n + 1) // 512
+            last = g["n_blocks"] - 1
+            sub = O.build_cache(X[last * 512:(last + 1) * 512], oracle_params(p))
+            gl = dict(n_blocks=1, cent=g["cent"][last * 64:], pooled=g["pooled"][last * 64:])
+            compare_cache(gl, sub, X[last * 512:(last + 1) * 512])
+        qrow = host_rows(w, "q", [n], w.Hq * w.D, seq=b)[0]
+        ref = attention_from_rows(w, qrow, idx_h[b], int(cnt_h[b]), seq=b)
+        err = float(np.abs(out_h[b, 0] - ref).max())
+        say(f"seq {b} decode attention (16 splits) max abs err {err:.3g}")
+        assert err <= 2e-2
+
+
+def test_prefill_10m_flat_last_chunk():
+    say("case: T=10M, last 32768 queries, flat")
+    w = S.WORKLOADS[5]
+    t0 = time.time()
+    X, Y, _ = S.latent_inputs(w)
+    say(f"inputs {time.time() - t0:.1f}s")
+    p = lsa.Params(k=w.k)
+    c = gpu_cache(X, p)
+    Yd = torch.from_numpy(Y).cuda()
+    idx, cnt = lsa.index_prefill(c, Yd, w.q_start, p)
+    Q = device_normal(w, "q", (w.Tq, w.Hq, w.D), row0=w.q_start)
+    K = device_normal(w, "k", (w.T, w.Hkv, w.D))
+    V = device_normal(w, "v", (w.T, w.Hkv, w.D))
+    out = lsa.sparse_attention(Q, K, V, idx, cnt)
+    torch.cuda.synchronize()
+    # the device generator fills all 5.12e9 elements like the host rows (this
+    # needs a grid-stride launch: a dispatch holds fewer than 2^32 work-items)
+    for r in [0, 2097152, 8388608, w.T - 1]:
+        assert np.array_equal(K[r].float().cpu().numpy().reshape(-1).astype(np.float64),
+                              host_rows(w, "k", [r], w.Hkv * w.D)[0]), f"K row {r}"
+    del K, V
+    t0 = time.time()
+    oc = oracle_cache_parallel(X, oracle_params(p))
+    say("build", compare_cache(cache_to_host(c), oc, X), f"oracle {time.time() - t0:.1f}s")
+    idx_h, cnt_h = idx.cpu().numpy(), cnt.cpu().numpy()
+    rows = np.linspace(0, w.Tq - 1, 8).astype(int)
+    say("index", compare_lists(idx_h[rows], cnt_h[rows], w.q_start + rows, Y[rows], oc))
+    arows = rows[::2]
+    q_rows = host_rows(w, "q", w.q_start + arows, w.Hq * w.D)
+    _attn_check(w, q_rows, out.float().cpu().numpy(), idx_h, cnt_h, arows, label="prefill 10M")
