@@ -435,7 +435,7 @@ int lsa_index_prefill(const lsa_cache* c, const float* latent_q, int64_t q_start
 int lsa_index_decode(lsa_cache* const* caches, int32_t B, const float* latent_q,
                      const float* latent_k_new, const lsa_params* p, int32_t* idx,
                      int32_t* count, void* workspace, int64_t ws_bytes, void* stream) {
-  if (!caches || !p || B < 0 || B > 64) return LSA_ERR_ARG;
+  if (!caches || !p || B < 0 || B > kMaxDecode) return LSA_ERR_ARG;
   int rc = lsa_check_params(p);
   if (rc) return rc;
   if (B == 0) return LSA_OK;
@@ -453,10 +453,42 @@ int lsa_index_decode(lsa_cache* const* caches, int32_t B, const float* latent_q,
   const WsLayout wl = index_ws_layout(p, B);
   if (ws_bytes < wl.total) return LSA_ERR_WORKSPACE;
   hipStream_t s = as_stream(stream);
-  // append the new key of every sequence (clusters a block when it fills)
-  for (int b = 0; b < B; ++b) {
-    rc = append_keys(caches[b]->st, latent_k_new + (int64_t)b * kLatent, 1, s);
-    if (rc) return rc;
+  // append the new key of every sequence (one launch), then cluster every
+  // block that this key completed (one launch), then update trees
+  {
+    AppendJobs aj;
+    WardJobs wj;
+    memset(&aj, 0, sizeof(aj));
+    memset(&wj, 0, sizeof(wj));
+    int nfire = 0;
+    for (int b = 0; b < B; ++b) {
+      CacheState& st = caches[b]->st;
+      float* stg = reinterpret_cast<float*>(st.base + st.lay.off_staging);
+      aj.dst[b] = stg + (st.n_tokens % kBlock) * kLatent;
+      if ((st.n_tokens + 1) % kBlock == 0) {
+        wj.keys[nfire] = stg;
+        wj.block[nfire] = st.n_blocks;
+        wj.cent[nfire] = st.base + st.lay.off_cent;
+        wj.members[nfire] = reinterpret_cast<uint32_t*>(st.base + st.lay.off_members);
+        ++nfire;
+      }
+    }
+    hipError_t e = launch_append_rows(latent_k_new, aj, B, s);
+    if (e != hipSuccess) return LSA_ERR_HIP;
+    e = launch_ward_jobs(wj, nfire, p->index_dtype, s);
+    if (e != hipSuccess) return LSA_ERR_HIP;
+    for (int b = 0; b < B; ++b) {
+      CacheState& st = caches[b]->st;
+      const int64_t old_blocks = st.n_blocks;
+      st.n_tokens += 1;
+      if (st.n_tokens % kBlock == 0) {
+        st.n_blocks += 1;
+        if (st.tree) {
+          rc = update_tree(st, old_blocks, s);
+          if (rc) return rc;
+        }
+      }
+    }
   }
   IndexWs ws = make_ws(workspace, wl);
   hipError_t e = launch_qnorm(latent_q, B, ws.yhat, p->index_dtype, ws.hist, s);

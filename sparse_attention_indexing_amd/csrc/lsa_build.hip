@@ -300,13 +300,9 @@ __device__ __forceinline__ void quad_unit(double* v) {
 
 // One workgroup per full block: pooled keys -> 64 buckets.
 template <int DT>
-__global__ __launch_bounds__(kThreads) void k_ward_blocks(const float* __restrict__ keys,
-                                                          int64_t first_block, void* cent,
-                                                          uint32_t* __restrict__ members) {
-  __shared__ WardLds L;
+__device__ void ward_block_body(WardLds& L, const float* __restrict__ src, int64_t blk, void* cent,
+                                uint32_t* __restrict__ members) {
   const int tid = threadIdx.x;
-  const float* src = keys + (int64_t)blockIdx.x * kBlock * kLatent;
-  const int64_t blk = first_block + blockIdx.x;
   load_pooled(L, src);
   if (tid < kN) { L.size[tid] = 1; L.label[tid] = tid; }
   __syncthreads();
@@ -344,6 +340,29 @@ __global__ __launch_bounds__(kThreads) void k_ward_blocks(const float* __restric
     quad_unit(v);
     store16<DT>(cent, blk * kBuckets + r, q, v);
   }
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_ward_blocks(const float* __restrict__ keys,
+                                                          int64_t first_block, void* cent,
+                                                          uint32_t* __restrict__ members) {
+  __shared__ WardLds L;
+  ward_block_body<DT>(L, keys + (int64_t)blockIdx.x * kBlock * kLatent, first_block + blockIdx.x,
+                      cent, members);
+}
+
+// Blocks of different caches (decode: every sequence whose new key completed a block).
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_ward_jobs(WardJobs jobs) {
+  __shared__ WardLds L;
+  const int j = blockIdx.x;
+  ward_block_body<DT>(L, jobs.keys[j], jobs.block[j], jobs.cent[j], jobs.members[j]);
+}
+
+// Append one latent key per sequence: row b of src -> dst[b].
+__global__ void k_append_rows(const float* __restrict__ src, AppendJobs jobs) {
+  const int b = blockIdx.x, d = threadIdx.x;
+  jobs.dst[b][d] = src[(int64_t)b * kLatent + d];
 }
 
 // One workgroup per group of (up to) 128 nodes of the level below: greedy
@@ -443,6 +462,21 @@ hipError_t launch_tree_groups(const void* child_cent, const int32_t* child_minb,
   else
     hipLaunchKernelGGL(k_tree_groups<LSA_F32>, dim3((unsigned)(g1 - g0)), dim3(kThreads), 0, s,
                        child_cent, child_minb, n_child, g0, cent, child, minb, child_is_bucket);
+  return hipGetLastError();
+}
+
+hipError_t launch_ward_jobs(const WardJobs& jobs, int n, int dtype, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (dtype == LSA_BF16)
+    hipLaunchKernelGGL(k_ward_jobs<LSA_BF16>, dim3((unsigned)n), dim3(kThreads), 0, s, jobs);
+  else
+    hipLaunchKernelGGL(k_ward_jobs<LSA_F32>, dim3((unsigned)n), dim3(kThreads), 0, s, jobs);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_rows(const float* src, const AppendJobs& jobs, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_append_rows, dim3((unsigned)n), dim3(kLatent), 0, s, src, jobs);
   return hipGetLastError();
 }
 

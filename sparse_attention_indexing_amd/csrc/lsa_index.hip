@@ -161,6 +161,11 @@ __device__ __forceinline__ int tile_row(int r, int lane) {
   return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 }
 
+// Threshold sample: one bucket out of every 16, at offset 7 j mod 16 inside
+// group j, so the sample covers every bucket rank of a block (ranks follow
+// the smallest member, and early and late ranks differ in size and spread).
+__device__ __forceinline__ int64_t sample_bucket(int64_t j) { return 16 * j + ((7 * j) & 15); }
+
 // ------------------------------------------------------------------ thresh
 // Histogram of sampled scores per query -> tau.  Workgroup = 128 queries.
 template <int DT>
@@ -184,13 +189,15 @@ __global__ __launch_bounds__(256) void k_thresh(IndexCtx ctx, IndexWs ws) {
   const int64_t wq = mfma_query(ctx, blockIdx.x, wave, 0);
   const void* cent = qcent(ctx, wq < ctx.n ? wq : 0);
   __syncthreads();
-  const int64_t n_tiles = wmax / kTile;
-  for (int64_t t = 0; t < n_tiles; t += kSampleStride) {
-    f32x16 acc = score_tile<DT>(cent, t * kTile + col, half, qf);
+  const int64_t n_samp = wmax / kSampleStride;          // sampled buckets of the widest query
+  for (int64_t t = 0; t * kTile < n_samp; ++t) {
+    const int64_t jl = t * kTile + col;                  // this lane's A row: sample jl
+    f32x16 acc = score_tile<DT>(cent, jl < n_samp ? sample_bucket(jl) : 0, half, qf);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int64_t g = t * kTile + tile_row(r, lane);
-      if (g < ne) {
+      const int64_t j = t * kTile + tile_row(r, lane);
+      const int64_t g = sample_bucket(j);
+      if (j < n_samp && g < ne) {
         int bin = (int)__builtin_floorf((acc[r] + 1.0f) * (kBins / 2));
         bin = bin < 0 ? 0 : (bin >= kBins ? kBins - 1 : bin);
         atomicAdd(&hist[32 * wave + col][bin], 1u);
@@ -204,9 +211,8 @@ __global__ __launch_bounds__(256) void k_thresh(IndexCtx ctx, IndexWs ws) {
       const int64_t nej = n_eligible(qpos(ctx, qj));
       float tau = -3.0e38f;
       if (nej > ctx.cap) {
-        const int64_t ntl = nej / kTile;
-        const int64_t nsamp = (ntl + kSampleStride - 1) / kSampleStride;
-        const int64_t want = (2 * (int64_t)ctx.top_b * nsamp + ntl - 1) / ntl;
+        // expect ~2 B full-set scores above tau: 2 B / 16 samples above it
+        const int64_t want = (2 * (int64_t)ctx.top_b + kSampleStride - 1) / kSampleStride;
         int64_t cum = 0;
         for (int b = kBins - 1; b >= 0; --b) {
           cum += hist[tid][b];
@@ -238,22 +244,24 @@ __global__ __launch_bounds__(256) void k_thresh_hist(IndexCtx ctx, IndexWs ws) {
     int64_t o = __shfl_xor(wmax, off, 64);
     wmax = o > wmax ? o : wmax;
   }
-  const int64_t n_tiles = wmax / kTile;
-  const int64_t s0 = (int64_t)blockIdx.x * kHistSegTiles * kSampleStride;
-  if (s0 >= n_tiles || ne <= ctx.cap) {
-    if (__ballot(s0 < n_tiles && ne > ctx.cap) == 0) return;
-  }
+  const int64_t n_tiles = (wmax / kSampleStride + kTile - 1) / kTile;   // tiles of samples
+  const int64_t s0 = (int64_t)blockIdx.x * kHistSegTiles;
+  // wave-uniform exit: every lane must stay for the MFMAs (they read all 64 lanes)
+  if (__ballot(s0 < n_tiles && ne > ctx.cap) == 0) return;
   QFrag qf;
   load_qfrag<DT>(qf, ws.yhat, valid ? qi : 0, valid, half);
   const int64_t wq = mfma_query(ctx, blockIdx.y, wave, 0);
   const void* cent = qcent(ctx, wq < ctx.n ? wq : 0);
   uint32_t* h = ws.hist + (valid ? qi : 0) * 256;
-  for (int64_t t = s0; t < n_tiles && t < s0 + kHistSegTiles * kSampleStride; t += kSampleStride) {
-    f32x16 acc = score_tile<DT>(cent, t * kTile + col, half, qf);
+  const int64_t n_samp = wmax / kSampleStride;
+  for (int64_t t = s0; t < n_tiles && t < s0 + kHistSegTiles; ++t) {
+    const int64_t jl = t * kTile + col;
+    f32x16 acc = score_tile<DT>(cent, jl < n_samp ? sample_bucket(jl) : 0, half, qf);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int64_t g = t * kTile + tile_row(r, lane);
-      if (g < ne && ne > ctx.cap) {
+      const int64_t j = t * kTile + tile_row(r, lane);
+      const int64_t g = sample_bucket(j);
+      if (j < n_samp && g < ne && ne > ctx.cap) {
         int bin = (int)__builtin_floorf((acc[r] + 1.0f) * (kBins / 2));
         bin = bin < 0 ? 0 : (bin >= kBins ? kBins - 1 : bin);
         atomicAdd(&h[bin], 1u);
@@ -268,9 +276,7 @@ __global__ __launch_bounds__(64) void k_thresh_tau(IndexCtx ctx, IndexWs ws) {
   const int64_t nej = n_eligible(qpos(ctx, qj));
   float tau = -3.0e38f;
   if (nej > ctx.cap) {
-    const int64_t ntl = nej / kTile;
-    const int64_t nsamp = (ntl + kSampleStride - 1) / kSampleStride;
-    const int64_t want = (2 * (int64_t)ctx.top_b * nsamp + ntl - 1) / ntl;
+    const int64_t want = (2 * (int64_t)ctx.top_b + kSampleStride - 1) / kSampleStride;
     const uint32_t* h = ws.hist + qj * 256;
     int64_t cum = 0;
     for (int b = kBins - 1; b >= 0; --b) {
@@ -867,8 +873,9 @@ hipError_t launch_thresh(const IndexCtx& ctx, const IndexWs& ws, int dtype, hipS
       const int64_t t = (ctx.pos[i] / kBlock) * kBuckets / kTile;
       max_tiles = t > max_tiles ? t : max_tiles;
     }
-    const int64_t per_wg = (int64_t)kHistSegTiles * kSampleStride;
-    const int64_t gx = (max_tiles + per_wg - 1) / per_wg;
+    // tiles of 32 sampled buckets (one bucket in 16), kHistSegTiles per workgroup
+    const int64_t samp_tiles = (max_tiles * kTile / kSampleStride + kTile - 1) / kTile;
+    const int64_t gx = (samp_tiles + kHistSegTiles - 1) / kHistSegTiles;
     if (gx > 0) {
       dim3 grid((unsigned)gx, (unsigned)query_tiles(ctx));
       if (dtype == LSA_BF16) hipLaunchKernelGGL(k_thresh_hist<LSA_BF16>, grid, dim3(256), 0, s, ctx, ws);

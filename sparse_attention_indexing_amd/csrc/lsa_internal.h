@@ -126,6 +126,18 @@ struct IndexWs {
   uint32_t* hist;      // [n, 256] sampled-score histogram (decode)
 };
 
+// Decode bookkeeping launched once per step for all sequences.
+constexpr int kMaxDecode = 64;        // sequences per lsa_index_decode call
+struct WardJobs {
+  const float* keys[kMaxDecode];      // 512 staged keys of the completed block
+  int64_t block[kMaxDecode];
+  void* cent[kMaxDecode];
+  uint32_t* members[kMaxDecode];
+};
+struct AppendJobs {
+  float* dst[kMaxDecode];             // staging row of each sequence's new key
+};
+
 // ---------------------------------------------------------------- launchers
 // All launchers enqueue on `s` and return hipSuccess or the launch error.
 
@@ -136,6 +148,8 @@ hipError_t launch_tree_groups(const void* child_cent, const int32_t* child_minb,
                               int32_t* child, int32_t* minb, int dtype, int child_is_bucket,
                               hipStream_t s);
 hipError_t launch_copy_rows(float* dst, const float* src, int64_t n, hipStream_t s);
+hipError_t launch_ward_jobs(const WardJobs& jobs, int n, int dtype, hipStream_t s);
+hipError_t launch_append_rows(const float* src, const AppendJobs& jobs, int n, hipStream_t s);
 
 hipError_t launch_qnorm(const float* y, int64_t n, void* yhat, int dtype, uint32_t* hist,
                         hipStream_t s);
