@@ -270,7 +270,9 @@ __global__ __launch_bounds__(256) void k_thresh_hist(IndexCtx ctx, IndexWs ws) {
   }
 }
 
-__global__ __launch_bounds__(64) void k_thresh_tau(IndexCtx ctx, IndexWs ws) {
+// `preset_all`: the 128-query path's convention (ne <= cap keeps every bucket
+// at slot g, so the count starts at ne).
+__global__ __launch_bounds__(64) void k_thresh_tau(IndexCtx ctx, IndexWs ws, int preset_all) {
   const int64_t qj = (int64_t)blockIdx.x * 64 + threadIdx.x;
   if (qj >= ctx.n) return;
   const int64_t nej = n_eligible(qpos(ctx, qj));
@@ -285,7 +287,7 @@ __global__ __launch_bounds__(64) void k_thresh_tau(IndexCtx ctx, IndexWs ws) {
     }
   }
   ws.tau[qj] = tau;
-  ws.cand_cnt[qj] = 0;
+  ws.cand_cnt[qj] = (preset_all && nej <= ctx.cap) ? (int32_t)nej : 0;
   ws.status[qj] = 0;
 }
 
@@ -329,6 +331,332 @@ __global__ __launch_bounds__(256) void k_score_filter(IndexCtx ctx, IndexWs ws, 
       }
     }
   }
+}
+
+// ------------------------------------------------------------------ bf16 prefill scoring, 128 queries per wave
+// Prefill queries share one cache, so every wave can hold the fragments of
+// all 128 queries of its workgroup (4 groups of 32 columns) and score its own
+// 32-bucket tiles against them: 16 MFMAs per tile, and each centroid row is
+// read once per workgroup instead of once per wave.  The 4 waves interleave
+// tiles; each keeps the next two tiles in flight.  grid.x walks query tiles,
+// so the workgroups that read one bucket segment are dispatched together and
+// share it in L2.
+//
+// Candidate convention of this path: a query with no more eligible buckets
+// than candidate slots (ne <= cap) keeps all of them, each stored directly at
+// slot g with the count preset to ne; other queries append (score, bucket)
+// for scores >= tau, staged in LDS and flushed with one atomic per query.
+constexpr int kCapL = 64;           // LDS candidate slots per query and workgroup
+
+struct Q128 {
+  bf16x8 b[4][4];                   // [query group][k step]
+};
+
+__device__ __forceinline__ void load_q128(Q128& q, const void* yhat, int64_t q0, int64_t n, int col,
+                                          int half) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t qi = q0 + 32 * j + col;
+    const bool valid = qi < n;
+    const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(yhat) +
+                                                      (valid ? qi : 0) * kLatent + 32 * half);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      uint4 u = valid ? src[kk] : make_uint4(0, 0, 0, 0);
+      q.b[j][kk] = __builtin_bit_cast(bf16x8, u);
+    }
+  }
+}
+
+__device__ __forceinline__ void load_atile(uint4 (&a)[4], const void* cent, int64_t row, int half) {
+  const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(cent) +
+                                                    row * kLatent + 32 * half);
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) a[kk] = src[kk];
+}
+
+__device__ __forceinline__ void mfma_q128(f32x16 (&acc)[4], const uint4 (&a)[4], const Q128& q) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[kk]), q.b[j][kk],
+                                                       acc[j], 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ float max16(const f32x16& v) {
+  float m0 = __builtin_fmaxf(__builtin_fmaxf(v[0], v[1]), v[2]);
+  float m1 = __builtin_fmaxf(__builtin_fmaxf(v[3], v[4]), v[5]);
+  float m2 = __builtin_fmaxf(__builtin_fmaxf(v[6], v[7]), v[8]);
+  float m3 = __builtin_fmaxf(__builtin_fmaxf(v[9], v[10]), v[11]);
+  float m4 = __builtin_fmaxf(__builtin_fmaxf(v[12], v[13]), v[14]);
+  m0 = __builtin_fmaxf(__builtin_fmaxf(m0, m1), m2);
+  m3 = __builtin_fmaxf(__builtin_fmaxf(m3, m4), v[15]);
+  return __builtin_fmaxf(m0, m3);
+}
+
+// Per-lane view of the 4 queries (one per group) whose column this lane holds.
+struct QCols {
+  int32_t qi[4];
+  int32_t ne[4];
+  float tau[4];
+  bool all[4];
+};
+
+__device__ __forceinline__ int32_t load_qcols(QCols& c, const IndexCtx& ctx, const float* tau,
+                                              int64_t q0, int col) {
+  int32_t nmax = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t qi = q0 + 32 * j + col;
+    const bool valid = qi < ctx.n;
+    c.qi[j] = valid ? (int32_t)qi : 0;
+    c.ne[j] = valid ? (int32_t)n_eligible(ctx.q_start + qi) : 0;
+    c.tau[j] = (valid && tau) ? tau[qi] : 3.0e38f;
+    c.all[j] = valid && c.ne[j] <= ctx.cap;
+    nmax = c.ne[j] > nmax ? c.ne[j] : nmax;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const int32_t o = __shfl_xor(nmax, off, 64);
+    nmax = o > nmax ? o : nmax;
+  }
+  return __builtin_amdgcn_readfirstlane(nmax);   // the same in every wave of the workgroup
+}
+
+// Low-pass epilogue (few candidates per query and tile): one wave-wide
+// compare per (query group, row); the rare passing lanes append to their
+// query's LDS list, or to global memory once the list is full.
+template <bool kFull>
+__device__ __forceinline__ void lowpass_tile(const f32x16 (&acc)[4], int32_t t, const QCols& qc,
+                                             int lane, int col, int* s_cnt, uint2* s_buf,
+                                             const IndexWs& ws, int cap) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int32_t g = t * kTile + tile_row(r, lane);
+      bool pass = acc[j][r] >= qc.tau[j];
+      if (!kFull) pass = pass && g < qc.ne[j];
+      if (pass) {
+        const uint2 e = make_uint2(__float_as_uint(acc[j][r]), (uint32_t)g);
+        const int ql = 32 * j + col;
+        const int slot = atomicAdd(&s_cnt[ql], 1);
+        if (slot < kCapL) {
+          s_buf[ql * kCapL + slot] = e;
+        } else {
+          const int gs = atomicAdd(&ws.cand_cnt[qc.qi[j]], 1);
+          if (gs < cap) ws.cand[(int64_t)qc.qi[j] * cap + gs] = e;
+        }
+      }
+    }
+  }
+}
+
+// High-pass epilogue (many candidates, or every eligible bucket kept): per
+// query and tile one atomic reserves the slots of both lanes that hold the
+// query's 32 rows; queries with ne <= cap store bucket g at slot g.
+__device__ __forceinline__ void highpass_tile(const f32x16 (&acc)[4], int32_t t, const QCols& qc,
+                                              int lane, int col, int half, const IndexWs& ws,
+                                              int cap) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t bits = 0;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int32_t g = t * kTile + tile_row(r, lane);
+      const bool p = (qc.all[j] || acc[j][r] >= qc.tau[j]) && g < qc.ne[j];
+      bits |= (uint32_t)p << r;
+    }
+    if (__ballot(bits != 0) == 0) continue;
+    uint2* dst = ws.cand + (int64_t)qc.qi[j] * cap;
+    const int nl = __popc(bits);
+    const int np = __shfl_xor(nl, 32, 64);
+    int base = 0;
+    if (!qc.all[j] && half == 0 && nl + np > 0) base = atomicAdd(&ws.cand_cnt[qc.qi[j]], nl + np);
+    base = __shfl(base, col, 64);
+    int slot = base + (half ? np : 0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      if ((bits >> r) & 1u) {
+        const int32_t g = t * kTile + tile_row(r, lane);
+        const uint2 e = make_uint2(__float_as_uint(acc[j][r]), (uint32_t)g);
+        if (qc.all[j]) dst[g] = e;
+        else if (slot < cap) dst[slot] = e;
+        ++slot;
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(256, 2) void k_score_filter_q128(IndexCtx ctx, IndexWs ws,
+                                                              int seg_tiles) {
+  __shared__ int s_cnt[kQueriesPerWg];
+  __shared__ uint2 s_buf[kQueriesPerWg * kCapL];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31, half = lane >> 5;
+  const int64_t q0 = (int64_t)blockIdx.x * kQueriesPerWg;
+  QCols qc;
+  const int32_t nmax = load_qcols(qc, ctx, ws.tau, q0, col);
+  int32_t nmin = 0x7fffffff;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (q0 + 32 * j + col < ctx.n) nmin = qc.ne[j] < nmin ? qc.ne[j] : nmin;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const int32_t o = __shfl_xor(nmin, off, 64);
+    nmin = o < nmin ? o : nmin;
+  }
+  nmin = __builtin_amdgcn_readfirstlane(nmin);
+  const int32_t t0 = (int32_t)blockIdx.y * seg_tiles;
+  int32_t t1 = (nmax + kTile - 1) / kTile;
+  if (t1 > t0 + seg_tiles) t1 = t0 + seg_tiles;
+  if (t0 >= t1) return;                                  // uniform over the workgroup
+  // low-pass when every query expects at most kCapL / 4 candidates here
+  const bool lowpass = nmin > ctx.cap &&
+                       (int64_t)seg_tiles * kTile * 2 * ctx.top_b <= (int64_t)(kCapL / 4) * nmin;
+  const int32_t t_full = nmin / kTile;                   // tiles below every query's ne
+  if (tid < kQueriesPerWg) s_cnt[tid] = 0;
+  Q128 q;
+  load_q128(q, ws.yhat, q0, ctx.n, col, half);
+  const void* cent = ctx.cent[0];
+  const int32_t tl = t1 - 1;
+  __syncthreads();
+
+  auto epilogue = [&](const f32x16 (&acc)[4], int32_t t) {
+    if (!lowpass) highpass_tile(acc, t, qc, lane, col, half, ws, ctx.cap);
+    else if (t < t_full) lowpass_tile<true>(acc, t, qc, lane, col, s_cnt, s_buf, ws, ctx.cap);
+    else lowpass_tile<false>(acc, t, qc, lane, col, s_cnt, s_buf, ws, ctx.cap);
+  };
+  // two register buffers: each is reloaded (clamped to the last tile, so the
+  // number of loads in flight is the same on every path) as soon as its
+  // MFMAs have been issued, before the epilogue of the tile it held
+  uint4 ra[4], rb[4];
+  int32_t t = t0 + wave;
+  load_atile(ra, cent, (int64_t)(t < tl ? t : tl) * kTile + col, half);
+  __builtin_amdgcn_sched_barrier(0);   // keep ra's loads older than rb's
+  load_atile(rb, cent, (int64_t)(t + 4 < tl ? t + 4 : tl) * kTile + col, half);
+  for (; t < t1; t += 8) {
+    f32x16 acc[4];
+    mfma_q128(acc, ra, q);
+    load_atile(ra, cent, (int64_t)(t + 8 < tl ? t + 8 : tl) * kTile + col, half);
+    epilogue(acc, t);
+    mfma_q128(acc, rb, q);
+    load_atile(rb, cent, (int64_t)(t + 12 < tl ? t + 12 : tl) * kTile + col, half);
+    if (t + 4 < t1) epilogue(acc, t + 4);
+  }
+  __syncthreads();
+  // flush: two threads per query
+  const int ql = tid >> 1, sub = tid & 1;
+  const int64_t qi = q0 + ql;
+  int n = s_cnt[ql];
+  n = n < kCapL ? n : kCapL;
+  int base = 0;
+  if (sub == 0 && n > 0 && qi < ctx.n) base = atomicAdd(&ws.cand_cnt[qi], n);
+  base = __shfl(base, lane & ~1, 64);
+  if (qi < ctx.n) {
+    uint2* dst = ws.cand + qi * (int64_t)ctx.cap;
+    for (int i = sub; i < n; i += 2)
+      if (base + i < ctx.cap) dst[base + i] = s_buf[ql * kCapL + i];
+  }
+}
+
+// Threshold for the same path: every wave scores its own sampled tiles
+// against the workgroup's 128 queries into one LDS histogram per query.  With
+// few query tiles the samples are split over grid.y workgroups whose
+// histograms are added in global memory and finished by k_thresh_tau.
+__global__ __launch_bounds__(512, 1) void k_thresh_q128(IndexCtx ctx, IndexWs ws, int seg_tiles,
+                                                        int split) {
+  __shared__ uint32_t hist[kQueriesPerWg][kBins];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31, half = lane >> 5;
+  const int64_t q0 = (int64_t)blockIdx.x * kQueriesPerWg;
+  for (int i = tid; i < kQueriesPerWg * kBins; i += 512) (&hist[0][0])[i] = 0;
+  QCols qc;
+  const int32_t nmax = load_qcols(qc, ctx, nullptr, q0, col);
+  const int32_t n_samp = nmax / kSampleStride;            // samples of the widest query
+  const int32_t s0 = (int32_t)blockIdx.y * seg_tiles;
+  int32_t s1 = (n_samp + kTile - 1) / kTile;
+  if (s1 > s0 + seg_tiles) s1 = s0 + seg_tiles;
+  Q128 q;
+  load_q128(q, ws.yhat, q0, ctx.n, col, half);
+  const void* cent = ctx.cent[0];
+  __syncthreads();
+  if (s0 < s1) {
+    const int32_t jlast = n_samp - 1;
+    auto row_of = [&](int32_t t) {
+      const int32_t j = t * kTile + col;
+      return sample_bucket(j < jlast ? j : jlast);
+    };
+    auto epilogue = [&](const f32x16 (&acc)[4], int32_t t) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (qc.all[j]) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int32_t jj = t * kTile + tile_row(r, lane);
+          if (jj < n_samp && 16 * jj + ((7 * jj) & 15) < qc.ne[j]) {
+            int bin = (int)((acc[j][r] + 1.0f) * (kBins / 2));
+            bin = bin < 0 ? 0 : (bin >= kBins ? kBins - 1 : bin);
+            atomicAdd(&hist[32 * j + col][bin], 1u);
+          }
+        }
+      }
+    };
+    constexpr int W = 8;
+    uint4 ra[4], rb[4];
+    int32_t t = s0 + wave;
+    const int32_t tl = s1 - 1;
+    load_atile(ra, cent, row_of(t < tl ? t : tl), half);
+    __builtin_amdgcn_sched_barrier(0);
+    load_atile(rb, cent, row_of(t + W < tl ? t + W : tl), half);
+    for (; t < s1; t += 2 * W) {
+      f32x16 acc[4];
+      mfma_q128(acc, ra, q);
+      load_atile(ra, cent, row_of(t + 2 * W < tl ? t + 2 * W : tl), half);
+      epilogue(acc, t);
+      mfma_q128(acc, rb, q);
+      load_atile(rb, cent, row_of(t + 3 * W < tl ? t + 3 * W : tl), half);
+      if (t + W < s1) epilogue(acc, t + W);
+    }
+  }
+  __syncthreads();
+  if (split) {
+    for (int i = tid; i < kQueriesPerWg * kBins; i += 512) {
+      const uint32_t v = (&hist[0][0])[i];
+      const int64_t qj = q0 + i / kBins;
+      if (v && qj < ctx.n) atomicAdd(&ws.hist[qj * kBins + (i % kBins)], v);
+    }
+    return;
+  }
+  if (tid < kQueriesPerWg) {
+    const int64_t qj = q0 + tid;
+    if (qj < ctx.n) {
+      const int64_t nej = n_eligible(ctx.q_start + qj);
+      float tau = -3.0e38f;
+      if (nej > ctx.cap) {
+        const int64_t want = (2 * (int64_t)ctx.top_b + kSampleStride - 1) / kSampleStride;
+        int64_t cum = 0;
+        for (int b = kBins - 1; b >= 0; --b) {
+          cum += hist[tid][b];
+          if (cum >= want) { tau = (float)b / (kBins / 2) - 1.0f; break; }
+        }
+      }
+      ws.tau[qj] = tau;
+      ws.cand_cnt[qj] = nej <= ctx.cap ? (int32_t)nej : 0;
+      ws.status[qj] = 0;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_fill_u32(uint32_t* p, int64_t n, uint32_t v) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = v;
 }
 
 // ------------------------------------------------------------------ exact select
@@ -883,7 +1211,28 @@ hipError_t launch_thresh(const IndexCtx& ctx, const IndexWs& ws, int dtype, hipS
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(k_thresh_tau, dim3((unsigned)((ctx.n + 63) / 64)), dim3(64), 0, s, ctx, ws);
+    hipLaunchKernelGGL(k_thresh_tau, dim3((unsigned)((ctx.n + 63) / 64)), dim3(64), 0, s, ctx, ws, 0);
+    return hipGetLastError();
+  }
+  if (dtype == LSA_BF16) {
+    // 128 queries per wave; split the samples when there are few query tiles
+    const int64_t qt = query_tiles(ctx);
+    const int64_t last = ctx.q_start + ctx.n - 1;
+    const int64_t samp_tiles = ((last / kBlock) * kBuckets / kSampleStride + kTile - 1) / kTile;
+    int64_t split = qt < 128 ? (256 + qt - 1) / qt : 1;
+    const int64_t max_split = (samp_tiles + 15) / 16;
+    if (split > max_split) split = max_split;
+    if (split < 1) split = 1;
+    const int64_t seg = (samp_tiles + split - 1) / split;
+    if (split > 1) {
+      const int64_t nh = ctx.n * kBins;
+      const int64_t gb = (nh + 255) / 256 < 4096 ? (nh + 255) / 256 : 4096;
+      hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)gb), dim3(256), 0, s, ws.hist, nh, 0u);
+    }
+    hipLaunchKernelGGL(k_thresh_q128, dim3((unsigned)qt, (unsigned)split), dim3(512), 0, s, ctx, ws,
+                       (int)(seg > 0 ? seg : 1), (int)(split > 1));
+    if (split > 1)
+      hipLaunchKernelGGL(k_thresh_tau, dim3((unsigned)((ctx.n + 63) / 64)), dim3(64), 0, s, ctx, ws, 1);
     return hipGetLastError();
   }
   dim3 grid((unsigned)query_tiles(ctx));
@@ -895,6 +1244,21 @@ hipError_t launch_thresh(const IndexCtx& ctx, const IndexWs& ws, int dtype, hipS
 hipError_t launch_score_filter(const IndexCtx& ctx, const IndexWs& ws, int dtype,
                                int64_t max_tiles, hipStream_t s) {
   if (ctx.n <= 0 || max_tiles <= 0) return hipSuccess;
+  if (!ctx.per_seq && dtype == LSA_BF16) {
+    // segment length: about kCapL / 4 expected candidates per query for the
+    // widest query (~2 B of ne_max pass), so the LDS lists rarely overflow;
+    // when even 16 tiles expect more, workgroups take the high-pass epilogue
+    // and longer segments only save query loads
+    const int64_t last = ctx.q_start + ctx.n - 1;
+    const int64_t ne_max = (last / kBlock) * kBuckets;
+    const int64_t seg_buckets = (int64_t)(kCapL / 4) * ne_max / (2 * (int64_t)(ctx.top_b > 0 ? ctx.top_b : 1));
+    int64_t seg = 16;
+    while (seg * 2 * kTile <= seg_buckets && seg < 512) seg *= 2;
+    if (seg_buckets < 16 * kTile) seg = 128;
+    dim3 grid((unsigned)query_tiles(ctx), (unsigned)((max_tiles + seg - 1) / seg));
+    hipLaunchKernelGGL(k_score_filter_q128, grid, dim3(256), 0, s, ctx, ws, (int)seg);
+    return hipGetLastError();
+  }
   // decode has few queries: shorter segments give enough workgroups to stream HBM
   const int seg = ctx.per_seq ? 32 : kSegTiles;
   dim3 grid((unsigned)((max_tiles + seg - 1) / seg), (unsigned)query_tiles(ctx));

@@ -13,6 +13,7 @@ import lsa_synth as S
 import sparse_attention_indexing_amd as lsa
 from oracle import lsa_oracle as O
 from parity_util import (bf16_tensor, cache_to_host, check_list_invariants, compare_cache,
+                         oracle_cache_parallel,
                          compare_lists, gpu_cache, oracle_params)
 
 pytestmark = pytest.mark.gpu
@@ -122,6 +123,24 @@ def test_index_last_chunk_and_determinism():
     oc = O.build_cache(X, oracle_params(p))
     rows = np.arange(0, Tq, 37)
     compare_lists(a[0].cpu().numpy()[rows], a[1].cpu().numpy()[rows], T - Tq + rows, Y[rows], oc)
+
+
+def test_index_lowpass_last_chunk():
+    """T=65536, last 2048 queries, k=16: every query has ~8K eligible buckets
+    and keeps 69, so the scoring kernel stages its few candidates in LDS
+    (the low-pass epilogue) and splits the threshold samples over workgroups."""
+    say("case: index T=65536 last 2048 queries bf16 k=16 (low-pass filter)")
+    w = S.WORKLOADS[2]
+    T, Tq = 65536, 2048
+    X, Y, _ = S.latent_inputs(w, T=T, query_rows=(T - Tq, T))
+    p = lsa.Params(k=16, index_dtype=lsa.LSA_BF16)
+    c = gpu_cache(X, p)
+    idx, cnt = lsa.index_prefill(c, torch.from_numpy(Y).cuda(), T - Tq, p)
+    torch.cuda.synchronize()
+    oc = oracle_cache_parallel(X, oracle_params(p))
+    rows = np.unique(np.concatenate([np.arange(0, Tq, 29), np.arange(Tq - 8, Tq)]))
+    rep = compare_lists(idx.cpu().numpy()[rows], cnt.cpu().numpy()[rows], T - Tq + rows, Y[rows], oc)
+    say("index", rep)
 
 
 # ---------------------------------------------------------------- attention
