@@ -14,7 +14,8 @@ from dataclasses import dataclass, fields
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "liblsa.so")
+# LSA_LIBRARY selects another build of the same library (same C ABI)
+LIB_PATH = os.environ.get("LSA_LIBRARY") or os.path.join(_PKG, "liblsa.so")
 
 LSA_F32, LSA_BF16 = 0, 1
 LSA_FLAT, LSA_TREE = 0, 1

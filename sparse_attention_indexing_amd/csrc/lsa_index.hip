@@ -346,7 +346,7 @@ __global__ __launch_bounds__(256) void k_score_filter(IndexCtx ctx, IndexWs ws, 
 // than candidate slots (ne <= cap) keeps all of them, each stored directly at
 // slot g with the count preset to ne; other queries append (score, bucket)
 // for scores >= tau, staged in LDS and flushed with one atomic per query.
-constexpr int kCapL = 64;           // LDS candidate slots per query and workgroup
+constexpr int kCapL = 48;           // LDS candidate slots per query and workgroup
 
 struct Q128 {
   bf16x8 b[4][4];                   // [query group][k step]
@@ -427,33 +427,59 @@ __device__ __forceinline__ int32_t load_qcols(QCols& c, const IndexCtx& ctx, con
   return __builtin_amdgcn_readfirstlane(nmax);   // the same in every wave of the workgroup
 }
 
-// Low-pass epilogue (few candidates per query and tile): one wave-wide
-// compare per (query group, row); the rare passing lanes append to their
-// query's LDS list, or to global memory once the list is full.
-template <bool kFull>
-__device__ __forceinline__ void lowpass_tile(const f32x16 (&acc)[4], int32_t t, const QCols& qc,
-                                             int lane, int col, int* s_cnt, uint2* s_buf,
-                                             const IndexWs& ws, int cap) {
+// Low-pass epilogue (few candidates per query and tile).  In the tile loop
+// each lane only takes the max of its 16 scores per query group (8 v_max3)
+// and compares it with the query's tau; a lane whose max passes copies its 16
+// scores into the wave's LDS entry buffer (slots from a ballot, no atomics).
+// expand_entries then turns buffered entries into candidates with one entry
+// per lane, appending to the query's LDS list (global memory once full).
+constexpr int kEnt = 64;            // buffered (lane, group) entries per wave
+
+struct LowPassLds {
+  int cnt[kQueriesPerWg];                             // candidates per query
+  uint2 buf[kQueriesPerWg * kCapL];                   // (score bits, bucket)
+  float tau[kQueriesPerWg];
+  float ent[4][kEnt][16];                             // buffered scores
+  uint32_t meta[4][kEnt];                             // tile << 8 | half << 7 | query
+};
+
+__device__ __forceinline__ void lds_append(LowPassLds& L, const IndexWs& ws, int cap, int ql,
+                                           int64_t qi, float s, int32_t g) {
+  const uint2 e = make_uint2(__float_as_uint(s), (uint32_t)g);
+  const int slot = atomicAdd(&L.cnt[ql], 1);
+  if (slot < kCapL) {
+    L.buf[ql * kCapL + slot] = e;
+  } else {
+    const int gs = atomicAdd(&ws.cand_cnt[qi], 1);
+    if (gs < cap) ws.cand[qi * cap + gs] = e;
+  }
+}
+
+// one buffered entry per lane: its 16 rows against the query's tau and ne
+__device__ __forceinline__ void expand_entries(LowPassLds& L, const IndexCtx& ctx, const IndexWs& ws,
+                                               int64_t q0, int wave, int lane, int n) {
+  __builtin_amdgcn_wave_barrier();
+  if (lane < n) {
+    const uint32_t meta = L.meta[wave][lane];
+    const int ql = meta & 127, h = (meta >> 7) & 1;
+    const int32_t gb = (int32_t)(meta >> 8) * kTile + 4 * h;
+    const int64_t qi = q0 + ql;
+    const float tau = L.tau[ql];
+    const int32_t ne = (int32_t)n_eligible(ctx.q_start + qi);
+    const float4* src = reinterpret_cast<const float4*>(L.ent[wave][lane]);
+    float v[16];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+    for (int i = 0; i < 4; ++i) {
+      const float4 x = src[i];
+      v[4 * i] = x.x; v[4 * i + 1] = x.y; v[4 * i + 2] = x.z; v[4 * i + 3] = x.w;
+    }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int32_t g = t * kTile + tile_row(r, lane);
-      bool pass = acc[j][r] >= qc.tau[j];
-      if (!kFull) pass = pass && g < qc.ne[j];
-      if (pass) {
-        const uint2 e = make_uint2(__float_as_uint(acc[j][r]), (uint32_t)g);
-        const int ql = 32 * j + col;
-        const int slot = atomicAdd(&s_cnt[ql], 1);
-        if (slot < kCapL) {
-          s_buf[ql * kCapL + slot] = e;
-        } else {
-          const int gs = atomicAdd(&ws.cand_cnt[qc.qi[j]], 1);
-          if (gs < cap) ws.cand[(int64_t)qc.qi[j] * cap + gs] = e;
-        }
-      }
+      const int32_t g = gb + 8 * (r >> 2) + (r & 3);
+      if (v[r] >= tau && g < ne) lds_append(L, ws, ctx.cap, ql, qi, v[r], g);
     }
   }
+  __builtin_amdgcn_wave_barrier();
 }
 
 // High-pass epilogue (many candidates, or every eligible bucket kept): per
@@ -494,8 +520,7 @@ __device__ __forceinline__ void highpass_tile(const f32x16 (&acc)[4], int32_t t,
 
 __global__ __launch_bounds__(256, 2) void k_score_filter_q128(IndexCtx ctx, IndexWs ws,
                                                               int seg_tiles) {
-  __shared__ int s_cnt[kQueriesPerWg];
-  __shared__ uint2 s_buf[kQueriesPerWg * kCapL];
+  __shared__ __attribute__((aligned(16))) LowPassLds L;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
@@ -519,18 +544,42 @@ __global__ __launch_bounds__(256, 2) void k_score_filter_q128(IndexCtx ctx, Inde
   // low-pass when every query expects at most kCapL / 4 candidates here
   const bool lowpass = nmin > ctx.cap &&
                        (int64_t)seg_tiles * kTile * 2 * ctx.top_b <= (int64_t)(kCapL / 4) * nmin;
-  const int32_t t_full = nmin / kTile;                   // tiles below every query's ne
-  if (tid < kQueriesPerWg) s_cnt[tid] = 0;
+  if (tid < kQueriesPerWg) {
+    L.cnt[tid] = 0;
+    L.tau[tid] = q0 + tid < ctx.n ? ws.tau[q0 + tid] : 3.0e38f;
+  }
   Q128 q;
   load_q128(q, ws.yhat, q0, ctx.n, col, half);
   const void* cent = ctx.cent[0];
   const int32_t tl = t1 - 1;
   __syncthreads();
 
+  int ecnt = 0;                                          // wave-uniform
   auto epilogue = [&](const f32x16 (&acc)[4], int32_t t) {
-    if (!lowpass) highpass_tile(acc, t, qc, lane, col, half, ws, ctx.cap);
-    else if (t < t_full) lowpass_tile<true>(acc, t, qc, lane, col, s_cnt, s_buf, ws, ctx.cap);
-    else lowpass_tile<false>(acc, t, qc, lane, col, s_cnt, s_buf, ws, ctx.cap);
+    if (!lowpass) {
+      highpass_tile(acc, t, qc, lane, col, half, ws, ctx.cap);
+      return;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint64_t mk = __ballot(max16(acc[j]) >= qc.tau[j]);
+      if (mk == 0) continue;
+      const int n = __popcll(mk);
+      if (ecnt + n > kEnt) {
+        expand_entries(L, ctx, ws, q0, wave, lane, ecnt);
+        ecnt = 0;
+      }
+      if ((mk >> lane) & 1ull) {
+        const int e = ecnt + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u));
+        float4* dst = reinterpret_cast<float4*>(L.ent[wave][e]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          dst[i] = make_float4(acc[j][4 * i], acc[j][4 * i + 1], acc[j][4 * i + 2], acc[j][4 * i + 3]);
+        L.meta[wave][e] = ((uint32_t)t << 8) | ((uint32_t)half << 7) | (uint32_t)(32 * j + col);
+      }
+      ecnt += n;
+    }
   };
   // two register buffers: each is reloaded (clamped to the last tile, so the
   // number of loads in flight is the same on every path) as soon as its
@@ -549,11 +598,12 @@ __global__ __launch_bounds__(256, 2) void k_score_filter_q128(IndexCtx ctx, Inde
     load_atile(rb, cent, (int64_t)(t + 12 < tl ? t + 12 : tl) * kTile + col, half);
     if (t + 4 < t1) epilogue(acc, t + 4);
   }
+  if (ecnt) expand_entries(L, ctx, ws, q0, wave, lane, ecnt);
   __syncthreads();
   // flush: two threads per query
   const int ql = tid >> 1, sub = tid & 1;
   const int64_t qi = q0 + ql;
-  int n = s_cnt[ql];
+  int n = L.cnt[ql];
   n = n < kCapL ? n : kCapL;
   int base = 0;
   if (sub == 0 && n > 0 && qi < ctx.n) base = atomicAdd(&ws.cand_cnt[qi], n);
@@ -561,7 +611,7 @@ __global__ __launch_bounds__(256, 2) void k_score_filter_q128(IndexCtx ctx, Inde
   if (qi < ctx.n) {
     uint2* dst = ws.cand + qi * (int64_t)ctx.cap;
     for (int i = sub; i < n; i += 2)
-      if (base + i < ctx.cap) dst[base + i] = s_buf[ql * kCapL + i];
+      if (base + i < ctx.cap) dst[base + i] = L.buf[ql * kCapL + i];
   }
 }
 
@@ -657,6 +707,223 @@ __global__ __launch_bounds__(512, 1) void k_thresh_q128(IndexCtx ctx, IndexWs ws
 __global__ __launch_bounds__(256) void k_fill_u32(uint32_t* p, int64_t n, uint32_t v) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = v;
+}
+
+// ------------------------------------------------------------------ decode scoring (bf16)
+// Decode scores one query per sequence against that sequence's own
+// centroids: a matrix-vector product, bound by reading 128 B per bucket.
+// Eight lanes share a centroid row (16 B = 8 dims each), so one wave-wide
+// load reads 8 consecutive rows (1 KiB, fully coalesced) and the partial dot
+// products are summed across the 8 lanes; each lane keeps 8 loads in flight.
+constexpr int kDecRowsPerWg = 1024;     // buckets per filter workgroup
+constexpr int kDecSampPerWg = 512;      // sampled buckets per threshold workgroup
+
+__device__ __forceinline__ void load_q8(float (&yq)[8], const void* yhat, int64_t qi, int sub) {
+  const uint4 u = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(yhat) +
+                                                 qi * kLatent)[sub];
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    yq[2 * e] = bf16_to_f32((uint16_t)(w[e] & 0xffffu));
+    yq[2 * e + 1] = bf16_to_f32((uint16_t)(w[e] >> 16));
+  }
+}
+
+__device__ __forceinline__ float dot8(const uint4& u, const float (&yq)[8]) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    s = __builtin_fmaf(__uint_as_float(w[e] << 16), yq[2 * e], s);
+    s = __builtin_fmaf(__uint_as_float(w[e] & 0xffff0000u), yq[2 * e + 1], s);
+  }
+  return s;
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// sum over the 8 lanes of a row with DPP (quad xor 1, quad xor 2, half-row
+// mirror): every lane of the 8 ends with the same sum
+__device__ __forceinline__ float sum8(float s) {
+  s += dpp_f<0xB1>(s);
+  s += dpp_f<0x4E>(s);
+  s += dpp_f<0x141>(s);
+  return s;
+}
+
+// 64 rows per batch per wave: row rb + 8 k + (lane / 8), dims 8 (lane % 8) ..
+__device__ __forceinline__ void load_rows8(uint4 (&u)[8], const uint4* cent, int64_t rb,
+                                           int64_t rlast, int grp, int sub) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    int64_t row = rb + 8 * k + grp;
+    row = row < rlast ? row : rlast;
+    u[k] = cent[row * 8 + sub];
+  }
+}
+
+constexpr int kDecStage = 64;           // LDS candidate slots per wave
+
+// grid.x = chunks of kDecRowsPerWg buckets, grid.y = query (sequence).
+// Scores >= tau are staged per wave in LDS and flushed with one atomic.
+__global__ __launch_bounds__(256) void k_dec_filter(IndexCtx ctx, IndexWs ws) {
+  __shared__ uint2 s_buf[4][kDecStage];
+  const int64_t qi = blockIdx.y;
+  const int64_t ne = n_eligible(ctx.pos[qi]);
+  const int64_t r0 = (int64_t)blockIdx.x * kDecRowsPerWg;
+  if (r0 >= ne) return;
+  const int64_t r1 = r0 + kDecRowsPerWg < ne ? r0 + kDecRowsPerWg : ne;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int sub = lane & 7, grp = lane >> 3;
+  float yq[8];
+  load_q8(yq, ws.yhat, qi, sub);
+  const float tau = ws.tau[qi];
+  const uint4* cent = reinterpret_cast<const uint4*>(ctx.cent[qi]);
+  uint2* cand = ws.cand + qi * (int64_t)ctx.cap;
+  uint2* stage = s_buf[wave];
+  int cnt = 0;                                           // wave-uniform
+  auto flush = [&]() {
+    __builtin_amdgcn_wave_barrier();
+    int base = 0;
+    if (lane == 0) base = atomicAdd(&ws.cand_cnt[qi], cnt);
+    base = __shfl(base, 0, 64);
+    if (lane < cnt && base + lane < ctx.cap) cand[base + lane] = stage[lane];
+    __builtin_amdgcn_wave_barrier();
+    cnt = 0;
+  };
+  auto process = [&](const uint4 (&u)[8], int64_t rb) {
+    float s[8];
+    uint64_t m[8];
+    int npass = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      s[k] = sum8(dot8(u[k], yq));
+      const bool pass = (sub == 0) & (rb + 8 * k + grp < r1) & (s[k] >= tau);
+      m[k] = __ballot(pass);
+      npass += __popcll(m[k]);
+    }
+    npass = __builtin_amdgcn_readfirstlane(npass);
+    if (npass == 0) return;
+    if (cnt + npass > kDecStage) flush();
+    int base = cnt;
+    uint2* dst = stage;
+    if (npass > kDecStage) {                               // only when every row passes
+      int g = 0;
+      if (lane == 0) g = atomicAdd(&ws.cand_cnt[qi], npass);
+      base = __shfl(g, 0, 64);
+      dst = cand;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if ((m[k] >> lane) & 1ull) {
+        const int slot = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m[k] >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m[k], 0u));
+        if (dst != cand || slot < ctx.cap)
+          dst[slot] = make_uint2(__float_as_uint(s[k]), (uint32_t)(rb + 8 * k + grp));
+      }
+      base += __popcll(m[k]);
+    }
+    if (dst == stage) cnt += npass;
+  };
+  // one batch of 8 loads per wave at a time; latency is covered by the many
+  // resident waves (small register footprint), not by software pipelining
+  const int64_t rlast = r1 - 1;
+  for (int64_t rb = r0 + 64 * wave; rb < r1; rb += 256) {
+    uint4 u[8];
+    load_rows8(u, cent, rb, rlast, grp, sub);
+    __builtin_amdgcn_sched_barrier(0);   // all 8 loads before any use
+    process(u, rb);
+  }
+  if (cnt) flush();
+}
+
+// Sampled histogram for the decode threshold: grid.x = chunks of
+// kDecSampPerWg samples, grid.y = query; one LDS histogram per workgroup,
+// added into the query's global histogram (cleared by k_qnorm).
+__global__ __launch_bounds__(256) void k_dec_hist(IndexCtx ctx, IndexWs ws) {
+  __shared__ uint32_t h[kBins];
+  const int64_t qi = blockIdx.y;
+  const int64_t ne = n_eligible(ctx.pos[qi]);
+  const int64_t n_samp = ne / kSampleStride;
+  const int64_t j0 = (int64_t)blockIdx.x * kDecSampPerWg;
+  if (ne <= ctx.cap || j0 >= n_samp) return;
+  const int64_t j1 = j0 + kDecSampPerWg < n_samp ? j0 + kDecSampPerWg : n_samp;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int sub = lane & 7, grp = lane >> 3;
+  h[tid] = 0u;
+  float yq[8];
+  load_q8(yq, ws.yhat, qi, sub);
+  const uint4* cent = reinterpret_cast<const uint4*>(ctx.cent[qi]);
+  __syncthreads();
+  for (int64_t jb = j0 + 64 * wave; jb < j1; jb += 256) {
+    uint4 u[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      int64_t j = jb + 8 * k + grp;
+      j = j < j1 ? j : j1 - 1;
+      u[k] = cent[sample_bucket(j) * 8 + sub];
+    }
+    __builtin_amdgcn_sched_barrier(0);   // all 8 loads before any use
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float s = sum8(dot8(u[k], yq));
+      const int64_t j = jb + 8 * k + grp;
+      if ((sub == 0) & (j < j1)) {
+        int bin = (int)((s + 1.0f) * (kBins / 2));
+        bin = bin < 0 ? 0 : (bin >= kBins ? kBins - 1 : bin);
+        atomicAdd(&h[bin], 1u);
+      }
+    }
+  }
+  __syncthreads();
+  if (h[tid]) atomicAdd(&ws.hist[qi * kBins + tid], h[tid]);
+}
+
+// tau from the global histogram, one wave per query: lane l sums the 4 bins
+// 4 (63 - l) .. 4 (63 - l) + 3, so an inclusive prefix over lanes counts
+// samples from the top bin down.
+__global__ __launch_bounds__(64) void k_dec_tau(IndexCtx ctx, IndexWs ws) {
+  const int64_t qi = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int64_t ne = n_eligible(ctx.pos[qi]);
+  const uint32_t* h = ws.hist + qi * kBins;
+  const int b0 = 4 * (63 - lane);
+  const uint32_t c0 = h[b0], c1 = h[b0 + 1], c2 = h[b0 + 2], c3 = h[b0 + 3];
+  const uint32_t mine = c0 + c1 + c2 + c3;
+  uint32_t incl = mine;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t o = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += o;
+  }
+  const uint32_t want = (uint32_t)((2 * (int64_t)ctx.top_b + kSampleStride - 1) / kSampleStride);
+  const uint64_t hit = __ballot(incl >= want);
+  float tau = -3.0e38f;
+  if (ne > ctx.cap && hit) {
+    const int l = __builtin_ctzll(hit);                 // first lane (highest bins) reaching want
+    if (lane == l) {
+      uint32_t cum = incl - mine;                        // samples above this lane's bins
+      int b = b0 + 3;
+      const uint32_t cs[4] = {c0, c1, c2, c3};
+      for (int e = 3; e >= 0; --e) {
+        cum += cs[e];
+        b = b0 + e;
+        if (cum >= want) break;
+      }
+      tau = (float)b / (kBins / 2) - 1.0f;
+    }
+    tau = __shfl(tau, l, 64);
+  }
+  if (lane == 0) {
+    ws.tau[qi] = tau;
+    ws.cand_cnt[qi] = 0;
+    ws.status[qi] = 0;
+  }
 }
 
 // ------------------------------------------------------------------ exact select
@@ -1194,6 +1461,21 @@ static int64_t query_tiles(const IndexCtx& ctx) {
 
 hipError_t launch_thresh(const IndexCtx& ctx, const IndexWs& ws, int dtype, hipStream_t s) {
   if (ctx.n <= 0) return hipSuccess;
+  if (ctx.per_seq && dtype == LSA_BF16) {
+    int64_t max_samp = 0;
+    for (int64_t i = 0; i < ctx.n; ++i) {
+      const int64_t ns = (ctx.pos[i] / kBlock) * kBuckets / kSampleStride;
+      max_samp = ns > max_samp ? ns : max_samp;
+    }
+    const int64_t gx = (max_samp + kDecSampPerWg - 1) / kDecSampPerWg;
+    if (gx > 0) {
+      hipLaunchKernelGGL(k_dec_hist, dim3((unsigned)gx, (unsigned)ctx.n), dim3(256), 0, s, ctx, ws);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(k_dec_tau, dim3((unsigned)ctx.n), dim3(64), 0, s, ctx, ws);
+    return hipGetLastError();
+  }
   if (ctx.per_seq) {
     // decode: many workgroups per query, global histogram, then tau
     int64_t max_tiles = 0;
@@ -1257,6 +1539,11 @@ hipError_t launch_score_filter(const IndexCtx& ctx, const IndexWs& ws, int dtype
     if (seg_buckets < 16 * kTile) seg = 128;
     dim3 grid((unsigned)query_tiles(ctx), (unsigned)((max_tiles + seg - 1) / seg));
     hipLaunchKernelGGL(k_score_filter_q128, grid, dim3(256), 0, s, ctx, ws, (int)seg);
+    return hipGetLastError();
+  }
+  if (ctx.per_seq && dtype == LSA_BF16) {
+    const int64_t gx = (max_tiles * kTile + kDecRowsPerWg - 1) / kDecRowsPerWg;
+    hipLaunchKernelGGL(k_dec_filter, dim3((unsigned)gx, (unsigned)ctx.n), dim3(256), 0, s, ctx, ws);
     return hipGetLastError();
   }
   // decode has few queries: shorter segments give enough workgroups to stream HBM
