@@ -387,6 +387,33 @@ __device__ __forceinline__ void mfma_q128(f32x16 (&acc)[4], const uint4 (&a)[4],
   }
 }
 
+// One tile for the low-pass path: the MFMAs run query group by query group,
+// and the 16-row max and ballot of group j are computed while the MFMAs of
+// group j + 1 execute (the scheduling barriers ask for 1 MFMA, then 3 VALU).
+__device__ __forceinline__ float max16(const f32x16& v);
+
+__device__ __forceinline__ void mfma_q128_masks(f32x16 (&acc)[4], uint64_t (&mks)[4],
+                                                const uint4 (&a)[4], const Q128& q,
+                                                const float (&tau)[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[kk]), q.b[j][kk],
+                                                       acc[j], 0, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) mks[j] = __ballot(max16(acc[j]) >= tau[j]);
+  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+#pragma unroll
+  for (int i = 0; i < 12; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+  }
+}
+
 __device__ __forceinline__ float max16(const f32x16& v) {
   float m0 = __builtin_fmaxf(__builtin_fmaxf(v[0], v[1]), v[2]);
   float m1 = __builtin_fmaxf(__builtin_fmaxf(v[3], v[4]), v[5]);
@@ -433,53 +460,135 @@ __device__ __forceinline__ int32_t load_qcols(QCols& c, const IndexCtx& ctx, con
 // scores into the wave's LDS entry buffer (slots from a ballot, no atomics).
 // expand_entries then turns buffered entries into candidates with one entry
 // per lane, appending to the query's LDS list (global memory once full).
-constexpr int kEnt = 64;            // buffered (lane, group) entries per wave
 
+template <int W, int E>
 struct LowPassLds {
+  static constexpr int kEntries = E;                  // buffered entries per wave
   int cnt[kQueriesPerWg];                             // candidates per query
   uint2 buf[kQueriesPerWg * kCapL];                   // (score bits, bucket)
   float tau[kQueriesPerWg];
-  float ent[4][kEnt][16];                             // buffered scores
-  uint32_t meta[4][kEnt];                             // tile << 8 | half << 7 | query
+  float ent[W][E][16];                                // buffered scores per wave
+  uint32_t meta[W][E];                                // tile << 8 | half << 7 | query
 };
 
-__device__ __forceinline__ void lds_append(LowPassLds& L, const IndexWs& ws, int cap, int ql,
-                                           int64_t qi, float s, int32_t g) {
-  const uint2 e = make_uint2(__float_as_uint(s), (uint32_t)g);
-  const int slot = atomicAdd(&L.cnt[ql], 1);
-  if (slot < kCapL) {
-    L.buf[ql * kCapL + slot] = e;
-  } else {
-    const int gs = atomicAdd(&ws.cand_cnt[qi], 1);
-    if (gs < cap) ws.cand[qi * cap + gs] = e;
+template <class LL>
+__device__ __forceinline__ void lowpass_buffer_masks(LL& L, const IndexCtx& ctx, const IndexWs& ws,
+                                                     const f32x16 (&acc)[4], const float (&tau)[4],
+                                                     const uint64_t (&mks)[4], int32_t t, int64_t q0,
+                                                     int wave, int lane, int col, int half,
+                                                     int& ecnt);
+
+// append the rows of `bits` (bit r: row r of 16) with one LDS reservation
+template <class LL>
+__device__ __forceinline__ void lds_append16(LL& L, const IndexWs& ws, int cap, int ql, int64_t qi,
+                                             const float (&v)[16], uint32_t bits, int32_t gb) {
+  const int c = __popc(bits);
+  int slot = atomicAdd(&L.cnt[ql], c);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    if ((bits >> r) & 1u) {
+      const uint2 e = make_uint2(__float_as_uint(v[r]), (uint32_t)(gb + 8 * (r >> 2) + (r & 3)));
+      if (slot < kCapL) {
+        L.buf[ql * kCapL + slot] = e;
+      } else {
+        const int gs = atomicAdd(&ws.cand_cnt[qi], 1);
+        if (gs < cap) ws.cand[qi * cap + gs] = e;
+      }
+      ++slot;
+    }
   }
 }
 
-// one buffered entry per lane: its 16 rows against the query's tau and ne
-__device__ __forceinline__ void expand_entries(LowPassLds& L, const IndexCtx& ctx, const IndexWs& ws,
+// buffered entries, one per lane at a time: 16 rows against the query's tau and ne
+template <class LL>
+__device__ __forceinline__ void expand_entries(LL& L, const IndexCtx& ctx, const IndexWs& ws,
                                                int64_t q0, int wave, int lane, int n) {
   __builtin_amdgcn_wave_barrier();
-  if (lane < n) {
-    const uint32_t meta = L.meta[wave][lane];
+  for (int e = lane; e < n; e += 64) {
+    const uint32_t meta = L.meta[wave][e];
     const int ql = meta & 127, h = (meta >> 7) & 1;
     const int32_t gb = (int32_t)(meta >> 8) * kTile + 4 * h;
     const int64_t qi = q0 + ql;
     const float tau = L.tau[ql];
     const int32_t ne = (int32_t)n_eligible(ctx.q_start + qi);
-    const float4* src = reinterpret_cast<const float4*>(L.ent[wave][lane]);
+    const float4* src = reinterpret_cast<const float4*>(L.ent[wave][e]);
     float v[16];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float4 x = src[i];
       v[4 * i] = x.x; v[4 * i + 1] = x.y; v[4 * i + 2] = x.z; v[4 * i + 3] = x.w;
     }
+    uint32_t bits = 0;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int32_t g = gb + 8 * (r >> 2) + (r & 3);
-      if (v[r] >= tau && g < ne) lds_append(L, ws, ctx.cap, ql, qi, v[r], g);
+      bits |= (uint32_t)((v[r] >= tau) & (g < ne)) << r;
     }
+    if (bits) lds_append16(L, ws, ctx.cap, ql, qi, v, bits, gb);
   }
   __builtin_amdgcn_wave_barrier();
+}
+
+template <class LL>
+__device__ __forceinline__ void lowpass_buffer(LL& L, const IndexCtx& ctx, const IndexWs& ws,
+                                               const f32x16 (&acc)[4], const float (&tau)[4],
+                                               int32_t t, int64_t q0, int wave, int lane, int col,
+                                               int half, int& ecnt) {
+  uint64_t mks[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) mks[j] = __ballot(max16(acc[j]) >= tau[j]);
+  lowpass_buffer_masks(L, ctx, ws, acc, tau, mks, t, q0, wave, lane, col, half, ecnt);
+}
+
+// the same with the per-group ballots of max16(acc[j]) >= tau[j] given
+template <class LL>
+__device__ __forceinline__ void lowpass_buffer_masks(LL& L, const IndexCtx& ctx, const IndexWs& ws,
+                                                     const f32x16 (&acc)[4], const float (&tau)[4],
+                                                     const uint64_t (&mks)[4], int32_t t, int64_t q0,
+                                                     int wave, int lane, int col, int half,
+                                                     int& ecnt) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint64_t mk = mks[j];
+    if (mk == 0) continue;
+    const int n = __popcll(mk);
+    if (ecnt + n <= LL::kEntries) {
+      if ((mk >> lane) & 1ull) {
+        const int e = ecnt + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u));
+        float4* dst = reinterpret_cast<float4*>(L.ent[wave][e]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          dst[i] = make_float4(acc[j][4 * i], acc[j][4 * i + 1], acc[j][4 * i + 2], acc[j][4 * i + 3]);
+        L.meta[wave][e] = ((uint32_t)t << 8) | ((uint32_t)half << 7) | (uint32_t)(32 * j + col);
+      }
+      ecnt += n;
+    } else if ((mk >> lane) & 1ull) {
+      // the buffer is full: append this lane's passing rows directly
+      const int ql = 32 * j + col;
+      const int64_t qi = q0 + ql;
+      const int32_t ne = (int32_t)n_eligible(ctx.q_start + qi);
+      const int32_t gb = t * kTile + 4 * half;
+      float v[16];
+      uint32_t bits = 0;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        v[r] = acc[j][r];
+        bits |= (uint32_t)((v[r] >= tau[j]) & (gb + 8 * (r >> 2) + (r & 3) < ne)) << r;
+      }
+      if (bits) lds_append16(L, ws, ctx.cap, ql, qi, v, bits, gb);
+    }
+  }
+}
+
+// after a tile's epilogue (its accumulators are dead): expand when half full
+template <class LL>
+__device__ __forceinline__ void lowpass_drain(LL& L, const IndexCtx& ctx, const IndexWs& ws,
+                                              int64_t q0, int wave, int lane, int& ecnt, bool all) {
+  if (ecnt > (all ? 0 : LL::kEntries / 2)) {
+    expand_entries(L, ctx, ws, q0, wave, lane, ecnt);
+    ecnt = 0;
+  }
 }
 
 // High-pass epilogue (many candidates, or every eligible bucket kept): per
@@ -518,69 +627,26 @@ __device__ __forceinline__ void highpass_tile(const f32x16 (&acc)[4], int32_t t,
   }
 }
 
-__global__ __launch_bounds__(256, 2) void k_score_filter_q128(IndexCtx ctx, IndexWs ws,
-                                                              int seg_tiles) {
-  __shared__ __attribute__((aligned(16))) LowPassLds L;
+// High-pass scoring: query tiles whose queries keep a large share of their
+// eligible buckets (or all of them).  128 queries per workgroup, each wave
+// scores its own tiles against all of them; grid.x = query tiles [0, x),
+// grid.y = bucket segments.
+__global__ __launch_bounds__(256, 2) void k_score_highpass(IndexCtx ctx, IndexWs ws,
+                                                           int seg_tiles) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
   const int64_t q0 = (int64_t)blockIdx.x * kQueriesPerWg;
   QCols qc;
   const int32_t nmax = load_qcols(qc, ctx, ws.tau, q0, col);
-  int32_t nmin = 0x7fffffff;
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    if (q0 + 32 * j + col < ctx.n) nmin = qc.ne[j] < nmin ? qc.ne[j] : nmin;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const int32_t o = __shfl_xor(nmin, off, 64);
-    nmin = o < nmin ? o : nmin;
-  }
-  nmin = __builtin_amdgcn_readfirstlane(nmin);
   const int32_t t0 = (int32_t)blockIdx.y * seg_tiles;
   int32_t t1 = (nmax + kTile - 1) / kTile;
   if (t1 > t0 + seg_tiles) t1 = t0 + seg_tiles;
   if (t0 >= t1) return;                                  // uniform over the workgroup
-  // low-pass when every query expects at most kCapL / 4 candidates here
-  const bool lowpass = nmin > ctx.cap &&
-                       (int64_t)seg_tiles * kTile * 2 * ctx.top_b <= (int64_t)(kCapL / 4) * nmin;
-  if (tid < kQueriesPerWg) {
-    L.cnt[tid] = 0;
-    L.tau[tid] = q0 + tid < ctx.n ? ws.tau[q0 + tid] : 3.0e38f;
-  }
   Q128 q;
   load_q128(q, ws.yhat, q0, ctx.n, col, half);
   const void* cent = ctx.cent[0];
   const int32_t tl = t1 - 1;
-  __syncthreads();
-
-  int ecnt = 0;                                          // wave-uniform
-  auto epilogue = [&](const f32x16 (&acc)[4], int32_t t) {
-    if (!lowpass) {
-      highpass_tile(acc, t, qc, lane, col, half, ws, ctx.cap);
-      return;
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint64_t mk = __ballot(max16(acc[j]) >= qc.tau[j]);
-      if (mk == 0) continue;
-      const int n = __popcll(mk);
-      if (ecnt + n > kEnt) {
-        expand_entries(L, ctx, ws, q0, wave, lane, ecnt);
-        ecnt = 0;
-      }
-      if ((mk >> lane) & 1ull) {
-        const int e = ecnt + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32),
-                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u));
-        float4* dst = reinterpret_cast<float4*>(L.ent[wave][e]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          dst[i] = make_float4(acc[j][4 * i], acc[j][4 * i + 1], acc[j][4 * i + 2], acc[j][4 * i + 3]);
-        L.meta[wave][e] = ((uint32_t)t << 8) | ((uint32_t)half << 7) | (uint32_t)(32 * j + col);
-      }
-      ecnt += n;
-    }
-  };
   // two register buffers: each is reloaded (clamped to the last tile, so the
   // number of loads in flight is the same on every path) as soon as its
   // MFMAs have been issued, before the epilogue of the tile it held
@@ -593,12 +659,62 @@ __global__ __launch_bounds__(256, 2) void k_score_filter_q128(IndexCtx ctx, Inde
     f32x16 acc[4];
     mfma_q128(acc, ra, q);
     load_atile(ra, cent, (int64_t)(t + 8 < tl ? t + 8 : tl) * kTile + col, half);
-    epilogue(acc, t);
+    highpass_tile(acc, t, qc, lane, col, half, ws, ctx.cap);
     mfma_q128(acc, rb, q);
     load_atile(rb, cent, (int64_t)(t + 12 < tl ? t + 12 : tl) * kTile + col, half);
-    if (t + 4 < t1) epilogue(acc, t + 4);
+    if (t + 4 < t1) highpass_tile(acc, t + 4, qc, lane, col, half, ws, ctx.cap);
   }
-  if (ecnt) expand_entries(L, ctx, ws, q0, wave, lane, ecnt);
+}
+
+// Low-pass scoring: query tiles whose queries keep a small share of their
+// eligible buckets.  Same tile loop as the high-pass kernel; the epilogue
+// buffers flagged lanes (lowpass_buffer) and expands the buffer after a
+// tile when it is half full, so the expansion never runs while a tile's
+// accumulators are live.  grid.x = query tiles from qt0 on, grid.y =
+// bucket segments.
+__global__ __launch_bounds__(256, 2) void k_score_lowpass(IndexCtx ctx, IndexWs ws, int seg_tiles,
+                                                          int qt0) {
+  __shared__ __attribute__((aligned(16))) LowPassLds<4, 64> L;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31, half = lane >> 5;
+  const int64_t q0 = (int64_t)(qt0 + blockIdx.x) * kQueriesPerWg;
+  QCols qc;
+  const int32_t nmax = load_qcols(qc, ctx, ws.tau, q0, col);
+  const int32_t t0 = (int32_t)blockIdx.y * seg_tiles;
+  int32_t t1 = (nmax + kTile - 1) / kTile;
+  if (t1 > t0 + seg_tiles) t1 = t0 + seg_tiles;
+  if (t0 >= t1) return;                                  // uniform over the workgroup
+  if (tid < kQueriesPerWg) {
+    L.cnt[tid] = 0;
+    L.tau[tid] = q0 + tid < ctx.n ? ws.tau[q0 + tid] : 3.0e38f;
+  }
+  Q128 q;
+  load_q128(q, ws.yhat, q0, ctx.n, col, half);
+  const void* cent = ctx.cent[0];
+  const int32_t tl = t1 - 1;
+  __syncthreads();
+  int ecnt = 0;                                          // wave-uniform
+  uint4 ra[4], rb[4];
+  int32_t t = t0 + wave;
+  load_atile(ra, cent, (int64_t)(t < tl ? t : tl) * kTile + col, half);
+  __builtin_amdgcn_sched_barrier(0);   // keep ra's loads older than rb's
+  load_atile(rb, cent, (int64_t)(t + 4 < tl ? t + 4 : tl) * kTile + col, half);
+  for (; t < t1; t += 8) {
+    f32x16 acc[4];
+    uint64_t mks[4];
+    mfma_q128_masks(acc, mks, ra, q, qc.tau);
+    load_atile(ra, cent, (int64_t)(t + 8 < tl ? t + 8 : tl) * kTile + col, half);
+    lowpass_buffer_masks(L, ctx, ws, acc, qc.tau, mks, t, q0, wave, lane, col, half, ecnt);
+    lowpass_drain(L, ctx, ws, q0, wave, lane, ecnt, false);
+    mfma_q128_masks(acc, mks, rb, q, qc.tau);
+    load_atile(rb, cent, (int64_t)(t + 12 < tl ? t + 12 : tl) * kTile + col, half);
+    if (t + 4 < t1) {
+      lowpass_buffer_masks(L, ctx, ws, acc, qc.tau, mks, t + 4, q0, wave, lane, col, half, ecnt);
+      lowpass_drain(L, ctx, ws, q0, wave, lane, ecnt, false);
+    }
+  }
+  lowpass_drain(L, ctx, ws, q0, wave, lane, ecnt, true);
   __syncthreads();
   // flush: two threads per query
   const int ql = tid >> 1, sub = tid & 1;
@@ -1537,8 +1653,24 @@ hipError_t launch_score_filter(const IndexCtx& ctx, const IndexWs& ws, int dtype
     int64_t seg = 16;
     while (seg * 2 * kTile <= seg_buckets && seg < 512) seg *= 2;
     if (seg_buckets < 16 * kTile) seg = 128;
-    dim3 grid((unsigned)query_tiles(ctx), (unsigned)((max_tiles + seg - 1) / seg));
-    hipLaunchKernelGGL(k_score_filter_q128, grid, dim3(256), 0, s, ctx, ws, (int)seg);
+    // query tiles [x_lp, qt) are low-pass (ne grows with the position, so the
+    // first query of a tile has its smallest ne); earlier tiles are high-pass
+    const int64_t qt = query_tiles(ctx);
+    const int64_t nseg = (max_tiles + seg - 1) / seg;
+    int64_t x_lp = qt;
+    for (int64_t x = 0; x < qt; ++x) {
+      const int64_t nmin = ((ctx.q_start + x * kQueriesPerWg) / kBlock) * kBuckets;
+      if (nmin > ctx.cap && seg * kTile * 2 * (int64_t)ctx.top_b <= (int64_t)(kCapL / 4) * nmin) {
+        x_lp = x;
+        break;
+      }
+    }
+    if (x_lp > 0)
+      hipLaunchKernelGGL(k_score_highpass, dim3((unsigned)x_lp, (unsigned)nseg), dim3(256), 0, s,
+                         ctx, ws, (int)seg);
+    if (x_lp < qt)
+      hipLaunchKernelGGL(k_score_lowpass, dim3((unsigned)(qt - x_lp), (unsigned)nseg), dim3(256),
+                         0, s, ctx, ws, (int)seg, (int)x_lp);
     return hipGetLastError();
   }
   if (ctx.per_seq && dtype == LSA_BF16) {
