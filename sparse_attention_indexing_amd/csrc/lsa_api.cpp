@@ -242,6 +242,9 @@ int run_selection(const IndexCtx& ctx, const IndexWs& ws, const lsa_params* p,
                   int32_t* ranked, hipStream_t s) {
   const int dt = p->index_dtype;
   hipError_t e;
+  // exact selection mode of the expansion kernel: 0 = tree candidates as they
+  // are, 1 = redo a query whose flat candidate list is unusable, 2 = always
+  int exact_mode = 0;
   if (tree) {
     e = launch_tree_search(ctx, *tree, ws, dt, s);
     if (e != hipSuccess) return LSA_ERR_HIP;
@@ -252,10 +255,9 @@ int run_selection(const IndexCtx& ctx, const IndexWs& ws, const lsa_params* p,
       e = launch_score_filter(ctx, ws, dt, max_elig / 32, s);
       if (e != hipSuccess) return LSA_ERR_HIP;
     }
-    e = launch_exact_select(ctx, ws, dt, p->exact_select, s);
-    if (e != hipSuccess) return LSA_ERR_HIP;
+    exact_mode = p->exact_select ? 2 : 1;
   }
-  e = launch_select_expand(ctx, ws, idx, count, ranked, s);
+  e = launch_select_expand(ctx, ws, idx, count, ranked, dt, exact_mode, s);
   return hip_status(e);
 }
 

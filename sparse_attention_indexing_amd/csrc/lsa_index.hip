@@ -1108,29 +1108,23 @@ __device__ __forceinline__ int block_scan_excl(int v, int* wsum, int* total) {
   return base + x - v;
 }
 
-// One workgroup per query.  Re-does queries whose candidate list is unusable
-// (or every query when `force`): exact B-th largest score by 4 radix passes
-// of 8 bits over the order-preserving integer image of the fp32 score, then
-// emits every bucket above it and, among buckets equal to it, the lowest.
+// Exact top-B of one query, for a workgroup whose candidate list is unusable
+// (fewer than B or more than `cap` candidates) or when exact selection is
+// forced: the B-th largest score by 4 radix passes of 8 bits over the
+// order-preserving integer image of the fp32 score, then every bucket above
+// it and, among buckets equal to it, the lowest.  Writes raw score bits to
+// skey[] and buckets to sbkt[] (LDS) and returns the count (min(B, ne)).
 template <int DT>
-__global__ __launch_bounds__(256) void k_exact_select(IndexCtx ctx, IndexWs ws, int force) {
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t s_prefix, s_want;
-  __shared__ int wsum[4];
-  __shared__ int s_out;
+__device__ int exact_select_lds(const IndexCtx& ctx, const IndexWs& ws, int64_t qi, int64_t ne,
+                                int64_t beff, uint32_t* skey, uint32_t* sbkt, uint32_t* hist,
+                                uint32_t* s_prefix, uint32_t* s_want, int* wsum, int* s_out) {
   const int tid = threadIdx.x;
-  const int64_t qi = blockIdx.x;
-  if (qi >= ctx.n) return;
-  const int64_t ne = n_eligible(qpos(ctx, qi));
-  const int64_t beff = ne < ctx.top_b ? ne : ctx.top_b;
-  const int cnt = ws.cand_cnt[qi];
-  if (!force && cnt >= beff && cnt <= ctx.cap) return;
   const void* cent = qcent(ctx, qi);
   float yq[kLatent];
   load_yq<DT>(yq, ws.yhat, qi);
   uint32_t prefix = 0, mask = 0;
   uint32_t want = (uint32_t)beff;
-  if (tid == 0) { s_out = 0; }
+  if (tid == 0) *s_out = 0;
   if (beff > 0) {
     for (int shift = 24; shift >= 0; shift -= 8) {
       hist[tid] = 0;
@@ -1144,21 +1138,19 @@ __global__ __launch_bounds__(256) void k_exact_select(IndexCtx ctx, IndexWs ws, 
         uint32_t cum = 0;
         for (int b = 255; b >= 0; --b) {
           if (cum + hist[b] >= want) {
-            s_prefix = prefix | ((uint32_t)b << shift);
-            s_want = want - cum;
+            *s_prefix = prefix | ((uint32_t)b << shift);
+            *s_want = want - cum;
             break;
           }
           cum += hist[b];
         }
       }
       __syncthreads();
-      prefix = s_prefix;
-      want = s_want;
+      prefix = *s_prefix;
+      want = *s_want;
       mask |= 255u << shift;
       __syncthreads();
     }
-    // emit: everything above the threshold key, and the `want` lowest buckets equal to it
-    uint2* cand = ws.cand + qi * (int64_t)ctx.cap;
     int eq_base = 0;
     for (int64_t g0 = 0; g0 < ne; g0 += 256) {
       const int64_t g = g0 + tid;
@@ -1170,17 +1162,15 @@ __global__ __launch_bounds__(256) void k_exact_select(IndexCtx ctx, IndexWs ws, 
       int eq_tot;
       const int eq_rank = eq_base + block_scan_excl(eq, wsum, &eq_tot);
       if (gt || (eq && eq_rank < (int)want)) {
-        const int slot = atomicAdd(&s_out, 1);
-        if (slot < ctx.cap) cand[slot] = make_uint2(__float_as_uint(s), (uint32_t)g);
+        const int slot = atomicAdd(s_out, 1);
+        if (slot < ctx.cap) { skey[slot] = __float_as_uint(s); sbkt[slot] = (uint32_t)g; }
       }
       eq_base += eq_tot;
     }
   }
   __syncthreads();
-  if (tid == 0) {
-    ws.cand_cnt[qi] = (int)beff;
-    ws.status[qi] = 1;
-  }
+  if (tid == 0) ws.status[qi] = 1;
+  return (int)beff;
 }
 
 // ------------------------------------------------------------------ tree search
@@ -1426,8 +1416,10 @@ __device__ uint32_t weighted_select(int c, KeyF key, FiltF filt, const uint8_t* 
 // buckets tied at S* are walked in bucket order, the crossing one is cut.
 // Every candidate list holds the exact top-B (or every eligible bucket), so
 // the crossing lies inside it.  The far keys are then radix-sorted.
+template <int DT>
 __global__ __launch_bounds__(256) void k_select_expand(IndexCtx ctx, IndexWs ws, int32_t* idx,
-                                                       int32_t* count, int32_t* ranked) {
+                                                       int32_t* count, int32_t* ranked,
+                                                       int exact_mode) {
   extern __shared__ uint64_t sm[];
   const int cap = ctx.cap;
   const int kf = ctx.k > 1 ? ctx.k : 1;
@@ -1445,16 +1437,33 @@ __global__ __launch_bounds__(256) void k_select_expand(IndexCtx ctx, IndexWs ws,
   if (qi >= ctx.n) return;
   const int64_t p = qpos(ctx, qi);
   const uint32_t* mem = qmem(ctx, qi);
-  int c = ws.cand_cnt[qi];
-  c = c < cap ? c : cap;
-  const uint2* cand = ws.cand + qi * (int64_t)cap;
   const int64_t s_end = p + 1 < ctx.n_sink ? p + 1 : ctx.n_sink;
   const int64_t w_start = p - ctx.window + 1 > 0 ? p - ctx.window + 1 : 0;
-  // candidates and their far-key contributions (members outside the near set)
+  // candidates (raw score bits, bucket) into LDS: from the scoring pass, or
+  // from the exact selection when that list is unusable (exact_mode 1) or
+  // always (exact_mode 2); tree candidates are taken as they are (mode 0)
+  int c = ws.cand_cnt[qi];
+  {
+    const int64_t ne = n_eligible(p);
+    const int64_t beff = ne < ctx.top_b ? ne : ctx.top_b;
+    if (exact_mode == 2 || (exact_mode == 1 && (c < beff || c > cap))) {
+      c = exact_select_lds<DT>(ctx, ws, qi, ne, beff, skey, sbkt, &hist[0][0], &s_prefix, &s_want,
+                               wsum, &s_total);
+    } else {
+      c = c < cap ? c : cap;
+      const uint2* cand = ws.cand + qi * (int64_t)cap;
+      for (int i = tid; i < c; i += 256) {
+        const uint2 e = cand[i];
+        skey[i] = e.x;
+        sbkt[i] = e.y;
+      }
+    }
+  }
+  __syncthreads();
+  // far-key contributions (members outside the near set)
   int my_w = 0;
   for (int i = tid; i < c; i += 256) {
-    const uint2 e = cand[i];
-    const uint32_t g = e.y;
+    const uint32_t g = sbkt[i];
     const uint32_t m = mem[g];
     const int64_t kb = (int64_t)(g / kBuckets) * kBlock;
     int ci = 0;
@@ -1469,8 +1478,7 @@ __global__ __launch_bounds__(256) void k_select_expand(IndexCtx ctx, IndexWs ws,
         }
       }
     }
-    skey[i] = f32_orderable(__uint_as_float(e.x));
-    sbkt[i] = g;
+    skey[i] = f32_orderable(__uint_as_float(skey[i]));
     contrib[i] = (uint8_t)ci;
     my_w += ci;
   }
@@ -1497,9 +1505,19 @@ __global__ __launch_bounds__(256) void k_select_expand(IndexCtx ctx, IndexWs ws,
     prefix = weighted_select(c, [&](int i) { return skey[i]; }, [&](int) { return true; },
                              contrib, want, hist, &s_prefix, &s_want);
     const uint32_t sstar = prefix;
-    gstar_key = weighted_select(c, [&](int i) { return 0xFFFFFFFFu - sbkt[i]; },
-                                [&](int i) { return skey[i] == sstar; }, contrib, want, hist,
-                                &s_prefix, &s_want);
+    // buckets tied at S*: almost always one, which is then the cut bucket
+    int n_eq = 0;
+    for (int i = tid; i < c; i += 256)
+      if (skey[i] == sstar && contrib[i]) { ++n_eq; s_prefix = 0xFFFFFFFFu - sbkt[i]; }
+    int eq_tot;
+    (void)block_scan_excl(n_eq, wsum, &eq_tot);
+    if (eq_tot == 1) {
+      gstar_key = s_prefix;
+    } else {
+      gstar_key = weighted_select(c, [&](int i) { return 0xFFFFFFFFu - sbkt[i]; },
+                                  [&](int i) { return skey[i] == sstar; }, contrib, want, hist,
+                                  &s_prefix, &s_want);
+    }
     if (tid == 0) s_trunc_m = (int)want;
   }
   __syncthreads();
@@ -1686,15 +1704,6 @@ hipError_t launch_score_filter(const IndexCtx& ctx, const IndexWs& ws, int dtype
   return hipGetLastError();
 }
 
-hipError_t launch_exact_select(const IndexCtx& ctx, const IndexWs& ws, int dtype, int force,
-                               hipStream_t s) {
-  if (ctx.n <= 0) return hipSuccess;
-  dim3 grid((unsigned)ctx.n);
-  if (dtype == LSA_BF16) hipLaunchKernelGGL(k_exact_select<LSA_BF16>, grid, dim3(256), 0, s, ctx, ws, force);
-  else hipLaunchKernelGGL(k_exact_select<LSA_F32>, grid, dim3(256), 0, s, ctx, ws, force);
-  return hipGetLastError();
-}
-
 static void allow_large_lds(const void* fn);
 
 hipError_t launch_tree_search(const IndexCtx& ctx, const TreeCtx& tc, const IndexWs& ws,
@@ -1728,13 +1737,22 @@ static int pow2_ceil_host(int x) {
 }
 
 hipError_t launch_select_expand(const IndexCtx& ctx, const IndexWs& ws, int32_t* idx,
-                                int32_t* count, int32_t* ranked, hipStream_t s) {
+                                int32_t* count, int32_t* ranked, int dtype, int exact_mode,
+                                hipStream_t s) {
   if (ctx.n <= 0) return hipSuccess;
   const size_t smem = (size_t)ctx.cap * 9 + (size_t)(ctx.k > 1 ? ctx.k : 1) * 8;
   static bool once = false;
-  if (!once) { allow_large_lds(reinterpret_cast<const void*>(k_select_expand)); once = true; }
-  hipLaunchKernelGGL(k_select_expand, dim3((unsigned)ctx.n), dim3(256), smem, s, ctx, ws, idx,
-                     count, ranked);
+  if (!once) {
+    allow_large_lds(reinterpret_cast<const void*>(k_select_expand<LSA_BF16>));
+    allow_large_lds(reinterpret_cast<const void*>(k_select_expand<LSA_F32>));
+    once = true;
+  }
+  if (dtype == LSA_BF16)
+    hipLaunchKernelGGL(k_select_expand<LSA_BF16>, dim3((unsigned)ctx.n), dim3(256), smem, s, ctx, ws,
+                       idx, count, ranked, exact_mode);
+  else
+    hipLaunchKernelGGL(k_select_expand<LSA_F32>, dim3((unsigned)ctx.n), dim3(256), smem, s, ctx, ws,
+                       idx, count, ranked, exact_mode);
   return hipGetLastError();
 }
 

@@ -156,12 +156,11 @@ hipError_t launch_qnorm(const float* y, int64_t n, void* yhat, int dtype, uint32
 hipError_t launch_thresh(const IndexCtx& ctx, const IndexWs& ws, int dtype, hipStream_t s);
 hipError_t launch_score_filter(const IndexCtx& ctx, const IndexWs& ws, int dtype,
                                int64_t max_tiles, hipStream_t s);
-hipError_t launch_exact_select(const IndexCtx& ctx, const IndexWs& ws, int dtype, int force,
-                               hipStream_t s);
 hipError_t launch_tree_search(const IndexCtx& ctx, const TreeCtx& tc, const IndexWs& ws,
                               int dtype, hipStream_t s);
 hipError_t launch_select_expand(const IndexCtx& ctx, const IndexWs& ws, int32_t* idx,
-                                int32_t* count, int32_t* ranked, hipStream_t s);
+                                int32_t* count, int32_t* ranked, int dtype, int exact_mode,
+                                hipStream_t s);
 
 hipError_t launch_attention(const void* q, const void* k, const void* v, int32_t B, int64_t Tq,
                             int64_t Tmax, int32_t Hq, int32_t Hkv, const int32_t* idx,
