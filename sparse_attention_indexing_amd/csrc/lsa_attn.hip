@@ -555,17 +555,35 @@ __global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ 
   const float* ob = ws;
   const float* mb = ws + rows * splits * Hq * kHeadDim;
   const float* lb = mb + rows * splits * Hq;
+  // splits in chunks of 16 whose loads are all issued before any use
   float M = -__builtin_inff();
-  for (int s = 0; s < splits; ++s) M = fmaxf(M, mb[(row * splits + s) * Hq + h]);
+  for (int s0 = 0; s0 < splits; s0 += 16) {
+    float mm[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      mm[j] = s0 + j < splits ? mb[(row * splits + s0 + j) * Hq + h] : -__builtin_inff();
+#pragma unroll
+    for (int j = 0; j < 16; ++j) M = fmaxf(M, mm[j]);
+  }
   float num = 0.f, den = 0.f;
   if (M != -__builtin_inff()) {
-    for (int s = 0; s < splits; ++s) {
-      const int64_t slot = row * splits + s;
-      const float ms = mb[slot * Hq + h];
-      if (ms == -__builtin_inff()) continue;
-      const float w = __expf(ms - M);
-      num = __builtin_fmaf(w, ob[(slot * Hq + h) * kHeadDim + d], num);
-      den = __builtin_fmaf(w, lb[slot * Hq + h], den);
+    for (int s0 = 0; s0 < splits; s0 += 16) {
+      float mm[16], oo[16], ll[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const bool ok = s0 + j < splits;
+        const int64_t slot = row * splits + (ok ? s0 + j : 0);
+        mm[j] = ok ? mb[slot * Hq + h] : -__builtin_inff();
+        oo[j] = ob[(slot * Hq + h) * kHeadDim + d];
+        ll[j] = lb[slot * Hq + h];
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        // a split with no keys has m = -inf and contributes nothing
+        const float w = mm[j] == -__builtin_inff() ? 0.f : __expf(mm[j] - M);
+        num = __builtin_fmaf(w, oo[j], num);
+        den = __builtin_fmaf(w, ll[j], den);
+      }
     }
   }
   const float r = den > 0.f ? num / den : 0.f;

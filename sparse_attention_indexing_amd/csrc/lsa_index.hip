@@ -1296,44 +1296,62 @@ __global__ __launch_bounds__(64) void k_tree_search(IndexCtx ctx, TreeCtx tc, In
 
 // ------------------------------------------------------------------ select + expand
 // Lanes of the wave whose 8-bit digit equals this lane's (among `active`).
+// lanes of `active` whose digit d (DB bits) equals this lane's
+template <int DB>
 __device__ __forceinline__ uint64_t match_digit(uint32_t d, uint64_t active) {
   uint64_t peers = active;
 #pragma unroll
-  for (int bit = 0; bit < 8; ++bit) {
+  for (int bit = 0; bit < DB; ++bit) {
     const uint64_t m = __ballot((d >> bit) & 1u);
     peers &= ((d >> bit) & 1u) ? m : ~m;
   }
   return peers;
 }
 
-// Stable LSD radix sort (8-bit digits) of n non-negative int32 keys in LDS,
+// Stable LSD radix sort (DB-bit digits) of n non-negative int32 keys in LDS,
 // ascending.  Wave w owns the contiguous chunk [w*ch, (w+1)*ch); `tmp` is a
-// second buffer of n ints, `cnt` 4 x 256 counters.  Returns the buffer that
-// holds the result.
-__device__ int32_t* radix_sort_i32(int32_t* keys, int32_t* tmp, int n, int max_key,
-                                   uint32_t (*cnt)[256]) {
+// second buffer of n ints, `cnt` 4 x 2^DB counters (one row per wave); the
+// scatter ranks lanes with equal digits by ballots, which keeps it stable.
+// Returns the buffer that holds the result.
+template <int DB>
+__device__ int32_t* radix_sort_i32(int32_t* keys, int32_t* tmp, int n, int max_key, uint32_t* cnt) {
+  constexpr int NB = 1 << DB;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ch = (n + 3) / 4;
   const int c0 = wave * ch;
   const int c1 = (c0 + ch) < n ? (c0 + ch) : n;
   int bits = 0;
-  while (bits < 31 && (max_key >> bits) != 0) bits += 8;
-  for (int shift = 0; shift < bits; shift += 8) {
-    for (int i = tid; i < 4 * 256; i += 256) (&cnt[0][0])[i] = 0;
+  while (bits < 31 && (max_key >> bits) != 0) bits += DB;
+  __shared__ int wsum_r[4];
+  for (int shift = 0; shift < bits; shift += DB) {
+    for (int i = tid; i < 4 * NB; i += 256) cnt[i] = 0;
     __syncthreads();
-    for (int e = c0 + lane; e < c1; e += 64) atomicAdd(&cnt[wave][(keys[e] >> shift) & 255], 1u);
+    uint32_t* my = cnt + wave * NB;
+    for (int e = c0 + lane; e < c1; e += 64) atomicAdd(&my[((uint32_t)keys[e] >> shift) & (NB - 1)], 1u);
     __syncthreads();
     {
-      // digit-major, wave-minor exclusive offsets
-      const int d = tid;
-      uint32_t tot = 0, pre[4];
+      // digit-major, wave-minor exclusive offsets; thread t owns digits
+      // t * NB / 256 .. (t + 1) * NB / 256 - 1
+      constexpr int PD = NB / 256;
+      uint32_t tot = 0;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) { pre[w] = tot; tot += cnt[w][d]; }
-      __shared__ int wsum_r[4];
-      int tmp_tot;
-      const int start = block_scan_excl((int)tot, wsum_r, &tmp_tot);
+      for (int q = 0; q < PD; ++q) {
+        const int d = tid * PD + q;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) cnt[w][d] = (uint32_t)start + pre[w];
+        for (int w = 0; w < 4; ++w) tot += cnt[w * NB + d];
+      }
+      int all;
+      uint32_t run = (uint32_t)block_scan_excl((int)tot, wsum_r, &all);
+#pragma unroll
+      for (int q = 0; q < PD; ++q) {
+        const int d = tid * PD + q;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t v = cnt[w * NB + d];
+          cnt[w * NB + d] = run;
+          run += v;
+        }
+      }
     }
     __syncthreads();
     for (int e0 = c0; e0 < c1; e0 += 64) {
@@ -1341,13 +1359,13 @@ __device__ int32_t* radix_sort_i32(int32_t* keys, int32_t* tmp, int n, int max_k
       const bool ok = e < c1;
       const uint64_t active = __ballot(ok);
       const int32_t key = ok ? keys[e] : 0;
-      const uint32_t d = ((uint32_t)key >> shift) & 255u;
-      const uint64_t peers = match_digit(d, active);
+      const uint32_t d = ((uint32_t)key >> shift) & (NB - 1);
+      const uint64_t peers = match_digit<DB>(d, active);
       if (ok) {
         const int rank = __popcll(peers & ((1ull << lane) - 1ull));
-        const uint32_t base = cnt[wave][d];
+        const uint32_t base = my[d];
         tmp[base + rank] = key;
-        if (rank == 0) cnt[wave][d] = base + (uint32_t)__popcll(peers);
+        if (rank == 0) my[d] = base + (uint32_t)__popcll(peers);
       }
     }
     __syncthreads();
@@ -1416,7 +1434,10 @@ __device__ uint32_t weighted_select(int c, KeyF key, FiltF filt, const uint8_t* 
 // buckets tied at S* are walked in bucket order, the crossing one is cut.
 // Every candidate list holds the exact top-B (or every eligible bucket), so
 // the crossing lies inside it.  The far keys are then radix-sorted.
-template <int DT>
+// PER = candidate slots per thread (cap / 256): thread t owns candidates
+// t, t + 256, ..., whose member words stay in registers from the contribution
+// count to the emission.
+template <int DT, int PER>
 __global__ __launch_bounds__(256) void k_select_expand(IndexCtx ctx, IndexWs ws, int32_t* idx,
                                                        int32_t* count, int32_t* ranked,
                                                        int exact_mode) {
@@ -1452,29 +1473,51 @@ __global__ __launch_bounds__(256) void k_select_expand(IndexCtx ctx, IndexWs ws,
     } else {
       c = c < cap ? c : cap;
       const uint2* cand = ws.cand + qi * (int64_t)cap;
-      for (int i = tid; i < c; i += 256) {
-        const uint2 e = cand[i];
-        skey[i] = e.x;
-        sbkt[i] = e.y;
+      uint2 e[PER];
+#pragma unroll
+      for (int jj = 0; jj < PER; ++jj) {
+        const int i = tid + 256 * jj;
+        e[jj] = i < c ? cand[i] : make_uint2(0, 0);
+      }
+#pragma unroll
+      for (int jj = 0; jj < PER; ++jj) {
+        const int i = tid + 256 * jj;
+        if (i < c) { skey[i] = e[jj].x; sbkt[i] = e[jj].y; }
       }
     }
   }
   __syncthreads();
+  // member words of this thread's candidates (all loads issued together)
+  uint32_t mw[PER];
+#pragma unroll
+  for (int jj = 0; jj < PER; ++jj) {
+    const int i = tid + 256 * jj;
+    mw[jj] = i < c ? mem[sbkt[i]] : 0xFFFFFFFFu;
+  }
   // far-key contributions (members outside the near set)
   int my_w = 0;
-  for (int i = tid; i < c; i += 256) {
+#pragma unroll
+  for (int jj = 0; jj < PER; ++jj) {
+    const int i = tid + 256 * jj;
+    if (i >= c) continue;
     const uint32_t g = sbkt[i];
-    const uint32_t m = mem[g];
+    const uint32_t m = mw[jj];
     const int64_t kb = (int64_t)(g / kBuckets) * kBlock;
     int ci = 0;
+    if (kb >= s_end && kb + kBlock <= w_start) {
+      // block without sink or window keys: every member key is far
 #pragma unroll
-    for (int q = 0; q < kCapItems; ++q) {
-      const uint32_t j = (m >> (8 * q)) & 0xFFu;
-      if (j != 0xFFu) {
+      for (int q = 0; q < kCapItems; ++q) ci += ((m >> (8 * q)) & 0xFFu) != 0xFFu ? kPool : 0;
+    } else {
 #pragma unroll
-        for (int u = 0; u < kPool; ++u) {
-          const int64_t key = kb + kPool * j + u;
-          ci += !(key < s_end || key >= w_start);
+      for (int q = 0; q < kCapItems; ++q) {
+        const uint32_t j = (m >> (8 * q)) & 0xFFu;
+        if (j != 0xFFu) {
+#pragma unroll
+          for (int u = 0; u < kPool; ++u) {
+            const int64_t key = kb + kPool * j + u;
+            ci += !(key < s_end || key >= w_start);
+          }
         }
       }
     }
@@ -1526,22 +1569,45 @@ __global__ __launch_bounds__(256) void k_select_expand(IndexCtx ctx, IndexWs ws,
   const int trunc_m = s_trunc_m;
   const uint32_t gstar = 0xFFFFFFFFu - gstar_key;
   const int n_far = cut ? k : total;
-  for (int i0 = 0; i0 < c; i0 += 256) {
-    const int i = i0 + tid;
-    int take = 0;
-    if (i < c) {
-      if (!cut || skey[i] > prefix || (skey[i] == prefix && sbkt[i] < gstar)) take = contrib[i];
-      else if (skey[i] == prefix && sbkt[i] == gstar) take = trunc_m;
+  // each thread takes a contiguous run of candidates, so one block scan gives
+  // every thread its output offset
+  {
+    auto take_of = [&](int i) -> int {
+      if (!cut || skey[i] > prefix || (skey[i] == prefix && sbkt[i] < gstar)) return contrib[i];
+      if (skey[i] == prefix && sbkt[i] == gstar) return trunc_m;
+      return 0;
+    };
+    int tk[PER];
+    int mine = 0;
+#pragma unroll
+    for (int jj = 0; jj < PER; ++jj) {
+      const int i = tid + 256 * jj;
+      tk[jj] = i < c ? take_of(i) : 0;
+      mine += tk[jj];
     }
-    int chunk_tot;
-    const int o0 = block_scan_excl(take, wsum, &chunk_tot);
-    const int base = s_total;
-    if (take > 0) {
-      int o = base + o0;
+    int all_take;
+    int o = block_scan_excl(mine, wsum, &all_take);
+#pragma unroll
+    for (int jj = 0; jj < PER; ++jj) {
+      int left = tk[jj];
+      if (left == 0) continue;
+      const int i = tid + 256 * jj;
       const uint32_t g = sbkt[i];
-      const uint32_t m = mem[g];
+      const uint32_t m = mw[jj];
       const int64_t kb = (int64_t)(g / kBuckets) * kBlock;
-      int left = take;
+      if (left == (int)contrib[i] && kb >= s_end && kb + kBlock <= w_start) {
+        // the whole bucket, in a block without sink or window keys
+#pragma unroll
+        for (int q = 0; q < kCapItems; ++q) {
+          const uint32_t j = (m >> (8 * q)) & 0xFFu;
+          if (j != 0xFFu) {
+            const int32_t k0 = (int32_t)(kb + kPool * j);
+            far[o] = k0; far[o + 1] = k0 + 1; far[o + 2] = k0 + 2; far[o + 3] = k0 + 3;
+            o += kPool;
+          }
+        }
+        continue;
+      }
       for (int q = 0; q < kCapItems && left > 0; ++q) {
         const uint32_t j = (m >> (8 * q)) & 0xFFu;
         if (j == 0xFFu) break;
@@ -1551,11 +1617,9 @@ __global__ __launch_bounds__(256) void k_select_expand(IndexCtx ctx, IndexWs ws,
         }
       }
     }
-    __syncthreads();
-    if (tid == 0) s_total = base + chunk_tot;
-    __syncthreads();
   }
-  const int32_t* sorted_far = radix_sort_i32(far, far2, n_far, (int)(p > 0 ? p : 0), hist);
+  __syncthreads();
+  const int32_t* sorted_far = radix_sort_i32<8>(far, far2, n_far, (int)(p > 0 ? p : 0), &hist[0][0]);
   // sinks | far | window, -1 padded
   int32_t* out = idx + qi * (int64_t)ctx.list_len;
   int cnt;
@@ -1741,18 +1805,23 @@ hipError_t launch_select_expand(const IndexCtx& ctx, const IndexWs& ws, int32_t*
                                 hipStream_t s) {
   if (ctx.n <= 0) return hipSuccess;
   const size_t smem = (size_t)ctx.cap * 9 + (size_t)(ctx.k > 1 ? ctx.k : 1) * 8;
-  static bool once = false;
-  if (!once) {
-    allow_large_lds(reinterpret_cast<const void*>(k_select_expand<LSA_BF16>));
-    allow_large_lds(reinterpret_cast<const void*>(k_select_expand<LSA_F32>));
-    once = true;
+  // candidate slots per thread: cap / 256 rounded up to 8, 16 or 32
+  const int per = (ctx.cap + 255) / 256;
+  if (per > 32) return hipErrorInvalidValue;
+  auto run = [&](auto kern) {
+    allow_large_lds(reinterpret_cast<const void*>(kern));
+    hipLaunchKernelGGL(kern, dim3((unsigned)ctx.n), dim3(256), smem, s, ctx, ws, idx, count, ranked,
+                       exact_mode);
+  };
+  if (dtype == LSA_BF16) {
+    if (per <= 8) run(k_select_expand<LSA_BF16, 8>);
+    else if (per <= 16) run(k_select_expand<LSA_BF16, 16>);
+    else run(k_select_expand<LSA_BF16, 32>);
+  } else {
+    if (per <= 8) run(k_select_expand<LSA_F32, 8>);
+    else if (per <= 16) run(k_select_expand<LSA_F32, 16>);
+    else run(k_select_expand<LSA_F32, 32>);
   }
-  if (dtype == LSA_BF16)
-    hipLaunchKernelGGL(k_select_expand<LSA_BF16>, dim3((unsigned)ctx.n), dim3(256), smem, s, ctx, ws,
-                       idx, count, ranked, exact_mode);
-  else
-    hipLaunchKernelGGL(k_select_expand<LSA_F32>, dim3((unsigned)ctx.n), dim3(256), smem, s, ctx, ws,
-                       idx, count, ranked, exact_mode);
   return hipGetLastError();
 }
 
