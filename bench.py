@@ -43,7 +43,9 @@ def parse():
                     help="also run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--decode", action="store_true",
                     help="time decode steps (cfg 3: 16 sequences at 1M; cfg 5: one at 10M)")
-    ap.add_argument("--splits", type=int, default=16, help="decode attention splits")
+    ap.add_argument("--splits", type=int, default=0,
+                    help="decode attention splits (0: about 72 listed keys per split, a power of "
+                         "two up to 64)")
     return ap.parse_args()
 
 
@@ -128,6 +130,12 @@ def bench_decode(args, w, dev):
     mode = lsa.LSA_TREE if args.mode == "tree" else lsa.LSA_FLAT
     p = lsa.Params(k=w.k, n_sink=w.n_sink, window=w.window, mode=mode, beam=w.beam)
     L = lsa.list_len(p)
+    if args.splits <= 0:
+        # measured on this workload family: ~64-80 keys per split balances the
+        # number of workgroups against the per-split overhead and the combine
+        args.splits = 1
+        while args.splits < 64 and L / (2 * args.splits) >= 72:
+            args.splits *= 2
     caches, keys_new, queries = [], [], []
     t_gen = time.perf_counter()
     for b in range(B):

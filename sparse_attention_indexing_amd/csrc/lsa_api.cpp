@@ -455,8 +455,9 @@ int lsa_index_decode(lsa_cache* const* caches, int32_t B, const float* latent_q,
   const WsLayout wl = index_ws_layout(p, B);
   if (ws_bytes < wl.total) return LSA_ERR_WORKSPACE;
   hipStream_t s = as_stream(stream);
-  // append the new key of every sequence (one launch), then cluster every
-  // block that this key completed (one launch), then update trees
+  // append the new key of every sequence and prepare the step (one launch),
+  // then cluster every block that this key completed (one launch), then
+  // update trees
   {
     AppendJobs aj;
     WardJobs wj;
@@ -475,7 +476,10 @@ int lsa_index_decode(lsa_cache* const* caches, int32_t B, const float* latent_q,
         ++nfire;
       }
     }
-    hipError_t e = launch_append_rows(latent_k_new, aj, B, s);
+    // one launch: append the new keys, normalise the queries, clear the
+    // per-step histograms and counts
+    hipError_t e = launch_dec_prep(latent_q, latent_k_new, aj, B, make_ws(workspace, wl).yhat,
+                                   make_ws(workspace, wl), p->index_dtype, s);
     if (e != hipSuccess) return LSA_ERR_HIP;
     e = launch_ward_jobs(wj, nfire, p->index_dtype, s);
     if (e != hipSuccess) return LSA_ERR_HIP;
@@ -493,8 +497,6 @@ int lsa_index_decode(lsa_cache* const* caches, int32_t B, const float* latent_q,
     }
   }
   IndexWs ws = make_ws(workspace, wl);
-  hipError_t e = launch_qnorm(latent_q, B, ws.yhat, p->index_dtype, ws.hist, s);
-  if (e != hipSuccess) return LSA_ERR_HIP;
   const int L = p->n_sink + p->window + p->k;
   if (tree) {
     // tree search is per cache: one launch per sequence

@@ -359,12 +359,6 @@ __global__ __launch_bounds__(kThreads) void k_ward_jobs(WardJobs jobs) {
   ward_block_body<DT>(L, jobs.keys[j], jobs.block[j], jobs.cent[j], jobs.members[j]);
 }
 
-// Append one latent key per sequence: row b of src -> dst[b].
-__global__ void k_append_rows(const float* __restrict__ src, AppendJobs jobs) {
-  const int b = blockIdx.x, d = threadIdx.x;
-  jobs.dst[b][d] = src[(int64_t)b * kLatent + d];
-}
-
 // One workgroup per group of (up to) 128 nodes of the level below: greedy
 // pairing by the singleton Ward cost; parents ordered by their smaller child.
 template <int DT>
@@ -471,12 +465,6 @@ hipError_t launch_ward_jobs(const WardJobs& jobs, int n, int dtype, hipStream_t 
     hipLaunchKernelGGL(k_ward_jobs<LSA_BF16>, dim3((unsigned)n), dim3(kThreads), 0, s, jobs);
   else
     hipLaunchKernelGGL(k_ward_jobs<LSA_F32>, dim3((unsigned)n), dim3(kThreads), 0, s, jobs);
-  return hipGetLastError();
-}
-
-hipError_t launch_append_rows(const float* src, const AppendJobs& jobs, int n, hipStream_t s) {
-  if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_append_rows, dim3((unsigned)n), dim3(kLatent), 0, s, src, jobs);
   return hipGetLastError();
 }
 

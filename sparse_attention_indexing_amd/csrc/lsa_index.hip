@@ -97,6 +97,41 @@ __global__ __launch_bounds__(256) void k_qnorm(const float* __restrict__ y, int6
   }
 }
 
+// Decode preparation, 16 lanes per sequence: append the new latent key to the
+// cache's staging row, normalise the query, clear the sampled histogram and
+// the candidate count and status of the step.
+template <int DT>
+__global__ __launch_bounds__(256) void k_dec_prep(const float* __restrict__ y,
+                                                  const float* __restrict__ k_new, AppendJobs jobs,
+                                                  int64_t n, void* __restrict__ yhat, IndexWs ws) {
+  const int64_t i = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int l = threadIdx.x & 15;
+  if (i >= n) return;
+  reinterpret_cast<float4*>(jobs.dst[i])[l] = reinterpret_cast<const float4*>(k_new + i * kLatent)[l];
+#pragma unroll
+  for (int b = 0; b < 16; ++b) ws.hist[i * 256 + 16 * l + b] = 0u;
+  if (l == 0) { ws.cand_cnt[i] = 0; ws.status[i] = 0; }
+  const float4 x = reinterpret_cast<const float4*>(y + i * kLatent)[l];
+  double ss = (double)x.x * x.x;
+  ss = __builtin_fma((double)x.y, (double)x.y, ss);
+  ss = __builtin_fma((double)x.z, (double)x.z, ss);
+  ss = __builtin_fma((double)x.w, (double)x.w, ss);
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) ss += __shfl_xor(ss, off, 16);
+  const double nr = __builtin_sqrt(ss);
+  const bool zero = nr < 1e-30;
+  const double v0 = zero ? 0.0 : x.x / nr, v1 = zero ? 0.0 : x.y / nr;
+  const double v2 = zero ? 0.0 : x.z / nr, v3 = zero ? 0.0 : x.w / nr;
+  if (DT == LSA_BF16) {
+    uint2 w;
+    w.x = (uint32_t)f64_to_bf16_rne(v0) | ((uint32_t)f64_to_bf16_rne(v1) << 16);
+    w.y = (uint32_t)f64_to_bf16_rne(v2) | ((uint32_t)f64_to_bf16_rne(v3) << 16);
+    reinterpret_cast<uint2*>(yhat)[i * 16 + l] = w;
+  } else {
+    reinterpret_cast<float4*>(yhat)[i * 16 + l] = make_float4((float)v0, (float)v1, (float)v2, (float)v3);
+  }
+}
+
 // ------------------------------------------------------------------ MFMA tile
 // One wave scores 32 bucket rows (A) against 32 queries (B) with a 64-deep
 // reduction.  Lane l holds row / column l % 32 and the 32 dims of half l / 32;
@@ -883,8 +918,46 @@ __device__ __forceinline__ void load_rows8(uint4 (&u)[8], const uint4* cent, int
 
 constexpr int kDecStage = 64;           // LDS candidate slots per wave
 
+// tau of query qi from its sampled histogram, computed by one wave: lane l
+// sums the 4 bins 4 (63 - l) .. 4 (63 - l) + 3, so an inclusive prefix over
+// lanes counts samples from the top bin down; tau is the lower edge of the
+// bin where the count reaches about 2 B / 16 samples (the same in every lane)
+__device__ __forceinline__ float dec_tau_wave(const IndexCtx& ctx, const IndexWs& ws, int64_t qi,
+                                             int lane) {
+  const int64_t ne = n_eligible(ctx.pos[qi]);
+  if (ne <= ctx.cap) return -3.0e38f;
+  const uint32_t* h = ws.hist + qi * kBins;
+  const int b0 = 4 * (63 - lane);
+  const uint32_t c0 = h[b0], c1 = h[b0 + 1], c2 = h[b0 + 2], c3 = h[b0 + 3];
+  const uint32_t mine = c0 + c1 + c2 + c3;
+  uint32_t incl = mine;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t o = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += o;
+  }
+  const uint32_t want = (uint32_t)((2 * (int64_t)ctx.top_b + kSampleStride - 1) / kSampleStride);
+  const uint64_t hit = __ballot(incl >= want);
+  if (!hit) return -3.0e38f;
+  const int l = __builtin_ctzll(hit);
+  float tau = 0.f;
+  if (lane == l) {
+    uint32_t cum = incl - mine;
+    int b = b0 + 3;
+    const uint32_t cs[4] = {c0, c1, c2, c3};
+    for (int e = 3; e >= 0; --e) {
+      cum += cs[e];
+      b = b0 + e;
+      if (cum >= want) break;
+    }
+    tau = (float)b / (kBins / 2) - 1.0f;
+  }
+  return __shfl(tau, l, 64);
+}
+
 // grid.x = chunks of kDecRowsPerWg buckets, grid.y = query (sequence).
-// Scores >= tau are staged per wave in LDS and flushed with one atomic.
+// Scores >= tau are staged per wave in LDS and flushed with one atomic; the
+// candidate count starts at zero (k_dec_prep).
 __global__ __launch_bounds__(256) void k_dec_filter(IndexCtx ctx, IndexWs ws) {
   __shared__ uint2 s_buf[4][kDecStage];
   const int64_t qi = blockIdx.y;
@@ -897,7 +970,8 @@ __global__ __launch_bounds__(256) void k_dec_filter(IndexCtx ctx, IndexWs ws) {
   const int sub = lane & 7, grp = lane >> 3;
   float yq[8];
   load_q8(yq, ws.yhat, qi, sub);
-  const float tau = ws.tau[qi];
+  // every wave derives tau from the sampled histogram (the same value)
+  const float tau = dec_tau_wave(ctx, ws, qi, lane);
   const uint4* cent = reinterpret_cast<const uint4*>(ctx.cent[qi]);
   uint2* cand = ws.cand + qi * (int64_t)ctx.cap;
   uint2* stage = s_buf[wave];
@@ -998,48 +1072,6 @@ __global__ __launch_bounds__(256) void k_dec_hist(IndexCtx ctx, IndexWs ws) {
   }
   __syncthreads();
   if (h[tid]) atomicAdd(&ws.hist[qi * kBins + tid], h[tid]);
-}
-
-// tau from the global histogram, one wave per query: lane l sums the 4 bins
-// 4 (63 - l) .. 4 (63 - l) + 3, so an inclusive prefix over lanes counts
-// samples from the top bin down.
-__global__ __launch_bounds__(64) void k_dec_tau(IndexCtx ctx, IndexWs ws) {
-  const int64_t qi = blockIdx.x;
-  const int lane = threadIdx.x;
-  const int64_t ne = n_eligible(ctx.pos[qi]);
-  const uint32_t* h = ws.hist + qi * kBins;
-  const int b0 = 4 * (63 - lane);
-  const uint32_t c0 = h[b0], c1 = h[b0 + 1], c2 = h[b0 + 2], c3 = h[b0 + 3];
-  const uint32_t mine = c0 + c1 + c2 + c3;
-  uint32_t incl = mine;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t o = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += o;
-  }
-  const uint32_t want = (uint32_t)((2 * (int64_t)ctx.top_b + kSampleStride - 1) / kSampleStride);
-  const uint64_t hit = __ballot(incl >= want);
-  float tau = -3.0e38f;
-  if (ne > ctx.cap && hit) {
-    const int l = __builtin_ctzll(hit);                 // first lane (highest bins) reaching want
-    if (lane == l) {
-      uint32_t cum = incl - mine;                        // samples above this lane's bins
-      int b = b0 + 3;
-      const uint32_t cs[4] = {c0, c1, c2, c3};
-      for (int e = 3; e >= 0; --e) {
-        cum += cs[e];
-        b = b0 + e;
-        if (cum >= want) break;
-      }
-      tau = (float)b / (kBins / 2) - 1.0f;
-    }
-    tau = __shfl(tau, l, 64);
-  }
-  if (lane == 0) {
-    ws.tau[qi] = tau;
-    ws.cand_cnt[qi] = 0;
-    ws.status[qi] = 0;
-  }
 }
 
 // ------------------------------------------------------------------ exact select
@@ -1238,11 +1270,12 @@ __global__ __launch_bounds__(64) void k_tree_search(IndexCtx ctx, TreeCtx tc, In
       if (j < nbeam) {
         const int32_t c = tc.child[lvl + 1][2 * beam[j] + h];
         if (c >= 0) {
+          // the centroid is loaded together with the child's smallest block
+          // (not after it) and the score is masked afterwards
           const int64_t mb = lvl == 0 ? (int64_t)c / kBuckets : (int64_t)tc.minb[lvl][c];
-          if (mb < qb) {
-            const float s = vscore<DT>(tc.cent[lvl], c, yq);
+          const float s = vscore<DT>(tc.cent[lvl], c, yq);
+          if (mb < qb)
             e[h] = ((uint64_t)f32_orderable(s) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)c);
-          }
         }
       }
     }
@@ -1280,16 +1313,26 @@ __global__ __launch_bounds__(64) void k_tree_search(IndexCtx ctx, TreeCtx tc, In
   // score eligible buckets and write the candidate list
   uint2* cand = ws.cand + qi * (int64_t)ctx.cap;
   int out = 0;
-  for (int j0 = 0; j0 < n; j0 += 64) {
-    const int j = j0 + lane;
-    int32_t g = j < n ? cur[j] : -1;
-    const bool ok = g >= 0 && (int64_t)g < ne;
-    float s = 0.f;
-    if (ok) s = vscore<DT>(tc.cent[0], g, yq);
-    const uint64_t bal = __ballot(ok);
-    const int pos = out + __popcll(bal & ((1ull << lane) - 1ull));
-    if (ok) cand[pos] = make_uint2(__float_as_uint(s), (uint32_t)g);
-    out += __popcll(bal);
+  // four buckets per lane per round, so their centroid loads overlap
+  for (int j0 = 0; j0 < n; j0 += 256) {
+    int32_t g[4];
+    bool ok[4];
+    float s[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = j0 + 64 * u + lane;
+      g[u] = j < n ? cur[j] : -1;
+      ok[u] = g[u] >= 0 && (int64_t)g[u] < ne;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) s[u] = vscore<DT>(tc.cent[0], ok[u] ? g[u] : 0, yq);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint64_t bal = __ballot(ok[u]);
+      const int pos = out + __popcll(bal & ((1ull << lane) - 1ull));
+      if (ok[u]) cand[pos] = make_uint2(__float_as_uint(s[u]), (uint32_t)g[u]);
+      out += __popcll(bal);
+    }
   }
   if (lane == 0) ws.cand_cnt[qi] = out;
 }
@@ -1653,6 +1696,17 @@ hipError_t launch_qnorm(const float* y, int64_t n, void* yhat, int dtype, uint32
   return hipGetLastError();
 }
 
+hipError_t launch_dec_prep(const float* y, const float* k_new, const AppendJobs& jobs, int64_t n,
+                           void* yhat, const IndexWs& ws, int dtype, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  dim3 grid((unsigned)((n + 15) / 16));
+  if (dtype == LSA_BF16)
+    hipLaunchKernelGGL(k_dec_prep<LSA_BF16>, grid, dim3(256), 0, s, y, k_new, jobs, n, yhat, ws);
+  else
+    hipLaunchKernelGGL(k_dec_prep<LSA_F32>, grid, dim3(256), 0, s, y, k_new, jobs, n, yhat, ws);
+  return hipGetLastError();
+}
+
 static int64_t query_tiles(const IndexCtx& ctx) {
   return ctx.per_seq ? (ctx.n + 3) / 4 : (ctx.n + kQueriesPerWg - 1) / kQueriesPerWg;
 }
@@ -1666,12 +1720,9 @@ hipError_t launch_thresh(const IndexCtx& ctx, const IndexWs& ws, int dtype, hipS
       max_samp = ns > max_samp ? ns : max_samp;
     }
     const int64_t gx = (max_samp + kDecSampPerWg - 1) / kDecSampPerWg;
-    if (gx > 0) {
+    // tau itself is derived by every k_dec_filter wave from the histogram
+    if (gx > 0)
       hipLaunchKernelGGL(k_dec_hist, dim3((unsigned)gx, (unsigned)ctx.n), dim3(256), 0, s, ctx, ws);
-      hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL(k_dec_tau, dim3((unsigned)ctx.n), dim3(64), 0, s, ctx, ws);
     return hipGetLastError();
   }
   if (ctx.per_seq) {

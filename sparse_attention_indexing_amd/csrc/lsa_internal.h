@@ -149,10 +149,11 @@ hipError_t launch_tree_groups(const void* child_cent, const int32_t* child_minb,
                               hipStream_t s);
 hipError_t launch_copy_rows(float* dst, const float* src, int64_t n, hipStream_t s);
 hipError_t launch_ward_jobs(const WardJobs& jobs, int n, int dtype, hipStream_t s);
-hipError_t launch_append_rows(const float* src, const AppendJobs& jobs, int n, hipStream_t s);
 
 hipError_t launch_qnorm(const float* y, int64_t n, void* yhat, int dtype, uint32_t* hist,
                         hipStream_t s);
+hipError_t launch_dec_prep(const float* y, const float* k_new, const AppendJobs& jobs, int64_t n,
+                           void* yhat, const IndexWs& ws, int dtype, hipStream_t s);
 hipError_t launch_thresh(const IndexCtx& ctx, const IndexWs& ws, int dtype, hipStream_t s);
 hipError_t launch_score_filter(const IndexCtx& ctx, const IndexWs& ws, int dtype,
                                int64_t max_tiles, hipStream_t s);
