@@ -47,27 +47,74 @@ __device__ __forceinline__ double pair_cost(const WardLds& L, int a, int b) {
   return a < b ? L.cost[tri(a, b)] : L.cost[tri(b, a)];
 }
 
-// lexicographic (value, i) minimum across the 64 lanes of a wave
-__device__ __forceinline__ void wave_argmin(double& v, int& i) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    double ov = __shfl_xor(v, off, 64);
-    int oi = __shfl_xor(i, off, 64);
-    if (ov < v || (ov == v && oi < i)) { v = ov; i = oi; }
-  }
+// Cross-lane helpers on DPP (no LDS round trips).  64-bit values move as two
+// 32-bit halves; quad_perm [1,0,3,2] / [2,3,0,1], row_half_mirror and
+// row_mirror combine lanes within rows of 16, readlane combines the 4 rows.
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+  return ((uint64_t)hi << 32) | lo;
 }
 
-// lexicographic (value, lo, hi) minimum across a wave
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) { return a < b ? a : b; }
+
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
+  v = umin64(v, dpp_u64<0xB1>(v));
+  v = umin64(v, dpp_u64<0x4E>(v));
+  v = umin64(v, dpp_u64<0x141>(v));
+  v = umin64(v, dpp_u64<0x140>(v));
+  return umin64(umin64(readlane_u64(v, 0), readlane_u64(v, 16)),
+                umin64(readlane_u64(v, 32), readlane_u64(v, 48)));
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  auto mn = [](uint32_t a, uint32_t b) { return a < b ? a : b; };
+  v = mn(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+  v = mn(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+  v = mn(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
+  v = mn(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));
+  return mn(mn((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16)),
+            mn((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
+}
+
+// sum over the 4 lanes of a quad (every lane of the quad gets the sum)
+__device__ __forceinline__ double quad_sum_f64(double x) {
+  uint64_t u = (uint64_t)__double_as_longlong(x);
+  x += __longlong_as_double((long long)dpp_u64<0xB1>(u));
+  u = (uint64_t)__double_as_longlong(x);
+  x += __longlong_as_double((long long)dpp_u64<0x4E>(u));
+  return x;
+}
+
+// Lexicographic (value, i) minimum across the 64 lanes of a wave (all lanes
+// active).  Values are non-negative costs or +inf, whose bit patterns order
+// like the values; the smallest value wins, then the smallest index among the
+// lanes holding it.
+__device__ __forceinline__ void wave_argmin(double& v, int& i) {
+  const uint64_t bits = (uint64_t)__double_as_longlong(v);
+  const uint64_t m = wave_min_u64(bits);
+  const uint32_t k = wave_min_u32(bits == m ? (uint32_t)i : 0xFFFFFFFFu);
+  v = __longlong_as_double((long long)m);
+  i = (int)k;
+}
+
+// lexicographic (value, lo, hi) minimum across a wave (lo, hi < 128, or
+// 0x7fffffff for none)
 __device__ __forceinline__ void wave_argmin3(double& v, int& lo, int& hi) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    double ov = __shfl_xor(v, off, 64);
-    int olo = __shfl_xor(lo, off, 64);
-    int ohi = __shfl_xor(hi, off, 64);
-    if (ov < v || (ov == v && (olo < lo || (olo == lo && ohi < hi)))) {
-      v = ov; lo = olo; hi = ohi;
-    }
-  }
+  const uint64_t bits = (uint64_t)__double_as_longlong(v);
+  const uint64_t m = wave_min_u64(bits);
+  const uint32_t key = ((uint32_t)(lo < kN ? lo : 0xFFFF) << 16) | (uint32_t)(hi < kN ? hi : 0xFFFF);
+  const uint32_t k = wave_min_u32(bits == m ? key : 0xFFFFFFFFu);
+  v = __longlong_as_double((long long)m);
+  lo = (k >> 16) >= (uint32_t)kN ? 0x7fffffff : (int)(k >> 16);
+  hi = (k & 0xFFFFu) >= (uint32_t)kN ? 0x7fffffff : (int)(k & 0xFFFFu);
 }
 
 // Rescan row r: nearest feasible active partner (smallest index on ties).  One wave.
@@ -119,10 +166,8 @@ __device__ void ward_core(WardLds& L, int n, int cap, int target) {
           sb = __builtin_fma(eb, eb, sb);
         }
       }
-      sa += __shfl_xor(sa, 1, 64);
-      sa += __shfl_xor(sa, 2, 64);
-      sb += __shfl_xor(sb, 1, 64);
-      sb += __shfl_xor(sb, 2, 64);
+      sa = quad_sum_f64(sa);
+      sb = quad_sum_f64(sb);
       if (q == 0) {
         if (da_on) L.cost[tri(ra, j)] = 0.5 * sa;
         if (db_on) L.cost[tri(rb, j)] = 0.5 * sb;
@@ -180,8 +225,7 @@ __device__ void ward_core(WardLds& L, int n, int cap, int target) {
             s = __builtin_fma(e, e, s);
           }
         }
-        s += __shfl_xor(s, 1, 64);
-        s += __shfl_xor(s, 2, 64);
+        s = quad_sum_f64(s);
         if (q == 0 && so > 0 && o != a) {
           const double c = (double)nab * (double)so / (double)(nab + so) * s;
           if (o < a) L.cost[tri(o, a)] = c; else L.cost[tri(a, o)] = c;
@@ -234,8 +278,7 @@ __device__ void load_pooled(WardLds& L, const float* __restrict__ src) {
       double ss = 0.0;
 #pragma unroll
       for (int d = 0; d < 16; ++d) ss = __builtin_fma((double)x[d], (double)x[d], ss);
-      ss += __shfl_xor(ss, 1, 64);
-      ss += __shfl_xor(ss, 2, 64);
+      ss = quad_sum_f64(ss);
       const double nrm = __builtin_sqrt(ss);
       const bool zero = nrm < 1e-30;
 #pragma unroll
@@ -290,8 +333,7 @@ __device__ __forceinline__ void quad_unit(double* v) {
   double ss = 0.0;
 #pragma unroll
   for (int d = 0; d < 16; ++d) ss = __builtin_fma(v[d], v[d], ss);
-  ss += __shfl_xor(ss, 1, 64);
-  ss += __shfl_xor(ss, 2, 64);
+  ss = quad_sum_f64(ss);  // quad-uniform control flow only reads lanes of the same quad
   const double n = __builtin_sqrt(ss);
   const bool zero = n < 1e-30;
 #pragma unroll

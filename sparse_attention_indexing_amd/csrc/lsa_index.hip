@@ -383,14 +383,18 @@ __global__ __launch_bounds__(256) void k_score_filter(IndexCtx ctx, IndexWs ws, 
 // for scores >= tau, staged in LDS and flushed with one atomic per query.
 constexpr int kCapL = 48;           // LDS candidate slots per query and workgroup
 
-struct Q128 {
-  bf16x8 b[4][4];                   // [query group][k step]
+// NG query groups of 32 per wave (4 for 128 queries)
+template <int NG>
+struct QGroups {
+  bf16x8 b[NG][4];                  // [query group][k step]
 };
+using Q128 = QGroups<4>;
 
-__device__ __forceinline__ void load_q128(Q128& q, const void* yhat, int64_t q0, int64_t n, int col,
-                                          int half) {
+template <int NG>
+__device__ __forceinline__ void load_q128(QGroups<NG>& q, const void* yhat, int64_t q0, int64_t n,
+                                          int col, int half) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < NG; ++j) {
     const int64_t qi = q0 + 32 * j + col;
     const bool valid = qi < n;
     const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(yhat) +
@@ -427,11 +431,12 @@ __device__ __forceinline__ void mfma_q128(f32x16 (&acc)[4], const uint4 (&a)[4],
 // group j + 1 execute (the scheduling barriers ask for 1 MFMA, then 3 VALU).
 __device__ __forceinline__ float max16(const f32x16& v);
 
-__device__ __forceinline__ void mfma_q128_masks(f32x16 (&acc)[4], uint64_t (&mks)[4],
-                                                const uint4 (&a)[4], const Q128& q,
-                                                const float (&tau)[4]) {
+template <int NG>
+__device__ __forceinline__ void mfma_q128_masks(f32x16 (&acc)[NG], uint64_t (&mks)[NG],
+                                                const uint4 (&a)[4], const QGroups<NG>& q,
+                                                const float (&tau)[NG]) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < NG; ++j) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
 #pragma unroll
@@ -440,10 +445,10 @@ __device__ __forceinline__ void mfma_q128_masks(f32x16 (&acc)[4], uint64_t (&mks
                                                        acc[j], 0, 0, 0);
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) mks[j] = __ballot(max16(acc[j]) >= tau[j]);
+  for (int j = 0; j < NG; ++j) mks[j] = __ballot(max16(acc[j]) >= tau[j]);
   __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 #pragma unroll
-  for (int i = 0; i < 12; ++i) {
+  for (int i = 0; i < 4 * (NG - 1); ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
   }
@@ -460,19 +465,22 @@ __device__ __forceinline__ float max16(const f32x16& v) {
   return __builtin_fmaxf(m0, m3);
 }
 
-// Per-lane view of the 4 queries (one per group) whose column this lane holds.
-struct QCols {
-  int32_t qi[4];
-  int32_t ne[4];
-  float tau[4];
-  bool all[4];
+// Per-lane view of the NG queries (one per group) whose column this lane holds.
+template <int NG>
+struct QColsN {
+  int32_t qi[NG];
+  int32_t ne[NG];
+  float tau[NG];
+  bool all[NG];
 };
+using QCols = QColsN<4>;
 
-__device__ __forceinline__ int32_t load_qcols(QCols& c, const IndexCtx& ctx, const float* tau,
+template <int NG>
+__device__ __forceinline__ int32_t load_qcols(QColsN<NG>& c, const IndexCtx& ctx, const float* tau,
                                               int64_t q0, int col) {
   int32_t nmax = 0;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < NG; ++j) {
     const int64_t qi = q0 + 32 * j + col;
     const bool valid = qi < ctx.n;
     c.qi[j] = valid ? (int32_t)qi : 0;
@@ -496,20 +504,21 @@ __device__ __forceinline__ int32_t load_qcols(QCols& c, const IndexCtx& ctx, con
 // expand_entries then turns buffered entries into candidates with one entry
 // per lane, appending to the query's LDS list (global memory once full).
 
-template <int W, int E>
+template <int W, int E, int NQ>
 struct LowPassLds {
   static constexpr int kEntries = E;                  // buffered entries per wave
-  int cnt[kQueriesPerWg];                             // candidates per query
-  uint2 buf[kQueriesPerWg * kCapL];                   // (score bits, bucket)
-  float tau[kQueriesPerWg];
+  static constexpr int kQueries = NQ;                 // queries of the workgroup
+  int cnt[NQ];                                        // candidates per query
+  uint2 buf[NQ * kCapL];                              // (score bits, bucket)
+  float tau[NQ];
   float ent[W][E][16];                                // buffered scores per wave
   uint32_t meta[W][E];                                // tile << 8 | half << 7 | query
 };
 
-template <class LL>
+template <class LL, int NG>
 __device__ __forceinline__ void lowpass_buffer_masks(LL& L, const IndexCtx& ctx, const IndexWs& ws,
-                                                     const f32x16 (&acc)[4], const float (&tau)[4],
-                                                     const uint64_t (&mks)[4], int32_t t, int64_t q0,
+                                                     const f32x16 (&acc)[NG], const float (&tau)[NG],
+                                                     const uint64_t (&mks)[NG], int32_t t, int64_t q0,
                                                      int wave, int lane, int col, int half,
                                                      int& ecnt);
 
@@ -564,26 +573,15 @@ __device__ __forceinline__ void expand_entries(LL& L, const IndexCtx& ctx, const
   __builtin_amdgcn_wave_barrier();
 }
 
-template <class LL>
-__device__ __forceinline__ void lowpass_buffer(LL& L, const IndexCtx& ctx, const IndexWs& ws,
-                                               const f32x16 (&acc)[4], const float (&tau)[4],
-                                               int32_t t, int64_t q0, int wave, int lane, int col,
-                                               int half, int& ecnt) {
-  uint64_t mks[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) mks[j] = __ballot(max16(acc[j]) >= tau[j]);
-  lowpass_buffer_masks(L, ctx, ws, acc, tau, mks, t, q0, wave, lane, col, half, ecnt);
-}
-
-// the same with the per-group ballots of max16(acc[j]) >= tau[j] given
-template <class LL>
+// Buffer the lanes flagged in the per-group ballots of max16(acc[j]) >= tau[j]
+template <class LL, int NG>
 __device__ __forceinline__ void lowpass_buffer_masks(LL& L, const IndexCtx& ctx, const IndexWs& ws,
-                                                     const f32x16 (&acc)[4], const float (&tau)[4],
-                                                     const uint64_t (&mks)[4], int32_t t, int64_t q0,
+                                                     const f32x16 (&acc)[NG], const float (&tau)[NG],
+                                                     const uint64_t (&mks)[NG], int32_t t, int64_t q0,
                                                      int wave, int lane, int col, int half,
                                                      int& ecnt) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < NG; ++j) {
     const uint64_t mk = mks[j];
     if (mk == 0) continue;
     const int n = __popcll(mk);
@@ -707,24 +705,26 @@ __global__ __launch_bounds__(256, 2) void k_score_highpass(IndexCtx ctx, IndexWs
 // tile when it is half full, so the expansion never runs while a tile's
 // accumulators are live.  grid.x = query tiles from qt0 on, grid.y =
 // bucket segments.
+template <int NG>
 __global__ __launch_bounds__(256, 2) void k_score_lowpass(IndexCtx ctx, IndexWs ws, int seg_tiles,
-                                                          int qt0) {
-  __shared__ __attribute__((aligned(16))) LowPassLds<4, 64> L;
+                                                          int64_t qbase) {
+  constexpr int NQ = 32 * NG;                            // queries per workgroup
+  __shared__ __attribute__((aligned(16))) LowPassLds<4, 64, NQ> L;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
-  const int64_t q0 = (int64_t)(qt0 + blockIdx.x) * kQueriesPerWg;
-  QCols qc;
+  const int64_t q0 = qbase + (int64_t)blockIdx.x * NQ;
+  QColsN<NG> qc;
   const int32_t nmax = load_qcols(qc, ctx, ws.tau, q0, col);
   const int32_t t0 = (int32_t)blockIdx.y * seg_tiles;
   int32_t t1 = (nmax + kTile - 1) / kTile;
   if (t1 > t0 + seg_tiles) t1 = t0 + seg_tiles;
   if (t0 >= t1) return;                                  // uniform over the workgroup
-  if (tid < kQueriesPerWg) {
+  if (tid < NQ) {
     L.cnt[tid] = 0;
     L.tau[tid] = q0 + tid < ctx.n ? ws.tau[q0 + tid] : 3.0e38f;
   }
-  Q128 q;
+  QGroups<NG> q;
   load_q128(q, ws.yhat, q0, ctx.n, col, half);
   const void* cent = ctx.cent[0];
   const int32_t tl = t1 - 1;
@@ -736,8 +736,8 @@ __global__ __launch_bounds__(256, 2) void k_score_lowpass(IndexCtx ctx, IndexWs 
   __builtin_amdgcn_sched_barrier(0);   // keep ra's loads older than rb's
   load_atile(rb, cent, (int64_t)(t + 4 < tl ? t + 4 : tl) * kTile + col, half);
   for (; t < t1; t += 8) {
-    f32x16 acc[4];
-    uint64_t mks[4];
+    f32x16 acc[NG];
+    uint64_t mks[NG];
     mfma_q128_masks(acc, mks, ra, q, qc.tau);
     load_atile(ra, cent, (int64_t)(t + 8 < tl ? t + 8 : tl) * kTile + col, half);
     lowpass_buffer_masks(L, ctx, ws, acc, qc.tau, mks, t, q0, wave, lane, col, half, ecnt);
@@ -753,16 +753,18 @@ __global__ __launch_bounds__(256, 2) void k_score_lowpass(IndexCtx ctx, IndexWs 
   __syncthreads();
   // flush: two threads per query
   const int ql = tid >> 1, sub = tid & 1;
-  const int64_t qi = q0 + ql;
-  int n = L.cnt[ql];
-  n = n < kCapL ? n : kCapL;
-  int base = 0;
-  if (sub == 0 && n > 0 && qi < ctx.n) base = atomicAdd(&ws.cand_cnt[qi], n);
-  base = __shfl(base, lane & ~1, 64);
-  if (qi < ctx.n) {
-    uint2* dst = ws.cand + qi * (int64_t)ctx.cap;
-    for (int i = sub; i < n; i += 2)
-      if (base + i < ctx.cap) dst[base + i] = L.buf[ql * kCapL + i];
+  if (ql < NQ) {
+    const int64_t qi = q0 + ql;
+    int n = L.cnt[ql];
+    n = n < kCapL ? n : kCapL;
+    int base = 0;
+    if (sub == 0 && n > 0 && qi < ctx.n) base = atomicAdd(&ws.cand_cnt[qi], n);
+    base = __shfl(base, lane & ~1, 64);
+    if (qi < ctx.n) {
+      uint2* dst = ws.cand + qi * (int64_t)ctx.cap;
+      for (int i = sub; i < n; i += 2)
+        if (base + i < ctx.cap) dst[base + i] = L.buf[ql * kCapL + i];
+    }
   }
 }
 
@@ -1801,9 +1803,15 @@ hipError_t launch_score_filter(const IndexCtx& ctx, const IndexWs& ws, int dtype
     if (x_lp > 0)
       hipLaunchKernelGGL(k_score_highpass, dim3((unsigned)x_lp, (unsigned)nseg), dim3(256), 0, s,
                          ctx, ws, (int)seg);
-    if (x_lp < qt)
-      hipLaunchKernelGGL(k_score_lowpass, dim3((unsigned)(qt - x_lp), (unsigned)nseg), dim3(256),
-                         0, s, ctx, ws, (int)seg, (int)x_lp);
+    if (x_lp < qt) {
+      // 128 queries per workgroup (4 groups of 32 per wave); 3 groups (96
+      // queries) measured slower at two or three waves per SIMD
+      constexpr int kNG = 4;
+      const int64_t qb = x_lp * kQueriesPerWg;
+      const int64_t nt = (ctx.n - qb + 32 * kNG - 1) / (32 * kNG);
+      hipLaunchKernelGGL(k_score_lowpass<kNG>, dim3((unsigned)nt, (unsigned)nseg), dim3(256), 0, s,
+                         ctx, ws, (int)seg, qb);
+    }
     return hipGetLastError();
   }
   if (ctx.per_seq && dtype == LSA_BF16) {
