@@ -381,7 +381,7 @@ __global__ __launch_bounds__(256) void k_score_filter(IndexCtx ctx, IndexWs ws, 
 // than candidate slots (ne <= cap) keeps all of them, each stored directly at
 // slot g with the count preset to ne; other queries append (score, bucket)
 // for scores >= tau, staged in LDS and flushed with one atomic per query.
-constexpr int kCapL = 48;           // LDS candidate slots per query and workgroup
+constexpr int kCapL = 40;           // LDS candidate slots per query and workgroup
 
 // NG query groups of 32 per wave (4 for 128 queries)
 template <int NG>
@@ -500,127 +500,115 @@ __device__ __forceinline__ int32_t load_qcols(QColsN<NG>& c, const IndexCtx& ctx
 // Low-pass epilogue (few candidates per query and tile).  In the tile loop
 // each lane only takes the max of its 16 scores per query group (8 v_max3)
 // and compares it with the query's tau; a lane whose max passes copies its 16
-// scores into the wave's LDS entry buffer (slots from a ballot, no atomics).
-// expand_entries then turns buffered entries into candidates with one entry
-// per lane, appending to the query's LDS list (global memory once full).
+// scores into its wave's LDS ring (slots from a ballot, no atomics).  Full
+// passes of 64 ring entries, one per lane, then find the passing rows and
+// append them to the query's LDS list (global memory once the list is full).
+constexpr int kRing = 128;          // ring entries per wave (power of two)
 
-template <int W, int E, int NQ>
+template <int NQ>
 struct LowPassLds {
-  static constexpr int kEntries = E;                  // buffered entries per wave
-  static constexpr int kQueries = NQ;                 // queries of the workgroup
   int cnt[NQ];                                        // candidates per query
-  uint2 buf[NQ * kCapL];                              // (score bits, bucket)
   float tau[NQ];
-  float ent[W][E][16];                                // buffered scores per wave
-  uint32_t meta[W][E];                                // tile << 8 | half << 7 | query
+  int32_t ne[NQ];                                     // eligible buckets per query
+  uint2 buf[NQ * kCapL];                              // (score bits, bucket)
+  float ent[4][kRing][16];                            // ring of flagged lanes per wave
+  uint32_t meta[4][kRing];                            // tile << 8 | half << 7 | query
 };
 
-template <class LL, int NG>
-__device__ __forceinline__ void lowpass_buffer_masks(LL& L, const IndexCtx& ctx, const IndexWs& ws,
-                                                     const f32x16 (&acc)[NG], const float (&tau)[NG],
-                                                     const uint64_t (&mks)[NG], int32_t t, int64_t q0,
-                                                     int wave, int lane, int col, int half,
-                                                     int& ecnt);
-
-// append the rows of `bits` (bit r: row r of 16) with one LDS reservation
+// One pass over up to 64 ring entries starting at `head` (wave-uniform).
 template <class LL>
-__device__ __forceinline__ void lds_append16(LL& L, const IndexWs& ws, int cap, int ql, int64_t qi,
-                                             const float (&v)[16], uint32_t bits, int32_t gb) {
-  const int c = __popc(bits);
-  int slot = atomicAdd(&L.cnt[ql], c);
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    if ((bits >> r) & 1u) {
-      const uint2 e = make_uint2(__float_as_uint(v[r]), (uint32_t)(gb + 8 * (r >> 2) + (r & 3)));
-      if (slot < kCapL) {
-        L.buf[ql * kCapL + slot] = e;
-      } else {
-        const int gs = atomicAdd(&ws.cand_cnt[qi], 1);
-        if (gs < cap) ws.cand[qi * cap + gs] = e;
-      }
-      ++slot;
-    }
-  }
-}
-
-// buffered entries, one per lane at a time: 16 rows against the query's tau and ne
-template <class LL>
-__device__ __forceinline__ void expand_entries(LL& L, const IndexCtx& ctx, const IndexWs& ws,
-                                               int64_t q0, int wave, int lane, int n) {
+__device__ __forceinline__ void ring_pass(LL& L, const IndexCtx& ctx, const IndexWs& ws,
+                                          int64_t q0, int wave, int lane, uint32_t head,
+                                          uint32_t count) {
   __builtin_amdgcn_wave_barrier();
-  for (int e = lane; e < n; e += 64) {
+  if ((uint32_t)lane < count) {
+    const uint32_t e = (head + (uint32_t)lane) & (kRing - 1);
     const uint32_t meta = L.meta[wave][e];
-    const int ql = meta & 127, h = (meta >> 7) & 1;
-    const int32_t gb = (int32_t)(meta >> 8) * kTile + 4 * h;
-    const int64_t qi = q0 + ql;
+    const int ql = meta & 127;
+    const int32_t gb = (int32_t)(meta >> 8) * kTile + 4 * (int)((meta >> 7) & 1);
     const float tau = L.tau[ql];
-    const int32_t ne = (int32_t)n_eligible(ctx.q_start + qi);
+    const int32_t ne = L.ne[ql];
     const float4* src = reinterpret_cast<const float4*>(L.ent[wave][e]);
-    float v[16];
+    uint32_t bits = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float4 x = src[i];
-      v[4 * i] = x.x; v[4 * i + 1] = x.y; v[4 * i + 2] = x.z; v[4 * i + 3] = x.w;
+      bits |= (uint32_t)(x.x >= tau) << (4 * i);
+      bits |= (uint32_t)(x.y >= tau) << (4 * i + 1);
+      bits |= (uint32_t)(x.z >= tau) << (4 * i + 2);
+      bits |= (uint32_t)(x.w >= tau) << (4 * i + 3);
     }
-    uint32_t bits = 0;
+    // rows 4i..4i+3 hold buckets gb + 8i .. gb + 8i + 3; only the last
+    // eligible tile of a query cuts a run
+    if (gb + 27 >= ne) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int32_t g = gb + 8 * (r >> 2) + (r & 3);
-      bits |= (uint32_t)((v[r] >= tau) & (g < ne)) << r;
+      for (int i = 0; i < 4; ++i) {
+        int v = ne - (gb + 8 * i);
+        v = v < 0 ? 0 : (v > 4 ? 4 : v);
+        bits &= ~((0xFu & ~((1u << v) - 1u)) << (4 * i));
+      }
     }
-    if (bits) lds_append16(L, ws, ctx.cap, ql, qi, v, bits, gb);
+    if (bits) {
+      int slot = atomicAdd(&L.cnt[ql], __popc(bits));
+      const int64_t qi = q0 + ql;
+      const float* row = L.ent[wave][e];
+      do {
+        const int r = __builtin_ctz(bits);
+        bits &= bits - 1;
+        const uint2 c = make_uint2(__float_as_uint(row[r]), (uint32_t)(gb + 8 * (r >> 2) + (r & 3)));
+        if (slot < kCapL) {
+          L.buf[ql * kCapL + slot] = c;
+        } else {
+          const int gs = atomicAdd(&ws.cand_cnt[qi], 1);
+          if (gs < ctx.cap) ws.cand[qi * ctx.cap + gs] = c;
+        }
+        ++slot;
+      } while (bits);
+    }
   }
   __builtin_amdgcn_wave_barrier();
 }
 
-// Buffer the lanes flagged in the per-group ballots of max16(acc[j]) >= tau[j]
+// Copy the lanes flagged in the per-group ballots into the ring; a group that
+// would not fit first drains one full pass (more than 64 entries are queued
+// whenever that happens).
 template <class LL, int NG>
-__device__ __forceinline__ void lowpass_buffer_masks(LL& L, const IndexCtx& ctx, const IndexWs& ws,
-                                                     const f32x16 (&acc)[NG], const float (&tau)[NG],
-                                                     const uint64_t (&mks)[NG], int32_t t, int64_t q0,
-                                                     int wave, int lane, int col, int half,
-                                                     int& ecnt) {
+__device__ __forceinline__ void ring_push(LL& L, const IndexCtx& ctx, const IndexWs& ws,
+                                          const f32x16 (&acc)[NG], const uint64_t (&mks)[NG],
+                                          int32_t t, int64_t q0, int wave, int lane, int col,
+                                          int half, uint32_t& head, uint32_t& tail) {
 #pragma unroll
   for (int j = 0; j < NG; ++j) {
     const uint64_t mk = mks[j];
     if (mk == 0) continue;
-    const int n = __popcll(mk);
-    if (ecnt + n <= LL::kEntries) {
-      if ((mk >> lane) & 1ull) {
-        const int e = ecnt + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32),
-                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u));
-        float4* dst = reinterpret_cast<float4*>(L.ent[wave][e]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          dst[i] = make_float4(acc[j][4 * i], acc[j][4 * i + 1], acc[j][4 * i + 2], acc[j][4 * i + 3]);
-        L.meta[wave][e] = ((uint32_t)t << 8) | ((uint32_t)half << 7) | (uint32_t)(32 * j + col);
-      }
-      ecnt += n;
-    } else if ((mk >> lane) & 1ull) {
-      // the buffer is full: append this lane's passing rows directly
-      const int ql = 32 * j + col;
-      const int64_t qi = q0 + ql;
-      const int32_t ne = (int32_t)n_eligible(ctx.q_start + qi);
-      const int32_t gb = t * kTile + 4 * half;
-      float v[16];
-      uint32_t bits = 0;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        v[r] = acc[j][r];
-        bits |= (uint32_t)((v[r] >= tau[j]) & (gb + 8 * (r >> 2) + (r & 3) < ne)) << r;
-      }
-      if (bits) lds_append16(L, ws, ctx.cap, ql, qi, v, bits, gb);
+    const uint32_t n = (uint32_t)__popcll(mk);
+    if (tail - head + n > (uint32_t)kRing) {
+      ring_pass(L, ctx, ws, q0, wave, lane, head, 64u);
+      head += 64u;
     }
+    if ((mk >> lane) & 1ull) {
+      const uint32_t e = (tail + __builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32),
+                                  __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u))) & (kRing - 1);
+      float4* dst = reinterpret_cast<float4*>(L.ent[wave][e]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        dst[i] = make_float4(acc[j][4 * i], acc[j][4 * i + 1], acc[j][4 * i + 2], acc[j][4 * i + 3]);
+      L.meta[wave][e] = ((uint32_t)t << 8) | ((uint32_t)half << 7) | (uint32_t)(32 * j + col);
+    }
+    tail += n;
   }
 }
 
-// after a tile's epilogue (its accumulators are dead): expand when half full
+// after a tile's epilogue (its accumulators are dead): full passes only,
+// or everything at the end
 template <class LL>
-__device__ __forceinline__ void lowpass_drain(LL& L, const IndexCtx& ctx, const IndexWs& ws,
-                                              int64_t q0, int wave, int lane, int& ecnt, bool all) {
-  if (ecnt > (all ? 0 : LL::kEntries / 2)) {
-    expand_entries(L, ctx, ws, q0, wave, lane, ecnt);
-    ecnt = 0;
+__device__ __forceinline__ void ring_drain(LL& L, const IndexCtx& ctx, const IndexWs& ws,
+                                           int64_t q0, int wave, int lane, uint32_t& head,
+                                           uint32_t tail, bool all) {
+  while (tail - head >= 64u || (all && tail != head)) {
+    const uint32_t c = tail - head < 64u ? tail - head : 64u;
+    ring_pass(L, ctx, ws, q0, wave, lane, head, c);
+    head += c;
   }
 }
 
@@ -709,7 +697,7 @@ template <int NG>
 __global__ __launch_bounds__(256, 2) void k_score_lowpass(IndexCtx ctx, IndexWs ws, int seg_tiles,
                                                           int64_t qbase) {
   constexpr int NQ = 32 * NG;                            // queries per workgroup
-  __shared__ __attribute__((aligned(16))) LowPassLds<4, 64, NQ> L;
+  __shared__ __attribute__((aligned(16))) LowPassLds<NQ> L;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
@@ -721,15 +709,17 @@ __global__ __launch_bounds__(256, 2) void k_score_lowpass(IndexCtx ctx, IndexWs 
   if (t1 > t0 + seg_tiles) t1 = t0 + seg_tiles;
   if (t0 >= t1) return;                                  // uniform over the workgroup
   if (tid < NQ) {
+    const bool valid = q0 + tid < ctx.n;
     L.cnt[tid] = 0;
-    L.tau[tid] = q0 + tid < ctx.n ? ws.tau[q0 + tid] : 3.0e38f;
+    L.tau[tid] = valid ? ws.tau[q0 + tid] : 3.0e38f;
+    L.ne[tid] = valid ? (int32_t)n_eligible(ctx.q_start + q0 + tid) : 0;
   }
   QGroups<NG> q;
   load_q128(q, ws.yhat, q0, ctx.n, col, half);
   const void* cent = ctx.cent[0];
   const int32_t tl = t1 - 1;
   __syncthreads();
-  int ecnt = 0;                                          // wave-uniform
+  uint32_t head = 0, tail = 0;                           // ring indices, wave-uniform
   uint4 ra[4], rb[4];
   int32_t t = t0 + wave;
   load_atile(ra, cent, (int64_t)(t < tl ? t : tl) * kTile + col, half);
@@ -740,16 +730,16 @@ __global__ __launch_bounds__(256, 2) void k_score_lowpass(IndexCtx ctx, IndexWs 
     uint64_t mks[NG];
     mfma_q128_masks(acc, mks, ra, q, qc.tau);
     load_atile(ra, cent, (int64_t)(t + 8 < tl ? t + 8 : tl) * kTile + col, half);
-    lowpass_buffer_masks(L, ctx, ws, acc, qc.tau, mks, t, q0, wave, lane, col, half, ecnt);
-    lowpass_drain(L, ctx, ws, q0, wave, lane, ecnt, false);
+    ring_push(L, ctx, ws, acc, mks, t, q0, wave, lane, col, half, head, tail);
+    ring_drain(L, ctx, ws, q0, wave, lane, head, tail, false);
     mfma_q128_masks(acc, mks, rb, q, qc.tau);
     load_atile(rb, cent, (int64_t)(t + 12 < tl ? t + 12 : tl) * kTile + col, half);
     if (t + 4 < t1) {
-      lowpass_buffer_masks(L, ctx, ws, acc, qc.tau, mks, t + 4, q0, wave, lane, col, half, ecnt);
-      lowpass_drain(L, ctx, ws, q0, wave, lane, ecnt, false);
+      ring_push(L, ctx, ws, acc, mks, t + 4, q0, wave, lane, col, half, head, tail);
+      ring_drain(L, ctx, ws, q0, wave, lane, head, tail, false);
     }
   }
-  lowpass_drain(L, ctx, ws, q0, wave, lane, ecnt, true);
+  ring_drain(L, ctx, ws, q0, wave, lane, head, tail, true);
   __syncthreads();
   // flush: two threads per query
   const int ql = tid >> 1, sub = tid & 1;
@@ -1785,8 +1775,8 @@ hipError_t launch_score_filter(const IndexCtx& ctx, const IndexWs& ws, int dtype
     const int64_t last = ctx.q_start + ctx.n - 1;
     const int64_t ne_max = (last / kBlock) * kBuckets;
     const int64_t seg_buckets = (int64_t)(kCapL / 4) * ne_max / (2 * (int64_t)(ctx.top_b > 0 ? ctx.top_b : 1));
-    int64_t seg = 16;
-    while (seg * 2 * kTile <= seg_buckets && seg < 512) seg *= 2;
+    int64_t seg = seg_buckets / kTile;
+    seg = seg < 16 ? 16 : (seg > 512 ? 512 : seg & ~(int64_t)7);
     if (seg_buckets < 16 * kTile) seg = 128;
     // query tiles [x_lp, qt) are low-pass (ne grows with the position, so the
     // first query of a tile has its smallest ne); earlier tiles are high-pass
