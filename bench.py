@@ -44,8 +44,7 @@ def parse():
     ap.add_argument("--decode", action="store_true",
                     help="time decode steps (cfg 3: 16 sequences at 1M; cfg 5: one at 10M)")
     ap.add_argument("--splits", type=int, default=0,
-                    help="decode attention splits (0: about 72 listed keys per split, a power of "
-                         "two up to 64)")
+                    help="decode attention splits (0: the library's lsa_attention_default_splits)")
     return ap.parse_args()
 
 
@@ -131,11 +130,7 @@ def bench_decode(args, w, dev):
     p = lsa.Params(k=w.k, n_sink=w.n_sink, window=w.window, mode=mode, beam=w.beam)
     L = lsa.list_len(p)
     if args.splits <= 0:
-        # measured on this workload family: ~64-80 keys per split balances the
-        # number of workgroups against the per-split overhead and the combine
-        args.splits = 1
-        while args.splits < 64 and L / (2 * args.splits) >= 72:
-            args.splits *= 2
+        args.splits = lsa.attention_default_splits(B, L)
     caches, keys_new, queries = [], [], []
     t_gen = time.perf_counter()
     for b in range(B):

@@ -203,6 +203,12 @@ int lsa_index_decode(lsa_cache* const* caches, int32_t B, const float* latent_q,
 int64_t lsa_attention_workspace_bytes(int32_t B, int64_t Tq, int32_t Hq, int32_t D,
                                       int32_t splits);
 
+/* A split count for lsa_sparse_attention: the largest power of two (<= 256)
+ * that keeps at least 32 listed keys per split and rows * splits <= 512
+ * workgroups (two per compute unit), so that few query rows (decode) still
+ * spread over the whole chip.  rows = B * Tq. */
+int32_t lsa_attention_default_splits(int64_t rows, int32_t L_max);
+
 /*
  * lsa_sparse_attention [visual "Intro", "What one query actually does"]:
  * ordinary softmax attention of every query head over the keys listed for

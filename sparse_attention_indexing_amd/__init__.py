@@ -94,6 +94,7 @@ def lib():
         "lsa_index_prefill": (ctypes.c_int, [vp, vp, i64, i64, P, vp, vp, vp, vp, i64, vp]),
         "lsa_index_decode": (ctypes.c_int, [ctypes.POINTER(vp), i32, vp, vp, P, vp, vp, vp, i64, vp]),
         "lsa_attention_workspace_bytes": (i64, [i32, i64, i32, i32, i32]),
+        "lsa_attention_default_splits": (i32, [i64, i32]),
         "lsa_sparse_attention": (ctypes.c_int, [vp, vp, vp, i32, i64, i64, i32, i32, i32, vp, vp,
                                                 i32, ctypes.c_float, i32, i32, vp, vp, i64, vp]),
     }
@@ -126,6 +127,10 @@ def _need(t, dtype, name):
 
 def list_len(p: Params) -> int:
     return _check("lsa_list_len", lib().lsa_list_len(ctypes.byref(p.c())))
+
+
+def attention_default_splits(rows: int, L_max: int) -> int:
+    return int(lib().lsa_attention_default_splits(rows, L_max))
 
 
 def top_buckets(p: Params) -> int:

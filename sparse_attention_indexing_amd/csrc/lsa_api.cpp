@@ -556,6 +556,13 @@ int64_t lsa_attention_workspace_bytes(int32_t B, int64_t Tq, int32_t Hq, int32_t
   return rows * splits * Hq * ((int64_t)kHeadDim + 2) * 4;
 }
 
+int32_t lsa_attention_default_splits(int64_t rows, int32_t L_max) {
+  if (rows <= 0 || L_max <= 0) return 1;
+  int32_t splits = 1;
+  while (splits < 256 && rows * splits < 512 && L_max / (2 * splits) >= 32) splits *= 2;
+  return splits;
+}
+
 int lsa_sparse_attention(const void* q, const void* k_cache, const void* v_cache, int32_t B,
                          int64_t Tq, int64_t Tmax, int32_t Hq, int32_t Hkv, int32_t D,
                          const int32_t* idx, const int32_t* count, int32_t L_max, float scale,
@@ -568,6 +575,7 @@ int lsa_sparse_attention(const void* q, const void* k_cache, const void* v_cache
   if ((int64_t)B * Tq == 0) return LSA_OK;
   if (!q || !k_cache || !v_cache || !idx || !count || !out) return LSA_ERR_ARG;
   if ((int64_t)B * Tq > (int64_t)0x7fffffff || splits > 65535) return LSA_ERR_UNSUPPORTED;
+  if (splits > 1 && (int64_t)B * Tq * Hq * 4 > (int64_t)0x7fffffff) return LSA_ERR_UNSUPPORTED;
   const int64_t need = lsa_attention_workspace_bytes(B, Tq, Hq, D, splits);
   if (need > 0 && (!workspace || ws_bytes < need)) return LSA_ERR_WORKSPACE;
   hipError_t e = launch_attention(q, k_cache, v_cache, B, Tq, Tmax, Hq, Hkv, idx, count, L_max,

@@ -110,11 +110,15 @@ __global__ __launch_bounds__(64 * kMaxWaves, 3) void k_attn_bf16(AttnArgs a) {
   extern __shared__ uint16_t attn_lds[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nwaves = blockDim.x >> 6;
-  // Workgroups are dealt to the 8 XCDs round-robin; give each XCD a contiguous
-  // range of rows so neighbouring queries (shared window, similar buckets)
-  // meet in the same L2.
-  const int64_t per_xcd = (a.rows + 7) / 8;
-  const int64_t row = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  // Workgroups are dealt to the 8 XCDs round-robin; with 8+ rows give each
+  // XCD a contiguous range of rows so neighbouring queries (shared window,
+  // similar buckets) meet in the same L2; with fewer rows grid.x = rows and
+  // the splits of a row spread over the XCDs.
+  int64_t row = blockIdx.x;
+  if (a.rows >= 8) {
+    const int64_t per_xcd = (a.rows + 7) / 8;
+    row = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  }
   if (row >= a.rows) return;
   const int split = blockIdx.y;
   const int64_t b = row / a.Tq;
@@ -301,8 +305,14 @@ __device__ __forceinline__ void g2lds16(const void* g, char* lds_row) {
 __global__ __launch_bounds__(256, 2) void k_attn_bf16_h4(AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds3[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t per_xcd = (a.rows + 7) / 8;
-  const int64_t row = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  // with 8+ rows, workgroups of consecutive rows (which share many keys) go
+  // to the same XCD; with fewer rows grid.x = rows and the splits of a row
+  // spread over the XCDs
+  int64_t row = blockIdx.x;
+  if (a.rows >= 8) {
+    const int64_t per_xcd = (a.rows + 7) / 8;
+    row = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  }
   if (row >= a.rows) return;
   const int split = blockIdx.y;
   const int64_t b = row / a.Tq;
@@ -545,50 +555,66 @@ __global__ __launch_bounds__(64) void k_attn_f32(AttnArgsF32 a) {
 }
 
 // Combine split partials: out = sum_s e^(m_s - M) O_s / sum_s e^(m_s - M) l_s.
+// One workgroup per (row, head, 32-dim quarter): thread t owns dims
+// 4 (t % 8) .. +3 of the quarter and splits t / 8, t / 8 + 32, ...; the 32
+// split groups meet in LDS.  All loads of a thread are independent, so a
+// row with many splits costs about one memory round trip.
 template <int DT>
-__global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ ws, void* out,
+__global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ ws, void* out,
                                                       int64_t rows, int32_t Hq, int32_t splits) {
-  const int64_t rh = blockIdx.x;           // row * Hq + h
+  __shared__ float s_m[32];
+  __shared__ float s_den[32];
+  __shared__ float4 s_num[32][8];
+  const int64_t rhq = blockIdx.x;          // (row * Hq + h) * 4 + quarter
+  const int64_t rh = rhq >> 2;
+  const int quarter = (int)(rhq & 3);
   const int64_t row = rh / Hq;
   const int h = (int)(rh % Hq);
-  const int d = threadIdx.x;
+  const int c = threadIdx.x & 7, g = threadIdx.x >> 3;
   const float* ob = ws;
   const float* mb = ws + rows * splits * Hq * kHeadDim;
   const float* lb = mb + rows * splits * Hq;
-  // splits in chunks of 16 whose loads are all issued before any use
+  float mg = -__builtin_inff();
+  for (int sp = g; sp < splits; sp += 32) mg = fmaxf(mg, mb[(row * splits + sp) * Hq + h]);
+  if (c == 0) s_m[g] = mg;
+  __syncthreads();
   float M = -__builtin_inff();
-  for (int s0 = 0; s0 < splits; s0 += 16) {
-    float mm[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
-      mm[j] = s0 + j < splits ? mb[(row * splits + s0 + j) * Hq + h] : -__builtin_inff();
-#pragma unroll
-    for (int j = 0; j < 16; ++j) M = fmaxf(M, mm[j]);
-  }
-  float num = 0.f, den = 0.f;
+  for (int i = 0; i < 32; ++i) M = fmaxf(M, s_m[i]);
+  float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+  float den = 0.f;
   if (M != -__builtin_inff()) {
-    for (int s0 = 0; s0 < splits; s0 += 16) {
-      float mm[16], oo[16], ll[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const bool ok = s0 + j < splits;
-        const int64_t slot = row * splits + (ok ? s0 + j : 0);
-        mm[j] = ok ? mb[slot * Hq + h] : -__builtin_inff();
-        oo[j] = ob[(slot * Hq + h) * kHeadDim + d];
-        ll[j] = lb[slot * Hq + h];
-      }
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        // a split with no keys has m = -inf and contributes nothing
-        const float w = mm[j] == -__builtin_inff() ? 0.f : __expf(mm[j] - M);
-        num = __builtin_fmaf(w, oo[j], num);
-        den = __builtin_fmaf(w, ll[j], den);
-      }
+    for (int sp = g; sp < splits; sp += 32) {
+      const int64_t slot = row * splits + sp;
+      const float m = mb[slot * Hq + h];
+      const float lv = lb[slot * Hq + h];
+      const float4 o = reinterpret_cast<const float4*>(ob + (slot * Hq + h) * kHeadDim + 32 * quarter)[c];
+      // a split with no keys has m = -inf and contributes nothing
+      const float w = m == -__builtin_inff() ? 0.f : __expf(m - M);
+      num.x = __builtin_fmaf(w, o.x, num.x);
+      num.y = __builtin_fmaf(w, o.y, num.y);
+      num.z = __builtin_fmaf(w, o.z, num.z);
+      num.w = __builtin_fmaf(w, o.w, num.w);
+      den = __builtin_fmaf(w, lv, den);
     }
   }
-  const float r = den > 0.f ? num / den : 0.f;
-  if (DT == LSA_BF16) reinterpret_cast<uint16_t*>(out)[rh * kHeadDim + d] = f32_to_bf16_rne(r);
-  else reinterpret_cast<float*>(out)[rh * kHeadDim + d] = r;
+  s_num[g][c] = num;
+  if (c == 0) s_den[g] = den;
+  __syncthreads();
+  if (threadIdx.x < 32) {
+    const int cc = threadIdx.x >> 2, e = threadIdx.x & 3;
+    float nn = 0.f, dd = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const float4 v = s_num[i][cc];
+      nn += e == 0 ? v.x : (e == 1 ? v.y : (e == 2 ? v.z : v.w));
+      dd += s_den[i];
+    }
+    const float r = dd > 0.f ? nn / dd : 0.f;
+    const int64_t oi = rh * kHeadDim + 32 * quarter + threadIdx.x;
+    if (DT == LSA_BF16) reinterpret_cast<uint16_t*>(out)[oi] = f32_to_bf16_rne(r);
+    else reinterpret_cast<float*>(out)[oi] = r;
+  }
 }
 
 }  // namespace
@@ -614,12 +640,12 @@ hipError_t launch_attention(const void* q, const void* k, const void* v, int32_t
         (void)hipGetLastError();
         attr3 = true;
       }
-      const int64_t grid = (rows + 7) / 8 * 8;
+      const int64_t grid = rows >= 8 ? (rows + 7) / 8 * 8 : rows;
       hipLaunchKernelGGL(k_attn_bf16_h4, dim3((unsigned)grid, (unsigned)splits), dim3(256),
                          (size_t)kLds3, s, a);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess || splits == 1) return e;
-      hipLaunchKernelGGL(k_attn_combine<LSA_BF16>, dim3((unsigned)(rows * Hq)), dim3(kHeadDim), 0,
+      hipLaunchKernelGGL(k_attn_combine<LSA_BF16>, dim3((unsigned)(rows * Hq * 4)), dim3(256), 0,
                          s, ws, out, rows, Hq, splits);
       return hipGetLastError();
     }
@@ -633,7 +659,7 @@ hipError_t launch_attention(const void* q, const void* k, const void* v, int32_t
     }
     const int per = (L_max + splits - 1) / splits;
     const size_t smem = (size_t)nw * kWaveLds * sizeof(uint16_t) + (size_t)per * sizeof(int32_t);
-    const int64_t grid = (rows + 7) / 8 * 8;
+    const int64_t grid = rows >= 8 ? (rows + 7) / 8 * 8 : rows;
     hipLaunchKernelGGL(k_attn_bf16, dim3((unsigned)grid, (unsigned)splits), dim3(64 * nw), smem, s, a);
   } else {
     AttnArgsF32 a;
@@ -646,10 +672,10 @@ hipError_t launch_attention(const void* q, const void* k, const void* v, int32_t
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   if (dtype == LSA_BF16)
-    hipLaunchKernelGGL(k_attn_combine<LSA_BF16>, dim3((unsigned)(rows * Hq)), dim3(kHeadDim), 0, s,
+    hipLaunchKernelGGL(k_attn_combine<LSA_BF16>, dim3((unsigned)(rows * Hq * 4)), dim3(256), 0, s,
                        ws, out, rows, Hq, splits);
   else
-    hipLaunchKernelGGL(k_attn_combine<LSA_F32>, dim3((unsigned)(rows * Hq)), dim3(kHeadDim), 0, s,
+    hipLaunchKernelGGL(k_attn_combine<LSA_F32>, dim3((unsigned)(rows * Hq * 4)), dim3(256), 0, s,
                        ws, out, rows, Hq, splits);
   return hipGetLastError();
 }

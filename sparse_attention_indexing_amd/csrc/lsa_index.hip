@@ -858,7 +858,7 @@ __global__ __launch_bounds__(256) void k_fill_u32(uint32_t* p, int64_t n, uint32
 // Eight lanes share a centroid row (16 B = 8 dims each), so one wave-wide
 // load reads 8 consecutive rows (1 KiB, fully coalesced) and the partial dot
 // products are summed across the 8 lanes; each lane keeps 8 loads in flight.
-constexpr int kDecRowsPerWg = 1024;     // buckets per filter workgroup
+constexpr int kDecMinRowsPerWg = 1024;  // fewest buckets per filter workgroup
 constexpr int kDecSampPerWg = 512;      // sampled buckets per threshold workgroup
 
 __device__ __forceinline__ void load_q8(float (&yq)[8], const void* yhat, int64_t qi, int sub) {
@@ -947,28 +947,38 @@ __device__ __forceinline__ float dec_tau_wave(const IndexCtx& ctx, const IndexWs
   return __shfl(tau, l, 64);
 }
 
-// grid.x = chunks of kDecRowsPerWg buckets, grid.y = query (sequence).
-// Scores >= tau are staged per wave in LDS and flushed with one atomic; the
-// candidate count starts at zero (k_dec_prep).
-__global__ __launch_bounds__(256) void k_dec_filter(IndexCtx ctx, IndexWs ws) {
+// grid.x = chunks of `rows_per_wg` buckets (a multiple of 256), grid.y =
+// query (sequence).  Scores >= tau are staged per wave in LDS; at the end the
+// workgroup reserves its slots with one atomic (a sequence's counter is hit
+// once per workgroup, not once per wave, so the same-address atomics that
+// end every workgroup stay few).  The candidate count starts at zero
+// (k_dec_prep).  Each wave keeps two batches of 8 row loads in flight.
+__global__ __launch_bounds__(256) void k_dec_filter(IndexCtx ctx, IndexWs ws, int rows_per_wg) {
   __shared__ uint2 s_buf[4][kDecStage];
+  __shared__ int s_cnt[4];
+  __shared__ int s_base;
   const int64_t qi = blockIdx.y;
   const int64_t ne = n_eligible(ctx.pos[qi]);
-  const int64_t r0 = (int64_t)blockIdx.x * kDecRowsPerWg;
-  if (r0 >= ne) return;
-  const int64_t r1 = r0 + kDecRowsPerWg < ne ? r0 + kDecRowsPerWg : ne;
+  const int64_t r0 = (int64_t)blockIdx.x * rows_per_wg;
+  if (r0 >= ne) return;                                  // uniform over the workgroup
+  const int64_t r1 = r0 + rows_per_wg < ne ? r0 + rows_per_wg : ne;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int sub = lane & 7, grp = lane >> 3;
+  const uint4* cent = reinterpret_cast<const uint4*>(ctx.cent[qi]);
+  const int64_t rlast = r1 - 1;
+  int64_t rb = r0 + 64 * wave;
+  uint4 ua[8], ub[8];
+  load_rows8(ua, cent, rb, rlast, grp, sub);            // in flight while tau is derived
   float yq[8];
   load_q8(yq, ws.yhat, qi, sub);
   // every wave derives tau from the sampled histogram (the same value)
   const float tau = dec_tau_wave(ctx, ws, qi, lane);
-  const uint4* cent = reinterpret_cast<const uint4*>(ctx.cent[qi]);
   uint2* cand = ws.cand + qi * (int64_t)ctx.cap;
   uint2* stage = s_buf[wave];
   int cnt = 0;                                           // wave-uniform
-  auto flush = [&]() {
+  // a full stage goes out on its own (rare: the stage holds 64 candidates)
+  auto flush_wave = [&]() {
     __builtin_amdgcn_wave_barrier();
     int base = 0;
     if (lane == 0) base = atomicAdd(&ws.cand_cnt[qi], cnt);
@@ -977,20 +987,20 @@ __global__ __launch_bounds__(256) void k_dec_filter(IndexCtx ctx, IndexWs ws) {
     __builtin_amdgcn_wave_barrier();
     cnt = 0;
   };
-  auto process = [&](const uint4 (&u)[8], int64_t rb) {
-    float s[8];
+  auto process = [&](const uint4 (&u)[8], int64_t rbb) {
+    float sc[8];
     uint64_t m[8];
     int npass = 0;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      s[k] = sum8(dot8(u[k], yq));
-      const bool pass = (sub == 0) & (rb + 8 * k + grp < r1) & (s[k] >= tau);
+      sc[k] = sum8(dot8(u[k], yq));
+      const bool pass = (sub == 0) & (rbb + 8 * k + grp < r1) & (sc[k] >= tau);
       m[k] = __ballot(pass);
       npass += __popcll(m[k]);
     }
     npass = __builtin_amdgcn_readfirstlane(npass);
     if (npass == 0) return;
-    if (cnt + npass > kDecStage) flush();
+    if (cnt + npass > kDecStage) flush_wave();
     int base = cnt;
     uint2* dst = stage;
     if (npass > kDecStage) {                               // only when every row passes
@@ -1005,22 +1015,38 @@ __global__ __launch_bounds__(256) void k_dec_filter(IndexCtx ctx, IndexWs ws) {
         const int slot = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m[k] >> 32),
                                      __builtin_amdgcn_mbcnt_lo((uint32_t)m[k], 0u));
         if (dst != cand || slot < ctx.cap)
-          dst[slot] = make_uint2(__float_as_uint(s[k]), (uint32_t)(rb + 8 * k + grp));
+          dst[slot] = make_uint2(__float_as_uint(sc[k]), (uint32_t)(rbb + 8 * k + grp));
       }
       base += __popcll(m[k]);
     }
     if (dst == stage) cnt += npass;
   };
-  // one batch of 8 loads per wave at a time; latency is covered by the many
-  // resident waves (small register footprint), not by software pipelining
-  const int64_t rlast = r1 - 1;
-  for (int64_t rb = r0 + 64 * wave; rb < r1; rb += 256) {
-    uint4 u[8];
-    load_rows8(u, cent, rb, rlast, grp, sub);
-    __builtin_amdgcn_sched_barrier(0);   // all 8 loads before any use
-    process(u, rb);
+  // batches of 64 rows per wave, 256 rows per workgroup step; the next
+  // batch is requested before the current one is used (loads past r1 are
+  // clamped to the last row and masked in process)
+  for (;; rb += 512) {
+    load_rows8(ub, cent, rb + 256, rlast, grp, sub);
+    __builtin_amdgcn_sched_barrier(0);
+    if (rb < r1) process(ua, rb);
+    if (rb + 256 >= r1) break;
+    load_rows8(ua, cent, rb + 512, rlast, grp, sub);
+    __builtin_amdgcn_sched_barrier(0);
+    process(ub, rb + 256);
+    if (rb + 512 >= r1) break;
   }
-  if (cnt) flush();
+  // one reservation per workgroup for what the waves still hold
+  if (threadIdx.x < 4) s_cnt[threadIdx.x] = 0;
+  __syncthreads();
+  if (lane == 0) s_cnt[wave] = cnt;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int tot = s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
+    s_base = tot > 0 ? atomicAdd(&ws.cand_cnt[qi], tot) : 0;
+  }
+  __syncthreads();
+  int off = s_base;
+  for (int w = 0; w < wave; ++w) off += s_cnt[w];
+  if (lane < cnt && off + lane < ctx.cap) cand[off + lane] = stage[lane];
 }
 
 // Sampled histogram for the decode threshold: grid.x = chunks of
@@ -1805,8 +1831,14 @@ hipError_t launch_score_filter(const IndexCtx& ctx, const IndexWs& ws, int dtype
     return hipGetLastError();
   }
   if (ctx.per_seq && dtype == LSA_BF16) {
-    const int64_t gx = (max_tiles * kTile + kDecRowsPerWg - 1) / kDecRowsPerWg;
-    hipLaunchKernelGGL(k_dec_filter, dim3((unsigned)gx, (unsigned)ctx.n), dim3(256), 0, s, ctx, ws);
+    // about 1,024 workgroups in all, at least kDecMinRowsPerWg buckets each
+    const int64_t rows = max_tiles * kTile;
+    int64_t steps = (rows * ctx.n + 1024 * 256 - 1) / (1024 * 256);
+    if (steps < kDecMinRowsPerWg / 256) steps = kDecMinRowsPerWg / 256;
+    const int64_t per = 256 * steps;
+    const int64_t gx = (rows + per - 1) / per;
+    hipLaunchKernelGGL(k_dec_filter, dim3((unsigned)gx, (unsigned)ctx.n), dim3(256), 0, s, ctx, ws,
+                       (int)per);
     return hipGetLastError();
   }
   // decode has few queries: shorter segments give enough workgroups to stream HBM

@@ -174,15 +174,20 @@ def test_attention_f32_on_oracle_lists():
     assert err <= 1e-4
 
 
-@pytest.mark.parametrize("splits", [1, 3])
-def test_attention_bf16_on_oracle_lists(splits):
-    say(f"case: attention bf16 splits={splits}")
+@pytest.mark.parametrize("splits,few", [(1, False), (3, False), (64, True), (200, True)])
+def test_attention_bf16_on_oracle_lists(splits, few):
+    """Many rows (XCD-grouped workgroups) and, as in decode, a few rows whose
+    lists are cut into many splits (more than the combine's 32 split groups)."""
+    say(f"case: attention bf16 splits={splits} few_rows={few}")
     w = S.WORKLOADS[2]
     T = 8192
     X, Y, _ = S.latent_inputs(w, T=T, query_rows=(0, T))
     p = lsa.Params(k=2048, index_dtype=lsa.LSA_BF16)
     oc = O.build_cache(X, oracle_params(p))
-    rows = np.concatenate([[0, 1, 5, 600], np.arange(2000, T, 397), [T - 1]])
+    if few:
+        rows = np.array([T - 1, 5000, 600])
+    else:
+        rows = np.concatenate([[0, 1, 5, 600], np.arange(2000, T, 397), [T - 1]])
     q, k, v, qb, kb, vb = _qkv_host(w, T, rows)
     res = [O.index_query(Y[r], int(r), oc) for r in rows]
     idx = np.stack([r.idx for r in res]).astype(np.int32)
