@@ -575,7 +575,7 @@ int lsa_sparse_attention(const void* q, const void* k_cache, const void* v_cache
   if ((int64_t)B * Tq == 0) return LSA_OK;
   if (!q || !k_cache || !v_cache || !idx || !count || !out) return LSA_ERR_ARG;
   if ((int64_t)B * Tq > (int64_t)0x7fffffff || splits > 65535) return LSA_ERR_UNSUPPORTED;
-  if (splits > 1 && (int64_t)B * Tq * Hq * 4 > (int64_t)0x7fffffff) return LSA_ERR_UNSUPPORTED;
+  if (splits > 1 && (int64_t)B * Tq * Hq * 2 > (int64_t)0x7fffffff) return LSA_ERR_UNSUPPORTED;
   const int64_t need = lsa_attention_workspace_bytes(B, Tq, Hq, D, splits);
   if (need > 0 && (!workspace || ws_bytes < need)) return LSA_ERR_WORKSPACE;
   hipError_t e = launch_attention(q, k_cache, v_cache, B, Tq, Tmax, Hq, Hkv, idx, count, L_max,

@@ -555,63 +555,71 @@ __global__ __launch_bounds__(64) void k_attn_f32(AttnArgsF32 a) {
 }
 
 // Combine split partials: out = sum_s e^(m_s - M) O_s / sum_s e^(m_s - M) l_s.
-// One workgroup per (row, head, 32-dim quarter): thread t owns dims
-// 4 (t % 8) .. +3 of the quarter and splits t / 8, t / 8 + 32, ...; the 32
-// split groups meet in LDS.  All loads of a thread are independent, so a
-// row with many splits costs about one memory round trip.
+// One workgroup per (row, head, 64-dim half): thread t owns dims
+// 4 (t % 16) .. +3 of the half and splits t / 16, t / 16 + 16, ...; each
+// thread keeps its sums relative to its own running max (loads of four
+// splits in flight at a time), and the 16 split groups meet in LDS.
 template <int DT>
 __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ ws, void* out,
                                                       int64_t rows, int32_t Hq, int32_t splits) {
-  __shared__ float s_m[32];
-  __shared__ float s_den[32];
-  __shared__ float4 s_num[32][8];
-  const int64_t rhq = blockIdx.x;          // (row * Hq + h) * 4 + quarter
-  const int64_t rh = rhq >> 2;
-  const int quarter = (int)(rhq & 3);
+  __shared__ float s_m[16];
+  __shared__ float s_den[16];
+  __shared__ float4 s_num[16][16];
+  const int64_t rhh = blockIdx.x;          // (row * Hq + h) * 2 + half
+  const int64_t rh = rhh >> 1;
+  const int hf = (int)(rhh & 1);
   const int64_t row = rh / Hq;
   const int h = (int)(rh % Hq);
-  const int c = threadIdx.x & 7, g = threadIdx.x >> 3;
+  const int c = threadIdx.x & 15, g = threadIdx.x >> 4;
   const float* ob = ws;
   const float* mb = ws + rows * splits * Hq * kHeadDim;
   const float* lb = mb + rows * splits * Hq;
-  float mg = -__builtin_inff();
-  for (int sp = g; sp < splits; sp += 32) mg = fmaxf(mg, mb[(row * splits + sp) * Hq + h]);
-  if (c == 0) s_m[g] = mg;
-  __syncthreads();
-  float M = -__builtin_inff();
-#pragma unroll
-  for (int i = 0; i < 32; ++i) M = fmaxf(M, s_m[i]);
+  float mg = -__builtin_inff(), den = 0.f;
   float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
-  float den = 0.f;
-  if (M != -__builtin_inff()) {
-    for (int sp = g; sp < splits; sp += 32) {
-      const int64_t slot = row * splits + sp;
-      const float m = mb[slot * Hq + h];
-      const float lv = lb[slot * Hq + h];
-      const float4 o = reinterpret_cast<const float4*>(ob + (slot * Hq + h) * kHeadDim + 32 * quarter)[c];
-      // a split with no keys has m = -inf and contributes nothing
-      const float w = m == -__builtin_inff() ? 0.f : __expf(m - M);
-      num.x = __builtin_fmaf(w, o.x, num.x);
-      num.y = __builtin_fmaf(w, o.y, num.y);
-      num.z = __builtin_fmaf(w, o.z, num.z);
-      num.w = __builtin_fmaf(w, o.w, num.w);
-      den = __builtin_fmaf(w, lv, den);
+  for (int s0 = g; s0 < splits; s0 += 64) {
+    float m[4], lv[4];
+    float4 o[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int sp = s0 + 16 * u;
+      const int64_t slot = row * splits + (sp < splits ? sp : 0);
+      m[u] = sp < splits ? mb[slot * Hq + h] : -__builtin_inff();
+      lv[u] = lb[slot * Hq + h];
+      o[u] = reinterpret_cast<const float4*>(ob + (slot * Hq + h) * kHeadDim + 64 * hf)[c];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (m[u] == -__builtin_inff()) continue;   // no keys in this split
+      const float mn = fmaxf(mg, m[u]);
+      const float a = __expf(mg - mn), w = __expf(m[u] - mn);   // mg = -inf gives a = 0
+      num.x = num.x * a + w * o[u].x;
+      num.y = num.y * a + w * o[u].y;
+      num.z = num.z * a + w * o[u].z;
+      num.w = num.w * a + w * o[u].w;
+      den = den * a + w * lv[u];
+      mg = mn;
     }
   }
+  if (c == 0) { s_m[g] = mg; s_den[g] = den; }
   s_num[g][c] = num;
-  if (c == 0) s_den[g] = den;
   __syncthreads();
-  if (threadIdx.x < 32) {
+  if (threadIdx.x < 64) {
     const int cc = threadIdx.x >> 2, e = threadIdx.x & 3;
-    float nn = 0.f, dd = 0.f;
+    float M = -__builtin_inff();
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const float4 v = s_num[i][cc];
-      nn += e == 0 ? v.x : (e == 1 ? v.y : (e == 2 ? v.z : v.w));
-      dd += s_den[i];
+    for (int i = 0; i < 16; ++i) M = fmaxf(M, s_m[i]);
+    float nn = 0.f, dd = 0.f;
+    if (M != -__builtin_inff()) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float w = s_m[i] == -__builtin_inff() ? 0.f : __expf(s_m[i] - M);
+        const float4 v = s_num[i][cc];
+        nn = __builtin_fmaf(w, e == 0 ? v.x : (e == 1 ? v.y : (e == 2 ? v.z : v.w)), nn);
+        dd = __builtin_fmaf(w, s_den[i], dd);
+      }
     }
     const float r = dd > 0.f ? nn / dd : 0.f;
-    const int64_t oi = rh * kHeadDim + 32 * quarter + threadIdx.x;
+    const int64_t oi = rh * kHeadDim + 64 * hf + threadIdx.x;
     if (DT == LSA_BF16) reinterpret_cast<uint16_t*>(out)[oi] = f32_to_bf16_rne(r);
     else reinterpret_cast<float*>(out)[oi] = r;
   }
@@ -645,7 +653,7 @@ hipError_t launch_attention(const void* q, const void* k, const void* v, int32_t
                          (size_t)kLds3, s, a);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess || splits == 1) return e;
-      hipLaunchKernelGGL(k_attn_combine<LSA_BF16>, dim3((unsigned)(rows * Hq * 4)), dim3(256), 0,
+      hipLaunchKernelGGL(k_attn_combine<LSA_BF16>, dim3((unsigned)(rows * Hq * 2)), dim3(256), 0,
                          s, ws, out, rows, Hq, splits);
       return hipGetLastError();
     }
@@ -672,10 +680,10 @@ hipError_t launch_attention(const void* q, const void* k, const void* v, int32_t
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   if (dtype == LSA_BF16)
-    hipLaunchKernelGGL(k_attn_combine<LSA_BF16>, dim3((unsigned)(rows * Hq * 4)), dim3(256), 0, s,
+    hipLaunchKernelGGL(k_attn_combine<LSA_BF16>, dim3((unsigned)(rows * Hq * 2)), dim3(256), 0, s,
                        ws, out, rows, Hq, splits);
   else
-    hipLaunchKernelGGL(k_attn_combine<LSA_F32>, dim3((unsigned)(rows * Hq * 4)), dim3(256), 0, s,
+    hipLaunchKernelGGL(k_attn_combine<LSA_F32>, dim3((unsigned)(rows * Hq * 2)), dim3(256), 0, s,
                        ws, out, rows, Hq, splits);
   return hipGetLastError();
 }

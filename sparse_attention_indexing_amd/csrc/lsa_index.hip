@@ -1137,7 +1137,10 @@ __device__ __forceinline__ void load_yq(float* yq, const void* yhat, int64_t qi)
 }
 
 // 256-thread exclusive prefix sum; returns the exclusive value, *total = sum.
-__device__ __forceinline__ int block_scan_excl(int v, int* wsum, int* total) {
+// Exclusive prefix sum of one int per thread over a workgroup of NT threads
+// (wsum: NT / 64 ints of LDS); *total receives the sum of all.
+template <int NT>
+__device__ __forceinline__ int block_scan_nt(int v, int* wsum, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int x = v;
 #pragma unroll
@@ -1149,7 +1152,7 @@ __device__ __forceinline__ int block_scan_excl(int v, int* wsum, int* total) {
   __syncthreads();
   int base = 0, tot = 0;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
+  for (int w = 0; w < NT / 64; ++w) {
     if (w < wave) base += wsum[w];
     tot += wsum[w];
   }
@@ -1158,13 +1161,17 @@ __device__ __forceinline__ int block_scan_excl(int v, int* wsum, int* total) {
   return base + x - v;
 }
 
+__device__ __forceinline__ int block_scan_excl(int v, int* wsum, int* total) {
+  return block_scan_nt<256>(v, wsum, total);
+}
+
 // Exact top-B of one query, for a workgroup whose candidate list is unusable
 // (fewer than B or more than `cap` candidates) or when exact selection is
 // forced: the B-th largest score by 4 radix passes of 8 bits over the
 // order-preserving integer image of the fp32 score, then every bucket above
 // it and, among buckets equal to it, the lowest.  Writes raw score bits to
 // skey[] and buckets to sbkt[] (LDS) and returns the count (min(B, ne)).
-template <int DT>
+template <int DT, int NT = 256>
 __device__ int exact_select_lds(const IndexCtx& ctx, const IndexWs& ws, int64_t qi, int64_t ne,
                                 int64_t beff, uint32_t* skey, uint32_t* sbkt, uint32_t* hist,
                                 uint32_t* s_prefix, uint32_t* s_want, int* wsum, int* s_out) {
@@ -1177,9 +1184,9 @@ __device__ int exact_select_lds(const IndexCtx& ctx, const IndexWs& ws, int64_t 
   if (tid == 0) *s_out = 0;
   if (beff > 0) {
     for (int shift = 24; shift >= 0; shift -= 8) {
-      hist[tid] = 0;
+      for (int b = tid; b < 256; b += NT) hist[b] = 0;
       __syncthreads();
-      for (int64_t g = tid; g < ne; g += 256) {
+      for (int64_t g = tid; g < ne; g += NT) {
         const uint32_t key = f32_orderable(vscore<DT>(cent, g, yq));
         if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
       }
@@ -1202,7 +1209,7 @@ __device__ int exact_select_lds(const IndexCtx& ctx, const IndexWs& ws, int64_t 
       __syncthreads();
     }
     int eq_base = 0;
-    for (int64_t g0 = 0; g0 < ne; g0 += 256) {
+    for (int64_t g0 = 0; g0 < ne; g0 += NT) {
       const int64_t g = g0 + tid;
       float s = 0.f;
       uint32_t key = 0;
@@ -1210,7 +1217,7 @@ __device__ int exact_select_lds(const IndexCtx& ctx, const IndexWs& ws, int64_t 
       const int gt = (g < ne) && key > prefix;
       const int eq = (g < ne) && key == prefix;
       int eq_tot;
-      const int eq_rank = eq_base + block_scan_excl(eq, wsum, &eq_tot);
+      const int eq_rank = eq_base + block_scan_nt<NT>(eq, wsum, &eq_tot);
       if (gt || (eq && eq_rank < (int)want)) {
         const int slot = atomicAdd(s_out, 1);
         if (slot < ctx.cap) { skey[slot] = __float_as_uint(s); sbkt[slot] = (uint32_t)g; }

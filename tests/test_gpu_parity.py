@@ -108,6 +108,35 @@ def test_index_sampled_threshold(k, exact):
     say("index", rep)
 
 
+@pytest.mark.parametrize("k,exact", [(256, 0), (2048, 0), (2048, 1)])
+def test_index_few_queries(k, exact):
+    """A few queries, as in decode: lists against the oracle, and the kept
+    buckets in rank order (the optional `ranked` output) against the oracle's
+    ranking, up to near ties."""
+    say(f"case: index few queries T=32768 k={k} exact={exact}")
+    w = S.WORKLOADS[2]
+    T, Tq = 32768, 200
+    X, Y, _ = S.latent_inputs(w, T=T, query_rows=(T - Tq, T))
+    p = lsa.Params(k=k, index_dtype=lsa.LSA_BF16, exact_select=exact)
+    c = gpu_cache(X, p)
+    idx, cnt, rk = lsa.index_prefill(c, torch.from_numpy(Y).cuda(), T - Tq, p, ranked=True)
+    torch.cuda.synchronize()
+    oc = O.build_cache(X, oracle_params(p))
+    rows = np.arange(0, Tq, 7)
+    rep = compare_lists(idx.cpu().numpy()[rows], cnt.cpu().numpy()[rows], T - Tq + rows, Y[rows], oc)
+    say("index", rep)
+    rk = rk.cpu().numpy()
+    prm = oracle_params(p)
+    for r in rows:
+        pos = T - Tq + int(r)
+        order, sc = O.flat_rank(O.normalize_query(Y[r], prm.index_dtype), oc, pos)
+        nb = min(lsa.top_buckets(p), len(order))
+        got = rk[r, :nb]
+        assert np.all(rk[r, nb:] == -1)
+        assert len(np.unique(got)) == nb and got.min() >= 0
+        assert np.all(np.abs(sc[got] - sc[order[:nb]]) < 1e-5), f"ranking at position {pos}"
+
+
 def test_index_last_chunk_and_determinism():
     say("case: index last chunk, twice")
     w = S.WORKLOADS[2]
