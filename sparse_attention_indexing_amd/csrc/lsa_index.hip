@@ -16,13 +16,15 @@
 //   1. k_thresh: bf16 MFMA scores on a 1/16 sample of bucket tiles, a per-query
 //      histogram, and a threshold tau whose expected pass count is ~2x the
 //      number of buckets kept (B);
-//   2. k_score_filter: every eligible score on MFMA; scores >= tau are
-//      appended (score, bucket) to a per-query candidate list;
-//   3. k_exact_select: queries whose list holds fewer than B or more than
-//      `cap` candidates are redone exactly (radix select on recomputed
-//      scores, ties to the lower bucket);
-//   4. k_select_expand: sort candidates by (score desc, bucket asc), keep B,
-//      expand, sort the far keys, write sinks | far | window.
+//   2. k_score_lowpass / k_score_highpass (k_dec_filter in decode): every
+//      eligible score on MFMA; scores >= tau are appended (score, bucket) to
+//      a per-query candidate list;
+//   3. k_select_expand: a query whose list holds fewer than B or more than
+//      `cap` candidates is first redone exactly (radix select on recomputed
+//      scores, ties to the lower bucket); then the buckets are taken in
+//      (score desc, bucket asc) order until k far keys are reached (weighted
+//      radix select), expanded, the far keys sorted, and sinks | far |
+//      window written.
 // Every bucket with a score >= the B-th best score is a candidate, so the
 // kept set equals the exact top-B whenever step 2 did not overflow.
 #include "lsa_internal.h"
