@@ -1236,31 +1236,39 @@ __device__ int exact_select_lds(const IndexCtx& ctx, const IndexWs& ws, int64_t 
 // One wave per query.  Beam descent from the root, keeping the best `beam`
 // eligible children (score desc, node asc) on every level down to lstar; then
 // every eligible bucket under the final beam becomes a candidate.
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-  const uint32_t lo = __shfl_xor((uint32_t)v, m, 64);
-  const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m, 64);
-  return ((uint64_t)hi << 32) | lo;
+// The `keep` largest of up to 128 unique nonzero 64-bit keys held two per lane
+// (zero = empty): the keep-th largest upper half (score) by a bitwise search
+// with wave ballots, then, only when that score is tied, the same search on
+// the lower half among the tied keys.  Returns each lane's two "selected"
+// flags; exactly `keep` keys are selected (keep <= number of nonzero keys).
+__device__ __forceinline__ uint32_t kth_largest_u32(uint32_t a, uint32_t b, bool va, bool vb,
+                                                    int keep) {
+  uint32_t prefix = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = prefix | (1u << bit);
+    const int cnt = __popcll(__ballot(va && a >= cand)) + __popcll(__ballot(vb && b >= cand));
+    if (cnt >= keep) prefix = cand;
+  }
+  return prefix;
 }
 
-// Sort 128 keys held two per lane (element lane and lane + 64) in descending order.
-__device__ __forceinline__ void wave_bitonic128_desc(uint64_t& e0, uint64_t& e1) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int k = 2; k <= 128; k <<= 1) {
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      if (j == 64) {  // k == 128: pairs (lane, lane + 64), lower index takes the max
-        const uint64_t a = e0, b = e1;
-        e0 = a > b ? a : b;
-        e1 = a > b ? b : a;
-      } else {
-        const uint64_t o0 = shfl_xor_u64(e0, j), o1 = shfl_xor_u64(e1, j);
-        const bool lower = (lane & j) == 0;
-        const bool d0 = (lane & k) == 0, d1 = ((lane + 64) & k) == 0;
-        e0 = (lower == d0) ? (e0 > o0 ? e0 : o0) : (e0 > o0 ? o0 : e0);
-        e1 = (lower == d1) ? (e1 > o1 ? e1 : o1) : (e1 > o1 ? o1 : e1);
-      }
-    }
+__device__ __forceinline__ void wave_select_top(uint64_t e0, uint64_t e1, int keep, bool& s0,
+                                                bool& s1) {
+  const uint32_t u0 = (uint32_t)(e0 >> 32), u1 = (uint32_t)(e1 >> 32);
+  const uint32_t smin = kth_largest_u32(u0, u1, true, true, keep);
+  const int gt = __popcll(__ballot(u0 > smin)) + __popcll(__ballot(u1 > smin));
+  const bool q0 = u0 == smin, q1 = u1 == smin;
+  const int eq = __popcll(__ballot(q0)) + __popcll(__ballot(q1));
+  const int need = keep - gt;
+  if (need == eq) {
+    s0 = u0 >= smin;
+    s1 = u1 >= smin;
+  } else {
+    // tied scores: the lower halves (complemented node ids) break the tie
+    const uint32_t v0 = (uint32_t)e0, v1 = (uint32_t)e1;
+    const uint32_t vmin = kth_largest_u32(v0, v1, q0, q1, need);
+    s0 = u0 > smin || (q0 && v0 >= vmin);
+    s1 = u1 > smin || (q1 && v1 >= vmin);
   }
 }
 
@@ -1306,13 +1314,19 @@ __global__ __launch_bounds__(64) void k_tree_search(IndexCtx ctx, TreeCtx tc, In
         }
       }
     }
-    // valid entries are nonzero (orderable keys of finite scores have the top bit set or are > 0)
-    wave_bitonic128_desc(e[0], e[1]);
+    // valid entries are nonzero (the order-preserving image of a finite score
+    // is at least 0x00800000); the next beam is the set of the `keep` largest
+    // keys (score desc, node asc), in no particular order
     const int nvalid = __popcll(__ballot(e[0] != 0)) + __popcll(__ballot(e[1] != 0));
     const int keep = nvalid < tc.beam ? nvalid : tc.beam;
+    bool s0 = false, s1 = false;
+    if (keep > 0) wave_select_top(e[0], e[1], keep, s0, s1);
+    const uint64_t m0 = __ballot(s0), m1 = __ballot(s1);
+    const int p0 = __popcll(m0 & ((1ull << lane) - 1ull));
+    const int p1 = __popcll(m0) + __popcll(m1 & ((1ull << lane) - 1ull));
     __syncthreads();
-    if (lane < keep) beam[lane] = (int32_t)(0xFFFFFFFFu - (uint32_t)(e[0] & 0xFFFFFFFFu));
-    if (lane + 64 < keep) beam[lane + 64] = (int32_t)(0xFFFFFFFFu - (uint32_t)(e[1] & 0xFFFFFFFFu));
+    if (s0 && p0 < keep) beam[p0] = (int32_t)(0xFFFFFFFFu - (uint32_t)(e[0] & 0xFFFFFFFFu));
+    if (s1 && p1 < keep) beam[p1] = (int32_t)(0xFFFFFFFFu - (uint32_t)(e[1] & 0xFFFFFFFFu));
     nbeam = keep;
     __syncthreads();
   }
