@@ -1125,6 +1125,45 @@ __device__ __forceinline__ float vscore(const void* cent, int64_t g, const float
   return s;
 }
 
+// Scores of two rows (same summation order as vscore); both rows' loads are
+// issued before either product, then `between` runs (more independent
+// loads), then the products.
+template <int DT, class F>
+__device__ __forceinline__ void vscore2(const void* cent, int64_t ga, int64_t gb, const float* yq,
+                                        float& sa, float& sb, F between) {
+  if (DT == LSA_BF16) {
+    const uint4* pa = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(cent) + ga * kLatent);
+    const uint4* pb = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(cent) + gb * kLatent);
+    uint4 ua[8], ub[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ua[j] = pa[j];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ub[j] = pb[j];
+    __builtin_amdgcn_sched_barrier(0);
+    between();
+    __builtin_amdgcn_sched_barrier(0);
+    float x = 0.f, y = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t wa[4] = {ua[j].x, ua[j].y, ua[j].z, ua[j].w};
+      const uint32_t wb[4] = {ub[j].x, ub[j].y, ub[j].z, ub[j].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x = __builtin_fmaf(bf16_to_f32((uint16_t)(wa[e] & 0xffff)), yq[8 * j + 2 * e], x);
+        x = __builtin_fmaf(bf16_to_f32((uint16_t)(wa[e] >> 16)), yq[8 * j + 2 * e + 1], x);
+        y = __builtin_fmaf(bf16_to_f32((uint16_t)(wb[e] & 0xffff)), yq[8 * j + 2 * e], y);
+        y = __builtin_fmaf(bf16_to_f32((uint16_t)(wb[e] >> 16)), yq[8 * j + 2 * e + 1], y);
+      }
+    }
+    sa = x;
+    sb = y;
+  } else {
+    between();
+    sa = vscore<DT>(cent, ga, yq);
+    sb = vscore<DT>(cent, gb, yq);
+  }
+}
+
 template <int DT>
 __device__ __forceinline__ void load_yq(float* yq, const void* yhat, int64_t qi) {
   if (DT == LSA_BF16) {
@@ -1297,23 +1336,32 @@ __global__ __launch_bounds__(64) void k_tree_search(IndexCtx ctx, TreeCtx tc, In
   __syncthreads();
   int nbeam = 1;
   for (int lvl = tc.height - 1; lvl >= tc.lstar; --lvl) {
-    uint64_t e[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      e[h] = 0;
-      const int j = lane;  // beam slot
-      if (j < nbeam) {
-        const int32_t c = tc.child[lvl + 1][2 * beam[j] + h];
-        if (c >= 0) {
-          // the centroid is loaded together with the child's smallest block
-          // (not after it) and the score is masked afterwards
-          const int64_t mb = lvl == 0 ? (int64_t)c / kBuckets : (int64_t)tc.minb[lvl][c];
-          const float s = vscore<DT>(tc.cent[lvl], c, yq);
-          if (mb < qb)
-            e[h] = ((uint64_t)f32_orderable(s) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)c);
-        }
-      }
+    // both children of beam slot `lane`: one 8-byte load of the pair, then
+    // both centroids and smallest blocks together (index 0 stands in for a
+    // missing child and is masked afterwards)
+    const int32_t* chl = tc.child[lvl + 1];
+    const void* cl = tc.cent[lvl];
+    const int32_t* mbl = tc.minb[lvl];
+    int32_t c0 = -1, c1 = -1;
+    if (lane < nbeam) {
+      const int2 cc = reinterpret_cast<const int2*>(chl)[beam[lane]];
+      c0 = cc.x;
+      c1 = cc.y;
     }
+    const int32_t g0 = c0 >= 0 ? c0 : 0, g1 = c1 >= 0 ? c1 : 0;
+    int64_t mb0 = (int64_t)g0 / kBuckets, mb1 = (int64_t)g1 / kBuckets;
+    float sc0, sc1;
+    vscore2<DT>(cl, g0, g1, yq, sc0, sc1, [&]() {
+      if (lvl > 0) {
+        mb0 = mbl[g0];
+        mb1 = mbl[g1];
+      }
+    });
+    uint64_t e[2];
+    e[0] = (c0 >= 0 && mb0 < qb)
+               ? ((uint64_t)f32_orderable(sc0) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)c0) : 0ull;
+    e[1] = (c1 >= 0 && mb1 < qb)
+               ? ((uint64_t)f32_orderable(sc1) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)c1) : 0ull;
     // valid entries are nonzero (the order-preserving image of a finite score
     // is at least 0x00800000); the next beam is the set of the `keep` largest
     // keys (score desc, node asc), in no particular order
