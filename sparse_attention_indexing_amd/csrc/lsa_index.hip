@@ -1580,7 +1580,9 @@ __global__ __launch_bounds__(256) void k_select_expand(IndexCtx ctx, IndexWs ws,
   uint32_t* sbkt = skey + cap;                                // [cap] bucket ids
   uint8_t* contrib = reinterpret_cast<uint8_t*>(sbkt + cap);  // [cap]
   int32_t* far = reinterpret_cast<int32_t*>(contrib + cap);   // [kf]
-  int32_t* far2 = far + kf;                                   // [kf]
+  // radix-sort buffer for the far keys: reuses skey/sbkt, which are dead once
+  // the far keys are emitted (kf <= 2 cap since cap >= 3 B > 3 k / 4)
+  int32_t* far2 = reinterpret_cast<int32_t*>(sm);
   __shared__ uint32_t hist[4][256];
   __shared__ int wsum[4];
   __shared__ uint32_t s_prefix, s_want;
@@ -1956,7 +1958,9 @@ hipError_t launch_select_expand(const IndexCtx& ctx, const IndexWs& ws, int32_t*
                                 int32_t* count, int32_t* ranked, int dtype, int exact_mode,
                                 hipStream_t s) {
   if (ctx.n <= 0) return hipSuccess;
-  const size_t smem = (size_t)ctx.cap * 9 + (size_t)(ctx.k > 1 ? ctx.k : 1) * 8;
+  const int64_t kf = ctx.k > 1 ? ctx.k : 1;
+  if (kf > 2 * (int64_t)ctx.cap) return hipErrorInvalidValue;   // the far-key sort reuses 8 cap bytes
+  const size_t smem = (size_t)ctx.cap * 9 + (size_t)kf * 4;
   // candidate slots per thread: cap / 256 rounded up to 8, 16 or 32
   const int per = (ctx.cap + 255) / 256;
   if (per > 32) return hipErrorInvalidValue;
