@@ -384,6 +384,7 @@ __global__ __launch_bounds__(256) void k_score_filter(IndexCtx ctx, IndexWs ws, 
 // slot g with the count preset to ne; other queries append (score, bucket)
 // for scores >= tau, staged in LDS and flushed with one atomic per query.
 constexpr int kCapL = 40;           // LDS candidate slots per query and workgroup
+constexpr int kSelectWideQueries = 64;   // up to this many queries: 1,024-thread selection
 
 // NG query groups of 32 per wave (4 for 128 queries)
 template <int NG>
@@ -1441,48 +1442,47 @@ __device__ __forceinline__ uint64_t match_digit(uint32_t d, uint64_t active) {
 }
 
 // Stable LSD radix sort (DB-bit digits) of n non-negative int32 keys in LDS,
-// ascending.  Wave w owns the contiguous chunk [w*ch, (w+1)*ch); `tmp` is a
-// second buffer of n ints, `cnt` 4 x 2^DB counters (one row per wave); the
-// scatter ranks lanes with equal digits by ballots, which keeps it stable.
-// Returns the buffer that holds the result.
-template <int DB>
+// ascending, by a workgroup of NT threads (NW = NT / 64 waves).  Wave w owns
+// the contiguous chunk [w*ch, (w+1)*ch); `tmp` is a second buffer of n ints,
+// `cnt` NW x 2^DB counters (one row per wave); the scatter ranks lanes with
+// equal digits by ballots, which keeps it stable.  Returns the buffer that
+// holds the result.
+template <int DB, int NT = 256>
 __device__ int32_t* radix_sort_i32(int32_t* keys, int32_t* tmp, int n, int max_key, uint32_t* cnt) {
   constexpr int NB = 1 << DB;
+  constexpr int NW = NT / 64;
+  constexpr int E = NB * NW / NT;                // counters per thread in the scan
+  static_assert(E >= 1 && NB * NW == E * NT, "counter layout");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int ch = (n + 3) / 4;
+  const int ch = (n + NW - 1) / NW;
   const int c0 = wave * ch;
   const int c1 = (c0 + ch) < n ? (c0 + ch) : n;
   int bits = 0;
   while (bits < 31 && (max_key >> bits) != 0) bits += DB;
-  __shared__ int wsum_r[4];
+  __shared__ int wsum_r[NW];
   for (int shift = 0; shift < bits; shift += DB) {
-    for (int i = tid; i < 4 * NB; i += 256) cnt[i] = 0;
+    for (int i = tid; i < NW * NB; i += NT) cnt[i] = 0;
     __syncthreads();
     uint32_t* my = cnt + wave * NB;
     for (int e = c0 + lane; e < c1; e += 64) atomicAdd(&my[((uint32_t)keys[e] >> shift) & (NB - 1)], 1u);
     __syncthreads();
     {
-      // digit-major, wave-minor exclusive offsets; thread t owns digits
-      // t * NB / 256 .. (t + 1) * NB / 256 - 1
-      constexpr int PD = NB / 256;
+      // digit-major, wave-minor exclusive offsets; thread t owns the E
+      // consecutive (digit, wave) counters E t .. E t + E - 1
       uint32_t tot = 0;
 #pragma unroll
-      for (int q = 0; q < PD; ++q) {
-        const int d = tid * PD + q;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) tot += cnt[w * NB + d];
+      for (int q = 0; q < E; ++q) {
+        const int x = E * tid + q;
+        tot += cnt[(x % NW) * NB + x / NW];
       }
       int all;
-      uint32_t run = (uint32_t)block_scan_excl((int)tot, wsum_r, &all);
+      uint32_t run = (uint32_t)block_scan_nt<NT>((int)tot, wsum_r, &all);
 #pragma unroll
-      for (int q = 0; q < PD; ++q) {
-        const int d = tid * PD + q;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t v = cnt[w * NB + d];
-          cnt[w * NB + d] = run;
-          run += v;
-        }
+      for (int q = 0; q < E; ++q) {
+        const int x = E * tid + q;
+        const uint32_t v = cnt[(x % NW) * NB + x / NW];
+        cnt[(x % NW) * NB + x / NW] = run;
+        run += v;
       }
     }
     __syncthreads();
@@ -1511,15 +1511,15 @@ __device__ int32_t* radix_sort_i32(int32_t* keys, int32_t* tmp, int n, int max_k
 // the largest key down) reaches `want`.  On return `want` is the weight
 // still needed from the items whose key equals K.  Requires the total weight
 // of the passing items to be >= want.
-template <class KeyF, class FiltF>
+template <int NT, class KeyF, class FiltF>
 __device__ uint32_t weighted_select(int c, KeyF key, FiltF filt, const uint8_t* w, uint32_t& want,
                                     uint32_t (*hist)[256], uint32_t* s_prefix, uint32_t* s_want) {
   const int tid = threadIdx.x;
   uint32_t prefix = 0, mask = 0;
   for (int shift = 24; shift >= 0; shift -= 8) {
-    hist[0][tid] = 0;
+    if (tid < 256) hist[0][tid] = 0;
     __syncthreads();
-    for (int i = tid; i < c; i += 256) {
+    for (int i = tid; i < c; i += NT) {
       const uint32_t kv = key(i);
       if ((kv & mask) == prefix && w[i] && filt(i)) atomicAdd(&hist[0][(kv >> shift) & 255u], (uint32_t)w[i]);
     }
@@ -1566,11 +1566,13 @@ __device__ uint32_t weighted_select(int c, KeyF key, FiltF filt, const uint8_t* 
 // buckets tied at S* are walked in bucket order, the crossing one is cut.
 // Every candidate list holds the exact top-B (or every eligible bucket), so
 // the crossing lies inside it.  The far keys are then radix-sorted.
-// PER = candidate slots per thread (cap / 256): thread t owns candidates
-// t, t + 256, ..., whose member words stay in registers from the contribution
-// count to the emission.
-template <int DT, int PER>
-__global__ __launch_bounds__(256) void k_select_expand(IndexCtx ctx, IndexWs ws, int32_t* idx,
+// PER = candidate slots per thread (cap / NT): thread t owns candidates
+// t, t + NT, ..., whose member words stay in registers from the contribution
+// count to the emission.  NT = 256 for many queries; a few queries (decode)
+// take NT = 1,024, which shortens every data-parallel phase of the one
+// workgroup that a query waits on.
+template <int DT, int PER, int NT = 256>
+__global__ __launch_bounds__(NT) void k_select_expand(IndexCtx ctx, IndexWs ws, int32_t* idx,
                                                        int32_t* count, int32_t* ranked,
                                                        int exact_mode) {
   extern __shared__ uint64_t sm[];
@@ -1583,8 +1585,8 @@ __global__ __launch_bounds__(256) void k_select_expand(IndexCtx ctx, IndexWs ws,
   // radix-sort buffer for the far keys: reuses skey/sbkt, which are dead once
   // the far keys are emitted (kf <= 2 cap since cap >= 3 B > 3 k / 4)
   int32_t* far2 = reinterpret_cast<int32_t*>(sm);
-  __shared__ uint32_t hist[4][256];
-  __shared__ int wsum[4];
+  __shared__ uint32_t hist[NT / 64][256];
+  __shared__ int wsum[NT / 64];
   __shared__ uint32_t s_prefix, s_want;
   __shared__ int s_total, s_trunc_m;
   const int tid = threadIdx.x;
@@ -1602,7 +1604,7 @@ __global__ __launch_bounds__(256) void k_select_expand(IndexCtx ctx, IndexWs ws,
     const int64_t ne = n_eligible(p);
     const int64_t beff = ne < ctx.top_b ? ne : ctx.top_b;
     if (exact_mode == 2 || (exact_mode == 1 && (c < beff || c > cap))) {
-      c = exact_select_lds<DT>(ctx, ws, qi, ne, beff, skey, sbkt, &hist[0][0], &s_prefix, &s_want,
+      c = exact_select_lds<DT, NT>(ctx, ws, qi, ne, beff, skey, sbkt, &hist[0][0], &s_prefix, &s_want,
                                wsum, &s_total);
     } else {
       c = c < cap ? c : cap;
@@ -1610,12 +1612,12 @@ __global__ __launch_bounds__(256) void k_select_expand(IndexCtx ctx, IndexWs ws,
       uint2 e[PER];
 #pragma unroll
       for (int jj = 0; jj < PER; ++jj) {
-        const int i = tid + 256 * jj;
+        const int i = tid + NT * jj;
         e[jj] = i < c ? cand[i] : make_uint2(0, 0);
       }
 #pragma unroll
       for (int jj = 0; jj < PER; ++jj) {
-        const int i = tid + 256 * jj;
+        const int i = tid + NT * jj;
         if (i < c) { skey[i] = e[jj].x; sbkt[i] = e[jj].y; }
       }
     }
@@ -1625,14 +1627,14 @@ __global__ __launch_bounds__(256) void k_select_expand(IndexCtx ctx, IndexWs ws,
   uint32_t mw[PER];
 #pragma unroll
   for (int jj = 0; jj < PER; ++jj) {
-    const int i = tid + 256 * jj;
+    const int i = tid + NT * jj;
     mw[jj] = i < c ? mem[sbkt[i]] : 0xFFFFFFFFu;
   }
   // far-key contributions (members outside the near set)
   int my_w = 0;
 #pragma unroll
   for (int jj = 0; jj < PER; ++jj) {
-    const int i = tid + 256 * jj;
+    const int i = tid + NT * jj;
     if (i >= c) continue;
     const uint32_t g = sbkt[i];
     const uint32_t m = mw[jj];
@@ -1661,12 +1663,12 @@ __global__ __launch_bounds__(256) void k_select_expand(IndexCtx ctx, IndexWs ws,
   }
   if (tid == 0) { s_trunc_m = 0; s_total = 0; }
   int total;
-  (void)block_scan_excl(my_w, wsum, &total);   // also orders the LDS writes above
+  (void)block_scan_nt<NT>(my_w, wsum, &total);   // also orders the LDS writes above
   // optional output: the kept buckets best first (O(c^2) ranking; for tests)
   if (ranked) {
     const int nb = c < ctx.top_b ? c : ctx.top_b;
-    for (int r = nb + tid; r < ctx.top_b; r += 256) ranked[qi * ctx.top_b + r] = -1;
-    for (int i = tid; i < c; i += 256) {
+    for (int r = nb + tid; r < ctx.top_b; r += NT) ranked[qi * ctx.top_b + r] = -1;
+    for (int i = tid; i < c; i += NT) {
       int ahead = 0;
       for (int j = 0; j < c; ++j)
         ahead += skey[j] > skey[i] || (skey[j] == skey[i] && sbkt[j] < sbkt[i]);
@@ -1679,19 +1681,19 @@ __global__ __launch_bounds__(256) void k_select_expand(IndexCtx ctx, IndexWs ws,
   uint32_t prefix = 0, gstar_key = 0, want = (uint32_t)k;
   const bool cut = k > 0 && total >= k;
   if (cut) {
-    prefix = weighted_select(c, [&](int i) { return skey[i]; }, [&](int) { return true; },
+    prefix = weighted_select<NT>(c, [&](int i) { return skey[i]; }, [&](int) { return true; },
                              contrib, want, hist, &s_prefix, &s_want);
     const uint32_t sstar = prefix;
     // buckets tied at S*: almost always one, which is then the cut bucket
     int n_eq = 0;
-    for (int i = tid; i < c; i += 256)
+    for (int i = tid; i < c; i += NT)
       if (skey[i] == sstar && contrib[i]) { ++n_eq; s_prefix = 0xFFFFFFFFu - sbkt[i]; }
     int eq_tot;
-    (void)block_scan_excl(n_eq, wsum, &eq_tot);
+    (void)block_scan_nt<NT>(n_eq, wsum, &eq_tot);
     if (eq_tot == 1) {
       gstar_key = s_prefix;
     } else {
-      gstar_key = weighted_select(c, [&](int i) { return 0xFFFFFFFFu - sbkt[i]; },
+      gstar_key = weighted_select<NT>(c, [&](int i) { return 0xFFFFFFFFu - sbkt[i]; },
                                   [&](int i) { return skey[i] == sstar; }, contrib, want, hist,
                                   &s_prefix, &s_want);
     }
@@ -1715,17 +1717,17 @@ __global__ __launch_bounds__(256) void k_select_expand(IndexCtx ctx, IndexWs ws,
     int mine = 0;
 #pragma unroll
     for (int jj = 0; jj < PER; ++jj) {
-      const int i = tid + 256 * jj;
+      const int i = tid + NT * jj;
       tk[jj] = i < c ? take_of(i) : 0;
       mine += tk[jj];
     }
     int all_take;
-    int o = block_scan_excl(mine, wsum, &all_take);
+    int o = block_scan_nt<NT>(mine, wsum, &all_take);
 #pragma unroll
     for (int jj = 0; jj < PER; ++jj) {
       int left = tk[jj];
       if (left == 0) continue;
-      const int i = tid + 256 * jj;
+      const int i = tid + NT * jj;
       const uint32_t g = sbkt[i];
       const uint32_t m = mw[jj];
       const int64_t kb = (int64_t)(g / kBuckets) * kBlock;
@@ -1753,17 +1755,17 @@ __global__ __launch_bounds__(256) void k_select_expand(IndexCtx ctx, IndexWs ws,
     }
   }
   __syncthreads();
-  const int32_t* sorted_far = radix_sort_i32<8>(far, far2, n_far, (int)(p > 0 ? p : 0), &hist[0][0]);
+  const int32_t* sorted_far = radix_sort_i32<8, NT>(far, far2, n_far, (int)(p > 0 ? p : 0), &hist[0][0]);
   // sinks | far | window, -1 padded
   int32_t* out = idx + qi * (int64_t)ctx.list_len;
   int cnt;
   if (w_start <= s_end) {
     cnt = (int)(p + 1);
-    for (int i = tid; i < ctx.list_len; i += 256) out[i] = i < cnt ? i : -1;
+    for (int i = tid; i < ctx.list_len; i += NT) out[i] = i < cnt ? i : -1;
   } else {
     const int ns = (int)s_end, nw = (int)(p - w_start + 1);
     cnt = ns + n_far + nw;
-    for (int i = tid; i < ctx.list_len; i += 256) {
+    for (int i = tid; i < ctx.list_len; i += NT) {
       int32_t v = -1;
       if (i < ns) v = i;
       else if (i < ns + n_far) v = sorted_far[i - ns];
@@ -1961,22 +1963,37 @@ hipError_t launch_select_expand(const IndexCtx& ctx, const IndexWs& ws, int32_t*
   const int64_t kf = ctx.k > 1 ? ctx.k : 1;
   if (kf > 2 * (int64_t)ctx.cap) return hipErrorInvalidValue;   // the far-key sort reuses 8 cap bytes
   const size_t smem = (size_t)ctx.cap * 9 + (size_t)kf * 4;
+  auto run = [&](auto kern, int nt) {
+    allow_large_lds(reinterpret_cast<const void*>(kern));
+    hipLaunchKernelGGL(kern, dim3((unsigned)ctx.n), dim3(nt), smem, s, ctx, ws, idx, count, ranked,
+                       exact_mode);
+  };
+  if (ctx.n <= kSelectWideQueries) {
+    // candidate slots per thread of a 1,024-thread workgroup: 2, 4 or 8
+    const int per = (ctx.cap + 1023) / 1024;
+    if (per > 8) return hipErrorInvalidValue;
+    if (dtype == LSA_BF16) {
+      if (per <= 2) run(k_select_expand<LSA_BF16, 2, 1024>, 1024);
+      else if (per <= 4) run(k_select_expand<LSA_BF16, 4, 1024>, 1024);
+      else run(k_select_expand<LSA_BF16, 8, 1024>, 1024);
+    } else {
+      if (per <= 2) run(k_select_expand<LSA_F32, 2, 1024>, 1024);
+      else if (per <= 4) run(k_select_expand<LSA_F32, 4, 1024>, 1024);
+      else run(k_select_expand<LSA_F32, 8, 1024>, 1024);
+    }
+    return hipGetLastError();
+  }
   // candidate slots per thread: cap / 256 rounded up to 8, 16 or 32
   const int per = (ctx.cap + 255) / 256;
   if (per > 32) return hipErrorInvalidValue;
-  auto run = [&](auto kern) {
-    allow_large_lds(reinterpret_cast<const void*>(kern));
-    hipLaunchKernelGGL(kern, dim3((unsigned)ctx.n), dim3(256), smem, s, ctx, ws, idx, count, ranked,
-                       exact_mode);
-  };
   if (dtype == LSA_BF16) {
-    if (per <= 8) run(k_select_expand<LSA_BF16, 8>);
-    else if (per <= 16) run(k_select_expand<LSA_BF16, 16>);
-    else run(k_select_expand<LSA_BF16, 32>);
+    if (per <= 8) run(k_select_expand<LSA_BF16, 8>, 256);
+    else if (per <= 16) run(k_select_expand<LSA_BF16, 16>, 256);
+    else run(k_select_expand<LSA_BF16, 32>, 256);
   } else {
-    if (per <= 8) run(k_select_expand<LSA_F32, 8>);
-    else if (per <= 16) run(k_select_expand<LSA_F32, 16>);
-    else run(k_select_expand<LSA_F32, 32>);
+    if (per <= 8) run(k_select_expand<LSA_F32, 8>, 256);
+    else if (per <= 16) run(k_select_expand<LSA_F32, 16>, 256);
+    else run(k_select_expand<LSA_F32, 32>, 256);
   }
   return hipGetLastError();
 }
