@@ -1983,6 +1983,21 @@ hipError_t launch_select_expand(const IndexCtx& ctx, const IndexWs& ws, int32_t*
     }
     return hipGetLastError();
   }
+  // long candidate lists (cap >= 4,096): 512 threads per query (measured
+  // faster at k = 4,096; slower at k = 2,048, where 256 threads keep more
+  // workgroups per compute unit)
+  if (ctx.cap >= 4096) {
+    const int per512 = (ctx.cap + 511) / 512;
+    if (per512 > 16) return hipErrorInvalidValue;
+    if (dtype == LSA_BF16) {
+      if (per512 <= 8) run(k_select_expand<LSA_BF16, 8, 512>, 512);
+      else run(k_select_expand<LSA_BF16, 16, 512>, 512);
+    } else {
+      if (per512 <= 8) run(k_select_expand<LSA_F32, 8, 512>, 512);
+      else run(k_select_expand<LSA_F32, 16, 512>, 512);
+    }
+    return hipGetLastError();
+  }
   // candidate slots per thread: cap / 256 rounded up to 8, 16 or 32
   const int per = (ctx.cap + 255) / 256;
   if (per > 32) return hipErrorInvalidValue;
