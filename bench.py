@@ -30,6 +30,14 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def workload_name(name: str, mode: str) -> str:
+    """The workload's name with its indexing-mode suffix set to the mode actually run."""
+    for suffix in ("_flat", "_tree"):
+        if name.endswith(suffix):
+            return name[: -len(suffix)] + "_" + mode
+    return name
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -187,7 +195,8 @@ def bench_decode(args, w, dev):
         "n_gpus": 1, "steps": len(steady), "warmup": 8, "ms_per_step": round(tot_steady / 1e3, 5),
         "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": w.name if args.cfg == 3 else "decode_t10m_b1_bf16", "T": T,
+        "config": {"workload": workload_name(w.name if args.cfg == 3 else "decode_t10m_b1_bf16",
+                                             args.mode), "T": T,
                    "batch": B, "k": w.k, "mode": args.mode, "attention_splits": args.splits,
                    "parallelism": "none"},
         "stages_us": {"index_decode": round(float(np.median(st[:, 0])), 2),
@@ -320,7 +329,7 @@ def main():
     pos = np.arange(w.q_start, w.T, dtype=np.int64)
     pairs = int((64 * (pos // 512)).sum())
     kname = ("k_attn_bf16_h4" if w.Hkv == 4 else "k_attn_bf16") if w.dtype == "bf16" else "k_attn_f32"
-    traffic = measured_traffic(kname, w.name)
+    traffic = measured_traffic(kname, workload_name(w.name, args.mode))
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4),
                     traffic=None if traffic is None else round(traffic),
@@ -334,7 +343,8 @@ def main():
         "unit": "query tok/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
-        "config": {"workload": w.name, "T": w.T, "Tq": w.Tq, "Hq": w.Hq, "Hkv": w.Hkv,
+        "config": {"workload": workload_name(w.name, args.mode), "T": w.T, "Tq": w.Tq,
+                   "Hq": w.Hq, "Hkv": w.Hkv,
                    "head_dim": w.D, "k": w.k, "mode": args.mode, "n_sink": w.n_sink,
                    "window": w.window, "latent_components": w.n_comp, "parallelism": "none"},
         "stages_ms": {"build": round(float(t_build), 4), "index": round(float(t_index), 4),
