@@ -277,34 +277,45 @@ __global__ __launch_bounds__(64 * kMaxWaves, 3) void k_attn_bf16(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Four-KV-head path (Hkv = 4, the shape of the 128K .. 10M workloads).  A
-// token's K (and V) rows for all four KV heads are 1 KiB contiguous, so the
-// workgroup streams each tile of 16 tokens with one 64-lane 16-byte load per
-// token and tensor, straight from global memory into LDS
-// (global_load_lds_dwordx4: lane i writes bytes [16 i, 16 i + 16) of the
-// row).  Two LDS stages: tile t+1 is in flight while tile t is computed.
-// Wave w then computes KV head w: S = Q K^T on 16x16x32 MFMAs (B from LDS,
-// 64 contiguous bytes per lane), online softmax with DPP row reductions, and
-// O += P V on 16x16x16 MFMAs whose A (P) and B (V) operands come from
-// transposing LDS reads.  Rows are padded (K: 1040 B, V: 1056 B) so that the
-// 16 lanes of a group hit distinct banks.
-constexpr int kT3 = 16;                 // tokens per tile
-constexpr int kKRow3 = 1040;            // bytes per token row of K in LDS
-constexpr int kVRow3 = 1056;            // bytes per token row of V in LDS
-constexpr int kStage3 = kT3 * (kKRow3 + kVRow3);   // bytes per stage
-constexpr int kP3 = kT3 * 16 * 2;       // P tile [16 keys][16 heads] bf16, per wave
-constexpr int kLds3 = 2 * kStage3 + 4 * kP3;
+// Four-KV-head path (Hkv = 4, the shape of the 128K .. 10M workloads),
+// register staged.  Wave w owns KV head w and streams that head's K and V
+// rows (256 B each per token) on its own: no workgroup barrier inside the
+// loop.  Tiles of 16 tokens are loaded with plain 16-byte loads into a ring
+// of kRing4 register buffers, kRing4 - 1 tiles ahead of the one being
+// computed, so each wave keeps 16 KiB in flight and two workgroups share a
+// CU.  K goes straight into the B operand of 16x16x32 MFMAs: for product j,
+// lane (n, u) holds bytes [16 (4j + u), +16) of key n, and Q uses the same
+// dim order.  V is written to a per-wave LDS tile, its 16-byte chunks XOR
+// swizzled by row (chunk ^ 2 (row & 7)) so that the transposing reads of the
+// PV products hit distinct banks.  The loop runs whole ring cycles: tiles at
+// or past the end, and invalid list entries, load token 0 with zero weight.
+// The row's index list is staged in LDS, kList4 entries at a time.
+//
+// Softmax in base 2 with a lazy reference max m per head row: the O and l
+// accumulators are rescaled only when a score exceeds m by more than 2^kLazy
+// (O and l always share the reference, so the result does not depend on
+// when this happens); l is summed per lane and reduced once at the end.
+constexpr int kRing4 = 3;                      // register buffers per wave
+constexpr int kVTile4 = 16 * 256;              // V tile of one KV head in LDS (bytes)
+constexpr int kP4 = 16 * 16 * 2;               // P tile [16 keys][16 heads] bf16, per wave
+constexpr int kList4 = 8192;                   // index-list entries staged at a time
+constexpr int kLds4 = 4 * (kVTile4 + kP4) + kList4 * 4;
+constexpr float kLazy = 8.f;
 
 typedef short v4s_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ void g2lds16(const void* g, char* lds_row) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_row, 16, 0, 0);
+// two floats -> packed bf16 pair (v_cvt_pk_bf16_f32, round to nearest even)
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 __global__ __launch_bounds__(256, 2) void k_attn_bf16_h4(AttnArgs a) {
-  extern __shared__ __attribute__((aligned(16))) char lds3[];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  extern __shared__ __attribute__((aligned(16))) char lds4[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // with 8+ rows, workgroups of consecutive rows (which share many keys) go
   // to the same XCD; with fewer rows grid.x = rows and the splits of a row
   // spread over the XCDs
@@ -323,118 +334,139 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16_h4(AttnArgs a) {
   const int k1 = (k0 + per) < cnt ? (k0 + per) : cnt;
   const int n = k1 > k0 ? k1 - k0 : 0;
   const int32_t* lst = a.idx + row * (int64_t)a.L + k0;
-  const char* kbase = reinterpret_cast<const char*>(a.k + b * a.Tmax * 4 * kHeadDim);
-  const char* vbase = reinterpret_cast<const char*>(a.v + b * a.Tmax * 4 * kHeadDim);
-  uint16_t* ps = reinterpret_cast<uint16_t*>(lds3 + 2 * kStage3 + wave * kP3);
-  const int r16 = lane & 15, u = lane >> 4;
   const int kvh = wave;
-
-  // zero the V rows once: skipped (invalid) tokens must never feed NaN garbage
-  for (int i = threadIdx.x; i < 2 * kT3 * kVRow3 / 16; i += 256) {
-    const int st = i / (kT3 * kVRow3 / 16), r = i % (kT3 * kVRow3 / 16);
-    reinterpret_cast<uint4*>(lds3 + st * kStage3 + kT3 * kKRow3)[r] = make_uint4(0, 0, 0, 0);
-  }
-  __syncthreads();
-
-  // positions of a tile: lane l < 16 holds key t + l (-1 past the end or outside the cache)
-  auto load_pos = [&](int t) -> int32_t {
-    int32_t p = (lane < kT3 && t + lane < n) ? lst[t + lane] : -1;
-    return (p >= 0 && p < a.Tmax) ? p : -1;
-  };
-  // wave w loads tokens 4w .. 4w+3 of a tile (K and V rows, 1 KiB each)
-  auto issue = [&](int st, int32_t pl) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int tok = 4 * wave + j;
-      const int32_t p = __builtin_amdgcn_readfirstlane(__shfl(pl, tok, 64));
-      if (p >= 0) {
-        char* sb = lds3 + st * kStage3;
-        g2lds16(kbase + (int64_t)p * 1024 + 16 * lane, sb + tok * kKRow3);
-        g2lds16(vbase + (int64_t)p * 1024 + 16 * lane, sb + kT3 * kKRow3 + tok * kVRow3);
-      }
-    }
-  };
+  const char* kb = reinterpret_cast<const char*>(a.k + b * a.Tmax * 4 * kHeadDim) + kvh * 256;
+  const char* vb = reinterpret_cast<const char*>(a.v + b * a.Tmax * 4 * kHeadDim) + kvh * 256;
+  char* vt = lds4 + wave * (kVTile4 + kP4);
+  uint16_t* ps = reinterpret_cast<uint16_t*>(vt + kVTile4);
+  int32_t* slist = reinterpret_cast<int32_t*>(lds4 + 4 * (kVTile4 + kP4));
+  const int r16 = lane & 15, u = lane >> 4;
+  const int64_t Tmax = a.Tmax;
 
   bf16x8 qf[4];
   {
     const bool ok = r16 < a.G;
-    const uint16_t* qrow = a.q + (row * a.Hq + (int64_t)kvh * a.G + (ok ? r16 : 0)) * kHeadDim + 32 * u;
+    const uint4* qrow = reinterpret_cast<const uint4*>(
+        a.q + (row * a.Hq + (int64_t)kvh * a.G + (ok ? r16 : 0)) * kHeadDim);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      uint4 w = ok ? reinterpret_cast<const uint4*>(qrow)[j] : make_uint4(0, 0, 0, 0);
+      uint4 w = ok ? qrow[4 * j + u] : make_uint4(0, 0, 0, 0);
       qf[j] = __builtin_bit_cast(bf16x8, w);
     }
   }
   f32x4 o[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m[4], l[4];
+  // m: reference max per head row, uniform over the row's 16 lanes, with a
+  // finite floor so that exp2(-inf - m) = 0; lp: this lane's partial sums
+  float m[4], lp[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) { m[i] = -__builtin_inff(); l[i] = 0.f; }
+  for (int i = 0; i < 4; ++i) { m[i] = -1e30f; lp[i] = 0.f; }
 
-  int32_t pl_cur = load_pos(0), pl_nxt = load_pos(kT3);
-  if (n > 0) issue(0, pl_cur);
-  int st = 0;
-  for (int t = 0; t < n; t += kT3, st ^= 1) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's loads of tile t landed
-    __syncthreads();                      // everyone's loads landed; stage st^1 is free
-    int32_t pl_nn = -1;
-    if (t + kT3 < n) {
-      issue(st ^ 1, pl_nxt);
-      pl_nn = load_pos(t + 2 * kT3);
-    }
-    const char* kst = lds3 + st * kStage3;
-    const char* vst = kst + kT3 * kKRow3;
-    // S = Q K^T: key column r16, dims [32u + 8j, +8) from K row r16, head kvh
-    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-    {
-      const uint4* kr = reinterpret_cast<const uint4*>(kst + r16 * kKRow3 + kvh * 256 + 64 * u);
+  const int vi = lane >> 4, vc = lane & 15;    // V loads: token 4 vi + j, chunk vc
+  // transposing V reads: source lane s of a 16-lane group points at key row
+  // 4u + (s >> 2), dims 16j + 4 (s & 3) .. +3 (byte 8 (s & 1) of chunk 2j + cv)
+  const int sk = 4 * u + (r16 >> 2), cv = (r16 & 3) >> 1, sw = 2 * (sk & 7);
+  const char* vrd = vt + 256 * sk + 8 * (r16 & 1);
+  const uint16_t* prd = ps + sk * 16 + 4 * (r16 & 3);
+
+  u32x4_t kr[kRing4][4], vr[kRing4][4];
+  bool kval[kRing4];
+  for (int c0 = 0; c0 < n; c0 += kList4) {
+    const int cn = (n - c0) < kList4 ? (n - c0) : kList4;
+    if (c0 > 0) __syncthreads();               // every wave is done with the previous chunk
+    for (int i = threadIdx.x; i < cn; i += 256) slist[i] = lst[c0 + i];
+    __syncthreads();
+    const int nt = (cn + 15) >> 4;
+
+    // tile T into one ring buffer; kv: this lane's key (column r16) is real
+    auto issue = [&](int T, u32x4_t (&k)[4], u32x4_t (&v)[4], bool& kv) {
+      const int tb = T << 4;
+      const int tr = T < nt ? tb : 0;          // padding tiles read entry 0, rejected by tb
+      const int pk = slist[tr + r16];
+      const int4 p4 = *reinterpret_cast<const int4*>(slist + tr + 4 * vi);
+      kv = tb + r16 < cn && pk >= 0 && pk < Tmax;
+      const char* kp = kb + (int64_t)(kv ? pk : 0) * 1024 + 16 * u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) k[j] = *reinterpret_cast<const u32x4_t*>(kp + 64 * j);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int p = j == 0 ? p4.x : (j == 1 ? p4.y : (j == 2 ? p4.z : p4.w));
+        const bool ok = tb + 4 * vi + j < cn && p >= 0 && p < Tmax;
+        v[j] = *reinterpret_cast<const u32x4_t*>(vb + (int64_t)(ok ? p : 0) * 1024 + 16 * vc);
+      }
+    };
+    auto compute = [&](const u32x4_t (&k)[4], const u32x4_t (&v)[4], bool kv) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int rr = 4 * vi + j;
+        *reinterpret_cast<u32x4_t*>(vt + 256 * rr + 16 * (vc ^ (2 * (rr & 7)))) = v[j];
+      }
+      // S = Q K^T: row = head 4u + i, column = key r16
+      f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[j], __builtin_bit_cast(bf16x8, kr[j]), sacc, 0, 0, 0);
-    }
-    const bool valid = __shfl(pl_cur, r16, 64) >= 0;
-    float pv[4], alpha[4];
-    bool grew = false;
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[j], __builtin_bit_cast(bf16x8, k[j]), sacc, 0, 0, 0);
+      float x[4], pv[4];
+      bool grow = false;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float x = valid ? sacc[i] * a.scale_log2 : -__builtin_inff();
-      const float mx = row16_max(x);
-      const float mn = fmaxf(m[i], mx);
-      const bool empty = mn == -__builtin_inff();
-      grew |= mn > m[i];
-      alpha[i] = empty ? 1.f : __builtin_amdgcn_exp2f(m[i] - mn);
-      pv[i] = empty ? 0.f : __builtin_amdgcn_exp2f(x - mn);
-      l[i] = l[i] * alpha[i] + row16_sum(pv[i]);
-      m[i] = mn;
-    }
-    if (__ballot(grew)) {
+      for (int i = 0; i < 4; ++i) {
+        x[i] = kv ? sacc[i] * a.scale_log2 : -__builtin_inff();
+        grow |= x[i] > m[i] + kLazy;
+      }
+      if (__ballot(grow)) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
+        for (int i = 0; i < 4; ++i) {
+          const float mn = fmaxf(m[i], row16_max(x[i]));
+          const float alpha = __builtin_amdgcn_exp2f(m[i] - mn);
+          lp[i] *= alpha;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o[j][i] *= alpha[i];
-    }
-    {
+          for (int j = 0; j < 8; ++j) o[j][i] *= alpha;
+          m[i] = mn;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pv[i] = __builtin_amdgcn_exp2f(x[i] - m[i]);
+        lp[i] += pv[i];
+      }
       uint2 w2;
-      w2.x = (uint32_t)f32_to_bf16_rne(pv[0]) | ((uint32_t)f32_to_bf16_rne(pv[1]) << 16);
-      w2.y = (uint32_t)f32_to_bf16_rne(pv[2]) | ((uint32_t)f32_to_bf16_rne(pv[3]) << 16);
+      w2.x = pack_bf16x2(pv[0], pv[1]);
+      w2.y = pack_bf16x2(pv[2], pv[3]);
       *reinterpret_cast<uint2*>(ps + r16 * 16 + 4 * u) = w2;   // P[key r16][heads 4u..4u+3]
-    }
-    wave_fence();
-    // O += P V with 16x16x16 MFMAs: A = P (head r16, keys 4u..4u+3), B = V
-    // (dim 16j + r16, keys 4u..4u+3); source lane s points at key 4u + (s >> 2)
-    const int sk = 4 * u + (r16 >> 2), sc = 4 * (r16 & 3);
-    const v4s_t pa4 = __builtin_bit_cast(v4s_t, ds_read_tr16(ps + sk * 16 + sc));
-    const uint16_t* vrow = reinterpret_cast<const uint16_t*>(vst + sk * kVRow3 + kvh * 256) + sc;
+      wave_fence();
+      // O += P V with 16x16x16 MFMAs: A = P (head r16, keys 4u..4u+3), B = V
+      const v4s_t pa4 = __builtin_bit_cast(v4s_t, ds_read_tr16(prd));
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const v4s_t vb4 = __builtin_bit_cast(v4s_t, ds_read_tr16(vrow + 16 * j));
-      o[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa4, vb4, o[j], 0, 0, 0);
+      for (int j = 0; j < 8; ++j) {
+        const v4s_t vb4 = __builtin_bit_cast(
+            v4s_t, ds_read_tr16(reinterpret_cast<const uint16_t*>(vrd + 16 * ((2 * j + cv) ^ sw))));
+        o[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa4, vb4, o[j], 0, 0, 0);
+      }
+      wave_fence();
+    };
+
+    // The compiler derives each wait from the load order, so the prologue's
+    // tiles are pinned in ring order; every cycle then issues tile t + 2 and
+    // computes tile t, with two tiles (16 loads per lane) still in flight.
+    static_assert(kRing4 == 3, "the ring cycle below is written out for three buffers");
+    issue(0, kr[0], vr[0], kval[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(1, kr[1], vr[1], kval[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int t0 = 0; t0 < nt; t0 += kRing4) {
+      issue(t0 + 2, kr[2], vr[2], kval[2]);
+      compute(kr[0], vr[0], kval[0]);
+      issue(t0 + 3, kr[0], vr[0], kval[0]);
+      compute(kr[1], vr[1], kval[1]);
+      issue(t0 + 4, kr[1], vr[1], kval[1]);
+      compute(kr[2], vr[2], kval[2]);
     }
-    wave_fence();
-    pl_cur = pl_nxt;
-    pl_nxt = pl_nn;
+    __builtin_amdgcn_s_waitcnt(0x0F70);        // vmcnt(0): the padding tiles' loads retired
   }
+  float l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) l[i] = row16_sum(lp[i]);
   // write: rows 4u + i < G, dims 16j + r16
   if (a.splits == 1) {
 #pragma unroll
@@ -644,13 +676,13 @@ hipError_t launch_attention(const void* q, const void* k, const void* v, int32_t
       static bool attr3 = false;
       if (!attr3) {
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_attn_bf16_h4),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, kLds3);
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, kLds4);
         (void)hipGetLastError();
         attr3 = true;
       }
       const int64_t grid = rows >= 8 ? (rows + 7) / 8 * 8 : rows;
       hipLaunchKernelGGL(k_attn_bf16_h4, dim3((unsigned)grid, (unsigned)splits), dim3(256),
-                         (size_t)kLds3, s, a);
+                         (size_t)kLds4, s, a);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess || splits == 1) return e;
       hipLaunchKernelGGL(k_attn_combine<LSA_BF16>, dim3((unsigned)(rows * Hq * 2)), dim3(256), 0,
