@@ -234,6 +234,53 @@ def test_attention_bf16_on_oracle_lists(splits, few):
     assert err <= 2e-2
 
 
+@pytest.mark.parametrize("chunk", [0, 1000, 5000])
+def test_prefill_attention_overlapped(chunk):
+    """The overlapped call (indexing of chunk i+1 on the library's side stream
+    while chunk i attends) equals lsa_index_prefill + lsa_sparse_attention bit
+    for bit, also with a ragged last chunk; its timing events bracket every
+    attention launch; sampled rows match the oracle's lists and attention."""
+    say(f"case: prefill_attention chunk={chunk}")
+    w = S.WORKLOADS[2]
+    T, Tq = 16384, 5000
+    q0 = T - Tq
+    X, Y, _ = S.latent_inputs(w, T=T, query_rows=(q0, T))
+    p = lsa.Params(k=2048, index_dtype=lsa.LSA_BF16)
+    c = gpu_cache(X, p)
+    q, k, v, qb, kb, vb = _qkv_host(w, T, np.arange(q0, T))
+    Q = bf16_tensor(qb).cuda().view(Tq, w.Hq, w.D)
+    K = bf16_tensor(kb).cuda().view(T, w.Hkv, w.D)
+    V = bf16_tensor(vb).cuda().view(T, w.Hkv, w.D)
+    Yd = torch.from_numpy(Y).cuda()
+    ch = lsa.prefill_chunk(p, q0, Tq, chunk)
+    assert ch == (chunk or 2048)     # a 16K context scans little: chunks overlap
+    nch = -(-Tq // ch)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * nch)]
+    for e in evs:
+        e.record()
+    out, idx, cnt = lsa.prefill_attention(c, Yd, q0, p, Q, K, V, chunk=chunk, attn_events=evs)
+    idx2, cnt2 = lsa.index_prefill(c, Yd, q0, p)
+    out2 = lsa.sparse_attention(Q, K, V, idx2, cnt2)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2) and torch.equal(cnt, cnt2)
+    assert torch.equal(out, out2)
+    ms = [evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(nch)]
+    say("attention launches (ms)", [round(x, 3) for x in ms])
+    assert all(x > 0 for x in ms)
+    oc = O.build_cache(X, oracle_params(p))
+    idx, cnt, out = idx.cpu().numpy(), cnt.cpu().numpy(), out.float().cpu().numpy()
+    err, checked = 0.0, 0
+    for r in (0, 999, 1000, 2500, 4095, 4096, Tq - 1):
+        res = O.index_query(Y[r], q0 + r, oc)
+        if res.exempt:
+            continue
+        checked += 1
+        assert cnt[r] == res.count and np.array_equal(idx[r, :cnt[r]], res.idx[:res.count]), r
+        err = max(err, np.abs(out[r] - O.attention_query(q[r], k, v, res.idx, res.count)).max())
+    say("rows checked", checked, "attention max abs err", err)
+    assert checked >= 4 and err <= 2e-2
+
+
 def test_end_to_end_c1():
     """GPU lists feed GPU attention; compared with the oracle's own lists and
     attention wherever the query is not a near tie."""
