@@ -1,19 +1,16 @@
 """Benchmark of the LSA hot path on one MI355X.
 
 One step = one pass of the whole prefill path over one synthetic layer:
-build_bucket_cache over all T keys, then lsa_prefill_attention, which indexes
-the Tq queries (lsa_index_prefill) and attends over their lists
-(lsa_sparse_attention) in 2,048-query chunks, indexing chunk i+1 on a second
-stream while chunk i attends (the library overlaps only when indexing scans a
-cache-resident centroid set; --sequential: the two calls one after the other
-over all queries).  Default workload: T = Tq = 131,072, bf16 K/V, 32 query /
-4 KV heads, head_dim 128, 1,024-component latent mixture, flat search,
-k = 2,048, 4 sinks, 512-key window.
+build_bucket_cache over all T keys, lsa_index_prefill for all Tq queries,
+lsa_sparse_attention over the resulting lists (which the library runs as
+back-to-back launches of 2,048 query rows).  Default workload: T = Tq =
+131,072, bf16 K/V, 32 query / 4 KV heads, head_dim 128, 1,024-component latent
+mixture, flat search, k = 2,048, 4 sinks, 512-key window.
 
 Prints one JSON line (metric: prefill query tok/s per layer).  The roofline
-object describes the dominant kernel (the attention), each launch timed with
-HIP events recorded on the stream it runs on; the cpu_baseline object times
-the CPU oracle on a bounded sample of the same workload.
+object describes the dominant kernel (the attention), timed with HIP events on
+the stream its launches run on and reported per launch; the cpu_baseline object times the CPU oracle on a bounded
+sample of the same workload.
 """
 from __future__ import annotations
 
@@ -48,10 +45,6 @@ def parse():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--cfg", type=int, default=2, help="workload (2 = 128K prefill, flat)")
-    ap.add_argument("--chunk", type=int, default=0,
-                    help="prefill: queries per overlapped chunk (0: the library's choice)")
-    ap.add_argument("--sequential", action="store_true",
-                    help="prefill: index every query, then attend (no overlap; per-stage times)")
     ap.add_argument("--mode", default="flat", choices=["flat", "tree"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -259,10 +252,7 @@ def main():
     cache_mem = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     idx = torch.empty((w.Tq, L), dtype=torch.int32, device=dev)
     cnt = torch.empty((w.Tq,), dtype=torch.int32, device=dev)
-    chunk = lsa.prefill_chunk(p, w.q_start, w.Tq, args.chunk)
-    n_chunks = -(-w.Tq // chunk)
-    ws = torch.empty(lsa.index_workspace_bytes(p, w.Tq if args.sequential else chunk),
-                     dtype=torch.uint8, device=dev)
+    ws = torch.empty(lsa.index_workspace_bytes(p, w.Tq), dtype=torch.uint8, device=dev)
     out = torch.empty_like(Q)
 
     class _Cache(lsa.BucketCache):
@@ -292,18 +282,8 @@ def main():
         build_once_ms = b0.elapsed_time(b1)
         log(f"cache for {w.T // 512} blocks built in {build_once_ms:.2f} ms")
 
-    def attn_events():
-        # two timing events per attention launch, recorded once so that their
-        # handles exist before they are handed to the library
-        evs = [ev() for _ in range(2 * (1 if args.sequential else n_chunks))]
-        for e in evs:
-            e.record()
-        return evs
-
-    def step(times=None, pairs=None):
-        e0, e1, e2 = ev(), ev(), ev()
-        if pairs is None:
-            pairs = attn_events()
+    def step(times=None):
+        e0, e1, e2, e3 = ev(), ev(), ev(), ev()
         if full_prefill:
             c = _Cache()
             e0.record()
@@ -312,18 +292,12 @@ def main():
             c = prebuilt
             e0.record()
         e1.record()
-        if args.sequential:
-            lsa.index_prefill(c, Yd, w.q_start, p, workspace=ws, out=(idx, cnt))
-            pairs[0].record()
-            lsa.sparse_attention(Q, K, V, idx, cnt, out=out)
-            pairs[1].record()
-        else:
-            # index of chunk i+1 (library side stream) overlaps attention of chunk i
-            lsa.prefill_attention(c, Yd, w.q_start, p, Q, K, V, chunk=chunk, workspace=ws,
-                                  out=out, lists=(idx, cnt), attn_events=pairs)
+        lsa.index_prefill(c, Yd, w.q_start, p, workspace=ws, out=(idx, cnt))
         e2.record()
+        lsa.sparse_attention(Q, K, V, idx, cnt, out=out)
+        e3.record()
         if times is not None:
-            times.append((e0, e1, e2, pairs))
+            times.append((e0, e1, e2, e3))
         return c
 
     if args.calib_copy:
@@ -336,21 +310,17 @@ def main():
         step()
     torch.cuda.synchronize()
     times = []
-    pools = [attn_events() for _ in range(args.steps)]
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(times, pools[i])
+    for _ in range(args.steps):
+        step(times)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
-    stage = np.array([[a.elapsed_time(b), b.elapsed_time(c),
-                       sum(pr[2 * j].elapsed_time(pr[2 * j + 1]) for j in range(len(pr) // 2))]
-                      for a, b, c, pr in times])
-    t_build, t_index_attn, t_attn = stage.mean(axis=0)
-    launches = 1 if args.sequential else n_chunks
-    log(f"per step: build {t_build:.3f} ms, index + attention {t_index_attn:.3f} ms, attention "
-        f"kernels {t_attn:.3f} ms in {launches} launches; wall {ms_step:.3f} ms")
+    stage = np.array([[a.elapsed_time(b), b.elapsed_time(c), c.elapsed_time(d)]
+                      for a, b, c, d in times])
+    t_build, t_index, t_attn = stage.mean(axis=0)
+    log(f"per step: build {t_build:.3f} ms, index {t_index:.3f} ms, attention {t_attn:.3f} ms; "
+        f"wall {ms_step:.3f} ms")
 
     # algorithmic bytes of the attention launch: gathered K and V rows for every
     # KV head, plus Q, O and the index lists
@@ -363,10 +333,12 @@ def main():
     pos = np.arange(w.q_start, w.T, dtype=np.int64)
     pairs = int((64 * (pos // 512)).sum())
     kname = ("k_attn_bf16_h4" if w.Hkv == 4 else "k_attn_bf16") if w.dtype == "bf16" else "k_attn_f32"
-    traffic = measured_traffic(kname, workload_name(w.name, args.mode),
-                               w.Tq if args.sequential else chunk)
-    # per launch: one launch per chunk; bytes and time averaged over the launches
+    # the bf16 attention runs as back-to-back launches of up to launch_rows query
+    # rows; bytes and time are reported per launch, averaged over the step's launches
+    launch_rows = min(lsa.attention_launch_rows(), w.Tq) if w.dtype == "bf16" else w.Tq
+    launches = -(-w.Tq // launch_rows)
     t_launch = t_attn / launches
+    traffic = measured_traffic(kname, workload_name(w.name, args.mode), launch_rows)
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4),
                     traffic=None if traffic is None else round(traffic),
@@ -386,13 +358,10 @@ def main():
                    "Hq": w.Hq, "Hkv": w.Hkv,
                    "head_dim": w.D, "k": w.k, "mode": args.mode, "n_sink": w.n_sink,
                    "window": w.window, "latent_components": w.n_comp, "parallelism": "none"},
-        "stages_ms": {"build": round(float(t_build), 4),
-                      "index_and_attention": round(float(t_index_attn), 4),
-                      "attention_kernels": round(float(t_attn), 4)},
+        "stages_ms": {"build": round(float(t_build), 4), "index": round(float(t_index), 4),
+                      "attention": round(float(t_attn), 4)},
         "step": ("build + index + attention" if full_prefill else
-                 "index + attention for the last chunk (cache built before timing)")
-                + ("" if args.sequential or n_chunks == 1 else
-                   f"; {chunk}-query chunks, indexing of chunk i+1 overlapped with attention of chunk i"),
+                 "index + attention for the last chunk (cache built before timing)"),
         "scoring": {"pairs": pairs, "algorithmic_tflop": round(pairs * 128 / 1e12, 4)},
         "roofline": roofline,
     }

@@ -203,6 +203,11 @@ int lsa_index_decode(lsa_cache* const* caches, int32_t B, const float* latent_q,
 int64_t lsa_attention_workspace_bytes(int32_t B, int64_t Tq, int32_t Hq, int32_t D,
                                       int32_t splits);
 
+/* Rows per launch of the bf16 attention: a call over more query rows issues
+ * ceil(B * Tq / this) launches back to back on its stream, so that the rows
+ * in flight stay neighbours (their lists share keys in the caches). */
+int64_t lsa_attention_launch_rows(void);
+
 /* A split count for lsa_sparse_attention: the largest power of two (<= 256)
  * that keeps at least 32 listed keys per split and rows * splits <= 512
  * workgroups (two per compute unit), so that few query rows (decode) still
@@ -230,52 +235,6 @@ int lsa_sparse_attention(const void* q, const void* k_cache, const void* v_cache
                          const int32_t* idx, const int32_t* count, int32_t L_max, float scale,
                          int32_t dtype, int32_t splits, void* out, void* workspace,
                          int64_t ws_bytes, void* stream);
-
-/* Query chunk of lsa_prefill_attention when its scan is cache-resident. */
-#define LSA_PREFILL_CHUNK 2048
-/* Largest centroid scan per query (bytes) at which chunks are overlapped. */
-#define LSA_PREFILL_OVERLAP_SCAN (8 << 20)
-
-/*
- * lsa_prefill_chunk: the query chunk lsa_prefill_attention uses for these
- * arguments.  chunk > 0 is taken as given (capped at Tq).  chunk == 0 picks
- * one: a query at the last position scans up to 64 centroids of
- * ((q_start + Tq - 1) / 512) blocks; when that is at most
- * LSA_PREFILL_OVERLAP_SCAN bytes (cache-resident: indexing is then bound by
- * compute and LDS, while the attention is bound by HBM) the chunk is
- * LSA_PREFILL_CHUNK, else Tq (no overlap: both phases would stream from HBM
- * and only contend).  Returns the chunk (0 when Tq == 0) or a negative
- * status (LSA_ERR_ARG for q_start < 0, Tq < 0 or chunk < 0).
- */
-int64_t lsa_prefill_chunk(const lsa_params* p, int64_t q_start, int64_t Tq, int64_t chunk);
-
-/*
- * lsa_prefill_attention: lsa_index_prefill followed by lsa_sparse_attention
- * (B = 1, splits = 1) for the Tq queries at q_start .. q_start+Tq-1, with
- * the two overlapped.  The queries are taken in chunks of
- * lsa_prefill_chunk(p, q_start, Tq, chunk) rows; chunk i+1 is indexed on a
- * second stream, owned by the library, while chunk i attends on `stream`
- * (a single chunk runs both calls on `stream`).
- * Results are those of the two calls: idx / count as lsa_index_prefill
- * writes them ([Tq, L] with L = lsa_list_len(p), [Tq]), out [Tq, Hq, D] as
- * lsa_sparse_attention writes it; q [Tq, Hq, D], k_cache / v_cache
- * [Tmax, Hkv, D] in dtype, latent_q fp32 [Tq, 64], all device memory.
- * workspace: at least lsa_index_workspace_bytes(p, that chunk).
- * attn_events: optional host array of 2 * ceil(Tq / that chunk) hipEvent_t
- * handles owned by the caller; events 2i and 2i+1 are recorded on `stream`
- * right before and right after chunk i's attention launch (for timing).
- * On return `stream` is ordered after all of the call's work, on both
- * streams.  `stream` must belong to the current device; calls for one
- * device are serialised on the host.  Errors: those of the two calls,
- * checked before anything is enqueued; LSA_ERR_HIP if the side stream
- * cannot be created.
- */
-int lsa_prefill_attention(const lsa_cache* c, const float* latent_q, int64_t q_start, int64_t Tq,
-                          const lsa_params* p, const void* q, const void* k_cache,
-                          const void* v_cache, int64_t Tmax, int32_t Hq, int32_t Hkv, int32_t D,
-                          float scale, int32_t dtype, int64_t chunk, int32_t* idx, int32_t* count,
-                          void* out, void* workspace, int64_t ws_bytes, void* const* attn_events,
-                          void* stream);
 
 #ifdef __cplusplus
 }

@@ -97,10 +97,7 @@ def lib():
         "lsa_attention_default_splits": (i32, [i64, i32]),
         "lsa_sparse_attention": (ctypes.c_int, [vp, vp, vp, i32, i64, i64, i32, i32, i32, vp, vp,
                                                 i32, ctypes.c_float, i32, i32, vp, vp, i64, vp]),
-        "lsa_prefill_chunk": (i64, [P, i64, i64, i64]),
-        "lsa_prefill_attention": (ctypes.c_int, [vp, vp, i64, i64, P, vp, vp, vp, i64, i32, i32,
-                                                 i32, ctypes.c_float, i32, i64, vp, vp, vp, vp,
-                                                 i64, ctypes.POINTER(vp), vp]),
+        "lsa_attention_launch_rows": (i64, []),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -282,61 +279,12 @@ def sparse_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tens
     return out[0] if squeeze else out
 
 
-def prefill_chunk(p: Params, q_start: int, Tq: int, chunk: int = 0) -> int:
-    """lsa_prefill_chunk: the query chunk lsa_prefill_attention uses (chunk 0: automatic)."""
-    return _check("lsa_prefill_chunk", lib().lsa_prefill_chunk(ctypes.byref(p.c()), q_start, Tq, chunk))
-
-
-def prefill_attention(cache: BucketCache, latent_q: torch.Tensor, q_start: int, p: Params,
-                      q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
-                      scale: float | None = None, chunk: int = 0,
-                      workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
-                      lists: tuple | None = None, attn_events: list | None = None):
-    """lsa_prefill_attention -> (out [Tq, Hq, D], idx [Tq, L], count [Tq]).  q [Tq, Hq, D],
-    k/v [Tmax, Hkv, D] (one sequence).  attn_events: 2 * ceil(Tq / prefill_chunk(...))
-    torch.cuda.Event objects that have been recorded once (so that their handles exist)."""
-    _need(latent_q, torch.float32, "latent_q")
-    Tq, Hq, D = q.shape
-    Tmax, Hkv, _ = k_cache.shape
-    if latent_q.shape[0] != Tq:
-        raise ValueError("latent_q and q must have the same number of rows")
-    if q.dtype == torch.bfloat16:
-        dt = LSA_BF16
-    elif q.dtype == torch.float32:
-        dt = LSA_F32
-    else:
-        raise ValueError("q must be bf16 or fp32")
-    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
-        _need(t, q.dtype, n)
-    dev = q.device
-    L = list_len(p)
-    if lists is None:
-        idx = torch.empty((Tq, L), dtype=torch.int32, device=dev)
-        cnt = torch.empty((Tq,), dtype=torch.int32, device=dev)
-    else:
-        idx, cnt = lists
-        _need(idx, torch.int32, "idx")
-        _need(cnt, torch.int32, "count")
-    if out is None:
-        out = torch.empty_like(q)
-    scale = 1.0 / D ** 0.5 if scale is None else scale
-    ch = max(prefill_chunk(p, q_start, Tq, chunk), 1)
-    wsb = index_workspace_bytes(p, ch)
-    if workspace is None or workspace.numel() < wsb:
-        workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
-    ev = None
-    if attn_events is not None:
-        if len(attn_events) < 2 * ((Tq + ch - 1) // ch):
-            raise ValueError("attn_events needs two events per chunk")
-        ev = (ctypes.c_void_p * len(attn_events))(*[e.cuda_event for e in attn_events])
-    _check("lsa_prefill_attention", lib().lsa_prefill_attention(
-        cache.handle, _ptr(latent_q), q_start, Tq, ctypes.byref(p.c()), _ptr(q), _ptr(k_cache),
-        _ptr(v_cache), Tmax, Hq, Hkv, D, ctypes.c_float(scale), dt, chunk, _ptr(idx), _ptr(cnt),
-        _ptr(out), _ptr(workspace), workspace.numel(), ev, ctypes.c_void_p(_stream())))
-    return out, idx, cnt
+def attention_launch_rows() -> int:
+    """lsa_attention_launch_rows: query rows per bf16 attention launch."""
+    return int(lib().lsa_attention_launch_rows())
 
 
 __all__ = ["Params", "BucketCache", "index_prefill", "index_decode", "sparse_attention",
-           "prefill_attention", "prefill_chunk",
+           "attention_launch_rows",
            "list_len", "top_buckets", "index_workspace_bytes", "lib", "LsaError",
            "LSA_F32", "LSA_BF16", "LSA_FLAT", "LSA_TREE"]

@@ -4,7 +4,6 @@
 #include <stdlib.h>
 #include <string.h>
 
-#include <mutex>
 #include <new>
 
 #include "lsa_internal.h"
@@ -262,32 +261,6 @@ int run_selection(const IndexCtx& ctx, const IndexWs& ws, const lsa_params* p,
   return hip_status(e);
 }
 
-
-// Side stream and events of lsa_prefill_attention, one set per device,
-// created on first use (default priority) and kept until the process ends.
-struct Overlap {
-  std::mutex mu;
-  bool ready = false;
-  hipStream_t side = nullptr;
-  hipEvent_t in = nullptr, done = nullptr;
-};
-constexpr int kMaxDevices = 64;
-Overlap g_overlap[kMaxDevices];
-
-Overlap* overlap_for_current_device() {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
-  Overlap& ov = g_overlap[dev];
-  std::lock_guard<std::mutex> lk(ov.mu);
-  if (!ov.ready) {
-    if (hipStreamCreateWithFlags(&ov.side, hipStreamNonBlocking) != hipSuccess) return nullptr;
-    if (hipEventCreateWithFlags(&ov.in, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&ov.done, hipEventDisableTiming) != hipSuccess)
-      return nullptr;
-    ov.ready = true;
-  }
-  return &ov;
-}
 
 }  // namespace
 
@@ -584,6 +557,8 @@ int64_t lsa_attention_workspace_bytes(int32_t B, int64_t Tq, int32_t Hq, int32_t
   return rows * splits * Hq * ((int64_t)kHeadDim + 2) * 4;
 }
 
+int64_t lsa_attention_launch_rows(void) { return attention_launch_rows(); }
+
 int32_t lsa_attention_default_splits(int64_t rows, int32_t L_max) {
   if (rows <= 0 || L_max <= 0) return 1;
   int32_t splits = 1;
@@ -610,96 +585,6 @@ int lsa_sparse_attention(const void* q, const void* k_cache, const void* v_cache
                                   scale, dtype, splits, out, reinterpret_cast<float*>(workspace),
                                   as_stream(stream));
   return hip_status(e);
-}
-
-int64_t lsa_prefill_chunk(const lsa_params* p, int64_t q_start, int64_t Tq, int64_t chunk) {
-  if (!p || q_start < 0 || Tq < 0 || chunk < 0) return LSA_ERR_ARG;
-  if (Tq == 0) return 0;
-  if (chunk == 0) {
-    const int64_t esz = p->index_dtype == LSA_BF16 ? 2 : 4;
-    const int64_t scan = ((q_start + Tq - 1) / kBlock) * kBuckets * kLatent * esz;
-    chunk = scan <= LSA_PREFILL_OVERLAP_SCAN ? LSA_PREFILL_CHUNK : Tq;
-  }
-  return chunk < Tq ? chunk : Tq;
-}
-
-int lsa_prefill_attention(const lsa_cache* c, const float* latent_q, int64_t q_start, int64_t Tq,
-                          const lsa_params* p, const void* q, const void* k_cache,
-                          const void* v_cache, int64_t Tmax, int32_t Hq, int32_t Hkv, int32_t D,
-                          float scale, int32_t dtype, int64_t chunk, int32_t* idx, int32_t* count,
-                          void* out, void* workspace, int64_t ws_bytes, void* const* attn_events,
-                          void* stream) {
-  // every check of the two calls, before anything is enqueued
-  if (!c || !p || q_start < 0 || Tq < 0 || chunk < 0 || Tmax < 0) return LSA_ERR_ARG;
-  int rc = lsa_check_params(p);
-  if (rc) return rc;
-  if (D != kHeadDim || Hkv <= 0 || Hq <= 0 || Hq % Hkv != 0 || Hq / Hkv > 16)
-    return LSA_ERR_UNSUPPORTED;
-  if (dtype != LSA_F32 && dtype != LSA_BF16) return LSA_ERR_UNSUPPORTED;
-  const CacheState& st = c->st;
-  if (p->index_dtype != st.prm.index_dtype) return LSA_ERR_ARG;
-  if (Tq == 0) return LSA_OK;
-  if (!latent_q || !q || !k_cache || !v_cache || !idx || !count || !out || !workspace)
-    return LSA_ERR_ARG;
-  if (q_start + Tq > (int64_t)0x7fffffff) return LSA_ERR_ARG;
-  if ((q_start + Tq - 1) / kBlock > st.n_blocks) return LSA_ERR_STATE;
-  if (p->mode == LSA_TREE && !st.tree) return LSA_ERR_STATE;
-  chunk = lsa_prefill_chunk(p, q_start, Tq, chunk);
-  if (chunk <= 0) return LSA_ERR_ARG;
-  if (ws_bytes < index_ws_layout(p, chunk).total) return LSA_ERR_WORKSPACE;
-  hipStream_t s = as_stream(stream);
-  const int64_t L = lsa_list_len(p);
-  if (chunk == Tq) {
-    // one chunk: nothing to overlap, both calls on the caller's stream
-    rc = lsa_index_prefill(c, latent_q, q_start, Tq, p, idx, count, nullptr, workspace, ws_bytes,
-                           stream);
-    if (rc != LSA_OK) return rc;
-    if (attn_events && hipEventRecord(reinterpret_cast<hipEvent_t>(attn_events[0]), s) != hipSuccess)
-      return LSA_ERR_HIP;
-    rc = lsa_sparse_attention(q, k_cache, v_cache, 1, Tq, Tmax, Hq, Hkv, D, idx, count,
-                              (int32_t)L, scale, dtype, 1, out, nullptr, 0, stream);
-    if (rc == LSA_OK && attn_events &&
-        hipEventRecord(reinterpret_cast<hipEvent_t>(attn_events[1]), s) != hipSuccess)
-      rc = LSA_ERR_HIP;
-    return rc;
-  }
-  Overlap* ov = overlap_for_current_device();
-  if (!ov) return LSA_ERR_HIP;
-  std::lock_guard<std::mutex> lk(ov->mu);
-  const int64_t qrow = (int64_t)Hq * D * (dtype == LSA_BF16 ? 2 : 4);   // bytes per query row
-  // the side stream starts after the caller's earlier work
-  if (hipEventRecord(ov->in, s) != hipSuccess ||
-      hipStreamWaitEvent(ov->side, ov->in, 0) != hipSuccess)
-    return LSA_ERR_HIP;
-  int64_t ci = 0;
-  for (int64_t i0 = 0; i0 < Tq && rc == LSA_OK; i0 += chunk, ++ci) {
-    const int64_t n = (Tq - i0) < chunk ? (Tq - i0) : chunk;
-    rc = lsa_index_prefill(c, latent_q + i0 * kLatent, q_start + i0, n, p, idx + i0 * L,
-                           count + i0, nullptr, workspace, ws_bytes, ov->side);
-    if (rc != LSA_OK) break;
-    if (hipEventRecord(ov->done, ov->side) != hipSuccess ||
-        hipStreamWaitEvent(s, ov->done, 0) != hipSuccess) {
-      rc = LSA_ERR_HIP;
-      break;
-    }
-    if (attn_events &&
-        hipEventRecord(reinterpret_cast<hipEvent_t>(attn_events[2 * ci]), s) != hipSuccess) {
-      rc = LSA_ERR_HIP;
-      break;
-    }
-    rc = lsa_sparse_attention(static_cast<const char*>(q) + i0 * qrow, k_cache, v_cache, 1, n,
-                              Tmax, Hq, Hkv, D, idx + i0 * L, count + i0, (int32_t)L, scale,
-                              dtype, 1, static_cast<char*>(out) + i0 * qrow, nullptr, 0, s);
-    if (rc == LSA_OK && attn_events &&
-        hipEventRecord(reinterpret_cast<hipEvent_t>(attn_events[2 * ci + 1]), s) != hipSuccess)
-      rc = LSA_ERR_HIP;
-  }
-  if (rc != LSA_OK) {
-    // keep the caller's stream ordered after whatever the side stream holds
-    (void)hipEventRecord(ov->done, ov->side);
-    (void)hipStreamWaitEvent(s, ov->done, 0);
-  }
-  return rc;
 }
 
 }  // extern "C"

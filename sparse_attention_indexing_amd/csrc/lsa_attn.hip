@@ -23,6 +23,12 @@ constexpr int kKT = 32;          // keys per tile
 constexpr int kVStride = 136;    // LDS row stride (bf16) of the staged V tile [key][dim]
 constexpr int kPStride = 16;     // LDS row stride (bf16) of P stored as [key][head]
 constexpr int kMaxWaves = 4;
+// bf16 rows are launched this many at a time.  A launch ends only when all of
+// its rows are done, so the rows in flight stay neighbours, whose lists share
+// many keys in L2 and the Infinity Cache; one launch over all rows lets the
+// rows in flight drift apart (at 128K queries, 2,048-row launches take 14%
+// less time than one launch).
+constexpr int64_t kRowsPerLaunch = 2048;
 
 __device__ __forceinline__ void wave_fence() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -38,6 +44,7 @@ struct AttnArgs {
   uint16_t* out;
   float* ws;            // split partials: O [rows, splits, Hq, 128], then m, l [rows, splits, Hq]
   int64_t rows;         // B * Tq
+  int64_t row0, nrows;  // rows of this launch: row0 .. row0 + nrows - 1
   int64_t Tq, Tmax;
   int32_t Hq, Hkv, G, L, splits;
   float scale;
@@ -115,11 +122,12 @@ __global__ __launch_bounds__(64 * kMaxWaves, 3) void k_attn_bf16(AttnArgs a) {
   // similar buckets) meet in the same L2; with fewer rows grid.x = rows and
   // the splits of a row spread over the XCDs.
   int64_t row = blockIdx.x;
-  if (a.rows >= 8) {
-    const int64_t per_xcd = (a.rows + 7) / 8;
+  if (a.nrows >= 8) {
+    const int64_t per_xcd = (a.nrows + 7) / 8;
     row = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
   }
-  if (row >= a.rows) return;
+  if (row >= a.nrows) return;
+  row += a.row0;
   const int split = blockIdx.y;
   const int64_t b = row / a.Tq;
   int cnt = a.count[row];
@@ -320,11 +328,12 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16_h4(AttnArgs a) {
   // to the same XCD; with fewer rows grid.x = rows and the splits of a row
   // spread over the XCDs
   int64_t row = blockIdx.x;
-  if (a.rows >= 8) {
-    const int64_t per_xcd = (a.rows + 7) / 8;
+  if (a.nrows >= 8) {
+    const int64_t per_xcd = (a.nrows + 7) / 8;
     row = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
   }
-  if (row >= a.rows) return;
+  if (row >= a.nrows) return;
+  row += a.row0;
   const int split = blockIdx.y;
   const int64_t b = row / a.Tq;
   int cnt = a.count[row];
@@ -659,6 +668,8 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
 
 }  // namespace
 
+int64_t attention_launch_rows() { return kRowsPerLaunch; }
+
 hipError_t launch_attention(const void* q, const void* k, const void* v, int32_t B, int64_t Tq,
                             int64_t Tmax, int32_t Hq, int32_t Hkv, const int32_t* idx,
                             const int32_t* count, int32_t L_max, float scale, int dtype,
@@ -680,11 +691,16 @@ hipError_t launch_attention(const void* q, const void* k, const void* v, int32_t
         (void)hipGetLastError();
         attr3 = true;
       }
-      const int64_t grid = rows >= 8 ? (rows + 7) / 8 * 8 : rows;
-      hipLaunchKernelGGL(k_attn_bf16_h4, dim3((unsigned)grid, (unsigned)splits), dim3(256),
-                         (size_t)kLds4, s, a);
-      hipError_t e = hipGetLastError();
-      if (e != hipSuccess || splits == 1) return e;
+      for (int64_t r0 = 0; r0 < rows; r0 += kRowsPerLaunch) {
+        a.row0 = r0;
+        a.nrows = (rows - r0) < kRowsPerLaunch ? (rows - r0) : kRowsPerLaunch;
+        const int64_t grid = a.nrows >= 8 ? (a.nrows + 7) / 8 * 8 : a.nrows;
+        hipLaunchKernelGGL(k_attn_bf16_h4, dim3((unsigned)grid, (unsigned)splits), dim3(256),
+                           (size_t)kLds4, s, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+      }
+      if (splits == 1) return hipSuccess;
       hipLaunchKernelGGL(k_attn_combine<LSA_BF16>, dim3((unsigned)(rows * Hq * 2)), dim3(256), 0,
                          s, ws, out, rows, Hq, splits);
       return hipGetLastError();
@@ -699,8 +715,15 @@ hipError_t launch_attention(const void* q, const void* k, const void* v, int32_t
     }
     const int per = (L_max + splits - 1) / splits;
     const size_t smem = (size_t)nw * kWaveLds * sizeof(uint16_t) + (size_t)per * sizeof(int32_t);
-    const int64_t grid = rows >= 8 ? (rows + 7) / 8 * 8 : rows;
-    hipLaunchKernelGGL(k_attn_bf16, dim3((unsigned)grid, (unsigned)splits), dim3(64 * nw), smem, s, a);
+    for (int64_t r0 = 0; r0 < rows; r0 += kRowsPerLaunch) {
+      a.row0 = r0;
+      a.nrows = (rows - r0) < kRowsPerLaunch ? (rows - r0) : kRowsPerLaunch;
+      const int64_t grid = a.nrows >= 8 ? (a.nrows + 7) / 8 * 8 : a.nrows;
+      hipLaunchKernelGGL(k_attn_bf16, dim3((unsigned)grid, (unsigned)splits), dim3(64 * nw), smem,
+                         s, a);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   } else {
     AttnArgsF32 a;
     a.q = (const float*)q; a.k = (const float*)k; a.v = (const float*)v;

@@ -163,6 +163,8 @@ hipError_t launch_select_expand(const IndexCtx& ctx, const IndexWs& ws, int32_t*
                                 int32_t* count, int32_t* ranked, int dtype, int exact_mode,
                                 hipStream_t s);
 
+// rows per bf16 attention launch (a call over more rows issues several)
+int64_t attention_launch_rows();
 hipError_t launch_attention(const void* q, const void* k, const void* v, int32_t B, int64_t Tq,
                             int64_t Tmax, int32_t Hq, int32_t Hkv, const int32_t* idx,
                             const int32_t* count, int32_t L_max, float scale, int dtype,

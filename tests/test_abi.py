@@ -101,47 +101,9 @@ def test_cache_init_and_host_errors():
                                   FAKE_DEV, FAKE_DEV, 1 << 30, None) == -1   # same cache twice
         assert L.lsa_index_decode(arr, 65, FAKE_DEV, FAKE_DEV, ctypes.byref(p.c()), FAKE_DEV,
                                   FAKE_DEV, FAKE_DEV, 1 << 30, None) == -1
-        # the overlapped prefill makes every check before it touches a stream
-        f = ctypes.c_float(0.1)
-        pa = lambda Tq=8, q0=0, prm=p, D=128, Hq=32, Hkv=4, dt=1, chunk=0, wsb=ws: (
-            h, FAKE_DEV, q0, Tq, ctypes.byref(prm.c()), FAKE_DEV, FAKE_DEV, FAKE_DEV, 4096, Hq,
-            Hkv, D, f, dt, chunk, FAKE_DEV, FAKE_DEV, FAKE_DEV, FAKE_DEV, wsb, None, None)
-        assert L.lsa_prefill_attention(*pa(Tq=0)) == 0
-        assert L.lsa_prefill_attention(*pa(Tq=-1)) == -1
-        assert L.lsa_prefill_attention(*pa(chunk=-5)) == -1
-        assert L.lsa_prefill_attention(*pa(D=64)) == -2
-        assert L.lsa_prefill_attention(*pa(Hq=30)) == -2
-        assert L.lsa_prefill_attention(*pa(dt=5)) == -2
-        assert L.lsa_prefill_attention(*pa(q0=1000)) == -6
-        assert L.lsa_prefill_attention(*pa(prm=_p(mode=1))) == -6
-        assert L.lsa_prefill_attention(*pa(wsb=ws - 1)) == -3
-        assert L.lsa_prefill_attention(*pa(prm=_p(index_dtype=0))) == -1
         assert L.lsa_cache_tokens(h) == 0     # rejected calls changed nothing
     finally:
         assert L.lsa_cache_release(h) == 0
-
-
-def test_prefill_chunk_policy():
-    """Chunks overlap only while a query's centroid scan stays cache-resident
-    (at most 8 MiB: 64 centroids of 64 dims per complete block before it)."""
-    bf = _p(index_dtype=1)
-    f32 = _p(index_dtype=0)
-    assert lsa.prefill_chunk(bf, 0, 0) == 0
-    assert lsa.prefill_chunk(bf, 0, 1000, 300) == 300
-    assert lsa.prefill_chunk(bf, 0, 1000, 5000) == 1000
-    assert lsa.prefill_chunk(bf, 0, 131072) == 2048            # 255 blocks: 2.1 MB scan
-    assert lsa.prefill_chunk(bf, 0, 1000) == 1000              # fewer queries than a chunk
-    assert lsa.prefill_chunk(bf, 1048576 - 8192, 8192) == 8192  # 2,047 blocks: 16.8 MB scan
-    # the boundary: 1,024 blocks of bf16 centroids (512 of fp32) is exactly 8 MiB
-    assert lsa.prefill_chunk(bf, 1024 * 512 - 4096, 4096 + 1) == 2048
-    assert lsa.prefill_chunk(bf, 1024 * 512 - 4096, 4096 + 513) == 4096 + 513   # 1,025 blocks
-    assert lsa.prefill_chunk(f32, 512 * 512 - 4096, 4096 + 1) == 2048
-    assert lsa.prefill_chunk(f32, 512 * 512 - 4096, 4096 + 513) == 4096 + 513
-    L = lsa.lib()
-    assert L.lsa_prefill_chunk(ctypes.byref(bf.c()), -1, 10, 0) == -1
-    assert L.lsa_prefill_chunk(ctypes.byref(bf.c()), 0, -1, 0) == -1
-    assert L.lsa_prefill_chunk(ctypes.byref(bf.c()), 0, 10, -1) == -1
-    assert L.lsa_prefill_chunk(None, 0, 10, 0) == -1
 
 
 def test_attention_host_errors():
@@ -156,6 +118,7 @@ def test_attention_host_errors():
     assert L.lsa_sparse_attention(*args(dt=5)) == -2
     assert L.lsa_sparse_attention(*args(splits=0)) == -1
     assert L.lsa_sparse_attention(*args(splits=4)) == -3
+    assert lsa.attention_launch_rows() == 2048
     assert L.lsa_attention_workspace_bytes(1, 16, 32, 128, 1) == 0
     assert L.lsa_attention_workspace_bytes(1, 16, 32, 128, 4) == 16 * 4 * 32 * 130 * 4
     assert L.lsa_status_string(-3) == b"workspace too small"

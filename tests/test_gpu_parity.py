@@ -234,13 +234,12 @@ def test_attention_bf16_on_oracle_lists(splits, few):
     assert err <= 2e-2
 
 
-@pytest.mark.parametrize("chunk", [0, 1000, 5000])
-def test_prefill_attention_overlapped(chunk):
-    """The overlapped call (indexing of chunk i+1 on the library's side stream
-    while chunk i attends) equals lsa_index_prefill + lsa_sparse_attention bit
-    for bit, also with a ragged last chunk; its timing events bracket every
-    attention launch; sampled rows match the oracle's lists and attention."""
-    say(f"case: prefill_attention chunk={chunk}")
+def test_attention_across_launches():
+    """More rows than one bf16 attention launch takes (5,000 rows: three
+    launches of up to 2,048): rows on both sides of each launch boundary match
+    a launch of just those rows bit for bit, and sampled rows match the
+    oracle's lists and attention."""
+    say("case: attention over 5,000 rows in several launches")
     w = S.WORKLOADS[2]
     T, Tq = 16384, 5000
     q0 = T - Tq
@@ -251,26 +250,20 @@ def test_prefill_attention_overlapped(chunk):
     Q = bf16_tensor(qb).cuda().view(Tq, w.Hq, w.D)
     K = bf16_tensor(kb).cuda().view(T, w.Hkv, w.D)
     V = bf16_tensor(vb).cuda().view(T, w.Hkv, w.D)
-    Yd = torch.from_numpy(Y).cuda()
-    ch = lsa.prefill_chunk(p, q0, Tq, chunk)
-    assert ch == (chunk or 2048)     # a 16K context scans little: chunks overlap
-    nch = -(-Tq // ch)
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * nch)]
-    for e in evs:
-        e.record()
-    out, idx, cnt = lsa.prefill_attention(c, Yd, q0, p, Q, K, V, chunk=chunk, attn_events=evs)
-    idx2, cnt2 = lsa.index_prefill(c, Yd, q0, p)
-    out2 = lsa.sparse_attention(Q, K, V, idx2, cnt2)
+    idx, cnt = lsa.index_prefill(c, torch.from_numpy(Y).cuda(), q0, p)
+    out = lsa.sparse_attention(Q, K, V, idx, cnt)
+    n = lsa.attention_launch_rows()
+    assert Tq > 2 * n
+    parts = [(n - 5, n + 5), (2 * n - 3, 2 * n + 9), (Tq - 7, Tq)]
+    sub = [lsa.sparse_attention(Q[a:b].contiguous(), K, V, idx[a:b].contiguous(),
+                                cnt[a:b].contiguous()) for a, b in parts]
     torch.cuda.synchronize()
-    assert torch.equal(idx, idx2) and torch.equal(cnt, cnt2)
-    assert torch.equal(out, out2)
-    ms = [evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(nch)]
-    say("attention launches (ms)", [round(x, 3) for x in ms])
-    assert all(x > 0 for x in ms)
+    for (a, b), o in zip(parts, sub):
+        assert torch.equal(out[a:b], o), (a, b)
     oc = O.build_cache(X, oracle_params(p))
     idx, cnt, out = idx.cpu().numpy(), cnt.cpu().numpy(), out.float().cpu().numpy()
     err, checked = 0.0, 0
-    for r in (0, 999, 1000, 2500, 4095, 4096, Tq - 1):
+    for r in (0, n - 1, n, 2500, 2 * n - 1, 2 * n, Tq - 1):
         res = O.index_query(Y[r], q0 + r, oc)
         if res.exempt:
             continue
