@@ -1442,13 +1442,15 @@ __device__ __forceinline__ uint64_t match_digit(uint32_t d, uint64_t active) {
 }
 
 // Stable LSD radix sort (DB-bit digits) of n non-negative int32 keys in LDS,
-// ascending, by a workgroup of NT threads (NW = NT / 64 waves).  Wave w owns
+// ascending by their bits lo and up (the bits below lo keep their input
+// order), by a workgroup of NT threads (NW = NT / 64 waves).  Wave w owns
 // the contiguous chunk [w*ch, (w+1)*ch); `tmp` is a second buffer of n ints,
 // `cnt` NW x 2^DB counters (one row per wave); the scatter ranks lanes with
 // equal digits by ballots, which keeps it stable.  Returns the buffer that
 // holds the result.
 template <int DB, int NT = 256>
-__device__ int32_t* radix_sort_i32(int32_t* keys, int32_t* tmp, int n, int max_key, uint32_t* cnt) {
+__device__ int32_t* radix_sort_i32(int32_t* keys, int32_t* tmp, int n, int max_key, int lo,
+                                   uint32_t* cnt) {
   constexpr int NB = 1 << DB;
   constexpr int NW = NT / 64;
   constexpr int E = NB * NW / NT;                // counters per thread in the scan
@@ -1457,14 +1459,24 @@ __device__ int32_t* radix_sort_i32(int32_t* keys, int32_t* tmp, int n, int max_k
   const int ch = (n + NW - 1) / NW;
   const int c0 = wave * ch;
   const int c1 = (c0 + ch) < n ? (c0 + ch) : n;
-  int bits = 0;
+  int bits = lo;
   while (bits < 31 && (max_key >> bits) != 0) bits += DB;
   __shared__ int wsum_r[NW];
-  for (int shift = 0; shift < bits; shift += DB) {
+  for (int shift = lo; shift < bits; shift += DB) {
     for (int i = tid; i < NW * NB; i += NT) cnt[i] = 0;
     __syncthreads();
     uint32_t* my = cnt + wave * NB;
-    for (int e = c0 + lane; e < c1; e += 64) atomicAdd(&my[((uint32_t)keys[e] >> shift) & (NB - 1)], 1u);
+    // histogram with one atomic per distinct digit and wave (sorted runs of
+    // keys share their high digits, which would serialise per-lane atomics)
+    for (int e0 = c0; e0 < c1; e0 += 64) {
+      const int e = e0 + lane;
+      const bool ok = e < c1;
+      const uint64_t active = __ballot(ok);
+      const uint32_t d = ok ? ((uint32_t)keys[e] >> shift) & (NB - 1) : 0u;
+      const uint64_t peers = match_digit<DB>(d, active);
+      if (ok && (peers & ((1ull << lane) - 1ull)) == 0)
+        atomicAdd(&my[d], (uint32_t)__popcll(peers));
+    }
     __syncthreads();
     {
       // digit-major, wave-minor exclusive offsets; thread t owns the E
@@ -1701,12 +1713,42 @@ __global__ __launch_bounds__(NT) void k_select_expand(IndexCtx ctx, IndexWs ws, 
   }
   __syncthreads();
   // ---- emit far keys: whole buckets above S* (every bucket without a cut),
-  // the cut bucket's first members
+  // the cut bucket's first members.  They are emitted as pooled items (4
+  // consecutive keys at a multiple of 4) with the mask of their keys taken:
+  // an item belongs to one bucket, so sorting the items by position sorts the
+  // keys, with a quarter of the elements.
   const int trunc_m = s_trunc_m;
   const uint32_t gstar = 0xFFFFFFFFu - gstar_key;
   const int n_far = cut ? k : total;
-  // each thread takes a contiguous run of candidates, so one block scan gives
-  // every thread its output offset
+  static_assert(kPool == 4, "items are packed as (position / 4) << 4 | 4-bit key mask");
+  // the items of candidate i taking `take` far keys, in member (= key) order
+  auto for_items = [&](int i, uint32_t m, int take, auto&& f) {
+    const int64_t kb = (int64_t)(sbkt[i] / kBuckets) * kBlock;
+    const bool clean = kb >= s_end && kb + kBlock <= w_start;   // no sink or window key
+    if (clean && take == (int)contrib[i]) {
+      // the whole bucket: every member item with all of its keys
+#pragma unroll
+      for (int q = 0; q < kCapItems; ++q) {
+        const uint32_t j = (m >> (8 * q)) & 0xFFu;
+        if (j != 0xFFu) f((int32_t)(((kb + kPool * j) >> 2) << 4) | 15);
+      }
+      return;
+    }
+#pragma unroll
+    for (int q = 0; q < kCapItems; ++q) {
+      const uint32_t j = (m >> (8 * q)) & 0xFFu;
+      if (j == 0xFFu || take <= 0) break;
+      const int64_t k0 = kb + kPool * j;
+      uint32_t mask = 0;
+#pragma unroll
+      for (int u = 0; u < kPool; ++u) {
+        const int64_t key = k0 + u;
+        if (take > 0 && (clean || !(key < s_end || key >= w_start))) { mask |= 1u << u; --take; }
+      }
+      if (mask) f((int32_t)((k0 >> 2) << 4) | (int32_t)mask);
+    }
+  };
+  int n_items;
   {
     auto take_of = [&](int i) -> int {
       if (!cut || skey[i] > prefix || (skey[i] == prefix && sbkt[i] < gstar)) return contrib[i];
@@ -1719,44 +1761,19 @@ __global__ __launch_bounds__(NT) void k_select_expand(IndexCtx ctx, IndexWs ws, 
     for (int jj = 0; jj < PER; ++jj) {
       const int i = tid + NT * jj;
       tk[jj] = i < c ? take_of(i) : 0;
-      mine += tk[jj];
+      if (tk[jj] > 0) for_items(i, mw[jj], tk[jj], [&](int32_t) { ++mine; });
     }
-    int all_take;
-    int o = block_scan_nt<NT>(mine, wsum, &all_take);
+    int o = block_scan_nt<NT>(mine, wsum, &n_items);
 #pragma unroll
-    for (int jj = 0; jj < PER; ++jj) {
-      int left = tk[jj];
-      if (left == 0) continue;
-      const int i = tid + NT * jj;
-      const uint32_t g = sbkt[i];
-      const uint32_t m = mw[jj];
-      const int64_t kb = (int64_t)(g / kBuckets) * kBlock;
-      if (left == (int)contrib[i] && kb >= s_end && kb + kBlock <= w_start) {
-        // the whole bucket, in a block without sink or window keys
-#pragma unroll
-        for (int q = 0; q < kCapItems; ++q) {
-          const uint32_t j = (m >> (8 * q)) & 0xFFu;
-          if (j != 0xFFu) {
-            const int32_t k0 = (int32_t)(kb + kPool * j);
-            far[o] = k0; far[o + 1] = k0 + 1; far[o + 2] = k0 + 2; far[o + 3] = k0 + 3;
-            o += kPool;
-          }
-        }
-        continue;
-      }
-      for (int q = 0; q < kCapItems && left > 0; ++q) {
-        const uint32_t j = (m >> (8 * q)) & 0xFFu;
-        if (j == 0xFFu) break;
-        for (int u = 0; u < kPool && left > 0; ++u) {
-          const int64_t key = kb + kPool * j + u;
-          if (!(key < s_end || key >= w_start)) { far[o++] = (int32_t)key; --left; }
-        }
-      }
-    }
+    for (int jj = 0; jj < PER; ++jj)
+      if (tk[jj] > 0) for_items(tid + NT * jj, mw[jj], tk[jj], [&](int32_t it) { far[o++] = it; });
   }
   __syncthreads();
-  const int32_t* sorted_far = radix_sort_i32<8, NT>(far, far2, n_far, (int)(p > 0 ? p : 0), &hist[0][0]);
-  // sinks | far | window, -1 padded
+  // sort by position (bits 4 and up); positions are below p
+  const int32_t* items = radix_sort_i32<8, NT>(far, far2, n_items, (int)((p > 0 ? p : 0) >> 2) << 4,
+                                               4, &hist[0][0]);
+  // sinks | far | window, -1 padded; the far keys come from the sorted items,
+  // each thread expanding a contiguous run of them
   int32_t* out = idx + qi * (int64_t)ctx.list_len;
   int cnt;
   if (w_start <= s_end) {
@@ -1765,12 +1782,24 @@ __global__ __launch_bounds__(NT) void k_select_expand(IndexCtx ctx, IndexWs ws, 
   } else {
     const int ns = (int)s_end, nw = (int)(p - w_start + 1);
     cnt = ns + n_far + nw;
+    const int run = (n_items + NT - 1) / NT;
+    const int i0 = tid * run < n_items ? tid * run : n_items;
+    const int i1 = i0 + run < n_items ? i0 + run : n_items;
+    int nk = 0;
+    for (int i = i0; i < i1; ++i) nk += __popc((uint32_t)items[i] & 15u);
+    int tot_k;
+    int o = ns + block_scan_nt<NT>(nk, wsum, &tot_k);
+    for (int i = i0; i < i1; ++i) {
+      const int32_t it = items[i];
+      const int32_t base = (it >> 4) << 2;
+#pragma unroll
+      for (int u = 0; u < kPool; ++u)
+        if ((it >> u) & 1) out[o++] = base + u;
+    }
     for (int i = tid; i < ctx.list_len; i += NT) {
-      int32_t v = -1;
-      if (i < ns) v = i;
-      else if (i < ns + n_far) v = sorted_far[i - ns];
-      else if (i < cnt) v = (int32_t)(w_start + (i - ns - n_far));
-      out[i] = v;
+      if (i < ns) out[i] = i;
+      else if (i >= ns + n_far && i < cnt) out[i] = (int32_t)(w_start + (i - ns - n_far));
+      else if (i >= cnt) out[i] = -1;
     }
   }
   if (tid == 0) count[qi] = cnt;
