@@ -336,11 +336,15 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16_h4(AttnArgs a) {
   row += a.row0;
   const int split = blockIdx.y;
   const int64_t b = row / a.Tq;
+  // split ranges come from the list capacity, so the list can be staged while
+  // the row's count is still in flight; the count only trims the range
+  const int per = (a.L + a.splits - 1) / a.splits;
+  const int k0 = split * per;
+  const int kend = (k0 + per) < a.L ? (k0 + per) : a.L;
+  const int navail = kend > k0 ? kend - k0 : 0;
   int cnt = a.count[row];
   cnt = cnt < 0 ? 0 : (cnt > a.L ? a.L : cnt);
-  const int per = (cnt + a.splits - 1) / a.splits;
-  const int k0 = split * per;
-  const int k1 = (k0 + per) < cnt ? (k0 + per) : cnt;
+  const int k1 = kend < cnt ? kend : cnt;
   const int n = k1 > k0 ? k1 - k0 : 0;
   const int32_t* lst = a.idx + row * (int64_t)a.L + k0;
   const int kvh = wave;
@@ -352,6 +356,16 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16_h4(AttnArgs a) {
   const int r16 = lane & 15, u = lane >> 4;
   const int64_t Tmax = a.Tmax;
 
+  // the first batch of list entries is requested before anything else: the
+  // tiles' addresses wait on it
+  constexpr int kB = 12;
+  const int m0 = navail < kList4 ? navail : kList4;    // entries of the first chunk
+  int32_t t0[kB];
+#pragma unroll
+  for (int u = 0; u < kB; ++u) {
+    const int i = (int)threadIdx.x + 256 * u;
+    t0[u] = i < m0 ? lst[i] : 0;
+  }
   bf16x8 qf[4];
   {
     const bool ok = r16 < a.G;
@@ -381,11 +395,38 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16_h4(AttnArgs a) {
 
   u32x4_t kr[kRing4][4], vr[kRing4][4];
   bool kval[kRing4];
+  // list entries [c0 + from, c0 + m) into slist: every load of a batch is
+  // issued before the stores, one memory latency per 3,072 entries
+  auto stage = [&](int c0, int from, int m) {
+    for (int base = from; base < m; base += 256 * kB) {
+      int32_t t[kB];
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        const int i = base + (int)threadIdx.x + 256 * u;
+        t[u] = i < m ? lst[c0 + i] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        const int i = base + (int)threadIdx.x + 256 * u;
+        if (i < m) slist[i] = t[u];
+      }
+    }
+  };
+  // the first chunk is staged without waiting for the count
+#pragma unroll
+  for (int u = 0; u < kB; ++u) {
+    const int i = (int)threadIdx.x + 256 * u;
+    if (i < m0) slist[i] = t0[u];
+  }
+  stage(0, 256 * kB, m0);
+  __syncthreads();
   for (int c0 = 0; c0 < n; c0 += kList4) {
     const int cn = (n - c0) < kList4 ? (n - c0) : kList4;
-    if (c0 > 0) __syncthreads();               // every wave is done with the previous chunk
-    for (int i = threadIdx.x; i < cn; i += 256) slist[i] = lst[c0 + i];
-    __syncthreads();
+    if (c0 > 0) {
+      __syncthreads();                         // every wave is done with the previous chunk
+      stage(c0, 0, cn);
+      __syncthreads();
+    }
     const int nt = (cn + 15) >> 4;
 
     // tile T into one ring buffer; kv: this lane's key (column r16) is real
