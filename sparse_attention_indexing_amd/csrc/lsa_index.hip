@@ -1443,7 +1443,8 @@ __device__ __forceinline__ uint64_t match_digit(uint32_t d, uint64_t active) {
 
 // Stable LSD radix sort (DB-bit digits) of n non-negative int32 keys in LDS,
 // ascending by their bits lo and up (the bits below lo keep their input
-// order), by a workgroup of NT threads (NW = NT / 64 waves).  Wave w owns
+// order), by a workgroup of NT threads of which the first NW = min(NT / 64, 4)
+// waves hold the keys.  Wave w owns
 // the contiguous chunk [w*ch, (w+1)*ch); `tmp` is a second buffer of n ints,
 // `cnt` NW x 2^DB counters (one row per wave); the scatter ranks lanes with
 // equal digits by ballots, which keeps it stable.  Returns the buffer that
@@ -1452,7 +1453,9 @@ template <int DB, int NT = 256>
 __device__ int32_t* radix_sort_i32(int32_t* keys, int32_t* tmp, int n, int max_key, int lo,
                                    uint32_t* cnt) {
   constexpr int NB = 1 << DB;
-  constexpr int NW = NT / 64;
+  // at most four waves hold keys: fewer counters to clear and scan, which is
+  // what a sort of a few hundred keys by a wide workgroup spends its time on
+  constexpr int NW = (NT / 64) < 4 ? (NT / 64) : 4;
   constexpr int E = NB * NW / NT;                // counters per thread in the scan
   static_assert(E >= 1 && NB * NW == E * NT, "counter layout");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1461,7 +1464,7 @@ __device__ int32_t* radix_sort_i32(int32_t* keys, int32_t* tmp, int n, int max_k
   const int c1 = (c0 + ch) < n ? (c0 + ch) : n;
   int bits = lo;
   while (bits < 31 && (max_key >> bits) != 0) bits += DB;
-  __shared__ int wsum_r[NW];
+  __shared__ int wsum_r[NT / 64];
   for (int shift = lo; shift < bits; shift += DB) {
     for (int i = tid; i < NW * NB; i += NT) cnt[i] = 0;
     __syncthreads();
@@ -1611,6 +1614,17 @@ __global__ __launch_bounds__(NT) void k_select_expand(IndexCtx ctx, IndexWs ws, 
   // candidates (raw score bits, bucket) into LDS: from the scoring pass, or
   // from the exact selection when that list is unusable (exact_mode 1) or
   // always (exact_mode 2); tree candidates are taken as they are (mode 0)
+  const uint2* cand = ws.cand + qi * (int64_t)cap;
+  uint2 e[PER];
+  if constexpr (NT >= 1024) {
+    // a few queries (decode): every slot is requested together with the count,
+    // which saves the count's latency on the path that a query waits on
+#pragma unroll
+    for (int jj = 0; jj < PER; ++jj) {
+      const int i = tid + NT * jj;
+      e[jj] = i < cap ? cand[i] : make_uint2(0, 0);
+    }
+  }
   int c = ws.cand_cnt[qi];
   {
     const int64_t ne = n_eligible(p);
@@ -1620,12 +1634,12 @@ __global__ __launch_bounds__(NT) void k_select_expand(IndexCtx ctx, IndexWs ws, 
                                wsum, &s_total);
     } else {
       c = c < cap ? c : cap;
-      const uint2* cand = ws.cand + qi * (int64_t)cap;
-      uint2 e[PER];
+      if constexpr (NT < 1024) {
 #pragma unroll
-      for (int jj = 0; jj < PER; ++jj) {
-        const int i = tid + NT * jj;
-        e[jj] = i < c ? cand[i] : make_uint2(0, 0);
+        for (int jj = 0; jj < PER; ++jj) {
+          const int i = tid + NT * jj;
+          e[jj] = i < c ? cand[i] : make_uint2(0, 0);
+        }
       }
 #pragma unroll
       for (int jj = 0; jj < PER; ++jj) {
