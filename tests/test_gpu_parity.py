@@ -274,6 +274,75 @@ def test_attention_across_launches():
     assert checked >= 4 and err <= 2e-2
 
 
+def _random_lists(rng, positions, L, short=()):
+    """Sorted distinct key positions <= each query position, L per row (fewer
+    for the rows in `short`), -1 padded."""
+    idx = np.full((len(positions), L), -1, np.int32)
+    cnt = np.zeros(len(positions), np.int32)
+    for i, pos in enumerate(positions):
+        n = min(L - (100 if i in short else 0), int(pos) + 1)
+        idx[i, :n] = np.sort(rng.choice(int(pos) + 1, size=n, replace=False))
+        cnt[i] = n
+    return idx, cnt
+
+
+@pytest.mark.parametrize("L", [8192, 8193, 9000])
+def test_attention_lists_longer_than_a_staged_chunk(L):
+    """Lists longer than the 8,192 entries that the four-KV-head bf16 kernel
+    stages in LDS at a time (a second chunk), one row shorter than L."""
+    say(f"case: attention bf16 with lists of {L} keys")
+    w = S.WORKLOADS[2]
+    T = 20000
+    rows = np.array([T - 1, 15000, 12345])
+    q, k, v, qb, kb, vb = _qkv_host(w, T, rows)
+    idx, cnt = _random_lists(np.random.default_rng(L), rows, L, short=(2,))
+    out = lsa.sparse_attention(bf16_tensor(qb).cuda().view(len(rows), w.Hq, w.D),
+                               bf16_tensor(kb).cuda().view(T, w.Hkv, w.D),
+                               bf16_tensor(vb).cuda().view(T, w.Hkv, w.D),
+                               torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda())
+    torch.cuda.synchronize()
+    out = out.float().cpu().numpy()
+    err = max(np.abs(out[i] - O.attention_query(q[i], k, v, idx[i], cnt[i])).max()
+              for i in range(len(rows)))
+    say("attention bf16 max abs err", err)
+    assert err <= 2e-2
+
+
+def test_attention_batched_rows_across_launches():
+    """Two sequences of 1,500 query rows each (3,000 rows: two launches of up to
+    2,048, the boundary inside the second sequence), each with its own K/V."""
+    say("case: attention bf16, B = 2 x 1,500 rows")
+    w = S.WORKLOADS[2]
+    B, T, Tq, L = 2, 4096, 1500, 600
+    pos = np.arange(T - Tq, T)
+    qs, ks, vs, qbs, kbs, vbs = [], [], [], [], [], []
+    for b in range(B):
+        q, qb = S.normal_rows(w, "q", pos, w.Hq * w.D, seq=b)
+        k, kb = S.normal_rows(w, "k", np.arange(T), w.Hkv * w.D, seq=b)
+        v, vb = S.normal_rows(w, "v", np.arange(T), w.Hkv * w.D, seq=b)
+        qs.append(q.reshape(Tq, w.Hq, w.D)); ks.append(k.reshape(T, w.Hkv, w.D))
+        vs.append(v.reshape(T, w.Hkv, w.D))
+        qbs.append(qb); kbs.append(kb); vbs.append(vb)
+    rng = np.random.default_rng(7)
+    lists = [_random_lists(rng, pos, L) for _ in range(B)]
+    idx = np.stack([x[0] for x in lists])
+    cnt = np.stack([x[1] for x in lists])
+    dev = lambda bits, shape: bf16_tensor(np.stack(bits)).cuda().view(*shape)
+    out = lsa.sparse_attention(dev(qbs, (B, Tq, w.Hq, w.D)), dev(kbs, (B, T, w.Hkv, w.D)),
+                               dev(vbs, (B, T, w.Hkv, w.D)), torch.from_numpy(idx).cuda(),
+                               torch.from_numpy(cnt).cuda())
+    torch.cuda.synchronize()
+    out = out.float().cpu().numpy()
+    n = lsa.attention_launch_rows()
+    err = 0.0
+    for g in (0, 1, Tq - 1, Tq, n - 2, n - 1, n, n + 1, B * Tq - 1):
+        b, r = divmod(g, Tq)
+        err = max(err, np.abs(out[b, r] - O.attention_query(qs[b][r], ks[b], vs[b], idx[b, r],
+                                                            cnt[b, r])).max())
+    say("attention bf16 max abs err", err)
+    assert err <= 2e-2
+
+
 def test_end_to_end_c1():
     """GPU lists feed GPU attention; compared with the oracle's own lists and
     attention wherever the query is not a near tie."""
