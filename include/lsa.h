@@ -228,7 +228,10 @@ int32_t lsa_attention_default_splits(int64_t rows, int32_t L_max);
  * scale multiplies q.k (pass 1/sqrt(D)).  splits >= 1 splits each list into
  * that many parts whose partial softmax states are combined afterwards
  * (decode); needs lsa_attention_workspace_bytes of workspace.
- * A row with count 0 produces zeros.
+ * A row with count 0 produces zeros.  List entries outside [0, Tmax) and
+ * entries past a row's count are ignored; the bf16 kernels still load token
+ * 0's rows for them (with zero weight), so Tmax must be at least 1 when
+ * B * Tq > 0 (else LSA_ERR_ARG).
  */
 int lsa_sparse_attention(const void* q, const void* k_cache, const void* v_cache, int32_t B,
                          int64_t Tq, int64_t Tmax, int32_t Hq, int32_t Hkv, int32_t D,

@@ -577,6 +577,7 @@ int lsa_sparse_attention(const void* q, const void* k_cache, const void* v_cache
   if (dtype != LSA_F32 && dtype != LSA_BF16) return LSA_ERR_UNSUPPORTED;
   if ((int64_t)B * Tq == 0) return LSA_OK;
   if (!q || !k_cache || !v_cache || !idx || !count || !out) return LSA_ERR_ARG;
+  if (Tmax < 1) return LSA_ERR_ARG;   // invalid list entries read token 0 (with zero weight)
   if ((int64_t)B * Tq > (int64_t)0x7fffffff || splits > 65535) return LSA_ERR_UNSUPPORTED;
   if (splits > 1 && (int64_t)B * Tq * Hq * 2 > (int64_t)0x7fffffff) return LSA_ERR_UNSUPPORTED;
   const int64_t need = lsa_attention_workspace_bytes(B, Tq, Hq, D, splits);

@@ -118,6 +118,9 @@ def test_attention_host_errors():
     assert L.lsa_sparse_attention(*args(dt=5)) == -2
     assert L.lsa_sparse_attention(*args(splits=0)) == -1
     assert L.lsa_sparse_attention(*args(splits=4)) == -3
+    empty_cache = list(args())
+    empty_cache[5] = 0                     # Tmax = 0 with rows to attend
+    assert L.lsa_sparse_attention(*empty_cache) == -1
     assert lsa.attention_launch_rows() == 2048
     assert L.lsa_attention_workspace_bytes(1, 16, 32, 128, 1) == 0
     assert L.lsa_attention_workspace_bytes(1, 16, 32, 128, 4) == 16 * 4 * 32 * 130 * 4
