@@ -54,6 +54,9 @@ def parse():
                     help="time decode steps (cfg 3: 16 sequences at 1M; cfg 5: one at 10M)")
     ap.add_argument("--splits", type=int, default=0,
                     help="decode attention splits (0: the library's lsa_attention_default_splits)")
+    ap.add_argument("--whole-context", action="store_true",
+                    help="prefill the whole context in chunks of the workload's query count "
+                         "(cfg 4, 5): append a chunk of keys, index its queries, attend")
     return ap.parse_args()
 
 
@@ -212,6 +215,120 @@ def bench_decode(args, w, dev):
     print(json.dumps(res), flush=True)
 
 
+def bench_whole_context(args, w, dev):
+    """The whole context prefilled in chunks of w.Tq queries, aligned so that the
+    last chunk is the workload's measured final chunk (the first one is shorter).
+    Per chunk: build_bucket_cache appends the chunk's latent keys (clustering the
+    blocks that fill up, rebuilding the tree's right edge in tree mode), then
+    lsa_index_prefill indexes the chunk's queries and lsa_sparse_attention
+    attends over their lists.  K and V hold all T tokens; Q and the output are
+    one chunk's buffers, reused (their values do not change the work; the
+    per-position latent queries decide the lists).  One step = the whole
+    context; no warm-up beyond one small chunk on a scratch cache."""
+    import ctypes
+
+    import torch
+
+    import lsa_synth as S
+    import sparse_attention_indexing_amd as lsa
+
+    if w.batch != 1 or w.q_start == 0:
+        raise SystemExit("--whole-context needs a last-chunk workload (cfg 4, 5)")
+    t_gen = time.perf_counter()
+    X, Y, _ = S.latent_inputs(w, query_rows=(0, w.T))
+    Xd = torch.from_numpy(X).to(dev)
+    Yd = torch.from_numpy(Y).to(dev)
+    del X, Y
+    C = w.Tq
+    Q = torch.empty((C, w.Hq, w.D), dtype=torch.bfloat16, device=dev)
+    K = torch.empty((w.T, w.Hkv, w.D), dtype=torch.bfloat16, device=dev)
+    V = torch.empty_like(K)
+    for t, name, off in ((Q, "q", w.q_start * w.Hq * w.D), (K, "k", 0), (V, "v", 0)):
+        S.device_fill_normal(t.data_ptr(), t.numel(), S.philox_key(w.cfg, name), off, True,
+                             torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.perf_counter() - t_gen:.1f}s")
+    mode = lsa.LSA_TREE if args.mode == "tree" else lsa.LSA_FLAT
+    p = lsa.Params(k=w.k, n_sink=w.n_sink, window=w.window, mode=mode, beam=w.beam,
+                   index_dtype=lsa.LSA_BF16)
+    L = lsa.list_len(p)
+    nbytes = lsa.lib().lsa_cache_bytes(ctypes.byref(p.c()), w.T)
+    cache_mem = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    idx = torch.empty((C, L), dtype=torch.int32, device=dev)
+    cnt = torch.empty((C,), dtype=torch.int32, device=dev)
+    ws = torch.empty(lsa.index_workspace_bytes(p, C), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(Q)
+    rows_total = torch.zeros((), dtype=torch.int64, device=dev)
+
+    def fresh_cache():
+        c = lsa.BucketCache.__new__(lsa.BucketCache)
+        c.params, c.mem = p, cache_mem
+        h = ctypes.c_void_p()
+        lsa._check("lsa_cache_init", lsa.lib().lsa_cache_init(
+            ctypes.byref(p.c()), w.T, lsa._ptr(cache_mem), nbytes, ctypes.byref(h)))
+        c.handle = h
+        return c
+
+    first = w.T - (w.T - 1) // C * C if w.T % C else C
+    bounds = [(0, first)] + [(s0, s0 + C) for s0 in range(first, w.T, C)]
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    # warm-up: the first chunk on a scratch cache
+    c = fresh_cache()
+    c.build(Xd[:first])
+    lsa.index_prefill(c, Yd[:first], 0, p, workspace=ws, out=(idx[:first], cnt[:first]))
+    lsa.sparse_attention(Q[:first], K, V, idx[:first], cnt[:first], out=out[:first])
+    torch.cuda.synchronize()
+    c = fresh_cache()
+    marks = []
+    t0 = time.perf_counter()
+    for i, (s0, s1) in enumerate(bounds):
+        n = s1 - s0
+        e = [ev() for _ in range(4)]
+        e[0].record()
+        c.build(Xd[s0:s1])
+        e[1].record()
+        lsa.index_prefill(c, Yd[s0:s1], s0, p, workspace=ws, out=(idx[:n], cnt[:n]))
+        e[2].record()
+        lsa.sparse_attention(Q[:n], K, V, idx[:n], cnt[:n], out=out[:n])
+        e[3].record()
+        rows_total += cnt[:n].to(torch.int64).sum()
+        marks.append(e)
+        if (i + 1) % 50 == 0:
+            log(f"chunk {i + 1}/{len(bounds)} queued, {time.perf_counter() - t0:.1f}s")
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    st = np.array([[a.elapsed_time(b), b.elapsed_time(c_), c_.elapsed_time(d)] for a, b, c_, d in marks])
+    t_build, t_index, t_attn = st.sum(axis=0)
+    total_ms = marks[0][0].elapsed_time(marks[-1][3])
+    log(f"whole context: {total_ms:.1f} ms on the GPU ({wall:.1f} s wall): build {t_build:.1f}, "
+        f"index {t_index:.1f}, attention {t_attn:.1f} ms over {len(bounds)} chunks")
+    launches = sum(-(-(s1 - s0) // lsa.attention_launch_rows()) for s0, s1 in bounds)
+    whole_name = workload_name(w.name, args.mode).replace("_q32k", "_whole").replace("_q8k", "_whole")
+    if not whole_name.endswith("_" + args.mode):
+        whole_name += "_" + args.mode
+    attn_bytes = (int(rows_total.item()) * w.Hkv * w.D * 2 * 2 + 2 * w.T * w.Hq * w.D * 2
+                  + w.T * L * 4)
+    achieved = attn_bytes / (t_attn * 1e-3) / 1e9
+    res = {
+        "metric": f"whole-context prefill query tok/s per layer ({args.mode})",
+        "value": round(w.T / (total_ms * 1e-3), 1), "unit": "query tok/s", "n_gpus": 1,
+        "steps": 1, "warmup": 1, "ms_per_step": round(total_ms, 2), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": whole_name, "T": w.T, "chunk": C, "chunks": len(bounds),
+                   "Hq": w.Hq, "Hkv": w.Hkv, "head_dim": w.D, "k": w.k, "mode": args.mode,
+                   "parallelism": "none"},
+        "stages_ms": {"build": round(float(t_build), 2), "index": round(float(t_index), 2),
+                      "attention": round(float(t_attn), 2)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "k_attn_bf16_h4", "launches_per_step": launches,
+                     "algorithmic_bytes": round(attn_bytes / launches),
+                     "kernel_ms": round(float(t_attn) / launches, 4)},
+        "wall_s": round(wall, 2),
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -228,6 +345,8 @@ def main():
     torch.cuda.set_device(dev)
     if args.decode:
         return bench_decode(args, w, dev)
+    if args.whole_context:
+        return bench_whole_context(args, w, dev)
     if w.batch != 1:
         raise SystemExit("prefill timing needs a single-sequence workload (cfg 1, 2, 4, 5)")
     t_gen = time.perf_counter()

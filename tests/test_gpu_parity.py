@@ -393,6 +393,54 @@ def test_tree_build_and_search():
     say("tree index", rep)
 
 
+# ---------------------------------------------------------------- whole-context prefill
+
+def _oracle_prefix(oc, nb):
+    """The oracle cache as it stands with only the first nb blocks clustered."""
+    M = oc.params.n_buckets
+    return O.BucketCache(oc.params, nb, oc.centroids[:nb * M], oc.members[:nb * M],
+                         oc.pooled[:nb * M], oc.block_min_gap[:nb], oc.block_ess[:nb])
+
+
+@pytest.mark.parametrize("mode", [lsa.LSA_FLAT, lsa.LSA_TREE])
+def test_chunked_whole_context_prefill(mode):
+    """A whole context prefilled in chunks: the cache grows by a chunk of keys
+    (clustering the blocks that fill up, and in tree mode rebuilding the tree
+    above them), then the chunk's queries are indexed.  11,000 tokens in
+    chunks of 2,048 (the last one ragged, ending inside a block).  Flat lists
+    equal one index over the finished cache bit for bit (the causal mask hides
+    later blocks); tree lists match the oracle's tree over the blocks that exist
+    when the chunk is indexed."""
+    say(f"case: chunked whole-context prefill mode={mode}")
+    w = S.WORKLOADS[4]
+    T, C = 11000, 2048
+    X, Y, _ = S.latent_inputs(w, T=T, query_rows=(0, T))
+    p = lsa.Params(k=256, index_dtype=lsa.LSA_BF16, mode=mode, beam=64)
+    c = lsa.BucketCache(p, T)
+    Xd, Yd = torch.from_numpy(X).cuda(), torch.from_numpy(Y).cuda()
+    L = lsa.list_len(p)
+    idx = torch.empty((T, L), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((T,), dtype=torch.int32, device="cuda")
+    bounds = [(s0, min(T, s0 + C)) for s0 in range(0, T, C)]
+    for s0, s1 in bounds:
+        c.build(Xd[s0:s1].contiguous())
+        lsa.index_prefill(c, Yd[s0:s1].contiguous(), s0, p, out=(idx[s0:s1], cnt[s0:s1]))
+    torch.cuda.synchronize()
+    oc = O.build_cache(X, oracle_params(p))
+    if mode == lsa.LSA_FLAT:
+        c2 = gpu_cache(X, p)
+        idx2, cnt2 = lsa.index_prefill(c2, Yd, 0, p)
+        torch.cuda.synchronize()
+        assert torch.equal(idx, idx2) and torch.equal(cnt, cnt2)
+    idx, cnt = idx.cpu().numpy(), cnt.cpu().numpy()
+    for s0, s1 in bounds:
+        trees = dict(tree=O.build_tree(_oracle_prefix(oc, s1 // 512))) if mode == lsa.LSA_TREE else {}
+        rows = np.unique(np.concatenate([np.arange(s0, s1, 97), [s0, s1 - 1]]))
+        rep = compare_lists(idx[rows], cnt[rows], rows, Y[rows], _oracle_prefix(oc, s1 // 512),
+                            mode="tree" if mode == lsa.LSA_TREE else "flat", **trees)
+        say(f"chunk {s0}..{s1}", rep)
+
+
 # ---------------------------------------------------------------- decode
 
 @pytest.mark.parametrize("mode", [lsa.LSA_FLAT, lsa.LSA_TREE])
