@@ -54,6 +54,9 @@ def parse():
                     help="time decode steps (cfg 3: 16 sequences at 1M; cfg 5: one at 10M)")
     ap.add_argument("--splits", type=int, default=0,
                     help="decode attention splits (0: the library's lsa_attention_default_splits)")
+    ap.add_argument("--tree-sweep", action="store_true",
+                    help="last chunk (cfg 4, 5): index time and far-key recall against flat "
+                         "search for tree beam widths and leaf levels")
     ap.add_argument("--whole-context", action="store_true",
                     help="prefill the whole context in chunks of the workload's query count "
                          "(cfg 4, 5): append a chunk of keys, index its queries, attend")
@@ -215,6 +218,90 @@ def bench_decode(args, w, dev):
     print(json.dumps(res), flush=True)
 
 
+def bench_tree_sweep(args, w, dev):
+    """Tree beam search against flat search on the workload's last chunk.  For
+    beam widths 8..64 and leaf levels from the default (the smallest level
+    where beam * 2^level reaches the B buckets to keep) upward -- stopping the
+    beam higher up and ranking every bucket under it flat, the two-stage search
+    -- the chunk's index time (HIP events, best of three) and each query's
+    far-key recall: the share of its exact flat list's far keys (outside the
+    sinks and the window) that the tree list also holds."""
+    import ctypes
+
+    import torch
+
+    import lsa_synth as S
+    import sparse_attention_indexing_amd as lsa
+
+    if w.batch != 1 or w.q_start == 0:
+        raise SystemExit("--tree-sweep needs a last-chunk workload (cfg 4, 5)")
+    X, Y, _ = S.latent_inputs(w)
+    Xd, Yd = torch.from_numpy(X).to(dev), torch.from_numpy(Y).to(dev)
+    del X, Y
+    base = dict(k=w.k, n_sink=w.n_sink, window=w.window, index_dtype=lsa.LSA_BF16)
+    c = lsa.BucketCache(lsa.Params(mode=lsa.LSA_TREE, **base), w.T)
+    c.build(Xd)
+    torch.cuda.synchronize()
+    ws = torch.empty(lsa.index_workspace_bytes(lsa.Params(**base), w.Tq), dtype=torch.uint8,
+                     device=dev)
+
+    def run(p):
+        best, out = None, None
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            out = lsa.index_prefill(c, Yd, w.q_start, p, workspace=ws)
+            e1.record()
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1)
+            best = t if best is None else min(best, t)
+        return best, out
+
+    pos = torch.arange(w.q_start, w.T, device=dev, dtype=torch.int64)[:, None]
+
+    def far_keys(idx):
+        i64 = idx.to(torch.int64)
+        m = (i64 >= w.n_sink) & (i64 <= pos - w.window)   # neither a sink nor a window key
+        rows = torch.arange(w.Tq, device=dev, dtype=torch.int64)[:, None].expand_as(i64)
+        return rows[m], rows[m] * w.T + i64[m], m.sum(dim=1)
+
+    flat_ms, (fidx, _) = run(lsa.Params(mode=lsa.LSA_FLAT, **base))
+    _, fkey, fcount = far_keys(fidx)
+    points = []
+    for beam in (8, 16, 32, 64):
+        p0 = lsa.Params(mode=lsa.LSA_TREE, beam=beam, **base)
+        l0 = 0
+        while beam << l0 < lsa.top_buckets(p0):
+            l0 += 1
+        for leaf in range(l0, l0 + 4):
+            p = lsa.Params(mode=lsa.LSA_TREE, beam=beam, leaf_level=leaf, **base)
+            if lsa.lib().lsa_check_params(ctypes.byref(p.c())) != 0:
+                break
+            ms, (tidx, _) = run(p)
+            trow, tkey, _ = far_keys(tidx)
+            hit = torch.isin(tkey, fkey)
+            hits = torch.bincount(trow[hit], minlength=w.Tq).to(torch.float64)
+            rec = hits / fcount.clamp(min=1).to(torch.float64)
+            rec = rec[fcount > 0]
+            points.append(dict(beam=beam, leaf_level=leaf, scored_under_beam=beam << leaf,
+                               index_ms=round(ms, 4), recall_mean=round(rec.mean().item(), 4),
+                               recall_p10=round(torch.quantile(rec, 0.1).item(), 4),
+                               recall_min=round(rec.min().item(), 4)))
+            log(f"beam {beam:3d} leaf {leaf:2d}: index {ms:7.3f} ms, recall {points[-1]['recall_mean']:.3f}")
+    default = next(q for q in points if q["beam"] == 64)
+    res = {
+        "metric": "tree/flat far-key recall (beam 64, default leaf level)",
+        "value": default["recall_mean"], "unit": "fraction", "n_gpus": 1, "steps": 3, "warmup": 0,
+        "ms_per_step": default["index_ms"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name.replace("_tree", "") + "_tree_sweep", "T": w.T, "Tq": w.Tq,
+                   "k": w.k, "parallelism": "none"},
+        "flat_index_ms": round(flat_ms, 4),
+        "points": points,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def bench_whole_context(args, w, dev):
     """The whole context prefilled in chunks of w.Tq queries, aligned so that the
     last chunk is the workload's measured final chunk (the first one is shorter).
@@ -347,6 +434,8 @@ def main():
         return bench_decode(args, w, dev)
     if args.whole_context:
         return bench_whole_context(args, w, dev)
+    if args.tree_sweep:
+        return bench_tree_sweep(args, w, dev)
     if w.batch != 1:
         raise SystemExit("prefill timing needs a single-sequence workload (cfg 1, 2, 4, 5)")
     t_gen = time.perf_counter()
