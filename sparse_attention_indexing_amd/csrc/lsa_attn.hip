@@ -297,7 +297,11 @@ __global__ __launch_bounds__(64 * kMaxWaves, 3) void k_attn_bf16(AttnArgs a) {
 // swizzled by row (chunk ^ 2 (row & 7)) so that the transposing reads of the
 // PV products hit distinct banks.  The loop runs whole ring cycles: tiles at
 // or past the end, and invalid list entries, load token 0 with zero weight.
-// The row's index list is staged in LDS, kList4 entries at a time.
+// The row's index list is staged in LDS, kList4 entries at a time, each
+// entry checked once there: invalid entries, and the tail of the last tile
+// past the count, are stored as -1, and 16 more -1 entries after the stage
+// serve the padding tiles.  In the loop an entry e < 0 loads token 0 and
+// gets zero weight.
 //
 // Softmax in base 2 with a lazy reference max m per head row: the O and l
 // accumulators are rescaled only when a score exceeds m by more than 2^kLazy
@@ -307,7 +311,7 @@ constexpr int kRing4 = 3;                      // register buffers per wave
 constexpr int kVTile4 = 16 * 256;              // V tile of one KV head in LDS (bytes)
 constexpr int kP4 = 16 * 16 * 2;               // P tile [16 keys][16 heads] bf16, per wave
 constexpr int kList4 = 8192;                   // index-list entries staged at a time
-constexpr int kLds4 = 4 * (kVTile4 + kP4) + kList4 * 4;
+constexpr int kLds4 = 4 * (kVTile4 + kP4) + (kList4 + 16) * 4;
 constexpr float kLazy = 8.f;
 
 typedef short v4s_t __attribute__((ext_vector_type(4)));
@@ -354,7 +358,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16_h4(AttnArgs a) {
   uint16_t* ps = reinterpret_cast<uint16_t*>(vt + kVTile4);
   int32_t* slist = reinterpret_cast<int32_t*>(lds4 + 4 * (kVTile4 + kP4));
   const int r16 = lane & 15, u = lane >> 4;
-  const int64_t Tmax = a.Tmax;
+  // token indices below tlim are valid (unsigned compare rejects e < 0)
+  const uint32_t tlim = a.Tmax < 0x7fffffff ? (uint32_t)a.Tmax : 0x7fffffffu;
 
   // the first batch of list entries is requested before anything else: the
   // tiles' addresses wait on it
@@ -366,15 +371,19 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16_h4(AttnArgs a) {
     const int i = (int)threadIdx.x + 256 * u;
     t0[u] = i < m0 ? lst[i] : 0;
   }
+  // a negative scale is applied as |scale| to -q (flipping bf16 sign bits is
+  // exact), so the threshold test below can compare raw scores
+  const float sl = fabsf(a.scale_log2), inv_sl = 1.f / sl;
   bf16x8 qf[4];
   {
     const bool ok = r16 < a.G;
-    const uint4* qrow = reinterpret_cast<const uint4*>(
+    const uint32_t flip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
+    const u32x4_t* qrow = reinterpret_cast<const u32x4_t*>(
         a.q + (row * a.Hq + (int64_t)kvh * a.G + (ok ? r16 : 0)) * kHeadDim);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      uint4 w = ok ? qrow[4 * j + u] : make_uint4(0, 0, 0, 0);
-      qf[j] = __builtin_bit_cast(bf16x8, w);
+      u32x4_t w = ok ? qrow[4 * j + u] : u32x4_t{0, 0, 0, 0};
+      qf[j] = __builtin_bit_cast(bf16x8, w ^ flip);
     }
   }
   f32x4 o[8];
@@ -382,9 +391,10 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16_h4(AttnArgs a) {
   for (int j = 0; j < 8; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   // m: reference max per head row, uniform over the row's 16 lanes, with a
   // finite floor so that exp2(-inf - m) = 0; lp: this lane's partial sums
-  float m[4], lp[4];
+  // mth: the raw score above which a key moves the reference (m + 2^kLazy)
+  float m[4], lp[4], mth[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) { m[i] = -1e30f; lp[i] = 0.f; }
+  for (int i = 0; i < 4; ++i) { m[i] = -1e30f; lp[i] = 0.f; mth[i] = -__builtin_inff(); }
 
   const int vi = lane >> 4, vc = lane & 15;    // V loads: token 4 vi + j, chunk vc
   // transposing V reads: source lane s of a 16-lane group points at key row
@@ -395,55 +405,64 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16_h4(AttnArgs a) {
 
   u32x4_t kr[kRing4][4], vr[kRing4][4];
   bool kval[kRing4];
-  // list entries [c0 + from, c0 + m) into slist: every load of a batch is
-  // issued before the stores, one memory latency per 3,072 entries
-  auto stage = [&](int c0, int from, int m) {
-    for (int base = from; base < m; base += 256 * kB) {
+  // slot i of a stage holding cn entries: the entry if it is valid, else -1
+  auto put = [&](int i, int32_t e, int cn) {
+    slist[i] = (i < cn && (uint32_t)e < tlim) ? e : -1;
+  };
+  // list entries [c0 + from, c0 + m) into slist, slots up to the next
+  // multiple of 16: every load of a batch is issued before the stores, one
+  // memory latency per 3,072 entries
+  auto stage = [&](int c0, int from, int m, int cn) {
+    const int m16 = (m + 15) & ~15;
+    for (int base = from; base < m16; base += 256 * kB) {
       int32_t t[kB];
 #pragma unroll
       for (int u = 0; u < kB; ++u) {
         const int i = base + (int)threadIdx.x + 256 * u;
-        t[u] = i < m ? lst[c0 + i] : 0;
+        t[u] = i < m ? lst[c0 + i] : -1;
       }
 #pragma unroll
       for (int u = 0; u < kB; ++u) {
         const int i = base + (int)threadIdx.x + 256 * u;
-        if (i < m) slist[i] = t[u];
+        if (i < m16) put(i, t[u], cn);
       }
     }
   };
-  // the first chunk is staged without waiting for the count
+  if (threadIdx.x < 16) slist[kList4 + threadIdx.x] = -1;
+  // the first chunk's loads do not wait for the count (the stores do)
+  {
+    const int cn = n < kList4 ? n : kList4;
+    const int m16 = (m0 + 15) & ~15;
 #pragma unroll
-  for (int u = 0; u < kB; ++u) {
-    const int i = (int)threadIdx.x + 256 * u;
-    if (i < m0) slist[i] = t0[u];
+    for (int u = 0; u < kB; ++u) {
+      const int i = (int)threadIdx.x + 256 * u;
+      if (i < m16) put(i, t0[u], cn);
+    }
+    stage(0, 256 * kB, m0, cn);
   }
-  stage(0, 256 * kB, m0);
   __syncthreads();
   for (int c0 = 0; c0 < n; c0 += kList4) {
     const int cn = (n - c0) < kList4 ? (n - c0) : kList4;
     if (c0 > 0) {
       __syncthreads();                         // every wave is done with the previous chunk
-      stage(c0, 0, cn);
+      stage(c0, 0, cn, cn);
       __syncthreads();
     }
     const int nt = (cn + 15) >> 4;
 
     // tile T into one ring buffer; kv: this lane's key (column r16) is real
     auto issue = [&](int T, u32x4_t (&k)[4], u32x4_t (&v)[4], bool& kv) {
-      const int tb = T << 4;
-      const int tr = T < nt ? tb : 0;          // padding tiles read entry 0, rejected by tb
+      const int tr = T < nt ? T << 4 : kList4; // padding tiles read the -1 entries
       const int pk = slist[tr + r16];
       const int4 p4 = *reinterpret_cast<const int4*>(slist + tr + 4 * vi);
-      kv = tb + r16 < cn && pk >= 0 && pk < Tmax;
-      const char* kp = kb + (int64_t)(kv ? pk : 0) * 1024 + 16 * u;
+      kv = pk >= 0;
+      const char* kp = kb + (uint64_t)(uint32_t)(pk > 0 ? pk : 0) * 1024 + 16 * u;
 #pragma unroll
       for (int j = 0; j < 4; ++j) k[j] = *reinterpret_cast<const u32x4_t*>(kp + 64 * j);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int p = j == 0 ? p4.x : (j == 1 ? p4.y : (j == 2 ? p4.z : p4.w));
-        const bool ok = tb + 4 * vi + j < cn && p >= 0 && p < Tmax;
-        v[j] = *reinterpret_cast<const u32x4_t*>(vb + (int64_t)(ok ? p : 0) * 1024 + 16 * vc);
+        v[j] = *reinterpret_cast<const u32x4_t*>(vb + (uint64_t)(uint32_t)(p > 0 ? p : 0) * 1024 + 16 * vc);
       }
     };
     auto compute = [&](const u32x4_t (&k)[4], const u32x4_t (&v)[4], bool kv) {
@@ -457,27 +476,26 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16_h4(AttnArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[j], __builtin_bit_cast(bf16x8, k[j]), sacc, 0, 0, 0);
-      float x[4], pv[4];
+      float pv[4];
       bool grow = false;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[i] = kv ? sacc[i] * a.scale_log2 : -__builtin_inff();
-        grow |= x[i] > m[i] + kLazy;
-      }
-      if (__ballot(grow)) {
+      for (int i = 0; i < 4; ++i) grow |= sacc[i] > mth[i];
+      if (__ballot(grow && kv)) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float mn = fmaxf(m[i], row16_max(x[i]));
+          const float x = kv ? sacc[i] * sl : -__builtin_inff();
+          const float mn = fmaxf(m[i], row16_max(x));
           const float alpha = __builtin_amdgcn_exp2f(m[i] - mn);
           lp[i] *= alpha;
 #pragma unroll
           for (int j = 0; j < 8; ++j) o[j][i] *= alpha;
           m[i] = mn;
+          mth[i] = (mn + kLazy) * inv_sl;
         }
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        pv[i] = __builtin_amdgcn_exp2f(x[i] - m[i]);
+        pv[i] = kv ? __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], sl, -m[i])) : 0.f;
         lp[i] += pv[i];
       }
       uint2 w2;

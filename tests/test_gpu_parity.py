@@ -308,6 +308,47 @@ def test_attention_lists_longer_than_a_staged_chunk(L):
     assert err <= 2e-2
 
 
+@pytest.mark.parametrize("scale,splits", [(None, 1), (-0.07, 1), (0.0, 1), (-0.07, 5)])
+def test_attention_invalid_entries_ragged_counts_and_scale(scale, splits):
+    """Entries outside [0, Tmax) inside a row's count are ignored, counts that
+    are not a multiple of the 16-key tile (and 0) end the row, and the scale
+    may be negative or zero; the reference attends over the valid entries."""
+    say(f"case: attention bf16 invalid entries scale={scale} splits={splits}")
+    w = S.WORKLOADS[2]
+    T = 5000
+    rows = np.array([T - 1, 4000, 3333, 1000, 17, 2500])
+    q, k, v, qb, kb, vb = _qkv_host(w, T, rows)
+    rng = np.random.default_rng(11)
+    idx, cnt = _random_lists(rng, rows, 700)
+    bad = np.array([-1, -7, T, T + 5, 2**31 - 1, -2**31], np.int32)
+    for i in range(len(rows)):
+        nb = min(24, int(cnt[i]) // 3)
+        at = rng.choice(int(cnt[i]), size=nb, replace=False)
+        idx[i, at] = rng.choice(bad, size=nb)
+    cnt[1] = 693
+    cnt[2] = 1
+    cnt[4] = 0
+    out = lsa.sparse_attention(bf16_tensor(qb).cuda().view(len(rows), w.Hq, w.D),
+                               bf16_tensor(kb).cuda().view(T, w.Hkv, w.D),
+                               bf16_tensor(vb).cuda().view(T, w.Hkv, w.D),
+                               torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda(),
+                               scale=scale, splits=splits)
+    torch.cuda.synchronize()
+    out = out.float().cpu().numpy()
+    assert not out[4].any()
+    err = 0.0
+    for i in range(len(rows)):
+        if cnt[i] == 0:
+            continue
+        sel = idx[i, :cnt[i]]
+        sel = sel[(sel >= 0) & (sel < T)]
+        ref = (O.attention_query(q[i], k, v, sel, len(sel), scale=scale) if len(sel)
+               else np.zeros_like(out[i]))
+        err = max(err, np.abs(out[i] - ref).max())
+    say("attention bf16 max abs err", err)
+    assert err <= 2e-2
+
+
 def test_attention_batched_rows_across_launches():
     """Two sequences of 1,500 query rows each (3,000 rows: two launches of up to
     2,048, the boundary inside the second sequence), each with its own K/V."""
