@@ -107,13 +107,24 @@ def cpu_baseline(w, X, Y, budget_s: float):
                        f"{w.Tq} queries; one thread")
 
 
+def attention_kernel_name(lsa, w, B: int, Tmax: int) -> str:
+    """The attention kernel (template instance) that lsa_sparse_attention runs."""
+    if w.dtype != "bf16":
+        return "k_attn_f32"
+    if w.Hkv != 4:
+        return "k_attn_bf16"
+    nw = 1 if lsa.attention_head_major(B, Tmax, w.Hkv, w.D, lsa.LSA_BF16) else 4
+    return f"k_attn_bf16_h4<{nw}>"
+
+
 def measured_traffic(kernel: str, workload: str, rows_per_launch: int):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or None
-    when there is none, the kernel source changed since it was taken, or its
-    launches covered another number of query rows."""
+    when there is none, it was taken on another kernel, the kernel source
+    changed since, or its launches covered another number of query rows."""
     import hashlib
     root = os.path.dirname(os.path.abspath(__file__))
-    path = os.path.join(root, "profiles", f"{kernel}.{workload}.traffic.md")
+    stem = kernel.split("<")[0]
+    path = os.path.join(root, "profiles", f"{stem}.{workload}.traffic.md")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -122,6 +133,8 @@ def measured_traffic(kernel: str, workload: str, rows_per_launch: int):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
     try:
+        if fields["kernel"] != kernel:
+            return None
         src = open(os.path.join(root, fields["kernel_source"]), "rb").read()
         if hashlib.sha256(src).hexdigest()[:16] != fields["kernel_source_sha256_16"]:
             return None
@@ -408,7 +421,8 @@ def bench_whole_context(args, w, dev):
                       "attention": round(float(t_attn), 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "k_attn_bf16_h4", "launches_per_step": launches,
+                     "kernel": attention_kernel_name(lsa, w, 1, w.T),
+                     "launches_per_step": launches,
                      "algorithmic_bytes": round(attn_bytes / launches),
                      "kernel_ms": round(float(t_attn) / launches, 4)},
         "wall_s": round(wall, 2),
@@ -540,7 +554,7 @@ def main():
     # algorithmic FLOPs of flat scoring: 2 * 64 per eligible (query, bucket) pair
     pos = np.arange(w.q_start, w.T, dtype=np.int64)
     pairs = int((64 * (pos // 512)).sum())
-    kname = ("k_attn_bf16_h4" if w.Hkv == 4 else "k_attn_bf16") if w.dtype == "bf16" else "k_attn_f32"
+    kname = attention_kernel_name(lsa, w, 1, w.T)
     # the bf16 attention runs as back-to-back launches of up to launch_rows query
     # rows; bytes and time are reported per launch, averaged over the step's launches
     launch_rows = min(lsa.attention_launch_rows(), w.Tq) if w.dtype == "bf16" else w.Tq

@@ -208,6 +208,15 @@ int64_t lsa_attention_workspace_bytes(int32_t B, int64_t Tq, int32_t Hq, int32_t
  * in flight stay neighbours (their lists share keys in the caches). */
 int64_t lsa_attention_launch_rows(void);
 
+/* 1 when lsa_sparse_attention with these shapes runs one workgroup per
+ * (query row, KV head), grouping each KV head's workgroups on their own XCDs
+ * (bf16, Hkv = 4, D = 128, and K and V caches of at most 256 MiB each:
+ * B * Tmax * Hkv * D * 2 bytes); 0 when each workgroup takes a whole row
+ * (larger caches, where reading each listed token's rows of all heads
+ * together pays more than the per-XCD cache reuse), and for other dtypes and
+ * shapes.  Both layouts compute the same results. */
+int32_t lsa_attention_head_major(int32_t B, int64_t Tmax, int32_t Hkv, int32_t D, int32_t dtype);
+
 /* A split count for lsa_sparse_attention: the largest power of two (<= 256)
  * that keeps at least 32 listed keys per split and rows * splits <= 512
  * workgroups (two per compute unit), so that few query rows (decode) still

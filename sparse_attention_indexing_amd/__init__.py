@@ -98,6 +98,7 @@ def lib():
         "lsa_sparse_attention": (ctypes.c_int, [vp, vp, vp, i32, i64, i64, i32, i32, i32, vp, vp,
                                                 i32, ctypes.c_float, i32, i32, vp, vp, i64, vp]),
         "lsa_attention_launch_rows": (i64, []),
+        "lsa_attention_head_major": (i32, [i32, i64, i32, i32, i32]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -284,7 +285,13 @@ def attention_launch_rows() -> int:
     return int(lib().lsa_attention_launch_rows())
 
 
+def attention_head_major(B: int, Tmax: int, Hkv: int, D: int, dtype: int) -> bool:
+    """lsa_attention_head_major: whether attention over these shapes runs one
+    workgroup per (query row, KV head)."""
+    return bool(lib().lsa_attention_head_major(B, Tmax, Hkv, D, dtype))
+
+
 __all__ = ["Params", "BucketCache", "index_prefill", "index_decode", "sparse_attention",
-           "attention_launch_rows",
+           "attention_launch_rows", "attention_head_major",
            "list_len", "top_buckets", "index_workspace_bytes", "lib", "LsaError",
            "LSA_F32", "LSA_BF16", "LSA_FLAT", "LSA_TREE"]

@@ -559,6 +559,10 @@ int64_t lsa_attention_workspace_bytes(int32_t B, int64_t Tq, int32_t Hq, int32_t
 
 int64_t lsa_attention_launch_rows(void) { return attention_launch_rows(); }
 
+int32_t lsa_attention_head_major(int32_t B, int64_t Tmax, int32_t Hkv, int32_t D, int32_t dtype) {
+  return attention_head_major(B, Tmax, Hkv, D, dtype) ? 1 : 0;
+}
+
 int32_t lsa_attention_default_splits(int64_t rows, int32_t L_max) {
   if (rows <= 0 || L_max <= 0) return 1;
   int32_t splits = 1;

@@ -286,18 +286,26 @@ __global__ __launch_bounds__(64 * kMaxWaves, 3) void k_attn_bf16(AttnArgs a) {
 
 // ---------------------------------------------------------------------------
 // Four-KV-head path (Hkv = 4, the shape of the 128K .. 10M workloads),
-// register staged.  Wave w owns KV head w and streams that head's K and V
-// rows (256 B each per token) on its own: no workgroup barrier inside the
-// loop.  Tiles of 16 tokens are loaded with plain 16-byte loads into a ring
+// register staged.  Every wave owns one (row, KV head) and streams that
+// head's K and V rows (256 B each per token) on its own: no barrier inside
+// the loop.  Two workgroup shapes (NW waves per workgroup):
+//   NW = 4: one row per workgroup, wave w takes KV head w.  The four waves
+//     read each listed token's whole 1 KiB K and V rows together, the better
+//     pattern once K/V are much larger than the caches (1M, 10M tokens).
+//   NW = 1: one (row, head) per workgroup, and the XCD that a workgroup runs
+//     on (blockIdx.x mod 8) fixes its head: XCDs h and h + 4 serve KV head h,
+//     for the first and second half of the launch's rows.  Each XCD's L2
+//     then holds one head's rows (a quarter of the bytes per token) for four
+//     times as many neighbouring queries, which pays when K/V fit the
+//     Infinity Cache (the 128K workload: 256 MiB).  Tiles of 16 tokens are loaded with plain 16-byte loads into a ring
 // of kRing4 register buffers, kRing4 - 1 tiles ahead of the one being
-// computed, so each wave keeps 16 KiB in flight and two workgroups share a
-// CU.  K goes straight into the B operand of 16x16x32 MFMAs: for product j,
+// computed, so each wave keeps 16 KiB in flight and 8 waves share a CU.  K goes straight into the B operand of 16x16x32 MFMAs: for product j,
 // lane (n, u) holds bytes [16 (4j + u), +16) of key n, and Q uses the same
 // dim order.  V is written to a per-wave LDS tile, its 16-byte chunks XOR
 // swizzled by row (chunk ^ 2 (row & 7)) so that the transposing reads of the
 // PV products hit distinct banks.  The loop runs whole ring cycles: tiles at
 // or past the end, and invalid list entries, load token 0 with zero weight.
-// The row's index list is staged in LDS, kList4 entries at a time, each
+// The row's index list is staged in LDS, kList4<NW> entries at a time, each
 // entry checked once there: invalid entries, and the tail of the last tile
 // past the count, are stored as -1, and 16 more -1 entries after the stage
 // serve the padding tiles.  In the loop an entry e < 0 loads token 0 and
@@ -310,8 +318,15 @@ __global__ __launch_bounds__(64 * kMaxWaves, 3) void k_attn_bf16(AttnArgs a) {
 constexpr int kRing4 = 3;                      // register buffers per wave
 constexpr int kVTile4 = 16 * 256;              // V tile of one KV head in LDS (bytes)
 constexpr int kP4 = 16 * 16 * 2;               // P tile [16 keys][16 heads] bf16, per wave
-constexpr int kList4 = 8192;                   // index-list entries staged at a time
-constexpr int kLds4 = 4 * (kVTile4 + kP4) + (kList4 + 16) * 4;
+// index-list entries staged at a time, and per thread in one batch of loads
+template <int NW> constexpr int kList4 = NW == 4 ? 8192 : 3072;
+template <int NW> constexpr int kBatch4 = NW == 4 ? 12 : 48;
+template <int NW> constexpr int kLds4 = NW * (kVTile4 + kP4) + (kList4<NW> + 16) * 4;
+// K and V caches of at most this many bytes each (B * Tmax * Hkv * D * 2)
+// take the per-head workgroups.  Measured: 14% less attention time at 128 MiB
+// (128K tokens), 3-12% more at 1 GiB and beyond (1M and 10M tokens, 16 x 1M
+// decode); sizes in between were not measured.
+constexpr int64_t kHeadMajorMaxKvBytes = 256ll << 20;
 constexpr float kLazy = 8.f;
 
 typedef short v4s_t __attribute__((ext_vector_type(4)));
@@ -324,19 +339,44 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
-__global__ __launch_bounds__(256, 2) void k_attn_bf16_h4(AttnArgs a) {
+// grid.x of a launch of nrows rows
+template <int NW>
+int64_t attn_h4_grid(int64_t nrows) {
+  if (NW == 4) return nrows >= 8 ? (nrows + 7) / 8 * 8 : nrows;
+  return nrows >= 8 ? 8 * ((nrows + 1) / 2) : 4 * nrows;
+}
+
+template <int NW>
+__global__ __launch_bounds__(64 * NW, 2) void k_attn_bf16_h4(AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds4[];
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  constexpr int NT = 64 * NW, kList = kList4<NW>, kB = kBatch4<NW>;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = NW == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid >> 6);
   // with 8+ rows, workgroups of consecutive rows (which share many keys) go
-  // to the same XCD; with fewer rows grid.x = rows and the splits of a row
-  // spread over the XCDs
-  int64_t row = blockIdx.x;
-  if (a.nrows >= 8) {
-    const int64_t per_xcd = (a.nrows + 7) / 8;
-    row = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  // to the same XCD; with fewer rows the splits of a row spread over the XCDs
+  int64_t row;
+  int kvh;
+  if constexpr (NW == 4) {
+    row = blockIdx.x;
+    kvh = wave;
+    if (a.nrows >= 8) {
+      const int64_t per_xcd = (a.nrows + 7) / 8;
+      row = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    }
+  } else if (a.nrows >= 8) {
+    const int x = blockIdx.x & 7;
+    kvh = x & 3;
+    row = (int64_t)(x >> 2) * ((a.nrows + 1) / 2) + (blockIdx.x >> 3);
+  } else {
+    row = blockIdx.x >> 2;
+    kvh = blockIdx.x & 3;
   }
+  // every wave of the workgroup has the same row, so the return is uniform
   if (row >= a.nrows) return;
+  // list stages are written by one wave (NW = 1) or by the whole workgroup
+  auto stage_sync = [] {
+    if constexpr (NW == 1) wave_fence(); else __syncthreads();
+  };
   row += a.row0;
   const int split = blockIdx.y;
   const int64_t b = row / a.Tq;
@@ -351,24 +391,22 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16_h4(AttnArgs a) {
   const int k1 = kend < cnt ? kend : cnt;
   const int n = k1 > k0 ? k1 - k0 : 0;
   const int32_t* lst = a.idx + row * (int64_t)a.L + k0;
-  const int kvh = wave;
   const char* kb = reinterpret_cast<const char*>(a.k + b * a.Tmax * 4 * kHeadDim) + kvh * 256;
   const char* vb = reinterpret_cast<const char*>(a.v + b * a.Tmax * 4 * kHeadDim) + kvh * 256;
   char* vt = lds4 + wave * (kVTile4 + kP4);
   uint16_t* ps = reinterpret_cast<uint16_t*>(vt + kVTile4);
-  int32_t* slist = reinterpret_cast<int32_t*>(lds4 + 4 * (kVTile4 + kP4));
+  int32_t* slist = reinterpret_cast<int32_t*>(lds4 + NW * (kVTile4 + kP4));
   const int r16 = lane & 15, u = lane >> 4;
   // token indices below tlim are valid (unsigned compare rejects e < 0)
   const uint32_t tlim = a.Tmax < 0x7fffffff ? (uint32_t)a.Tmax : 0x7fffffffu;
 
   // the first batch of list entries is requested before anything else: the
   // tiles' addresses wait on it
-  constexpr int kB = 12;
-  const int m0 = navail < kList4 ? navail : kList4;    // entries of the first chunk
+  const int m0 = navail < kList ? navail : kList;      // entries of the first chunk
   int32_t t0[kB];
 #pragma unroll
   for (int u = 0; u < kB; ++u) {
-    const int i = (int)threadIdx.x + 256 * u;
+    const int i = tid + NT * u;
     t0[u] = i < m0 ? lst[i] : 0;
   }
   // a negative scale is applied as |scale| to -q (flipping bf16 sign bits is
@@ -411,48 +449,48 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16_h4(AttnArgs a) {
   };
   // list entries [c0 + from, c0 + m) into slist, slots up to the next
   // multiple of 16: every load of a batch is issued before the stores, one
-  // memory latency per 3,072 entries
+  // memory latency per NT * kB entries
   auto stage = [&](int c0, int from, int m, int cn) {
     const int m16 = (m + 15) & ~15;
-    for (int base = from; base < m16; base += 256 * kB) {
+    for (int base = from; base < m16; base += NT * kB) {
       int32_t t[kB];
 #pragma unroll
       for (int u = 0; u < kB; ++u) {
-        const int i = base + (int)threadIdx.x + 256 * u;
+        const int i = base + tid + NT * u;
         t[u] = i < m ? lst[c0 + i] : -1;
       }
 #pragma unroll
       for (int u = 0; u < kB; ++u) {
-        const int i = base + (int)threadIdx.x + 256 * u;
+        const int i = base + tid + NT * u;
         if (i < m16) put(i, t[u], cn);
       }
     }
   };
-  if (threadIdx.x < 16) slist[kList4 + threadIdx.x] = -1;
+  if (tid < 16) slist[kList + tid] = -1;
   // the first chunk's loads do not wait for the count (the stores do)
   {
-    const int cn = n < kList4 ? n : kList4;
+    const int cn = n < kList ? n : kList;
     const int m16 = (m0 + 15) & ~15;
 #pragma unroll
     for (int u = 0; u < kB; ++u) {
-      const int i = (int)threadIdx.x + 256 * u;
+      const int i = tid + NT * u;
       if (i < m16) put(i, t0[u], cn);
     }
-    stage(0, 256 * kB, m0, cn);
+    stage(0, NT * kB, m0, cn);
   }
-  __syncthreads();
-  for (int c0 = 0; c0 < n; c0 += kList4) {
-    const int cn = (n - c0) < kList4 ? (n - c0) : kList4;
+  stage_sync();
+  for (int c0 = 0; c0 < n; c0 += kList) {
+    const int cn = (n - c0) < kList ? (n - c0) : kList;
     if (c0 > 0) {
-      __syncthreads();                         // every wave is done with the previous chunk
+      stage_sync();                            // every wave is done with the previous chunk
       stage(c0, 0, cn, cn);
-      __syncthreads();
+      stage_sync();
     }
     const int nt = (cn + 15) >> 4;
 
     // tile T into one ring buffer; kv: this lane's key (column r16) is real
     auto issue = [&](int T, u32x4_t (&k)[4], u32x4_t (&v)[4], bool& kv) {
-      const int tr = T < nt ? T << 4 : kList4; // padding tiles read the -1 entries
+      const int tr = T < nt ? T << 4 : kList;  // padding tiles read the -1 entries
       const int pk = slist[tr + r16];
       const int4 p4 = *reinterpret_cast<const int4*>(slist + tr + 4 * vi);
       kv = pk >= 0;
@@ -729,6 +767,13 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
 
 int64_t attention_launch_rows() { return kRowsPerLaunch; }
 
+bool attention_head_major(int32_t B, int64_t Tmax, int32_t Hkv, int32_t D, int dtype) {
+  if (dtype != LSA_BF16 || Hkv != 4 || D != kHeadDim || B < 0 || Tmax < 0) return false;
+  if (B == 0 || Tmax == 0) return true;
+  const int64_t per_token = (int64_t)Hkv * D * 2;   // bytes of one token's row
+  return Tmax <= kHeadMajorMaxKvBytes / per_token / B;
+}
+
 hipError_t launch_attention(const void* q, const void* k, const void* v, int32_t B, int64_t Tq,
                             int64_t Tmax, int32_t Hq, int32_t Hkv, const int32_t* idx,
                             const int32_t* count, int32_t L_max, float scale, int dtype,
@@ -745,17 +790,21 @@ hipError_t launch_attention(const void* q, const void* k, const void* v, int32_t
     if (Hkv == 4) {
       static bool attr3 = false;
       if (!attr3) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_attn_bf16_h4),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, kLds4);
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_attn_bf16_h4<4>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, kLds4<4>);
         (void)hipGetLastError();
         attr3 = true;
       }
+      const bool head_major = attention_head_major(B, Tmax, Hkv, kHeadDim, dtype);
       for (int64_t r0 = 0; r0 < rows; r0 += kRowsPerLaunch) {
         a.row0 = r0;
         a.nrows = (rows - r0) < kRowsPerLaunch ? (rows - r0) : kRowsPerLaunch;
-        const int64_t grid = a.nrows >= 8 ? (a.nrows + 7) / 8 * 8 : a.nrows;
-        hipLaunchKernelGGL(k_attn_bf16_h4, dim3((unsigned)grid, (unsigned)splits), dim3(256),
-                           (size_t)kLds4, s, a);
+        if (head_major)
+          hipLaunchKernelGGL(k_attn_bf16_h4<1>, dim3((unsigned)attn_h4_grid<1>(a.nrows),
+                             (unsigned)splits), dim3(64), (size_t)kLds4<1>, s, a);
+        else
+          hipLaunchKernelGGL(k_attn_bf16_h4<4>, dim3((unsigned)attn_h4_grid<4>(a.nrows),
+                             (unsigned)splits), dim3(256), (size_t)kLds4<4>, s, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
       }

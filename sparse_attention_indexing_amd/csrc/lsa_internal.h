@@ -165,6 +165,7 @@ hipError_t launch_select_expand(const IndexCtx& ctx, const IndexWs& ws, int32_t*
 
 // rows per bf16 attention launch (a call over more rows issues several)
 int64_t attention_launch_rows();
+bool attention_head_major(int32_t B, int64_t Tmax, int32_t Hkv, int32_t D, int dtype);
 hipError_t launch_attention(const void* q, const void* k, const void* v, int32_t B, int64_t Tq,
                             int64_t Tmax, int32_t Hq, int32_t Hkv, const int32_t* idx,
                             const int32_t* count, int32_t L_max, float scale, int dtype,

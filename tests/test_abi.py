@@ -122,6 +122,13 @@ def test_attention_host_errors():
     empty_cache[5] = 0                     # Tmax = 0 with rows to attend
     assert L.lsa_sparse_attention(*empty_cache) == -1
     assert lsa.attention_launch_rows() == 2048
+    # per-(row, KV head) workgroups for bf16, 4 KV heads, caches of <= 256 MiB each
+    hm = lambda B, T, Hkv=4, D=128, dt=lsa.LSA_BF16: lsa.attention_head_major(B, T, Hkv, D, dt)
+    assert hm(1, 131072) and hm(1, 262144) and not hm(1, 262145)
+    assert hm(2, 131072) and not hm(2, 131073) and hm(0, 10**9) and hm(7, 0)
+    assert not hm(1, 1 << 20) and not hm(16, 1 << 20) and not hm(1, 10**7)
+    assert not hm(1, 4096, dt=lsa.LSA_F32) and not hm(1, 4096, Hkv=8) and not hm(1, 4096, D=64)
+    assert not hm(1 << 30, 1 << 32) and not hm(-1, 4) and not hm(1, -4)
     assert L.lsa_attention_workspace_bytes(1, 16, 32, 128, 1) == 0
     assert L.lsa_attention_workspace_bytes(1, 16, 32, 128, 4) == 16 * 4 * 32 * 130 * 4
     assert L.lsa_status_string(-3) == b"workspace too small"

@@ -237,8 +237,9 @@ def test_attention_bf16_on_oracle_lists(splits, few):
 def test_attention_across_launches():
     """More rows than one bf16 attention launch takes (5,000 rows: three
     launches of up to 2,048): rows on both sides of each launch boundary match
-    a launch of just those rows bit for bit, and sampled rows match the
-    oracle's lists and attention."""
+    a launch of just those rows bit for bit, in both workgroup layouts (one
+    per (row, KV head) and one per row), the two layouts agree bit for bit,
+    and sampled rows match the oracle's lists and attention."""
     say("case: attention over 5,000 rows in several launches")
     w = S.WORKLOADS[2]
     T, Tq = 16384, 5000
@@ -248,18 +249,23 @@ def test_attention_across_launches():
     c = gpu_cache(X, p)
     q, k, v, qb, kb, vb = _qkv_host(w, T, np.arange(q0, T))
     Q = bf16_tensor(qb).cuda().view(Tq, w.Hq, w.D)
-    K = bf16_tensor(kb).cuda().view(T, w.Hkv, w.D)
-    V = bf16_tensor(vb).cuda().view(T, w.Hkv, w.D)
     idx, cnt = lsa.index_prefill(c, torch.from_numpy(Y).cuda(), q0, p)
-    out = lsa.sparse_attention(Q, K, V, idx, cnt)
     n = lsa.attention_launch_rows()
     assert Tq > 2 * n
     parts = [(n - 5, n + 5), (2 * n - 3, 2 * n + 9), (Tq - 7, Tq)]
-    sub = [lsa.sparse_attention(Q[a:b].contiguous(), K, V, idx[a:b].contiguous(),
-                                cnt[a:b].contiguous()) for a, b in parts]
-    torch.cuda.synchronize()
-    for (a, b), o in zip(parts, sub):
-        assert torch.equal(out[a:b], o), (a, b)
+    outs = []
+    for row_layout in (False, True):
+        K, V = _kv_dev(kb, 0, T, w, row_layout), _kv_dev(vb, 0, T, w, row_layout)
+        out = lsa.sparse_attention(Q, K, V, idx, cnt)
+        sub = [lsa.sparse_attention(Q[a:b].contiguous(), K, V, idx[a:b].contiguous(),
+                                    cnt[a:b].contiguous()) for a, b in parts]
+        torch.cuda.synchronize()
+        for (a, b), o in zip(parts, sub):
+            assert torch.equal(out[a:b], o), (row_layout, a, b)
+        outs.append(out)
+        del K, V
+    assert torch.equal(outs[0], outs[1])
+    out = outs[0]
     oc = O.build_cache(X, oracle_params(p))
     idx, cnt, out = idx.cpu().numpy(), cnt.cpu().numpy(), out.float().cpu().numpy()
     err, checked = 0.0, 0
@@ -274,6 +280,23 @@ def test_attention_across_launches():
     assert checked >= 4 and err <= 2e-2
 
 
+def _kv_dev(bits, B, T, w, row_layout):
+    """K or V on the device as [B, Tmax, Hkv, D] bf16 (B = 0: [Tmax, Hkv, D]).
+    With row_layout the cache gets unused zero rows up to a size that makes
+    the attention take one workgroup per query row instead of per (row, KV
+    head); only the first T rows are ever listed."""
+    nb = max(B, 1)
+    Tmax = T
+    if row_layout:
+        Tmax = (256 << 20) // (nb * w.Hkv * w.D * 2) + 1
+        assert not lsa.attention_head_major(nb, Tmax, w.Hkv, w.D, lsa.LSA_BF16)
+    else:
+        assert lsa.attention_head_major(nb, Tmax, w.Hkv, w.D, lsa.LSA_BF16)
+    t = torch.zeros((nb, Tmax, w.Hkv, w.D), dtype=torch.bfloat16, device="cuda")
+    t[:, :T] = bf16_tensor(bits).cuda().view(nb, T, w.Hkv, w.D)
+    return t if B else t[0]
+
+
 def _random_lists(rng, positions, L, short=()):
     """Sorted distinct key positions <= each query position, L per row (fewer
     for the rows in `short`), -1 padded."""
@@ -286,19 +309,20 @@ def _random_lists(rng, positions, L, short=()):
     return idx, cnt
 
 
-@pytest.mark.parametrize("L", [8192, 8193, 9000])
-def test_attention_lists_longer_than_a_staged_chunk(L):
-    """Lists longer than the 8,192 entries that the four-KV-head bf16 kernel
-    stages in LDS at a time (a second chunk), one row shorter than L."""
-    say(f"case: attention bf16 with lists of {L} keys")
+@pytest.mark.parametrize("L,row_layout", [(3072, False), (3073, False), (7000, False),
+                                          (8192, True), (8193, True), (9000, True)])
+def test_attention_lists_longer_than_a_staged_chunk(L, row_layout):
+    """Lists longer than the entries that the four-KV-head bf16 kernel stages
+    in LDS at a time (3,072 with a workgroup per (row, KV head), 8,192 with a
+    workgroup per row): a second or third chunk, one row shorter than L."""
+    say(f"case: attention bf16 with lists of {L} keys row_layout={row_layout}")
     w = S.WORKLOADS[2]
     T = 20000
     rows = np.array([T - 1, 15000, 12345])
     q, k, v, qb, kb, vb = _qkv_host(w, T, rows)
     idx, cnt = _random_lists(np.random.default_rng(L), rows, L, short=(2,))
     out = lsa.sparse_attention(bf16_tensor(qb).cuda().view(len(rows), w.Hq, w.D),
-                               bf16_tensor(kb).cuda().view(T, w.Hkv, w.D),
-                               bf16_tensor(vb).cuda().view(T, w.Hkv, w.D),
+                               _kv_dev(kb, 0, T, w, row_layout), _kv_dev(vb, 0, T, w, row_layout),
                                torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda())
     torch.cuda.synchronize()
     out = out.float().cpu().numpy()
@@ -308,19 +332,24 @@ def test_attention_lists_longer_than_a_staged_chunk(L):
     assert err <= 2e-2
 
 
-@pytest.mark.parametrize("scale,splits", [(None, 1), (-0.07, 1), (0.0, 1), (-0.07, 5)])
-def test_attention_invalid_entries_ragged_counts_and_scale(scale, splits):
+@pytest.mark.parametrize("scale,splits,row_layout", [
+    (None, 1, False), (-0.07, 1, False), (0.0, 1, False), (-0.07, 5, False),
+    (None, 1, True), (-0.07, 1, True), (0.0, 1, True), (-0.07, 5, True)])
+def test_attention_invalid_entries_ragged_counts_and_scale(scale, splits, row_layout):
     """Entries outside [0, Tmax) inside a row's count are ignored, counts that
     are not a multiple of the 16-key tile (and 0) end the row, and the scale
     may be negative or zero; the reference attends over the valid entries."""
-    say(f"case: attention bf16 invalid entries scale={scale} splits={splits}")
+    say(f"case: attention bf16 invalid entries scale={scale} splits={splits} "
+        f"row_layout={row_layout}")
     w = S.WORKLOADS[2]
     T = 5000
     rows = np.array([T - 1, 4000, 3333, 1000, 17, 2500])
     q, k, v, qb, kb, vb = _qkv_host(w, T, rows)
     rng = np.random.default_rng(11)
     idx, cnt = _random_lists(rng, rows, 700)
-    bad = np.array([-1, -7, T, T + 5, 2**31 - 1, -2**31], np.int32)
+    kd, vd = _kv_dev(kb, 0, T, w, row_layout), _kv_dev(vb, 0, T, w, row_layout)
+    Tmax = kd.shape[0]
+    bad = np.array([-1, -7, Tmax, Tmax + 5, 2**31 - 1, -2**31], np.int32)
     for i in range(len(rows)):
         nb = min(24, int(cnt[i]) // 3)
         at = rng.choice(int(cnt[i]), size=nb, replace=False)
@@ -328,9 +357,7 @@ def test_attention_invalid_entries_ragged_counts_and_scale(scale, splits):
     cnt[1] = 693
     cnt[2] = 1
     cnt[4] = 0
-    out = lsa.sparse_attention(bf16_tensor(qb).cuda().view(len(rows), w.Hq, w.D),
-                               bf16_tensor(kb).cuda().view(T, w.Hkv, w.D),
-                               bf16_tensor(vb).cuda().view(T, w.Hkv, w.D),
+    out = lsa.sparse_attention(bf16_tensor(qb).cuda().view(len(rows), w.Hq, w.D), kd, vd,
                                torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda(),
                                scale=scale, splits=splits)
     torch.cuda.synchronize()
@@ -349,10 +376,11 @@ def test_attention_invalid_entries_ragged_counts_and_scale(scale, splits):
     assert err <= 2e-2
 
 
-def test_attention_batched_rows_across_launches():
+@pytest.mark.parametrize("row_layout", [False, True])
+def test_attention_batched_rows_across_launches(row_layout):
     """Two sequences of 1,500 query rows each (3,000 rows: two launches of up to
     2,048, the boundary inside the second sequence), each with its own K/V."""
-    say("case: attention bf16, B = 2 x 1,500 rows")
+    say(f"case: attention bf16, B = 2 x 1,500 rows row_layout={row_layout}")
     w = S.WORKLOADS[2]
     B, T, Tq, L = 2, 4096, 1500, 600
     pos = np.arange(T - Tq, T)
@@ -369,9 +397,10 @@ def test_attention_batched_rows_across_launches():
     idx = np.stack([x[0] for x in lists])
     cnt = np.stack([x[1] for x in lists])
     dev = lambda bits, shape: bf16_tensor(np.stack(bits)).cuda().view(*shape)
-    out = lsa.sparse_attention(dev(qbs, (B, Tq, w.Hq, w.D)), dev(kbs, (B, T, w.Hkv, w.D)),
-                               dev(vbs, (B, T, w.Hkv, w.D)), torch.from_numpy(idx).cuda(),
-                               torch.from_numpy(cnt).cuda())
+    out = lsa.sparse_attention(dev(qbs, (B, Tq, w.Hq, w.D)),
+                               _kv_dev(np.stack(kbs), B, T, w, row_layout),
+                               _kv_dev(np.stack(vbs), B, T, w, row_layout),
+                               torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda())
     torch.cuda.synchronize()
     out = out.float().cpu().numpy()
     n = lsa.attention_launch_rows()

@@ -51,6 +51,8 @@ def test_prefill_128k_full_size():
     Q = device_normal(w, "q", (w.Tq, w.Hq, w.D))
     K = device_normal(w, "k", (w.T, w.Hkv, w.D))
     V = device_normal(w, "v", (w.T, w.Hkv, w.D))
+    # the benchmark's layout at this size: one workgroup per (row, KV head)
+    assert lsa.attention_head_major(1, w.T, w.Hkv, w.D, lsa.LSA_BF16)
     out = lsa.sparse_attention(Q, K, V, idx, cnt)
     torch.cuda.synchronize()
     oc = oracle_cache_parallel(X, oracle_params(p))
@@ -148,6 +150,8 @@ def test_prefill_10m_flat_last_chunk():
     Q = device_normal(w, "q", (w.Tq, w.Hq, w.D), row0=w.q_start)
     K = device_normal(w, "k", (w.T, w.Hkv, w.D))
     V = device_normal(w, "v", (w.T, w.Hkv, w.D))
+    # the benchmark's layout at this size: one workgroup per query row
+    assert not lsa.attention_head_major(1, w.T, w.Hkv, w.D, lsa.LSA_BF16)
     out = lsa.sparse_attention(Q, K, V, idx, cnt)
     torch.cuda.synchronize()
     # the device generator fills all 5.12e9 elements like the host rows (this
