@@ -297,14 +297,20 @@ __global__ __launch_bounds__(64 * kMaxWaves, 3) void k_attn_bf16(AttnArgs a) {
 //     for the first and second half of the launch's rows.  Each XCD's L2
 //     then holds one head's rows (a quarter of the bytes per token) for four
 //     times as many neighbouring queries, which pays when K/V fit the
-//     Infinity Cache (the 128K workload: 256 MiB).  Tiles of 16 tokens are loaded with plain 16-byte loads into a ring
-// of kRing4 register buffers, kRing4 - 1 tiles ahead of the one being
-// computed, so each wave keeps 16 KiB in flight and 8 waves share a CU.  K goes straight into the B operand of 16x16x32 MFMAs: for product j,
-// lane (n, u) holds bytes [16 (4j + u), +16) of key n, and Q uses the same
-// dim order.  V is written to a per-wave LDS tile, its 16-byte chunks XOR
-// swizzled by row (chunk ^ 2 (row & 7)) so that the transposing reads of the
-// PV products hit distinct banks.  The loop runs whole ring cycles: tiles at
-// or past the end, and invalid list entries, load token 0 with zero weight.
+//     Infinity Cache (the 128K workload: 128 MiB each).
+// Tiles of 16 tokens are loaded with 16-byte loads, each instruction reading
+// four tokens' whole 256 B head rows (whole cache lines), into a ring of
+// kRing4 register buffers, kRing4 - 1 tiles ahead of the one being computed,
+// so each wave keeps 16 KiB in flight.  K and V then go to per-wave LDS
+// tiles.  The K tile's 16-byte chunks are XOR swizzled by row (chunk ^ row)
+// so that the reads of the QK^T operands (16x16x32 MFMAs; for product j,
+// lane (n, u) takes bytes [16 (4j + u), +16) of key n, and Q uses the same
+// dim order) hit distinct banks; the V tile's chunks are swizzled by
+// chunk ^ 2 (row & 7) for the transposing reads of the PV products.  Loading
+// K straight into the MFMA layout instead (16 keys x 64 B per instruction,
+// two requests per cache line) made the loop bound by L2 requests.  The
+// loop runs whole ring cycles: tiles at or past the end, and invalid list
+// entries, load token 0 with zero weight.
 // The row's index list is staged in LDS, kList4<NW> entries at a time, each
 // entry checked once there: invalid entries, and the tail of the last tile
 // past the count, are stored as -1, and 16 more -1 entries after the stage
@@ -316,12 +322,16 @@ __global__ __launch_bounds__(64 * kMaxWaves, 3) void k_attn_bf16(AttnArgs a) {
 // (O and l always share the reference, so the result does not depend on
 // when this happens); l is summed per lane and reduced once at the end.
 constexpr int kRing4 = 3;                      // register buffers per wave
-constexpr int kVTile4 = 16 * 256;              // V tile of one KV head in LDS (bytes)
+constexpr int kVTile4 = 16 * 256;              // K or V tile of one KV head in LDS (bytes)
 constexpr int kP4 = 16 * 16 * 2;               // P tile [16 keys][16 heads] bf16, per wave
-// index-list entries staged at a time, and per thread in one batch of loads
-template <int NW> constexpr int kList4 = NW == 4 ? 8192 : 3072;
-template <int NW> constexpr int kBatch4 = NW == 4 ? 12 : 48;
-template <int NW> constexpr int kLds4 = NW * (kVTile4 + kP4) + (kList4<NW> + 16) * 4;
+constexpr int kWave4 = 2 * kVTile4 + kP4;      // LDS of one wave: V tile, K tile, P tile
+// index-list entries staged at a time, and per thread in one batch of loads;
+// with NW = 1, 2,816 entries let eight workgroups share a CU's 160 KiB
+template <int NW> constexpr int kList4 = NW == 4 ? 8192 : 2816;
+template <int NW> constexpr int kBatch4 = NW == 4 ? 12 : 44;
+template <int NW> constexpr int kLds4 = NW * kWave4 + (kList4<NW> + 16) * 4;
+static_assert(8 * kLds4<1> <= 160 * 1024 && 2 * kLds4<4> <= 160 * 1024, "LDS per CU");
+static_assert(kBatch4<1> * 64 == kList4<1>, "one batch stages a whole chunk");
 // K and V caches of at most this many bytes each (B * Tmax * Hkv * D * 2)
 // take the per-head workgroups.  Measured: 14% less attention time at 128 MiB
 // (128K tokens), 3-12% more at 1 GiB and beyond (1M and 10M tokens, 16 x 1M
@@ -393,9 +403,10 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn_bf16_h4(AttnArgs a) {
   const int32_t* lst = a.idx + row * (int64_t)a.L + k0;
   const char* kb = reinterpret_cast<const char*>(a.k + b * a.Tmax * 4 * kHeadDim) + kvh * 256;
   const char* vb = reinterpret_cast<const char*>(a.v + b * a.Tmax * 4 * kHeadDim) + kvh * 256;
-  char* vt = lds4 + wave * (kVTile4 + kP4);
-  uint16_t* ps = reinterpret_cast<uint16_t*>(vt + kVTile4);
-  int32_t* slist = reinterpret_cast<int32_t*>(lds4 + NW * (kVTile4 + kP4));
+  char* vt = lds4 + wave * kWave4;
+  char* kt = vt + kVTile4;
+  uint16_t* ps = reinterpret_cast<uint16_t*>(kt + kVTile4);
+  int32_t* slist = reinterpret_cast<int32_t*>(lds4 + NW * kWave4);
   const int r16 = lane & 15, u = lane >> 4;
   // token indices below tlim are valid (unsigned compare rejects e < 0)
   const uint32_t tlim = a.Tmax < 0x7fffffff ? (uint32_t)a.Tmax : 0x7fffffffu;
@@ -494,26 +505,32 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn_bf16_h4(AttnArgs a) {
       const int pk = slist[tr + r16];
       const int4 p4 = *reinterpret_cast<const int4*>(slist + tr + 4 * vi);
       kv = pk >= 0;
-      const char* kp = kb + (uint64_t)(uint32_t)(pk > 0 ? pk : 0) * 1024 + 16 * u;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) k[j] = *reinterpret_cast<const u32x4_t*>(kp + 64 * j);
+      // load j: token 4 vi + j, chunk vc of its K and V head rows
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int p = j == 0 ? p4.x : (j == 1 ? p4.y : (j == 2 ? p4.z : p4.w));
-        v[j] = *reinterpret_cast<const u32x4_t*>(vb + (uint64_t)(uint32_t)(p > 0 ? p : 0) * 1024 + 16 * vc);
+        const uint64_t off = (uint64_t)(uint32_t)(p > 0 ? p : 0) * 1024 + 16 * vc;
+        k[j] = *reinterpret_cast<const u32x4_t*>(kb + off);
+        v[j] = *reinterpret_cast<const u32x4_t*>(vb + off);
       }
     };
     auto compute = [&](const u32x4_t (&k)[4], const u32x4_t (&v)[4], bool kv) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int rr = 4 * vi + j;
+        *reinterpret_cast<u32x4_t*>(kt + 256 * rr + 16 * (vc ^ rr)) = k[j];
         *reinterpret_cast<u32x4_t*>(vt + 256 * rr + 16 * (vc ^ (2 * (rr & 7)))) = v[j];
       }
+      wave_fence();
       // S = Q K^T: row = head 4u + i, column = key r16
+      u32x4_t kf[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        kf[j] = *reinterpret_cast<const u32x4_t*>(kt + 256 * r16 + 16 * ((4 * j + u) ^ r16));
       f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[j], __builtin_bit_cast(bf16x8, k[j]), sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[j], __builtin_bit_cast(bf16x8, kf[j]), sacc, 0, 0, 0);
       float pv[4];
       bool grow = false;
 #pragma unroll
