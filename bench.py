@@ -3,7 +3,7 @@
 One step = one pass of the whole prefill path over one synthetic layer:
 build_bucket_cache over all T keys, lsa_index_prefill for all Tq queries,
 lsa_sparse_attention over the resulting lists (which the library runs as
-back-to-back launches of 2,048 query rows).  Default workload: T = Tq =
+back-to-back launches of 1,024 query rows).  Default workload: T = Tq =
 131,072, bf16 K/V, 32 query / 4 KV heads, head_dim 128, 1,024-component latent
 mixture, flat search, k = 2,048, 4 sinks, 512-key window.
 

@@ -121,7 +121,7 @@ def test_attention_host_errors():
     empty_cache = list(args())
     empty_cache[5] = 0                     # Tmax = 0 with rows to attend
     assert L.lsa_sparse_attention(*empty_cache) == -1
-    assert lsa.attention_launch_rows() == 2048
+    assert lsa.attention_launch_rows() == 1024
     # per-(row, KV head) workgroups for bf16, 4 KV heads, caches of <= 256 MiB each
     hm = lambda B, T, Hkv=4, D=128, dt=lsa.LSA_BF16: lsa.attention_head_major(B, T, Hkv, D, dt)
     assert hm(1, 131072) and hm(1, 262144) and not hm(1, 262145)

@@ -236,7 +236,7 @@ def test_attention_bf16_on_oracle_lists(splits, few):
 
 def test_attention_across_launches():
     """More rows than one bf16 attention launch takes (5,000 rows: three
-    launches of up to 2,048): rows on both sides of each launch boundary match
+    launches of up to 1,024): rows on both sides of each launch boundary match
     a launch of just those rows bit for bit, in both workgroup layouts (one
     per (row, KV head) and one per row), the two layouts agree bit for bit,
     and sampled rows match the oracle's lists and attention."""
@@ -378,8 +378,9 @@ def test_attention_invalid_entries_ragged_counts_and_scale(scale, splits, row_la
 
 @pytest.mark.parametrize("row_layout", [False, True])
 def test_attention_batched_rows_across_launches(row_layout):
-    """Two sequences of 1,500 query rows each (3,000 rows: two launches of up to
-    2,048, the boundary inside the second sequence), each with its own K/V."""
+    """Two sequences of 1,500 query rows each, each with its own K/V: 3,000
+    rows, so three launches of up to 1,024, the launch boundaries inside both
+    sequences."""
     say(f"case: attention bf16, B = 2 x 1,500 rows row_layout={row_layout}")
     w = S.WORKLOADS[2]
     B, T, Tq, L = 2, 4096, 1500, 600
@@ -405,7 +406,8 @@ def test_attention_batched_rows_across_launches(row_layout):
     out = out.float().cpu().numpy()
     n = lsa.attention_launch_rows()
     err = 0.0
-    for g in (0, 1, Tq - 1, Tq, n - 2, n - 1, n, n + 1, B * Tq - 1):
+    assert n < Tq < 2 * n < B * Tq
+    for g in (0, 1, Tq - 1, Tq, n - 2, n - 1, n, n + 1, 2 * n - 1, 2 * n, B * Tq - 1):
         b, r = divmod(g, Tq)
         err = max(err, np.abs(out[b, r] - O.attention_query(qs[b][r], ks[b], vs[b], idx[b, r],
                                                             cnt[b, r])).max())
