@@ -516,11 +516,12 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn_bf16_h4(AttnArgs a) {
       }
     };
     auto compute = [&](const u32x4_t (&k)[4], const u32x4_t (&v)[4], bool kv) {
+      // the K tile's reads enter the LDS queue right behind its writes, and
+      // the V tile is written while the QK^T products run
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int rr = 4 * vi + j;
         *reinterpret_cast<u32x4_t*>(kt + 256 * rr + 16 * (vc ^ rr)) = k[j];
-        *reinterpret_cast<u32x4_t*>(vt + 256 * rr + 16 * (vc ^ (2 * (rr & 7)))) = v[j];
       }
       wave_fence();
       // S = Q K^T: row = head 4u + i, column = key r16
@@ -532,6 +533,11 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn_bf16_h4(AttnArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[j], __builtin_bit_cast(bf16x8, kf[j]), sacc, 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int rr = 4 * vi + j;
+        *reinterpret_cast<u32x4_t*>(vt + 256 * rr + 16 * (vc ^ (2 * (rr & 7)))) = v[j];
+      }
       float pv[4];
       bool grow = false;
 #pragma unroll
