@@ -303,11 +303,14 @@ __global__ __launch_bounds__(64 * kMaxWaves, 3) void k_attn_bf16(AttnArgs a) {
 // four tokens' whole 256 B head rows (whole cache lines), into a ring of
 // kRing4 register buffers, kRing4 - 1 tiles ahead of the one being computed,
 // so each wave keeps 16 KiB in flight.  K and V then go to per-wave LDS
-// tiles.  The K tile's 16-byte chunks are XOR swizzled by row (chunk ^ row)
-// so that the reads of the QK^T operands (16x16x32 MFMAs; for product j,
-// lane (n, u) takes bytes [16 (4j + u), +16) of key n, and Q uses the same
-// dim order) hit distinct banks; the V tile's chunks are swizzled by
-// chunk ^ 2 (row & 7) for the transposing reads of the PV products.  Loading
+// tiles.  The products are taken transposed, S^T = K Q^T and O^T = V^T P^T,
+// so that the scores come out with one head per lane column and four keys
+// per lane, which is the layout of P^T as an MFMA operand: P stays in
+// registers.  The K tile's 16-byte chunks are XOR swizzled by row
+// (chunk ^ row) so that the reads of the K operands (16x16x32 MFMAs; for
+// product j, lane (key n, u) takes bytes [16 (4j + u), +16) of key n, and Q
+// uses the same dim order) hit distinct banks; the V tile's chunks are
+// swizzled by chunk ^ 2 (row & 7) for the transposing reads of V^T.  Loading
 // K straight into the MFMA layout instead (16 keys x 64 B per instruction,
 // two requests per cache line) made the loop bound by L2 requests.  The
 // loop runs whole ring cycles: tiles at or past the end, and invalid list
@@ -324,8 +327,7 @@ __global__ __launch_bounds__(64 * kMaxWaves, 3) void k_attn_bf16(AttnArgs a) {
 // when this happens); l is summed per lane and reduced once at the end.
 constexpr int kRing4 = 3;                      // register buffers per wave
 constexpr int kVTile4 = 16 * 256;              // K or V tile of one KV head in LDS (bytes)
-constexpr int kP4 = 16 * 16 * 2;               // P tile [16 keys][16 heads] bf16, per wave
-constexpr int kWave4 = 2 * kVTile4 + kP4;      // LDS of one wave: V tile, K tile, P tile
+constexpr int kWave4 = 2 * kVTile4;            // LDS of one wave: V tile, K tile
 // index-list entries staged at a time, and per thread in one batch of loads;
 // with NW = 1, 2,816 entries let eight workgroups share a CU's 160 KiB
 template <int NW> constexpr int kList4 = NW == 4 ? 8192 : 2816;
@@ -406,7 +408,6 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn_bf16_h4(AttnArgs a) {
   const char* vb = reinterpret_cast<const char*>(a.v + b * a.Tmax * 4 * kHeadDim) + kvh * 256;
   char* vt = lds4 + wave * kWave4;
   char* kt = vt + kVTile4;
-  uint16_t* ps = reinterpret_cast<uint16_t*>(kt + kVTile4);
   int32_t* slist = reinterpret_cast<int32_t*>(lds4 + NW * kWave4);
   const int r16 = lane & 15, u = lane >> 4;
   // token indices below tlim are valid (unsigned compare rejects e < 0)
@@ -439,22 +440,21 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn_bf16_h4(AttnArgs a) {
   f32x4 o[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // m: reference max per head row, uniform over the row's 16 lanes, with a
-  // finite floor so that exp2(-inf - m) = 0; lp: this lane's partial sums
-  // mth: the raw score above which a key moves the reference (m + 2^kLazy)
-  float m[4], lp[4], mth[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) { m[i] = -1e30f; lp[i] = 0.f; mth[i] = -__builtin_inff(); }
+  // lane (head r16, u): m, the head's reference max (uniform over the head's
+  // four lanes), with a finite floor so that exp2(-inf - m) = 0; mth, the raw
+  // score above which a key moves the reference (m + 2^kLazy); lp, this
+  // lane's partial sum over its keys 4u .. 4u + 3 of every tile
+  float m = -1e30f, lp = 0.f, mth = -__builtin_inff();
 
   const int vi = lane >> 4, vc = lane & 15;    // V loads: token 4 vi + j, chunk vc
   // transposing V reads: source lane s of a 16-lane group points at key row
-  // 4u + (s >> 2), dims 16j + 4 (s & 3) .. +3 (byte 8 (s & 1) of chunk 2j + cv)
+  // 4u + (s >> 2), dims 16j + 4 (s & 3) .. +3 (byte 8 (s & 1) of chunk 2j + cv);
+  // lane (r16, u) receives dim 16j + r16 of keys 4u .. 4u + 3
   const int sk = 4 * u + (r16 >> 2), cv = (r16 & 3) >> 1, sw = 2 * (sk & 7);
   const char* vrd = vt + 256 * sk + 8 * (r16 & 1);
-  const uint16_t* prd = ps + sk * 16 + 4 * (r16 & 3);
 
   u32x4_t kr[kRing4][4], vr[kRing4][4];
-  bool kval[kRing4];
+  uint32_t kval[kRing4];                       // bit i: key 4u + i of the tile is real
   // slot i of a stage holding cn entries: the entry if it is valid, else -1
   auto put = [&](int i, int32_t e, int cn) {
     slist[i] = (i < cn && (uint32_t)e < tlim) ? e : -1;
@@ -500,12 +500,13 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn_bf16_h4(AttnArgs a) {
     }
     const int nt = (cn + 15) >> 4;
 
-    // tile T into one ring buffer; kv: this lane's key (column r16) is real
-    auto issue = [&](int T, u32x4_t (&k)[4], u32x4_t (&v)[4], bool& kv) {
+    // tile T into one ring buffer; kv: which of keys 4u .. 4u + 3 are real
+    // (the entries this lane also loads V rows for: vi = u)
+    auto issue = [&](int T, u32x4_t (&k)[4], u32x4_t (&v)[4], uint32_t& kv) {
       const int tr = T < nt ? T << 4 : kList;  // padding tiles read the -1 entries
-      const int pk = slist[tr + r16];
       const int4 p4 = *reinterpret_cast<const int4*>(slist + tr + 4 * vi);
-      kv = pk >= 0;
+      kv = (p4.x >= 0 ? 1u : 0u) | (p4.y >= 0 ? 2u : 0u) | (p4.z >= 0 ? 4u : 0u) |
+           (p4.w >= 0 ? 8u : 0u);
       // load j: token 4 vi + j, chunk vc of its K and V head rows
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -515,16 +516,16 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn_bf16_h4(AttnArgs a) {
         v[j] = *reinterpret_cast<const u32x4_t*>(vb + off);
       }
     };
-    auto compute = [&](const u32x4_t (&k)[4], const u32x4_t (&v)[4], bool kv) {
+    auto compute = [&](const u32x4_t (&k)[4], const u32x4_t (&v)[4], uint32_t kv) {
       // the K tile's reads enter the LDS queue right behind its writes, and
-      // the V tile is written while the QK^T products run
+      // the V tile is written while the K Q^T products run
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int rr = 4 * vi + j;
         *reinterpret_cast<u32x4_t*>(kt + 256 * rr + 16 * (vc ^ rr)) = k[j];
       }
       wave_fence();
-      // S = Q K^T: row = head 4u + i, column = key r16
+      // S^T = K Q^T: row = key 4u + i, column = head r16
       u32x4_t kf[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
@@ -532,46 +533,50 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn_bf16_h4(AttnArgs a) {
       f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[j], __builtin_bit_cast(bf16x8, kf[j]), sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[j]), qf[j], sacc, 0, 0, 0);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int rr = 4 * vi + j;
         *reinterpret_cast<u32x4_t*>(vt + 256 * rr + 16 * (vc ^ (2 * (rr & 7)))) = v[j];
       }
-      float pv[4];
       bool grow = false;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) grow |= sacc[i] > mth[i];
-      if (__ballot(grow && kv)) {
+      for (int i = 0; i < 4; ++i) grow |= ((kv >> i) & 1u) && sacc[i] > mth;
+      if (__ballot(grow)) {
+        // the head's max over the tile: this lane's keys, then its 4 lanes
+        float x = -__builtin_inff();
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float x = kv ? sacc[i] * sl : -__builtin_inff();
-          const float mn = fmaxf(m[i], row16_max(x));
-          const float alpha = __builtin_amdgcn_exp2f(m[i] - mn);
-          lp[i] *= alpha;
+        for (int i = 0; i < 4; ++i)
+          if ((kv >> i) & 1u) x = fmaxf(x, sacc[i] * sl);
+        x = fmaxf(x, __shfl_xor(x, 16, 64));
+        x = fmaxf(x, __shfl_xor(x, 32, 64));
+        const float mn = fmaxf(m, x);
+        const float alpha = __builtin_amdgcn_exp2f(m - mn);
+        lp *= alpha;
 #pragma unroll
-          for (int j = 0; j < 8; ++j) o[j][i] *= alpha;
-          m[i] = mn;
-          mth[i] = (mn + kLazy) * inv_sl;
-        }
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[j][i] *= alpha;
+        m = mn;
+        mth = (mn + kLazy) * inv_sl;
       }
+      float pv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        pv[i] = kv ? __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], sl, -m[i])) : 0.f;
-        lp[i] += pv[i];
+        pv[i] = ((kv >> i) & 1u) ? __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], sl, -m)) : 0.f;
+        lp += pv[i];
       }
+      // P^T as the B operand of 16x16x16 MFMAs: lane (head r16, u), keys 4u .. 4u + 3
       uint2 w2;
       w2.x = pack_bf16x2(pv[0], pv[1]);
       w2.y = pack_bf16x2(pv[2], pv[3]);
-      *reinterpret_cast<uint2*>(ps + r16 * 16 + 4 * u) = w2;   // P[key r16][heads 4u..4u+3]
-      wave_fence();
-      // O += P V with 16x16x16 MFMAs: A = P (head r16, keys 4u..4u+3), B = V
-      const v4s_t pa4 = __builtin_bit_cast(v4s_t, ds_read_tr16(prd));
+      const v4s_t pb4 = __builtin_bit_cast(v4s_t, w2);
+      // O^T += V^T P^T: A = V^T (dim 16j + r16, keys 4u .. 4u + 3)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const v4s_t vb4 = __builtin_bit_cast(
+        const v4s_t va4 = __builtin_bit_cast(
             v4s_t, ds_read_tr16(reinterpret_cast<const uint16_t*>(vrd + 16 * ((2 * j + cv) ^ sw))));
-        o[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa4, vb4, o[j], 0, 0, 0);
+        o[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va4, pb4, o[j], 0, 0, 0);
       }
       wave_fence();
     };
@@ -594,36 +599,34 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn_bf16_h4(AttnArgs a) {
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);        // vmcnt(0): the padding tiles' loads retired
   }
-  float l[4];
+  // the head's sum over its four lanes
+  float l = lp;
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  // write: lane (head r16 < G, u) holds O^T rows 16j + 4u + i, i = 0..3
+  if (r16 < a.G) {
+    const int64_t h = (int64_t)kvh * a.G + r16;
+    if (a.splits == 1) {
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      uint16_t* orow = a.out + (row * a.Hq + h) * kHeadDim + 4 * u;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) l[i] = row16_sum(lp[i]);
-  // write: rows 4u + i < G, dims 16j + r16
-  if (a.splits == 1) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int hr = 4 * u + i;
-      if (hr < a.G) {
-        const float inv = l[i] > 0.f ? 1.f / l[i] : 0.f;
-        uint16_t* orow = a.out + (row * a.Hq + (int64_t)kvh * a.G + hr) * kHeadDim;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) orow[16 * j + r16] = f32_to_bf16_rne(o[j][i] * inv);
+      for (int j = 0; j < 8; ++j) {
+        uint2 w;
+        w.x = pack_bf16x2(o[j][0] * inv, o[j][1] * inv);
+        w.y = pack_bf16x2(o[j][2] * inv, o[j][3] * inv);
+        *reinterpret_cast<uint2*>(orow + 16 * j) = w;
       }
-    }
-  } else {
-    const int64_t slot = row * a.splits + split;
-    float* ob = a.ws;
-    float* mb = a.ws + a.rows * a.splits * a.Hq * kHeadDim;
-    float* lb = mb + a.rows * a.splits * a.Hq;
+    } else {
+      const int64_t slot = row * a.splits + split;
+      float* ob = a.ws;
+      float* mb = a.ws + a.rows * a.splits * a.Hq * kHeadDim;
+      float* lb = mb + a.rows * a.splits * a.Hq;
+      float* orow = ob + (slot * a.Hq + h) * kHeadDim + 4 * u;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int hr = 4 * u + i;
-      if (hr < a.G) {
-        const int64_t h = (int64_t)kvh * a.G + hr;
-        float* orow = ob + (slot * a.Hq + h) * kHeadDim;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) orow[16 * j + r16] = o[j][i];
-        if (r16 == 0) { mb[slot * a.Hq + h] = m[i] * 0.6931471805599453f; lb[slot * a.Hq + h] = l[i]; }
-      }
+      for (int j = 0; j < 8; ++j)
+        *reinterpret_cast<float4*>(orow + 16 * j) = make_float4(o[j][0], o[j][1], o[j][2], o[j][3]);
+      // running max back to natural-log units for the combine step
+      if (u == 0) { mb[slot * a.Hq + h] = m * 0.6931471805599453f; lb[slot * a.Hq + h] = l; }
     }
   }
 }
