@@ -218,8 +218,8 @@ int64_t lsa_attention_launch_rows(void);
 int32_t lsa_attention_head_major(int32_t B, int64_t Tmax, int32_t Hkv, int32_t D, int32_t dtype);
 
 /* A split count for lsa_sparse_attention: the largest power of two (<= 256)
- * that keeps at least 32 listed keys per split and rows * splits <= 512
- * workgroups (two per compute unit), so that few query rows (decode) still
+ * that keeps at least 32 listed keys per split and rows * splits <= 256
+ * (one row's split per compute unit), so that few query rows (decode) still
  * spread over the whole chip.  rows = B * Tq. */
 int32_t lsa_attention_default_splits(int64_t rows, int32_t L_max);
 

@@ -566,7 +566,7 @@ int32_t lsa_attention_head_major(int32_t B, int64_t Tmax, int32_t Hkv, int32_t D
 int32_t lsa_attention_default_splits(int64_t rows, int32_t L_max) {
   if (rows <= 0 || L_max <= 0) return 1;
   int32_t splits = 1;
-  while (splits < 256 && rows * splits < 512 && L_max / (2 * splits) >= 32) splits *= 2;
+  while (splits < 256 && rows * splits < 256 && L_max / (2 * splits) >= 32) splits *= 2;
   return splits;
 }
 
