@@ -336,9 +336,10 @@ template <int NW> constexpr int kLds4 = NW * kWave4 + (kList4<NW> + 16) * 4;
 static_assert(8 * kLds4<1> <= 160 * 1024 && 2 * kLds4<4> <= 160 * 1024, "LDS per CU");
 static_assert(kBatch4<1> * 64 == kList4<1>, "one batch stages a whole chunk");
 // K and V caches of at most this many bytes each (B * Tmax * Hkv * D * 2)
-// take the per-head workgroups.  Measured: 14% less attention time at 128 MiB
-// (128K tokens), 3-12% more at 1 GiB and beyond (1M and 10M tokens, 16 x 1M
-// decode); sizes in between were not measured.
+// take the per-head workgroups.  Measured against one workgroup per row: 23%
+// less attention time at 128 MiB (128K tokens), 6-7% more at 1 GiB and
+// beyond (1M and 10M tokens, 16 x 1M decode); sizes in between were not
+// measured.
 constexpr int64_t kHeadMajorMaxKvBytes = 256ll << 20;
 constexpr float kLazy = 8.f;
 
