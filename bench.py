@@ -112,9 +112,9 @@ def attention_kernel_name(lsa, w, B: int, Tmax: int) -> str:
     if w.dtype != "bf16":
         return "k_attn_f32"
     if w.Hkv != 4:
-        return "k_attn_bf16"
+        return "k_attn_bf16<1, 0>"
     nw = 1 if lsa.attention_head_major(B, Tmax, w.Hkv, w.D, lsa.LSA_BF16) else 4
-    return f"k_attn_bf16_h4<{nw}>"
+    return f"k_attn_bf16<{nw}, 4>"
 
 
 def measured_traffic(kernel: str, workload: str, rows_per_launch: int):

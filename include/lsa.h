@@ -208,13 +208,14 @@ int64_t lsa_attention_workspace_bytes(int32_t B, int64_t Tq, int32_t Hq, int32_t
  * in flight stay neighbours (their lists share keys in the caches). */
 int64_t lsa_attention_launch_rows(void);
 
-/* 1 when lsa_sparse_attention with these shapes runs one workgroup per
- * (query row, KV head), grouping each KV head's workgroups on their own XCDs
- * (bf16, Hkv = 4, D = 128, and K and V caches of at most 256 MiB each:
- * B * Tmax * Hkv * D * 2 bytes); 0 when each workgroup takes a whole row
- * (larger caches, where reading each listed token's rows of all heads
- * together pays more than the per-XCD cache reuse), and for other dtypes and
- * shapes.  Both layouts compute the same results. */
+/* 1 when lsa_sparse_attention in bf16 runs one workgroup per (query row,
+ * KV head), grouping each KV head's workgroups on their own XCDs when Hkv
+ * divides 8: always for Hkv != 4, and for Hkv = 4 when the K and V caches
+ * hold at most 256 MiB each (B * Tmax * Hkv * D * 2 bytes).  0 when each
+ * workgroup takes a whole row (Hkv = 4 with larger caches, where reading
+ * each listed token's rows of all heads together pays more than the per-XCD
+ * cache reuse), and for fp32 or D != 128.  Both layouts compute the same
+ * results. */
 int32_t lsa_attention_head_major(int32_t B, int64_t Tmax, int32_t Hkv, int32_t D, int32_t dtype);
 
 /* A split count for lsa_sparse_attention: the largest power of two (<= 256)

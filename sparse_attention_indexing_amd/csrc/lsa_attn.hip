@@ -4,13 +4,11 @@
 // ordinary attention runs over the sinks, the selected keys and the window,
 // and one index list per query is shared by all of its attention heads.
 //
-// bf16 path: one workgroup per query row (and split), one wave per KV head.
-// The GQA group of G <= 16 query heads forms the M side of 16x16x32 bf16
-// MFMAs, so every gathered K/V row (256 B per KV head) is read once for the
-// whole group.  Keys are processed 32 at a time: K rows are loaded straight
-// into MFMA operand registers (64 contiguous bytes per lane), V rows are
-// staged in LDS and read back with keys along the reduction dimension.
-// Online softmax in fp32; P is rounded to bf16 for the PV product.
+// bf16 path (k_attn_bf16): one wave per (query row, KV head, split).  The GQA
+// group of G <= 16 query heads forms one side of 16x16 bf16 MFMAs, so every
+// gathered K/V row (256 B per KV head) is read once for the whole group.
+// Online softmax in fp32; P is rounded to bf16 for the PV product.  fp32
+// path (k_attn_f32): one wave per (query row, head).
 #include "lsa_internal.h"
 
 namespace lsa {
@@ -19,10 +17,6 @@ namespace {
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
-constexpr int kKT = 32;          // keys per tile
-constexpr int kVStride = 136;    // LDS row stride (bf16) of the staged V tile [key][dim]
-constexpr int kPStride = 16;     // LDS row stride (bf16) of P stored as [key][head]
-constexpr int kMaxWaves = 4;
 // bf16 rows are launched this many at a time.  A launch ends only when all of
 // its rows are done, so the rows in flight stay neighbours, whose lists share
 // many keys in L2 and the Infinity Cache; one launch over all rows lets the
@@ -52,8 +46,6 @@ struct AttnArgs {
   float scale_log2;     // scale * log2(e): softmax in base 2
 };
 
-constexpr int kWaveLds = kKT * kVStride + kKT * kPStride;  // bf16 elements per wave
-
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
 
@@ -66,239 +58,23 @@ __device__ __forceinline__ uint2 ds_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(uint2, r);
 }
 
-// Reductions over the 16 lanes of a DPP row (quad swaps, half mirror, mirror).
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, dpp_f<0xB1>(v));    // quad_perm [1,0,3,2]
-  v = fmaxf(v, dpp_f<0x4E>(v));    // quad_perm [2,3,0,1]
-  v = fmaxf(v, dpp_f<0x141>(v));   // row_half_mirror
-  v = fmaxf(v, dpp_f<0x140>(v));   // row_mirror
-  return v;
-}
-__device__ __forceinline__ float row16_sum(float v) {
-  v += dpp_f<0xB1>(v);
-  v += dpp_f<0x4E>(v);
-  v += dpp_f<0x141>(v);
-  v += dpp_f<0x140>(v);
-  return v;
-}
-
-// K fragment of one key row for 16x16x32 MFMAs: dims [32u, 32u + 32) (64 B)
-__device__ __forceinline__ void load_krow(uint4* w, const uint16_t* base, int u) {
-  const uint4* src = reinterpret_cast<const uint4*>(base + 32 * u);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) w[j] = src[j];
-}
-// half a V row: dims [64h, 64h + 64) (128 B), kept in eight named registers
-struct VHalf {
-  uint4 r0, r1, r2, r3, r4, r5, r6, r7;
-};
-__device__ __forceinline__ VHalf load_vhalf(const uint16_t* base, int h) {
-  const uint4* src = reinterpret_cast<const uint4*>(base + 64 * h);
-  VHalf v;
-  v.r0 = src[0]; v.r1 = src[1]; v.r2 = src[2]; v.r3 = src[3];
-  v.r4 = src[4]; v.r5 = src[5]; v.r6 = src[6]; v.r7 = src[7];
-  return v;
-}
-__device__ __forceinline__ void store_vhalf(uint16_t* dst, const VHalf& v) {
-  uint4* d = reinterpret_cast<uint4*>(dst);
-  d[0] = v.r0; d[1] = v.r1; d[2] = v.r2; d[3] = v.r3;
-  d[4] = v.r4; d[5] = v.r5; d[6] = v.r6; d[7] = v.r7;
-}
-
-// One workgroup per (query row, split); wave w handles KV heads w, w + nwaves, ...
-// The row's index list is staged in LDS once.  Gathers are software
-// pipelined: the K and V rows of tile t+1 are requested right after the QK^T
-// products of tile t, so their latency overlaps the softmax and PV of tile t.
-// Positions outside [0, Tmax) are skipped (masked to zero weight).
-__global__ __launch_bounds__(64 * kMaxWaves, 3) void k_attn_bf16(AttnArgs a) {
-  extern __shared__ uint16_t attn_lds[];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nwaves = blockDim.x >> 6;
-  // Workgroups are dealt to the 8 XCDs round-robin; with 8+ rows give each
-  // XCD a contiguous range of rows so neighbouring queries (shared window,
-  // similar buckets) meet in the same L2; with fewer rows grid.x = rows and
-  // the splits of a row spread over the XCDs.
-  int64_t row = blockIdx.x;
-  if (a.nrows >= 8) {
-    const int64_t per_xcd = (a.nrows + 7) / 8;
-    row = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-  }
-  if (row >= a.nrows) return;
-  row += a.row0;
-  const int split = blockIdx.y;
-  const int64_t b = row / a.Tq;
-  int cnt = a.count[row];
-  cnt = cnt < 0 ? 0 : (cnt > a.L ? a.L : cnt);
-  const int per = (cnt + a.splits - 1) / a.splits;
-  const int k0 = split * per;
-  const int k1 = (k0 + per) < cnt ? (k0 + per) : cnt;
-  const int n = k1 > k0 ? k1 - k0 : 0;
-  const int32_t* lst = a.idx + row * (int64_t)a.L + k0;
-  int32_t* lst_s = reinterpret_cast<int32_t*>(attn_lds + nwaves * kWaveLds);
-  for (int i = threadIdx.x; i < n; i += blockDim.x) {
-    const int32_t v = lst[i];
-    lst_s[i] = (v >= 0 && v < a.Tmax) ? v : -1;
-  }
-  __syncthreads();
-  const int r16 = lane & 15, u = lane >> 4;
-  const int kk = lane >> 1, hv = lane & 1;       // V staging: key kk, dims half hv
-  uint16_t* vs = attn_lds + wave * kWaveLds;
-  uint16_t* ps = vs + kKT * kVStride;
-  const uint16_t* kbase = a.k + b * a.Tmax * a.Hkv * kHeadDim;
-  const uint16_t* vbase = a.v + b * a.Tmax * a.Hkv * kHeadDim;
-
-  for (int kvh = wave; kvh < a.Hkv; kvh += nwaves) {
-    // Q fragment: head row r16 of the group, dims [32u + 8j, +8)
-    bf16x8 qf[4];
-    {
-      const bool ok = r16 < a.G;
-      const uint16_t* qrow = a.q + (row * a.Hq + (int64_t)kvh * a.G + (ok ? r16 : 0)) * kHeadDim + 32 * u;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        uint4 w = ok ? reinterpret_cast<const uint4*>(qrow)[j] : make_uint4(0, 0, 0, 0);
-        qf[j] = __builtin_bit_cast(bf16x8, w);
-      }
-    }
-    f32x4 o[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m[4], l[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) { m[i] = -__builtin_inff(); l[i] = 0.f; }
-
-    auto pos_at = [&](int i) -> int32_t { return i < n ? lst_s[i] : -1; };
-    auto row_of = [&](const uint16_t* base, int32_t p) {
-      return base + ((int64_t)(p >= 0 ? p : 0) * a.Hkv + kvh) * kHeadDim;
-    };
-    int32_t pa = pos_at(r16), pb = pos_at(16 + r16), pv = pos_at(kk);
-    uint4 wa[4], wb[4];
-    load_krow(wa, row_of(kbase, pa), u);
-    load_krow(wb, row_of(kbase, pb), u);
-    VHalf vr = load_vhalf(row_of(vbase, pv), hv);
-    for (int t = 0; t < n; t += kKT) {
-      // stage this tile's V rows (registers -> LDS)
-      store_vhalf(vs + kk * kVStride + 64 * hv, vr);
-      // S = Q K^T for keys t + r16 (A) and t + 16 + r16 (B)
-      f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[j], __builtin_bit_cast(bf16x8, wa[j]), sa, 0, 0, 0);
-        sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[j], __builtin_bit_cast(bf16x8, wb[j]), sb, 0, 0, 0);
-      }
-      const bool va = pa >= 0, vb = pb >= 0;
-      // request the next tile now
-      if (t + kKT < n) {
-        pa = pos_at(t + kKT + r16);
-        pb = pos_at(t + kKT + 16 + r16);
-        pv = pos_at(t + kKT + kk);
-        load_krow(wa, row_of(kbase, pa), u);
-        load_krow(wb, row_of(kbase, pb), u);
-        vr = load_vhalf(row_of(vbase, pv), hv);
-      }
-      // online softmax (base 2); lane holds rows 4u + i for key column r16
-      float pA[4], pB[4], alpha[4];
-      bool grew = false;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float xa = va ? sa[i] * a.scale_log2 : -__builtin_inff();
-        const float xb = vb ? sb[i] * a.scale_log2 : -__builtin_inff();
-        const float mx = row16_max(fmaxf(xa, xb));
-        const float mn = fmaxf(m[i], mx);
-        const bool empty = mn == -__builtin_inff();
-        grew |= mn > m[i];
-        alpha[i] = empty ? 1.f : __builtin_amdgcn_exp2f(m[i] - mn);
-        pA[i] = empty ? 0.f : __builtin_amdgcn_exp2f(xa - mn);
-        pB[i] = empty ? 0.f : __builtin_amdgcn_exp2f(xb - mn);
-        l[i] = l[i] * alpha[i] + row16_sum(pA[i] + pB[i]);
-        m[i] = mn;
-      }
-      if (__ballot(grew)) {   // rescale only when some row maximum moved
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) o[j][i] *= alpha[i];
-      }
-      // P (bf16) to LDS as [key][head]: 8 contiguous bytes per key and lane
-      {
-        uint2 wa2, wb2;
-        wa2.x = (uint32_t)f32_to_bf16_rne(pA[0]) | ((uint32_t)f32_to_bf16_rne(pA[1]) << 16);
-        wa2.y = (uint32_t)f32_to_bf16_rne(pA[2]) | ((uint32_t)f32_to_bf16_rne(pA[3]) << 16);
-        wb2.x = (uint32_t)f32_to_bf16_rne(pB[0]) | ((uint32_t)f32_to_bf16_rne(pB[1]) << 16);
-        wb2.y = (uint32_t)f32_to_bf16_rne(pB[2]) | ((uint32_t)f32_to_bf16_rne(pB[3]) << 16);
-        *reinterpret_cast<uint2*>(ps + r16 * kPStride + 4 * u) = wa2;
-        *reinterpret_cast<uint2*>(ps + (16 + r16) * kPStride + 4 * u) = wb2;
-      }
-      wave_fence();
-      // O += P V.  A = P: lane row r16 = head, keys [8u, +8); B = V: column
-      // 16j + r16 = dim, keys [8u, +8).  Both come from transposing reads:
-      // source lane s of a group points at key 8u + (s >> 2) (+4), column 4 (s & 3).
-      const int sk = 8 * u + (r16 >> 2), sc = 4 * (r16 & 3);
-      bf16x8 pf;
-      {
-        const uint2 lo = ds_read_tr16(ps + sk * kPStride + sc);
-        const uint2 hi = ds_read_tr16(ps + (sk + 4) * kPStride + sc);
-        pf = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint2 lo = ds_read_tr16(vs + sk * kVStride + 16 * j + sc);
-        const uint2 hi = ds_read_tr16(vs + (sk + 4) * kVStride + 16 * j + sc);
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-        o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf, vf, o[j], 0, 0, 0);
-      }
-      wave_fence();
-    }
-    // write: rows 4u + i < G, dims 16j + r16
-    if (a.splits == 1) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int hr = 4 * u + i;
-        if (hr < a.G) {
-          const float inv = l[i] > 0.f ? 1.f / l[i] : 0.f;
-          uint16_t* orow = a.out + (row * a.Hq + (int64_t)kvh * a.G + hr) * kHeadDim;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) orow[16 * j + r16] = f32_to_bf16_rne(o[j][i] * inv);
-        }
-      }
-    } else {
-      const int64_t slot = row * a.splits + split;
-      float* ob = a.ws;
-      float* mb = a.ws + a.rows * a.splits * a.Hq * kHeadDim;
-      float* lb = mb + a.rows * a.splits * a.Hq;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int hr = 4 * u + i;
-        if (hr < a.G) {
-          const int64_t h = (int64_t)kvh * a.G + hr;
-          float* orow = ob + (slot * a.Hq + h) * kHeadDim;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) orow[16 * j + r16] = o[j][i];
-          // running max back to natural-log units for the combine step
-          if (r16 == 0) { mb[slot * a.Hq + h] = m[i] * 0.6931471805599453f; lb[slot * a.Hq + h] = l[i]; }
-        }
-      }
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
-// Four-KV-head path (Hkv = 4, the shape of the 128K .. 10M workloads),
-// register staged.  Every wave owns one (row, KV head) and streams that
-// head's K and V rows (256 B each per token) on its own: no barrier inside
-// the loop.  Two workgroup shapes (NW waves per workgroup):
-//   NW = 4: one row per workgroup, wave w takes KV head w.  The four waves
-//     read each listed token's whole 1 KiB K and V rows together, the better
-//     pattern once K/V are much larger than the caches (1M, 10M tokens).
-//   NW = 1: one (row, head) per workgroup, and the XCD that a workgroup runs
-//     on (blockIdx.x mod 8) fixes its head: XCDs h and h + 4 serve KV head h,
-//     for the first and second half of the launch's rows.  Each XCD's L2
-//     then holds one head's rows (a quarter of the bytes per token) for four
-//     times as many neighbouring queries, which pays when K/V fit the
-//     Infinity Cache (the 128K workload: 128 MiB each).
+// bf16 attention, register staged.  Every wave owns one (row, KV head) and
+// streams that head's K and V rows (256 B each per token) on its own: no
+// barrier inside the loop.  HKV is the number of KV heads (0: any, read from
+// the arguments; 4, the shape of the 128K .. 10M workloads, as a constant).
+// Two workgroup shapes (NW waves per workgroup):
+//   NW = 4 (HKV = 4): one row per workgroup, wave w takes KV head w.  The
+//     four waves read each listed token's whole 1 KiB K and V rows together,
+//     the better pattern once K/V are much larger than the caches (1M, 10M
+//     tokens).
+//   NW = 1: one (row, head) per workgroup.  When the head count divides 8,
+//     the XCD that a workgroup runs on (blockIdx.x mod 8) fixes its head:
+//     XCDs h, h + Hkv, ... serve KV head h, each for its share of the
+//     launch's rows.  Each XCD's L2 then holds one head's rows for many
+//     neighbouring queries, which pays when K/V fit the Infinity Cache (the
+//     128K workload: 128 MiB each, XCDs h and h + 4 per head, a quarter of
+//     the bytes per token for four times as many queries as with NW = 4).
 // Tiles of 16 tokens are loaded with 16-byte loads, each instruction reading
 // four tokens' whole 256 B head rows (whole cache lines), into a ring of
 // kRing4 register buffers, kRing4 - 1 tiles ahead of the one being computed,
@@ -353,17 +129,25 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
-// grid.x of a launch of nrows rows
-template <int NW>
-int64_t attn_h4_grid(int64_t nrows) {
-  if (NW == 4) return nrows >= 8 ? (nrows + 7) / 8 * 8 : nrows;
-  return nrows >= 8 ? 8 * ((nrows + 1) / 2) : 4 * nrows;
+// NW = 1 with hkv KV heads: whether each XCD serves one head (hkv divides 8)
+__host__ __device__ constexpr bool xcd_per_head(int hkv, int64_t nrows) {
+  return nrows >= 8 && hkv <= 8 && 8 % hkv == 0;
 }
 
+// grid.x of a launch of nrows rows
 template <int NW>
-__global__ __launch_bounds__(64 * NW, 2) void k_attn_bf16_h4(AttnArgs a) {
+int64_t attn_grid(int hkv, int64_t nrows) {
+  if (NW == 4) return nrows >= 8 ? (nrows + 7) / 8 * 8 : nrows;
+  if (xcd_per_head(hkv, nrows)) return 8 * ((nrows + 8 / hkv - 1) / (8 / hkv));
+  return hkv * nrows;
+}
+
+template <int NW, int HKV>
+__global__ __launch_bounds__(64 * NW, 2) void k_attn_bf16(AttnArgs a) {
+  static_assert(NW == 1 || HKV == 4, "one workgroup per row is written for four KV heads");
   extern __shared__ __attribute__((aligned(16))) char lds4[];
   constexpr int NT = 64 * NW, kList = kList4<NW>, kB = kBatch4<NW>;
+  const int hkv = HKV ? HKV : a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = NW == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid >> 6);
   // with 8+ rows, workgroups of consecutive rows (which share many keys) go
@@ -377,13 +161,13 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn_bf16_h4(AttnArgs a) {
       const int64_t per_xcd = (a.nrows + 7) / 8;
       row = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
     }
-  } else if (a.nrows >= 8) {
-    const int x = blockIdx.x & 7;
-    kvh = x & 3;
-    row = (int64_t)(x >> 2) * ((a.nrows + 1) / 2) + (blockIdx.x >> 3);
+  } else if (xcd_per_head(hkv, a.nrows)) {
+    const int x = blockIdx.x & 7, parts = 8 / hkv;
+    kvh = x % hkv;
+    row = (int64_t)(x / hkv) * ((a.nrows + parts - 1) / parts) + (blockIdx.x >> 3);
   } else {
-    row = blockIdx.x >> 2;
-    kvh = blockIdx.x & 3;
+    row = blockIdx.x / hkv;
+    kvh = blockIdx.x % hkv;
   }
   // every wave of the workgroup has the same row, so the return is uniform
   if (row >= a.nrows) return;
@@ -405,8 +189,10 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn_bf16_h4(AttnArgs a) {
   const int k1 = kend < cnt ? kend : cnt;
   const int n = k1 > k0 ? k1 - k0 : 0;
   const int32_t* lst = a.idx + row * (int64_t)a.L + k0;
-  const char* kb = reinterpret_cast<const char*>(a.k + b * a.Tmax * 4 * kHeadDim) + kvh * 256;
-  const char* vb = reinterpret_cast<const char*>(a.v + b * a.Tmax * 4 * kHeadDim) + kvh * 256;
+  // one token's K (or V) row holds all hkv heads: 256 B each
+  const uint64_t tok = (uint64_t)hkv * 256;
+  const char* kb = reinterpret_cast<const char*>(a.k + b * a.Tmax * hkv * kHeadDim) + kvh * 256;
+  const char* vb = reinterpret_cast<const char*>(a.v + b * a.Tmax * hkv * kHeadDim) + kvh * 256;
   char* vt = lds4 + wave * kWave4;
   char* kt = vt + kVTile4;
   int32_t* slist = reinterpret_cast<int32_t*>(lds4 + NW * kWave4);
@@ -512,7 +298,7 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn_bf16_h4(AttnArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int p = j == 0 ? p4.x : (j == 1 ? p4.y : (j == 2 ? p4.z : p4.w));
-        const uint64_t off = (uint64_t)(uint32_t)(p > 0 ? p : 0) * 1024 + 16 * vc;
+        const uint64_t off = (uint64_t)(uint32_t)(p > 0 ? p : 0) * tok + 16 * vc;
         k[j] = *reinterpret_cast<const u32x4_t*>(kb + off);
         v[j] = *reinterpret_cast<const u32x4_t*>(vb + off);
       }
@@ -796,8 +582,9 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
 int64_t attention_launch_rows() { return kRowsPerLaunch; }
 
 bool attention_head_major(int32_t B, int64_t Tmax, int32_t Hkv, int32_t D, int dtype) {
-  if (dtype != LSA_BF16 || Hkv != 4 || D != kHeadDim || B < 0 || Tmax < 0) return false;
-  if (B == 0 || Tmax == 0) return true;
+  if (dtype != LSA_BF16 || Hkv <= 0 || D != kHeadDim || B < 0 || Tmax < 0) return false;
+  // one workgroup per row exists for four KV heads only
+  if (Hkv != 4 || B == 0 || Tmax == 0) return true;
   const int64_t per_token = (int64_t)Hkv * D * 2;   // bytes of one token's row
   return Tmax <= kHeadMajorMaxKvBytes / per_token / B;
 }
@@ -815,48 +602,26 @@ hipError_t launch_attention(const void* q, const void* k, const void* v, int32_t
     a.rows = rows; a.Tq = Tq; a.Tmax = Tmax; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv;
     a.L = L_max; a.splits = splits; a.scale = scale;
     a.scale_log2 = scale * 1.4426950408889634f;
-    if (Hkv == 4) {
-      static bool attr3 = false;
-      if (!attr3) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_attn_bf16_h4<4>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, kLds4<4>);
-        (void)hipGetLastError();
-        attr3 = true;
-      }
-      const bool head_major = attention_head_major(B, Tmax, Hkv, kHeadDim, dtype);
-      for (int64_t r0 = 0; r0 < rows; r0 += kRowsPerLaunch) {
-        a.row0 = r0;
-        a.nrows = (rows - r0) < kRowsPerLaunch ? (rows - r0) : kRowsPerLaunch;
-        if (head_major)
-          hipLaunchKernelGGL(k_attn_bf16_h4<1>, dim3((unsigned)attn_h4_grid<1>(a.nrows),
-                             (unsigned)splits), dim3(64), (size_t)kLds4<1>, s, a);
-        else
-          hipLaunchKernelGGL(k_attn_bf16_h4<4>, dim3((unsigned)attn_h4_grid<4>(a.nrows),
-                             (unsigned)splits), dim3(256), (size_t)kLds4<4>, s, a);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-      }
-      if (splits == 1) return hipSuccess;
-      hipLaunchKernelGGL(k_attn_combine<LSA_BF16>, dim3((unsigned)(rows * Hq * 2)), dim3(256), 0,
-                         s, ws, out, rows, Hq, splits);
-      return hipGetLastError();
-    }
-    const int nw = Hkv < kMaxWaves ? Hkv : kMaxWaves;
     static bool attr_set = false;
     if (!attr_set) {
-      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_attn_bf16),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_attn_bf16<4, 4>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kLds4<4>);
       (void)hipGetLastError();  // advisory; never report it as a launch failure
       attr_set = true;
     }
-    const int per = (L_max + splits - 1) / splits;
-    const size_t smem = (size_t)nw * kWaveLds * sizeof(uint16_t) + (size_t)per * sizeof(int32_t);
+    const bool head_major = attention_head_major(B, Tmax, Hkv, kHeadDim, dtype);
     for (int64_t r0 = 0; r0 < rows; r0 += kRowsPerLaunch) {
       a.row0 = r0;
       a.nrows = (rows - r0) < kRowsPerLaunch ? (rows - r0) : kRowsPerLaunch;
-      const int64_t grid = a.nrows >= 8 ? (a.nrows + 7) / 8 * 8 : a.nrows;
-      hipLaunchKernelGGL(k_attn_bf16, dim3((unsigned)grid, (unsigned)splits), dim3(64 * nw), smem,
-                         s, a);
+      if (Hkv != 4)
+        hipLaunchKernelGGL((k_attn_bf16<1, 0>), dim3((unsigned)attn_grid<1>(Hkv, a.nrows),
+                           (unsigned)splits), dim3(64), (size_t)kLds4<1>, s, a);
+      else if (head_major)
+        hipLaunchKernelGGL((k_attn_bf16<1, 4>), dim3((unsigned)attn_grid<1>(4, a.nrows),
+                           (unsigned)splits), dim3(64), (size_t)kLds4<1>, s, a);
+      else
+        hipLaunchKernelGGL((k_attn_bf16<4, 4>), dim3((unsigned)attn_grid<4>(4, a.nrows),
+                           (unsigned)splits), dim3(256), (size_t)kLds4<4>, s, a);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }

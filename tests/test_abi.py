@@ -127,7 +127,8 @@ def test_attention_host_errors():
     assert hm(1, 131072) and hm(1, 262144) and not hm(1, 262145)
     assert hm(2, 131072) and not hm(2, 131073) and hm(0, 10**9) and hm(7, 0)
     assert not hm(1, 1 << 20) and not hm(16, 1 << 20) and not hm(1, 10**7)
-    assert not hm(1, 4096, dt=lsa.LSA_F32) and not hm(1, 4096, Hkv=8) and not hm(1, 4096, D=64)
+    assert not hm(1, 4096, dt=lsa.LSA_F32) and not hm(1, 4096, D=64) and not hm(1, 4096, Hkv=0)
+    assert hm(1, 4096, Hkv=8) and hm(16, 1 << 20, Hkv=1) and hm(1, 10**7, Hkv=3)
     assert not hm(1 << 30, 1 << 32) and not hm(-1, 4) and not hm(1, -4)
     assert L.lsa_attention_workspace_bytes(1, 16, 32, 128, 1) == 0
     assert L.lsa_attention_workspace_bytes(1, 16, 32, 128, 4) == 16 * 4 * 32 * 130 * 4

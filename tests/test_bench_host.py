@@ -13,7 +13,7 @@ import bench  # noqa: E402
 import lsa_synth as S  # noqa: E402
 import sparse_attention_indexing_amd as lsa  # noqa: E402
 
-KERNEL, WORKLOAD = "k_attn_bf16_h4<1>", "prefill_t128k_bf16_flat"
+KERNEL, WORKLOAD = "k_attn_bf16<1, 4>", "prefill_t128k_bf16_flat"
 
 
 def test_workload_names():
@@ -26,8 +26,8 @@ def test_attention_kernel_names():
     # the 128K workload's caches take one workgroup per (row, KV head), the 1M
     # and 10M ones one workgroup per row
     assert bench.attention_kernel_name(lsa, S.WORKLOADS[2], 1, S.WORKLOADS[2].T) == KERNEL
-    assert bench.attention_kernel_name(lsa, S.WORKLOADS[4], 1, S.WORKLOADS[4].T) == "k_attn_bf16_h4<4>"
-    assert bench.attention_kernel_name(lsa, S.WORKLOADS[5], 1, S.WORKLOADS[5].T) == "k_attn_bf16_h4<4>"
+    assert bench.attention_kernel_name(lsa, S.WORKLOADS[4], 1, S.WORKLOADS[4].T) == "k_attn_bf16<4, 4>"
+    assert bench.attention_kernel_name(lsa, S.WORKLOADS[5], 1, S.WORKLOADS[5].T) == "k_attn_bf16<4, 4>"
     assert bench.attention_kernel_name(lsa, S.WORKLOADS[1], 1, 4096) == "k_attn_f32"
 
 
@@ -38,6 +38,6 @@ def test_committed_traffic_matches_the_committed_kernel():
     t = bench.measured_traffic(KERNEL, WORKLOAD, rows)
     assert t is not None and t > 1e8
     # any other instance, launch size or workload has no figure
-    assert bench.measured_traffic("k_attn_bf16_h4<4>", WORKLOAD, rows) is None
+    assert bench.measured_traffic("k_attn_bf16<4, 4>", WORKLOAD, rows) is None
     assert bench.measured_traffic(KERNEL, WORKLOAD, 2 * rows) is None
     assert bench.measured_traffic(KERNEL, "prefill_t10m_q32k_bf16_flat", rows) is None

@@ -376,6 +376,42 @@ def test_attention_invalid_entries_ragged_counts_and_scale(scale, splits, row_la
     assert err <= 2e-2
 
 
+def _bf16_normal(rng, shape):
+    """Seeded normal values rounded to bf16 (nearest even): (float64 values, bf16 bits)."""
+    u = rng.standard_normal(shape).astype(np.float32).view(np.uint32)
+    bits = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    vals = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return vals, bits
+
+
+@pytest.mark.parametrize("Hq,Hkv,nrows,splits", [
+    (16, 1, 40, 1), (8, 2, 40, 3), (32, 8, 40, 1), (24, 3, 12, 1), (32, 2, 5, 4),
+    (16, 16, 20, 1), (64, 4, 40, 1), (64, 4, 6, 2)])
+def test_attention_bf16_gqa_shapes(Hq, Hkv, nrows, splits):
+    """Other GQA shapes (1 to 16 KV heads, 1 to 16 query heads per KV head):
+    one workgroup per (row, KV head), each XCD serving one head when Hkv
+    divides 8, with many rows and with few (whose splits spread over the
+    XCDs)."""
+    say(f"case: attention bf16 Hq={Hq} Hkv={Hkv} rows={nrows} splits={splits}")
+    D, T, L = 128, 3000, 900
+    assert lsa.attention_head_major(1, T, Hkv, D, lsa.LSA_BF16)
+    rng = np.random.default_rng(Hq * 100 + Hkv)
+    q, qb = _bf16_normal(rng, (nrows, Hq, D))
+    k, kb = _bf16_normal(rng, (T, Hkv, D))
+    v, vb = _bf16_normal(rng, (T, Hkv, D))
+    rows = np.linspace(T // 3, T - 1, nrows).astype(int)
+    idx, cnt = _random_lists(rng, rows, L, short=(1,))
+    out = lsa.sparse_attention(bf16_tensor(qb).cuda(), bf16_tensor(kb).cuda(),
+                               bf16_tensor(vb).cuda(), torch.from_numpy(idx).cuda(),
+                               torch.from_numpy(cnt).cuda(), splits=splits)
+    torch.cuda.synchronize()
+    out = out.float().cpu().numpy()
+    err = max(np.abs(out[i] - O.attention_query(q[i], k, v, idx[i], cnt[i])).max()
+              for i in range(nrows))
+    say("attention bf16 max abs err", err)
+    assert err <= 2e-2
+
+
 @pytest.mark.parametrize("row_layout", [False, True])
 def test_attention_batched_rows_across_launches(row_layout):
     """Two sequences of 1,500 query rows each, each with its own K/V: 3,000
