@@ -31,8 +31,11 @@
  *     are independent.
  *   - Supported shapes: d_latent 64, n_pool 4, block 512, 64 buckets per
  *     block, bucket cap 16 keys, head_dim 128, Hq % Hkv == 0,
- *     Hq / Hkv <= 16, 0 <= k <= 8192, 0 <= n_sink, 1 <= window <= 8192.
- *     Anything else returns LSA_ERR_UNSUPPORTED.
+ *     Hq / Hkv <= 16, 0 <= k <= 8192, 0 <= n_sink <= 8192,
+ *     1 <= window <= 8192, and 3 * lsa_top_buckets(p) <= 8192 (the
+ *     candidates of one query fit one workgroup's LDS; this holds for every
+ *     k with the default window and sinks).  Anything else returns
+ *     LSA_ERR_UNSUPPORTED.
  */
 #ifndef LSA_H
 #define LSA_H
@@ -73,7 +76,7 @@ typedef struct {
   int32_t mode;            /* LSA_FLAT or LSA_TREE (cache: build a tree too) */
   int32_t beam;            /* tree beam width, 1..64 */
   int32_t leaf_level;      /* tree: level where the beam stops; -1 = smallest l
-                              with beam * 2^l >= ceil(k/4) + 65 */
+                              with beam * 2^l >= lsa_top_buckets(p) */
   int32_t index_dtype;     /* stored centroids and normalised queries: LSA_F32 | LSA_BF16 */
   int32_t exact_select;    /* 0: sampled threshold + exact fallback; 1: always exact */
 } lsa_params;
@@ -90,9 +93,17 @@ int lsa_check_params(const lsa_params* p);
 /* Index list length n_sink + window + k (or a negative status). */
 int32_t lsa_list_len(const lsa_params* p);
 
-/* Buckets kept per query before expansion: ceil(k / n_pool) + n_buckets + 1.
- * This many always suffice: each bucket that avoids the sinks and the window
- * gives at least n_pool keys, and at most n_buckets + 1 buckets touch them. */
+/* Buckets kept per query before expansion:
+ *   B = ceil(k / n_pool) + n_buckets * ceil((window - 1) / block_keys)
+ *       + ceil(n_sink / n_pool)
+ * (ceil(k / 4) + 65 for the default window of 512 and 4 sinks).  The B best
+ * buckets always hold k far keys, or every eligible bucket is kept: a bucket
+ * holding no sink or window key gives at least n_pool far keys, and the
+ * window reaches back into at most ceil((window - 1) / block_keys) eligible
+ * blocks of n_buckets buckets, the sinks into ceil(n_sink / n_pool) buckets
+ * ([72x "The same steps in general"]: keys of an opened bucket that are
+ * already sinks or window keys are skipped and the next key takes their
+ * place, so opening stops only once k far keys are taken). */
 int32_t lsa_top_buckets(const lsa_params* p);
 
 /* ---------------------------------------------------------------- cache --
@@ -156,6 +167,17 @@ int build_bucket_cache(lsa_cache* c, const float* latent_keys, int64_t n_new, vo
  * Workspace for lsa_index_prefill with up to max_queries queries, or for
  * lsa_index_decode with a batch of max_queries sequences. */
 int64_t lsa_index_workspace_bytes(const lsa_params* p, int64_t max_queries);
+
+/* Byte offset, inside the workspace of an lsa_index_prefill call over
+ * n_queries queries (or an lsa_index_decode call over n_queries sequences),
+ * of the int32 flag per query that the call leaves behind: 1 when that
+ * query's B best buckets were selected by the exact fallback (its
+ * candidate list from the sampled score threshold held fewer than B or more
+ * candidates than fit, so every eligible bucket was rescored in one
+ * workgroup), 0 otherwise (always 1 with exact_select).  The flags stay
+ * valid, once the stream has passed the call, until the workspace is
+ * reused.  Negative status on invalid parameters. */
+int64_t lsa_index_status_offset(const lsa_params* p, int64_t n_queries);
 
 /*
  * lsa_index_prefill: index lists for the Tq queries at positions

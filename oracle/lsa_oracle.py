@@ -33,7 +33,9 @@ the design notes of the repository):
   * tree: pairing inside consecutive groups of 128 nodes of the level below,
     points = stored unit centroids with weight 1, leftover node copied up;
     beam on levels >= l*, then flat ranking of all eligible buckets under the
-    final beam (l* = smallest l with beam * 2^l >= ceil(k/4) + 65).
+    final beam (l* = smallest l with beam * 2^l >= top_b, the bucket count
+    that provably holds k far keys: ceil(k/4) + 65 for the default window
+    and sinks).
 
 Pins (tests marked "not gpu"): brute-force ESS for the Ward cost, SciPy's Ward
 linkage when the cap is off, the telescoping ESS invariant, exhaustive greedy
@@ -81,8 +83,18 @@ class Params:
 
     @property
     def top_b(self) -> int:
-        """Buckets that provably suffice for k far keys: ceil(k / n_pool) + 65."""
-        return -(-self.k // self.n_pool) + self.n_buckets + 1
+        """Buckets that provably hold k far keys when ranked best-first.
+
+        A bucket with no sink or window key gives at least n_pool far keys, so
+        ceil(k / n_pool) such buckets suffice.  The buckets that can hold a
+        sink or window key are counted on top: every bucket of each eligible
+        block the window reaches back into (ceil((window - 1) / block) blocks)
+        and one bucket per pooled item of the sinks (ceil(n_sink / n_pool)).
+        With the default window of 512 and 4 sinks this is ceil(k / 4) + 65.
+        """
+        win_blocks = -(-(self.window - 1) // self.block)
+        return (-(-self.k // self.n_pool) + self.n_buckets * win_blocks
+                + -(-self.n_sink // self.n_pool))
 
 
 # --------------------------------------------------------------------------
@@ -330,7 +342,7 @@ def build_tree(cache: BucketCache, dtype: str | None = None) -> Tree:
 
 
 def leaf_level(prm: Params) -> int:
-    """Smallest l with beam * 2^l >= ceil(k / n_pool) + 65 (beam levels stop there)."""
+    """Smallest l with beam * 2^l >= top_b (beam levels stop there)."""
     if prm.leaf_level >= 0:
         return prm.leaf_level
     l = 0

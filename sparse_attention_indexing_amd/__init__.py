@@ -14,8 +14,7 @@ from dataclasses import dataclass, fields
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-# LSA_LIBRARY selects another build of the same library (same C ABI)
-LIB_PATH = os.environ.get("LSA_LIBRARY") or os.path.join(_PKG, "liblsa.so")
+LIB_PATH = os.path.join(_PKG, "liblsa.so")
 
 LSA_F32, LSA_BF16 = 0, 1
 LSA_FLAT, LSA_TREE = 0, 1
@@ -91,6 +90,7 @@ def lib():
         "lsa_cache_get_view": (ctypes.c_int, [vp, ctypes.POINTER(_View)]),
         "build_bucket_cache": (ctypes.c_int, [vp, vp, i64, vp]),
         "lsa_index_workspace_bytes": (i64, [P, i64]),
+        "lsa_index_status_offset": (i64, [P, i64]),
         "lsa_index_prefill": (ctypes.c_int, [vp, vp, i64, i64, P, vp, vp, vp, vp, i64, vp]),
         "lsa_index_decode": (ctypes.c_int, [ctypes.POINTER(vp), i32, vp, vp, P, vp, vp, vp, i64, vp]),
         "lsa_attention_workspace_bytes": (i64, [i32, i64, i32, i32, i32]),
@@ -141,6 +141,13 @@ def top_buckets(p: Params) -> int:
 
 def index_workspace_bytes(p: Params, n: int) -> int:
     return _check("lsa_index_workspace_bytes", lib().lsa_index_workspace_bytes(ctypes.byref(p.c()), n))
+
+
+def exact_fallbacks(p: Params, n: int, workspace: torch.Tensor) -> int:
+    """How many of the n queries of the last index call on `workspace` had their
+    bucket selection redone exactly (lsa_index_status_offset).  Synchronises."""
+    off = _check("lsa_index_status_offset", lib().lsa_index_status_offset(ctypes.byref(p.c()), n))
+    return int(workspace[off:off + 4 * n].view(torch.int32).sum().item())
 
 
 class BucketCache:
@@ -200,8 +207,10 @@ class BucketCache:
 
 def index_prefill(cache: BucketCache, latent_q: torch.Tensor, q_start: int, p: Params,
                   ranked: bool = False, workspace: torch.Tensor | None = None,
-                  out: tuple | None = None):
-    """lsa_index_prefill -> (idx [Tq, L] int32, count [Tq] int32[, ranked [Tq, B]])."""
+                  out: tuple | None = None, stats: dict | None = None):
+    """lsa_index_prefill -> (idx [Tq, L] int32, count [Tq] int32[, ranked [Tq, B]]).
+    With `stats`, stats["exact_fallbacks"] receives the number of queries whose
+    bucket selection took the exact fallback (this synchronises)."""
     _need(latent_q, torch.float32, "latent_q")
     Tq = latent_q.shape[0]
     L = list_len(p)
@@ -218,12 +227,17 @@ def index_prefill(cache: BucketCache, latent_q: torch.Tensor, q_start: int, p: P
     _check("lsa_index_prefill", lib().lsa_index_prefill(
         cache.handle, _ptr(latent_q), q_start, Tq, ctypes.byref(p.c()), _ptr(idx), _ptr(cnt),
         _ptr(rk), _ptr(workspace), workspace.numel(), ctypes.c_void_p(_stream())))
+    if stats is not None:
+        stats["exact_fallbacks"] = exact_fallbacks(p, Tq, workspace)
     return (idx, cnt, rk) if ranked else (idx, cnt)
 
 
 def index_decode(caches: list, latent_q: torch.Tensor, latent_k_new: torch.Tensor, p: Params,
-                 workspace: torch.Tensor | None = None, out: tuple | None = None):
-    """lsa_index_decode -> (idx [B, L] int32, count [B] int32)."""
+                 workspace: torch.Tensor | None = None, out: tuple | None = None,
+                 stats: dict | None = None):
+    """lsa_index_decode -> (idx [B, L] int32, count [B] int32).  With `stats`,
+    stats["exact_fallbacks"] receives the number of sequences whose bucket
+    selection took the exact fallback (this synchronises)."""
     _need(latent_q, torch.float32, "latent_q")
     _need(latent_k_new, torch.float32, "latent_k_new")
     B = len(caches)
@@ -241,6 +255,8 @@ def index_decode(caches: list, latent_q: torch.Tensor, latent_k_new: torch.Tenso
     _check("lsa_index_decode", lib().lsa_index_decode(
         arr, B, _ptr(latent_q), _ptr(latent_k_new), ctypes.byref(p.c()), _ptr(idx), _ptr(cnt),
         _ptr(workspace), workspace.numel(), ctypes.c_void_p(_stream())))
+    if stats is not None:
+        stats["exact_fallbacks"] = exact_fallbacks(p, B, workspace)
     return idx, cnt
 
 
@@ -293,5 +309,6 @@ def attention_head_major(B: int, Tmax: int, Hkv: int, D: int, dtype: int) -> boo
 
 __all__ = ["Params", "BucketCache", "index_prefill", "index_decode", "sparse_attention",
            "attention_launch_rows", "attention_head_major",
-           "list_len", "top_buckets", "index_workspace_bytes", "lib", "LsaError",
+           "list_len", "top_buckets", "index_workspace_bytes", "exact_fallbacks", "lib",
+           "LsaError",
            "LSA_F32", "LSA_BF16", "LSA_FLAT", "LSA_TREE"]

@@ -46,7 +46,15 @@ int check_query(const lsa_params* p) {
   return LSA_OK;
 }
 
-int32_t top_b(const lsa_params* p) { return (p->k + kPool - 1) / kPool + kBuckets + 1; }
+// Buckets kept per query before expansion.  A bucket without a sink or
+// window key gives at least kPool far keys; on top of ceil(k / kPool) such
+// buckets come every bucket that can hold a sink or window key: all buckets
+// of each eligible block the window reaches back into, and one per pooled
+// item of the sinks.  (Default window 512 and 4 sinks: ceil(k / 4) + 65.)
+int32_t top_b(const lsa_params* p) {
+  const int32_t win_blocks = (p->window - 1 + kBlock - 1) / kBlock;
+  return (p->k + kPool - 1) / kPool + kBuckets * win_blocks + (p->n_sink + kPool - 1) / kPool;
+}
 
 // candidate slots per query: a power of two >= 3 B (tau aims at ~2 B)
 int32_t cand_cap(const lsa_params* p) {
@@ -304,6 +312,8 @@ int lsa_check_params(const lsa_params* p) {
   if (rc) return rc;
   rc = check_query(p);
   if (rc) return rc;
+  // the selection holds every candidate of a query in one workgroup's LDS
+  if (cand_cap(p) > kMaxCap) return LSA_ERR_UNSUPPORTED;
   if (p->mode == LSA_TREE && ((int64_t)p->beam << leaf_level(p)) > cand_cap(p))
     return LSA_ERR_UNSUPPORTED;
   return LSA_OK;
@@ -397,6 +407,13 @@ int64_t lsa_index_workspace_bytes(const lsa_params* p, int64_t max_queries) {
   if (rc) return rc;
   if (max_queries < 0) return LSA_ERR_ARG;
   return index_ws_layout(p, max_queries).total;
+}
+
+int64_t lsa_index_status_offset(const lsa_params* p, int64_t n_queries) {
+  int rc = lsa_check_params(p);
+  if (rc) return rc;
+  if (n_queries < 0) return LSA_ERR_ARG;
+  return index_ws_layout(p, n_queries).off_status;
 }
 
 int lsa_index_prefill(const lsa_cache* c, const float* latent_q, int64_t q_start, int64_t Tq,

@@ -22,6 +22,7 @@ constexpr int kMaxWindow = 8192;
 constexpr int kHeadDim = 128;
 constexpr int kMaxSeq = 32;        // sequences per batched decode launch
 constexpr int kMaxBeam = 64;
+constexpr int kMaxCap = 8192;      // candidate slots per query (power of two >= 3 B)
 constexpr int kSampleStride = 16;  // threshold sample: every 16th tile of 32 buckets
 
 // ---------------------------------------------------------------- numerics

@@ -13,6 +13,24 @@ import sparse_attention_indexing_amd as lsa
 from oracle import lsa_oracle as O
 
 
+class FallbackReport:
+    """A `stats` sink for the binding's index calls: prints, for every call,
+    how many queries took the exact top-B fallback (their candidate list from
+    the sampled threshold was unusable), and keeps the running total."""
+
+    def __init__(self):
+        self.total = 0
+        self.calls = 0
+
+    def __setitem__(self, key, value):
+        self.total += value
+        self.calls += 1
+        print(f"index call {self.calls}: {key} = {value} (running total {self.total})", flush=True)
+
+
+FB = FallbackReport()
+
+
 def oracle_params(p: lsa.Params) -> O.Params:
     return O.Params(k=p.k, n_sink=p.n_sink, window=p.window,
                     index_dtype="bf16" if p.index_dtype == lsa.LSA_BF16 else "f32",
@@ -78,6 +96,29 @@ def compare_cache(g: dict, oc: O.BucketCache, X: np.ndarray) -> dict:
         assert np.array_equal(g["cent"][b * 64:(b + 1) * 64], oc.centroids[b * 64:(b + 1) * 64]), \
             f"block {b}: centroids differ"
     return dict(blocks=nb, exempt=exempt, exempt_mismatched=mismatched)
+
+
+def compare_tree(g: dict, ot: O.Tree, gap: float, label: str = "") -> int:
+    """Tree levels bit-exact (children, smallest block, centroids) from level 1
+    up to the first level where some group's pairing decision has a gap below
+    `gap` (a near tie, where both pairings are correct and everything above may
+    differ); the levels above are checked for structure only.  Prints and
+    returns the number of levels compared exactly."""
+    assert len(g["levels"]) == ot.height
+    exact = 0
+    for l, lv in enumerate(g["levels"], start=1):
+        n_below = ot.levels[l - 1]["cent"].shape[0]
+        kids = lv["child"][lv["child"] >= 0]
+        assert sorted(kids.tolist()) == list(range(n_below)), f"level {l}: not one parent per node"
+        if exact == l - 1 and ot.group_min_gap[l - 1] >= gap:
+            assert np.array_equal(lv["child"], ot.levels[l]["child"]), f"level {l} children"
+            assert np.array_equal(lv["min_block"], ot.levels[l]["min_block"]), f"level {l} min_block"
+            assert np.array_equal(lv["cent"], ot.levels[l]["cent"]), f"level {l} centroids"
+            exact = l
+    print(f"{label} tree levels compared bit for bit: {exact} of {ot.height}"
+          + ("" if exact == ot.height else
+             f" (level {exact + 1} has a pairing gap of {ot.group_min_gap[exact]:.3g})"), flush=True)
+    return exact
 
 
 def check_list_invariants(lst: np.ndarray, cnt: int, p: int, prm: O.Params):

@@ -55,6 +55,25 @@ def test_sizes():
     assert lsa.list_len(_p(k=4096)) == 4612
     assert lsa.top_buckets(_p(k=2048)) == 512 + 65
     assert lsa.top_buckets(_p(k=4096)) == 1089
+    # the window's eligible blocks and the sinks' pooled items, worked by hand:
+    # window 2,048 reaches back into ceil(2,047 / 512) = 4 eligible blocks
+    assert lsa.top_buckets(_p(k=256, window=2048)) == 64 + 4 * 64 + 1
+    assert lsa.top_buckets(_p(k=2048, n_sink=64)) == 512 + 64 + 16
+    assert lsa.top_buckets(_p(k=2048, n_sink=0, window=1)) == 512        # only the query itself
+    assert lsa.top_buckets(_p(k=2048, n_sink=5, window=513)) == 512 + 64 + 2
+    assert lsa.top_buckets(_p(k=2048, window=514)) == 512 + 128 + 1
+    # every candidate of a query must fit one workgroup: 3 B <= 8,192
+    assert lsa.top_buckets(_p(k=8192, window=4096)) == 2048 + 512 + 1
+    from oracle import lsa_oracle as O
+    for k in (0, 1, 255, 2048, 4096):
+        for window in (1, 2, 511, 512, 513, 1024, 2048):
+            for n_sink in (0, 1, 4, 5, 64):
+                assert lsa.top_buckets(_p(k=k, window=window, n_sink=n_sink)) == O.Params(
+                    k=k, window=window, n_sink=n_sink).top_b, (k, window, n_sink)
+    L = lsa.lib()
+    for bad in [dict(k=8192, window=8192), dict(k=8192, n_sink=8192), dict(k=4096, window=8192,
+                                                                          n_sink=8192)]:
+        assert L.lsa_check_params(ctypes.byref(_p(**bad).c())) == -2, bad
     L = lsa.lib()
     flat = L.lsa_cache_bytes(ctypes.byref(_p().c()), 1 << 20)
     tree = L.lsa_cache_bytes(ctypes.byref(_p(mode=lsa.LSA_TREE).c()), 1 << 20)

@@ -12,9 +12,9 @@ import torch
 import lsa_synth as S
 import sparse_attention_indexing_amd as lsa
 from oracle import lsa_oracle as O
-from parity_util import (bf16_tensor, cache_to_host, check_list_invariants, compare_cache,
-                         oracle_cache_parallel,
-                         compare_lists, gpu_cache, oracle_params)
+from parity_util import (FB, bf16_tensor, cache_to_host, check_list_invariants, compare_cache,
+                         compare_lists, compare_tree, gpu_cache, oracle_cache_parallel,
+                         oracle_params)
 
 pytestmark = pytest.mark.gpu
 
@@ -83,7 +83,7 @@ def test_index_c1_all_queries():
     say("case: index T=4096 f32 all queries")
     w, X, Y, p = _c1()
     c = gpu_cache(X, p)
-    idx, cnt = lsa.index_prefill(c, torch.from_numpy(Y).cuda(), 0, p)
+    idx, cnt = lsa.index_prefill(c, torch.from_numpy(Y).cuda(), 0, p, stats=FB)
     torch.cuda.synchronize()
     oc = O.build_cache(X, oracle_params(p))
     rep = compare_lists(idx.cpu().numpy(), cnt.cpu().numpy(), range(4096), Y, oc)
@@ -100,7 +100,7 @@ def test_index_sampled_threshold(k, exact):
     X, Y, _ = S.latent_inputs(w, T=T, query_rows=(0, T))
     p = lsa.Params(k=k, index_dtype=lsa.LSA_BF16, exact_select=exact)
     c = gpu_cache(X, p)
-    idx, cnt = lsa.index_prefill(c, torch.from_numpy(Y).cuda(), 0, p)
+    idx, cnt = lsa.index_prefill(c, torch.from_numpy(Y).cuda(), 0, p, stats=FB)
     torch.cuda.synchronize()
     oc = O.build_cache(X, oracle_params(p))
     pos = np.unique(np.concatenate([np.arange(0, T, 61), np.arange(T - 64, T), [511, 512, 513]]))
@@ -119,7 +119,7 @@ def test_index_few_queries(k, exact):
     X, Y, _ = S.latent_inputs(w, T=T, query_rows=(T - Tq, T))
     p = lsa.Params(k=k, index_dtype=lsa.LSA_BF16, exact_select=exact)
     c = gpu_cache(X, p)
-    idx, cnt, rk = lsa.index_prefill(c, torch.from_numpy(Y).cuda(), T - Tq, p, ranked=True)
+    idx, cnt, rk = lsa.index_prefill(c, torch.from_numpy(Y).cuda(), T - Tq, p, ranked=True, stats=FB)
     torch.cuda.synchronize()
     oc = O.build_cache(X, oracle_params(p))
     rows = np.arange(0, Tq, 3)
@@ -145,8 +145,8 @@ def test_index_last_chunk_and_determinism():
     p = lsa.Params(k=512, index_dtype=lsa.LSA_BF16)
     c = gpu_cache(X, p)
     Yd = torch.from_numpy(Y).cuda()
-    a = lsa.index_prefill(c, Yd, T - Tq, p)
-    b = lsa.index_prefill(c, Yd, T - Tq, p)
+    a = lsa.index_prefill(c, Yd, T - Tq, p, stats=FB)
+    b = lsa.index_prefill(c, Yd, T - Tq, p, stats=FB)
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
     oc = O.build_cache(X, oracle_params(p))
@@ -164,11 +164,51 @@ def test_index_lowpass_last_chunk():
     X, Y, _ = S.latent_inputs(w, T=T, query_rows=(T - Tq, T))
     p = lsa.Params(k=16, index_dtype=lsa.LSA_BF16)
     c = gpu_cache(X, p)
-    idx, cnt = lsa.index_prefill(c, torch.from_numpy(Y).cuda(), T - Tq, p)
+    idx, cnt = lsa.index_prefill(c, torch.from_numpy(Y).cuda(), T - Tq, p, stats=FB)
     torch.cuda.synchronize()
     oc = oracle_cache_parallel(X, oracle_params(p))
     rows = np.unique(np.concatenate([np.arange(0, Tq, 29), np.arange(Tq - 8, Tq)]))
     rep = compare_lists(idx.cpu().numpy()[rows], cnt.cpu().numpy()[rows], T - Tq + rows, Y[rows], oc)
+    say("index", rep)
+
+
+@pytest.mark.parametrize("window,n_sink", [(2048, 4), (1000, 9), (1, 0)])
+def test_index_c1_other_windows_and_sinks_all_queries(window, n_sink):
+    """Every query of the 4K workload with windows other than 512 and other sink
+    counts.  With a window of 2,048 a query at the end of a block reads three
+    whole eligible blocks of recent keys in its window, which are also the
+    buckets it scores best; the kept bucket count grows with the window
+    (ceil(k/4) + 64 * ceil((window - 1) / 512) + ceil(n_sink / 4)), so the
+    list still holds k far keys, exactly the oracle's."""
+    say(f"case: index T=4096 f32 all queries window={window} n_sink={n_sink}")
+    w, X, Y, p = _c1()
+    p.window, p.n_sink = window, n_sink
+    c = gpu_cache(X, p)
+    idx, cnt = lsa.index_prefill(c, torch.from_numpy(Y).cuda(), 0, p, stats=FB)
+    torch.cuda.synchronize()
+    oc = O.build_cache(X, oracle_params(p))
+    rep = compare_lists(idx.cpu().numpy(), cnt.cpu().numpy(), range(4096), Y, oc)
+    say("index", rep)
+
+
+@pytest.mark.parametrize("window,n_sink,k", [(2048, 4, 256), (2048, 64, 2048), (512, 64, 256),
+                                             (700, 1, 1000)])
+def test_index_bf16_other_windows_and_sinks(window, n_sink, k):
+    """The bf16 prefill kernels (sampled threshold, high- and low-pass scoring,
+    selection) at T=32,768 with other windows and sink counts; queries at the
+    end of every block are included."""
+    say(f"case: index T=32768 bf16 window={window} n_sink={n_sink} k={k}")
+    w = S.WORKLOADS[2]
+    T = 32768
+    X, Y, _ = S.latent_inputs(w, T=T, query_rows=(0, T))
+    p = lsa.Params(k=k, window=window, n_sink=n_sink, index_dtype=lsa.LSA_BF16)
+    c = gpu_cache(X, p)
+    idx, cnt = lsa.index_prefill(c, torch.from_numpy(Y).cuda(), 0, p, stats=FB)
+    torch.cuda.synchronize()
+    oc = O.build_cache(X, oracle_params(p))
+    pos = np.unique(np.concatenate([np.arange(0, T, 211), np.arange(511, T, 512),
+                                    np.arange(T - 16, T), [0, 1, 63, 64, 65]]))
+    rep = compare_lists(idx.cpu().numpy()[pos], cnt.cpu().numpy()[pos], pos, Y[pos], oc)
     say("index", rep)
 
 
@@ -249,7 +289,7 @@ def test_attention_across_launches():
     c = gpu_cache(X, p)
     q, k, v, qb, kb, vb = _qkv_host(w, T, np.arange(q0, T))
     Q = bf16_tensor(qb).cuda().view(Tq, w.Hq, w.D)
-    idx, cnt = lsa.index_prefill(c, torch.from_numpy(Y).cuda(), q0, p)
+    idx, cnt = lsa.index_prefill(c, torch.from_numpy(Y).cuda(), q0, p, stats=FB)
     n = lsa.attention_launch_rows()
     assert Tq > 2 * n
     parts = [(n - 5, n + 5), (2 * n - 3, 2 * n + 9), (Tq - 7, Tq)]
@@ -457,7 +497,7 @@ def test_end_to_end_c1():
     say("case: end-to-end T=4096 f32")
     w, X, Y, p = _c1()
     c = gpu_cache(X, p)
-    idx, cnt = lsa.index_prefill(c, torch.from_numpy(Y).cuda(), 0, p)
+    idx, cnt = lsa.index_prefill(c, torch.from_numpy(Y).cuda(), 0, p, stats=FB)
     q, k, v, *_ = _qkv_host(w, 4096, np.arange(4096))
     out = lsa.sparse_attention(torch.from_numpy(q).cuda(), torch.from_numpy(k).cuda(),
                                torch.from_numpy(v).cuda(), idx, cnt)
@@ -476,28 +516,50 @@ def test_end_to_end_c1():
 
 # ---------------------------------------------------------------- tree
 
-def test_tree_build_and_search():
-    say("case: tree T=65536")
+@pytest.fixture(scope="module")
+def tree_65k():
+    """A tree-mode cache of 65,536 keys built in three appends, and the oracle's
+    cache and tree over the same keys."""
     w = S.WORKLOADS[4]
     T = 65536
     X, Y, _ = S.latent_inputs(w, T=T, query_rows=(T - 2048, T))
     p = lsa.Params(k=256, index_dtype=lsa.LSA_BF16, mode=lsa.LSA_TREE, beam=64)
     c = gpu_cache(X, p, chunks=[30000, 512, T - 30512])
-    g = cache_to_host(c)
     oc = O.build_cache(X, oracle_params(p))
-    compare_cache(g, oc, X)
-    ot = O.build_tree(oc)
-    assert len(g["levels"]) == ot.height
-    if min(ot.group_min_gap) > 1e-9:
-        for l, lv in enumerate(g["levels"], start=1):
-            assert np.array_equal(lv["child"], ot.levels[l]["child"]), f"level {l} children"
-            assert np.array_equal(lv["min_block"], ot.levels[l]["min_block"]), f"level {l} min_block"
-            assert np.array_equal(lv["cent"], ot.levels[l]["cent"]), f"level {l} centroids"
-    idx, cnt = lsa.index_prefill(c, torch.from_numpy(Y).cuda(), T - 2048, p)
+    return dict(T=T, X=X, Y=Y, c=c, oc=oc, ot=O.build_tree(oc))
+
+
+def test_tree_build_and_search(tree_65k):
+    say("case: tree T=65536")
+    t = tree_65k
+    g = cache_to_host(t["c"])
+    compare_cache(g, t["oc"], t["X"])
+    # the seeded inputs have no near-tie pairing: every level is compared
+    assert compare_tree(g, t["ot"], 1e-9, "T=65536") == t["ot"].height
+
+
+@pytest.mark.parametrize("beam,leaf,window,n_sink", [
+    (64, -1, 512, 4), (16, -1, 512, 4), (8, -1, 512, 4), (64, 3, 512, 4), (16, 6, 512, 4),
+    (1, 0, 512, 4), (64, -1, 2048, 64)])
+def test_tree_search_parameters(tree_65k, beam, leaf, window, n_sink):
+    """Tree search with narrower beams, the beam stopped one or more levels
+    above the automatic level l* (the two-stage search), a single-node beam
+    down to the buckets, and a wider window with more sinks (which raises B
+    and so l*): lists against the oracle's tree search."""
+    say(f"case: tree search T=65536 beam={beam} leaf_level={leaf} window={window} n_sink={n_sink}")
+    t = tree_65k
+    T = t["T"]
+    p = lsa.Params(k=256, index_dtype=lsa.LSA_BF16, mode=lsa.LSA_TREE, beam=beam, leaf_level=leaf,
+                   window=window, n_sink=n_sink)
+    idx, cnt = lsa.index_prefill(t["c"], torch.from_numpy(t["Y"]).cuda(), T - 2048, p, stats=FB)
     torch.cuda.synchronize()
-    rows = np.arange(0, 2048, 29)
-    rep = compare_lists(idx.cpu().numpy()[rows], cnt.cpu().numpy()[rows], T - 2048 + rows, Y[rows],
-                        oc, mode="tree", tree=ot)
+    oc = t["oc"]
+    oc_q = O.BucketCache(oracle_params(p), oc.n_blocks, oc.centroids, oc.members, oc.pooled,
+                         oc.block_min_gap, oc.block_ess)
+    say("l* =", O.leaf_level(oc_q.params), "B =", oc_q.params.top_b)
+    rows = np.unique(np.concatenate([np.arange(0, 2048, 29), np.arange(511, 2048, 512)]))
+    rep = compare_lists(idx.cpu().numpy()[rows], cnt.cpu().numpy()[rows], T - 2048 + rows,
+                        t["Y"][rows], oc_q, mode="tree", tree=t["ot"])
     say("tree index", rep)
 
 
@@ -532,12 +594,12 @@ def test_chunked_whole_context_prefill(mode):
     bounds = [(s0, min(T, s0 + C)) for s0 in range(0, T, C)]
     for s0, s1 in bounds:
         c.build(Xd[s0:s1].contiguous())
-        lsa.index_prefill(c, Yd[s0:s1].contiguous(), s0, p, out=(idx[s0:s1], cnt[s0:s1]))
+        lsa.index_prefill(c, Yd[s0:s1].contiguous(), s0, p, out=(idx[s0:s1], cnt[s0:s1]), stats=FB)
     torch.cuda.synchronize()
     oc = O.build_cache(X, oracle_params(p))
     if mode == lsa.LSA_FLAT:
         c2 = gpu_cache(X, p)
-        idx2, cnt2 = lsa.index_prefill(c2, Yd, 0, p)
+        idx2, cnt2 = lsa.index_prefill(c2, Yd, 0, p, stats=FB)
         torch.cuda.synchronize()
         assert torch.equal(idx, idx2) and torch.equal(cnt, cnt2)
     idx, cnt = idx.cpu().numpy(), cnt.cpu().numpy()
@@ -551,18 +613,19 @@ def test_chunked_whole_context_prefill(mode):
 
 # ---------------------------------------------------------------- decode
 
-@pytest.mark.parametrize("mode", [lsa.LSA_FLAT, lsa.LSA_TREE])
-def test_decode_steps(mode):
-    say(f"case: decode mode={mode}")
+@pytest.mark.parametrize("mode,window,n_sink", [(lsa.LSA_FLAT, 512, 4), (lsa.LSA_TREE, 512, 4),
+                                               (lsa.LSA_FLAT, 2048, 64), (lsa.LSA_TREE, 1500, 9)])
+def test_decode_steps(mode, window, n_sink):
+    say(f"case: decode mode={mode} window={window} n_sink={n_sink}")
     w = S.WORKLOADS[3]
     lens = [4 * 512 + 509, 3000, 1500]       # the first sequence fills a block on step 3
-    p = lsa.Params(k=256, index_dtype=lsa.LSA_BF16, mode=mode)
+    p = lsa.Params(k=256, index_dtype=lsa.LSA_BF16, mode=mode, window=window, n_sink=n_sink)
     seqs = [S.latent_inputs(w, seq=b, T=n + 4, query_rows=(0, n + 4)) for b, n in enumerate(lens)]
     caches = [gpu_cache(X[:n], p, max_tokens=n + 4) for (X, Y, _), n in zip(seqs, lens)]
     for step in range(4):
         q = torch.from_numpy(np.stack([Y[n + step] for (X, Y, _), n in zip(seqs, lens)])).cuda()
         kn = torch.from_numpy(np.stack([X[n + step] for (X, Y, _), n in zip(seqs, lens)])).cuda()
-        idx, cnt = lsa.index_decode(caches, q, kn, p)
+        idx, cnt = lsa.index_decode(caches, q, kn, p, stats=FB)
         torch.cuda.synchronize()
         for b, ((X, Y, _), n) in enumerate(zip(seqs, lens)):
             pos = n + step

@@ -12,9 +12,9 @@ import torch
 import lsa_synth as S
 import sparse_attention_indexing_amd as lsa
 from oracle import lsa_oracle as O
-from parity_util import (attention_from_rows, cache_to_host, compare_cache, compare_lists,
-                         device_normal, gpu_cache, host_rows, oracle_cache_parallel,
-                         oracle_params)
+from parity_util import (FB, attention_from_rows, cache_to_host, compare_cache, compare_lists,
+                         compare_tree, device_normal, gpu_cache, host_rows,
+                         oracle_cache_parallel, oracle_params)
 
 pytestmark = pytest.mark.gpu
 
@@ -47,7 +47,7 @@ def test_prefill_128k_full_size():
     p = lsa.Params(k=w.k)
     c = gpu_cache(X, p)
     Yd = torch.from_numpy(Y).cuda()
-    idx, cnt = lsa.index_prefill(c, Yd, w.q_start, p)
+    idx, cnt = lsa.index_prefill(c, Yd, w.q_start, p, stats=FB)
     Q = device_normal(w, "q", (w.Tq, w.Hq, w.D))
     K = device_normal(w, "k", (w.T, w.Hkv, w.D))
     V = device_normal(w, "v", (w.T, w.Hkv, w.D))
@@ -73,8 +73,8 @@ def test_prefill_1m_tree_and_flat():
     pf = lsa.Params(k=w.k, mode=lsa.LSA_FLAT)
     c = gpu_cache(X, pt)
     Yd = torch.from_numpy(Y).cuda()
-    it, ct = lsa.index_prefill(c, Yd, w.q_start, pt)
-    i_f, c_f = lsa.index_prefill(c, Yd, w.q_start, pf)
+    it, ct = lsa.index_prefill(c, Yd, w.q_start, pt, stats=FB)
+    i_f, c_f = lsa.index_prefill(c, Yd, w.q_start, pf, stats=FB)
     torch.cuda.synchronize()
     t0 = time.time()
     oc = oracle_cache_parallel(X, oracle_params(pt))
@@ -82,11 +82,8 @@ def test_prefill_1m_tree_and_flat():
     say("build", compare_cache(g, oc, X), f"{time.time() - t0:.1f}s")
     ot = O.build_tree(oc)
     assert len(g["levels"]) == ot.height == 17
-    if min(ot.group_min_gap) > 1e-12:
-        for l, lv in enumerate(g["levels"], start=1):
-            assert np.array_equal(lv["child"], ot.levels[l]["child"]), f"level {l} children"
-            assert np.array_equal(lv["min_block"], ot.levels[l]["min_block"]), f"level {l}"
-            assert np.array_equal(lv["cent"], ot.levels[l]["cent"]), f"level {l} centroids"
+    # the seeded inputs have no near-tie pairing: every level is compared
+    assert compare_tree(g, ot, 1e-12, "T=1M") == ot.height
     rows = np.linspace(0, w.Tq - 1, 24).astype(int)
     it_h, ct_h, if_h, cf_h = it.cpu().numpy(), ct.cpu().numpy(), i_f.cpu().numpy(), c_f.cpu().numpy()
     say("tree index", compare_lists(it_h[rows], ct_h[rows], w.q_start + rows, Y[rows], oc, "tree", ot))
@@ -112,7 +109,7 @@ def test_decode_1m_steady_and_firing():
     caches = [gpu_cache(X[:n], p, max_tokens=n + 1) for (X, Y, _), n in zip(seqs, lens)]
     q = torch.from_numpy(np.stack([Y[0] for (X, Y, _) in seqs])).cuda()
     kn = torch.from_numpy(np.stack([X[n] for (X, Y, _), n in zip(seqs, lens)])).cuda()
-    idx, cnt = lsa.index_decode(caches, q, kn, p)
+    idx, cnt = lsa.index_decode(caches, q, kn, p, stats=FB)
     Tmax = max(lens) + 1
     K = torch.stack([device_normal(w, "k", (Tmax, w.Hkv, w.D), seq=b) for b in range(2)])
     V = torch.stack([device_normal(w, "v", (Tmax, w.Hkv, w.D), seq=b) for b in range(2)])
@@ -146,7 +143,7 @@ def test_prefill_10m_flat_last_chunk():
     p = lsa.Params(k=w.k)
     c = gpu_cache(X, p)
     Yd = torch.from_numpy(Y).cuda()
-    idx, cnt = lsa.index_prefill(c, Yd, w.q_start, p)
+    idx, cnt = lsa.index_prefill(c, Yd, w.q_start, p, stats=FB)
     Q = device_normal(w, "q", (w.Tq, w.Hq, w.D), row0=w.q_start)
     K = device_normal(w, "k", (w.T, w.Hkv, w.D))
     V = device_normal(w, "v", (w.T, w.Hkv, w.D))

@@ -1,0 +1,115 @@
+"""The oracle's pins catch plausible mistakes.
+
+Each case plants one mistake in a copy of an oracle function (its source with
+one edit, compiled in the oracle module's namespace), swaps the copy in, and
+runs the pins named for that function: at least one of them must fail.  The
+planted copies exist only inside this test, on the CPU; the oracle itself is
+restored after every case.
+"""
+import inspect
+import textwrap
+
+import pytest
+
+from oracle import lsa_oracle as O
+
+import test_oracle_pins as P
+import test_oracle_tree_pins as TP
+
+
+def _broken(fn_name: str, old: str, new: str):
+    src = textwrap.dedent(inspect.getsource(getattr(O, fn_name)))
+    assert src.count(old) == 1, f"{fn_name}: the text to break is not found once: {old!r}"
+    ns = dict(vars(O))
+    exec(compile(src.replace(old, new), f"<broken {fn_name}>", "exec"), ns)
+    return ns[fn_name]
+
+
+TREE_RANK_PINS = [TP.test_tree_rank_beam1_follows_the_parent_not_the_best_bucket,
+                  TP.test_tree_rank_beam2_three_levels,
+                  TP.test_tree_rank_tie_at_the_beam_boundary_keeps_the_lower_node,
+                  TP.test_tree_rank_masks_subtrees_with_no_eligible_block,
+                  TP.test_tree_rank_leaf_phase_drops_ineligible_buckets]
+BUILD_TREE_PINS = [TP.test_build_tree_parent_centroid_is_the_rounded_unit_sum,
+                   TP.test_build_tree_one_child_parent_copies_its_child_bit_for_bit,
+                   TP.test_build_tree_pairs_only_inside_groups_of_128]
+
+MUTATIONS = [
+    # tree_rank
+    ("tree_rank", "o = np.lexsort((kids, -sc))", "o = np.lexsort((kids, sc))",
+     "beam keeps the lowest scores", TREE_RANK_PINS),
+    ("tree_rank", "o = np.lexsort((kids, -sc))", "o = np.lexsort((-kids, -sc))",
+     "beam ties go to the higher node", TREE_RANK_PINS),
+    ("tree_rank", 'kids = kids[here["min_block"][kids] < qb]', "kids = kids",
+     "no causal mask on tree nodes", TREE_RANK_PINS),
+    ("tree_rank", 'kids = kids[here["min_block"][kids] < qb]',
+     'kids = kids[here["min_block"][kids] <= qb]', "mask admits the query's own block",
+     TREE_RANK_PINS),
+    ("tree_rank", "nodes = nodes[nodes < eligible_buckets(p, prm)]", "nodes = nodes",
+     "leaf phase keeps ineligible buckets", TREE_RANK_PINS),
+    ("tree_rank", "range(H - 1, lstar - 1, -1)", "range(H - 1, lstar, -1)",
+     "beam stops one level early", TREE_RANK_PINS),
+    ("tree_rank", "beam = np.sort(kids[o[:prm.beam]])", "beam = np.sort(kids[o[:prm.beam + 1]])",
+     "beam one wider", TREE_RANK_PINS),
+    ("tree_rank", "o = np.lexsort((nodes, -sc))", "o = np.lexsort((nodes, sc))",
+     "leaf phase ranks worst first", TREE_RANK_PINS),
+    # build_tree
+    ("build_tree", 'cent.append(round_index(unit(below["cent"][kids].sum(axis=0)), dtype))',
+     'cent.append(round_index(below["cent"][kids].mean(axis=0), dtype))',
+     "parent = rounded mean of the children", BUILD_TREE_PINS),
+    ("build_tree", 'cent.append(round_index(unit(below["cent"][kids].sum(axis=0)), dtype))',
+     'cent.append(unit(below["cent"][kids].sum(axis=0)))',
+     "parent centroid not rounded", BUILD_TREE_PINS),
+    ("build_tree", 'cent.append(below["cent"][kids[0]].copy())',
+     'cent.append(round_index(unit(below["cent"][kids[0]]), dtype))',
+     "one-child parent renormalised", BUILD_TREE_PINS),
+    ("build_tree", 'minb.append(below["min_block"][kids].min())',
+     'minb.append(below["min_block"][kids].max())', "min_block takes the largest block",
+     BUILD_TREE_PINS),
+    ("build_tree", "for c in res.clusters:", "for c in sorted(res.clusters, key=max):",
+     "parents ordered by their larger child", BUILD_TREE_PINS),
+    ("build_tree", "min(n, g0 + TREE_GROUP)", "n", "pairing across the whole level",
+     BUILD_TREE_PINS),
+    # the bucket bound
+    ("leaf_level", "while prm.beam * (1 << l) < prm.top_b:",
+     "while prm.beam * (1 << l) < -(-prm.k // prm.n_pool) + 65:",
+     "l* from the default-window bound", [P.test_leaf_level_reading,
+                                           TP.test_top_b_reading_by_hand]),
+    # flat ranking, expansion, near set, Ward, attention
+    ("flat_rank", "order = np.lexsort((np.arange(ne), -s))",
+     "order = np.lexsort((-np.arange(ne), -s))", "flat ties to the higher bucket",
+     [P.test_flat_rank_ties_go_to_lower_bucket]),
+    ("eligible_buckets", "prm.n_buckets * (p // prm.block)",
+     "prm.n_buckets * (p // prm.block + 1)", "query's own block eligible",
+     [P.test_worked_query_counts_from_the_pages]),
+    ("near_set", "win = np.arange(max(0, p - prm.window + 1), p + 1)",
+     "win = np.arange(max(0, p - prm.window), p + 1)", "window of 513 keys",
+     [P.test_worked_query_counts_from_the_pages]),
+    ("expand", "if key not in near_s:", "if True:", "sinks and window not skipped",
+     [P.test_expansion_worked_example_by_hand]),
+    ("ward_merge", "flat = int(np.argmin(vals))",
+     "flat = int(len(vals) - 1 - np.argmin(vals[::-1]))", "Ward ties to the largest pair",
+     [P.test_ward_respects_cap_and_tie_rule]),
+    ("ward_merge", "(size[:, None] + size[None, :]) <= cap)",
+     "(size[:, None] + size[None, :]) <= cap + 1)", "size cap one too large",
+     [P.test_bucket_partition_invariants_and_counts]),
+    ("attention_query", "logits = (Kh @ q[h]) * scale", "logits = (Kh @ q[h])",
+     "attention scale dropped", [P.test_attention_with_full_list_equals_dense_causal_sdpa]),
+    ("attention_query", "hk = h * Hkv // Hq", "hk = h % Hkv", "GQA heads interleaved",
+     [P.test_attention_with_full_list_equals_dense_causal_sdpa]),
+    ("pool_keys", "return Khat[:T].reshape(-1, n_pool, Khat.shape[1]).sum(axis=1)",
+     "return Khat[:T].reshape(-1, n_pool, Khat.shape[1]).mean(axis=1)", "pooled mean, not sum",
+     [P.test_normalise_and_pool_are_sums_of_unit_keys]),
+]
+
+
+@pytest.mark.parametrize("fn,old,new,what,pins", MUTATIONS, ids=[m[3] for m in MUTATIONS])
+def test_planted_mistake_fails_a_pin(fn, old, new, what, pins, monkeypatch):
+    monkeypatch.setattr(O, fn, _broken(fn, old, new))
+    failed = []
+    for pin in pins:
+        try:
+            pin()
+        except Exception as e:          # an assertion or a crash: the pin caught it
+            failed.append((pin.__name__, type(e).__name__))
+    assert failed, f"no pin catches: {what}"
