@@ -25,6 +25,7 @@ import numpy as np
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+FP32_PEAK_TFLOPS = 157.3        # MI355X fp32 vector
 
 
 def log(*a):
@@ -48,6 +49,9 @@ def parse():
     ap.add_argument("--mode", default="flat", choices=["flat", "tree"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-extra", action="store_true",
+                    help="headline workload only (skip the 10M last-chunk and 16 x 1M decode "
+                         "lines folded into the default run)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--decode", action="store_true",
@@ -63,48 +67,85 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(w, X, Y, budget_s: float):
-    """Time the CPU oracle (one thread) on a bounded sample of the step: the
-    bucket-cache build over every block, then index + attention for evenly
-    spaced queries until the time budget is spent; scale to all Tq queries."""
+_CPU = {}   # oracle state handed to the forked CPU-baseline workers
+
+
+def _cpu_build(blocks):
+    """Worker: the oracle's clustering of some blocks, timed."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import lsa_oracle as O
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        O.build_cache(_CPU["X"], _CPU["prm"], blocks=blocks)
+        return time.perf_counter() - t0
+
+
+def _cpu_queries(positions):
+    """Worker: index + attention of the oracle for queries at `positions` until
+    its time budget is spent.  Input generation (the Q/K/V rows a query reads)
+    is not timed.  Returns (queries done, seconds in the oracle)."""
     from threadpoolctl import threadpool_limits
 
     import lsa_synth as S
     from oracle import lsa_oracle as O
+    w, cache, Y = _CPU["w"], _CPU["cache"], _CPU["Y"]
+    n, busy, t_start = 0, 0.0, time.perf_counter()
     with threadpool_limits(limits=1):
-        prm = O.Params(k=w.k, n_sink=w.n_sink, window=w.window, index_dtype=w.dtype)
-        nb_total = w.T // 512
-        t0 = time.perf_counter()
-        cache = O.build_cache(X, prm)
-        t_build = time.perf_counter() - t0
-        positions = np.linspace(w.q_start, w.T - 1, 256).astype(np.int64)
-        rng = np.random.default_rng(0)
-        rng.shuffle(positions)
-        n_q, t_q = 0, 0.0
-        t_start = time.perf_counter()
         for p in positions:
-            q, _ = S.normal_rows(w, "q", np.array([p]), w.Hq * w.D)       # input, not timed
+            q, _ = S.normal_rows(w, "q", np.array([p]), w.Hq * w.D)
             t1 = time.perf_counter()
             r = O.index_query(Y[p - w.q_start], int(p), cache)
             t2 = time.perf_counter()
             sel = r.idx[:r.count]
-            k, _ = S.normal_rows(w, "k", sel, w.Hkv * w.D)                 # input, not timed
+            k, _ = S.normal_rows(w, "k", sel, w.Hkv * w.D)
             v, _ = S.normal_rows(w, "v", sel, w.Hkv * w.D)
             t3 = time.perf_counter()
             O.attention_query(q.reshape(w.Hq, w.D), k.reshape(-1, w.Hkv, w.D),
                               v.reshape(-1, w.Hkv, w.D), np.arange(len(sel)), len(sel))
-            t4 = time.perf_counter()
-            t_q += (t2 - t1) + (t4 - t3)
-            n_q += 1
-            if time.perf_counter() - t_start > budget_s:
+            busy += (t2 - t1) + (time.perf_counter() - t3)
+            n += 1
+            if time.perf_counter() - t_start > _CPU["budget"]:
                 break
-        t_query = t_q / n_q
-    t_step = t_build + t_query * w.Tq
-    return dict(value=w.Tq / t_step, unit="query tok/s", cores=1, kind="oracle",
-                sample=f"bucket-cache build over all {nb_total} blocks ({t_build:.1f} s) timed in "
-                       f"full; index + attention timed for {n_q} evenly spaced queries "
-                       f"({t_query * 1e3:.1f} ms each, input generation excluded) and scaled to "
-                       f"{w.Tq} queries; one thread")
+    return n, busy
+
+
+def cpu_baseline(w, X, Y, budget_s: float):
+    """The CPU oracle (plain fp64 NumPy, not tuned) on the host's cores: one
+    forked worker process per core, one BLAS thread each.  The bucket-cache
+    build over every block is split across the workers (wall time of the
+    slowest); index + attention runs on evenly spaced queries, each worker
+    stopping when its time budget is spent; the query rate is the sum of the
+    workers' rates.  The step is extrapolated to all Tq queries."""
+    import multiprocessing as mp
+
+    from oracle import lsa_oracle as O
+    cores = len(os.sched_getaffinity(0))
+    prm = O.Params(k=w.k, n_sink=w.n_sink, window=w.window, index_dtype=w.dtype)
+    nb_total = w.T // 512
+    _CPU.update(X=X, prm=prm)
+    ctx = mp.get_context("fork")
+    chunks = [c for c in np.array_split(np.arange(nb_total), cores) if len(c)]
+    t0 = time.perf_counter()
+    with ctx.Pool(cores) as pool:
+        pool.map(_cpu_build, [c.tolist() for c in chunks])
+    t_build = time.perf_counter() - t0
+    cache = O.build_cache(X, prm)          # the same cache, for the query workers (not timed)
+    positions = np.unique(np.linspace(w.q_start, w.T - 1, min(w.Tq, 2048 * cores)).astype(np.int64))
+    np.random.default_rng(0).shuffle(positions)
+    _CPU.update(w=w, cache=cache, Y=Y, budget=budget_s)
+    with ctx.Pool(cores) as pool:
+        parts = pool.map(_cpu_queries, [positions[i::cores] for i in range(cores)])
+    _CPU.clear()
+    n_q = sum(n for n, _ in parts)
+    rate = sum(n / b for n, b in parts if b > 0)       # queries per second, all workers
+    t_step = t_build + w.Tq / rate
+    return dict(value=w.Tq / t_step, unit="query tok/s", cores=cores, kind="oracle",
+                sample=f"bucket-cache build over all {nb_total} blocks timed in full "
+                       f"({t_build:.2f} s on {cores} worker processes); index + attention "
+                       f"timed for {n_q} evenly spaced queries ({rate:.1f} queries/s over all "
+                       f"workers, input generation excluded) and scaled to {w.Tq} queries; "
+                       f"{cores} processes x 1 BLAS thread")
 
 
 def attention_kernel_name(lsa, w, B: int, Tmax: int) -> str:
@@ -145,23 +186,80 @@ def measured_traffic(kernel: str, workload: str, rows_per_launch: int):
         return None
 
 
-def bench_decode(args, w, dev):
+def attention_roofline(lsa, torch, w, idx, cnt, L: int, t_attn_ms: float, kname: str,
+                       workload: str) -> dict:
+    """Roofline of the attention kernel, per launch (averaged over the step's
+    launches of up to lsa_attention_launch_rows() query rows).
+
+    Algorithmic work of a launch: 4 * head_dim FLOP per (query head, listed
+    key) -- q.k and p.v, a multiply-add counted as 2 -- and its compulsory
+    bytes: the K and V rows (all KV heads) of the distinct keys that its rows
+    list, plus Q, O, the lists and counts.  Its intensity (FLOP per compulsory
+    byte) against the ridge of the two peaks decides which roof binds: above
+    it the MFMA roof (achieved = FLOP / time), below it the HBM roof
+    (achieved = compulsory bytes / time).  The logical gather (every listed
+    row's bytes, cache hits included) is reported beside it; where the caches
+    serve the gather, its rate can exceed HBM peak and is not a roofline
+    fraction.  `traffic` is the counter-measured bytes that cross the L2 per
+    launch when the committed counter summary matches this kernel."""
+    esz = 2 if w.dtype == "bf16" else 4
+    Tq = idx.shape[0]
+    launch_rows = min(lsa.attention_launch_rows(), Tq) if w.dtype == "bf16" else Tq
+    launches = -(-Tq // launch_rows)
+    t_launch = t_attn_ms / launches
+    cnt64 = cnt.to(torch.int64).clamp(min=0, max=L)
+    total_rows = int(cnt64.sum().item())
+    flop = total_rows * w.Hq * 4 * w.D
+    row_bytes = w.Hkv * w.D * esz * 2
+    col = torch.arange(L, device=idx.device)[None, :]
+    uniq = 0
+    for r0 in range(0, Tq, launch_rows):
+        r1 = min(Tq, r0 + launch_rows)
+        sub = idx[r0:r1]
+        uniq += int(torch.unique(sub[col < cnt64[r0:r1, None]]).numel())
+    fixed = 2 * Tq * w.Hq * w.D * esz + Tq * L * 4 + Tq * 4
+    compulsory = uniq * row_bytes + fixed
+    logical = total_rows * row_bytes + fixed
+    intensity = flop / compulsory
+    mfma_peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
+    ridge = mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9)
+    sec = t_launch * 1e-3
+    if intensity >= ridge:
+        achieved, peak, unit, bound = flop / launches / sec / 1e12, mfma_peak, "TFLOP/s", "mfma"
+    else:
+        achieved, peak, unit, bound = compulsory / launches / sec / 1e9, HBM_PEAK_GBS, "GB/s", "hbm"
+    traffic = measured_traffic(kname, workload, launch_rows)
+    roof = dict(bound=bound, achieved=round(achieved, 2), peak=peak, unit=unit,
+                frac=round(achieved / peak, 4), traffic=None if traffic is None else round(traffic),
+                kernel=kname, launches_per_step=launches, kernel_ms=round(float(t_launch), 4),
+                algorithmic_flop=round(flop / launches),
+                compulsory_bytes=round(compulsory / launches),
+                intensity_flop_per_byte=round(intensity, 1), ridge_flop_per_byte=round(ridge, 1),
+                logical_bytes=round(logical / launches),
+                logical_gbs=round(logical / launches / sec / 1e9, 1))
+    if traffic is not None:
+        roof["traffic_gbs"] = round(traffic / sec / 1e9, 1)
+        roof["traffic_frac"] = round(traffic / sec / 1e9 / HBM_PEAK_GBS, 4)
+    return roof
+
+
+def run_decode(w, dev, mode_name: str, splits: int = 0, batch: int | None = None) -> dict:
     """Batched decode: every sequence holds T cached tokens; each step appends one
     key per sequence (clustering a block when it fills), builds the index lists
     and runs split attention.  512 consecutive steps: 511 steady steps and one
-    block-completing step."""
+    block-completing step; the first 8 are warm-up."""
     import torch
 
     import lsa_synth as S
     import sparse_attention_indexing_amd as lsa
-    B = w.batch if args.cfg == 3 else 1
+    B = batch or w.batch
     T, n_steps = w.T, 512
     Tmax = T + n_steps
-    mode = lsa.LSA_TREE if args.mode == "tree" else lsa.LSA_FLAT
+    mode = lsa.LSA_TREE if mode_name == "tree" else lsa.LSA_FLAT
     p = lsa.Params(k=w.k, n_sink=w.n_sink, window=w.window, mode=mode, beam=w.beam)
     L = lsa.list_len(p)
-    if args.splits <= 0:
-        args.splits = lsa.attention_default_splits(B, L)
+    if splits <= 0:
+        splits = lsa.attention_default_splits(B, L)
     caches, keys_new, queries = [], [], []
     t_gen = time.perf_counter()
     for b in range(B):
@@ -192,9 +290,13 @@ def bench_decode(args, w, dev):
     idx = torch.empty((B, L), dtype=torch.int32, device=dev)
     cnt = torch.empty((B,), dtype=torch.int32, device=dev)
     ws = torch.empty(lsa.index_workspace_bytes(p, B), dtype=torch.uint8, device=dev)
-    wsa = torch.empty(max(lsa.lib().lsa_attention_workspace_bytes(B, 1, w.Hq, w.D, args.splits), 1),
+    wsa = torch.empty(max(lsa.lib().lsa_attention_workspace_bytes(B, 1, w.Hq, w.D, splits), 1),
                       dtype=torch.uint8, device=dev)
     out = torch.empty((B, 1, w.Hq, w.D), dtype=tdt, device=dev)
+    status_off = lsa.lib().lsa_index_status_offset(__import__("ctypes").byref(p.c()), B)
+    status = ws[status_off:status_off + 4 * B].view(torch.int32)
+    fallbacks = torch.zeros((), dtype=torch.int64, device=dev)
+    rows_listed = torch.zeros((), dtype=torch.int64, device=dev)
     torch.cuda.synchronize()
     ev = lambda: torch.cuda.Event(enable_timing=True)
     marks = []
@@ -203,31 +305,58 @@ def bench_decode(args, w, dev):
         e0.record()
         lsa.index_decode(caches, qn[s_], kn[s_], p, workspace=ws, out=(idx, cnt))
         e1.record()
-        lsa.sparse_attention(Qd[s_], Kc, Vc, idx.view(B, 1, L), cnt.view(B, 1), splits=args.splits,
+        lsa.sparse_attention(Qd[s_], Kc, Vc, idx.view(B, 1, L), cnt.view(B, 1), splits=splits,
                              out=out, workspace=wsa)
         e2.record()
         marks.append((e0, e1, e2))
+        if s_ >= 8:      # outside the timed interval of the steps
+            fallbacks += status.sum()
+            rows_listed += cnt.sum()
     torch.cuda.synchronize()
     tim = np.array([[a.elapsed_time(b_), b_.elapsed_time(c_)] for a, b_, c_ in marks]) * 1e3
     fire = [i for i in range(n_steps) if (T + i + 1) % 512 == 0]
     steady = [i for i in range(8, n_steps) if i not in fire]
     st = tim[steady]
-    tot_steady = float(np.median(st.sum(axis=1)))
+    tot = st.sum(axis=1)
+    tot_steady = float(np.median(tot))
+    idx_us = float(np.median(st[:, 0]))
+    # roofline of the indexing stage (the dominant one): its algorithmic bytes
+    # are the eligible buckets' centroids (the HBM stream every query scores;
+    # 128 B each in bf16, a member word of 4 B for each kept bucket aside)
+    elig = T // 512 * 64          # eligible buckets of a steady step's query
+    cent_bytes = B * elig * 64 * 2
+    kv_bytes = float(rows_listed.item()) / len(steady) * w.Hkv * w.D * 2 * 2
+    achieved = cent_bytes / (idx_us * 1e-6) / 1e9
+    name = w.name if w.cfg == 3 else "decode_t10m_b1_bf16_flat"
     res = {
-        "metric": f"decode us/token ({args.mode})", "value": round(tot_steady, 2), "unit": "us/token",
+        "metric": f"decode us/token ({mode_name})", "value": round(tot_steady, 2), "unit": "us/token",
         "n_gpus": 1, "steps": len(steady), "warmup": 8, "ms_per_step": round(tot_steady / 1e3, 5),
         "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": workload_name(w.name if args.cfg == 3 else "decode_t10m_b1_bf16",
-                                             args.mode), "T": T,
-                   "batch": B, "k": w.k, "mode": args.mode, "attention_splits": args.splits,
+        "config": {"workload": workload_name(name, mode_name), "T": T,
+                   "batch": B, "k": w.k, "mode": mode_name, "attention_splits": splits,
                    "parallelism": "none"},
-        "stages_us": {"index_decode": round(float(np.median(st[:, 0])), 2),
+        "step_us": {"median": round(tot_steady, 2), "p99": round(float(np.percentile(tot, 99)), 2),
+                    "max": round(float(tot.max()), 2)},
+        "stages_us": {"index_decode": round(idx_us, 2),
                       "attention": round(float(np.median(st[:, 1])), 2)},
         "firing_step_us": {"index_decode": round(float(tim[fire[0], 0]), 2),
                            "attention": round(float(tim[fire[0], 1]), 2)} if fire else None,
         "per_sequence_step_us": round(tot_steady / B, 3),
+        "exact_fallbacks": {"queries": int(fallbacks.item()), "of": B * (n_steps - 8)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "lsa_index_decode (all launches of the indexing stage)",
+                     "algorithmic_bytes": cent_bytes, "kernel_ms": round(idx_us / 1e3, 5),
+                     "attention_gather_bytes": round(kv_bytes),
+                     "attention_gather_gbs": round(kv_bytes / (float(np.median(st[:, 1])) * 1e-6)
+                                                   / 1e9, 1)},
     }
+    return res
+
+
+def bench_decode(args, w, dev):
+    res = run_decode(w, dev, args.mode, args.splits, w.batch if args.cfg == 3 else 1)
     print(json.dumps(res), flush=True)
 
 
@@ -430,28 +559,21 @@ def bench_whole_context(args, w, dev):
     print(json.dumps(res), flush=True)
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
-              "(the path runs on a single MI355X).", file=sys.stderr)
-        sys.exit(2)
+def run_prefill(w, dev, mode_name: str, steps: int, warmup: int, calib_copy: bool = False,
+                cpu_seconds: float = 0.0) -> dict:
+    """One prefill step = build_bucket_cache over all T keys (full-context
+    workloads) + lsa_index_prefill for all Tq queries + lsa_sparse_attention
+    over their lists; last-chunk workloads build the cache of every full
+    block once before timing and time index + attention.  Inputs are resident
+    in HBM before the timed region; stage times come from HIP events on the
+    stream the launches run on."""
+    import ctypes
+
     import torch
 
     import lsa_synth as S
     import sparse_attention_indexing_amd as lsa
 
-    w = S.WORKLOADS[args.cfg]
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    if args.decode:
-        return bench_decode(args, w, dev)
-    if args.whole_context:
-        return bench_whole_context(args, w, dev)
-    if args.tree_sweep:
-        return bench_tree_sweep(args, w, dev)
-    if w.batch != 1:
-        raise SystemExit("prefill timing needs a single-sequence workload (cfg 1, 2, 4, 5)")
     t_gen = time.perf_counter()
     X, Y, _ = S.latent_inputs(w)
     Xd = torch.from_numpy(X).to(dev)
@@ -464,38 +586,36 @@ def main():
         S.device_fill_normal(t.data_ptr(), t.numel(), S.philox_key(w.cfg, name), off, w.dtype == "bf16",
                              torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
-    log(f"inputs ready in {time.perf_counter() - t_gen:.1f}s")
+    log(f"{w.name}: inputs ready in {time.perf_counter() - t_gen:.1f}s")
 
-    mode = lsa.LSA_TREE if args.mode == "tree" else lsa.LSA_FLAT
+    mode = lsa.LSA_TREE if mode_name == "tree" else lsa.LSA_FLAT
     p = lsa.Params(k=w.k, n_sink=w.n_sink, window=w.window, mode=mode, beam=w.beam,
                    index_dtype=lsa.LSA_BF16 if w.dtype == "bf16" else lsa.LSA_F32)
     L = lsa.list_len(p)
-    nbytes = lsa.lib().lsa_cache_bytes(__import__("ctypes").byref(p.c()), w.T)
+    nbytes = lsa.lib().lsa_cache_bytes(ctypes.byref(p.c()), w.T)
     cache_mem = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     idx = torch.empty((w.Tq, L), dtype=torch.int32, device=dev)
     cnt = torch.empty((w.Tq,), dtype=torch.int32, device=dev)
     ws = torch.empty(lsa.index_workspace_bytes(p, w.Tq), dtype=torch.uint8, device=dev)
     out = torch.empty_like(Q)
 
-    class _Cache(lsa.BucketCache):
-        def __init__(self):  # reuse the same device memory every step
-            import ctypes
-            self.params = p
-            self.mem = cache_mem
-            h = ctypes.c_void_p()
-            lsa._check("lsa_cache_init", lsa.lib().lsa_cache_init(
-                ctypes.byref(p.c()), w.T, lsa._ptr(cache_mem), nbytes, ctypes.byref(h)))
-            self.handle = h
+    def fresh_cache():   # a cache over the same device memory, every step
+        c = lsa.BucketCache.__new__(lsa.BucketCache)
+        c.params, c.mem = p, cache_mem
+        h = ctypes.c_void_p()
+        lsa._check("lsa_cache_init", lsa.lib().lsa_cache_init(
+            ctypes.byref(p.c()), w.T, lsa._ptr(cache_mem), nbytes, ctypes.byref(h)))
+        c.handle = h
+        return c
 
     ev = lambda: torch.cuda.Event(enable_timing=True)
-
     full_prefill = w.q_start == 0
     prebuilt = None
     build_once_ms = None
     if not full_prefill:
         # last prefill chunk of a long context: the cache of every full block
         # exists before the chunk; building it is timed once, separately
-        prebuilt = _Cache()
+        prebuilt = fresh_cache()
         b0, b1 = ev(), ev()
         b0.record()
         prebuilt.build(Xd)
@@ -507,7 +627,7 @@ def main():
     def step(times=None):
         e0, e1, e2, e3 = ev(), ev(), ev(), ev()
         if full_prefill:
-            c = _Cache()
+            c = fresh_cache()
             e0.record()
             c.build(Xd)
         else:
@@ -522,77 +642,101 @@ def main():
             times.append((e0, e1, e2, e3))
         return c
 
-    if args.calib_copy:
+    if calib_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     times = []
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(steps):
         step(times)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_step = wall * 1e3 / args.steps
+    ms_step = wall * 1e3 / steps
     stage = np.array([[a.elapsed_time(b), b.elapsed_time(c), c.elapsed_time(d)]
                       for a, b, c, d in times])
     t_build, t_index, t_attn = stage.mean(axis=0)
     log(f"per step: build {t_build:.3f} ms, index {t_index:.3f} ms, attention {t_attn:.3f} ms; "
         f"wall {ms_step:.3f} ms")
-
-    # algorithmic bytes of the attention launch: gathered K and V rows for every
-    # KV head, plus Q, O and the index lists
-    total_rows = int(cnt.to(torch.int64).sum().item())
-    esz = 2 if w.dtype == "bf16" else 4
-    attn_bytes = (total_rows * w.Hkv * w.D * esz * 2 + 2 * w.Tq * w.Hq * w.D * esz
-                  + w.Tq * L * 4)
-    achieved = attn_bytes / (t_attn * 1e-3) / 1e9
-    # algorithmic FLOPs of flat scoring: 2 * 64 per eligible (query, bucket) pair
+    fallbacks = lsa.exact_fallbacks(p, w.Tq, ws)
+    # flat scoring: 2 * 64 FLOP per eligible (query, bucket) pair
     pos = np.arange(w.q_start, w.T, dtype=np.int64)
     pairs = int((64 * (pos // 512)).sum())
     kname = attention_kernel_name(lsa, w, 1, w.T)
-    # the bf16 attention runs as back-to-back launches of up to launch_rows query
-    # rows; bytes and time are reported per launch, averaged over the step's launches
-    launch_rows = min(lsa.attention_launch_rows(), w.Tq) if w.dtype == "bf16" else w.Tq
-    launches = -(-w.Tq // launch_rows)
-    t_launch = t_attn / launches
-    traffic = measured_traffic(kname, workload_name(w.name, args.mode), launch_rows)
-    roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBS, 4),
-                    traffic=None if traffic is None else round(traffic),
-                    kernel=kname, launches_per_step=launches,
-                    algorithmic_bytes=round(attn_bytes / launches),
-                    kernel_ms=round(float(t_launch), 4))
-    if traffic is not None:
-        roofline["traffic_gbs"] = round(traffic / (t_launch * 1e-3) / 1e9, 1)
-        roofline["traffic_frac"] = round(traffic / (t_launch * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
-    value = w.Tq / (ms_step * 1e-3)
+    wname = workload_name(w.name, mode_name)
+    roofline = attention_roofline(lsa, torch, w, idx, cnt, L, float(t_attn), kname, wname)
     res = {
-        "metric": f"prefill query tok/s per layer ({args.mode})", "value": round(value, 1),
-        "unit": "query tok/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "metric": f"prefill query tok/s per layer ({mode_name})",
+        "value": round(w.Tq / (ms_step * 1e-3), 1),
+        "unit": "query tok/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
-        "config": {"workload": workload_name(w.name, args.mode), "T": w.T, "Tq": w.Tq,
-                   "Hq": w.Hq, "Hkv": w.Hkv,
-                   "head_dim": w.D, "k": w.k, "mode": args.mode, "n_sink": w.n_sink,
+        "config": {"workload": wname, "T": w.T, "Tq": w.Tq, "Hq": w.Hq, "Hkv": w.Hkv,
+                   "head_dim": w.D, "k": w.k, "mode": mode_name, "n_sink": w.n_sink,
                    "window": w.window, "latent_components": w.n_comp, "parallelism": "none"},
         "stages_ms": {"build": round(float(t_build), 4), "index": round(float(t_index), 4),
                       "attention": round(float(t_attn), 4)},
         "step": ("build + index + attention" if full_prefill else
                  "index + attention for the last chunk (cache built before timing)"),
+        "exact_fallbacks": {"queries": fallbacks, "of": w.Tq},
         "scoring": {"pairs": pairs, "algorithmic_tflop": round(pairs * 128 / 1e12, 4)},
         "roofline": roofline,
     }
     if build_once_ms is not None:
         res["cache_build_ms"] = round(build_once_ms, 3)
-    if not args.no_cpu_baseline and w.T <= 1 << 17:
+    del Q, K, V, Xd, Yd, cache_mem, idx, cnt, ws, out, prebuilt
+    torch.cuda.empty_cache()
+    if cpu_seconds > 0:
         log("timing the CPU oracle on a sample ...")
-        cb = cpu_baseline(w, X, Y, args.cpu_seconds)
+        cb = cpu_baseline(w, X, Y, cpu_seconds)
         res["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
+    return res
+
+
+def _extra_summary(r: dict) -> dict:
+    keep = ("metric", "value", "unit", "ms_per_step", "step_us", "stages_ms", "stages_us",
+            "firing_step_us", "cache_build_ms", "exact_fallbacks", "roofline", "config",
+            "per_sequence_step_us", "step")
+    return {k: r[k] for k in keep if k in r}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the path runs on a single MI355X).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import lsa_synth as S
+
+    w = S.WORKLOADS[args.cfg]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.decode:
+        return bench_decode(args, w, dev)
+    if args.whole_context:
+        return bench_whole_context(args, w, dev)
+    if args.tree_sweep:
+        return bench_tree_sweep(args, w, dev)
+    if w.batch != 1:
+        raise SystemExit("prefill timing needs a single-sequence workload (cfg 1, 2, 4, 5)")
+    headline = args.cfg == 2 and args.mode == "flat" and not args.no_extra
+    res = run_prefill(w, dev, args.mode, args.steps, args.warmup, args.calib_copy,
+                      0.0 if args.no_cpu_baseline or w.T > 1 << 17 else args.cpu_seconds)
+    if headline:
+        # the metric's other ends, on the same GPU in the same run: the 10M
+        # last prefill chunk (flat) and one step of the 16 x 1M decode batch
+        res["extra"] = {}
+        r10 = run_prefill(S.WORKLOADS[5], dev, "flat", min(args.steps, 3), 1)
+        res["extra"][r10["config"]["workload"]] = _extra_summary(r10)
+        rdec = run_decode(S.WORKLOADS[3], dev, "flat")
+        res["extra"][rdec["config"]["workload"]] = _extra_summary(rdec)
     print(json.dumps(res), flush=True)
 
 

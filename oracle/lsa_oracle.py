@@ -300,7 +300,13 @@ class Tree:
         return len(self.levels) - 1
 
 
-def build_tree(cache: BucketCache, dtype: str | None = None) -> Tree:
+def pair_group(points: np.ndarray) -> WardResult:
+    """One group of a tree level: greedy Ward merging of its nodes with a size
+    cap of 2, down to ceil(n / 2) nodes (pairs, and one leftover if n is odd)."""
+    return ward_merge(points, cap=2, target=-(-len(points) // 2))
+
+
+def build_tree(cache: BucketCache, dtype: str | None = None, mapper=map) -> Tree:
     """Repeat the merging on the buckets to form a binary tree.
 
     Level 0 is the buckets (points = stored centroids).  Each higher level
@@ -310,7 +316,8 @@ def build_tree(cache: BucketCache, dtype: str | None = None) -> Tree:
     a leftover node becomes a one-child parent whose centroid is copied.
     Parents are ordered by their smaller child; a pair's centroid is the
     rounded unit vector of the sum of the two child centroids.  Stops when a
-    level has one node.
+    level has one node.  The groups of a level are independent; ``mapper``
+    (the builtin map, or a process pool's) applies pair_group to them.
     """
     dtype = dtype or cache.params.index_dtype
     n0 = cache.n_buckets
@@ -322,9 +329,9 @@ def build_tree(cache: BucketCache, dtype: str | None = None) -> Tree:
         below = levels[-1]
         n = below["cent"].shape[0]
         cent, child, minb, lvl_gap = [], [], [], math.inf
-        for g0 in range(0, n, TREE_GROUP):
-            idx = np.arange(g0, min(n, g0 + TREE_GROUP))
-            res = ward_merge(below["cent"][idx], cap=2, target=-(-len(idx) // 2))
+        groups = [np.arange(g0, min(n, g0 + TREE_GROUP)) for g0 in range(0, n, TREE_GROUP)]
+        results = mapper(pair_group, [below["cent"][idx] for idx in groups])
+        for idx, res in zip(groups, results):
             lvl_gap = min(lvl_gap, res.min_gap)
             for c in res.clusters:            # ordered by smaller child
                 kids = idx[c]

@@ -270,6 +270,25 @@ int run_selection(const IndexCtx& ctx, const IndexWs& ws, const lsa_params* p,
 }
 
 
+// Argument checks of the attention entry point (no launch); *need receives
+// the split-partials bytes.  1 = nothing to do.
+int check_attention(const void* q, const void* k_cache, const void* v_cache, int32_t B,
+                    int64_t Tq, int64_t Tmax, int32_t Hq, int32_t Hkv, int32_t D,
+                    const int32_t* idx, const int32_t* count, int32_t L_max, int32_t dtype,
+                    int32_t splits, const void* out, int64_t* need) {
+  if (B < 0 || Tq < 0 || Tmax < 0 || L_max < 0 || splits < 1) return LSA_ERR_ARG;
+  if (D != kHeadDim || Hkv <= 0 || Hq <= 0 || Hq % Hkv != 0 || Hq / Hkv > 16)
+    return LSA_ERR_UNSUPPORTED;
+  if (dtype != LSA_F32 && dtype != LSA_BF16) return LSA_ERR_UNSUPPORTED;
+  if ((int64_t)B * Tq == 0) return 1;
+  if (!q || !k_cache || !v_cache || !idx || !count || !out) return LSA_ERR_ARG;
+  if (Tmax < 1) return LSA_ERR_ARG;   // invalid list entries read token 0 (with zero weight)
+  if ((int64_t)B * Tq > (int64_t)0x7fffffff || splits > 65535) return LSA_ERR_UNSUPPORTED;
+  if (splits > 1 && (int64_t)B * Tq * Hq * 2 > (int64_t)0x7fffffff) return LSA_ERR_UNSUPPORTED;
+  *need = lsa_attention_workspace_bytes(B, Tq, Hq, D, splits);
+  return LSA_OK;
+}
+
 }  // namespace
 
 // ====================================================================== API
@@ -592,16 +611,10 @@ int lsa_sparse_attention(const void* q, const void* k_cache, const void* v_cache
                          const int32_t* idx, const int32_t* count, int32_t L_max, float scale,
                          int32_t dtype, int32_t splits, void* out, void* workspace,
                          int64_t ws_bytes, void* stream) {
-  if (B < 0 || Tq < 0 || Tmax < 0 || L_max < 0 || splits < 1) return LSA_ERR_ARG;
-  if (D != kHeadDim || Hkv <= 0 || Hq <= 0 || Hq % Hkv != 0 || Hq / Hkv > 16)
-    return LSA_ERR_UNSUPPORTED;
-  if (dtype != LSA_F32 && dtype != LSA_BF16) return LSA_ERR_UNSUPPORTED;
-  if ((int64_t)B * Tq == 0) return LSA_OK;
-  if (!q || !k_cache || !v_cache || !idx || !count || !out) return LSA_ERR_ARG;
-  if (Tmax < 1) return LSA_ERR_ARG;   // invalid list entries read token 0 (with zero weight)
-  if ((int64_t)B * Tq > (int64_t)0x7fffffff || splits > 65535) return LSA_ERR_UNSUPPORTED;
-  if (splits > 1 && (int64_t)B * Tq * Hq * 2 > (int64_t)0x7fffffff) return LSA_ERR_UNSUPPORTED;
-  const int64_t need = lsa_attention_workspace_bytes(B, Tq, Hq, D, splits);
+  int64_t need = 0;
+  const int rc = check_attention(q, k_cache, v_cache, B, Tq, Tmax, Hq, Hkv, D, idx, count, L_max,
+                                 dtype, splits, out, &need);
+  if (rc) return rc < 0 ? rc : LSA_OK;
   if (need > 0 && (!workspace || ws_bytes < need)) return LSA_ERR_WORKSPACE;
   hipError_t e = launch_attention(q, k_cache, v_cache, B, Tq, Tmax, Hq, Hkv, idx, count, L_max,
                                   scale, dtype, splits, out, reinterpret_cast<float*>(workspace),

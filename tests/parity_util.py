@@ -124,7 +124,7 @@ def compare_tree(g: dict, ot: O.Tree, gap: float, label: str = "") -> int:
 def check_list_invariants(lst: np.ndarray, cnt: int, p: int, prm: O.Params):
     v = lst[:cnt]
     assert np.all(lst[cnt:] == -1)
-    assert np.all(np.diff(v) > 0) and v[0] == 0 and v[-1] == p
+    assert np.all(np.diff(v) > 0) and v[-1] == p and (v[0] == 0 or prm.n_sink == 0)
     near = O.near_set(p, prm)
     assert np.isin(near, v).all()
     far = np.setdiff1d(v, near)
@@ -132,12 +132,55 @@ def check_list_invariants(lst: np.ndarray, cnt: int, p: int, prm: O.Params):
     assert np.all(far // 512 < p // 512)
 
 
+def n_procs() -> int:
+    """Worker processes for the oracle: the CPUs this process may use, at most 16."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+_G = {}   # oracle state handed to forked workers
+
+
+def _index_rows(job):
+    out = []
+    for p, y in job:
+        r = O.index_query(y, int(p), _G["oc"], _G["mode"], _G["tree"])
+        r.ranked = None          # the full ranking is not compared; keep the transfer small
+        out.append(r)
+    return out
+
+
+def oracle_index_parallel(positions, ys, oc: O.BucketCache, mode="flat", tree=None) -> list:
+    """O.index_query for every (position, query), queries split across forked
+    worker processes (numpy only; no GPU use in the workers)."""
+    pairs = list(zip([int(p) for p in positions], list(ys)))
+    procs = n_procs()
+    if procs == 1 or len(pairs) < 8:
+        _G.update(oc=oc, mode=mode, tree=tree)
+        return _index_rows(pairs)
+    _G.update(oc=oc, mode=mode, tree=tree)
+    jobs = [pairs[i::procs] for i in range(procs)]
+    with mp.get_context("fork").Pool(procs) as pool:
+        parts = pool.map(_index_rows, jobs)
+    _G.clear()
+    out = [None] * len(pairs)
+    for i, part in enumerate(parts):
+        out[i::procs] = part
+    return out
+
+
+def oracle_tree_parallel(oc: O.BucketCache) -> O.Tree:
+    """O.build_tree with the groups of each level paired in worker processes."""
+    with mp.get_context("fork").Pool(n_procs()) as pool:
+        return O.build_tree(oc, mapper=lambda f, xs: pool.map(f, xs, chunksize=32))
+
+
 def compare_lists(idx: np.ndarray, cnt: np.ndarray, positions, ys, oc: O.BucketCache,
-                  mode="flat", tree=None) -> dict:
+                  mode="flat", tree=None, parallel=False) -> dict:
     """GPU lists vs oracle lists, query by query."""
     exempt = differ = 0
+    ref = oracle_index_parallel(positions, ys, oc, mode, tree) if parallel else None
     for row, (p, y) in enumerate(zip(positions, ys)):
-        r = O.index_query(y, int(p), oc, mode, tree)
+        r = ref[row] if parallel else O.index_query(y, int(p), oc, mode, tree)
         gl, gc = idx[row], int(cnt[row])
         check_list_invariants(gl, gc, int(p), oc.params)
         same = gc == r.count and np.array_equal(gl[:gc], r.idx[:r.count])
@@ -166,10 +209,11 @@ def _build_part(blocks):
             c.block_min_gap[blocks], c.block_ess[blocks])
 
 
-def oracle_cache_parallel(X: np.ndarray, prm: O.Params, procs: int = 8) -> O.BucketCache:
+def oracle_cache_parallel(X: np.ndarray, prm: O.Params, procs: int | None = None) -> O.BucketCache:
     """The oracle's build_cache over all full blocks, blocks split across forked
     worker processes (numpy only; no GPU use in the workers)."""
     global _PX, _PPRM
+    procs = procs or n_procs()
     nb = X.shape[0] // prm.block
     if nb <= 64:
         return O.build_cache(X, prm)

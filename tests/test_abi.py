@@ -152,3 +152,4 @@ def test_attention_host_errors():
     assert L.lsa_attention_workspace_bytes(1, 16, 32, 128, 1) == 0
     assert L.lsa_attention_workspace_bytes(1, 16, 32, 128, 4) == 16 * 4 * 32 * 130 * 4
     assert L.lsa_status_string(-3) == b"workspace too small"
+

@@ -539,7 +539,7 @@ def test_tree_build_and_search(tree_65k):
 
 
 @pytest.mark.parametrize("beam,leaf,window,n_sink", [
-    (64, -1, 512, 4), (16, -1, 512, 4), (8, -1, 512, 4), (64, 3, 512, 4), (16, 6, 512, 4),
+    (64, -1, 512, 4), (16, -1, 512, 4), (8, -1, 512, 4), (64, 3, 512, 4), (16, 5, 512, 4),
     (1, 0, 512, 4), (64, -1, 2048, 64)])
 def test_tree_search_parameters(tree_65k, beam, leaf, window, n_sink):
     """Tree search with narrower beams, the beam stopped one or more levels

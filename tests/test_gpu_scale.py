@@ -14,7 +14,7 @@ import sparse_attention_indexing_amd as lsa
 from oracle import lsa_oracle as O
 from parity_util import (FB, attention_from_rows, cache_to_host, compare_cache, compare_lists,
                          compare_tree, device_normal, gpu_cache, host_rows,
-                         oracle_cache_parallel, oracle_params)
+                         oracle_cache_parallel, oracle_params, oracle_tree_parallel)
 
 pytestmark = pytest.mark.gpu
 
@@ -98,58 +98,112 @@ def test_prefill_1m_tree_and_flat():
     say(f"tree/flat far-key recall: mean {np.mean(rec):.3f} min {np.min(rec):.3f}")
 
 
-def test_decode_1m_steady_and_firing():
-    """Two sequences of the 16-sequence decode workload: one whose new key
-    completes a block (the block is clustered in the step), one steady."""
-    say("case: decode T=1M, block-completing and steady sequences")
+def _completed_block(gpu_cache_obj, X, b, p):
+    """The block `b` that a decode step completed matches the oracle's clustering."""
+    g = cache_to_host(gpu_cache_obj)
+    assert g["n_blocks"] == b + 1
+    sub = O.build_cache(X[b * 512:(b + 1) * 512], oracle_params(p))
+    gl = dict(n_blocks=1, cent=g["cent"][b * 64:(b + 1) * 64], pooled=g["pooled"][b * 64:(b + 1) * 64])
+    compare_cache(gl, sub, X[b * 512:(b + 1) * 512])
+    return g
+
+
+def test_decode_1m_16_sequences():
+    """One step of the 16-sequence decode workload (its launch shapes): 16
+    caches of 1,048,576 tokens, sequences 0 and 9 one key short of a full block
+    (their new key completes it and the block is clustered in the step), the
+    others steady.  Every sequence's list against the oracle over its own
+    cache, every sequence's split attention against the oracle."""
+    say("case: decode T=1M x 16 sequences, two block-completing")
     w = S.WORKLOADS[3]
-    lens = [w.T - 1, w.T]
+    B = w.batch
+    lens = [w.T - 1 if b in (0, 9) else w.T for b in range(B)]
     p = lsa.Params(k=w.k)
-    seqs = [S.latent_inputs(w, seq=b, T=n + 1, query_rows=(n, n + 1)) for b, n in enumerate(lens)]
-    caches = [gpu_cache(X[:n], p, max_tokens=n + 1) for (X, Y, _), n in zip(seqs, lens)]
-    q = torch.from_numpy(np.stack([Y[0] for (X, Y, _) in seqs])).cuda()
-    kn = torch.from_numpy(np.stack([X[n] for (X, Y, _), n in zip(seqs, lens)])).cuda()
-    idx, cnt = lsa.index_decode(caches, q, kn, p, stats=FB)
-    Tmax = max(lens) + 1
-    K = torch.stack([device_normal(w, "k", (Tmax, w.Hkv, w.D), seq=b) for b in range(2)])
-    V = torch.stack([device_normal(w, "v", (Tmax, w.Hkv, w.D), seq=b) for b in range(2)])
+    caches, keys, qs, Xs = [], [], [], []
+    for b, n in enumerate(lens):
+        X, Y, _ = S.latent_inputs(w, seq=b, T=n + 1, query_rows=(n, n + 1))
+        caches.append(gpu_cache(X[:n], p, max_tokens=n + 1))
+        keys.append(X[n])
+        qs.append(Y[0])
+        Xs.append(X)
+    st = {}
+    idx, cnt = lsa.index_decode(caches, torch.from_numpy(np.stack(qs)).cuda(),
+                                torch.from_numpy(np.stack(keys)).cuda(), p, stats=st)
+    say(f"exact fallbacks: {st['exact_fallbacks']} of {B}")
+    Tmax = w.T + 1
+    K = torch.stack([device_normal(w, "k", (Tmax, w.Hkv, w.D), seq=b) for b in range(B)])
+    V = torch.stack([device_normal(w, "v", (Tmax, w.Hkv, w.D), seq=b) for b in range(B)])
     Q = torch.stack([device_normal(w, "q", (1, w.Hq, w.D), seq=b, row0=n) for b, n in enumerate(lens)])
-    out = lsa.sparse_attention(Q, K, V, idx.view(2, 1, -1), cnt.view(2, 1), splits=16)
+    splits = lsa.attention_default_splits(B, idx.shape[1])
+    out = lsa.sparse_attention(Q, K, V, idx.view(B, 1, -1), cnt.view(B, 1), splits=splits)
     torch.cuda.synchronize()
+    del K, V
     idx_h, cnt_h, out_h = idx.cpu().numpy(), cnt.cpu().numpy(), out.float().cpu().numpy()
-    for b, ((X, Y, _), n) in enumerate(zip(seqs, lens)):
-        oc = oracle_cache_parallel(X[:n + 1], oracle_params(p))
-        say(f"seq {b}", compare_lists(idx_h[b:b + 1], cnt_h[b:b + 1], [n], Y[0:1], oc))
-        if b == 0:  # the block completed by this step matches the oracle's clustering
-            g = cache_to_host(caches[0])
-            assert g["n_blocks"] == (n + 1) // 512
-            last = g["n_blocks"] - 1
-            sub = O.build_cache(X[last * 512:(last + 1) * 512], oracle_params(p))
-            gl = dict(n_blocks=1, cent=g["cent"][last * 64:], pooled=g["pooled"][last * 64:])
-            compare_cache(gl, sub, X[last * 512:(last + 1) * 512])
+    err = 0.0
+    for b, n in enumerate(lens):
+        oc = oracle_cache_parallel(Xs[b][:n + 1], oracle_params(p))
+        say(f"seq {b} (p={n})", compare_lists(idx_h[b:b + 1], cnt_h[b:b + 1], [n], qs[b][None], oc))
+        if n % 512 == 511:
+            _completed_block(caches[b], Xs[b], n // 512, p)
         qrow = host_rows(w, "q", [n], w.Hq * w.D, seq=b)[0]
         ref = attention_from_rows(w, qrow, idx_h[b], int(cnt_h[b]), seq=b)
-        err = float(np.abs(out_h[b, 0] - ref).max())
-        say(f"seq {b} decode attention (16 splits) max abs err {err:.3g}")
-        assert err <= 2e-2
+        err = max(err, float(np.abs(out_h[b, 0] - ref).max()))
+        Xs[b] = None
+    say(f"decode attention ({splits} splits) max abs err {err:.3g} over {B} sequences")
+    assert err <= 2e-2
 
 
-def test_prefill_10m_flat_last_chunk():
-    say("case: T=10M, last 32768 queries, flat")
+# ---------------------------------------------------------------- 10M tokens
+
+T_FIRE = 19530 * 512 + 511     # a 10M-scale decode position whose key completes block 19,530
+
+
+@pytest.fixture(scope="module")
+def ctx10m():
+    """The 10,000,000-token workload: latent keys up to position 10M (the
+    decode step's key included), the prefill chunk's queries and the decode
+    queries; a tree-mode GPU cache over the first 10M keys; the oracle's
+    cache and tree over the 19,531 full blocks (which every step below sees)."""
     w = S.WORKLOADS[5]
     t0 = time.time()
-    X, Y, _ = S.latent_inputs(w)
-    say(f"inputs {time.time() - t0:.1f}s")
-    p = lsa.Params(k=w.k)
-    c = gpu_cache(X, p)
-    Yd = torch.from_numpy(Y).cuda()
-    idx, cnt = lsa.index_prefill(c, Yd, w.q_start, p, stats=FB)
+    X, Y, _ = S.latent_inputs(w, T=w.T + 1, query_rows=(w.q_start, w.T + 1))
+    yf = S.latent_inputs(w, T=T_FIRE + 1, query_rows=(T_FIRE, T_FIRE + 1))[1][0]
+    say(f"10M inputs {time.time() - t0:.1f}s")
+    pt = lsa.Params(k=w.k, mode=lsa.LSA_TREE, beam=w.beam)
+    c = gpu_cache(X[:w.T], pt)
+    t0 = time.time()
+    oc = oracle_cache_parallel(X[:w.T + 1], oracle_params(pt))
+    assert oc.n_blocks == 19531
+    say(f"oracle cache {time.time() - t0:.1f}s")
+    t0 = time.time()
+    ot = oracle_tree_parallel(oc)
+    say(f"oracle tree {time.time() - t0:.1f}s ({ot.height} levels)")
+    return dict(w=w, X=X, Y=Y, yf=yf, c=c, oc=oc, ot=ot, pt=pt)
+
+
+def test_prefill_10m_flat_and_tree_last_chunk(ctx10m):
+    """The last 32,768-query chunk at 10M tokens, flat and tree (beam 64, 21
+    levels): every block and every tree level of the cache against the oracle,
+    64 sampled queries' lists in each mode, and 16 sampled queries' attention
+    in each mode, in the launch configuration the benchmark times."""
+    say("case: T=10M, last 32768 queries, flat and tree")
+    w, X, Y, c = ctx10m["w"], ctx10m["X"], ctx10m["Y"], ctx10m["c"]
+    oc, ot = ctx10m["oc"], ctx10m["ot"]
+    g = cache_to_host(c)
+    say("build", compare_cache(g, oc, X[:w.T]))
+    assert len(g["levels"]) == ot.height == 21
+    compare_tree(g, ot, 1e-12, "T=10M")
+    Yd = torch.from_numpy(np.ascontiguousarray(Y[:w.Tq])).cuda()
+    pf = lsa.Params(k=w.k)
+    i_f, c_f = lsa.index_prefill(c, Yd, w.q_start, pf, stats=FB)
+    i_t, c_t = lsa.index_prefill(c, Yd, w.q_start, ctx10m["pt"], stats=FB)
     Q = device_normal(w, "q", (w.Tq, w.Hq, w.D), row0=w.q_start)
     K = device_normal(w, "k", (w.T, w.Hkv, w.D))
     V = device_normal(w, "v", (w.T, w.Hkv, w.D))
     # the benchmark's layout at this size: one workgroup per query row
     assert not lsa.attention_head_major(1, w.T, w.Hkv, w.D, lsa.LSA_BF16)
-    out = lsa.sparse_attention(Q, K, V, idx, cnt)
+    o_f = lsa.sparse_attention(Q, K, V, i_f, c_f)
+    o_t = lsa.sparse_attention(Q, K, V, i_t, c_t)
     torch.cuda.synchronize()
     # the device generator fills all 5.12e9 elements like the host rows (this
     # needs a grid-stride launch: a dispatch holds fewer than 2^32 work-items)
@@ -157,12 +211,56 @@ def test_prefill_10m_flat_last_chunk():
         assert np.array_equal(K[r].float().cpu().numpy().reshape(-1).astype(np.float64),
                               host_rows(w, "k", [r], w.Hkv * w.D)[0]), f"K row {r}"
     del K, V
-    t0 = time.time()
-    oc = oracle_cache_parallel(X, oracle_params(p))
-    say("build", compare_cache(cache_to_host(c), oc, X), f"oracle {time.time() - t0:.1f}s")
-    idx_h, cnt_h = idx.cpu().numpy(), cnt.cpu().numpy()
-    rows = np.linspace(0, w.Tq - 1, 8).astype(int)
-    say("index", compare_lists(idx_h[rows], cnt_h[rows], w.q_start + rows, Y[rows], oc))
-    arows = rows[::2]
+    rows = np.unique(np.concatenate([np.linspace(0, w.Tq - 1, 60).astype(int),
+                                     [w.Tq - 1, w.Tq - 2, w.Tq - 129, w.Tq - 130]]))
+    arows = rows[:: max(1, len(rows) // 16)][:16]
     q_rows = host_rows(w, "q", w.q_start + arows, w.Hq * w.D)
-    _attn_check(w, q_rows, out.float().cpu().numpy(), idx_h, cnt_h, arows, label="prefill 10M")
+    for mode, idx, cnt, out in (("flat", i_f, c_f, o_f), ("tree", i_t, c_t, o_t)):
+        idx_h, cnt_h = idx.cpu().numpy(), cnt.cpu().numpy()
+        say(f"{mode} index", compare_lists(idx_h[rows], cnt_h[rows], w.q_start + rows, Y[rows], oc,
+                                          mode, ot if mode == "tree" else None, parallel=True))
+        _attn_check(w, q_rows, out.float().cpu().numpy(), idx_h, cnt_h, arows,
+                    label=f"prefill 10M {mode}")
+
+
+def test_decode_10m_flat_and_tree_steady_and_completing(ctx10m):
+    """Batch-1 decode at 10M tokens in both modes: a steady step at position
+    10,000,000 and a step whose key completes block 19,530 (position
+    9,999,871; the block is clustered and, in tree mode, the tree's right
+    edge rebuilt in the step).  Lists against the oracle; the completed block
+    and, in tree mode, every tree level against the oracle's; split attention
+    against the oracle."""
+    say("case: decode T=10M batch 1, flat and tree, steady and block-completing")
+    w, X, Y, oc, ot = ctx10m["w"], ctx10m["X"], ctx10m["Y"], ctx10m["oc"], ctx10m["ot"]
+    Tmax = w.T + 1
+    K = device_normal(w, "k", (Tmax, w.Hkv, w.D))
+    V = device_normal(w, "v", (Tmax, w.Hkv, w.D))
+    err = 0.0
+    for mode in (lsa.LSA_FLAT, lsa.LSA_TREE):
+        p = lsa.Params(k=w.k, mode=mode, beam=w.beam)
+        for n, y in ((w.T, Y[-1]), (T_FIRE, ctx10m["yf"])):
+            say(f"decode mode={mode} p={n}")
+            c = gpu_cache(X[:n], p, max_tokens=n + 1)
+            st = {}
+            idx, cnt = lsa.index_decode([c], torch.from_numpy(y[None].copy()).cuda(),
+                                        torch.from_numpy(X[n][None].copy()).cuda(), p, stats=st)
+            Q = device_normal(w, "q", (1, 1, w.Hq, w.D), row0=n)
+            splits = lsa.attention_default_splits(1, idx.shape[1])
+            out = lsa.sparse_attention(Q, K[None], V[None], idx.view(1, 1, -1), cnt.view(1, 1),
+                                       splits=splits)
+            torch.cuda.synchronize()
+            say(f"exact fallbacks: {st['exact_fallbacks']}; attention splits {splits}")
+            idx_h, cnt_h = idx.cpu().numpy(), cnt.cpu().numpy()
+            say("index", compare_lists(idx_h, cnt_h, [n], y[None], oc,
+                                       "tree" if mode == lsa.LSA_TREE else "flat",
+                                       ot if mode == lsa.LSA_TREE else None))
+            if n == T_FIRE:
+                g = _completed_block(c, X, n // 512, p)
+                if mode == lsa.LSA_TREE:
+                    compare_tree(g, ot, 1e-12, "T=10M after the completing decode step")
+            ref = attention_from_rows(w, host_rows(w, "q", [n], w.Hq * w.D)[0], idx_h[0],
+                                      int(cnt_h[0]))
+            err = max(err, float(np.abs(out.float().cpu().numpy()[0, 0] - ref).max()))
+            del c
+    say(f"decode attention max abs err {err:.3g}")
+    assert err <= 2e-2
