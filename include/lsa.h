@@ -271,6 +271,27 @@ int lsa_sparse_attention(const void* q, const void* k_cache, const void* v_cache
                          int32_t dtype, int32_t splits, void* out, void* workspace,
                          int64_t ws_bytes, void* stream);
 
+/* ------------------------------------------- allocation-free attention --
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation as lsa_sparse_attention, with the split partials kept in a
+ * fixed device array of LSA_STATIC_SCRATCH_BYTES that the library holds on
+ * every GPU it runs on (one copy per device, kept until the process ends).
+ * The caller still owns q, the K/V caches, the lists and `out`; nothing is
+ * allocated.  The array of the current device is used, so the stream must
+ * belong to the current device.  Calls that overlap on one device (on
+ * different streams) race on the array; calls on one stream do not.
+ * Returns LSA_ERR_CAPACITY when the partials, i.e.
+ * lsa_attention_workspace_bytes(B, Tq, Hq, D, splits), exceed the array
+ * (splits == 1 needs none), and otherwise what lsa_sparse_attention
+ * returns. */
+#define LSA_STATIC_SCRATCH_BYTES (16 << 20)
+int lsa_sparse_attention_static(const void* q, const void* k_cache, const void* v_cache,
+                                int32_t B, int64_t Tq, int64_t Tmax, int32_t Hq, int32_t Hkv,
+                                int32_t D, const int32_t* idx, const int32_t* count,
+                                int32_t L_max, float scale, int32_t dtype, int32_t splits,
+                                void* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -97,6 +97,8 @@ def lib():
         "lsa_attention_default_splits": (i32, [i64, i32]),
         "lsa_sparse_attention": (ctypes.c_int, [vp, vp, vp, i32, i64, i64, i32, i32, i32, vp, vp,
                                                 i32, ctypes.c_float, i32, i32, vp, vp, i64, vp]),
+        "lsa_sparse_attention_static": (ctypes.c_int, [vp, vp, vp, i32, i64, i64, i32, i32, i32, vp,
+                                                       vp, i32, ctypes.c_float, i32, i32, vp, vp]),
         "lsa_attention_launch_rows": (i64, []),
         "lsa_attention_head_major": (i32, [i32, i64, i32, i32, i32]),
     }
@@ -296,6 +298,35 @@ def sparse_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tens
     return out[0] if squeeze else out
 
 
+def sparse_attention_static(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                            idx: torch.Tensor, count: torch.Tensor, scale: float | None = None,
+                            splits: int = 1, out: torch.Tensor | None = None) -> torch.Tensor:
+    """lsa_sparse_attention_static: lsa_sparse_attention with the split partials
+    in the library's fixed device array (no workspace; allocates nothing when
+    `out` is given).  Shapes as for sparse_attention."""
+    squeeze = q.dim() == 3
+    if squeeze:
+        q, k_cache, v_cache = q[None], k_cache[None], v_cache[None]
+    B, Tq, Hq, D = q.shape
+    _, Tmax, Hkv, _ = k_cache.shape
+    if q.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("q must be bf16 or fp32")
+    dt = LSA_BF16 if q.dtype == torch.bfloat16 else LSA_F32
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, q.dtype, n)
+    _need(idx, torch.int32, "idx")
+    _need(count, torch.int32, "count")
+    if out is None:
+        out = torch.empty_like(q)
+    elif squeeze:
+        out = out[None]
+    scale = 1.0 / D ** 0.5 if scale is None else scale
+    _check("lsa_sparse_attention_static", lib().lsa_sparse_attention_static(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), B, Tq, Tmax, Hq, Hkv, D, _ptr(idx), _ptr(count),
+        idx.shape[-1], ctypes.c_float(scale), dt, splits, _ptr(out), ctypes.c_void_p(_stream())))
+    return out[0] if squeeze else out
+
+
 def attention_launch_rows() -> int:
     """lsa_attention_launch_rows: query rows per bf16 attention launch."""
     return int(lib().lsa_attention_launch_rows())
@@ -308,6 +339,7 @@ def attention_head_major(B: int, Tmax: int, Hkv: int, D: int, dtype: int) -> boo
 
 
 __all__ = ["Params", "BucketCache", "index_prefill", "index_decode", "sparse_attention",
+           "sparse_attention_static",
            "attention_launch_rows", "attention_head_major",
            "list_len", "top_buckets", "index_workspace_bytes", "exact_fallbacks", "lib",
            "LsaError",

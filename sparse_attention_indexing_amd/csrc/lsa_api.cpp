@@ -4,6 +4,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 
 #include "lsa_internal.h"
@@ -14,9 +15,37 @@ struct lsa_cache {
   CacheState st;
 };
 
+// Split partials of lsa_sparse_attention_static, for callers that cannot
+// allocate device memory: a fixed array that every GPU the library runs on
+// holds (its own copy, at its own address) until the process ends.  Host
+// code never passes this name to a kernel; it uses the address that
+// hipGetSymbolAddress returns on each device (static_scratch below).
+static __device__ __align__(256) char scratch[LSA_STATIC_SCRATCH_BYTES];
+
 namespace {
 
 constexpr int64_t kAlign = 256;
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+hipError_t static_scratch(float** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *out = reinterpret_cast<float*>(addr[dev]);
+  return hipSuccess;
+}
 
 int64_t align_up(int64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -270,8 +299,8 @@ int run_selection(const IndexCtx& ctx, const IndexWs& ws, const lsa_params* p,
 }
 
 
-// Argument checks of the attention entry point (no launch); *need receives
-// the split-partials bytes.  1 = nothing to do.
+// Argument checks shared by both attention entry points (no launch); *need
+// receives the split-partials bytes.  1 = nothing to do.
 int check_attention(const void* q, const void* k_cache, const void* v_cache, int32_t B,
                     int64_t Tq, int64_t Tmax, int32_t Hq, int32_t Hkv, int32_t D,
                     const int32_t* idx, const int32_t* count, int32_t L_max, int32_t dtype,
@@ -619,6 +648,26 @@ int lsa_sparse_attention(const void* q, const void* k_cache, const void* v_cache
   hipError_t e = launch_attention(q, k_cache, v_cache, B, Tq, Tmax, Hq, Hkv, idx, count, L_max,
                                   scale, dtype, splits, out, reinterpret_cast<float*>(workspace),
                                   as_stream(stream));
+  return hip_status(e);
+}
+
+int lsa_sparse_attention_static(const void* q, const void* k_cache, const void* v_cache,
+                                int32_t B, int64_t Tq, int64_t Tmax, int32_t Hq, int32_t Hkv,
+                                int32_t D, const int32_t* idx, const int32_t* count,
+                                int32_t L_max, float scale, int32_t dtype, int32_t splits,
+                                void* out, void* stream) {
+  int64_t need = 0;
+  const int rc = check_attention(q, k_cache, v_cache, B, Tq, Tmax, Hq, Hkv, D, idx, count, L_max,
+                                 dtype, splits, out, &need);
+  if (rc) return rc < 0 ? rc : LSA_OK;
+  if (need > LSA_STATIC_SCRATCH_BYTES) return LSA_ERR_CAPACITY;
+  float* ws = nullptr;
+  if (need > 0) {
+    hipError_t e = static_scratch(&ws);
+    if (e != hipSuccess) return LSA_ERR_HIP;
+  }
+  hipError_t e = launch_attention(q, k_cache, v_cache, B, Tq, Tmax, Hq, Hkv, idx, count, L_max,
+                                  scale, dtype, splits, out, ws, as_stream(stream));
   return hip_status(e);
 }
 

@@ -153,3 +153,23 @@ def test_attention_host_errors():
     assert L.lsa_attention_workspace_bytes(1, 16, 32, 128, 4) == 16 * 4 * 32 * 130 * 4
     assert L.lsa_status_string(-3) == b"workspace too small"
 
+
+def test_static_attention_host_errors():
+    """The allocation-free attention checks its arguments like the other entry
+    point and rejects split partials beyond its fixed array, all on the host
+    before anything is launched."""
+    L = lsa.lib()
+    f = ctypes.c_float(0.1)
+    args = lambda D=128, Hq=32, Hkv=4, dt=1, splits=1, rows=16: (
+        FAKE_DEV, FAKE_DEV, FAKE_DEV, 1, rows, 1024, Hq, Hkv, D, FAKE_DEV, FAKE_DEV, 100, f, dt,
+        splits, FAKE_DEV, None)
+    assert L.lsa_sparse_attention_static(*args(D=64)) == -2
+    assert L.lsa_sparse_attention_static(*args(Hq=30)) == -2
+    assert L.lsa_sparse_attention_static(*args(dt=5)) == -2
+    assert L.lsa_sparse_attention_static(*args(splits=0)) == -1
+    assert L.lsa_sparse_attention_static(*args(rows=0)) == 0          # nothing to do
+    # partials of 64 rows x 64 splits x 32 heads x 130 floats = 68 MB > 16 MiB
+    assert L.lsa_attention_workspace_bytes(1, 64, 32, 128, 64) > (16 << 20)
+    assert L.lsa_sparse_attention_static(*args(rows=64, splits=64)) == -4
+    assert L.lsa_sparse_attention_static(FAKE_DEV, FAKE_DEV, FAKE_DEV, 1, 16, 1024, 32, 4, 128,
+                                         None, FAKE_DEV, 100, f, 1, 1, FAKE_DEV, None) == -1
