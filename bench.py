@@ -49,6 +49,12 @@ def parse():
     ap.add_argument("--mode", default="flat", choices=["flat", "tree"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--scan", type=int, default=0, choices=[0, 1, 4, 8],
+                    help="index with a scan baseline instead of LSA buckets: a token scan (1) "
+                         "or a block scan over runs of 4 or 8 keys")
+    ap.add_argument("--baselines", action="store_true",
+                    help="LSA flat search and the token / block-4 / block-8 scans on the same "
+                         "workload, one after the other, with their step times side by side")
     ap.add_argument("--no-extra", action="store_true",
                     help="headline workload only (skip the 10M last-chunk and 16 x 1M decode "
                          "lines folded into the default run)")
@@ -559,8 +565,11 @@ def bench_whole_context(args, w, dev):
     print(json.dumps(res), flush=True)
 
 
+SCAN_NAMES = {1: "token_scan", 4: "block4_scan", 8: "block8_scan"}
+
+
 def run_prefill(w, dev, mode_name: str, steps: int, warmup: int, calib_copy: bool = False,
-                cpu_seconds: float = 0.0) -> dict:
+                cpu_seconds: float = 0.0, scan_keys: int = 0) -> dict:
     """One prefill step = build_bucket_cache over all T keys (full-context
     workloads) + lsa_index_prefill for all Tq queries + lsa_sparse_attention
     over their lists; last-chunk workloads build the cache of every full
@@ -590,7 +599,10 @@ def run_prefill(w, dev, mode_name: str, steps: int, warmup: int, calib_copy: boo
 
     mode = lsa.LSA_TREE if mode_name == "tree" else lsa.LSA_FLAT
     p = lsa.Params(k=w.k, n_sink=w.n_sink, window=w.window, mode=mode, beam=w.beam,
-                   index_dtype=lsa.LSA_BF16 if w.dtype == "bf16" else lsa.LSA_F32)
+                   index_dtype=lsa.LSA_BF16 if w.dtype == "bf16" else lsa.LSA_F32,
+                   scan_keys=scan_keys)
+    if scan_keys:
+        mode_name = SCAN_NAMES[scan_keys]
     L = lsa.list_len(p)
     nbytes = lsa.lib().lsa_cache_bytes(ctypes.byref(p.c()), w.T)
     cache_mem = torch.empty(nbytes, dtype=torch.uint8, device=dev)
@@ -664,14 +676,20 @@ def run_prefill(w, dev, mode_name: str, steps: int, warmup: int, calib_copy: boo
     log(f"per step: build {t_build:.3f} ms, index {t_index:.3f} ms, attention {t_attn:.3f} ms; "
         f"wall {ms_step:.3f} ms")
     fallbacks = lsa.exact_fallbacks(p, w.Tq, ws)
-    # flat scoring: 2 * 64 FLOP per eligible (query, bucket) pair
+    # flat scoring: 2 * 64 FLOP per eligible (query, bucket) pair; a scan
+    # scores the runs of b keys that end before the window
     pos = np.arange(w.q_start, w.T, dtype=np.int64)
-    pairs = int((64 * (pos // 512)).sum())
+    if scan_keys:
+        pairs = int((np.maximum(pos - w.window + 1, 0) // scan_keys).sum())
+    else:
+        pairs = int((64 * (pos // 512)).sum())
     kname = attention_kernel_name(lsa, w, 1, w.T)
     wname = workload_name(w.name, mode_name)
+    if not wname.endswith("_" + mode_name):
+        wname += "_" + mode_name
     roofline = attention_roofline(lsa, torch, w, idx, cnt, L, float(t_attn), kname, wname)
     res = {
-        "metric": f"prefill query tok/s per layer ({mode_name})",
+        "metric": f"prefill query tok/s per layer ({mode_name.replace('_', ' ')})",
         "value": round(w.Tq / (ms_step * 1e-3), 1),
         "unit": "query tok/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
@@ -696,6 +714,29 @@ def run_prefill(w, dev, mode_name: str, steps: int, warmup: int, calib_copy: boo
         cb = cpu_baseline(w, X, Y, cpu_seconds)
         res["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
     return res
+
+
+def bench_baselines(args, w, dev):
+    """LSA's flat search next to the in-repo baselines on the same workload:
+    the token scan and the block scans over runs of 4 and 8 keys (same
+    expansion, sinks, window and attention).  Prints one JSON line: LSA's
+    step, and each baseline's step, index and attention times with its ratio
+    to LSA's."""
+    runs = {"lsa_flat": run_prefill(w, dev, "flat", args.steps, args.warmup)}
+    for b in (1, 4, 8):
+        runs[SCAN_NAMES[b]] = run_prefill(w, dev, "flat", args.steps, args.warmup, scan_keys=b)
+    lsa_r = runs["lsa_flat"]
+    res = {k: v for k, v in lsa_r.items() if k not in ("cpu_baseline",)}
+    res["baselines"] = {}
+    for name, r in runs.items():
+        st = r["stages_ms"]
+        res["baselines"][name] = {
+            "ms_per_step": r["ms_per_step"], "stages_ms": st,
+            "index_vs_lsa": round(st["index"] / lsa_r["stages_ms"]["index"], 3),
+            "step_vs_lsa": round(r["ms_per_step"] / lsa_r["ms_per_step"], 3),
+            "scores_per_step": r["scoring"]["pairs"],
+            "exact_fallbacks": r["exact_fallbacks"]}
+    print(json.dumps(res), flush=True)
 
 
 def _extra_summary(r: dict) -> dict:
@@ -726,9 +767,12 @@ def main():
         return bench_tree_sweep(args, w, dev)
     if w.batch != 1:
         raise SystemExit("prefill timing needs a single-sequence workload (cfg 1, 2, 4, 5)")
-    headline = args.cfg == 2 and args.mode == "flat" and not args.no_extra
+    if args.baselines:
+        return bench_baselines(args, w, dev)
+    headline = args.cfg == 2 and args.mode == "flat" and not args.no_extra and not args.scan
     res = run_prefill(w, dev, args.mode, args.steps, args.warmup, args.calib_copy,
-                      0.0 if args.no_cpu_baseline or w.T > 1 << 17 else args.cpu_seconds)
+                      0.0 if args.no_cpu_baseline or w.T > 1 << 17 or args.scan
+                      else args.cpu_seconds, scan_keys=args.scan)
     if headline:
         # the metric's other ends, on the same GPU in the same run: the 10M
         # last prefill chunk (flat) and one step of the 16 x 1M decode batch

@@ -32,10 +32,11 @@
  *   - Supported shapes: d_latent 64, n_pool 4, block 512, 64 buckets per
  *     block, bucket cap 16 keys, head_dim 128, Hq % Hkv == 0,
  *     Hq / Hkv <= 16, 0 <= k <= 8192, 0 <= n_sink <= 8192,
- *     1 <= window <= 8192, and 3 * lsa_top_buckets(p) <= 8192 (the
- *     candidates of one query fit one workgroup's LDS; this holds for every
- *     k with the default window and sinks).  Anything else returns
- *     LSA_ERR_UNSUPPORTED.
+ *     1 <= window <= 8192, and the candidates of one query must fit one
+ *     workgroup's LDS: with cap = 3 * lsa_top_buckets(p) rounded up (to a
+ *     power of two up to 8,192, else to a multiple of 1,024), cap <= 16,384
+ *     and 9 * cap + 4 * k <= 147,200 bytes (this holds for every k with the
+ *     default window and sinks).  Anything else returns LSA_ERR_UNSUPPORTED.
  */
 #ifndef LSA_H
 #define LSA_H
@@ -74,15 +75,38 @@ typedef struct {
   int32_t n_sink;          /* leading keys always read (clipped to the query) */
   int32_t window;          /* recent keys always read, query included */
   int32_t mode;            /* LSA_FLAT or LSA_TREE (cache: build a tree too) */
-  int32_t beam;            /* tree beam width, 1..64 */
+  int32_t beam;            /* tree beam width, 1..512 (beyond 64 a workgroup per query) */
   int32_t leaf_level;      /* tree: level where the beam stops; -1 = smallest l
                               with beam * 2^l >= lsa_top_buckets(p) */
   int32_t index_dtype;     /* stored centroids and normalised queries: LSA_F32 | LSA_BF16 */
   int32_t exact_select;    /* 0: sampled threshold + exact fallback; 1: always exact */
+  int32_t scan_keys;       /* 0: LSA buckets.  1, 4, 8: a scan baseline instead
+                              ([72x "Why choosing costs so much"], "One real query,
+                              start to finish"): a token scan (1) scores every key,
+                              a block scan every aligned run of 4 or 8 keys; see
+                              the scan section below */
+  int32_t score_heads;     /* 0 or 1: one latent query per position.  2, 4, 8: that
+                              many query heads per position, and a bucket scores
+                              the max over the heads' dot products ([catalog "Key
+                              points"], N-LSA: bucket selection uses the max score
+                              across heads); latent_q is then [Tq, H, 64].  Flat
+                              bf16 prefill only */
+  int32_t start_level;     /* tree: -1 = the beam starts at the root.  s >= 0:
+                              every eligible node of level s is scored first and
+                              the best `beam` kept, then the beam descends (the
+                              fixed-level search of [visual "A worked example"]'s
+                              table: score coarse groups, refine inside the
+                              winners; s = leaf level is the two-stage search).
+                              Clamped to [leaf level, tree height] */
 } lsa_params;
 
 /* Fills *p with the defaults above (k = 2048, flat, bf16). */
 void lsa_default_params(lsa_params* p);
+
+/* sizeof(lsa_params) in this build: a binding checks it against its own
+ * copy of the struct before passing one (a mismatch means a binding and a
+ * library from different versions). */
+int32_t lsa_params_bytes(void);
 
 /* Human-readable name of a status code (static storage). */
 const char* lsa_status_string(int status);

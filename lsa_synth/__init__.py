@@ -129,6 +129,20 @@ def latent_rows(cfg: int, n_comp: int, comp: np.ndarray, which: str, r0: int, r1
     return mu[comp[r0:r1]] + np.float32(sigma) * eps
 
 
+def latent_query_heads(w: Workload, heads: int, r0: int, r1: int, seq: int = 0,
+                       sigma: float = 0.3) -> np.ndarray:
+    """H latent query heads per position for rows [r0, r1): [rows, H, 64] fp32.
+    Every head of a position is drawn around that position's component mean
+    with its own noise; head 0 is the single query latent_inputs returns."""
+    comp = component_runs(w.cfg, r1, w.n_comp, seq)
+    mu = mixture_means(w.cfg, w.n_comp)
+    out = np.empty((r1 - r0, heads, mu.shape[1]), np.float32)
+    for h in range(heads):
+        eps = _noise_rows(w.cfg, 3 if h == 0 else 16 + h, seq, r0, r1, mu.shape[1])
+        out[:, h] = mu[comp[r0:r1]] + np.float32(sigma) * eps
+    return out
+
+
 def latent_inputs(w: Workload, seq: int = 0, T: int | None = None, query_rows=None):
     """(X [T,64] fp32 keys, Y [rows,64] fp32 queries, comp [T]) for one sequence.
 

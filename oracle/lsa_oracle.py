@@ -68,6 +68,7 @@ class Params:
     index_dtype: str = "bf16"   # "bf16" | "f32": stored centroids and queries
     beam: int = 64              # tree beam width
     leaf_level: int = -1        # -1: automatic l*
+    start_level: int = -1       # tree: level whose nodes are all scored first; -1: the root
 
     @property
     def items_per_block(self) -> int:
@@ -373,16 +374,43 @@ def eligible_buckets(p: int, prm: Params) -> int:
     return prm.n_buckets * (p // prm.block)
 
 
+def bucket_scores(yhat: np.ndarray, cent: np.ndarray) -> np.ndarray:
+    """Score of every bucket: yhat . c.  With several query heads (yhat [H, d];
+    [catalog "Key points"], N-LSA: bucket selection uses the max score across
+    heads) a bucket's score is the largest of its H dot products."""
+    if yhat.ndim == 1:
+        return cent @ yhat
+    return (cent @ yhat.T).max(axis=1)
+
+
 def flat_rank(yhat: np.ndarray, cache: BucketCache, p: int):
     """Score every eligible bucket centroid; order by (score desc, bucket asc)."""
     ne = eligible_buckets(p, cache.params)
-    s = cache.centroids[:ne] @ yhat
+    s = bucket_scores(yhat, cache.centroids[:ne])
     order = np.lexsort((np.arange(ne), -s))
     return order, s
 
 
+def _keep_best(nodes: np.ndarray, sc: np.ndarray, width: int):
+    """The `width` best nodes by (score desc, node asc), in node order, and the
+    gap between the width-th and (width+1)-th scores (inf if all are kept)."""
+    o = np.lexsort((nodes, -sc))
+    gap = math.inf
+    if len(o) > width:
+        srt = sc[o]
+        gap = srt[width - 1] - srt[width]
+    return np.sort(nodes[o[:width]]), gap
+
+
 def tree_rank(yhat: np.ndarray, cache: BucketCache, tree: Tree, p: int):
-    """Beam descent from the root, then flat ranking under the final beam.
+    """Beam descent, then flat ranking under the final beam.
+
+    The descent starts at the root, or -- with prm.start_level = s below the
+    root -- by scoring every eligible node of level s and keeping the best
+    `beam` of them: the coarse first stage of the fixed-level search in
+    [visual "A worked example"]'s table of search styles (score coarse groups,
+    then refine inside the winners).  With s = l* that is the two-stage search;
+    in between, a flat first stage and a beam below it.
 
     Returns (ranked buckets, bucket scores (NaN where not scored), smallest
     beam-boundary gap, number of node scores).
@@ -399,8 +427,16 @@ def tree_rank(yhat: np.ndarray, cache: BucketCache, tree: Tree, p: int):
         order, s = flat_rank(yhat, cache, p)
         s_all[:len(s)] = s
         return order, s_all, beam_gap, len(s)
-    beam = np.array([0])                      # the root, at level H
-    for lvl in range(H - 1, lstar - 1, -1):
+    S = H if prm.start_level < 0 else min(max(prm.start_level, lstar), H)
+    if S == H:
+        beam = np.array([0])                  # the root, at level H
+    else:
+        lv = tree.levels[S]
+        nodes = np.flatnonzero(lv["min_block"] < qb)
+        sc = lv["cent"][nodes] @ yhat
+        n_scores += len(nodes)
+        beam, beam_gap = _keep_best(nodes, sc, prm.beam)
+    for lvl in range(S - 1, lstar - 1, -1):
         above = tree.levels[lvl + 1]
         here = tree.levels[lvl]
         kids = above["child"][beam].ravel()
@@ -485,7 +521,8 @@ class IndexResult:
 def index_query(y: np.ndarray, p: int, cache: BucketCache, mode: str = "flat",
                 tree: Tree | None = None) -> IndexResult:
     """Index list of the query at position p: sorted(near | far), one list shared
-    by every head [visual "What one query actually does"]."""
+    by every head [visual "What one query actually does"].  y [d], or [H, d]
+    for max-over-heads bucket scores (flat mode)."""
     prm = cache.params
     yhat = normalize_query(y, prm.index_dtype)
     beam_gap = math.inf

@@ -31,7 +31,8 @@ class LsaError(RuntimeError):
 class _Params(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "d_latent", "n_pool", "block_keys", "n_buckets", "bucket_cap_keys", "k", "n_sink",
-        "window", "mode", "beam", "leaf_level", "index_dtype", "exact_select")]
+        "window", "mode", "beam", "leaf_level", "index_dtype", "exact_select", "scan_keys",
+        "score_heads", "start_level")]
 
 
 class _View(ctypes.Structure):
@@ -54,6 +55,9 @@ class Params:
     leaf_level: int = -1
     index_dtype: int = LSA_BF16
     exact_select: int = 0
+    scan_keys: int = 0            # 0: LSA buckets; 1 / 4 / 8: token / block scan baseline
+    score_heads: int = 0          # 2 / 4 / 8: query heads per position, max-over-heads scores
+    start_level: int = -1         # tree: level scored in full first (-1: start at the root)
     d_latent: int = 64
     n_pool: int = 4
     block_keys: int = 512
@@ -106,6 +110,12 @@ def lib():
         f = getattr(L, name)
         f.restype = res
         f.argtypes = args
+    L.lsa_params_bytes.restype = i32
+    L.lsa_params_bytes.argtypes = []
+    if L.lsa_params_bytes() != ctypes.sizeof(_Params):
+        raise RuntimeError(f"{LIB_PATH} was built with another lsa_params layout "
+                           f"({L.lsa_params_bytes()} bytes, the binding has "
+                           f"{ctypes.sizeof(_Params)}): rebuild the library")
     _lib = L
     return L
 
@@ -196,7 +206,7 @@ class BucketCache:
         nb = v.n_buckets
         out = dict(n_tokens=v.n_tokens, n_blocks=v.n_blocks, n_buckets=nb,
                    centroids=sub(v.centroids, nb * 64 * esz, dt, (nb, 64)),
-                   members=sub(v.members, nb * 4, torch.int32, (nb,)),
+                   members=None if not v.members else sub(v.members, nb * 4, torch.int32, (nb,)),
                    tree_height=v.tree_height, levels=[])
         for l in range(1, v.tree_height + 1):
             n = v.level_nodes[l]
@@ -215,6 +225,8 @@ def index_prefill(cache: BucketCache, latent_q: torch.Tensor, q_start: int, p: P
     bucket selection took the exact fallback (this synchronises)."""
     _need(latent_q, torch.float32, "latent_q")
     Tq = latent_q.shape[0]
+    if p.score_heads > 1 and (latent_q.dim() != 3 or latent_q.shape[1] != p.score_heads):
+        raise ValueError("latent_q must be [Tq, score_heads, 64] with several query heads")
     L = list_len(p)
     dev = latent_q.device
     if out is None:

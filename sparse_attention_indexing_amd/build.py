@@ -46,7 +46,17 @@ def _compile(src: str, obj: str, extra=()):
 
 
 def build(verbose: bool = True) -> list[str]:
+    """Compile and link both libraries.  Builds hold an exclusive lock on
+    _build/.lock, so two builds started together run one after the other
+    instead of writing the same objects at once."""
+    import fcntl
     os.makedirs(BUILD, exist_ok=True)
+    with open(os.path.join(BUILD, ".lock"), "w") as lock:
+        fcntl.flock(lock, fcntl.LOCK_EX)
+        return _build(verbose)
+
+
+def _build(verbose: bool) -> list[str]:
     jobs = []
     for s in LIB_SOURCES:
         jobs.append((os.path.join(CSRC, s), os.path.join(BUILD, s + ".o")))

@@ -62,6 +62,15 @@ int check_structure(const lsa_params* p) {
     return LSA_ERR_UNSUPPORTED;
   if (p->index_dtype != LSA_F32 && p->index_dtype != LSA_BF16) return LSA_ERR_UNSUPPORTED;
   if (p->mode != LSA_FLAT && p->mode != LSA_TREE) return LSA_ERR_UNSUPPORTED;
+  if (p->scan_keys != 0 && p->scan_keys != 1 && p->scan_keys != 4 && p->scan_keys != 8)
+    return LSA_ERR_UNSUPPORTED;
+  if (p->scan_keys && p->mode != LSA_FLAT) return LSA_ERR_UNSUPPORTED;
+  if (p->score_heads < 0 || p->score_heads > 8 || (p->score_heads & (p->score_heads - 1)))
+    return LSA_ERR_UNSUPPORTED;
+  // several query heads: flat bf16 prefill over LSA buckets
+  if (p->score_heads > 1 &&
+      (p->mode != LSA_FLAT || p->scan_keys || p->index_dtype != LSA_BF16))
+    return LSA_ERR_UNSUPPORTED;
   return LSA_OK;
 }
 
@@ -69,9 +78,13 @@ int check_query(const lsa_params* p) {
   if (p->k < 0 || p->k > kMaxK) return LSA_ERR_UNSUPPORTED;
   if (p->n_sink < 0 || p->n_sink > kMaxWindow) return LSA_ERR_UNSUPPORTED;
   if (p->window < 1 || p->window > kMaxWindow) return LSA_ERR_UNSUPPORTED;
-  if (p->beam < 1 || p->beam > kMaxBeam) return LSA_ERR_UNSUPPORTED;
+  if (p->beam < 1 || p->beam > kMaxBeamWide) return LSA_ERR_UNSUPPORTED;
+  if (p->start_level < -1 || p->start_level >= kMaxLevels) return LSA_ERR_UNSUPPORTED;
   if (p->leaf_level < -1 || p->leaf_level >= kMaxLevels) return LSA_ERR_UNSUPPORTED;
   if (p->exact_select != 0 && p->exact_select != 1) return LSA_ERR_UNSUPPORTED;
+  // a scan's runs are summarised block by block, so every run it scores must
+  // lie in a complete block: the window has to cover the query's own block
+  if (p->scan_keys && p->window < kBlock) return LSA_ERR_UNSUPPORTED;
   return LSA_OK;
 }
 
@@ -81,13 +94,21 @@ int check_query(const lsa_params* p) {
 // of each eligible block the window reaches back into, and one per pooled
 // item of the sinks.  (Default window 512 and 4 sinks: ceil(k / 4) + 65.)
 int32_t top_b(const lsa_params* p) {
+  if (p->scan_keys) {
+    // a scan's eligible runs end before the window; only runs holding a
+    // sink give fewer than scan_keys far keys
+    return (p->k + p->scan_keys - 1) / p->scan_keys + (p->n_sink + p->scan_keys - 1) / p->scan_keys;
+  }
   const int32_t win_blocks = (p->window - 1 + kBlock - 1) / kBlock;
   return (p->k + kPool - 1) / kPool + kBuckets * win_blocks + (p->n_sink + kPool - 1) / kPool;
 }
 
-// candidate slots per query: a power of two >= 3 B (tau aims at ~2 B)
+// candidate slots per query: >= 3 B (tau aims at ~2 B): a power of two up to
+// 8,192, beyond that a multiple of 1,024
 int32_t cand_cap(const lsa_params* p) {
-  int c = pow2_ceil(3 * (int64_t)top_b(p));
+  const int64_t want = 3 * (int64_t)top_b(p);
+  if (want > 8192) return (int32_t)((want + 1023) / 1024 * 1024);
+  int c = pow2_ceil(want);
   return c < 256 ? 256 : c;
 }
 
@@ -98,19 +119,24 @@ int leaf_level(const lsa_params* p) {
   return l;
 }
 
-CacheLayout make_layout(int64_t max_blocks, int dtype, int tree) {
+// rows of the centroid table per full block: 64 buckets, or a scan's runs
+int64_t rows_per_block(const lsa_params* p) {
+  return p->scan_keys ? kBlock / p->scan_keys : kBuckets;
+}
+
+CacheLayout make_layout(int64_t max_blocks, int dtype, int tree, int64_t per_block) {
   CacheLayout L;
   memset(&L, 0, sizeof(L));
   L.max_blocks = max_blocks;
   const int64_t esz = (int64_t)idx_elem_bytes(dtype);
-  const int64_t nb = max_blocks * kBuckets;
+  const int64_t nb = max_blocks * per_block;
   int64_t off = 0;
   L.off_staging = off;
   off = align_up(off + (int64_t)kBlock * kLatent * 4);
   L.off_cent = off;
   off = align_up(off + nb * kLatent * esz);
   L.off_members = off;
-  off = align_up(off + nb * 4);
+  if (per_block == kBuckets) off = align_up(off + nb * 4);   // scans keep no member table
   L.lvl_cap[0] = nb;
   L.n_levels = 0;
   if (tree && nb > 1) {
@@ -182,18 +208,24 @@ int append_keys(CacheState& c, const float* keys, int64_t n, hipStream_t s) {
     if (e != hipSuccess) return LSA_ERR_HIP;
     used = take;
     if (r + take == kBlock) {
-      e = launch_ward_blocks(stg, c.n_blocks, 1, c.base + c.lay.off_cent,
-                             reinterpret_cast<uint32_t*>(c.base + c.lay.off_members),
-                             c.prm.index_dtype, s);
+      e = c.prm.scan_keys
+              ? launch_scan_blocks(stg, c.n_blocks, 1, c.base + c.lay.off_cent, c.prm.scan_keys,
+                                   c.prm.index_dtype, s)
+              : launch_ward_blocks(stg, c.n_blocks, 1, c.base + c.lay.off_cent,
+                                   reinterpret_cast<uint32_t*>(c.base + c.lay.off_members),
+                                   c.prm.index_dtype, s);
       if (e != hipSuccess) return LSA_ERR_HIP;
       c.n_blocks += 1;
     }
   }
   const int64_t full = (n - used) / kBlock;
   if (full > 0) {
-    e = launch_ward_blocks(keys + used * kLatent, c.n_blocks, full, c.base + c.lay.off_cent,
-                           reinterpret_cast<uint32_t*>(c.base + c.lay.off_members),
-                           c.prm.index_dtype, s);
+    e = c.prm.scan_keys
+            ? launch_scan_blocks(keys + used * kLatent, c.n_blocks, full, c.base + c.lay.off_cent,
+                                 c.prm.scan_keys, c.prm.index_dtype, s)
+            : launch_ward_blocks(keys + used * kLatent, c.n_blocks, full, c.base + c.lay.off_cent,
+                                 reinterpret_cast<uint32_t*>(c.base + c.lay.off_members),
+                                 c.prm.index_dtype, s);
     if (e != hipSuccess) return LSA_ERR_HIP;
     c.n_blocks += full;
     used += full * kBlock;
@@ -213,11 +245,13 @@ struct WsLayout {
   int64_t off_yhat, off_tau, off_cnt, off_status, off_hist, off_cand, total;
 };
 
+int heads(const lsa_params* p) { return p->score_heads > 1 ? p->score_heads : 1; }
+
 WsLayout index_ws_layout(const lsa_params* p, int64_t nq) {
   WsLayout w;
   int64_t off = 0;
   w.off_yhat = off;
-  off = align_up(off + nq * kLatent * (int64_t)idx_elem_bytes(p->index_dtype));
+  off = align_up(off + nq * heads(p) * kLatent * (int64_t)idx_elem_bytes(p->index_dtype));
   w.off_tau = off;
   off = align_up(off + nq * 4);
   w.off_cnt = off;
@@ -254,6 +288,8 @@ IndexCtx base_ctx(const lsa_params* p, int64_t n) {
   ctx.top_b = top_b(p);
   ctx.cap = cand_cap(p);
   ctx.list_len = p->n_sink + p->window + p->k;
+  ctx.run_keys = p->scan_keys;
+  ctx.heads = heads(p);
   return ctx;
 }
 
@@ -263,6 +299,12 @@ TreeCtx make_tree_ctx(const CacheState& c, const lsa_params* p) {
   tc.height = c.height;
   tc.lstar = leaf_level(p);
   tc.beam = p->beam;
+  // the first stage's level: the root (height), or s clamped to [l*, height]
+  tc.start = c.height;
+  if (p->start_level >= 0 && p->start_level < c.height)
+    tc.start = p->start_level > tc.lstar ? p->start_level : tc.lstar;
+  tc.nodes[0] = c.n_blocks * kBuckets;
+  for (int l = 1; l <= c.height; ++l) tc.nodes[l] = c.level_n[l];
   tc.cent[0] = lvl_cent(c, 0);
   for (int l = 1; l <= c.height; ++l) {
     tc.cent[l] = lvl_cent(c, l);
@@ -289,7 +331,7 @@ int run_selection(const IndexCtx& ctx, const IndexWs& ws, const lsa_params* p,
     e = launch_thresh(ctx, ws, dt, s);
     if (e != hipSuccess) return LSA_ERR_HIP;
     if (!p->exact_select) {
-      e = launch_score_filter(ctx, ws, dt, max_elig / 32, s);
+      e = launch_score_filter(ctx, ws, dt, (max_elig + 31) / 32, s);
       if (e != hipSuccess) return LSA_ERR_HIP;
     }
     exact_mode = p->exact_select ? 2 : 1;
@@ -324,6 +366,8 @@ int check_attention(const void* q, const void* k_cache, const void* v_cache, int
 
 extern "C" {
 
+int32_t lsa_params_bytes(void) { return (int32_t)sizeof(lsa_params); }
+
 void lsa_default_params(lsa_params* p) {
   if (!p) return;
   p->d_latent = kLatent;
@@ -339,6 +383,9 @@ void lsa_default_params(lsa_params* p) {
   p->leaf_level = -1;
   p->index_dtype = LSA_BF16;
   p->exact_select = 0;
+  p->scan_keys = 0;
+  p->score_heads = 0;
+  p->start_level = -1;
 }
 
 const char* lsa_status_string(int status) {
@@ -362,6 +409,8 @@ int lsa_check_params(const lsa_params* p) {
   if (rc) return rc;
   // the selection holds every candidate of a query in one workgroup's LDS
   if (cand_cap(p) > kMaxCap) return LSA_ERR_UNSUPPORTED;
+  if ((int64_t)cand_cap(p) * 9 + 4 * (int64_t)(p->k > 1 ? p->k : 1) > kSelectLdsMax)
+    return LSA_ERR_UNSUPPORTED;
   if (p->mode == LSA_TREE && ((int64_t)p->beam << leaf_level(p)) > cand_cap(p))
     return LSA_ERR_UNSUPPORTED;
   return LSA_OK;
@@ -383,7 +432,8 @@ int64_t lsa_cache_bytes(const lsa_params* p, int64_t max_tokens) {
   int rc = lsa_check_params(p);
   if (rc) return rc;
   if (max_tokens < 0 || max_tokens > (int64_t)0x7fffffff) return LSA_ERR_ARG;
-  return make_layout(max_tokens / kBlock, p->index_dtype, p->mode == LSA_TREE).total;
+  return make_layout(max_tokens / kBlock, p->index_dtype, p->mode == LSA_TREE,
+                     rows_per_block(p)).total;
 }
 
 int lsa_cache_init(const lsa_params* p, int64_t max_tokens, void* cache_mem, int64_t bytes,
@@ -393,7 +443,8 @@ int lsa_cache_init(const lsa_params* p, int64_t max_tokens, void* cache_mem, int
   if (rc) return rc;
   if (max_tokens < 0 || max_tokens > (int64_t)0x7fffffff) return LSA_ERR_ARG;
   if (reinterpret_cast<uintptr_t>(cache_mem) % kAlign) return LSA_ERR_ARG;
-  CacheLayout lay = make_layout(max_tokens / kBlock, p->index_dtype, p->mode == LSA_TREE);
+  CacheLayout lay = make_layout(max_tokens / kBlock, p->index_dtype, p->mode == LSA_TREE,
+                                rows_per_block(p));
   if (bytes < lay.total) return LSA_ERR_CAPACITY;
   lsa_cache* c = new (std::nothrow) lsa_cache;
   if (!c) return LSA_ERR_ARG;
@@ -425,12 +476,12 @@ int lsa_cache_get_view(const lsa_cache* c, lsa_cache_view* out) {
   const CacheState& s = c->st;
   out->n_tokens = s.n_tokens;
   out->n_blocks = s.n_blocks;
-  out->n_buckets = s.n_blocks * kBuckets;
+  out->n_buckets = s.n_blocks * rows_per_block(&s.prm);
   out->centroids = s.base + s.lay.off_cent;
-  out->members = reinterpret_cast<uint32_t*>(s.base + s.lay.off_members);
+  out->members = s.prm.scan_keys ? nullptr : reinterpret_cast<uint32_t*>(s.base + s.lay.off_members);
   out->staging = reinterpret_cast<float*>(s.base + s.lay.off_staging);
   out->tree_height = s.tree ? s.height : 0;
-  out->level_nodes[0] = s.n_blocks * kBuckets;
+  out->level_nodes[0] = s.n_blocks * rows_per_block(&s.prm);
   if (s.tree) {
     for (int l = 1; l <= s.height; ++l) {
       out->level_nodes[l] = s.level_n[l];
@@ -471,7 +522,7 @@ int lsa_index_prefill(const lsa_cache* c, const float* latent_q, int64_t q_start
   int rc = lsa_check_params(p);
   if (rc) return rc;
   const CacheState& st = c->st;
-  if (p->index_dtype != st.prm.index_dtype) return LSA_ERR_ARG;
+  if (p->index_dtype != st.prm.index_dtype || p->scan_keys != st.prm.scan_keys) return LSA_ERR_ARG;
   if (Tq == 0) return LSA_OK;
   if (!latent_q || !idx || !count || !workspace) return LSA_ERR_ARG;
   if (q_start + Tq > (int64_t)0x7fffffff) return LSA_ERR_ARG;
@@ -488,9 +539,10 @@ int lsa_index_prefill(const lsa_cache* c, const float* latent_q, int64_t q_start
   ctx.per_seq = 0;
   ctx.cent[0] = lvl_cent(st, 0);
   ctx.members[0] = reinterpret_cast<const uint32_t*>(st.base + st.lay.off_members);
-  hipError_t e = launch_qnorm(latent_q, Tq, ws.yhat, p->index_dtype, nullptr, s);
+  hipError_t e = launch_qnorm(latent_q, Tq * heads(p), ws.yhat, p->index_dtype, nullptr, s);
   if (e != hipSuccess) return LSA_ERR_HIP;
-  const int64_t max_elig = (last / kBlock) * kBuckets;
+  int64_t max_elig = (last / kBlock) * kBuckets;
+  if (p->scan_keys) max_elig = (last - p->window + 1 > 0 ? last - p->window + 1 : 0) / p->scan_keys;
   TreeCtx tc;
   const TreeCtx* tp = nullptr;
   if (tree && st.height > 0 && leaf_level(p) < st.height) {
@@ -506,6 +558,7 @@ int lsa_index_decode(lsa_cache* const* caches, int32_t B, const float* latent_q,
   if (!caches || !p || B < 0 || B > kMaxDecode) return LSA_ERR_ARG;
   int rc = lsa_check_params(p);
   if (rc) return rc;
+  if (p->scan_keys || p->score_heads > 1) return LSA_ERR_UNSUPPORTED;   // prefill variants
   if (B == 0) return LSA_OK;
   if (!latent_q || !latent_k_new || !idx || !count || !workspace) return LSA_ERR_ARG;
   const bool tree = p->mode == LSA_TREE;

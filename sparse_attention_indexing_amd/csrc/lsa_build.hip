@@ -554,6 +554,90 @@ hipError_t launch_ward_jobs(const WardJobs& jobs, int n, int dtype, hipStream_t 
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ scan baselines
+// Run summaries of the scan baselines ([72x "Why choosing costs so much"]: a
+// token scan scores every key, a block scan every run of adjacent keys): for
+// each aligned run of b keys of a full block, the unit vector of the sum of
+// its unit keys (fp64, as the bucket centroids), rounded to the index dtype;
+// for b = 1 the unit key itself.  One workgroup per block; a quad of lanes
+// (16 dims each) owns one run at a time.
+template <int DT>
+__global__ __launch_bounds__(256) void k_scan_blocks(const float* __restrict__ keys,
+                                                     int64_t first_block, void* cent, int b) {
+  const int64_t blk = blockIdx.x;
+  const float* src = keys + blk * kBlock * kLatent;
+  const int tid = threadIdx.x, q = tid & 3;
+  const int runs = kBlock / b;
+#pragma unroll 1
+  for (int r = tid >> 2; r < runs; r += 64) {
+    double acc[16];
+#pragma unroll
+    for (int d = 0; d < 16; ++d) acc[d] = 0.0;
+#pragma unroll 1
+    for (int i = 0; i < b; ++i) {
+      const float4* row = reinterpret_cast<const float4*>(src + (int64_t)(r * b + i) * kLatent + 16 * q);
+      float x[16];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float4 f = row[v];
+        x[4 * v] = f.x; x[4 * v + 1] = f.y; x[4 * v + 2] = f.z; x[4 * v + 3] = f.w;
+      }
+      double ss = 0.0;
+#pragma unroll
+      for (int d = 0; d < 16; ++d) ss = __builtin_fma((double)x[d], (double)x[d], ss);
+      ss = quad_sum_f64(ss);
+      const double nrm = __builtin_sqrt(ss);
+      const bool zero = nrm < 1e-30;
+#pragma unroll
+      for (int d = 0; d < 16; ++d) acc[d] += zero ? 0.0 : (double)x[d] / nrm;
+    }
+    double ss = 0.0;
+#pragma unroll
+    for (int d = 0; d < 16; ++d) ss = __builtin_fma(acc[d], acc[d], ss);
+    ss = quad_sum_f64(ss);
+    const double nrm = __builtin_sqrt(ss);
+    const bool zero = nrm < 1e-30;
+    const int64_t row = (first_block + blk) * runs + r;
+    if constexpr (DT == LSA_BF16) {
+      uint16_t* dst = reinterpret_cast<uint16_t*>(cent) + row * kLatent + 16 * q;
+      uint32_t w[8];
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        const uint16_t lo = f64_to_bf16_rne(zero ? 0.0 : acc[2 * d] / nrm);
+        const uint16_t hi = f64_to_bf16_rne(zero ? 0.0 : acc[2 * d + 1] / nrm);
+        w[d] = (uint32_t)lo | ((uint32_t)hi << 16);
+      }
+      uint4* o = reinterpret_cast<uint4*>(dst);
+      o[0] = make_uint4(w[0], w[1], w[2], w[3]);
+      o[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    } else {
+      float4* o = reinterpret_cast<float4*>(reinterpret_cast<float*>(cent) + row * kLatent + 16 * q);
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        o[v] = make_float4((float)(zero ? 0.0 : acc[4 * v] / nrm), (float)(zero ? 0.0 : acc[4 * v + 1] / nrm),
+                           (float)(zero ? 0.0 : acc[4 * v + 2] / nrm), (float)(zero ? 0.0 : acc[4 * v + 3] / nrm));
+    }
+  }
+}
+
+hipError_t launch_scan_blocks(const float* keys, int64_t first_block, int64_t n_blocks, void* cent,
+                              int run_keys, int dtype, hipStream_t s) {
+  if (n_blocks <= 0) return hipSuccess;
+  for (int64_t b0 = 0; b0 < n_blocks; b0 += 65535) {
+    const int64_t nb = n_blocks - b0 < 65535 ? n_blocks - b0 : 65535;
+    const float* src = keys + b0 * kBlock * kLatent;
+    if (dtype == LSA_BF16)
+      hipLaunchKernelGGL(k_scan_blocks<LSA_BF16>, dim3((unsigned)nb), dim3(256), 0, s, src,
+                         first_block + b0, cent, run_keys);
+    else
+      hipLaunchKernelGGL(k_scan_blocks<LSA_F32>, dim3((unsigned)nb), dim3(256), 0, s, src,
+                         first_block + b0, cent, run_keys);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 hipError_t launch_copy_rows(float* dst, const float* src, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   const int64_t total = n * (kLatent / 4);

@@ -54,8 +54,14 @@ __device__ __forceinline__ const void* qcent(const IndexCtx& c, int64_t i) {
 __device__ __forceinline__ const uint32_t* qmem(const IndexCtx& c, int64_t i) {
   return c.per_seq ? c.members[i] : c.members[0];
 }
-// buckets of complete blocks before the query's own block
-__device__ __forceinline__ int64_t n_eligible(int64_t p) { return (int64_t)kBuckets * (p / kBlock); }
+// Buckets a query at position p scores.  LSA: the buckets of complete
+// blocks before the query's own block.  Scans (ctx.run_keys = b): every run
+// of b consecutive keys that ends before the window starts.
+__host__ __device__ __forceinline__ int64_t n_eligible(const IndexCtx& c, int64_t p) {
+  if (c.run_keys == 0) return (int64_t)kBuckets * (p / kBlock);
+  const int64_t w_start = p - c.window + 1 > 0 ? p - c.window + 1 : 0;
+  return w_start / c.run_keys;
+}
 
 // Query held by column `col` of wave `wave` in query tile `qt` of an MFMA
 // kernel.  Prefill: 32 queries per wave sharing one cache.  Decode: one query
@@ -213,7 +219,7 @@ __global__ __launch_bounds__(256) void k_thresh(IndexCtx ctx, IndexWs ws) {
   const int col = lane & 31, half = lane >> 5;
   const int64_t qi = mfma_query(ctx, blockIdx.x, wave, col);
   const bool valid = qi >= 0 && qi < ctx.n;
-  const int64_t ne = valid ? n_eligible(qpos(ctx, qi)) : 0;
+  const int64_t ne = valid ? n_eligible(ctx, qpos(ctx, qi)) : 0;
   QFrag qf;
   load_qfrag<DT>(qf, ws.yhat, valid ? qi : 0, valid, half);
   // loop bound: the wave's largest eligible count
@@ -245,7 +251,7 @@ __global__ __launch_bounds__(256) void k_thresh(IndexCtx ctx, IndexWs ws) {
   if (tid < kQueriesPerWg) {
     const int64_t qj = mfma_query(ctx, blockIdx.x, tid >> 5, tid & 31);
     if (qj >= 0 && qj < ctx.n) {
-      const int64_t nej = n_eligible(qpos(ctx, qj));
+      const int64_t nej = n_eligible(ctx, qpos(ctx, qj));
       float tau = -3.0e38f;
       if (nej > ctx.cap) {
         // expect ~2 B full-set scores above tau: 2 B / 16 samples above it
@@ -274,7 +280,7 @@ __global__ __launch_bounds__(256) void k_thresh_hist(IndexCtx ctx, IndexWs ws) {
   const int col = lane & 31, half = lane >> 5;
   const int64_t qi = mfma_query(ctx, blockIdx.y, wave, col);
   const bool valid = qi >= 0 && qi < ctx.n;
-  const int64_t ne = valid ? n_eligible(qpos(ctx, qi)) : 0;
+  const int64_t ne = valid ? n_eligible(ctx, qpos(ctx, qi)) : 0;
   int64_t wmax = ne;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
@@ -312,7 +318,7 @@ __global__ __launch_bounds__(256) void k_thresh_hist(IndexCtx ctx, IndexWs ws) {
 __global__ __launch_bounds__(64) void k_thresh_tau(IndexCtx ctx, IndexWs ws, int preset_all) {
   const int64_t qj = (int64_t)blockIdx.x * 64 + threadIdx.x;
   if (qj >= ctx.n) return;
-  const int64_t nej = n_eligible(qpos(ctx, qj));
+  const int64_t nej = n_eligible(ctx, qpos(ctx, qj));
   float tau = -3.0e38f;
   if (nej > ctx.cap) {
     const int64_t want = (2 * (int64_t)ctx.top_b + kSampleStride - 1) / kSampleStride;
@@ -336,7 +342,7 @@ __global__ __launch_bounds__(256) void k_score_filter(IndexCtx ctx, IndexWs ws, 
   const int col = lane & 31, half = lane >> 5;
   const int64_t qi = mfma_query(ctx, blockIdx.y, wave, col);
   const bool valid = qi >= 0 && qi < ctx.n;
-  const int64_t ne = valid ? n_eligible(qpos(ctx, qi)) : 0;
+  const int64_t ne = valid ? n_eligible(ctx, qpos(ctx, qi)) : 0;
   int64_t wmax = ne;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
@@ -344,7 +350,7 @@ __global__ __launch_bounds__(256) void k_score_filter(IndexCtx ctx, IndexWs ws, 
     wmax = o > wmax ? o : wmax;
   }
   const int64_t t0 = (int64_t)blockIdx.x * seg_tiles;
-  int64_t t1 = wmax / kTile;
+  int64_t t1 = (wmax + kTile - 1) / kTile;   // a scan's last tile may be partial
   if (t1 > t0 + seg_tiles) t1 = t0 + seg_tiles;
   if (t0 >= t1) return;
   QFrag qf;
@@ -487,7 +493,7 @@ __device__ __forceinline__ int32_t load_qcols(QColsN<NG>& c, const IndexCtx& ctx
     const int64_t qi = q0 + 32 * j + col;
     const bool valid = qi < ctx.n;
     c.qi[j] = valid ? (int32_t)qi : 0;
-    c.ne[j] = valid ? (int32_t)n_eligible(ctx.q_start + qi) : 0;
+    c.ne[j] = valid ? (int32_t)n_eligible(ctx, ctx.q_start + qi) : 0;
     c.tau[j] = (valid && tau) ? tau[qi] : 3.0e38f;
     c.all[j] = valid && c.ne[j] <= ctx.cap;
     nmax = c.ne[j] > nmax ? c.ne[j] : nmax;
@@ -715,7 +721,7 @@ __global__ __launch_bounds__(256, 2) void k_score_lowpass(IndexCtx ctx, IndexWs 
     const bool valid = q0 + tid < ctx.n;
     L.cnt[tid] = 0;
     L.tau[tid] = valid ? ws.tau[q0 + tid] : 3.0e38f;
-    L.ne[tid] = valid ? (int32_t)n_eligible(ctx.q_start + q0 + tid) : 0;
+    L.ne[tid] = valid ? (int32_t)n_eligible(ctx, ctx.q_start + q0 + tid) : 0;
   }
   QGroups<NG> q;
   load_q128(q, ws.yhat, q0, ctx.n, col, half);
@@ -833,7 +839,7 @@ __global__ __launch_bounds__(512, 1) void k_thresh_q128(IndexCtx ctx, IndexWs ws
   if (tid < kQueriesPerWg) {
     const int64_t qj = q0 + tid;
     if (qj < ctx.n) {
-      const int64_t nej = n_eligible(ctx.q_start + qj);
+      const int64_t nej = n_eligible(ctx, ctx.q_start + qj);
       float tau = -3.0e38f;
       if (nej > ctx.cap) {
         const int64_t want = (2 * (int64_t)ctx.top_b + kSampleStride - 1) / kSampleStride;
@@ -853,6 +859,199 @@ __global__ __launch_bounds__(512, 1) void k_thresh_q128(IndexCtx ctx, IndexWs ws
 __global__ __launch_bounds__(256) void k_fill_u32(uint32_t* p, int64_t n, uint32_t v) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = v;
+}
+
+// ------------------------------------------------------------------ max over query heads
+// [catalog "Key points"], N-LSA: bucket selection uses the max score across
+// heads.  A query position brings H query heads (ctx.heads = 2, 4 or 8); a
+// bucket's score is the largest of its H dot products.  Prefill, bf16: a
+// workgroup takes NQ = 128 / H query positions, whose 128 head vectors form
+// the A operand of 32x32x16 MFMAs (4 groups of 32 rows, held by every wave),
+// and a tile of 32 buckets the B operand, so a lane holds one bucket's scores
+// against 16 head rows of a group; rows 8 (r / 4) + 4 half + (r % 4) are H
+// consecutive heads of one position, so the max over heads is a max over
+// min(H, 4) registers (and, for H = 8, over the lane pair 32 apart).
+template <int H>
+__device__ __forceinline__ void load_heads(bf16x8 (&a)[4][4], const void* yhat, int64_t q0,
+                                           int64_t n, int col, int half) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = 32 * j + col;                       // workgroup-local head row
+    const int64_t qi = q0 + row / H;
+    const bool valid = qi < n;
+    const uint4* src = reinterpret_cast<const uint4*>(
+        reinterpret_cast<const uint16_t*>(yhat) + ((valid ? qi : 0) * H + row % H) * kLatent +
+        32 * half);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      a[j][kk] = __builtin_bit_cast(bf16x8, valid ? src[kk] : make_uint4(0, 0, 0, 0));
+  }
+}
+
+// Scores of one group j: m[i] = the max over heads of the i-th position this
+// lane holds (E = 16 / min(H, 4) of them), position (workgroup-local)
+// mh_pos<H>(j, i, half).
+template <int H>
+__device__ __forceinline__ void mh_max(const f32x16& acc, float (&m)[16 / (H < 4 ? H : 4)]) {
+  constexpr int R = H < 4 ? H : 4;
+#pragma unroll
+  for (int i = 0; i < 16 / R; ++i) {
+    float x = acc[R * i];
+#pragma unroll
+    for (int u = 1; u < R; ++u) x = fmaxf(x, acc[R * i + u]);
+    if constexpr (H == 8) x = fmaxf(x, __shfl_xor(x, 32, 64));
+    m[i] = x;
+  }
+}
+
+template <int H>
+__device__ __forceinline__ int mh_pos(int j, int i, int half) {
+  // the first head row of value i: 8 (i R / 4) + 4 half + (i R) % 4
+  constexpr int R = H < 4 ? H : 4;
+  const int row = 8 * ((R * i) >> 2) + (H == 8 ? 0 : 4 * half) + ((R * i) & 3);
+  return (32 * j + row) / H;
+}
+
+template <int H>
+__global__ __launch_bounds__(256) void k_mh_thresh(IndexCtx ctx, IndexWs ws) {
+  constexpr int NQ = 128 / H;
+  constexpr int E = 16 / (H < 4 ? H : 4);
+  __shared__ uint32_t hist[NQ][kBins];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31, half = lane >> 5;
+  const int64_t q0 = (int64_t)blockIdx.x * NQ;
+  for (int i = tid; i < NQ * kBins; i += 256) (&hist[0][0])[i] = 0;
+  const int64_t qlast = q0 + NQ - 1 < ctx.n - 1 ? q0 + NQ - 1 : ctx.n - 1;
+  const int64_t nmax = n_eligible(ctx, qpos(ctx, qlast));        // grows with the position
+  const int64_t n_samp = nmax / kSampleStride;
+  bf16x8 a[4][4];
+  load_heads<H>(a, ws.yhat, q0, ctx.n, col, half);
+  const void* cent = ctx.cent[0];
+  __syncthreads();
+  for (int64_t t = wave; t * kTile < n_samp; t += 4) {
+    const int64_t jl = t * kTile + col;
+    uint4 b[4];
+    load_atile(b, cent, sample_bucket(jl < n_samp ? jl : n_samp - 1), half);
+    const int64_t g = sample_bucket(jl);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f32x16 acc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j][kk], __builtin_bit_cast(bf16x8, b[kk]),
+                                                      acc, 0, 0, 0);
+      float m[E];
+      mh_max<H>(acc, m);
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        if (H == 8 && (i >> 1) != half) continue;          // each half counts two positions
+        const int ql = mh_pos<H>(j, i, half);
+        const int64_t qi = q0 + ql;
+        if (jl < n_samp && qi < ctx.n && g < n_eligible(ctx, qpos(ctx, qi))) {
+          int bin = (int)((m[i] + 1.0f) * (kBins / 2));
+          bin = bin < 0 ? 0 : (bin >= kBins ? kBins - 1 : bin);
+          atomicAdd(&hist[ql][bin], 1u);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < NQ) {
+    const int64_t qj = q0 + tid;
+    if (qj < ctx.n) {
+      const int64_t nej = n_eligible(ctx, qpos(ctx, qj));
+      float tau = -3.0e38f;
+      if (nej > ctx.cap) {
+        const int64_t want = (2 * (int64_t)ctx.top_b + kSampleStride - 1) / kSampleStride;
+        int64_t cum = 0;
+        for (int b = kBins - 1; b >= 0; --b) {
+          cum += hist[tid][b];
+          if (cum >= want) { tau = (float)b / (kBins / 2) - 1.0f; break; }
+        }
+      }
+      ws.tau[qj] = tau;
+      ws.cand_cnt[qj] = nej <= ctx.cap ? (int32_t)nej : 0;
+      ws.status[qj] = 0;
+    }
+  }
+}
+
+// Every eligible bucket's max-over-heads score against tau; a position that
+// keeps all its buckets (ne <= cap) stores bucket g at slot g, the others
+// append with one atomic per position and half-wave.  grid.x = position
+// tiles of NQ, grid.y = bucket segments of seg_tiles tiles; the 4 waves take
+// every 4th tile.
+template <int H>
+__global__ __launch_bounds__(256) void k_mh_filter(IndexCtx ctx, IndexWs ws, int seg_tiles) {
+  constexpr int NQ = 128 / H;
+  constexpr int E = 16 / (H < 4 ? H : 4);
+  __shared__ float s_tau[NQ];
+  __shared__ int32_t s_ne[NQ];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31, half = lane >> 5;
+  const int64_t q0 = (int64_t)blockIdx.x * NQ;
+  const int64_t qlast = q0 + NQ - 1 < ctx.n - 1 ? q0 + NQ - 1 : ctx.n - 1;
+  const int64_t nmax = n_eligible(ctx, qpos(ctx, qlast));
+  const int64_t t0 = (int64_t)blockIdx.y * seg_tiles;
+  int64_t t1 = (nmax + kTile - 1) / kTile;
+  if (t1 > t0 + seg_tiles) t1 = t0 + seg_tiles;
+  if (t0 >= t1) return;                                       // uniform over the workgroup
+  if (tid < NQ) {
+    const int64_t qi = q0 + tid;
+    const bool valid = qi < ctx.n;
+    s_tau[tid] = valid ? ws.tau[qi] : 3.0e38f;
+    s_ne[tid] = valid ? (int32_t)n_eligible(ctx, qpos(ctx, qi)) : 0;
+  }
+  bf16x8 a[4][4];
+  load_heads<H>(a, ws.yhat, q0, ctx.n, col, half);
+  const void* cent = ctx.cent[0];
+  __syncthreads();
+  for (int64_t t = t0 + wave; t < t1; t += 4) {
+    uint4 b[4];
+    load_atile(b, cent, t * kTile + col, half);
+    const int64_t g = t * kTile + col;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f32x16 acc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j][kk], __builtin_bit_cast(bf16x8, b[kk]),
+                                                      acc, 0, 0, 0);
+      float m[E];
+      mh_max<H>(acc, m);
+      // iteration i: the lanes of each half hold one position (for H = 8 the
+      // two halves hold the same four; half h appends positions 2h, 2h + 1)
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        const bool mine = H != 8 || (i >> 1) == half;
+        const int ql = mh_pos<H>(j, i, half);
+        const int64_t qi = q0 + ql;
+        const bool all = s_ne[ql] <= ctx.cap;
+        const bool pass = mine && qi < ctx.n && g < s_ne[ql] && (all || m[i] >= s_tau[ql]);
+        const uint64_t bal = __ballot(pass && !all);
+        const uint64_t mh = half ? (bal >> 32) : (bal & 0xFFFFFFFFull);
+        int base = 0;
+        if (mh && col == 0) base = atomicAdd(&ws.cand_cnt[qi], __popcll(mh));
+        base = __shfl(base, 32 * half, 64);
+        if (pass) {
+          uint2* dst = ws.cand + qi * (int64_t)ctx.cap;
+          const uint2 e = make_uint2(__float_as_uint(m[i]), (uint32_t)g);
+          if (all) {
+            dst[g] = e;
+          } else {
+            const int slot = base + __popcll(mh & ((1ull << col) - 1ull));
+            if (slot < ctx.cap) dst[slot] = e;
+          }
+        }
+      }
+    }
+  }
 }
 
 // ------------------------------------------------------------------ decode scoring (bf16)
@@ -919,7 +1118,7 @@ constexpr int kDecStage = 64;           // LDS candidate slots per wave
 // bin where the count reaches about 2 B / 16 samples (the same in every lane)
 __device__ __forceinline__ float dec_tau_wave(const IndexCtx& ctx, const IndexWs& ws, int64_t qi,
                                              int lane) {
-  const int64_t ne = n_eligible(ctx.pos[qi]);
+  const int64_t ne = n_eligible(ctx, ctx.pos[qi]);
   if (ne <= ctx.cap) return -3.0e38f;
   const uint32_t* h = ws.hist + qi * kBins;
   const int b0 = 4 * (63 - lane);
@@ -961,7 +1160,7 @@ __global__ __launch_bounds__(256) void k_dec_filter(IndexCtx ctx, IndexWs ws, in
   __shared__ int s_cnt[4];
   __shared__ int s_base;
   const int64_t qi = blockIdx.y;
-  const int64_t ne = n_eligible(ctx.pos[qi]);
+  const int64_t ne = n_eligible(ctx, ctx.pos[qi]);
   const int64_t r0 = (int64_t)blockIdx.x * rows_per_wg;
   if (r0 >= ne) return;                                  // uniform over the workgroup
   const int64_t r1 = r0 + rows_per_wg < ne ? r0 + rows_per_wg : ne;
@@ -1058,7 +1257,7 @@ __global__ __launch_bounds__(256) void k_dec_filter(IndexCtx ctx, IndexWs ws, in
 __global__ __launch_bounds__(256) void k_dec_hist(IndexCtx ctx, IndexWs ws) {
   __shared__ uint32_t h[kBins];
   const int64_t qi = blockIdx.y;
-  const int64_t ne = n_eligible(ctx.pos[qi]);
+  const int64_t ne = n_eligible(ctx, ctx.pos[qi]);
   const int64_t n_samp = ne / kSampleStride;
   const int64_t j0 = (int64_t)blockIdx.x * kDecSampPerWg;
   if (ne <= ctx.cap || j0 >= n_samp) return;
@@ -1178,6 +1377,36 @@ __device__ __forceinline__ void load_yq(float* yq, const void* yhat, int64_t qi)
   }
 }
 
+// Max over the H query heads of query qi (bf16 yhat rows qi * H .. qi * H +
+// H - 1) of their dot products with bucket row g: the exact fallback's score
+// when queries bring several heads.
+__device__ __forceinline__ float vscore_heads(const void* cent, int64_t g, const void* yhat,
+                                              int64_t qi, int H) {
+  const uint4* c = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(cent) + g * kLatent);
+  uint4 cv[8];
+#pragma unroll
+  for (int v = 0; v < 8; ++v) cv[v] = c[v];
+  float best = -__builtin_inff();
+  for (int h = 0; h < H; ++h) {
+    const uint4* y = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(yhat) +
+                                                    (qi * H + h) * kLatent);
+    float acc = 0.f;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      const uint4 yv = y[v];
+      const uint32_t cw[4] = {cv[v].x, cv[v].y, cv[v].z, cv[v].w};
+      const uint32_t yw[4] = {yv.x, yv.y, yv.z, yv.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc = __builtin_fmaf(bf16_to_f32((uint16_t)cw[e]), bf16_to_f32((uint16_t)yw[e]), acc);
+        acc = __builtin_fmaf(bf16_to_f32((uint16_t)(cw[e] >> 16)), bf16_to_f32((uint16_t)(yw[e] >> 16)), acc);
+      }
+    }
+    best = fmaxf(best, acc);
+  }
+  return best;
+}
+
 // 256-thread exclusive prefix sum; returns the exclusive value, *total = sum.
 // Exclusive prefix sum of one int per thread over a workgroup of NT threads
 // (wsum: NT / 64 ints of LDS); *total receives the sum of all.
@@ -1229,7 +1458,8 @@ __device__ int exact_select_lds(const IndexCtx& ctx, const IndexWs& ws, int64_t 
       for (int b = tid; b < 256; b += NT) hist[b] = 0;
       __syncthreads();
       for (int64_t g = tid; g < ne; g += NT) {
-        const uint32_t key = f32_orderable(vscore<DT>(cent, g, yq));
+        const uint32_t key = f32_orderable(ctx.heads > 1 ? vscore_heads(cent, g, ws.yhat, qi, ctx.heads)
+                                                         : vscore<DT>(cent, g, yq));
         if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
       }
       __syncthreads();
@@ -1255,7 +1485,10 @@ __device__ int exact_select_lds(const IndexCtx& ctx, const IndexWs& ws, int64_t 
       const int64_t g = g0 + tid;
       float s = 0.f;
       uint32_t key = 0;
-      if (g < ne) { s = vscore<DT>(cent, g, yq); key = f32_orderable(s); }
+      if (g < ne) {
+        s = ctx.heads > 1 ? vscore_heads(cent, g, ws.yhat, qi, ctx.heads) : vscore<DT>(cent, g, yq);
+        key = f32_orderable(s);
+      }
       const int gt = (g < ne) && key > prefix;
       const int eq = (g < ne) && key == prefix;
       int eq_tot;
@@ -1324,7 +1557,7 @@ __global__ __launch_bounds__(64) void k_tree_search(IndexCtx ctx, TreeCtx tc, In
   if (qi >= ctx.n) return;
   const int64_t p = qpos(ctx, qi);
   const int64_t qb = p / kBlock;
-  const int64_t ne = n_eligible(p);
+  const int64_t ne = n_eligible(ctx, p);
   if (lane == 0) { ws.status[qi] = 0; }
   if (ne == 0) {
     if (lane == 0) ws.cand_cnt[qi] = 0;
@@ -1425,6 +1658,198 @@ __global__ __launch_bounds__(64) void k_tree_search(IndexCtx ctx, TreeCtx tc, In
     }
   }
   if (lane == 0) ws.cand_cnt[qi] = out;
+}
+
+// ------------------------------------------------------------------ wide / fixed-level tree search
+// Beams wider than a wave (up to kMaxBeamWide nodes) and the fixed-level
+// search ([visual "A worked example"], table of search styles: score coarse
+// groups, then refine inside the winners): the first stage scores every
+// eligible node of the start level S (the root's children when S is the top)
+// and keeps the best `beam`; each level below keeps the best `beam` of the
+// kept nodes' eligible children, down to l*; the eligible buckets under the
+// final beam become the candidates, as in k_tree_search.  One workgroup of
+// 256 threads per query.  "Best" is (score desc, node asc): a radix select of
+// the beam-th largest orderable score (4 passes of 8 bits), then the nodes
+// above it and, among the nodes equal to it, the lowest.
+constexpr int kWideNT = 256;
+
+// The beam-th largest orderable score among items 0 .. n-1 (key(i) = 0: not
+// an item), and how many items equal to it are to be taken.  Every thread
+// returns the same values.
+template <class Key>
+__device__ __forceinline__ void wide_threshold(int64_t n, int want, Key key, uint32_t* hist,
+                                               uint32_t* s_prefix, uint32_t* s_want,
+                                               uint32_t& prefix, uint32_t& need) {
+  const int tid = threadIdx.x;
+  uint32_t pre = 0, mask = 0, w = (uint32_t)want;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int b = tid; b < 256; b += kWideNT) hist[b] = 0;
+    __syncthreads();
+    for (int64_t i = tid; i < n; i += kWideNT) {
+      const uint32_t k = key(i);
+      if (k && (k & mask) == pre) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t cum = 0;
+      // fewer items than wanted (known after the first pass): take them all,
+      // i.e. every key above 0 and none equal to it
+      *s_prefix = 0;
+      *s_want = 0;
+      for (int b = 255; b >= 0; --b) {
+        if (cum + hist[b] >= w) {
+          *s_prefix = pre | ((uint32_t)b << shift);
+          *s_want = w - cum;
+          break;
+        }
+        cum += hist[b];
+      }
+    }
+    __syncthreads();
+    pre = *s_prefix;
+    w = *s_want;
+    mask |= 255u << shift;
+    __syncthreads();
+    if (pre == 0) break;            // uniform: every thread read the same value
+  }
+  prefix = pre;
+  need = w;
+}
+
+template <int DT>
+__global__ __launch_bounds__(kWideNT) void k_tree_search_wide(IndexCtx ctx, TreeCtx tc, IndexWs ws) {
+  extern __shared__ int32_t tsm[];
+  int32_t* bufA = tsm;
+  int32_t* bufB = tsm + ctx.cap;
+  __shared__ uint32_t ckey[2 * kMaxBeamWide];     // children of the beam: orderable score
+  __shared__ int32_t cnode[2 * kMaxBeamWide];     //   and node
+  __shared__ int32_t beam[kMaxBeamWide];
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t s_prefix, s_want;
+  __shared__ int wsum[kWideNT / 64];
+  __shared__ int s_cnt;
+  const int tid = threadIdx.x;
+  const int64_t qi = blockIdx.x;
+  if (qi >= ctx.n) return;
+  const int64_t p = qpos(ctx, qi);
+  const int64_t qb = p / kBlock;
+  const int64_t ne = n_eligible(ctx, p);
+  if (tid == 0) ws.status[qi] = 0;
+  if (ne == 0) {
+    if (tid == 0) ws.cand_cnt[qi] = 0;
+    return;
+  }
+  float yq[kLatent];
+  load_yq<DT>(yq, ws.yhat, qi);
+  const int S = tc.start;
+  int nbeam;
+  // ---- first stage: every eligible node of level S (S < height), or the root
+  if (S >= tc.height) {
+    if (tid == 0) beam[0] = 0;
+    nbeam = 1;
+  } else {
+    const int64_t nS = tc.nodes[S];
+    const void* cS = tc.cent[S];
+    const int32_t* mS = tc.minb[S];
+    auto elig = [&](int64_t g) { return S == 0 ? g < ne : (int64_t)mS[g] < qb; };
+    auto key = [&](int64_t g) -> uint32_t {
+      return elig(g) ? f32_orderable(vscore<DT>(cS, g, yq)) : 0u;
+    };
+    uint32_t prefix, need;
+    wide_threshold(nS, tc.beam, key, hist, &s_prefix, &s_want, prefix, need);
+    // in node order: every node above the threshold, and the first `need` equal to it
+    if (tid == 0) s_cnt = 0;
+    __syncthreads();
+    int eq_base = 0;
+    for (int64_t g0 = 0; g0 < nS; g0 += kWideNT) {
+      const int64_t g = g0 + tid;
+      const uint32_t k = g < nS ? key(g) : 0u;
+      const int gt = k != 0 && k > prefix;
+      const int eq = k != 0 && k == prefix;
+      int eq_tot;
+      const int eq_rank = eq_base + block_scan_nt<kWideNT>(eq, wsum, &eq_tot);
+      if (gt || (eq && eq_rank < (int)need)) {
+        const int slot = atomicAdd(&s_cnt, 1);
+        if (slot < kMaxBeamWide) beam[slot] = (int32_t)g;
+      }
+      eq_base += eq_tot;
+    }
+    __syncthreads();
+    nbeam = s_cnt < tc.beam ? s_cnt : tc.beam;
+    __syncthreads();
+  }
+  // ---- descent: the best `beam` eligible children of the kept nodes, level by level
+  for (int lvl = (S < tc.height ? S : tc.height) - 1; lvl >= tc.lstar; --lvl) {
+    const int32_t* chl = tc.child[lvl + 1];
+    const void* cl = tc.cent[lvl];
+    const int32_t* mbl = tc.minb[lvl];
+    const int n = 2 * nbeam;
+    for (int i = tid; i < n; i += kWideNT) {
+      const int32_t c = chl[2 * (int64_t)beam[i >> 1] + (i & 1)];
+      bool ok = c >= 0;
+      if (ok) ok = lvl == 0 ? (int64_t)c < ne : (int64_t)mbl[c] < qb;
+      cnode[i] = c;
+      ckey[i] = ok ? f32_orderable(vscore<DT>(cl, c, yq)) : 0u;
+    }
+    __syncthreads();
+    uint32_t prefix, need;
+    wide_threshold(n, tc.beam, [&](int64_t i) { return ckey[i]; }, hist, &s_prefix, &s_want,
+                   prefix, need);
+    // the items equal to the threshold: the `need` lowest nodes among them
+    // (their number is small; ties need equal scores)
+    if (tid == 0) s_cnt = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += kWideNT) {
+      const uint32_t k = ckey[i];
+      bool take = k != 0 && k > prefix;
+      if (k != 0 && k == prefix) {
+        int lower = 0;
+        for (int j = 0; j < n; ++j) lower += ckey[j] == prefix && cnode[j] < cnode[i];
+        take = lower < (int)need;
+      }
+      if (take) {
+        const int slot = atomicAdd(&s_cnt, 1);
+        if (slot < kMaxBeamWide) beam[slot] = cnode[i];
+      }
+    }
+    __syncthreads();
+    nbeam = s_cnt < tc.beam ? s_cnt : tc.beam;
+    __syncthreads();
+  }
+  // ---- the buckets under the final beam
+  int n = nbeam;
+  for (int j = tid; j < n; j += kWideNT) bufA[j] = beam[j];
+  __syncthreads();
+  int32_t* cur = bufA;
+  int32_t* nxt = bufB;
+  for (int lvl = tc.lstar; lvl >= 1; --lvl) {
+    if (tid == 0) s_cnt = 0;
+    __syncthreads();
+    for (int i = tid; i < 2 * n; i += kWideNT) {
+      const int32_t c = tc.child[lvl][2 * (int64_t)cur[i >> 1] + (i & 1)];
+      if (c >= 0) {
+        const int slot = atomicAdd(&s_cnt, 1);
+        if (slot < ctx.cap) nxt[slot] = c;
+      }
+    }
+    __syncthreads();
+    n = s_cnt < ctx.cap ? s_cnt : ctx.cap;
+    __syncthreads();
+    int32_t* t = cur; cur = nxt; nxt = t;
+  }
+  uint2* cand = ws.cand + qi * (int64_t)ctx.cap;
+  if (tid == 0) s_cnt = 0;
+  __syncthreads();
+  for (int j = tid; j < n; j += kWideNT) {
+    const int32_t g = cur[j];
+    if (g >= 0 && (int64_t)g < ne) {
+      const float sc = vscore<DT>(tc.cent[0], g, yq);
+      const int slot = atomicAdd(&s_cnt, 1);
+      cand[slot] = make_uint2(__float_as_uint(sc), (uint32_t)g);
+    }
+  }
+  __syncthreads();
+  if (tid == 0) ws.cand_cnt[qi] = s_cnt;
 }
 
 // ------------------------------------------------------------------ select + expand
@@ -1627,7 +2052,7 @@ __global__ __launch_bounds__(NT) void k_select_expand(IndexCtx ctx, IndexWs ws, 
   }
   int c = ws.cand_cnt[qi];
   {
-    const int64_t ne = n_eligible(p);
+    const int64_t ne = n_eligible(ctx, p);
     const int64_t beff = ne < ctx.top_b ? ne : ctx.top_b;
     if (exact_mode == 2 || (exact_mode == 1 && (c < beff || c > cap))) {
       c = exact_select_lds<DT, NT>(ctx, ws, qi, ne, beff, skey, sbkt, &hist[0][0], &s_prefix, &s_want,
@@ -1654,7 +2079,7 @@ __global__ __launch_bounds__(NT) void k_select_expand(IndexCtx ctx, IndexWs ws, 
 #pragma unroll
   for (int jj = 0; jj < PER; ++jj) {
     const int i = tid + NT * jj;
-    mw[jj] = i < c ? mem[sbkt[i]] : 0xFFFFFFFFu;
+    mw[jj] = (i < c && ctx.run_keys == 0) ? mem[sbkt[i]] : 0xFFFFFFFFu;
   }
   // far-key contributions (members outside the near set)
   int my_w = 0;
@@ -1666,7 +2091,13 @@ __global__ __launch_bounds__(NT) void k_select_expand(IndexCtx ctx, IndexWs ws, 
     const uint32_t m = mw[jj];
     const int64_t kb = (int64_t)(g / kBuckets) * kBlock;
     int ci = 0;
-    if (kb >= s_end && kb + kBlock <= w_start) {
+    if (ctx.run_keys) {
+      // a scan's run: its keys that are not sinks (every eligible run ends
+      // before the window)
+      const int64_t r0 = (int64_t)g * ctx.run_keys;
+      const int64_t lo = s_end > r0 ? s_end : r0;
+      ci = r0 + ctx.run_keys > lo ? (int)(r0 + ctx.run_keys - lo) : 0;
+    } else if (kb >= s_end && kb + kBlock <= w_start) {
       // block without sink or window keys: every member key is far
 #pragma unroll
       for (int q = 0; q < kCapItems; ++q) ci += ((m >> (8 * q)) & 0xFFu) != 0xFFu ? kPool : 0;
@@ -1737,6 +2168,24 @@ __global__ __launch_bounds__(NT) void k_select_expand(IndexCtx ctx, IndexWs ws, 
   static_assert(kPool == 4, "items are packed as (position / 4) << 4 | 4-bit key mask");
   // the items of candidate i taking `take` far keys, in member (= key) order
   auto for_items = [&](int i, uint32_t m, int take, auto&& f) {
+    if (ctx.run_keys) {
+      // a scan's run of b keys (b = 1, 4 or 8, aligned to b): its first
+      // `take` keys that are not sinks, as items of 4 keys
+      const int64_t r0 = (int64_t)sbkt[i] * ctx.run_keys;
+      if (ctx.run_keys == 1) {
+        if (take > 0 && r0 >= s_end) f((int32_t)(((r0 >> 2) << 4) | (1 << (r0 & 3))));
+        return;
+      }
+      for (int q = 0; q < ctx.run_keys / kPool && take > 0; ++q) {
+        const int64_t k0 = r0 + kPool * q;
+        uint32_t mask = 0;
+#pragma unroll
+        for (int u = 0; u < kPool; ++u)
+          if (take > 0 && k0 + u >= s_end) { mask |= 1u << u; --take; }
+        if (mask) f((int32_t)((k0 >> 2) << 4) | (int32_t)mask);
+      }
+      return;
+    }
     const int64_t kb = (int64_t)(sbkt[i] / kBuckets) * kBlock;
     const bool clean = kb >= s_end && kb + kBlock <= w_start;   // no sink or window key
     if (clean && take == (int)contrib[i]) {
@@ -1783,9 +2232,13 @@ __global__ __launch_bounds__(NT) void k_select_expand(IndexCtx ctx, IndexWs ws, 
       if (tk[jj] > 0) for_items(tid + NT * jj, mw[jj], tk[jj], [&](int32_t it) { far[o++] = it; });
   }
   __syncthreads();
-  // sort by position (bits 4 and up); positions are below p
-  const int32_t* items = radix_sort_i32<8, NT>(far, far2, n_items, (int)((p > 0 ? p : 0) >> 2) << 4,
-                                               4, &hist[0][0]);
+  // sort by position (bits 4 and up); positions are below p.  A token scan
+  // (runs of one key) emits one item per key, so two items may share a
+  // position: their one-bit masks (bits 0..3) then order them, and the sort
+  // takes every bit
+  const int32_t* items = radix_sort_i32<8, NT>(far, far2, n_items,
+                                               ((int)((p > 0 ? p : 0) >> 2) << 4) | 15,
+                                               ctx.run_keys == 1 ? 0 : 4, &hist[0][0]);
   // sinks | far | window, -1 padded; the far keys come from the sorted items,
   // each thread expanding a contiguous run of them
   int32_t* out = idx + qi * (int64_t)ctx.list_len;
@@ -1849,10 +2302,18 @@ static int64_t query_tiles(const IndexCtx& ctx) {
 
 hipError_t launch_thresh(const IndexCtx& ctx, const IndexWs& ws, int dtype, hipStream_t s) {
   if (ctx.n <= 0) return hipSuccess;
+  if (ctx.heads > 1) {
+    // prefill, bf16: 128 / H positions per workgroup
+    const unsigned gx = (unsigned)((ctx.n * ctx.heads + 127) / 128);
+    if (ctx.heads == 2) hipLaunchKernelGGL(k_mh_thresh<2>, dim3(gx), dim3(256), 0, s, ctx, ws);
+    else if (ctx.heads == 4) hipLaunchKernelGGL(k_mh_thresh<4>, dim3(gx), dim3(256), 0, s, ctx, ws);
+    else hipLaunchKernelGGL(k_mh_thresh<8>, dim3(gx), dim3(256), 0, s, ctx, ws);
+    return hipGetLastError();
+  }
   if (ctx.per_seq && dtype == LSA_BF16) {
     int64_t max_samp = 0;
     for (int64_t i = 0; i < ctx.n; ++i) {
-      const int64_t ns = (ctx.pos[i] / kBlock) * kBuckets / kSampleStride;
+      const int64_t ns = n_eligible(ctx, ctx.pos[i]) / kSampleStride;
       max_samp = ns > max_samp ? ns : max_samp;
     }
     const int64_t gx = (max_samp + kDecSampPerWg - 1) / kDecSampPerWg;
@@ -1865,7 +2326,7 @@ hipError_t launch_thresh(const IndexCtx& ctx, const IndexWs& ws, int dtype, hipS
     // decode: many workgroups per query, global histogram, then tau
     int64_t max_tiles = 0;
     for (int64_t i = 0; i < ctx.n; ++i) {
-      const int64_t t = (ctx.pos[i] / kBlock) * kBuckets / kTile;
+      const int64_t t = n_eligible(ctx, ctx.pos[i]) / kTile;
       max_tiles = t > max_tiles ? t : max_tiles;
     }
     // tiles of 32 sampled buckets (one bucket in 16), kHistSegTiles per workgroup
@@ -1885,7 +2346,7 @@ hipError_t launch_thresh(const IndexCtx& ctx, const IndexWs& ws, int dtype, hipS
     // 128 queries per wave; split the samples when there are few query tiles
     const int64_t qt = query_tiles(ctx);
     const int64_t last = ctx.q_start + ctx.n - 1;
-    const int64_t samp_tiles = ((last / kBlock) * kBuckets / kSampleStride + kTile - 1) / kTile;
+    const int64_t samp_tiles = (n_eligible(ctx, last) / kSampleStride + kTile - 1) / kTile;
     int64_t split = qt < 128 ? (256 + qt - 1) / qt : 1;
     const int64_t max_split = (samp_tiles + 15) / 16;
     if (split > max_split) split = max_split;
@@ -1911,13 +2372,21 @@ hipError_t launch_thresh(const IndexCtx& ctx, const IndexWs& ws, int dtype, hipS
 hipError_t launch_score_filter(const IndexCtx& ctx, const IndexWs& ws, int dtype,
                                int64_t max_tiles, hipStream_t s) {
   if (ctx.n <= 0 || max_tiles <= 0) return hipSuccess;
+  if (ctx.heads > 1) {
+    constexpr int kSeg = 128;                       // tiles (4,096 buckets) per workgroup
+    const dim3 grid((unsigned)((ctx.n * ctx.heads + 127) / 128), (unsigned)((max_tiles + kSeg - 1) / kSeg));
+    if (ctx.heads == 2) hipLaunchKernelGGL(k_mh_filter<2>, grid, dim3(256), 0, s, ctx, ws, kSeg);
+    else if (ctx.heads == 4) hipLaunchKernelGGL(k_mh_filter<4>, grid, dim3(256), 0, s, ctx, ws, kSeg);
+    else hipLaunchKernelGGL(k_mh_filter<8>, grid, dim3(256), 0, s, ctx, ws, kSeg);
+    return hipGetLastError();
+  }
   if (!ctx.per_seq && dtype == LSA_BF16) {
     // segment length: about kCapL / 4 expected candidates per query for the
     // widest query (~2 B of ne_max pass), so the LDS lists rarely overflow;
     // when even 16 tiles expect more, workgroups take the high-pass epilogue
     // and longer segments only save query loads
     const int64_t last = ctx.q_start + ctx.n - 1;
-    const int64_t ne_max = (last / kBlock) * kBuckets;
+    const int64_t ne_max = n_eligible(ctx, last);
     const int64_t seg_buckets = (int64_t)(kCapL / 4) * ne_max / (2 * (int64_t)(ctx.top_b > 0 ? ctx.top_b : 1));
     int64_t seg = seg_buckets / kTile;
     seg = seg < 16 ? 16 : (seg > 512 ? 512 : seg & ~(int64_t)7);
@@ -1928,7 +2397,7 @@ hipError_t launch_score_filter(const IndexCtx& ctx, const IndexWs& ws, int dtype
     const int64_t nseg = (max_tiles + seg - 1) / seg;
     int64_t x_lp = qt;
     for (int64_t x = 0; x < qt; ++x) {
-      const int64_t nmin = ((ctx.q_start + x * kQueriesPerWg) / kBlock) * kBuckets;
+      const int64_t nmin = n_eligible(ctx, ctx.q_start + x * kQueriesPerWg);
       if (nmin > ctx.cap && seg * kTile * 2 * (int64_t)ctx.top_b <= (int64_t)(kCapL / 4) * nmin) {
         x_lp = x;
         break;
@@ -1967,11 +2436,23 @@ hipError_t launch_score_filter(const IndexCtx& ctx, const IndexWs& ws, int dtype
   return hipGetLastError();
 }
 
-static void allow_large_lds(const void* fn);
+static void allow_large_lds(const void* fn, size_t bytes = 128 * 1024);
 
 hipError_t launch_tree_search(const IndexCtx& ctx, const TreeCtx& tc, const IndexWs& ws,
                               int dtype, hipStream_t s) {
   if (ctx.n <= 0) return hipSuccess;
+  if (tc.beam > kMaxBeam || tc.start < tc.height) {
+    // wider beams and the fixed-level first stage: one workgroup per query
+    const size_t smem = (size_t)2 * ctx.cap * sizeof(int32_t);
+    allow_large_lds(reinterpret_cast<const void*>(k_tree_search_wide<LSA_BF16>));
+    allow_large_lds(reinterpret_cast<const void*>(k_tree_search_wide<LSA_F32>));
+    dim3 grid((unsigned)ctx.n);
+    if (dtype == LSA_BF16)
+      hipLaunchKernelGGL(k_tree_search_wide<LSA_BF16>, grid, dim3(kWideNT), smem, s, ctx, tc, ws);
+    else
+      hipLaunchKernelGGL(k_tree_search_wide<LSA_F32>, grid, dim3(kWideNT), smem, s, ctx, tc, ws);
+    return hipGetLastError();
+  }
   static bool once = false;
   if (!once) {
     allow_large_lds(reinterpret_cast<const void*>(k_tree_search<LSA_BF16>));
@@ -1988,8 +2469,8 @@ hipError_t launch_tree_search(const IndexCtx& ctx, const TreeCtx& tc, const Inde
 // Kernels whose dynamic LDS grows with k may need more than the default 64 KiB.
 // The request is advisory: an error from it is consumed so that it cannot be
 // mistaken for a launch failure by the next hipGetLastError.
-static void allow_large_lds(const void* fn) {
-  (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
+static void allow_large_lds(const void* fn, size_t bytes) {
+  (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
   (void)hipGetLastError();
 }
 
@@ -2007,10 +2488,17 @@ hipError_t launch_select_expand(const IndexCtx& ctx, const IndexWs& ws, int32_t*
   if (kf > 2 * (int64_t)ctx.cap) return hipErrorInvalidValue;   // the far-key sort reuses 8 cap bytes
   const size_t smem = (size_t)ctx.cap * 9 + (size_t)kf * 4;
   auto run = [&](auto kern, int nt) {
-    allow_large_lds(reinterpret_cast<const void*>(kern));
+    allow_large_lds(reinterpret_cast<const void*>(kern), smem > 128 * 1024 ? smem : 128 * 1024);
     hipLaunchKernelGGL(kern, dim3((unsigned)ctx.n), dim3(nt), smem, s, ctx, ws, idx, count, ranked,
                        exact_mode);
   };
+  if (ctx.cap > 8192) {
+    // the longest candidate lists (up to 16 slots per thread of 1,024)
+    if ((ctx.cap + 1023) / 1024 > 16) return hipErrorInvalidValue;
+    if (dtype == LSA_BF16) run(k_select_expand<LSA_BF16, 16, 1024>, 1024);
+    else run(k_select_expand<LSA_F32, 16, 1024>, 1024);
+    return hipGetLastError();
+  }
   if (ctx.n <= kSelectWideQueries) {
     // candidate slots per thread of a 1,024-thread workgroup: 2, 4 or 8
     const int per = (ctx.cap + 1023) / 1024;

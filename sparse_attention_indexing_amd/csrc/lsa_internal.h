@@ -21,8 +21,12 @@ constexpr int kMaxK = 8192;
 constexpr int kMaxWindow = 8192;
 constexpr int kHeadDim = 128;
 constexpr int kMaxSeq = 32;        // sequences per batched decode launch
-constexpr int kMaxBeam = 64;
-constexpr int kMaxCap = 8192;      // candidate slots per query (power of two >= 3 B)
+constexpr int kMaxBeam = 64;        // beam of the one-wave tree search
+constexpr int kMaxBeamWide = 512;   // beam of the one-workgroup tree search
+constexpr int kMaxCap = 16384;     // candidate slots per query (>= 3 B, see cand_cap)
+// dynamic LDS the selection may take (cap * 9 + k * 4 bytes): 160 KiB less its
+// static arrays at 1,024 threads
+constexpr int kSelectLdsMax = 160 * 1024 - 16640;
 constexpr int kSampleStride = 16;  // threshold sample: every 16th tile of 32 buckets
 
 // ---------------------------------------------------------------- numerics
@@ -104,6 +108,8 @@ struct IndexCtx {
   int32_t top_b;          // buckets kept before expansion
   int32_t cap;            // candidate slots per query
   int32_t list_len;
+  int32_t run_keys;       // 0: LSA buckets; b = 1, 4, 8: a scan over runs of b keys
+  int32_t heads;          // query heads per position (bucket score = max over them)
   const void* cent[kMaxSeq];
   const uint32_t* members[kMaxSeq];
   int64_t pos[kMaxSeq];
@@ -113,6 +119,8 @@ struct TreeCtx {
   int height;
   int lstar;
   int beam;
+  int start;                          // first-stage level (height: start at the root)
+  int64_t nodes[kMaxLevels];          // nodes per level
   const void* cent[kMaxLevels];       // level 0 = buckets
   const int32_t* child[kMaxLevels];   // level >= 1
   const int32_t* minb[kMaxLevels];    // level >= 1
@@ -149,6 +157,8 @@ hipError_t launch_tree_groups(const void* child_cent, const int32_t* child_minb,
                               int32_t* child, int32_t* minb, int dtype, int child_is_bucket,
                               hipStream_t s);
 hipError_t launch_copy_rows(float* dst, const float* src, int64_t n, hipStream_t s);
+hipError_t launch_scan_blocks(const float* keys, int64_t first_block, int64_t n_blocks, void* cent,
+                              int run_keys, int dtype, hipStream_t s);
 hipError_t launch_ward_jobs(const WardJobs& jobs, int n, int dtype, hipStream_t s);
 
 hipError_t launch_qnorm(const float* y, int64_t n, void* yhat, int dtype, uint32_t* hist,

@@ -41,7 +41,7 @@ def test_params_validation():
     assert L.lsa_check_params(ctypes.byref(_p().c())) == 0
     for bad in [dict(d_latent=32), dict(n_pool=8), dict(block_keys=256), dict(n_buckets=32),
                 dict(bucket_cap_keys=8), dict(k=-1), dict(k=9000), dict(window=0),
-                dict(beam=65), dict(index_dtype=7), dict(mode=3), dict(exact_select=2)]:
+                dict(beam=513), dict(index_dtype=7), dict(start_level=-2), dict(mode=3), dict(exact_select=2)]:
         assert L.lsa_check_params(ctypes.byref(_p(**bad).c())) == -2, bad
     assert L.lsa_check_params(None) == -1
     d = lsa._Params()
@@ -62,8 +62,18 @@ def test_sizes():
     assert lsa.top_buckets(_p(k=2048, n_sink=0, window=1)) == 512        # only the query itself
     assert lsa.top_buckets(_p(k=2048, n_sink=5, window=513)) == 512 + 64 + 2
     assert lsa.top_buckets(_p(k=2048, window=514)) == 512 + 128 + 1
-    # every candidate of a query must fit one workgroup: 3 B <= 8,192
+    # every candidate of a query must fit one workgroup (9 cap + 4 k bytes of LDS)
     assert lsa.top_buckets(_p(k=8192, window=4096)) == 2048 + 512 + 1
+    assert lsa.top_buckets(_p(k=8192, window=8192)) == 2048 + 1024 + 1      # cap 10,240
+    # the scans: ceil(k / b) + ceil(n_sink / b) runs
+    assert lsa.top_buckets(_p(k=4096, scan_keys=1)) == 4100                  # cap 13,312
+    assert lsa.top_buckets(_p(k=2048, scan_keys=8)) == 256 + 1
+    assert lsa.top_buckets(_p(k=2048, scan_keys=4, n_sink=5)) == 512 + 2
+    for bad in [dict(scan_keys=2), dict(scan_keys=1, mode=1), dict(scan_keys=4, window=511),
+                dict(scan_keys=1, k=8192), dict(score_heads=3), dict(score_heads=16),
+                dict(score_heads=8, mode=1), dict(score_heads=8, index_dtype=0),
+                dict(score_heads=2, scan_keys=4)]:
+        assert lsa.lib().lsa_check_params(ctypes.byref(_p(**bad).c())) == -2, bad
     from oracle import lsa_oracle as O
     for k in (0, 1, 255, 2048, 4096):
         for window in (1, 2, 511, 512, 513, 1024, 2048):
@@ -71,8 +81,7 @@ def test_sizes():
                 assert lsa.top_buckets(_p(k=k, window=window, n_sink=n_sink)) == O.Params(
                     k=k, window=window, n_sink=n_sink).top_b, (k, window, n_sink)
     L = lsa.lib()
-    for bad in [dict(k=8192, window=8192), dict(k=8192, n_sink=8192), dict(k=4096, window=8192,
-                                                                          n_sink=8192)]:
+    for bad in [dict(k=8192, n_sink=8192), dict(k=8192, window=8192, n_sink=8192)]:
         assert L.lsa_check_params(ctypes.byref(_p(**bad).c())) == -2, bad
     L = lsa.lib()
     flat = L.lsa_cache_bytes(ctypes.byref(_p().c()), 1 << 20)

@@ -538,19 +538,26 @@ def test_tree_build_and_search(tree_65k):
     assert compare_tree(g, t["ot"], 1e-9, "T=65536") == t["ot"].height
 
 
-@pytest.mark.parametrize("beam,leaf,window,n_sink", [
-    (64, -1, 512, 4), (16, -1, 512, 4), (8, -1, 512, 4), (64, 3, 512, 4), (16, 5, 512, 4),
-    (1, 0, 512, 4), (64, -1, 2048, 64)])
-def test_tree_search_parameters(tree_65k, beam, leaf, window, n_sink):
+@pytest.mark.parametrize("beam,leaf,window,n_sink,start", [
+    (64, -1, 512, 4, -1), (16, -1, 512, 4, -1), (8, -1, 512, 4, -1), (64, 3, 512, 4, -1),
+    (16, 5, 512, 4, -1), (1, 0, 512, 4, -1), (64, -1, 2048, 64, -1),
+    (128, -1, 512, 4, -1), (512, -1, 512, 4, -1), (200, 1, 512, 4, -1),
+    (64, -1, 512, 4, 2), (16, -1, 512, 4, 6), (128, 1, 512, 4, 4), (64, -1, 512, 4, 20),
+    (1, 0, 512, 4, 5)])
+def test_tree_search_parameters(tree_65k, beam, leaf, window, n_sink, start):
     """Tree search with narrower beams, the beam stopped one or more levels
     above the automatic level l* (the two-stage search), a single-node beam
     down to the buckets, and a wider window with more sinks (which raises B
-    and so l*): lists against the oracle's tree search."""
-    say(f"case: tree search T=65536 beam={beam} leaf_level={leaf} window={window} n_sink={n_sink}")
+    and so l*); beams wider than a wave (one workgroup per query); and the
+    fixed-level search, which scores every node of a start level first (at
+    l*: coarse groups, then the buckets inside the winners; higher: a flat
+    first stage, then the beam): lists against the oracle's tree search."""
+    say(f"case: tree search T=65536 beam={beam} leaf_level={leaf} window={window} n_sink={n_sink} "
+        f"start_level={start}")
     t = tree_65k
     T = t["T"]
     p = lsa.Params(k=256, index_dtype=lsa.LSA_BF16, mode=lsa.LSA_TREE, beam=beam, leaf_level=leaf,
-                   window=window, n_sink=n_sink)
+                   window=window, n_sink=n_sink, start_level=start)
     idx, cnt = lsa.index_prefill(t["c"], torch.from_numpy(t["Y"]).cuda(), T - 2048, p, stats=FB)
     torch.cuda.synchronize()
     oc = t["oc"]

@@ -96,6 +96,23 @@ def test_prefill_1m_tree_and_flat():
         b = set(it_h[r, :ct_h[r]].tolist())
         rec.append((len(a & b) - near) / max(1, len(a) - near))
     say(f"tree/flat far-key recall: mean {np.mean(rec):.3f} min {np.min(rec):.3f}")
+    # wider beams and the fixed-level search (a flat first stage over a
+    # coarse level): lists against the oracle, recall against flat search
+    for beam, start in ((256, -1), (64, 6), (64, 4)):
+        pv = lsa.Params(k=w.k, mode=lsa.LSA_TREE, beam=beam, start_level=start)
+        iv, cv = lsa.index_prefill(c, Yd, w.q_start, pv, stats=FB)
+        torch.cuda.synchronize()
+        iv_h, cv_h = iv.cpu().numpy(), cv.cpu().numpy()
+        oc_v = O.BucketCache(oracle_params(pv), oc.n_blocks, oc.centroids, oc.members, oc.pooled,
+                             oc.block_min_gap, oc.block_ess)
+        say(f"beam {beam} start level {start}",
+            compare_lists(iv_h[rows], cv_h[rows], w.q_start + rows, Y[rows], oc_v, "tree", ot))
+        rec = []
+        for r in range(0, w.Tq, 64):
+            a = set(if_h[r, :cf_h[r]].tolist())
+            b = set(iv_h[r, :cv_h[r]].tolist())
+            rec.append((len(a & b) - near) / max(1, len(a) - near))
+        say(f"beam {beam} start level {start}: far-key recall vs flat {np.mean(rec):.3f}")
 
 
 def _completed_block(gpu_cache_obj, X, b, p):

@@ -12,20 +12,28 @@ import textwrap
 import pytest
 
 from oracle import lsa_oracle as O
+from oracle import scan_oracle as SO
 
 import test_oracle_pins as P
 import test_oracle_tree_pins as TP
+import test_scan_oracle_pins as SP
+
+
+def _module(fn_name: str):
+    return SO if fn_name.startswith(("scan_", "run_")) else O
 
 
 def _broken(fn_name: str, old: str, new: str):
-    src = textwrap.dedent(inspect.getsource(getattr(O, fn_name)))
+    mod = _module(fn_name)
+    src = textwrap.dedent(inspect.getsource(getattr(mod, fn_name)))
     assert src.count(old) == 1, f"{fn_name}: the text to break is not found once: {old!r}"
-    ns = dict(vars(O))
+    ns = dict(vars(mod))
     exec(compile(src.replace(old, new), f"<broken {fn_name}>", "exec"), ns)
     return ns[fn_name]
 
 
-TREE_RANK_PINS = [TP.test_tree_rank_beam1_follows_the_parent_not_the_best_bucket,
+TREE_RANK_PINS = [TP.test_fixed_level_search_scores_every_node_of_its_start_level,
+                  TP.test_tree_rank_beam1_follows_the_parent_not_the_best_bucket,
                   TP.test_tree_rank_beam2_three_levels,
                   TP.test_tree_rank_tie_at_the_beam_boundary_keeps_the_lower_node,
                   TP.test_tree_rank_masks_subtrees_with_no_eligible_block,
@@ -33,6 +41,11 @@ TREE_RANK_PINS = [TP.test_tree_rank_beam1_follows_the_parent_not_the_best_bucket
 BUILD_TREE_PINS = [TP.test_build_tree_parent_centroid_is_the_rounded_unit_sum,
                    TP.test_build_tree_one_child_parent_copies_its_child_bit_for_bit,
                    TP.test_build_tree_pairs_only_inside_groups_of_128]
+
+SCAN_PINS = [SP.test_worked_query_scan_counts, SP.test_block_scan_hand_worked,
+             SP.test_run_direction_is_the_normalised_mean_of_unit_keys,
+             SP.test_token_scan_takes_the_k_best_far_keys,
+             SP.test_scan_with_k_covering_every_key_is_dense_causal]
 
 MUTATIONS = [
     # tree_rank
@@ -47,12 +60,17 @@ MUTATIONS = [
      TREE_RANK_PINS),
     ("tree_rank", "nodes = nodes[nodes < eligible_buckets(p, prm)]", "nodes = nodes",
      "leaf phase keeps ineligible buckets", TREE_RANK_PINS),
-    ("tree_rank", "range(H - 1, lstar - 1, -1)", "range(H - 1, lstar, -1)",
+    ("tree_rank", "range(S - 1, lstar - 1, -1)", "range(S - 1, lstar, -1)",
      "beam stops one level early", TREE_RANK_PINS),
     ("tree_rank", "beam = np.sort(kids[o[:prm.beam]])", "beam = np.sort(kids[o[:prm.beam + 1]])",
      "beam one wider", TREE_RANK_PINS),
     ("tree_rank", "o = np.lexsort((nodes, -sc))", "o = np.lexsort((nodes, sc))",
      "leaf phase ranks worst first", TREE_RANK_PINS),
+    ("tree_rank", "S = H if prm.start_level < 0 else min(max(prm.start_level, lstar), H)", "S = H",
+     "start level ignored", TREE_RANK_PINS),
+    ("tree_rank", 'nodes = np.flatnonzero(lv["min_block"] < qb)',
+     'nodes = np.arange(lv["cent"].shape[0])', "first stage without the causal mask",
+     TREE_RANK_PINS + [TP.test_fixed_level_search_masks_ineligible_nodes]),
     # build_tree
     ("build_tree", 'cent.append(round_index(unit(below["cent"][kids].sum(axis=0)), dtype))',
      'cent.append(round_index(below["cent"][kids].mean(axis=0), dtype))',
@@ -100,12 +118,24 @@ MUTATIONS = [
     ("pool_keys", "return Khat[:T].reshape(-1, n_pool, Khat.shape[1]).sum(axis=1)",
      "return Khat[:T].reshape(-1, n_pool, Khat.shape[1]).mean(axis=1)", "pooled mean, not sum",
      [P.test_normalise_and_pool_are_sums_of_unit_keys]),
+    # the scan baselines
+    ("scan_runs", "j_hi = w_start // b", "j_hi = -(-w_start // b)",
+     "scan includes the run that straddles the window", SCAN_PINS),
+    ("scan_runs", "j_lo = s_end // b", "j_lo = 0", "scan counts sink-only runs", SCAN_PINS),
+    ("scan_rank", "order = np.lexsort((runs, -s))", "order = np.lexsort((-runs, -s))",
+     "scan ties to the higher run", SCAN_PINS),
+    ("scan_rank", "order = np.lexsort((runs, -s))", "order = np.lexsort((runs, s))",
+     "scan opens the worst runs first", SCAN_PINS),
+    ("scan_expand", "if key not in near_s:", "if True:", "scan takes sink keys", SCAN_PINS),
+    ("run_directions", "return unit(normalize_keys(X[:n]).reshape(-1, b, X.shape[1]).sum(axis=1))",
+     "return unit(X[:n].reshape(-1, b, X.shape[1]).sum(axis=1))",
+     "run summary of raw (not unit) keys", SCAN_PINS),
 ]
 
 
 @pytest.mark.parametrize("fn,old,new,what,pins", MUTATIONS, ids=[m[3] for m in MUTATIONS])
 def test_planted_mistake_fails_a_pin(fn, old, new, what, pins, monkeypatch):
-    monkeypatch.setattr(O, fn, _broken(fn, old, new))
+    monkeypatch.setattr(_module(fn), fn, _broken(fn, old, new))
     failed = []
     for pin in pins:
         try:

@@ -344,3 +344,41 @@ def test_tree_with_beam_wider_than_every_level_equals_flat():
 def test_leaf_level_reading():
     assert O.leaf_level(O.Params(k=2048, beam=64)) == 4
     assert O.leaf_level(O.Params(k=4096, beam=64)) == 5
+
+
+# ---------------------------------------------------------------- max over heads
+
+def test_max_over_heads_bucket_scores_hand_worked():
+    """[catalog "Key points"], N-LSA: bucket selection uses the max score across
+    heads.  Two query heads e0, e1 and three buckets: A = (0.9, 0.1), B = (0.5,
+    0.8), C = (0.7, 0.7) (not normalised: the pin is about the rule).  Max over
+    heads: A 0.9, B 0.8, C 0.7 -> A, B, C.  The mean would rank C first
+    (0.7 > 0.65 = B > 0.5 = A), head 0 alone A, C, B, head 1 alone B, C, A."""
+    cent = np.array([[0.9, 0.1], [0.5, 0.8], [0.7, 0.7]])
+    yh = np.eye(2)
+    s = O.bucket_scores(yh, cent)
+    assert np.array_equal(s, [0.9, 0.8, 0.7])
+    assert list(np.lexsort((np.arange(3), -s))) == [0, 1, 2]
+    # one head is the plain dot product; identical heads change nothing
+    assert np.array_equal(O.bucket_scores(yh[0], cent), cent[:, 0])
+    assert np.array_equal(O.bucket_scores(np.stack([yh[1]] * 4), cent), cent[:, 1])
+
+
+def test_max_over_heads_lists_by_hand():
+    """The hand-worked three-block example with two query heads: head 0 = e0,
+    head 1 = e1 (2-d).  Bucket scores (max): b0 = max(0.196, 0.98) = 0.98,
+    b1 = 1, b2 = 1, b3 = 0.707 -> order b1, b2 (tie, lower first), b0, b3."""
+    prm = O.Params(n_pool=4, block=8, n_buckets=2, cap_keys=4, k=5, n_sink=2, window=4,
+                   index_dtype="f32", d_latent=2)
+    e0, e1 = np.array([1.0, 0.0]), np.array([0.0, 1.0])
+    cent = [e0 * 0.2 + e1, e0, e1, e0 * 0.5 + e1 * 0.5, e0, e0]
+    members = [[0, 1, 2, 3], [4, 5, 6, 7], [8, 9, 10, 11], [12, 13, 14, 15],
+               [16, 17, 18, 19], [20, 21, 22, 23]]
+    nb = 3
+    c = O.BucketCache(prm, nb, np.array([x / np.linalg.norm(x) for x in cent]), members,
+                      [None] * 6, np.full(nb, np.inf), np.zeros(nb))
+    r = O.index_query(np.stack([e0, e1]), 20, c)
+    assert list(r.ranked) == [1, 2, 0, 3]
+    # far: 4,5,6,7 from b1, then 8 from b2 (k = 5); sinks 0, 1; window 17..20
+    assert list(r.idx[:r.count]) == [0, 1, 4, 5, 6, 7, 8, 17, 18, 19, 20]
+    assert r.exempt          # b1 and b2 tie at 1 and b2 is the cut bucket

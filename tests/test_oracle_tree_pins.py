@@ -115,6 +115,45 @@ def test_tree_rank_beam2_three_levels():
     assert order.tolist() == [3, 5, 2, 4]                         # b2..b5 ranked flat
 
 
+def test_fixed_level_search_scores_every_node_of_its_start_level():
+    """The fixed-level (two-stage) search of [visual "A worked example"]'s table
+    of search styles, on the three-level tree with beam 1: started at level 1
+    (= the stopping level), every level-1 node is scored and N2 (0.8) wins, so
+    b5 (0.6) and b4 (0.2) are ranked -- where the descent from the root keeps
+    M0 (0.9 > 0.2) and then N1 (0.5 > 0.3) and ranks b3, b2.  Started at level
+    2 with the beam running to the buckets, the first stage keeps M0 and the
+    descent goes N1, then b3."""
+    c, t = _three_level_case(_tiny_params(beam=1, leaf_level=1))
+    assert O.tree_rank(E0, c, t, 40)[0].tolist() == [3, 2]
+    c, t = _three_level_case(_tiny_params(beam=1, leaf_level=1, start_level=1))
+    order, _, gap, n_scores = O.tree_rank(E0, c, t, 40)
+    assert order.tolist() == [5, 4] and n_scores == 4 + 2
+    assert math.isclose(gap, 0.8 - 0.5)
+    c, t = _three_level_case(_tiny_params(beam=1, leaf_level=0, start_level=2))
+    assert O.tree_rank(E0, c, t, 40)[0].tolist() == [3]
+    # beam 2 from level 1: N2 and N1 -> b2..b5 ranked flat (the same as the
+    # descent, whose level 2 keeps both nodes)
+    c, t = _three_level_case(_tiny_params(beam=2, leaf_level=1, start_level=1))
+    assert O.tree_rank(E0, c, t, 40)[0].tolist() == [3, 5, 2, 4]
+
+
+def test_fixed_level_search_masks_ineligible_nodes():
+    """The first stage of the fixed-level search skips nodes whose smallest block
+    is not before the query's block: in the masking case (query in block 2)
+    started at level 1 with beam 1, N2 (0.99, block 2 only) is skipped and N1
+    (0.6) wins."""
+    bs = [0.2, 0.1, 0.4, 0.5, 0.99, 0.98]
+    prm = _tiny_params(beam=1, leaf_level=1, start_level=1)
+    c = _tiny_cache(prm, np.stack([_unit_score(s, 1 + i) for i, s in enumerate(bs)]))
+    l1 = _level([_unit_score(0.3, 10), _unit_score(0.6, 11), _unit_score(0.99, 12)],
+                [[0, 1], [2, 3], [4, 5]], [0, 1, 2])
+    l2 = _level([_unit_score(0.5, 20), _unit_score(0.99, 12)], [[0, 1], [2, -1]], [0, 2])
+    l3 = _level([_unit_score(0.5, 30)], [[0, 1]], [0])
+    t = _tree(c, [l1, l2, l3])
+    order, _, _, n_scores = O.tree_rank(E0, c, t, 16)
+    assert order.tolist() == [3, 2] and n_scores == 2 + 2
+
+
 def test_tree_rank_tie_at_the_beam_boundary_keeps_the_lower_node():
     """Level 1 scores 0.5, 0.7, 0.5 with beam 2: N1 and the lower of the two tied
     nodes, N0, are kept (ranking ties go to the lower index), so the buckets
