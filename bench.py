@@ -736,7 +736,49 @@ def bench_baselines(args, w, dev):
             "step_vs_lsa": round(r["ms_per_step"] / lsa_r["ms_per_step"], 3),
             "scores_per_step": r["scoring"]["pairs"],
             "exact_fallbacks": r["exact_fallbacks"]}
+    d = run_dense(w, dev)
+    d["step_vs_lsa"] = round(d["ms_per_step"] / lsa_r["ms_per_step"], 3)
+    res["baselines"]["dense_causal_attention"] = d
     print(json.dumps(res), flush=True)
+
+
+def run_dense(w, dev) -> dict:
+    """Dense causal attention (every query attends to every key up to its
+    position) over the workload's query rows: all of them up to 8,192 rows,
+    else the last 2,048 rows of the chunk, scaled by the rows' share of the
+    chunk's key count (each row's work is proportional to its position)."""
+    import torch
+
+    import lsa_synth as S
+    import sparse_attention_indexing_amd as lsa
+    rows = w.Tq if w.Tq <= 8192 else 2048
+    r0 = w.Tq - rows
+    Q = torch.empty((rows, w.Hq, w.D), dtype=torch.bfloat16, device=dev)
+    K = torch.empty((w.T, w.Hkv, w.D), dtype=torch.bfloat16, device=dev)
+    V = torch.empty_like(K)
+    cs = torch.cuda.current_stream().cuda_stream
+    for t, name, off in ((Q, "q", (w.q_start + r0) * w.Hq * w.D), (K, "k", 0), (V, "v", 0)):
+        S.device_fill_normal(t.data_ptr(), t.numel(), S.philox_key(w.cfg, name), off, True, cs)
+    out = torch.empty_like(Q)
+    lsa.dense_attention(Q[: min(rows, 64)], K, V, w.q_start + r0, out=out[: min(rows, 64)])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    lsa.dense_attention(Q, K, V, w.q_start + r0, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    pos = np.arange(w.q_start, w.T, dtype=np.float64)
+    keys_all = float((pos + 1).sum())
+    keys_run = float((pos[r0:] + 1).sum())
+    flop = keys_run * w.Hq * 4 * w.D
+    ms_all = ms * keys_all / keys_run
+    del Q, K, V, out
+    torch.cuda.empty_cache()
+    return {"ms_per_step": round(ms_all, 3), "measured_rows": rows, "measured_ms": round(ms, 3),
+            "scaled": rows != w.Tq,
+            "tflops": round(flop / (ms * 1e-3) / 1e12, 1),
+            "mfma_frac": round(flop / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
 
 
 def _extra_summary(r: dict) -> dict:

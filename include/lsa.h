@@ -295,6 +295,23 @@ int lsa_sparse_attention(const void* q, const void* k_cache, const void* v_cache
                          int32_t dtype, int32_t splits, void* out, void* workspace,
                          int64_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------- dense attention --
+ * The full attention LSA is measured against ([summary], [abstract]: 72.4x
+ * prefill over full attention at 10M tokens): for each query row at position
+ * p = q_start + r, softmax attention of every query head over the keys
+ * [max(0, p - band + 1), p] of its KV head (band >= p + 1, e.g. INT64_MAX:
+ * every earlier key, dense causal attention; band = W: the recent window
+ * alone).  bf16, head_dim 128, Hq / Hkv in {1, 2, 4, 8, 16}.
+ *   q        [Tq, Hq, 128]   rows for positions q_start .. q_start + Tq - 1
+ *   k_cache  [Tk, Hkv, 128], v_cache likewise; q_start + Tq <= Tk
+ *   out      [Tq, Hq, 128]
+ * scale multiplies q.k.  No workspace; asynchronous on `stream`.  Other
+ * shapes or dtypes return LSA_ERR_UNSUPPORTED, q_start + Tq > Tk or band < 1
+ * LSA_ERR_ARG. */
+int lsa_dense_attention(const void* q, const void* k_cache, const void* v_cache, int64_t Tq,
+                        int64_t q_start, int64_t Tk, int32_t Hq, int32_t Hkv, int32_t D,
+                        int64_t band, float scale, int32_t dtype, void* out, void* stream);
+
 /* ------------------------------------------- allocation-free attention --
  * For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same

@@ -103,6 +103,8 @@ def lib():
                                                 i32, ctypes.c_float, i32, i32, vp, vp, i64, vp]),
         "lsa_sparse_attention_static": (ctypes.c_int, [vp, vp, vp, i32, i64, i64, i32, i32, i32, vp,
                                                        vp, i32, ctypes.c_float, i32, i32, vp, vp]),
+        "lsa_dense_attention": (ctypes.c_int, [vp, vp, vp, i64, i64, i64, i32, i32, i32, i64,
+                                               ctypes.c_float, i32, vp, vp]),
         "lsa_attention_launch_rows": (i64, []),
         "lsa_attention_head_major": (i32, [i32, i64, i32, i32, i32]),
     }
@@ -339,6 +341,26 @@ def sparse_attention_static(q: torch.Tensor, k_cache: torch.Tensor, v_cache: tor
     return out[0] if squeeze else out
 
 
+def dense_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, q_start: int,
+                    band: int | None = None, scale: float | None = None,
+                    out: torch.Tensor | None = None) -> torch.Tensor:
+    """lsa_dense_attention: q [Tq, Hq, 128] at positions q_start.., k/v [Tk, Hkv, 128]
+    (bf16); every query attends to keys [max(0, p - band + 1), p] (band None:
+    every earlier key)."""
+    Tq, Hq, D = q.shape
+    Tk, Hkv, _ = k_cache.shape
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, torch.bfloat16, n)
+    if out is None:
+        out = torch.empty_like(q)
+    scale = 1.0 / D ** 0.5 if scale is None else scale
+    band = (1 << 62) if band is None else band
+    _check("lsa_dense_attention", lib().lsa_dense_attention(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), Tq, q_start, Tk, Hq, Hkv, D, band,
+        ctypes.c_float(scale), LSA_BF16, _ptr(out), ctypes.c_void_p(_stream())))
+    return out
+
+
 def attention_launch_rows() -> int:
     """lsa_attention_launch_rows: query rows per bf16 attention launch."""
     return int(lib().lsa_attention_launch_rows())
@@ -351,7 +373,7 @@ def attention_head_major(B: int, Tmax: int, Hkv: int, D: int, dtype: int) -> boo
 
 
 __all__ = ["Params", "BucketCache", "index_prefill", "index_decode", "sparse_attention",
-           "sparse_attention_static",
+           "sparse_attention_static", "dense_attention",
            "attention_launch_rows", "attention_head_major",
            "list_len", "top_buckets", "index_workspace_bytes", "exact_fallbacks", "lib",
            "LsaError",

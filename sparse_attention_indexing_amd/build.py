@@ -27,7 +27,7 @@ DEVICE_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 
-LIB_SOURCES = ["lsa_api.cpp", "lsa_build.hip", "lsa_index.hip", "lsa_attn.hip"]
+LIB_SOURCES = ["lsa_api.cpp", "lsa_build.hip", "lsa_index.hip", "lsa_attn.hip", "lsa_dense.hip"]
 
 
 def _run(cmd):

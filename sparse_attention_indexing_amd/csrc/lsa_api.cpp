@@ -704,6 +704,23 @@ int lsa_sparse_attention(const void* q, const void* k_cache, const void* v_cache
   return hip_status(e);
 }
 
+int lsa_dense_attention(const void* q, const void* k_cache, const void* v_cache, int64_t Tq,
+                        int64_t q_start, int64_t Tk, int32_t Hq, int32_t Hkv, int32_t D,
+                        int64_t band, float scale, int32_t dtype, void* out, void* stream) {
+  if (Tq < 0 || q_start < 0 || Tk < 0 || band < 1) return LSA_ERR_ARG;
+  if (dtype != LSA_BF16 || D != kHeadDim || Hkv <= 0 || Hq <= 0 || Hq % Hkv != 0)
+    return LSA_ERR_UNSUPPORTED;
+  const int32_t G = Hq / Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return LSA_ERR_UNSUPPORTED;
+  if (Tq == 0) return LSA_OK;
+  if (!q || !k_cache || !v_cache || !out) return LSA_ERR_ARG;
+  if (q_start + Tq > Tk) return LSA_ERR_ARG;
+  if (Hkv > 65535) return LSA_ERR_UNSUPPORTED;
+  hipError_t e = launch_dense_attention(q, k_cache, v_cache, Tq, q_start, Tk, Hq, Hkv, band, scale,
+                                        out, as_stream(stream));
+  return hip_status(e);
+}
+
 int lsa_sparse_attention_static(const void* q, const void* k_cache, const void* v_cache,
                                 int32_t B, int64_t Tq, int64_t Tmax, int32_t Hq, int32_t Hkv,
                                 int32_t D, const int32_t* idx, const int32_t* count,

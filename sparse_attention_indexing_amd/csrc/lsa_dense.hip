@@ -1,0 +1,219 @@
+// Dense (and banded) causal attention over contiguous key ranges, bf16.
+//
+// The baseline the pages compare sparse attention with is full attention
+// ([72x "Why choosing costs so much"]; [summary]: 72.4x prefill over full
+// attention at 10M tokens): every query attends to every key up to its own
+// position.  The same kernel with a band of W keys computes attention over
+// the recent window [p - W + 1, p] alone.
+//
+// Layout: Q [rows, Hq, 128] for positions q_start .. q_start + rows - 1,
+// K / V [Tk, Hkv, 128], out [rows, Hq, 128]; head h reads KV head h / G.
+// A workgroup takes one KV head and 8 waves x (16 / G) consecutive positions;
+// each wave owns 16 MFMA columns = (16 / G) positions x G heads.  Key tiles of
+// 16 keys (4 KiB of K and 4 KiB of V for the KV head) are staged in LDS by the
+// whole workgroup, double buffered, one barrier per tile; the products are
+// taken transposed (S^T = K Q^T with 16x16x32 MFMAs, O^T = V^T P^T with
+// 16x16x16 MFMAs and transposing LDS reads of V), so P never leaves
+// registers.  Online softmax in base 2 per column.
+#include "lsa_internal.h"
+
+namespace lsa {
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v4s_t lds_v4s_t;
+
+__device__ __forceinline__ uint2 tr16(const uint16_t* p) {
+  v4s_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)(p));
+  return __builtin_bit_cast(uint2, r);
+}
+
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
+
+constexpr int kDenseWaves = 8;
+constexpr int kDenseNT = 64 * kDenseWaves;
+constexpr int kKTile = 16 * 256;              // 16 keys x 256 B (one KV head)
+
+struct DenseArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* out;
+  int64_t rows, q_start, Tk;
+  int64_t band;             // keys [p - band + 1, p]; >= p + 1 covers every key
+  int32_t Hq, Hkv, G;
+  float scale_log2;         // scale * log2(e)
+};
+
+template <int G>
+__global__ __launch_bounds__(kDenseNT) void k_dense_attn(DenseArgs a) {
+  constexpr int PW = 16 / G;                  // positions per wave
+  constexpr int P = kDenseWaves * PW;         // positions per workgroup
+  __shared__ __attribute__((aligned(16))) char lds[2][2][kKTile];   // [buffer][K, V]
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kvh = blockIdx.y;
+  const int64_t r0 = (int64_t)blockIdx.x * P;                // first row of the workgroup
+  const int r16 = lane & 15, u = lane >> 4;
+  // this lane's MFMA column: position pw, head g of the KV head's group
+  const int pw = r16 / G, g = r16 % G;
+  const int64_t row = r0 + (int64_t)wave * PW + pw;
+  const bool row_ok = row < a.rows;
+  const int64_t p = a.q_start + (row_ok ? row : a.rows - 1);
+  const int64_t lo = p - a.band + 1 > 0 ? p - a.band + 1 : 0;
+  // the wave's key range and the workgroup's
+  const int64_t w_row0 = r0 + (int64_t)wave * PW;
+  const int64_t w_plast = a.q_start + (w_row0 + PW - 1 < a.rows ? w_row0 + PW - 1 : a.rows - 1);
+  const int64_t w_pfirst = a.q_start + (w_row0 < a.rows ? w_row0 : a.rows - 1);
+  const int64_t w_lo = w_pfirst - a.band + 1 > 0 ? w_pfirst - a.band + 1 : 0;
+  const int64_t g_last = a.q_start + (r0 + P - 1 < a.rows ? r0 + P - 1 : a.rows - 1);
+  const int64_t g_first = a.q_start + r0;
+  const int64_t g_lo = g_first - a.band + 1 > 0 ? g_first - a.band + 1 : 0;
+  const int64_t t_first = g_lo >> 4, t_last = g_last >> 4;
+  const bool wave_live = w_row0 < a.rows;
+
+  // Q^T fragments: lane (column r16, u) holds dims 32 j + 8 u .. + 7
+  bf16x8 qf[4];
+  {
+    const int64_t h = (int64_t)kvh * G + g;
+    const u32x4_t* qrow = reinterpret_cast<const u32x4_t*>(
+        a.q + ((row_ok ? row : 0) * a.Hq + h) * kHeadDim);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) qf[j] = __builtin_bit_cast(bf16x8, row_ok ? qrow[4 * j + u] : u32x4_t{0, 0, 0, 0});
+  }
+  f32x4 o[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = -1e30f, lp = 0.f;
+  const float sl = a.scale_log2;
+
+  // tile loads: threads 0..255 take K, 256..511 V; thread t: key (t & 255) / 16,
+  // 16-byte chunk t % 16 of the key's 256 B head row
+  const int ld_v = tid >> 8, ld_key = (tid & 255) >> 4, ld_ch = tid & 15;
+  const uint16_t* src = ld_v ? a.v : a.k;
+  auto fetch = [&](int64_t t) -> u32x4_t {
+    int64_t key = t * 16 + ld_key;
+    key = key < a.Tk ? key : a.Tk - 1;
+    return *reinterpret_cast<const u32x4_t*>(src + (key * a.Hkv + kvh) * kHeadDim + 8 * ld_ch);
+  };
+  auto put = [&](int buf, u32x4_t x) {
+    const int rr = ld_key;
+    const int sw = ld_v ? (ld_ch ^ (2 * (rr & 7))) : (ld_ch ^ rr);
+    *reinterpret_cast<u32x4_t*>(&lds[buf][ld_v][256 * rr + 16 * sw]) = x;
+  };
+  // transposing V reads: source lane s of a 16-lane group points at key row
+  // 4 u + (s >> 2), dims 16 j + 4 (s & 3) .. +3; lane (r16, u) receives dim
+  // 16 j + r16 of keys 4 u .. 4 u + 3
+  const int sk = 4 * u + (r16 >> 2), cv = (r16 & 3) >> 1, vsw = 2 * (sk & 7);
+
+  put(0, fetch(t_first));
+  __syncthreads();
+  for (int64_t t = t_first; t <= t_last; ++t) {
+    const int buf = (int)((t - t_first) & 1);
+    u32x4_t nx{0, 0, 0, 0};
+    if (t < t_last) nx = fetch(t + 1);
+    const int64_t kb = t * 16;
+    // the wave computes only tiles that meet its key range
+    if (wave_live && kb + 15 >= w_lo && kb <= w_plast) {
+      const char* kt = lds[buf][0];
+      const char* vt = lds[buf][1];
+      u32x4_t kf[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        kf[j] = *reinterpret_cast<const u32x4_t*>(kt + 256 * r16 + 16 * ((4 * j + u) ^ r16));
+      f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[j]), qf[j], sacc,
+                                                       0, 0, 0);
+      // keys 4 u + i of this tile against the column's range [lo, p]
+      bool ok[4];
+      float x = -__builtin_inff();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t key = kb + 4 * u + i;
+        ok[i] = row_ok && key >= lo && key <= p;
+        if (ok[i]) x = fmaxf(x, sacc[i] * sl);
+      }
+      x = fmaxf(x, __shfl_xor(x, 16, 64));
+      x = fmaxf(x, __shfl_xor(x, 32, 64));
+      const float mn = fmaxf(m, x);
+      const float alpha = __builtin_amdgcn_exp2f(m - mn);
+      m = mn;
+      lp *= alpha;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[j][i] *= alpha;
+      float pv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pv[i] = ok[i] ? __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], sl, -m)) : 0.f;
+        lp += pv[i];
+      }
+      uint2 w2;
+      w2.x = pack2(pv[0], pv[1]);
+      w2.y = pack2(pv[2], pv[3]);
+      const v4s_t pb4 = __builtin_bit_cast(v4s_t, w2);
+      const char* vrd = vt + 256 * sk + 8 * (r16 & 1);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const v4s_t va4 = __builtin_bit_cast(
+            v4s_t, tr16(reinterpret_cast<const uint16_t*>(vrd + 16 * ((2 * j + cv) ^ vsw))));
+        o[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va4, pb4, o[j], 0, 0, 0);
+      }
+    }
+    if (t < t_last) put(buf ^ 1, nx);
+    __syncthreads();
+  }
+  float l = lp;
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  if (row_ok) {
+    const int64_t h = (int64_t)kvh * G + g;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    uint16_t* orow = a.out + (row * a.Hq + h) * kHeadDim + 4 * u;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      uint2 w;
+      w.x = pack2(o[j][0] * inv, o[j][1] * inv);
+      w.y = pack2(o[j][2] * inv, o[j][3] * inv);
+      *reinterpret_cast<uint2*>(orow + 16 * j) = w;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_dense_attention(const void* q, const void* k, const void* v, int64_t rows,
+                                  int64_t q_start, int64_t Tk, int32_t Hq, int32_t Hkv,
+                                  int64_t band, float scale, void* out, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  DenseArgs a;
+  a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;
+  a.out = (uint16_t*)out;
+  a.rows = rows; a.q_start = q_start; a.Tk = Tk; a.band = band;
+  a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  const int G = Hq / Hkv;
+  const int P = kDenseWaves * (16 / G);
+  dim3 grid((unsigned)((rows + P - 1) / P), (unsigned)Hkv);
+  switch (G) {
+    case 1: hipLaunchKernelGGL(k_dense_attn<1>, grid, dim3(kDenseNT), 0, s, a); break;
+    case 2: hipLaunchKernelGGL(k_dense_attn<2>, grid, dim3(kDenseNT), 0, s, a); break;
+    case 4: hipLaunchKernelGGL(k_dense_attn<4>, grid, dim3(kDenseNT), 0, s, a); break;
+    case 8: hipLaunchKernelGGL(k_dense_attn<8>, grid, dim3(kDenseNT), 0, s, a); break;
+    case 16: hipLaunchKernelGGL(k_dense_attn<16>, grid, dim3(kDenseNT), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace lsa

@@ -182,3 +182,16 @@ def test_static_attention_host_errors():
     assert L.lsa_sparse_attention_static(*args(rows=64, splits=64)) == -4
     assert L.lsa_sparse_attention_static(FAKE_DEV, FAKE_DEV, FAKE_DEV, 1, 16, 1024, 32, 4, 128,
                                          None, FAKE_DEV, 100, f, 1, 1, FAKE_DEV, None) == -1
+
+
+def test_dense_attention_host_errors():
+    L = lsa.lib()
+    f = ctypes.c_float(0.1)
+    args = lambda Tq=16, q_start=0, Tk=1024, Hq=32, Hkv=4, D=128, band=1 << 40, dt=1: (
+        FAKE_DEV, FAKE_DEV, FAKE_DEV, Tq, q_start, Tk, Hq, Hkv, D, band, f, dt, FAKE_DEV, None)
+    assert L.lsa_dense_attention(*args(D=64)) == -2
+    assert L.lsa_dense_attention(*args(Hq=24, Hkv=1)) == -2      # group of 24
+    assert L.lsa_dense_attention(*args(dt=0)) == -2
+    assert L.lsa_dense_attention(*args(band=0)) == -1
+    assert L.lsa_dense_attention(*args(q_start=1020)) == -1      # rows past the keys
+    assert L.lsa_dense_attention(*args(Tq=0)) == 0
