@@ -154,23 +154,31 @@ def cpu_baseline(w, X, Y, budget_s: float):
                        f"{cores} processes x 1 BLAS thread")
 
 
-def attention_kernel_name(lsa, w, B: int, Tmax: int) -> str:
-    """The attention kernel (template instance) that lsa_sparse_attention runs."""
+def attention_kernel_name(lsa, w, B: int, Tmax: int, prefill: bool = False) -> str:
+    """The attention kernel (template instance) that lsa_sparse_attention runs;
+    with prefill, the two kernels that lsa_sparse_attention_prefill runs per
+    launch of up to lsa_attention_launch_rows() rows (the near set's dense
+    tiles, then the far entries' gather)."""
     if w.dtype != "bf16":
         return "k_attn_f32"
     if w.Hkv != 4:
-        return "k_attn_bf16<1, 0>"
-    nw = 1 if lsa.attention_head_major(B, Tmax, w.Hkv, w.D, lsa.LSA_BF16) else 4
-    return f"k_attn_bf16<{nw}, 4>"
+        far = "k_attn_bf16<1, 0" + (", true>" if prefill else ">")
+    else:
+        nw = 1 if lsa.attention_head_major(B, Tmax, w.Hkv, w.D, lsa.LSA_BF16) else 4
+        far = f"k_attn_bf16<{nw}, 4" + (", true>" if prefill else ">")
+    return f"k_near_attn<{w.Hq // w.Hkv}> + {far}" if prefill else far
 
 
-def measured_traffic(kernel: str, workload: str, rows_per_launch: int):
+def measured_traffic(kernel: str, workload: str, rows_per_launch: int, root: str | None = None):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or None
     when there is none, it was taken on another kernel, the kernel source
-    changed since, or its launches covered another number of query rows."""
+    changed since, or its launches covered another number of query rows.
+    A summary of several kernels (a launch of the prefill attention runs the
+    near-set kernel and the gather) lists their sources, comma separated,
+    and hashes them concatenated."""
     import hashlib
-    root = os.path.dirname(os.path.abspath(__file__))
-    stem = kernel.split("<")[0]
+    root = root or os.path.dirname(os.path.abspath(__file__))
+    stem = kernel.split("<")[0] if "+" not in kernel else "attention_prefill"
     path = os.path.join(root, "profiles", f"{stem}.{workload}.traffic.md")
     if not os.path.exists(path):
         return None
@@ -182,7 +190,8 @@ def measured_traffic(kernel: str, workload: str, rows_per_launch: int):
     try:
         if fields["kernel"] != kernel:
             return None
-        src = open(os.path.join(root, fields["kernel_source"]), "rb").read()
+        src = b"".join(open(os.path.join(root, f.strip()), "rb").read()
+                       for f in fields["kernel_source"].split(","))
         if hashlib.sha256(src).hexdigest()[:16] != fields["kernel_source_sha256_16"]:
             return None
         if int(fields["rows_per_launch"]) != rows_per_launch:
@@ -455,8 +464,9 @@ def bench_whole_context(args, w, dev):
     last chunk is the workload's measured final chunk (the first one is shorter).
     Per chunk: build_bucket_cache appends the chunk's latent keys (clustering the
     blocks that fill up, rebuilding the tree's right edge in tree mode), then
-    lsa_index_prefill indexes the chunk's queries and lsa_sparse_attention
-    attends over their lists.  K and V hold all T tokens; Q and the output are
+    lsa_index_prefill indexes the chunk's queries and
+    lsa_sparse_attention_prefill attends over their lists (the near set dense
+    per tile of rows, the far entries gathered).  K and V hold all T tokens; Q and the output are
     one chunk's buffers, reused (their values do not change the work; the
     per-position latent queries decide the lists).  One step = the whole
     context; no warm-up beyond one small chunk on a scratch cache."""
@@ -494,6 +504,8 @@ def bench_whole_context(args, w, dev):
     ws = torch.empty(lsa.index_workspace_bytes(p, C), dtype=torch.uint8, device=dev)
     out = torch.empty_like(Q)
     rows_total = torch.zeros((), dtype=torch.int64, device=dev)
+    ws_attn = torch.empty(lsa.lib().lsa_prefill_attention_workspace_bytes(1, C, w.Hq, w.D),
+                          dtype=torch.uint8, device=dev)
 
     def fresh_cache():
         c = lsa.BucketCache.__new__(lsa.BucketCache)
@@ -511,7 +523,8 @@ def bench_whole_context(args, w, dev):
     c = fresh_cache()
     c.build(Xd[:first])
     lsa.index_prefill(c, Yd[:first], 0, p, workspace=ws, out=(idx[:first], cnt[:first]))
-    lsa.sparse_attention(Q[:first], K, V, idx[:first], cnt[:first], out=out[:first])
+    lsa.sparse_attention_prefill(Q[:first], K, V, idx[:first], cnt[:first], 0, p, out=out[:first],
+                                 workspace=ws_attn)
     torch.cuda.synchronize()
     c = fresh_cache()
     marks = []
@@ -524,7 +537,8 @@ def bench_whole_context(args, w, dev):
         e[1].record()
         lsa.index_prefill(c, Yd[s0:s1], s0, p, workspace=ws, out=(idx[:n], cnt[:n]))
         e[2].record()
-        lsa.sparse_attention(Q[:n], K, V, idx[:n], cnt[:n], out=out[:n])
+        lsa.sparse_attention_prefill(Q[:n], K, V, idx[:n], cnt[:n], s0, p, out=out[:n],
+                                     workspace=ws_attn)
         e[3].record()
         rows_total += cnt[:n].to(torch.int64).sum()
         marks.append(e)
@@ -610,6 +624,11 @@ def run_prefill(w, dev, mode_name: str, steps: int, warmup: int, calib_copy: boo
     cnt = torch.empty((w.Tq,), dtype=torch.int32, device=dev)
     ws = torch.empty(lsa.index_workspace_bytes(p, w.Tq), dtype=torch.uint8, device=dev)
     out = torch.empty_like(Q)
+    # bf16 lists of the method (and of the scans) hold the sinks and the
+    # window: the prefill attention takes that near set dense per tile of rows
+    prefill_attn = w.dtype == "bf16"
+    ws_attn = torch.empty(max(lsa.lib().lsa_prefill_attention_workspace_bytes(1, w.Tq, w.Hq, w.D), 1),
+                          dtype=torch.uint8, device=dev) if prefill_attn else None
 
     def fresh_cache():   # a cache over the same device memory, every step
         c = lsa.BucketCache.__new__(lsa.BucketCache)
@@ -648,7 +667,10 @@ def run_prefill(w, dev, mode_name: str, steps: int, warmup: int, calib_copy: boo
         e1.record()
         lsa.index_prefill(c, Yd, w.q_start, p, workspace=ws, out=(idx, cnt))
         e2.record()
-        lsa.sparse_attention(Q, K, V, idx, cnt, out=out)
+        if prefill_attn:
+            lsa.sparse_attention_prefill(Q, K, V, idx, cnt, w.q_start, p, out=out, workspace=ws_attn)
+        else:
+            lsa.sparse_attention(Q, K, V, idx, cnt, out=out)
         e3.record()
         if times is not None:
             times.append((e0, e1, e2, e3))
@@ -683,7 +705,7 @@ def run_prefill(w, dev, mode_name: str, steps: int, warmup: int, calib_copy: boo
         pairs = int((np.maximum(pos - w.window + 1, 0) // scan_keys).sum())
     else:
         pairs = int((64 * (pos // 512)).sum())
-    kname = attention_kernel_name(lsa, w, 1, w.T)
+    kname = attention_kernel_name(lsa, w, 1, w.T, prefill_attn)
     wname = workload_name(w.name, mode_name)
     if not wname.endswith("_" + mode_name):
         wname += "_" + mode_name
@@ -707,7 +729,7 @@ def run_prefill(w, dev, mode_name: str, steps: int, warmup: int, calib_copy: boo
     }
     if build_once_ms is not None:
         res["cache_build_ms"] = round(build_once_ms, 3)
-    del Q, K, V, Xd, Yd, cache_mem, idx, cnt, ws, out, prebuilt
+    del Q, K, V, Xd, Yd, cache_mem, idx, cnt, ws, out, prebuilt, ws_attn
     torch.cuda.empty_cache()
     if cpu_seconds > 0:
         log("timing the CPU oracle on a sample ...")

@@ -295,6 +295,38 @@ int lsa_sparse_attention(const void* q, const void* k_cache, const void* v_cache
                          int32_t dtype, int32_t splits, void* out, void* workspace,
                          int64_t ws_bytes, void* stream);
 
+/* ------------------------------------------------ prefill attention --
+ * Attention for a prefill chunk whose lists hold the sinks and the recent
+ * window, as every list lsa_index_prefill writes does ([72x "The same steps
+ * in general"]; [visual "What one query actually does"]: sinks and window
+ * are always read).  For the query row (b, t) at position p = q_start + t its
+ * near set is N(p) = [0, min(p + 1, n_sink)) U [max(p - window + 1, 0), p];
+ * the row attends over N(p) and over every entry of its list that lies
+ * outside N(p) (entries outside [0, Tmax) and past the count are ignored, as
+ * in lsa_sparse_attention).  For lists from lsa_index_prefill with the same
+ * n_sink, window and q_start this is exactly lsa_sparse_attention over the
+ * same lists (up to the order of rounding).
+ * The near set is attended once per tile of neighbouring rows (dense
+ * MFMA tiles over the tile's sinks and the union of its windows, whose K/V
+ * rows are read once per tile instead of once per row) and the list's other
+ * entries are gathered per row on top of that softmax state.
+ *   q [B, Tq, Hq, 128], k_cache / v_cache [B, Tmax, Hkv, 128], idx
+ *   [B, Tq, L_max], count [B, Tq], out [B, Tq, Hq, 128]; bf16 only,
+ *   Hq / Hkv in {1, 2, 4, 8, 16}; q_start + Tq <= Tmax; n_sink >= 0,
+ *   window >= 1.
+ * workspace: at least lsa_prefill_attention_workspace_bytes(B, Tq, Hq, D)
+ * bytes of device memory (the near state of one launch's rows), caller-owned.
+ * Returns LSA_ERR_UNSUPPORTED for fp32 or other shapes (use
+ * lsa_sparse_attention), LSA_ERR_ARG for inconsistent sizes or null
+ * pointers, LSA_ERR_WORKSPACE when the workspace is missing or short. */
+int64_t lsa_prefill_attention_workspace_bytes(int32_t B, int64_t Tq, int32_t Hq, int32_t D);
+int lsa_sparse_attention_prefill(const void* q, const void* k_cache, const void* v_cache,
+                                 int32_t B, int64_t Tq, int64_t q_start, int64_t Tmax,
+                                 int32_t Hq, int32_t Hkv, int32_t D, const int32_t* idx,
+                                 const int32_t* count, int32_t L_max, int32_t n_sink,
+                                 int32_t window, float scale, int32_t dtype, void* out,
+                                 void* workspace, int64_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------- dense attention --
  * The full attention LSA is measured against ([summary], [abstract]: 72.4x
  * prefill over full attention at 10M tokens): for each query row at position

@@ -474,6 +474,19 @@ def near_set(p: int, prm: Params) -> np.ndarray:
     return np.union1d(sinks, win)
 
 
+def near_union(idx: np.ndarray, count: int, p: int, prm: Params, T: int) -> np.ndarray:
+    """The keys a query reads when its near set is taken whole: the list's
+    valid entries (in [0, T)) outside the near set, in list order, then the
+    near set (sinks and window) ascending.  Every list this method writes holds
+    its near set once, so for such a list this is a reordering of the list
+    itself; for other lists it is the list with its near entries replaced by
+    the full near set."""
+    near = near_set(p, prm)
+    near_s = set(int(x) for x in near)
+    far = [int(e) for e in np.asarray(idx[:count]).tolist() if 0 <= e < T and int(e) not in near_s]
+    return np.asarray(far + [int(x) for x in near if x < T], np.int64)
+
+
 def expand(order: np.ndarray, cache: BucketCache, p: int, near: np.ndarray):
     """Open buckets best-first, appending their keys (ascending) that are not
     in the near set, until exactly k far keys are collected.

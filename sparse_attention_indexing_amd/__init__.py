@@ -105,6 +105,10 @@ def lib():
                                                        vp, i32, ctypes.c_float, i32, i32, vp, vp]),
         "lsa_dense_attention": (ctypes.c_int, [vp, vp, vp, i64, i64, i64, i32, i32, i32, i64,
                                                ctypes.c_float, i32, vp, vp]),
+        "lsa_prefill_attention_workspace_bytes": (i64, [i32, i64, i32, i32]),
+        "lsa_sparse_attention_prefill": (ctypes.c_int, [vp, vp, vp, i32, i64, i64, i64, i32, i32,
+                                                        i32, vp, vp, i32, i32, i32, ctypes.c_float,
+                                                        i32, vp, vp, i64, vp]),
         "lsa_attention_launch_rows": (i64, []),
         "lsa_attention_head_major": (i32, [i32, i64, i32, i32, i32]),
     }
@@ -309,6 +313,37 @@ def sparse_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tens
         _ptr(q), _ptr(k_cache), _ptr(v_cache), B, Tq, Tmax, Hq, Hkv, D, _ptr(idx), _ptr(count),
         L, ctypes.c_float(scale), dt, splits, _ptr(out), _ptr(workspace) if wsb > 0 else None,
         workspace.numel() if wsb > 0 else 0, ctypes.c_void_p(_stream())))
+    return out[0] if squeeze else out
+
+
+def sparse_attention_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                             idx: torch.Tensor, count: torch.Tensor, q_start: int, p: "Params",
+                             scale: float | None = None, out: torch.Tensor | None = None,
+                             workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """lsa_sparse_attention_prefill: attention of a prefill chunk (positions
+    q_start ..) over each row's near set (p.n_sink sinks, p.window window) and
+    its list's other entries.  bf16; shapes as for sparse_attention."""
+    squeeze = q.dim() == 3
+    if squeeze:
+        q, k_cache, v_cache = q[None], k_cache[None], v_cache[None]
+    B, Tq, Hq, D = q.shape
+    _, Tmax, Hkv, _ = k_cache.shape
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, torch.bfloat16, n)
+    _need(idx, torch.int32, "idx")
+    _need(count, torch.int32, "count")
+    L = idx.shape[-1]
+    if out is None:
+        out = torch.empty_like(q)
+    scale = 1.0 / D ** 0.5 if scale is None else scale
+    wsb = _check("lsa_prefill_attention_workspace_bytes",
+                 lib().lsa_prefill_attention_workspace_bytes(B, Tq, Hq, D))
+    if workspace is None or workspace.numel() < wsb:
+        workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=q.device)
+    _check("lsa_sparse_attention_prefill", lib().lsa_sparse_attention_prefill(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), B, Tq, q_start, Tmax, Hq, Hkv, D, _ptr(idx),
+        _ptr(count), L, p.n_sink, p.window, ctypes.c_float(scale), LSA_BF16, _ptr(out),
+        _ptr(workspace), workspace.numel(), ctypes.c_void_p(_stream())))
     return out[0] if squeeze else out
 
 

@@ -704,6 +704,36 @@ int lsa_sparse_attention(const void* q, const void* k_cache, const void* v_cache
   return hip_status(e);
 }
 
+int64_t lsa_prefill_attention_workspace_bytes(int32_t B, int64_t Tq, int32_t Hq, int32_t D) {
+  if (B < 0 || Tq < 0 || Hq <= 0 || D != kHeadDim) return LSA_ERR_ARG;
+  return near_state_bytes((int64_t)B * Tq, Hq);
+}
+
+int lsa_sparse_attention_prefill(const void* q, const void* k_cache, const void* v_cache,
+                                 int32_t B, int64_t Tq, int64_t q_start, int64_t Tmax,
+                                 int32_t Hq, int32_t Hkv, int32_t D, const int32_t* idx,
+                                 const int32_t* count, int32_t L_max, int32_t n_sink,
+                                 int32_t window, float scale, int32_t dtype, void* out,
+                                 void* workspace, int64_t ws_bytes, void* stream) {
+  int64_t need = 0;
+  const int rc = check_attention(q, k_cache, v_cache, B, Tq, Tmax, Hq, Hkv, D, idx, count, L_max,
+                                 dtype, 1, out, &need);
+  if (rc < 0) return rc;
+  if (dtype != LSA_BF16) return LSA_ERR_UNSUPPORTED;
+  const int32_t G = Hq / Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return LSA_ERR_UNSUPPORTED;
+  if (q_start < 0 || n_sink < 0 || window < 1) return LSA_ERR_ARG;
+  if (rc) return LSA_OK;                       // no rows
+  if (q_start + Tq > Tmax) return LSA_ERR_ARG;
+  if (Hkv > 65535) return LSA_ERR_UNSUPPORTED;
+  need = near_state_bytes((int64_t)B * Tq, Hq);
+  if (!workspace || ws_bytes < need) return LSA_ERR_WORKSPACE;
+  hipError_t e = launch_attention_prefill(q, k_cache, v_cache, B, Tq, q_start, Tmax, Hq, Hkv, idx,
+                                          count, L_max, n_sink, window, scale, out,
+                                          reinterpret_cast<float*>(workspace), as_stream(stream));
+  return hip_status(e);
+}
+
 int lsa_dense_attention(const void* q, const void* k_cache, const void* v_cache, int64_t Tq,
                         int64_t q_start, int64_t Tk, int32_t Hq, int32_t Hkv, int32_t D,
                         int64_t band, float scale, int32_t dtype, void* out, void* stream) {

@@ -44,6 +44,14 @@ struct AttnArgs {
   int32_t Hq, Hkv, G, L, splits;
   float scale;
   float scale_log2;     // scale * log2(e): softmax in base 2
+  // far-key mode: the softmax state of the near set (sinks and window) of
+  // each launch row, [nrows, Hq, 128] O, [nrows, Hq] m (base 2) and l, from
+  // k_near_attn; the kernel adds the list's entries outside the near set
+  const float* near_o;
+  const float* near_m;
+  const float* near_l;
+  int64_t q_start, n_sink, window;
+  int64_t nrows_launch;  // rows per launch (launch parity = row0 / nrows_launch)
 };
 
 typedef short v4s __attribute__((ext_vector_type(4)));
@@ -142,7 +150,7 @@ int64_t attn_grid(int hkv, int64_t nrows) {
   return hkv * nrows;
 }
 
-template <int NW, int HKV>
+template <int NW, int HKV, bool NEAR = false>
 __global__ __launch_bounds__(64 * NW, 2) void k_attn_bf16(AttnArgs a) {
   static_assert(NW == 1 || HKV == 4, "one workgroup per row is written for four KV heads");
   extern __shared__ __attribute__((aligned(16))) char lds4[];
@@ -204,10 +212,12 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn_bf16(AttnArgs a) {
   // tiles' addresses wait on it
   const int m0 = navail < kList ? navail : kList;      // entries of the first chunk
   int32_t t0[kB];
+  if constexpr (!NEAR) {
 #pragma unroll
-  for (int u = 0; u < kB; ++u) {
-    const int i = tid + NT * u;
-    t0[u] = i < m0 ? lst[i] : 0;
+    for (int u = 0; u < kB; ++u) {
+      const int i = tid + NT * u;
+      t0[u] = i < m0 ? lst[i] : 0;
+    }
   }
   // a negative scale is applied as |scale| to -q (flipping bf16 sign bits is
   // exact), so the threshold test below can compare raw scores
@@ -232,6 +242,26 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn_bf16(AttnArgs a) {
   // score above which a key moves the reference (m + 2^kLazy); lp, this
   // lane's partial sum over its keys 4u .. 4u + 3 of every tile
   float m = -1e30f, lp = 0.f, mth = -__builtin_inff();
+  // far-key mode: the query's position p and its near set [0, s_end) and
+  // [w_start, p]; the state starts from the near set's softmax state
+  int64_t p = 0, s_end = 0, w_start = 0;
+  if constexpr (NEAR) {
+    p = a.q_start + (row - b * a.Tq);
+    s_end = p + 1 < a.n_sink ? p + 1 : a.n_sink;
+    w_start = p - a.window + 1 > 0 ? p - a.window + 1 : 0;
+    if (r16 < a.G) {
+      const int64_t slot = (row - a.row0) * a.Hq + (int64_t)kvh * a.G + r16;
+      const float4* po = reinterpret_cast<const float4*>(a.near_o + slot * kHeadDim + 4 * u);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float4 x = po[4 * j];
+        o[j] = f32x4{x.x, x.y, x.z, x.w};
+      }
+      m = a.near_m[slot];
+      lp = u == 0 ? a.near_l[slot] : 0.f;
+      mth = (m + kLazy) * inv_sl;
+    }
+  }
 
   const int vi = lane >> 4, vc = lane & 15;    // V loads: token 4 vi + j, chunk vc
   // transposing V reads: source lane s of a 16-lane group points at key row
@@ -265,9 +295,62 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn_bf16(AttnArgs a) {
       }
     }
   };
+  // far-key mode: entries [c0, c0 + cn) that are valid and outside the near
+  // set, compacted into the stage in list order (each wave takes a
+  // contiguous run of a batch; the runs' counts give the waves' offsets);
+  // returns the number kept and pads the last tile with -1
+  __shared__ int s_wcnt[NW];
+  // far-key mode reads each list from its end in every other round of
+  // workgroups (and every other launch): lists are sorted by position, so the
+  // rows in flight sweep K/V together, and a round that starts where the last
+  // one ended finds those rows still in the caches
+  const bool rev = NEAR && ((((int64_t)blockIdx.x * 2 >= gridDim.x) ? 1 : 0) ^
+                            (int)((a.row0 / a.nrows_launch) & 1));
+  auto stage_far = [&](int c0, int cn) -> int {
+    auto keep = [&](int32_t x) {
+      const int64_t e = x;
+      return (uint32_t)x < tlim && !(e < s_end || (e >= w_start && e <= p));
+    };
+    int kept = 0;
+    for (int base = 0; base < cn; base += NT * kB) {
+      int32_t t[kB];
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        const int i = base + wave * 64 * kB + 64 * u + lane;
+        t[u] = i < cn ? lst[rev ? n - 1 - (c0 + i) : c0 + i] : -1;
+      }
+      int off = kept, total = 0;
+      if constexpr (NW > 1) {
+        // the waves' counts first (the ballots are taken again for the stores)
+        int wc = 0;
+#pragma unroll
+        for (int u = 0; u < kB; ++u) wc += __popcll(__ballot(keep(t[u])));
+        if (lane == 0) s_wcnt[wave] = wc;
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          off += w < wave ? s_wcnt[w] : 0;
+          total += s_wcnt[w];
+        }
+        __syncthreads();
+      }
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        const bool k = keep(t[u]);
+        const uint64_t bal = __ballot(k);
+        const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+        if (k) slist[off + (int)below] = t[u];
+        off += __popcll(bal);
+      }
+      kept += NW > 1 ? total : off - kept;
+    }
+    for (int i = kept + tid; i < ((kept + 15) & ~15); i += NT) slist[i] = -1;
+    return kept;
+  };
   if (tid < 16) slist[kList + tid] = -1;
   // the first chunk's loads do not wait for the count (the stores do)
-  {
+  if constexpr (!NEAR) {
     const int cn = n < kList ? n : kList;
     const int m16 = (m0 + 15) & ~15;
 #pragma unroll
@@ -279,8 +362,12 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn_bf16(AttnArgs a) {
   }
   stage_sync();
   for (int c0 = 0; c0 < n; c0 += kList) {
-    const int cn = (n - c0) < kList ? (n - c0) : kList;
-    if (c0 > 0) {
+    int cn = (n - c0) < kList ? (n - c0) : kList;
+    if constexpr (NEAR) {
+      stage_sync();                            // every wave is done with the previous chunk
+      cn = stage_far(c0, cn);
+      stage_sync();
+    } else if (c0 > 0) {
       stage_sync();                            // every wave is done with the previous chunk
       stage(c0, 0, cn, cn);
       stage_sync();
@@ -602,6 +689,9 @@ hipError_t launch_attention(const void* q, const void* k, const void* v, int32_t
     a.rows = rows; a.Tq = Tq; a.Tmax = Tmax; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv;
     a.L = L_max; a.splits = splits; a.scale = scale;
     a.scale_log2 = scale * 1.4426950408889634f;
+    a.near_o = a.near_m = a.near_l = nullptr;
+    a.q_start = a.n_sink = a.window = 0;
+    a.nrows_launch = kRowsPerLaunch;
     static bool attr_set = false;
     if (!attr_set) {
       (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_attn_bf16<4, 4>),
@@ -642,6 +732,75 @@ hipError_t launch_attention(const void* q, const void* k, const void* v, int32_t
     hipLaunchKernelGGL(k_attn_combine<LSA_F32>, dim3((unsigned)(rows * Hq * 2)), dim3(256), 0, s,
                        ws, out, rows, Hq, splits);
   return hipGetLastError();
+}
+
+// the near kernel runs over groups of this many rows (launches of the gather
+// kernel), so that it fills the chip; its state for a group stays in the
+// workspace until the group's gathers have read it
+constexpr int64_t kNearGroupLaunches = 4;
+
+int64_t near_state_bytes(int64_t rows, int32_t Hq) {
+  const int64_t g = kRowsPerLaunch * kNearGroupLaunches;
+  const int64_t r = rows < g ? rows : g;
+  return r * Hq * ((int64_t)kHeadDim + 2) * 4;
+}
+
+hipError_t launch_attention_prefill(const void* q, const void* k, const void* v, int32_t B,
+                                    int64_t Tq, int64_t q_start, int64_t Tmax, int32_t Hq,
+                                    int32_t Hkv, const int32_t* idx, const int32_t* count,
+                                    int32_t L_max, int64_t n_sink, int64_t window, float scale,
+                                    void* out, float* ws, hipStream_t s) {
+  const int64_t rows = (int64_t)B * Tq;
+  if (rows <= 0) return hipSuccess;
+  const int64_t group = kRowsPerLaunch * kNearGroupLaunches;
+  const int64_t grows = rows < group ? rows : group;   // rows of the near state
+  AttnArgs a;
+  a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;
+  a.idx = idx; a.count = count; a.out = (uint16_t*)out; a.ws = nullptr;
+  a.rows = rows; a.Tq = Tq; a.Tmax = Tmax; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv;
+  a.L = L_max; a.splits = 1; a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  // near state of a group's rows: O [grows, Hq, 128], then m, then l
+  float* po = ws;
+  float* pm = po + grows * Hq * kHeadDim;
+  float* pl = pm + grows * Hq;
+  a.q_start = q_start; a.n_sink = n_sink; a.window = window;
+  a.nrows_launch = kRowsPerLaunch;
+  static bool attr_set = false;
+  if (!attr_set) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_attn_bf16<4, 4, true>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kLds4<4>);
+    (void)hipGetLastError();  // advisory; never report it as a launch failure
+    attr_set = true;
+  }
+  const bool head_major = attention_head_major(B, Tmax, Hkv, kHeadDim, LSA_BF16);
+  for (int64_t g0 = 0; g0 < rows; g0 += group) {
+    const int64_t gn = (rows - g0) < group ? (rows - g0) : group;
+    hipError_t e = launch_near_attention(q, k, v, g0, gn, Tq, q_start, Tmax, Hq, Hkv, n_sink,
+                                         window, scale, po, pm, pl, s);
+    if (e != hipSuccess) return e;
+    for (int64_t r0 = g0; r0 < g0 + gn; r0 += kRowsPerLaunch) {
+      a.row0 = r0;
+      a.nrows = (g0 + gn - r0) < kRowsPerLaunch ? (g0 + gn - r0) : kRowsPerLaunch;
+      // the launch's rows start (r0 - g0) rows into the group's state
+      const int64_t off = (r0 - g0) * Hq;
+      a.near_o = po + off * kHeadDim;
+      a.near_m = pm + off;
+      a.near_l = pl + off;
+      if (Hkv != 4)
+        hipLaunchKernelGGL((k_attn_bf16<1, 0, true>), dim3((unsigned)attn_grid<1>(Hkv, a.nrows)),
+                           dim3(64), (size_t)kLds4<1>, s, a);
+      else if (head_major)
+        hipLaunchKernelGGL((k_attn_bf16<1, 4, true>), dim3((unsigned)attn_grid<1>(4, a.nrows)),
+                           dim3(64), (size_t)kLds4<1>, s, a);
+      else
+        hipLaunchKernelGGL((k_attn_bf16<4, 4, true>), dim3((unsigned)attn_grid<4>(4, a.nrows)),
+                           dim3(256), (size_t)kLds4<4>, s, a);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
 }
 
 }  // namespace lsa

@@ -190,6 +190,192 @@ __global__ __launch_bounds__(kDenseNT) void k_dense_attn(DenseArgs a) {
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// The near part of a query's list, dense.  Every list the index writes holds
+// the sinks and the recent window ([72x "The same steps in general"]; [visual
+// "What one query actually does"]: the sinks and the window are always
+// read): keys [0, min(p + 1, S)) and [max(p - W + 1, 0), p] for a query at
+// position p.  Consecutive queries share almost all of them (the windows of
+// 16 neighbours cover W + 15 keys), so instead of gathering them once per
+// query they are attended here once per tile of neighbouring queries, with the
+// same workgroup shape as k_dense_attn (8 waves x 16 / G positions, one KV
+// head), over the tile's sink keys and the union of its windows.  The result
+// is the softmax state of that partial attention per (row, head): O relative
+// to the reference max m (base 2, scaled), m, and the sum l; the gather kernel
+// starts from it and adds the list's remaining (far) keys.
+constexpr int kNearRing = 6;                 // K/V tiles in flight per near workgroup
+
+struct NearArgs {
+  const uint16_t* q;        // [B * Tq, Hq, 128]
+  const uint16_t* k;        // [B, Tmax, Hkv, 128]
+  const uint16_t* v;
+  float* po;                // [nrows, Hq, 128]: O of rows row0 .. row0 + nrows - 1
+  float* pm;                // [nrows, Hq]: m (base 2, scale applied)
+  float* pl;                // [nrows, Hq]: l
+  int64_t row0, nrows;      // the launch's rows (global row = b * Tq + t)
+  int64_t Tq, q_start, Tmax, n_sink, window;
+  int64_t tile0, tiles_per_seq;
+  int32_t Hq, Hkv;
+  float scale_log2;
+};
+
+// two workgroups per compute unit (at most 128 VGPRs)
+template <int G>
+__global__ __launch_bounds__(kDenseNT) __attribute__((amdgpu_waves_per_eu(4))) void k_near_attn(NearArgs a) {
+  constexpr int PW = 16 / G;                  // positions per wave
+  constexpr int P = kDenseWaves * PW;         // positions per workgroup
+  __shared__ __attribute__((aligned(16))) char lds[2][2][kKTile];   // [buffer][K, V]
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kvh = blockIdx.y;
+  const int64_t tile = a.tile0 + blockIdx.x;
+  const int64_t b = tile / a.tiles_per_seq;
+  const int64_t t0 = (tile % a.tiles_per_seq) * P;           // first position index of the tile
+  const int64_t t_end = t0 + P < a.Tq ? t0 + P : a.Tq;       // one past the last
+  const int r16 = lane & 15, u = lane >> 4;
+  const int pw = r16 / G, g = r16 % G;
+  // this lane's column: position index t, global row b * Tq + t
+  const int64_t t = t0 + (int64_t)wave * PW + pw;
+  const int64_t grow = b * a.Tq + t;
+  const bool col_ok = t < a.Tq && grow >= a.row0 && grow < a.row0 + a.nrows;
+  const int64_t p = a.q_start + (t < a.Tq ? t : a.Tq - 1);
+  const int64_t s_end = p + 1 < a.n_sink ? p + 1 : a.n_sink;
+  const int64_t w_start = p - a.window + 1 > 0 ? p - a.window + 1 : 0;
+  // the workgroup's keys: sinks [0, sk_end), then the windows [wk_lo, wk_hi]
+  const int64_t p_first = a.q_start + t0, p_last = a.q_start + t_end - 1;
+  const int64_t sk_end = p_last + 1 < a.n_sink ? p_last + 1 : a.n_sink;
+  const int64_t wk_lo = p_first - a.window + 1 > 0 ? p_first - a.window + 1 : 0;
+  const int64_t ts_end = (sk_end + 15) >> 4;                    // sink tiles [0, ts_end)
+  const int64_t tw0 = (wk_lo >> 4) > ts_end ? (wk_lo >> 4) : ts_end;
+  const int64_t n_tiles = ts_end + ((p_last >> 4) >= tw0 ? (p_last >> 4) - tw0 + 1 : 0);
+  auto tile_of = [&](int64_t i) -> int64_t { return i < ts_end ? i : tw0 + (i - ts_end); };
+  // the wave's keys, to skip tiles that none of its columns reads
+  const int64_t wt0 = t0 + (int64_t)wave * PW;
+  const bool wave_live = wt0 < t_end;
+  const int64_t wp_first = a.q_start + wt0;
+  const int64_t wp_last = a.q_start + (wt0 + PW - 1 < t_end - 1 ? wt0 + PW - 1 : t_end - 1);
+  const int64_t ws_end = wp_last + 1 < a.n_sink ? wp_last + 1 : a.n_sink;
+  const int64_t ww_lo = wp_first - a.window + 1 > 0 ? wp_first - a.window + 1 : 0;
+
+  bf16x8 qf[4];
+  {
+    const int64_t h = (int64_t)kvh * G + g;
+    const u32x4_t* qrow = reinterpret_cast<const u32x4_t*>(a.q + ((col_ok ? grow : 0) * a.Hq + h) * kHeadDim);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      qf[j] = __builtin_bit_cast(bf16x8, col_ok ? qrow[4 * j + u] : u32x4_t{0, 0, 0, 0});
+  }
+  f32x4 o[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = -1e30f, lp = 0.f;
+  const float sl = a.scale_log2;
+
+  const int ld_v = tid >> 8, ld_key = (tid & 255) >> 4, ld_ch = tid & 15;
+  const uint16_t* src = (ld_v ? a.v : a.k) + b * a.Tmax * a.Hkv * kHeadDim;
+  auto fetch = [&](int64_t i) -> u32x4_t {
+    int64_t key = tile_of(i) * 16 + ld_key;
+    key = key < a.Tmax ? key : a.Tmax - 1;
+    return *reinterpret_cast<const u32x4_t*>(src + (key * a.Hkv + kvh) * kHeadDim + 8 * ld_ch);
+  };
+  auto put = [&](int buf, u32x4_t x) {
+    const int rr = ld_key;
+    const int sw = ld_v ? (ld_ch ^ (2 * (rr & 7))) : (ld_ch ^ rr);
+    *reinterpret_cast<u32x4_t*>(&lds[buf][ld_v][256 * rr + 16 * sw]) = x;
+  };
+  const int sk = 4 * u + (r16 >> 2), cv = (r16 & 3) >> 1, vsw = 2 * (sk & 7);
+
+  // kNearRing tiles are requested ahead of the one computed (each thread
+  // holds its 16 bytes of each in registers); one barrier per tile, the LDS
+  // tiles double buffered
+  u32x4_t ring[kNearRing];
+  // Q first: with only ring loads pending in the loop, each tile's wait is
+  // kNearRing - 1 later loads
+  __builtin_amdgcn_s_waitcnt(0x0F70);          // vmcnt(0)
+#pragma unroll
+  for (int j = 0; j < kNearRing; ++j) {
+    ring[j] = fetch(j < n_tiles ? j : n_tiles - 1);
+    __builtin_amdgcn_sched_barrier(0);         // keep the loads in ring order
+  }
+  for (int64_t i0 = 0; i0 < n_tiles; i0 += kNearRing) {
+#pragma unroll
+    for (int j = 0; j < kNearRing; ++j) {
+      // whole ring cycles: tiles past the end are staged (a repeat of the
+      // last one) but not computed, and every load is unconditional (past the
+      // end it repeats the last tile), so that each wait on the ring is the
+      // same count of later loads
+      const int64_t i = i0 + j;
+      const int buf = j & 1;                   // kNearRing is even: buffers alternate
+      put(buf, ring[j]);
+      __syncthreads();
+      ring[j] = fetch(i + kNearRing < n_tiles ? i + kNearRing : n_tiles - 1);
+      const int64_t kb = tile_of(i < n_tiles ? i : n_tiles - 1) * 16;
+      if (i < n_tiles && wave_live && (kb < ws_end || (kb + 15 >= ww_lo && kb <= wp_last))) {
+        const char* kt = lds[buf][0];
+        const char* vt = lds[buf][1];
+        u32x4_t kf[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          kf[jj] = *reinterpret_cast<const u32x4_t*>(kt + 256 * r16 + 16 * ((4 * jj + u) ^ r16));
+        f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[jj]), qf[jj],
+                                                         sacc, 0, 0, 0);
+        // keys 4 u + e of this tile against the column's near set
+        bool ok[4];
+        float x = -__builtin_inff();
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t key = kb + 4 * u + e;
+          ok[e] = col_ok && key <= p && (key < s_end || key >= w_start);
+          if (ok[e]) x = fmaxf(x, sacc[e] * sl);
+        }
+        x = fmaxf(x, __shfl_xor(x, 16, 64));
+        x = fmaxf(x, __shfl_xor(x, 32, 64));
+        const float mn = fmaxf(m, x);
+        const float alpha = __builtin_amdgcn_exp2f(m - mn);
+        m = mn;
+        lp *= alpha;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[jj][e] *= alpha;
+        float pv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pv[e] = ok[e] ? __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[e], sl, -m)) : 0.f;
+          lp += pv[e];
+        }
+        uint2 w2;
+        w2.x = pack2(pv[0], pv[1]);
+        w2.y = pack2(pv[2], pv[3]);
+        const v4s_t pb4 = __builtin_bit_cast(v4s_t, w2);
+        const char* vrd = vt + 256 * sk + 8 * (r16 & 1);
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const v4s_t va4 = __builtin_bit_cast(
+              v4s_t, tr16(reinterpret_cast<const uint16_t*>(vrd + 16 * ((2 * jj + cv) ^ vsw))));
+          o[jj] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va4, pb4, o[jj], 0, 0, 0);
+        }
+      }
+    }
+  }
+  float l = lp;
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  if (col_ok) {
+    const int64_t h = (int64_t)kvh * G + g;
+    const int64_t slot = (grow - a.row0) * a.Hq + h;
+    float* orow = a.po + slot * kHeadDim + 4 * u;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      *reinterpret_cast<float4*>(orow + 16 * j) = make_float4(o[j][0], o[j][1], o[j][2], o[j][3]);
+    if (u == 0) { a.pm[slot] = m; a.pl[slot] = l; }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_dense_attention(const void* q, const void* k, const void* v, int64_t rows,
@@ -211,6 +397,39 @@ hipError_t launch_dense_attention(const void* q, const void* k, const void* v, i
     case 4: hipLaunchKernelGGL(k_dense_attn<4>, grid, dim3(kDenseNT), 0, s, a); break;
     case 8: hipLaunchKernelGGL(k_dense_attn<8>, grid, dim3(kDenseNT), 0, s, a); break;
     case 16: hipLaunchKernelGGL(k_dense_attn<16>, grid, dim3(kDenseNT), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_near_attention(const void* q, const void* k, const void* v, int64_t row0,
+                                 int64_t nrows, int64_t Tq, int64_t q_start, int64_t Tmax,
+                                 int32_t Hq, int32_t Hkv, int64_t n_sink, int64_t window,
+                                 float scale, float* po, float* pm, float* pl, hipStream_t s) {
+  if (nrows <= 0) return hipSuccess;
+  const int G = Hq / Hkv;
+  if (G < 1 || G > 16 || 16 % G != 0 || Hq % Hkv != 0) return hipErrorInvalidValue;
+  const int P = kDenseWaves * (16 / G);
+  NearArgs a;
+  a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;
+  a.po = po; a.pm = pm; a.pl = pl;
+  a.row0 = row0; a.nrows = nrows;
+  a.Tq = Tq; a.q_start = q_start; a.Tmax = Tmax; a.n_sink = n_sink; a.window = window;
+  a.tiles_per_seq = (Tq + P - 1) / P;
+  // the tiles holding the launch's first and last rows (tiles never straddle
+  // two sequences; a tile cut by the launch's bounds writes its rows only)
+  auto tile_of_row = [&](int64_t r) { return (r / Tq) * a.tiles_per_seq + (r % Tq) / P; };
+  a.tile0 = tile_of_row(row0);
+  const int64_t ntiles = tile_of_row(row0 + nrows - 1) - a.tile0 + 1;
+  a.Hq = Hq; a.Hkv = Hkv;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  dim3 grid((unsigned)ntiles, (unsigned)Hkv);
+  switch (G) {
+    case 1: hipLaunchKernelGGL(k_near_attn<1>, grid, dim3(kDenseNT), 0, s, a); break;
+    case 2: hipLaunchKernelGGL(k_near_attn<2>, grid, dim3(kDenseNT), 0, s, a); break;
+    case 4: hipLaunchKernelGGL(k_near_attn<4>, grid, dim3(kDenseNT), 0, s, a); break;
+    case 8: hipLaunchKernelGGL(k_near_attn<8>, grid, dim3(kDenseNT), 0, s, a); break;
+    case 16: hipLaunchKernelGGL(k_near_attn<16>, grid, dim3(kDenseNT), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

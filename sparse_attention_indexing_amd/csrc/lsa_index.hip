@@ -2011,7 +2011,7 @@ __device__ uint32_t weighted_select(int c, KeyF key, FiltF filt, const uint8_t* 
 // count to the emission.  NT = 256 for many queries; a few queries (decode)
 // take NT = 1,024, which shortens every data-parallel phase of the one
 // workgroup that a query waits on.
-template <int DT, int PER, int NT = 256>
+template <int DT, int PER, int NT = 256, bool SCAN = false>
 __global__ __launch_bounds__(NT) void k_select_expand(IndexCtx ctx, IndexWs ws, int32_t* idx,
                                                        int32_t* count, int32_t* ranked,
                                                        int exact_mode) {
@@ -2031,6 +2031,9 @@ __global__ __launch_bounds__(NT) void k_select_expand(IndexCtx ctx, IndexWs ws, 
   __shared__ int s_total, s_trunc_m;
   const int tid = threadIdx.x;
   const int64_t qi = blockIdx.x;
+  // keys per scan run; 0 for buckets (a compile-time 0 keeps the scan
+  // branches out of the bucket kernels)
+  const int run_keys = SCAN ? ctx.run_keys : 0;
   if (qi >= ctx.n) return;
   const int64_t p = qpos(ctx, qi);
   const uint32_t* mem = qmem(ctx, qi);
@@ -2079,7 +2082,7 @@ __global__ __launch_bounds__(NT) void k_select_expand(IndexCtx ctx, IndexWs ws, 
 #pragma unroll
   for (int jj = 0; jj < PER; ++jj) {
     const int i = tid + NT * jj;
-    mw[jj] = (i < c && ctx.run_keys == 0) ? mem[sbkt[i]] : 0xFFFFFFFFu;
+    mw[jj] = (i < c && run_keys == 0) ? mem[sbkt[i]] : 0xFFFFFFFFu;
   }
   // far-key contributions (members outside the near set)
   int my_w = 0;
@@ -2091,12 +2094,12 @@ __global__ __launch_bounds__(NT) void k_select_expand(IndexCtx ctx, IndexWs ws, 
     const uint32_t m = mw[jj];
     const int64_t kb = (int64_t)(g / kBuckets) * kBlock;
     int ci = 0;
-    if (ctx.run_keys) {
+    if (run_keys) {
       // a scan's run: its keys that are not sinks (every eligible run ends
       // before the window)
-      const int64_t r0 = (int64_t)g * ctx.run_keys;
+      const int64_t r0 = (int64_t)g * run_keys;
       const int64_t lo = s_end > r0 ? s_end : r0;
-      ci = r0 + ctx.run_keys > lo ? (int)(r0 + ctx.run_keys - lo) : 0;
+      ci = r0 + run_keys > lo ? (int)(r0 + run_keys - lo) : 0;
     } else if (kb >= s_end && kb + kBlock <= w_start) {
       // block without sink or window keys: every member key is far
 #pragma unroll
@@ -2168,15 +2171,15 @@ __global__ __launch_bounds__(NT) void k_select_expand(IndexCtx ctx, IndexWs ws, 
   static_assert(kPool == 4, "items are packed as (position / 4) << 4 | 4-bit key mask");
   // the items of candidate i taking `take` far keys, in member (= key) order
   auto for_items = [&](int i, uint32_t m, int take, auto&& f) {
-    if (ctx.run_keys) {
+    if (run_keys) {
       // a scan's run of b keys (b = 1, 4 or 8, aligned to b): its first
       // `take` keys that are not sinks, as items of 4 keys
-      const int64_t r0 = (int64_t)sbkt[i] * ctx.run_keys;
-      if (ctx.run_keys == 1) {
+      const int64_t r0 = (int64_t)sbkt[i] * run_keys;
+      if (run_keys == 1) {
         if (take > 0 && r0 >= s_end) f((int32_t)(((r0 >> 2) << 4) | (1 << (r0 & 3))));
         return;
       }
-      for (int q = 0; q < ctx.run_keys / kPool && take > 0; ++q) {
+      for (int q = 0; q < run_keys / kPool && take > 0; ++q) {
         const int64_t k0 = r0 + kPool * q;
         uint32_t mask = 0;
 #pragma unroll
@@ -2238,7 +2241,7 @@ __global__ __launch_bounds__(NT) void k_select_expand(IndexCtx ctx, IndexWs ws, 
   // takes every bit
   const int32_t* items = radix_sort_i32<8, NT>(far, far2, n_items,
                                                ((int)((p > 0 ? p : 0) >> 2) << 4) | 15,
-                                               ctx.run_keys == 1 ? 0 : 4, &hist[0][0]);
+                                               run_keys == 1 ? 0 : 4, &hist[0][0]);
   // sinks | far | window, -1 padded; the far keys come from the sorted items,
   // each thread expanding a contiguous run of them
   int32_t* out = idx + qi * (int64_t)ctx.list_len;
@@ -2487,16 +2490,23 @@ hipError_t launch_select_expand(const IndexCtx& ctx, const IndexWs& ws, int32_t*
   const int64_t kf = ctx.k > 1 ? ctx.k : 1;
   if (kf > 2 * (int64_t)ctx.cap) return hipErrorInvalidValue;   // the far-key sort reuses 8 cap bytes
   const size_t smem = (size_t)ctx.cap * 9 + (size_t)kf * 4;
-  auto run = [&](auto kern, int nt) {
+  auto launch = [&](auto kern, int nt) {
     allow_large_lds(reinterpret_cast<const void*>(kern), smem > 128 * 1024 ? smem : 128 * 1024);
     hipLaunchKernelGGL(kern, dim3((unsigned)ctx.n), dim3(nt), smem, s, ctx, ws, idx, count, ranked,
                        exact_mode);
   };
+  // the bucket kernel, or its scan-run instance
+  auto run = [&](auto kern, auto scan_kern, int nt) {
+    if (ctx.run_keys) launch(scan_kern, nt);
+    else launch(kern, nt);
+  };
+#define SELECT_KERNEL(DT_, PER_, NT_) \
+  run(k_select_expand<DT_, PER_, NT_>, k_select_expand<DT_, PER_, NT_, true>, NT_)
   if (ctx.cap > 8192) {
     // the longest candidate lists (up to 16 slots per thread of 1,024)
     if ((ctx.cap + 1023) / 1024 > 16) return hipErrorInvalidValue;
-    if (dtype == LSA_BF16) run(k_select_expand<LSA_BF16, 16, 1024>, 1024);
-    else run(k_select_expand<LSA_F32, 16, 1024>, 1024);
+    if (dtype == LSA_BF16) SELECT_KERNEL(LSA_BF16, 16, 1024);
+    else SELECT_KERNEL(LSA_F32, 16, 1024);
     return hipGetLastError();
   }
   if (ctx.n <= kSelectWideQueries) {
@@ -2504,13 +2514,13 @@ hipError_t launch_select_expand(const IndexCtx& ctx, const IndexWs& ws, int32_t*
     const int per = (ctx.cap + 1023) / 1024;
     if (per > 8) return hipErrorInvalidValue;
     if (dtype == LSA_BF16) {
-      if (per <= 2) run(k_select_expand<LSA_BF16, 2, 1024>, 1024);
-      else if (per <= 4) run(k_select_expand<LSA_BF16, 4, 1024>, 1024);
-      else run(k_select_expand<LSA_BF16, 8, 1024>, 1024);
+      if (per <= 2) SELECT_KERNEL(LSA_BF16, 2, 1024);
+      else if (per <= 4) SELECT_KERNEL(LSA_BF16, 4, 1024);
+      else SELECT_KERNEL(LSA_BF16, 8, 1024);
     } else {
-      if (per <= 2) run(k_select_expand<LSA_F32, 2, 1024>, 1024);
-      else if (per <= 4) run(k_select_expand<LSA_F32, 4, 1024>, 1024);
-      else run(k_select_expand<LSA_F32, 8, 1024>, 1024);
+      if (per <= 2) SELECT_KERNEL(LSA_F32, 2, 1024);
+      else if (per <= 4) SELECT_KERNEL(LSA_F32, 4, 1024);
+      else SELECT_KERNEL(LSA_F32, 8, 1024);
     }
     return hipGetLastError();
   }
@@ -2521,11 +2531,11 @@ hipError_t launch_select_expand(const IndexCtx& ctx, const IndexWs& ws, int32_t*
     const int per512 = (ctx.cap + 511) / 512;
     if (per512 > 16) return hipErrorInvalidValue;
     if (dtype == LSA_BF16) {
-      if (per512 <= 8) run(k_select_expand<LSA_BF16, 8, 512>, 512);
-      else run(k_select_expand<LSA_BF16, 16, 512>, 512);
+      if (per512 <= 8) SELECT_KERNEL(LSA_BF16, 8, 512);
+      else SELECT_KERNEL(LSA_BF16, 16, 512);
     } else {
-      if (per512 <= 8) run(k_select_expand<LSA_F32, 8, 512>, 512);
-      else run(k_select_expand<LSA_F32, 16, 512>, 512);
+      if (per512 <= 8) SELECT_KERNEL(LSA_F32, 8, 512);
+      else SELECT_KERNEL(LSA_F32, 16, 512);
     }
     return hipGetLastError();
   }
@@ -2533,15 +2543,16 @@ hipError_t launch_select_expand(const IndexCtx& ctx, const IndexWs& ws, int32_t*
   const int per = (ctx.cap + 255) / 256;
   if (per > 32) return hipErrorInvalidValue;
   if (dtype == LSA_BF16) {
-    if (per <= 8) run(k_select_expand<LSA_BF16, 8>, 256);
-    else if (per <= 16) run(k_select_expand<LSA_BF16, 16>, 256);
-    else run(k_select_expand<LSA_BF16, 32>, 256);
+    if (per <= 8) SELECT_KERNEL(LSA_BF16, 8, 256);
+    else if (per <= 16) SELECT_KERNEL(LSA_BF16, 16, 256);
+    else SELECT_KERNEL(LSA_BF16, 32, 256);
   } else {
-    if (per <= 8) run(k_select_expand<LSA_F32, 8>, 256);
-    else if (per <= 16) run(k_select_expand<LSA_F32, 16>, 256);
-    else run(k_select_expand<LSA_F32, 32>, 256);
+    if (per <= 8) SELECT_KERNEL(LSA_F32, 8, 256);
+    else if (per <= 16) SELECT_KERNEL(LSA_F32, 16, 256);
+    else SELECT_KERNEL(LSA_F32, 32, 256);
   }
   return hipGetLastError();
+#undef SELECT_KERNEL
 }
 
 }  // namespace lsa

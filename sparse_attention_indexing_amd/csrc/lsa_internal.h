@@ -184,5 +184,20 @@ hipError_t launch_attention(const void* q, const void* k, const void* v, int32_t
                             int64_t Tmax, int32_t Hq, int32_t Hkv, const int32_t* idx,
                             const int32_t* count, int32_t L_max, float scale, int dtype,
                             int32_t splits, void* out, float* ws, hipStream_t s);
+// the softmax state of each row's near set (sinks and window), written into
+// po [nrows, Hq, 128], pm and pl [nrows, Hq] for rows row0 .. row0 + nrows - 1
+hipError_t launch_near_attention(const void* q, const void* k, const void* v, int64_t row0,
+                                 int64_t nrows, int64_t Tq, int64_t q_start, int64_t Tmax,
+                                 int32_t Hq, int32_t Hkv, int64_t n_sink, int64_t window,
+                                 float scale, float* po, float* pm, float* pl, hipStream_t s);
+// bytes of near state that launch_attention_prefill needs for `rows` rows
+int64_t near_state_bytes(int64_t rows, int32_t Hq);
+// prefill attention in two parts: near set dense per tile of rows, then the
+// far entries of each list gathered on top of that state
+hipError_t launch_attention_prefill(const void* q, const void* k, const void* v, int32_t B,
+                                    int64_t Tq, int64_t q_start, int64_t Tmax, int32_t Hq,
+                                    int32_t Hkv, const int32_t* idx, const int32_t* count,
+                                    int32_t L_max, int64_t n_sink, int64_t window, float scale,
+                                    void* out, float* ws, hipStream_t s);
 
 }  // namespace lsa

@@ -195,3 +195,27 @@ def test_dense_attention_host_errors():
     assert L.lsa_dense_attention(*args(band=0)) == -1
     assert L.lsa_dense_attention(*args(q_start=1020)) == -1      # rows past the keys
     assert L.lsa_dense_attention(*args(Tq=0)) == 0
+
+
+def test_prefill_attention_host_errors():
+    """lsa_sparse_attention_prefill rejects fp32, other group sizes, rows past
+    the cache, bad sink/window counts and a short workspace on the host,
+    before anything is launched."""
+    L = lsa.lib()
+    f = ctypes.c_float(0.1)
+    need = L.lsa_prefill_attention_workspace_bytes(1, 16, 32, 128)
+    assert need == 16 * 32 * 130 * 4
+    # the near state of one group of four launches at most: 4,096 rows
+    assert L.lsa_prefill_attention_workspace_bytes(2, 100000, 32, 128) == 4096 * 32 * 130 * 4
+    assert L.lsa_prefill_attention_workspace_bytes(1, 16, 32, 64) == -1
+    args = lambda Tq=16, q_start=0, Tmax=1024, Hq=32, Hkv=4, D=128, n_sink=4, window=512, dt=1, \
+        ws=need: (FAKE_DEV, FAKE_DEV, FAKE_DEV, 1, Tq, q_start, Tmax, Hq, Hkv, D, FAKE_DEV, FAKE_DEV,
+                  100, n_sink, window, f, dt, FAKE_DEV, FAKE_DEV, ws, None)
+    assert L.lsa_sparse_attention_prefill(*args(dt=0)) == -2
+    assert L.lsa_sparse_attention_prefill(*args(D=64)) == -2
+    assert L.lsa_sparse_attention_prefill(*args(Hq=12, Hkv=4)) == -2     # group of 3
+    assert L.lsa_sparse_attention_prefill(*args(q_start=1010)) == -1     # rows past the cache
+    assert L.lsa_sparse_attention_prefill(*args(window=0)) == -1
+    assert L.lsa_sparse_attention_prefill(*args(n_sink=-1)) == -1
+    assert L.lsa_sparse_attention_prefill(*args(ws=need - 1)) == -3
+    assert L.lsa_sparse_attention_prefill(*args(Tq=0)) == 0

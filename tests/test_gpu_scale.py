@@ -54,7 +54,13 @@ def test_prefill_128k_full_size():
     # the benchmark's layout at this size: one workgroup per (row, KV head)
     assert lsa.attention_head_major(1, w.T, w.Hkv, w.D, lsa.LSA_BF16)
     out = lsa.sparse_attention(Q, K, V, idx, cnt)
+    # the benchmark's attention: the near set dense per tile of 16 rows, the
+    # far entries gathered per row
+    out_p = lsa.sparse_attention_prefill(Q, K, V, idx, cnt, w.q_start, p)
     torch.cuda.synchronize()
+    d = float((out_p.float() - out.float()).abs().max().item())
+    say(f"prefill attention vs lsa_sparse_attention over all {w.Tq} rows: max abs diff {d:.3g}")
+    assert d <= 1e-2
     oc = oracle_cache_parallel(X, oracle_params(p))
     say("build", compare_cache(cache_to_host(c), oc, X))
     idx_h, cnt_h = idx.cpu().numpy(), cnt.cpu().numpy()
@@ -63,6 +69,13 @@ def test_prefill_128k_full_size():
     arows = rows[::8]
     q_rows = host_rows(w, "q", arows, w.Hq * w.D)
     _attn_check(w, q_rows, out.float().cpu().numpy(), idx_h, cnt_h, arows, label="prefill 128K")
+    # every list holds its near set once, so near_union reorders it: the
+    # oracle attention over the list is the prefill attention's reference
+    for r in arows:
+        assert sorted(O.near_union(idx_h[r], int(cnt_h[r]), w.q_start + int(r), oracle_params(p),
+                                   w.T).tolist()) == sorted(idx_h[r, :cnt_h[r]].tolist())
+    _attn_check(w, q_rows, out_p.float().cpu().numpy(), idx_h, cnt_h, arows,
+                label="prefill 128K (near + far)")
 
 
 def test_prefill_1m_tree_and_flat():
@@ -221,7 +234,14 @@ def test_prefill_10m_flat_and_tree_last_chunk(ctx10m):
     assert not lsa.attention_head_major(1, w.T, w.Hkv, w.D, lsa.LSA_BF16)
     o_f = lsa.sparse_attention(Q, K, V, i_f, c_f)
     o_t = lsa.sparse_attention(Q, K, V, i_t, c_t)
+    # the benchmark's attention (near set dense per tile, far entries gathered)
+    op_f = lsa.sparse_attention_prefill(Q, K, V, i_f, c_f, w.q_start, pf)
+    op_t = lsa.sparse_attention_prefill(Q, K, V, i_t, c_t, w.q_start, ctx10m["pt"])
     torch.cuda.synchronize()
+    for a_, b_, m_ in ((op_f, o_f, "flat"), (op_t, o_t, "tree")):
+        d = float((a_.float() - b_.float()).abs().max().item())
+        say(f"10M {m_}: prefill attention vs lsa_sparse_attention, all rows: max abs diff {d:.3g}")
+        assert d <= 1e-2
     # the device generator fills all 5.12e9 elements like the host rows (this
     # needs a grid-stride launch: a dispatch holds fewer than 2^32 work-items)
     for r in [0, 2097152, 8388608, w.T - 1]:
@@ -232,12 +252,14 @@ def test_prefill_10m_flat_and_tree_last_chunk(ctx10m):
                                      [w.Tq - 1, w.Tq - 2, w.Tq - 129, w.Tq - 130]]))
     arows = rows[:: max(1, len(rows) // 16)][:16]
     q_rows = host_rows(w, "q", w.q_start + arows, w.Hq * w.D)
-    for mode, idx, cnt, out in (("flat", i_f, c_f, o_f), ("tree", i_t, c_t, o_t)):
+    for mode, idx, cnt, out, out_p in (("flat", i_f, c_f, o_f, op_f), ("tree", i_t, c_t, o_t, op_t)):
         idx_h, cnt_h = idx.cpu().numpy(), cnt.cpu().numpy()
         say(f"{mode} index", compare_lists(idx_h[rows], cnt_h[rows], w.q_start + rows, Y[rows], oc,
                                           mode, ot if mode == "tree" else None, parallel=True))
         _attn_check(w, q_rows, out.float().cpu().numpy(), idx_h, cnt_h, arows,
                     label=f"prefill 10M {mode}")
+        _attn_check(w, q_rows, out_p.float().cpu().numpy(), idx_h, cnt_h, arows,
+                    label=f"prefill 10M {mode} (near + far)")
 
 
 def test_decode_10m_flat_and_tree_steady_and_completing(ctx10m):

@@ -17,6 +17,7 @@ from oracle import scan_oracle as SO
 import test_oracle_pins as P
 import test_oracle_tree_pins as TP
 import test_scan_oracle_pins as SP
+import test_oracle_near_pins as NP
 
 
 def _module(fn_name: str):
@@ -47,7 +48,18 @@ SCAN_PINS = [SP.test_worked_query_scan_counts, SP.test_block_scan_hand_worked,
              SP.test_token_scan_takes_the_k_best_far_keys,
              SP.test_scan_with_k_covering_every_key_is_dense_causal]
 
+NEAR_PINS = [NP.test_near_union_hand_worked, NP.test_near_union_clips_sinks_to_the_query,
+             NP.test_near_union_count_limits_the_list,
+             NP.test_near_union_window_only_query_near_start]
+
 MUTATIONS = [
+    # near_union
+    ("near_union", "if 0 <= e < T and int(e) not in near_s]", "if 0 <= e < T]",
+     "near entries of the list counted twice", NEAR_PINS),
+    ("near_union", "np.asarray(idx[:count]).tolist()", "np.asarray(idx).tolist()",
+     "entries past the count read", NEAR_PINS),
+    ("near_union", "if 0 <= e < T and int(e) not in near_s]", "if int(e) not in near_s]",
+     "invalid entries kept", NEAR_PINS),
     # tree_rank
     ("tree_rank", "o = np.lexsort((kids, -sc))", "o = np.lexsort((kids, sc))",
      "beam keeps the lowest scores", TREE_RANK_PINS),
