@@ -1868,8 +1868,8 @@ __device__ __forceinline__ uint64_t match_digit(uint32_t d, uint64_t active) {
 
 // Stable LSD radix sort (DB-bit digits) of n non-negative int32 keys in LDS,
 // ascending by their bits lo and up (the bits below lo keep their input
-// order), by a workgroup of NT threads of which the first NW = min(NT / 64, 4)
-// waves hold the keys.  Wave w owns
+// order), by a workgroup of NT threads of which the first NW waves hold the
+// keys (4, or 8 when NT >= 1024; at most NT / 64 x 256 / 2^DB).  Wave w owns
 // the contiguous chunk [w*ch, (w+1)*ch); `tmp` is a second buffer of n ints,
 // `cnt` NW x 2^DB counters (one row per wave); the scatter ranks lanes with
 // equal digits by ballots, which keeps it stable.  Returns the buffer that
@@ -1878,9 +1878,14 @@ template <int DB, int NT = 256>
 __device__ int32_t* radix_sort_i32(int32_t* keys, int32_t* tmp, int n, int max_key, int lo,
                                    uint32_t* cnt) {
   constexpr int NB = 1 << DB;
-  // at most four waves hold keys: fewer counters to clear and scan, which is
-  // what a sort of a few hundred keys by a wide workgroup spends its time on
-  constexpr int NW = (NT / 64) < 4 ? (NT / 64) : 4;
+  // at most four waves hold keys (eight in a workgroup of 1,024 threads, whose
+  // query waits on it alone: measured best for the 500 - 1,100 items of a
+  // decode step): fewer counters to clear and scan, which is what a sort of a
+  // few hundred keys by a wide workgroup spends its time on
+  constexpr int NW0 = NT >= 1024 ? 8 : ((NT / 64) < 4 ? (NT / 64) : 4);
+  constexpr int NWc = (NT / 64) * 256 / NB;
+  constexpr int NW = NW0 < NWc ? NW0 : NWc;
+  static_assert(NW >= 1, "counters of one wave fit");
   constexpr int E = NB * NW / NT;                // counters per thread in the scan
   static_assert(E >= 1 && NB * NW == E * NT, "counter layout");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1998,6 +2003,108 @@ __device__ uint32_t weighted_select(int c, KeyF key, FiltF filt, const uint8_t* 
   return prefix;
 }
 
+
+// ---- few-query selection helpers (workgroups of NT >= 1024 threads) ------
+// A query that waits alone on its workgroup (decode) pays for every barrier of
+// the selection; these take the weighted select and the far-key sort in far
+// fewer of them.
+
+// Weighted selection in one histogram pass: candidates i < c of weight w[i] >
+// 0, ordered by key descending, then bucket ascending; finds the candidate at
+// which the running weight reaches `want` (its key, its bucket, and the weight
+// still needed from it).  The keys are binned linearly over their range into
+// kRangeBins bins (a monotone map, so every bin above the crossing one is taken
+// whole); the crossing bin is then ranked exactly by one wave.  Returns false
+// (uniformly) when that bin holds more than 64 candidates; the caller then
+// takes the radix passes.
+constexpr int kRangeBins = 2048;
+constexpr int kRangeSel = 4 + 3 * 64;   // words of `sh`
+
+template <int NT>
+__device__ bool range_select(int c, const uint32_t* key, const uint32_t* bkt, const uint8_t* w,
+                             uint32_t want, uint32_t* bins, uint32_t* sh, int* wsum,
+                             uint32_t& key_out, uint32_t& bkt_out, uint32_t& rest_out) {
+  static_assert(NT >= 1024 && kRangeBins % NT == 0, "bins per thread");
+  constexpr int E = kRangeBins / NT;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // key range of the weighted candidates
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+  for (int i = tid; i < c; i += NT)
+    if (w[i]) { lo = min(lo, key[i]); hi = max(hi, key[i]); }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    lo = min(lo, (uint32_t)__shfl_xor((int)lo, off, 64));
+    hi = max(hi, (uint32_t)__shfl_xor((int)hi, off, 64));
+  }
+  uint32_t* s_lo = sh + 4;                     // [NT / 64] (reused below)
+  uint32_t* s_hi = sh + 4 + 64;
+  if (lane == 0) { s_lo[wave] = lo; s_hi[wave] = hi; }
+  for (int b = tid; b < kRangeBins; b += NT) bins[b] = 0u;
+  if (tid == 0) sh[2] = 0u;
+  __syncthreads();
+  lo = 0xFFFFFFFFu; hi = 0u;
+#pragma unroll
+  for (int q = 0; q < NT / 64; ++q) { lo = min(lo, s_lo[q]); hi = max(hi, s_hi[q]); }
+  const float scale = (float)kRangeBins / ((float)(hi - lo) + 1.0f);
+  auto bin_of = [&](uint32_t kv) {
+    const int b = (int)((float)(kv - lo) * scale);
+    return b < 0 ? 0 : (b >= kRangeBins ? kRangeBins - 1 : b);
+  };
+  __syncthreads();                             // s_lo / s_hi read before reuse
+  for (int i = tid; i < c; i += NT)
+    if (w[i]) atomicAdd(&bins[bin_of(key[i])], (uint32_t)w[i]);
+  __syncthreads();
+  // thread t owns bins kRangeBins - 1 - (E t + q), q < E (descending)
+  uint32_t hb[E], mine = 0;
+#pragma unroll
+  for (int q = 0; q < E; ++q) { hb[q] = bins[kRangeBins - 1 - (E * tid + q)]; mine += hb[q]; }
+  int all;
+  uint32_t above = (uint32_t)block_scan_nt<NT>((int)mine, wsum, &all);
+#pragma unroll
+  for (int q = 0; q < E; ++q) {
+    if (above < want && above + hb[q] >= want) { sh[0] = (uint32_t)(kRangeBins - 1 - (E * tid + q)); sh[1] = above; }
+    above += hb[q];
+  }
+  __syncthreads();
+  const int bstar = (int)sh[0];
+  const uint32_t before = sh[1];
+  // the crossing bin's candidates
+  uint32_t* e_key = sh + 4;
+  uint32_t* e_bkt = sh + 4 + 64;
+  uint32_t* e_w = sh + 4 + 128;
+  for (int i = tid; i < c; i += NT)
+    if (w[i] && bin_of(key[i]) == bstar) {
+      const uint32_t slot = atomicAdd(&sh[2], 1u);
+      if (slot < 64) { e_key[slot] = key[i]; e_bkt[slot] = bkt[i]; e_w[slot] = w[i]; }
+    }
+  __syncthreads();
+  const uint32_t n = sh[2];
+  if (n > 64) return false;
+  if (wave == 0) {
+    // rank them by (key desc, bucket asc): lane l counts the weight of the
+    // candidates ranked before its own (broadcast reads of the slots)
+    const bool ok = (uint32_t)lane < n;
+    const uint32_t mk = ok ? e_key[lane] : 0u, mb = ok ? e_bkt[lane] : 0u;
+    uint32_t ahead = 0;
+    for (uint32_t j = 0; j < n; ++j) {
+      const uint32_t kj = e_key[j], bj = e_bkt[j];
+      ahead += (kj > mk || (kj == mk && bj < mb)) ? e_w[j] : 0u;
+    }
+    const uint32_t wl = ok ? e_w[lane] : 0u;
+    if (ok && before + ahead < want && before + ahead + wl >= want) {
+      sh[0] = mk;
+      sh[1] = mb;
+      sh[3] = want - before - ahead;
+    }
+  }
+  __syncthreads();
+  key_out = sh[0];
+  bkt_out = sh[1];
+  rest_out = sh[3];
+  __syncthreads();                             // sh read before any later reuse
+  return true;
+}
+
 // One workgroup per query.  The walk over buckets ranked by (score desc,
 // bucket asc) stops at the bucket where the running count of far keys
 // reaches k.  That bucket is found without sorting: a radix select on the
@@ -2029,6 +2136,7 @@ __global__ __launch_bounds__(NT) void k_select_expand(IndexCtx ctx, IndexWs ws, 
   __shared__ int wsum[NT / 64];
   __shared__ uint32_t s_prefix, s_want;
   __shared__ int s_total, s_trunc_m;
+  __shared__ uint32_t s_rsel[NT >= 1024 ? kRangeSel : 1];
   const int tid = threadIdx.x;
   const int64_t qi = blockIdx.x;
   // keys per scan run; 0 for buckets (a compile-time 0 keeps the scan
@@ -2054,10 +2162,12 @@ __global__ __launch_bounds__(NT) void k_select_expand(IndexCtx ctx, IndexWs ws, 
     }
   }
   int c = ws.cand_cnt[qi];
+  bool used_exact = false;
   {
     const int64_t ne = n_eligible(ctx, p);
     const int64_t beff = ne < ctx.top_b ? ne : ctx.top_b;
     if (exact_mode == 2 || (exact_mode == 1 && (c < beff || c > cap))) {
+      used_exact = true;
       c = exact_select_lds<DT, NT>(ctx, ws, qi, ne, beff, skey, sbkt, &hist[0][0], &s_prefix, &s_want,
                                wsum, &s_total);
     } else {
@@ -2076,13 +2186,24 @@ __global__ __launch_bounds__(NT) void k_select_expand(IndexCtx ctx, IndexWs ws, 
       }
     }
   }
-  __syncthreads();
-  // member words of this thread's candidates (all loads issued together)
+  // member words of this thread's candidates (all loads issued together;
+  // from the candidate registers when they hold the list, before the barrier)
   uint32_t mw[PER];
+  const bool mw_early = NT >= 1024 && !used_exact;
+  if (mw_early) {
 #pragma unroll
-  for (int jj = 0; jj < PER; ++jj) {
-    const int i = tid + NT * jj;
-    mw[jj] = (i < c && run_keys == 0) ? mem[sbkt[i]] : 0xFFFFFFFFu;
+    for (int jj = 0; jj < PER; ++jj) {
+      const int i = tid + NT * jj;
+      mw[jj] = (i < c && run_keys == 0) ? mem[e[jj].y] : 0xFFFFFFFFu;
+    }
+  }
+  __syncthreads();
+  if (!mw_early) {
+#pragma unroll
+    for (int jj = 0; jj < PER; ++jj) {
+      const int i = tid + NT * jj;
+      mw[jj] = (i < c && run_keys == 0) ? mem[sbkt[i]] : 0xFFFFFFFFu;
+    }
   }
   // far-key contributions (members outside the near set)
   int my_w = 0;
@@ -2141,6 +2262,13 @@ __global__ __launch_bounds__(NT) void k_select_expand(IndexCtx ctx, IndexWs ws, 
   uint32_t prefix = 0, gstar_key = 0, want = (uint32_t)k;
   const bool cut = k > 0 && total >= k;
   if (cut) {
+    bool fast = false;
+    if constexpr (NT >= 1024) {
+      uint32_t ko, bo, ro;
+      fast = range_select<NT>(c, skey, sbkt, contrib, want, &hist[0][0], s_rsel, wsum, ko, bo, ro);
+      if (fast) { prefix = ko; gstar_key = 0xFFFFFFFFu - bo; want = ro; }
+    }
+    if (!fast) {
     prefix = weighted_select<NT>(c, [&](int i) { return skey[i]; }, [&](int) { return true; },
                              contrib, want, hist, &s_prefix, &s_want);
     const uint32_t sstar = prefix;
@@ -2156,6 +2284,7 @@ __global__ __launch_bounds__(NT) void k_select_expand(IndexCtx ctx, IndexWs ws, 
       gstar_key = weighted_select<NT>(c, [&](int i) { return 0xFFFFFFFFu - sbkt[i]; },
                                   [&](int i) { return skey[i] == sstar; }, contrib, want, hist,
                                   &s_prefix, &s_want);
+    }
     }
     if (tid == 0) s_trunc_m = (int)want;
   }
@@ -2239,9 +2368,9 @@ __global__ __launch_bounds__(NT) void k_select_expand(IndexCtx ctx, IndexWs ws, 
   // (runs of one key) emits one item per key, so two items may share a
   // position: their one-bit masks (bits 0..3) then order them, and the sort
   // takes every bit
-  const int32_t* items = radix_sort_i32<8, NT>(far, far2, n_items,
-                                               ((int)((p > 0 ? p : 0) >> 2) << 4) | 15,
-                                               run_keys == 1 ? 0 : 4, &hist[0][0]);
+  const int max_item = ((int)((p > 0 ? p : 0) >> 2) << 4) | 15;
+  const int32_t* items = radix_sort_i32<8, NT>(far, far2, n_items, max_item, run_keys == 1 ? 0 : 4,
+                                               &hist[0][0]);
   // sinks | far | window, -1 padded; the far keys come from the sorted items,
   // each thread expanding a contiguous run of them
   int32_t* out = idx + qi * (int64_t)ctx.list_len;
