@@ -1442,10 +1442,13 @@ __device__ __forceinline__ int block_scan_excl(int v, int* wsum, int* total) {
 // order-preserving integer image of the fp32 score, then every bucket above
 // it and, among buckets equal to it, the lowest.  Writes raw score bits to
 // skey[] and buckets to sbkt[] (LDS) and returns the count (min(B, ne)).
+// `heads`: query heads per position (1 unless max-over-heads scoring; a
+// compile-time 1 keeps the multi-head scorer out of the bucket kernels).
 template <int DT, int NT = 256>
 __device__ int exact_select_lds(const IndexCtx& ctx, const IndexWs& ws, int64_t qi, int64_t ne,
                                 int64_t beff, uint32_t* skey, uint32_t* sbkt, uint32_t* hist,
-                                uint32_t* s_prefix, uint32_t* s_want, int* wsum, int* s_out) {
+                                uint32_t* s_prefix, uint32_t* s_want, int* wsum, int* s_out,
+                                int heads) {
   const int tid = threadIdx.x;
   const void* cent = qcent(ctx, qi);
   float yq[kLatent];
@@ -1458,8 +1461,8 @@ __device__ int exact_select_lds(const IndexCtx& ctx, const IndexWs& ws, int64_t 
       for (int b = tid; b < 256; b += NT) hist[b] = 0;
       __syncthreads();
       for (int64_t g = tid; g < ne; g += NT) {
-        const uint32_t key = f32_orderable(ctx.heads > 1 ? vscore_heads(cent, g, ws.yhat, qi, ctx.heads)
-                                                         : vscore<DT>(cent, g, yq));
+        const uint32_t key = f32_orderable(heads > 1 ? vscore_heads(cent, g, ws.yhat, qi, heads)
+                                                     : vscore<DT>(cent, g, yq));
         if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
       }
       __syncthreads();
@@ -1486,7 +1489,7 @@ __device__ int exact_select_lds(const IndexCtx& ctx, const IndexWs& ws, int64_t 
       float s = 0.f;
       uint32_t key = 0;
       if (g < ne) {
-        s = ctx.heads > 1 ? vscore_heads(cent, g, ws.yhat, qi, ctx.heads) : vscore<DT>(cent, g, yq);
+        s = heads > 1 ? vscore_heads(cent, g, ws.yhat, qi, heads) : vscore<DT>(cent, g, yq);
         key = f32_orderable(s);
       }
       const int gt = (g < ne) && key > prefix;
@@ -2140,7 +2143,9 @@ __global__ __launch_bounds__(NT) void k_select_expand(IndexCtx ctx, IndexWs ws, 
   const int tid = threadIdx.x;
   const int64_t qi = blockIdx.x;
   // keys per scan run; 0 for buckets (a compile-time 0 keeps the scan
-  // branches out of the bucket kernels)
+  // branches out of the bucket kernels, as SCAN = false also keeps out the
+  // max-over-heads scorer of the exact fallback: SCAN selects the instance
+  // for scans and for max-over-heads scoring)
   const int run_keys = SCAN ? ctx.run_keys : 0;
   if (qi >= ctx.n) return;
   const int64_t p = qpos(ctx, qi);
@@ -2169,7 +2174,7 @@ __global__ __launch_bounds__(NT) void k_select_expand(IndexCtx ctx, IndexWs ws, 
     if (exact_mode == 2 || (exact_mode == 1 && (c < beff || c > cap))) {
       used_exact = true;
       c = exact_select_lds<DT, NT>(ctx, ws, qi, ne, beff, skey, sbkt, &hist[0][0], &s_prefix, &s_want,
-                               wsum, &s_total);
+                                   wsum, &s_total, SCAN ? ctx.heads : 1);
     } else {
       c = c < cap ? c : cap;
       if constexpr (NT < 1024) {
@@ -2626,7 +2631,7 @@ hipError_t launch_select_expand(const IndexCtx& ctx, const IndexWs& ws, int32_t*
   };
   // the bucket kernel, or its scan-run instance
   auto run = [&](auto kern, auto scan_kern, int nt) {
-    if (ctx.run_keys) launch(scan_kern, nt);
+    if (ctx.run_keys || ctx.heads > 1) launch(scan_kern, nt);
     else launch(kern, nt);
   };
 #define SELECT_KERNEL(DT_, PER_, NT_) \
