@@ -312,7 +312,7 @@ int lsa_sparse_attention(const void* q, const void* k_cache, const void* v_cache
  * entries are gathered per row on top of that softmax state.
  *   q [B, Tq, Hq, 128], k_cache / v_cache [B, Tmax, Hkv, 128], idx
  *   [B, Tq, L_max], count [B, Tq], out [B, Tq, Hq, 128]; bf16 only,
- *   Hq / Hkv in {1, 2, 4, 8, 16}; q_start + Tq <= Tmax; n_sink >= 0,
+ *   Hq / Hkv in {1, 2, 4, 8, 16}; q_start + Tq <= Tmax < 2^31; n_sink >= 0,
  *   window >= 1.
  * workspace: at least lsa_prefill_attention_workspace_bytes(B, Tq, Hq, D)
  * bytes of device memory (the near state of one launch's rows), caller-owned.

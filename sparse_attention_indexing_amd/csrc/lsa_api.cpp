@@ -725,7 +725,7 @@ int lsa_sparse_attention_prefill(const void* q, const void* k_cache, const void*
   if (q_start < 0 || n_sink < 0 || window < 1) return LSA_ERR_ARG;
   if (rc) return LSA_OK;                       // no rows
   if (q_start + Tq > Tmax) return LSA_ERR_ARG;
-  if (Hkv > 65535) return LSA_ERR_UNSUPPORTED;
+  if (Hkv > 65535 || Tmax > 0x7fffffff) return LSA_ERR_UNSUPPORTED;   // 32-bit positions
   need = near_state_bytes((int64_t)B * Tq, Hq);
   if (!workspace || ws_bytes < need) return LSA_ERR_WORKSPACE;
   hipError_t e = launch_attention_prefill(q, k_cache, v_cache, B, Tq, q_start, Tmax, Hq, Hkv, idx,

@@ -215,34 +215,53 @@ struct NearArgs {
   float* pl;                // [nrows, Hq]: l
   int64_t row0, nrows;      // the launch's rows (global row = b * Tq + t)
   int64_t Tq, q_start, Tmax, n_sink, window;
-  int64_t tile0, tiles_per_seq;
+  int64_t tile0, tiles_per_seq, ntiles;   // the launch's tiles: tile0 .. tile0 + ntiles - 1
   int32_t Hq, Hkv;
   float scale_log2;
 };
 
-// two workgroups per compute unit (at most 128 VGPRs)
+// One workgroup per tile of P = 8 waves x 2 x 16 / G neighbouring positions
+// and one KV head: each wave owns two groups of 16 MFMA columns (positions x
+// the KV head's G query heads), so every K and V fragment it reads from LDS
+// feeds two products.
+constexpr int kNearGroups = 2;                // 16-column groups per wave
+constexpr float kNearLazy = 8.f;              // lazy max: rescale past 2^8
+
 template <int G>
-__global__ __launch_bounds__(kDenseNT) __attribute__((amdgpu_waves_per_eu(4))) void k_near_attn(NearArgs a) {
-  constexpr int PW = 16 / G;                  // positions per wave
-  constexpr int P = kDenseWaves * PW;         // positions per workgroup
+__global__ __launch_bounds__(kDenseNT) void k_near_attn(NearArgs a) {
+  constexpr int PW = 16 / G;                  // positions per 16-column group
+  constexpr int CG = kNearGroups;
+  constexpr int P = kDenseWaves * CG * PW;    // positions per workgroup
   __shared__ __attribute__((aligned(16))) char lds[2][2][kKTile];   // [buffer][K, V]
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kvh = blockIdx.y;
-  const int64_t tile = a.tile0 + blockIdx.x;
+  // neighbouring tiles share almost all of their window keys: the XCD that a
+  // workgroup runs on (blockIdx.x mod 8) takes a contiguous range of tiles,
+  // so that they meet in its L2
+  const int64_t per_xcd = (a.ntiles + 7) / 8;
+  const int64_t local = (int64_t)(blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (local >= a.ntiles) return;                            // uniform over the workgroup
+  const int64_t tile = a.tile0 + local;
   const int64_t b = tile / a.tiles_per_seq;
   const int64_t t0 = (tile % a.tiles_per_seq) * P;           // first position index of the tile
   const int64_t t_end = t0 + P < a.Tq ? t0 + P : a.Tq;       // one past the last
   const int r16 = lane & 15, u = lane >> 4;
   const int pw = r16 / G, g = r16 % G;
-  // this lane's column: position index t, global row b * Tq + t
-  const int64_t t = t0 + (int64_t)wave * PW + pw;
-  const int64_t grow = b * a.Tq + t;
-  const bool col_ok = t < a.Tq && grow >= a.row0 && grow < a.row0 + a.nrows;
-  const int64_t p = a.q_start + (t < a.Tq ? t : a.Tq - 1);
-  const int64_t s_end = p + 1 < a.n_sink ? p + 1 : a.n_sink;
-  const int64_t w_start = p - a.window + 1 > 0 ? p - a.window + 1 : 0;
-  // the workgroup's keys: sinks [0, sk_end), then the windows [wk_lo, wk_hi]
+  // this lane's columns: group c has position index t[c], global row b * Tq + t[c]
+  const int64_t wt0 = t0 + (int64_t)wave * CG * PW;          // the wave's first position
+  int64_t grow[CG], p[CG], s_end[CG], w_start[CG];
+  bool col_ok[CG];
+#pragma unroll
+  for (int c = 0; c < CG; ++c) {
+    const int64_t t = wt0 + c * PW + pw;
+    grow[c] = b * a.Tq + t;
+    col_ok[c] = t < a.Tq && grow[c] >= a.row0 && grow[c] < a.row0 + a.nrows;
+    p[c] = a.q_start + (t < a.Tq ? t : a.Tq - 1);
+    s_end[c] = p[c] + 1 < a.n_sink ? p[c] + 1 : a.n_sink;
+    w_start[c] = p[c] - a.window + 1 > 0 ? p[c] - a.window + 1 : 0;
+  }
+  // the workgroup's keys: sinks [0, sk_end), then the windows up to p_last
   const int64_t p_first = a.q_start + t0, p_last = a.q_start + t_end - 1;
   const int64_t sk_end = p_last + 1 < a.n_sink ? p_last + 1 : a.n_sink;
   const int64_t wk_lo = p_first - a.window + 1 > 0 ? p_first - a.window + 1 : 0;
@@ -251,26 +270,48 @@ __global__ __launch_bounds__(kDenseNT) __attribute__((amdgpu_waves_per_eu(4))) v
   const int64_t n_tiles = ts_end + ((p_last >> 4) >= tw0 ? (p_last >> 4) - tw0 + 1 : 0);
   auto tile_of = [&](int64_t i) -> int64_t { return i < ts_end ? i : tw0 + (i - ts_end); };
   // the wave's keys, to skip tiles that none of its columns reads
-  const int64_t wt0 = t0 + (int64_t)wave * PW;
   const bool wave_live = wt0 < t_end;
   const int64_t wp_first = a.q_start + wt0;
-  const int64_t wp_last = a.q_start + (wt0 + PW - 1 < t_end - 1 ? wt0 + PW - 1 : t_end - 1);
+  const int64_t wp_last = a.q_start + (wt0 + CG * PW - 1 < t_end - 1 ? wt0 + CG * PW - 1 : t_end - 1);
   const int64_t ws_end = wp_last + 1 < a.n_sink ? wp_last + 1 : a.n_sink;
   const int64_t ww_lo = wp_first - a.window + 1 > 0 ? wp_first - a.window + 1 : 0;
 
-  bf16x8 qf[4];
-  {
+  bf16x8 qf[CG][4];
+#pragma unroll
+  for (int c = 0; c < CG; ++c) {
     const int64_t h = (int64_t)kvh * G + g;
-    const u32x4_t* qrow = reinterpret_cast<const u32x4_t*>(a.q + ((col_ok ? grow : 0) * a.Hq + h) * kHeadDim);
+    const u32x4_t* qrow =
+        reinterpret_cast<const u32x4_t*>(a.q + ((col_ok[c] ? grow[c] : 0) * a.Hq + h) * kHeadDim);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      qf[j] = __builtin_bit_cast(bf16x8, col_ok ? qrow[4 * j + u] : u32x4_t{0, 0, 0, 0});
+      qf[c][j] = __builtin_bit_cast(bf16x8, col_ok[c] ? qrow[4 * j + u] : u32x4_t{0, 0, 0, 0});
   }
-  f32x4 o[8];
+  f32x4 o[CG][8];
+  float m[CG], lp[CG];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -1e30f, lp = 0.f;
+  for (int c = 0; c < CG; ++c) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[c][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m[c] = -1e30f;
+    lp[c] = 0.f;
+  }
   const float sl = a.scale_log2;
+  // positions as 32-bit values (the host keeps Tmax below 2^31)
+  int32_t p32[CG], se32[CG], ws32[CG];
+#pragma unroll
+  for (int c = 0; c < CG; ++c) {
+    // an invalid column takes an empty near set
+    p32[c] = col_ok[c] ? (int32_t)p[c] : -1;
+    se32[c] = (int32_t)s_end[c];
+    ws32[c] = (int32_t)w_start[c];
+  }
+  // a tile inside every column's window needs no mask: keys >= the largest
+  // window start and <= the smallest position of the wave (all columns valid)
+  bool all_ok = true;
+#pragma unroll
+  for (int c = 0; c < CG; ++c) all_ok &= col_ok[c];
+  const bool wave_full = __builtin_amdgcn_readfirstlane(__ballot(!all_ok) == 0 ? 1 : 0) != 0;
+  const int64_t full_lo = wp_last - a.window + 1, full_hi = wp_first;
 
   const int ld_v = tid >> 8, ld_key = (tid & 255) >> 4, ld_ch = tid & 15;
   const uint16_t* src = (ld_v ? a.v : a.k) + b * a.Tmax * a.Hkv * kHeadDim;
@@ -318,61 +359,85 @@ __global__ __launch_bounds__(kDenseNT) __attribute__((amdgpu_waves_per_eu(4))) v
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj)
           kf[jj] = *reinterpret_cast<const u32x4_t*>(kt + 256 * r16 + 16 * ((4 * jj + u) ^ r16));
-        f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+        f32x4 sacc[CG];
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[jj]), qf[jj],
-                                                         sacc, 0, 0, 0);
-        // keys 4 u + e of this tile against the column's near set
-        bool ok[4];
-        float x = -__builtin_inff();
+        for (int c = 0; c < CG; ++c) {
+          sacc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int64_t key = kb + 4 * u + e;
-          ok[e] = col_ok && key <= p && (key < s_end || key >= w_start);
-          if (ok[e]) x = fmaxf(x, sacc[e] * sl);
+          for (int jj = 0; jj < 4; ++jj)
+            sacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[jj]),
+                                                              qf[c][jj], sacc[c], 0, 0, 0);
         }
-        x = fmaxf(x, __shfl_xor(x, 16, 64));
-        x = fmaxf(x, __shfl_xor(x, 32, 64));
-        const float mn = fmaxf(m, x);
-        const float alpha = __builtin_amdgcn_exp2f(m - mn);
-        m = mn;
-        lp *= alpha;
+        const bool full = wave_full && kb >= full_lo && kb + 15 <= full_hi;
+        const int32_t kq = (int32_t)kb + 4 * u;            // this lane's first key
+        v4s_t pb4[CG];
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj)
+        for (int c = 0; c < CG; ++c) {
+          // scaled scores of keys 4 u + e (base 2); keys outside the column's
+          // near set get -inf
+          float xs[4];
+          bool up = false;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o[jj][e] *= alpha;
-        float pv[4];
+          for (int e = 0; e < 4; ++e) {
+            const int32_t key = kq + e;
+            const bool ok = full || (key <= p32[c] && (key < se32[c] || key >= ws32[c]));
+            xs[e] = ok ? sacc[c][e] * sl : -__builtin_inff();
+            up |= xs[e] > m[c] + kNearLazy;
+          }
+          // lazy reference max: O and l are rescaled only when a score
+          // exceeds it by more than 2^kNearLazy (they always share it, so the
+          // result does not depend on when that happens)
+          if (__ballot(up)) {
+            float x = fmaxf(fmaxf(xs[0], xs[1]), fmaxf(xs[2], xs[3]));
+            x = fmaxf(x, __shfl_xor(x, 16, 64));
+            x = fmaxf(x, __shfl_xor(x, 32, 64));
+            const float mn = fmaxf(m[c], x);
+            const float alpha = __builtin_amdgcn_exp2f(m[c] - mn);
+            m[c] = mn;
+            lp[c] *= alpha;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          pv[e] = ok[e] ? __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[e], sl, -m)) : 0.f;
-          lp += pv[e];
+            for (int jj = 0; jj < 8; ++jj)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) o[c][jj][e] *= alpha;
+          }
+          float pv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            pv[e] = __builtin_amdgcn_exp2f(xs[e] - m[c]);
+            lp[c] += pv[e];
+          }
+          uint2 w2;
+          w2.x = pack2(pv[0], pv[1]);
+          w2.y = pack2(pv[2], pv[3]);
+          pb4[c] = __builtin_bit_cast(v4s_t, w2);
         }
-        uint2 w2;
-        w2.x = pack2(pv[0], pv[1]);
-        w2.y = pack2(pv[2], pv[3]);
-        const v4s_t pb4 = __builtin_bit_cast(v4s_t, w2);
         const char* vrd = vt + 256 * sk + 8 * (r16 & 1);
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
           const v4s_t va4 = __builtin_bit_cast(
               v4s_t, tr16(reinterpret_cast<const uint16_t*>(vrd + 16 * ((2 * jj + cv) ^ vsw))));
-          o[jj] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va4, pb4, o[jj], 0, 0, 0);
+#pragma unroll
+          for (int c = 0; c < CG; ++c)
+            o[c][jj] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va4, pb4[c], o[c][jj], 0, 0, 0);
         }
       }
     }
   }
-  float l = lp;
-  l += __shfl_xor(l, 16, 64);
-  l += __shfl_xor(l, 32, 64);
-  if (col_ok) {
-    const int64_t h = (int64_t)kvh * G + g;
-    const int64_t slot = (grow - a.row0) * a.Hq + h;
-    float* orow = a.po + slot * kHeadDim + 4 * u;
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      *reinterpret_cast<float4*>(orow + 16 * j) = make_float4(o[j][0], o[j][1], o[j][2], o[j][3]);
-    if (u == 0) { a.pm[slot] = m; a.pl[slot] = l; }
+  for (int c = 0; c < CG; ++c) {
+    float l = lp[c];
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    if (col_ok[c]) {
+      const int64_t h = (int64_t)kvh * G + g;
+      const int64_t slot = (grow[c] - a.row0) * a.Hq + h;
+      float* orow = a.po + slot * kHeadDim + 4 * u;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        *reinterpret_cast<float4*>(orow + 16 * j) = make_float4(o[c][j][0], o[c][j][1], o[c][j][2],
+                                                                o[c][j][3]);
+      if (u == 0) { a.pm[slot] = m[c]; a.pl[slot] = l; }
+    }
   }
 }
 
@@ -409,7 +474,7 @@ hipError_t launch_near_attention(const void* q, const void* k, const void* v, in
   if (nrows <= 0) return hipSuccess;
   const int G = Hq / Hkv;
   if (G < 1 || G > 16 || 16 % G != 0 || Hq % Hkv != 0) return hipErrorInvalidValue;
-  const int P = kDenseWaves * (16 / G);
+  const int P = kDenseWaves * kNearGroups * (16 / G);
   NearArgs a;
   a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;
   a.po = po; a.pm = pm; a.pl = pl;
@@ -420,10 +485,11 @@ hipError_t launch_near_attention(const void* q, const void* k, const void* v, in
   // two sequences; a tile cut by the launch's bounds writes its rows only)
   auto tile_of_row = [&](int64_t r) { return (r / Tq) * a.tiles_per_seq + (r % Tq) / P; };
   a.tile0 = tile_of_row(row0);
-  const int64_t ntiles = tile_of_row(row0 + nrows - 1) - a.tile0 + 1;
+  a.ntiles = tile_of_row(row0 + nrows - 1) - a.tile0 + 1;
   a.Hq = Hq; a.Hkv = Hkv;
   a.scale_log2 = scale * 1.4426950408889634f;
-  dim3 grid((unsigned)ntiles, (unsigned)Hkv);
+  // eight XCD ranges of ceil(ntiles / 8) tiles each
+  dim3 grid((unsigned)(8 * ((a.ntiles + 7) / 8)), (unsigned)Hkv);
   switch (G) {
     case 1: hipLaunchKernelGGL(k_near_attn<1>, grid, dim3(kDenseNT), 0, s, a); break;
     case 2: hipLaunchKernelGGL(k_near_attn<2>, grid, dim3(kDenseNT), 0, s, a); break;
