@@ -158,15 +158,17 @@ def attention_kernel_name(lsa, w, B: int, Tmax: int, prefill: bool = False) -> s
     """The attention kernel (template instance) that lsa_sparse_attention runs;
     with prefill, the two kernels that lsa_sparse_attention_prefill runs per
     launch of up to lsa_attention_launch_rows() rows (the near set's dense
-    tiles, then the far entries' gather)."""
+    tiles, then the far entries' gather; in the one-workgroup-per-row layout
+    the gather takes the near keys too, and runs alone)."""
     if w.dtype != "bf16":
         return "k_attn_f32"
+    nw = 1
     if w.Hkv != 4:
         far = "k_attn_bf16<1, 0" + (", true>" if prefill else ">")
     else:
         nw = 1 if lsa.attention_head_major(B, Tmax, w.Hkv, w.D, lsa.LSA_BF16) else 4
         far = f"k_attn_bf16<{nw}, 4" + (", true>" if prefill else ">")
-    return f"k_near_attn<{w.Hq // w.Hkv}> + {far}" if prefill else far
+    return f"k_near_attn<{w.Hq // w.Hkv}> + {far}" if prefill and nw == 1 else far
 
 
 def measured_traffic(kernel: str, workload: str, rows_per_launch: int, root: str | None = None):

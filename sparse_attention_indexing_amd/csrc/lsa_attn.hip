@@ -245,11 +245,17 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn_bf16(AttnArgs a) {
   // far-key mode: the query's position p and its near set [0, s_end) and
   // [w_start, p]; the state starts from the near set's softmax state
   int64_t p = 0, s_end = 0, w_start = 0;
+  // several waves per row (the one-workgroup-per-row layout): no near state;
+  // the near keys are gathered like the far ones, staged after the list's
+  // entries. One wave per row: the state comes from the near kernel.
+  constexpr bool kInlineNear = NEAR && NW > 1;
+  int nn = 0;                                   // near keys appended
   if constexpr (NEAR) {
     p = a.q_start + (row - b * a.Tq);
     s_end = p + 1 < a.n_sink ? p + 1 : a.n_sink;
     w_start = p - a.window + 1 > 0 ? p - a.window + 1 : 0;
-    if (r16 < a.G) {
+    if constexpr (kInlineNear) nn = (int)(w_start <= s_end ? p + 1 : s_end + (p - w_start + 1));
+    if (!kInlineNear && r16 < a.G) {
       const int64_t slot = (row - a.row0) * a.Hq + (int64_t)kvh * a.G + r16;
       const float4* po = reinterpret_cast<const float4*>(a.near_o + slot * kHeadDim + 4 * u);
 #pragma unroll
@@ -307,24 +313,41 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn_bf16(AttnArgs a) {
   const bool rev = NEAR && ((((int64_t)blockIdx.x * 2 >= gridDim.x) ? 1 : 0) ^
                             (int)((a.row0 / a.nrows_launch) & 1));
   auto stage_far = [&](int c0, int cn) -> int {
-    auto keep = [&](int32_t x) {
+    // a list entry is kept when valid and outside the near set; appended near
+    // keys are always kept
+    auto far = [&](int32_t x) {
       const int64_t e = x;
       return (uint32_t)x < tlim && !(e < s_end || (e >= w_start && e <= p));
     };
     int kept = 0;
     for (int base = 0; base < cn; base += NT * kB) {
       int32_t t[kB];
+      uint64_t km = 0;                                     // inline near: bit u, t[u] is kept
 #pragma unroll
       for (int u = 0; u < kB; ++u) {
-        const int i = base + wave * 64 * kB + 64 * u + lane;
-        t[u] = i < cn ? lst[rev ? n - 1 - (c0 + i) : c0 + i] : -1;
+        const int v = c0 + base + wave * 64 * kB + 64 * u + lane;   // staged entry
+        const bool in = v < c0 + cn;
+        if constexpr (kInlineNear) {
+          // the list's entries (from the end with rev), then near key v - n
+          const int j = v - n;
+          if (!in) t[u] = -1;
+          else if (v < n) t[u] = lst[rev ? n - 1 - v : v];
+          else t[u] = (int32_t)(w_start <= s_end || j < s_end ? j : w_start + (j - s_end));
+          km |= (uint64_t)(in && (v >= n || far(t[u]))) << u;
+        } else {
+          t[u] = in ? lst[rev ? n - 1 - v : v] : -1;
+        }
       }
+      auto keep = [&](int u) {
+        if constexpr (kInlineNear) return ((km >> u) & 1ull) != 0;
+        else return far(t[u]);
+      };
       int off = kept, total = 0;
       if constexpr (NW > 1) {
         // the waves' counts first (the ballots are taken again for the stores)
         int wc = 0;
 #pragma unroll
-        for (int u = 0; u < kB; ++u) wc += __popcll(__ballot(keep(t[u])));
+        for (int u = 0; u < kB; ++u) wc += __popcll(__ballot(keep(u)));
         if (lane == 0) s_wcnt[wave] = wc;
         __syncthreads();
 #pragma unroll
@@ -336,7 +359,7 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn_bf16(AttnArgs a) {
       }
 #pragma unroll
       for (int u = 0; u < kB; ++u) {
-        const bool k = keep(t[u]);
+        const bool k = keep(u);
         const uint64_t bal = __ballot(k);
         const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
                                                          __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
@@ -361,8 +384,9 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn_bf16(AttnArgs a) {
     stage(0, NT * kB, m0, cn);
   }
   stage_sync();
-  for (int c0 = 0; c0 < n; c0 += kList) {
-    int cn = (n - c0) < kList ? (n - c0) : kList;
+  const int nv = n + nn;                          // staged entries (list, then near keys)
+  for (int c0 = 0; c0 < nv; c0 += kList) {
+    int cn = (nv - c0) < kList ? (nv - c0) : kList;
     if constexpr (NEAR) {
       stage_sync();                            // every wave is done with the previous chunk
       cn = stage_far(c0, cn);
@@ -774,19 +798,27 @@ hipError_t launch_attention_prefill(const void* q, const void* k, const void* v,
     attr_set = true;
   }
   const bool head_major = attention_head_major(B, Tmax, Hkv, kHeadDim, LSA_BF16);
+  // One workgroup per row (K/V beyond the Infinity Cache): the near keys are
+  // gathered with the far ones (the window's rows are cache hits either way,
+  // and a separate near pass measured slower there); otherwise the near
+  // kernel takes them dense per tile of rows.
+  const bool near_pass = Hkv != 4 || head_major;
   for (int64_t g0 = 0; g0 < rows; g0 += group) {
     const int64_t gn = (rows - g0) < group ? (rows - g0) : group;
-    hipError_t e = launch_near_attention(q, k, v, g0, gn, Tq, q_start, Tmax, Hq, Hkv, n_sink,
-                                         window, scale, po, pm, pl, s);
-    if (e != hipSuccess) return e;
+    hipError_t e = hipSuccess;
+    if (near_pass) {
+      e = launch_near_attention(q, k, v, g0, gn, Tq, q_start, Tmax, Hq, Hkv, n_sink, window, scale,
+                                po, pm, pl, s);
+      if (e != hipSuccess) return e;
+    }
     for (int64_t r0 = g0; r0 < g0 + gn; r0 += kRowsPerLaunch) {
       a.row0 = r0;
       a.nrows = (g0 + gn - r0) < kRowsPerLaunch ? (g0 + gn - r0) : kRowsPerLaunch;
       // the launch's rows start (r0 - g0) rows into the group's state
       const int64_t off = (r0 - g0) * Hq;
-      a.near_o = po + off * kHeadDim;
-      a.near_m = pm + off;
-      a.near_l = pl + off;
+      a.near_o = near_pass ? po + off * kHeadDim : nullptr;
+      a.near_m = near_pass ? pm + off : nullptr;
+      a.near_l = near_pass ? pl + off : nullptr;
       if (Hkv != 4)
         hipLaunchKernelGGL((k_attn_bf16<1, 0, true>), dim3((unsigned)attn_grid<1>(Hkv, a.nrows)),
                            dim3(64), (size_t)kLds4<1>, s, a);

@@ -1,4 +1,5 @@
-// Dense (and banded) causal attention over contiguous key ranges, bf16.
+// Dense (and banded) causal attention over contiguous key ranges, bf16, and
+// the near-set part of the prefill attention (k_near_attn, below).
 //
 // The baseline the pages compare sparse attention with is full attention
 // ([72x "Why choosing costs so much"]; [summary]: 72.4x prefill over full
@@ -197,13 +198,13 @@ __global__ __launch_bounds__(kDenseNT) void k_dense_attn(DenseArgs a) {
 // "What one query actually does"]: the sinks and the window are always
 // read): keys [0, min(p + 1, S)) and [max(p - W + 1, 0), p] for a query at
 // position p.  Consecutive queries share almost all of them (the windows of
-// 16 neighbours cover W + 15 keys), so instead of gathering them once per
-// query they are attended here once per tile of neighbouring queries, with the
-// same workgroup shape as k_dense_attn (8 waves x 16 / G positions, one KV
-// head), over the tile's sink keys and the union of its windows.  The result
-// is the softmax state of that partial attention per (row, head): O relative
-// to the reference max m (base 2, scaled), m, and the sum l; the gather kernel
-// starts from it and adds the list's remaining (far) keys.
+// 32 neighbours cover W + 31 keys), so instead of gathering them once per
+// query they are attended here once per tile of neighbouring queries (one KV
+// head, 8 waves, each with two groups of 16 MFMA columns), over the tile's
+// sink keys and the union of its windows.  The result is the softmax state of
+// that partial attention per (row, head): O relative to the reference max m
+// (base 2, scaled), m, and the sum l; the gather kernel starts from it and
+// adds the list's remaining (far) keys.
 constexpr int kNearRing = 6;                 // K/V tiles in flight per near workgroup
 
 struct NearArgs {

@@ -33,7 +33,7 @@ def test_attention_kernel_names():
     assert bench.attention_kernel_name(lsa, w2, 1, w2.T) == "k_attn_bf16<1, 4>"
     assert bench.attention_kernel_name(lsa, w2, 1, w2.T, True) == KERNEL
     assert bench.attention_kernel_name(lsa, w4, 1, w4.T) == "k_attn_bf16<4, 4>"
-    assert bench.attention_kernel_name(lsa, w5, 1, w5.T, True) == "k_near_attn<8> + k_attn_bf16<4, 4, true>"
+    assert bench.attention_kernel_name(lsa, w5, 1, w5.T, True) == "k_attn_bf16<4, 4, true>"
     assert bench.attention_kernel_name(lsa, S.WORKLOADS[1], 1, 4096) == "k_attn_f32"
 
 
