@@ -196,9 +196,11 @@ int64_t lsa_index_workspace_bytes(const lsa_params* p, int64_t max_queries);
  * n_queries queries (or an lsa_index_decode call over n_queries sequences),
  * of the int32 flag per query that the call leaves behind: 1 when that
  * query's B best buckets were selected by the exact fallback (its
- * candidate list from the sampled score threshold held fewer than B or more
- * candidates than fit, so every eligible bucket was rescored in one
- * workgroup), 0 otherwise (always 1 with exact_select).  The flags stay
+ * candidate list from the sampled score threshold held more candidates than
+ * fit, or fewer than k far keys while more buckets were eligible, so every
+ * eligible bucket was rescored in one workgroup; with a `ranked` output
+ * also when it held fewer than B buckets), 0 otherwise (always 1 with
+ * exact_select).  The flags stay
  * valid, once the stream has passed the call, until the workspace is
  * reused.  Negative status on invalid parameters. */
 int64_t lsa_index_status_offset(const lsa_params* p, int64_t n_queries);

@@ -103,7 +103,7 @@ int32_t top_b(const lsa_params* p) {
   return (p->k + kPool - 1) / kPool + kBuckets * win_blocks + (p->n_sink + kPool - 1) / kPool;
 }
 
-// candidate slots per query: >= 3 B (tau aims at ~2 B): a power of two up to
+// candidate slots per query: >= 3 B (tau aims at ~5/4 B): a power of two up to
 // 8,192, beyond that a multiple of 1,024
 int32_t cand_cap(const lsa_params* p) {
   const int64_t want = 3 * (int64_t)top_b(p);

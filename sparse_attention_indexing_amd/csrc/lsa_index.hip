@@ -209,6 +209,19 @@ __device__ __forceinline__ int tile_row(int r, int lane) {
 // the smallest member, and early and late ranks differ in size and spread).
 __device__ __forceinline__ int64_t sample_bucket(int64_t j) { return 16 * j + ((7 * j) & 15); }
 
+// tau aims at kTauNum / kTauDen x B buckets of the full set above it (B =
+// top_b, enough buckets for k far keys when every bucket holds the fewest
+// keys): 5/4 B / 16 samples above tau.  Buckets hold two pooled items on
+// average, so the candidates usually hold well over k far keys; when they
+// do not, the selection falls back to the exact top-B.
+constexpr int64_t kTauNum = 5, kTauDen = 4;
+__host__ __device__ __forceinline__ int64_t tau_candidates(int64_t top_b) {
+  return (kTauNum * top_b + kTauDen - 1) / kTauDen;
+}
+__host__ __device__ __forceinline__ int64_t tau_samples(int64_t top_b) {
+  return (tau_candidates(top_b) + kSampleStride - 1) / kSampleStride;
+}
+
 // ------------------------------------------------------------------ thresh
 // Histogram of sampled scores per query -> tau.  Workgroup = 128 queries.
 template <int DT>
@@ -254,8 +267,7 @@ __global__ __launch_bounds__(256) void k_thresh(IndexCtx ctx, IndexWs ws) {
       const int64_t nej = n_eligible(ctx, qpos(ctx, qj));
       float tau = -3.0e38f;
       if (nej > ctx.cap) {
-        // expect ~2 B full-set scores above tau: 2 B / 16 samples above it
-        const int64_t want = (2 * (int64_t)ctx.top_b + kSampleStride - 1) / kSampleStride;
+        const int64_t want = tau_samples(ctx.top_b);
         int64_t cum = 0;
         for (int b = kBins - 1; b >= 0; --b) {
           cum += hist[tid][b];
@@ -321,7 +333,7 @@ __global__ __launch_bounds__(64) void k_thresh_tau(IndexCtx ctx, IndexWs ws, int
   const int64_t nej = n_eligible(ctx, qpos(ctx, qj));
   float tau = -3.0e38f;
   if (nej > ctx.cap) {
-    const int64_t want = (2 * (int64_t)ctx.top_b + kSampleStride - 1) / kSampleStride;
+    const int64_t want = tau_samples(ctx.top_b);
     const uint32_t* h = ws.hist + qj * 256;
     int64_t cum = 0;
     for (int b = kBins - 1; b >= 0; --b) {
@@ -842,7 +854,7 @@ __global__ __launch_bounds__(512, 1) void k_thresh_q128(IndexCtx ctx, IndexWs ws
       const int64_t nej = n_eligible(ctx, ctx.q_start + qj);
       float tau = -3.0e38f;
       if (nej > ctx.cap) {
-        const int64_t want = (2 * (int64_t)ctx.top_b + kSampleStride - 1) / kSampleStride;
+        const int64_t want = tau_samples(ctx.top_b);
         int64_t cum = 0;
         for (int b = kBins - 1; b >= 0; --b) {
           cum += hist[tid][b];
@@ -965,7 +977,7 @@ __global__ __launch_bounds__(256) void k_mh_thresh(IndexCtx ctx, IndexWs ws) {
       const int64_t nej = n_eligible(ctx, qpos(ctx, qj));
       float tau = -3.0e38f;
       if (nej > ctx.cap) {
-        const int64_t want = (2 * (int64_t)ctx.top_b + kSampleStride - 1) / kSampleStride;
+        const int64_t want = tau_samples(ctx.top_b);
         int64_t cum = 0;
         for (int b = kBins - 1; b >= 0; --b) {
           cum += hist[tid][b];
@@ -1115,7 +1127,7 @@ constexpr int kDecStage = 64;           // LDS candidate slots per wave
 // tau of query qi from its sampled histogram, computed by one wave: lane l
 // sums the 4 bins 4 (63 - l) .. 4 (63 - l) + 3, so an inclusive prefix over
 // lanes counts samples from the top bin down; tau is the lower edge of the
-// bin where the count reaches about 2 B / 16 samples (the same in every lane)
+// bin where the count reaches tau_samples (the same in every lane)
 __device__ __forceinline__ float dec_tau_wave(const IndexCtx& ctx, const IndexWs& ws, int64_t qi,
                                              int lane) {
   const int64_t ne = n_eligible(ctx, ctx.pos[qi]);
@@ -1130,7 +1142,7 @@ __device__ __forceinline__ float dec_tau_wave(const IndexCtx& ctx, const IndexWs
     const uint32_t o = __shfl_up(incl, off, 64);
     if (lane >= off) incl += o;
   }
-  const uint32_t want = (uint32_t)((2 * (int64_t)ctx.top_b + kSampleStride - 1) / kSampleStride);
+  const uint32_t want = (uint32_t)tau_samples(ctx.top_b);
   const uint64_t hit = __ballot(incl >= want);
   if (!hit) return -3.0e38f;
   const int l = __builtin_ctzll(hit);
@@ -2168,88 +2180,97 @@ __global__ __launch_bounds__(NT) void k_select_expand(IndexCtx ctx, IndexWs ws, 
   }
   int c = ws.cand_cnt[qi];
   bool used_exact = false;
-  {
-    const int64_t ne = n_eligible(ctx, p);
-    const int64_t beff = ne < ctx.top_b ? ne : ctx.top_b;
-    if (exact_mode == 2 || (exact_mode == 1 && (c < beff || c > cap))) {
-      used_exact = true;
-      c = exact_select_lds<DT, NT>(ctx, ws, qi, ne, beff, skey, sbkt, &hist[0][0], &s_prefix, &s_want,
-                                   wsum, &s_total, SCAN ? ctx.heads : 1);
-    } else {
-      c = c < cap ? c : cap;
-      if constexpr (NT < 1024) {
-#pragma unroll
-        for (int jj = 0; jj < PER; ++jj) {
-          const int i = tid + NT * jj;
-          e[jj] = i < c ? cand[i] : make_uint2(0, 0);
-        }
-      }
+  const int64_t ne = n_eligible(ctx, p);
+  const int64_t beff = ne < ctx.top_b ? ne : ctx.top_b;
+  // the scoring pass's candidates serve unless they overflowed the list (or
+  // the ranking output asks for B buckets and they are fewer)
+  bool need_exact = exact_mode == 2 || (exact_mode == 1 && (c > cap || (ranked && c < beff)));
+  if (!need_exact) {
+    c = c < cap ? c : cap;
+    if constexpr (NT < 1024) {
 #pragma unroll
       for (int jj = 0; jj < PER; ++jj) {
         const int i = tid + NT * jj;
-        if (i < c) { skey[i] = e[jj].x; sbkt[i] = e[jj].y; }
+        e[jj] = i < c ? cand[i] : make_uint2(0, 0);
       }
     }
+#pragma unroll
+    for (int jj = 0; jj < PER; ++jj) {
+      const int i = tid + NT * jj;
+      if (i < c) { skey[i] = e[jj].x; sbkt[i] = e[jj].y; }
+    }
   }
+  int total;
   // member words of this thread's candidates (all loads issued together;
   // from the candidate registers when they hold the list, before the barrier)
   uint32_t mw[PER];
-  const bool mw_early = NT >= 1024 && !used_exact;
-  if (mw_early) {
+#pragma unroll 1
+  for (int pass = 0; pass < 2; ++pass) {
+    if (need_exact) {
+      used_exact = true;
+      c = exact_select_lds<DT, NT>(ctx, ws, qi, ne, beff, skey, sbkt, &hist[0][0], &s_prefix,
+                                   &s_want, wsum, &s_total, SCAN ? ctx.heads : 1);
+    }
+    const bool mw_early = NT >= 1024 && !used_exact;
+    if (mw_early) {
+#pragma unroll
+      for (int jj = 0; jj < PER; ++jj) {
+        const int i = tid + NT * jj;
+        mw[jj] = (i < c && run_keys == 0) ? mem[e[jj].y] : 0xFFFFFFFFu;
+      }
+    }
+    __syncthreads();
+    if (!mw_early) {
+#pragma unroll
+      for (int jj = 0; jj < PER; ++jj) {
+        const int i = tid + NT * jj;
+        mw[jj] = (i < c && run_keys == 0) ? mem[sbkt[i]] : 0xFFFFFFFFu;
+      }
+    }
+    // far-key contributions (members outside the near set)
+    int my_w = 0;
 #pragma unroll
     for (int jj = 0; jj < PER; ++jj) {
       const int i = tid + NT * jj;
-      mw[jj] = (i < c && run_keys == 0) ? mem[e[jj].y] : 0xFFFFFFFFu;
-    }
-  }
-  __syncthreads();
-  if (!mw_early) {
+      if (i >= c) continue;
+      const uint32_t g = sbkt[i];
+      const uint32_t m = mw[jj];
+      const int64_t kb = (int64_t)(g / kBuckets) * kBlock;
+      int ci = 0;
+      if (run_keys) {
+        // a scan's run: its keys that are not sinks (every eligible run ends
+        // before the window)
+        const int64_t r0 = (int64_t)g * run_keys;
+        const int64_t lo = s_end > r0 ? s_end : r0;
+        ci = r0 + run_keys > lo ? (int)(r0 + run_keys - lo) : 0;
+      } else if (kb >= s_end && kb + kBlock <= w_start) {
+        // block without sink or window keys: every member key is far
 #pragma unroll
-    for (int jj = 0; jj < PER; ++jj) {
-      const int i = tid + NT * jj;
-      mw[jj] = (i < c && run_keys == 0) ? mem[sbkt[i]] : 0xFFFFFFFFu;
-    }
-  }
-  // far-key contributions (members outside the near set)
-  int my_w = 0;
+        for (int q = 0; q < kCapItems; ++q) ci += ((m >> (8 * q)) & 0xFFu) != 0xFFu ? kPool : 0;
+      } else {
 #pragma unroll
-  for (int jj = 0; jj < PER; ++jj) {
-    const int i = tid + NT * jj;
-    if (i >= c) continue;
-    const uint32_t g = sbkt[i];
-    const uint32_t m = mw[jj];
-    const int64_t kb = (int64_t)(g / kBuckets) * kBlock;
-    int ci = 0;
-    if (run_keys) {
-      // a scan's run: its keys that are not sinks (every eligible run ends
-      // before the window)
-      const int64_t r0 = (int64_t)g * run_keys;
-      const int64_t lo = s_end > r0 ? s_end : r0;
-      ci = r0 + run_keys > lo ? (int)(r0 + run_keys - lo) : 0;
-    } else if (kb >= s_end && kb + kBlock <= w_start) {
-      // block without sink or window keys: every member key is far
+        for (int q = 0; q < kCapItems; ++q) {
+          const uint32_t j = (m >> (8 * q)) & 0xFFu;
+          if (j != 0xFFu) {
 #pragma unroll
-      for (int q = 0; q < kCapItems; ++q) ci += ((m >> (8 * q)) & 0xFFu) != 0xFFu ? kPool : 0;
-    } else {
-#pragma unroll
-      for (int q = 0; q < kCapItems; ++q) {
-        const uint32_t j = (m >> (8 * q)) & 0xFFu;
-        if (j != 0xFFu) {
-#pragma unroll
-          for (int u = 0; u < kPool; ++u) {
-            const int64_t key = kb + kPool * j + u;
-            ci += !(key < s_end || key >= w_start);
+            for (int u = 0; u < kPool; ++u) {
+              const int64_t key = kb + kPool * j + u;
+              ci += !(key < s_end || key >= w_start);
+            }
           }
         }
       }
+      skey[i] = f32_orderable(__uint_as_float(skey[i]));
+      contrib[i] = (uint8_t)ci;
+      my_w += ci;
     }
-    skey[i] = f32_orderable(__uint_as_float(skey[i]));
-    contrib[i] = (uint8_t)ci;
-    my_w += ci;
+    if (tid == 0) { s_trunc_m = 0; s_total = 0; }
+    (void)block_scan_nt<NT>(my_w, wsum, &total);   // also orders the LDS writes above
+    // candidates above tau holding fewer than k far keys while more buckets
+    // are eligible: the exact top-B instead (uniform over the workgroup)
+    need_exact = exact_mode == 1 && !used_exact && ctx.k > 0 && total < ctx.k && c < ne;
+    if (!need_exact) break;
   }
-  if (tid == 0) { s_trunc_m = 0; s_total = 0; }
-  int total;
-  (void)block_scan_nt<NT>(my_w, wsum, &total);   // also orders the LDS writes above
   // optional output: the kept buckets best first (O(c^2) ranking; for tests)
   if (ranked) {
     const int nb = c < ctx.top_b ? c : ctx.top_b;
@@ -2518,13 +2539,13 @@ hipError_t launch_score_filter(const IndexCtx& ctx, const IndexWs& ws, int dtype
     return hipGetLastError();
   }
   if (!ctx.per_seq && dtype == LSA_BF16) {
-    // segment length: about kCapL / 4 expected candidates per query for the
-    // widest query (~2 B of ne_max pass), so the LDS lists rarely overflow;
+    // segment length: about kCapL / 2 expected candidates per query for the
+    // widest query (~5/4 B of ne_max pass), so the LDS lists rarely overflow;
     // when even 16 tiles expect more, workgroups take the high-pass epilogue
     // and longer segments only save query loads
     const int64_t last = ctx.q_start + ctx.n - 1;
     const int64_t ne_max = n_eligible(ctx, last);
-    const int64_t seg_buckets = (int64_t)(kCapL / 4) * ne_max / (2 * (int64_t)(ctx.top_b > 0 ? ctx.top_b : 1));
+    const int64_t seg_buckets = (int64_t)(kCapL / 2) * ne_max / tau_candidates(ctx.top_b > 0 ? ctx.top_b : 1);
     int64_t seg = seg_buckets / kTile;
     seg = seg < 16 ? 16 : (seg > 512 ? 512 : seg & ~(int64_t)7);
     if (seg_buckets < 16 * kTile) seg = 128;
@@ -2535,7 +2556,7 @@ hipError_t launch_score_filter(const IndexCtx& ctx, const IndexWs& ws, int dtype
     int64_t x_lp = qt;
     for (int64_t x = 0; x < qt; ++x) {
       const int64_t nmin = n_eligible(ctx, ctx.q_start + x * kQueriesPerWg);
-      if (nmin > ctx.cap && seg * kTile * 2 * (int64_t)ctx.top_b <= (int64_t)(kCapL / 4) * nmin) {
+      if (nmin > ctx.cap && seg * kTile * tau_candidates(ctx.top_b) <= (int64_t)(kCapL / 2) * nmin) {
         x_lp = x;
         break;
       }
