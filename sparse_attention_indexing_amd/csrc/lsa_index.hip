@@ -2019,10 +2019,10 @@ __device__ uint32_t weighted_select(int c, KeyF key, FiltF filt, const uint8_t* 
 }
 
 
-// ---- few-query selection helpers (workgroups of NT >= 1024 threads) ------
+// ---- selection helpers ----------------------------------------------------
 // A query that waits alone on its workgroup (decode) pays for every barrier of
-// the selection; these take the weighted select and the far-key sort in far
-// fewer of them.
+// the selection; these take the weighted select (every workgroup size) and,
+// with 1,024 threads, the far-key sort in far fewer of them.
 
 // Weighted selection in one histogram pass: candidates i < c of weight w[i] >
 // 0, ordered by key descending, then bucket ascending; finds the candidate at
@@ -2031,15 +2031,16 @@ __device__ uint32_t weighted_select(int c, KeyF key, FiltF filt, const uint8_t* 
 // kRangeBins bins (a monotone map, so every bin above the crossing one is taken
 // whole); the crossing bin is then ranked exactly by one wave.  Returns false
 // (uniformly) when that bin holds more than 64 candidates; the caller then
-// takes the radix passes.
-constexpr int kRangeBins = 2048;
+// takes the radix passes.  Workgroups of many queries (256 or 512 threads)
+// use it too, with as many bins as their radix histograms hold.
 constexpr int kRangeSel = 4 + 3 * 64;   // words of `sh`
 
 template <int NT>
 __device__ bool range_select(int c, const uint32_t* key, const uint32_t* bkt, const uint8_t* w,
                              uint32_t want, uint32_t* bins, uint32_t* sh, int* wsum,
                              uint32_t& key_out, uint32_t& bkt_out, uint32_t& rest_out) {
-  static_assert(NT >= 1024 && kRangeBins % NT == 0, "bins per thread");
+  constexpr int kRangeBins = NT >= 512 ? 2048 : 1024;   // <= the NT / 64 x 256 radix bins
+  static_assert(NT >= 256 && kRangeBins % NT == 0 && kRangeBins <= NT / 64 * 256, "bins per thread");
   constexpr int E = kRangeBins / NT;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // key range of the weighted candidates
@@ -2126,8 +2127,9 @@ __device__ bool range_select(int c, const uint32_t* key, const uint32_t* bkt, co
 // fp32 scores weighted by each bucket's far-key contribution gives the score
 // S* at which the running sum crosses k; buckets above S* are taken whole,
 // buckets tied at S* are walked in bucket order, the crossing one is cut.
-// Every candidate list holds the exact top-B (or every eligible bucket), so
-// the crossing lies inside it.  The far keys are then radix-sorted.
+// A candidate list is used when it holds every bucket scoring at least tau
+// and k far keys (or every eligible bucket); else the exact top-B replaces
+// it, so the crossing lies inside it.  The far keys are then radix-sorted.
 // PER = candidate slots per thread (cap / NT): thread t owns candidates
 // t, t + NT, ..., whose member words stay in registers from the contribution
 // count to the emission.  NT = 256 for many queries; a few queries (decode)
@@ -2151,7 +2153,7 @@ __global__ __launch_bounds__(NT) void k_select_expand(IndexCtx ctx, IndexWs ws, 
   __shared__ int wsum[NT / 64];
   __shared__ uint32_t s_prefix, s_want;
   __shared__ int s_total, s_trunc_m;
-  __shared__ uint32_t s_rsel[NT >= 1024 ? kRangeSel : 1];
+  __shared__ uint32_t s_rsel[kRangeSel];
   const int tid = threadIdx.x;
   const int64_t qi = blockIdx.x;
   // keys per scan run; 0 for buckets (a compile-time 0 keeps the scan
@@ -2289,7 +2291,7 @@ __global__ __launch_bounds__(NT) void k_select_expand(IndexCtx ctx, IndexWs ws, 
   const bool cut = k > 0 && total >= k;
   if (cut) {
     bool fast = false;
-    if constexpr (NT >= 1024) {
+    {
       uint32_t ko, bo, ro;
       fast = range_select<NT>(c, skey, sbkt, contrib, want, &hist[0][0], s_rsel, wsum, ko, bo, ro);
       if (fast) { prefix = ko; gstar_key = 0xFFFFFFFFu - bo; want = ro; }
