@@ -209,17 +209,19 @@ __device__ __forceinline__ int tile_row(int r, int lane) {
 // the smallest member, and early and late ranks differ in size and spread).
 __device__ __forceinline__ int64_t sample_bucket(int64_t j) { return 16 * j + ((7 * j) & 15); }
 
-// tau aims at kTauNum / kTauDen x B buckets of the full set above it (B =
-// top_b, enough buckets for k far keys when every bucket holds the fewest
-// keys): 5/4 B / 16 samples above tau.  Buckets hold two pooled items on
-// average, so the candidates usually hold well over k far keys; when they
-// do not, the selection falls back to the exact top-B.
-constexpr int64_t kTauNum = 5, kTauDen = 4;
-__host__ __device__ __forceinline__ int64_t tau_candidates(int64_t top_b) {
-  return (kTauNum * top_b + kTauDen - 1) / kTauDen;
+// tau aims at a multiple of B buckets of the full set above it (B = top_b,
+// enough buckets for k far keys when every bucket holds the fewest keys),
+// divided by 16 samples.  LSA buckets hold two pooled items on average, so
+// 5/4 B of them usually hold well over k far keys; a scan's runs all hold
+// the same number of keys (B of them hold just k), so scans aim at 2 B.  When
+// the candidates hold fewer than k far keys, the selection falls back to
+// the exact top-B.
+__host__ __device__ __forceinline__ int64_t tau_candidates(const IndexCtx& ctx) {
+  const int64_t b = ctx.top_b > 0 ? ctx.top_b : 1;
+  return ctx.run_keys ? 2 * b : (5 * b + 3) / 4;
 }
-__host__ __device__ __forceinline__ int64_t tau_samples(int64_t top_b) {
-  return (tau_candidates(top_b) + kSampleStride - 1) / kSampleStride;
+__host__ __device__ __forceinline__ int64_t tau_samples(const IndexCtx& ctx) {
+  return (tau_candidates(ctx) + kSampleStride - 1) / kSampleStride;
 }
 
 // ------------------------------------------------------------------ thresh
@@ -267,7 +269,7 @@ __global__ __launch_bounds__(256) void k_thresh(IndexCtx ctx, IndexWs ws) {
       const int64_t nej = n_eligible(ctx, qpos(ctx, qj));
       float tau = -3.0e38f;
       if (nej > ctx.cap) {
-        const int64_t want = tau_samples(ctx.top_b);
+        const int64_t want = tau_samples(ctx);
         int64_t cum = 0;
         for (int b = kBins - 1; b >= 0; --b) {
           cum += hist[tid][b];
@@ -333,7 +335,7 @@ __global__ __launch_bounds__(64) void k_thresh_tau(IndexCtx ctx, IndexWs ws, int
   const int64_t nej = n_eligible(ctx, qpos(ctx, qj));
   float tau = -3.0e38f;
   if (nej > ctx.cap) {
-    const int64_t want = tau_samples(ctx.top_b);
+    const int64_t want = tau_samples(ctx);
     const uint32_t* h = ws.hist + qj * 256;
     int64_t cum = 0;
     for (int b = kBins - 1; b >= 0; --b) {
@@ -854,7 +856,7 @@ __global__ __launch_bounds__(512, 1) void k_thresh_q128(IndexCtx ctx, IndexWs ws
       const int64_t nej = n_eligible(ctx, ctx.q_start + qj);
       float tau = -3.0e38f;
       if (nej > ctx.cap) {
-        const int64_t want = tau_samples(ctx.top_b);
+        const int64_t want = tau_samples(ctx);
         int64_t cum = 0;
         for (int b = kBins - 1; b >= 0; --b) {
           cum += hist[tid][b];
@@ -977,7 +979,7 @@ __global__ __launch_bounds__(256) void k_mh_thresh(IndexCtx ctx, IndexWs ws) {
       const int64_t nej = n_eligible(ctx, qpos(ctx, qj));
       float tau = -3.0e38f;
       if (nej > ctx.cap) {
-        const int64_t want = tau_samples(ctx.top_b);
+        const int64_t want = tau_samples(ctx);
         int64_t cum = 0;
         for (int b = kBins - 1; b >= 0; --b) {
           cum += hist[tid][b];
@@ -1142,7 +1144,7 @@ __device__ __forceinline__ float dec_tau_wave(const IndexCtx& ctx, const IndexWs
     const uint32_t o = __shfl_up(incl, off, 64);
     if (lane >= off) incl += o;
   }
-  const uint32_t want = (uint32_t)tau_samples(ctx.top_b);
+  const uint32_t want = (uint32_t)tau_samples(ctx);
   const uint64_t hit = __ballot(incl >= want);
   if (!hit) return -3.0e38f;
   const int l = __builtin_ctzll(hit);
@@ -2542,12 +2544,12 @@ hipError_t launch_score_filter(const IndexCtx& ctx, const IndexWs& ws, int dtype
   }
   if (!ctx.per_seq && dtype == LSA_BF16) {
     // segment length: about kCapL / 2 expected candidates per query for the
-    // widest query (~5/4 B of ne_max pass), so the LDS lists rarely overflow;
+    // widest query (tau_candidates of ne_max pass), so the LDS lists rarely overflow;
     // when even 16 tiles expect more, workgroups take the high-pass epilogue
     // and longer segments only save query loads
     const int64_t last = ctx.q_start + ctx.n - 1;
     const int64_t ne_max = n_eligible(ctx, last);
-    const int64_t seg_buckets = (int64_t)(kCapL / 2) * ne_max / tau_candidates(ctx.top_b > 0 ? ctx.top_b : 1);
+    const int64_t seg_buckets = (int64_t)(kCapL / 2) * ne_max / tau_candidates(ctx);
     int64_t seg = seg_buckets / kTile;
     seg = seg < 16 ? 16 : (seg > 512 ? 512 : seg & ~(int64_t)7);
     if (seg_buckets < 16 * kTile) seg = 128;
@@ -2558,7 +2560,7 @@ hipError_t launch_score_filter(const IndexCtx& ctx, const IndexWs& ws, int dtype
     int64_t x_lp = qt;
     for (int64_t x = 0; x < qt; ++x) {
       const int64_t nmin = n_eligible(ctx, ctx.q_start + x * kQueriesPerWg);
-      if (nmin > ctx.cap && seg * kTile * tau_candidates(ctx.top_b) <= (int64_t)(kCapL / 2) * nmin) {
+      if (nmin > ctx.cap && seg * kTile * tau_candidates(ctx) <= (int64_t)(kCapL / 2) * nmin) {
         x_lp = x;
         break;
       }
