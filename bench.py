@@ -384,7 +384,9 @@ def bench_tree_sweep(args, w, dev):
     beam higher up and ranking every bucket under it flat, the two-stage search
     -- the chunk's index time (HIP events, best of three) and each query's
     far-key recall: the share of its exact flat list's far keys (outside the
-    sinks and the window) that the tree list also holds."""
+    sinks and the window) that the tree list also holds.  Then beams of 128,
+    256 and 512, and beam 64 with a fixed-level first stage (start level =
+    the leaf level, +2, +4), each at its default leaf level."""
     import ctypes
 
     import torch
@@ -447,6 +449,29 @@ def bench_tree_sweep(args, w, dev):
                                recall_p10=round(torch.quantile(rec, 0.1).item(), 4),
                                recall_min=round(rec.min().item(), 4)))
             log(f"beam {beam:3d} leaf {leaf:2d}: index {ms:7.3f} ms, recall {points[-1]['recall_mean']:.3f}")
+    # wider beams (one workgroup per query) at their default leaf level, and
+    # beam 64 with a fixed-level first stage: every node of level `start`
+    # scored, the best 64 kept, then the descent (start = leaf level: the
+    # two-stage search)
+    wide = []
+    for beam, start in ((128, -1), (256, -1), (512, -1), (64, 0), (64, 2), (64, 4)):
+        p0 = lsa.Params(mode=lsa.LSA_TREE, beam=beam, **base)
+        l0 = 0
+        while beam << l0 < lsa.top_buckets(p0):
+            l0 += 1
+        st = -1 if start < 0 else l0 + start
+        p = lsa.Params(mode=lsa.LSA_TREE, beam=beam, start_level=st, **base)
+        if lsa.lib().lsa_check_params(ctypes.byref(p.c())) != 0:
+            continue
+        ms, (tidx, _) = run(p)
+        trow, tkey, _ = far_keys(tidx)
+        hit = torch.isin(tkey, fkey)
+        hits = torch.bincount(trow[hit], minlength=w.Tq).to(torch.float64)
+        rec = (hits / fcount.clamp(min=1).to(torch.float64))[fcount > 0]
+        wide.append(dict(beam=beam, leaf_level=l0, start_level=st, index_ms=round(ms, 4),
+                         recall_mean=round(rec.mean().item(), 4),
+                         recall_p10=round(torch.quantile(rec, 0.1).item(), 4)))
+        log(f"beam {beam:3d} start {st:2d}: index {ms:7.3f} ms, recall {wide[-1]['recall_mean']:.3f}")
     default = next(q for q in points if q["beam"] == 64)
     res = {
         "metric": "tree/flat far-key recall (beam 64, default leaf level)",
@@ -457,6 +482,7 @@ def bench_tree_sweep(args, w, dev):
                    "k": w.k, "parallelism": "none"},
         "flat_index_ms": round(flat_ms, 4),
         "points": points,
+        "wide_and_fixed_level": wide,
     }
     print(json.dumps(res), flush=True)
 
