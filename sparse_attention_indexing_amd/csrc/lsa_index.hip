@@ -14,19 +14,20 @@
 // Flat prefill selection is exact without materialising the
 // (queries x buckets) score matrix:
 //   1. k_thresh: bf16 MFMA scores on a 1/16 sample of bucket tiles, a per-query
-//      histogram, and a threshold tau whose expected pass count is ~2x the
-//      number of buckets kept (B);
+//      histogram, and a threshold tau whose expected pass count is 5/4 of the
+//      number of buckets kept (B) (2 B for the scans' runs);
 //   2. k_score_lowpass / k_score_highpass (k_dec_filter in decode): every
 //      eligible score on MFMA; scores >= tau are appended (score, bucket) to
 //      a per-query candidate list;
-//   3. k_select_expand: a query whose list holds fewer than B or more than
-//      `cap` candidates is first redone exactly (radix select on recomputed
-//      scores, ties to the lower bucket); then the buckets are taken in
-//      (score desc, bucket asc) order until k far keys are reached (weighted
-//      radix select), expanded, the far keys sorted, and sinks | far |
-//      window written.
-// Every bucket with a score >= the B-th best score is a candidate, so the
-// kept set equals the exact top-B whenever step 2 did not overflow.
+//   3. k_select_expand: the buckets are taken in (score desc, bucket asc)
+//      order until k far keys are reached (weighted select), expanded, the
+//      far keys sorted, and sinks | far | window written.  A query whose
+//      list overflowed `cap`, or whose candidates hold fewer than k far keys
+//      while more buckets are eligible, is first redone exactly (radix select
+//      on recomputed scores, ties to the lower bucket).
+// Every bucket scoring >= tau is a candidate, so when the candidates hold k
+// far keys every bucket ranked up to the crossing one is among them and the
+// walk equals the walk over all eligible buckets.
 #include "lsa_internal.h"
 
 namespace lsa {
@@ -1451,8 +1452,8 @@ __device__ __forceinline__ int block_scan_excl(int v, int* wsum, int* total) {
 }
 
 // Exact top-B of one query, for a workgroup whose candidate list is unusable
-// (fewer than B or more than `cap` candidates) or when exact selection is
-// forced: the B-th largest score by 4 radix passes of 8 bits over the
+// (more than `cap` candidates, or fewer than k far keys in them while more
+// buckets are eligible) or when exact selection is forced: the B-th largest score by 4 radix passes of 8 bits over the
 // order-preserving integer image of the fp32 score, then every bucket above
 // it and, among buckets equal to it, the lowest.  Writes raw score bits to
 // skey[] and buckets to sbkt[] (LDS) and returns the count (min(B, ne)).
