@@ -105,6 +105,13 @@ MUTATIONS = [
      "while prm.beam * (1 << l) < -(-prm.k // prm.n_pool) + 65:",
      "l* from the default-window bound", [P.test_leaf_level_reading,
                                            TP.test_top_b_reading_by_hand]),
+    # max over query heads (N-LSA scoring)
+    ("bucket_scores", "return (cent @ yhat.T).max(axis=1)", "return (cent @ yhat.T).mean(axis=1)",
+     "heads averaged instead of maxed", [P.test_max_over_heads_bucket_scores_hand_worked,
+                                         P.test_max_over_heads_lists_by_hand]),
+    ("bucket_scores", "return (cent @ yhat.T).max(axis=1)", "return cent @ yhat[0]",
+     "first head only", [P.test_max_over_heads_bucket_scores_hand_worked,
+                         P.test_max_over_heads_lists_by_hand]),
     # flat ranking, expansion, near set, Ward, attention
     ("flat_rank", "order = np.lexsort((np.arange(ne), -s))",
      "order = np.lexsort((-np.arange(ne), -s))", "flat ties to the higher bucket",
