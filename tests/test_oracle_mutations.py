@@ -105,6 +105,18 @@ MUTATIONS = [
      "while prm.beam * (1 << l) < -(-prm.k // prm.n_pool) + 65:",
      "l* from the default-window bound", [P.test_leaf_level_reading,
                                            TP.test_top_b_reading_by_hand]),
+    # rounding, normalisation, the Ward cost, the decode trigger
+    ("round_bf16", "return np.ldexp(np.rint(np.ldexp(x, 8 - e)), e - 8)",
+     "return np.ldexp(np.floor(np.ldexp(x, 8 - e)), e - 8)", "bf16 rounding truncates",
+     [P.test_round_bf16_matches_torch_nearest_even, P.test_normalize_query_by_hand]),
+    ("normalize_query", "return round_index(unit(np.asarray(y, np.float64)), dtype)",
+     "return round_index(np.asarray(y, np.float64), dtype)", "query not normalised",
+     [P.test_normalize_query_by_hand]),
+    ("ward_cost", "return n_a * n_b / (n_a + n_b) * float(np.dot(d, d))",
+     "return float(np.dot(d, d))", "Ward cost without the size factor",
+     [P.test_ward_cost_equals_brute_force_ess_increase]),
+    ("decode_fires", "return (p + 1) % prm.block == 0", "return p % prm.block == 0",
+     "block fires on its first key", [P.test_decode_fires_when_a_block_fills]),
     # max over query heads (N-LSA scoring)
     ("bucket_scores", "return (cent @ yhat.T).max(axis=1)", "return (cent @ yhat.T).mean(axis=1)",
      "heads averaged instead of maxed", [P.test_max_over_heads_bucket_scores_hand_worked,

@@ -173,6 +173,28 @@ def test_round_bf16_matches_torch_nearest_even():
     assert np.array_equal(O.round_bf16(x.astype(np.float64)), ref)
 
 
+def test_normalize_query_by_hand():
+    """A 3-4-5 query: unit length first (0.6, 0.8), then the index dtype's
+    rounding (0.6 is not a bf16 value: 0.6015625 is its nearest, 0.8 rounds
+    to 0.80078125); a zero query stays zero."""
+    y = np.zeros(64)
+    y[0], y[1] = 3.0, 4.0
+    f = O.normalize_query(y, "f32")
+    assert f[0] == np.float64(np.float32(0.6)) and f[1] == np.float64(np.float32(0.8))
+    assert not f[2:].any()
+    b = O.normalize_query(y, "bf16")
+    assert b[0] == 0.6015625 and b[1] == 0.80078125
+    assert not O.normalize_query(np.zeros(64), "bf16").any()
+
+
+def test_decode_fires_when_a_block_fills():
+    """Appending the key at position p completes block p // 512 exactly when p
+    is the block's last position (511, 1023, ...); [visual] "How the hierarchy
+    is built": a block is clustered once its 512 keys are present."""
+    prm = O.Params()
+    assert [p for p in range(0, 2048) if O.decode_fires(p, prm)] == [511, 1023, 1535, 2047]
+
+
 # ---------------------------------------------------------------- worked counts
 
 def test_worked_query_counts_from_the_pages():
