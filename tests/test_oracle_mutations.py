@@ -117,6 +117,17 @@ MUTATIONS = [
      [P.test_ward_cost_equals_brute_force_ess_increase]),
     ("decode_fires", "return (p + 1) % prm.block == 0", "return p % prm.block == 0",
      "block fires on its first key", [P.test_decode_fires_when_a_block_fills]),
+    # sinks, expansion order, the cache's centroids and key numbering
+    ("near_set", "sinks = np.arange(min(prm.n_sink, p + 1))", "sinks = np.arange(prm.n_sink)",
+     "sinks not clipped to the query", NEAR_PINS),
+    ("expand", "if len(far) == k:", "if len(far) == k + 1:", "one far key too many",
+     [P.test_expansion_worked_example_by_hand]),
+    ("build_cache", "cent[g] = round_index(unit(s), prm.index_dtype)",
+     "cent[g] = round_index(unit(P[c].mean(axis=0) * 0 + P[c][0]), prm.index_dtype)",
+     "centroid from the first member only", [P.test_centroid_is_normalised_sum_of_member_unit_keys]),
+    ("build_cache", "members[g] = [b * prm.block + prm.n_pool * j + i",
+     "members[g] = [b * prm.block + j + i", "members numbered by item, not key",
+     [P.test_bucket_partition_invariants_and_counts]),
     # max over query heads (N-LSA scoring)
     ("bucket_scores", "return (cent @ yhat.T).max(axis=1)", "return (cent @ yhat.T).mean(axis=1)",
      "heads averaged instead of maxed", [P.test_max_over_heads_bucket_scores_hand_worked,
@@ -166,6 +177,11 @@ MUTATIONS = [
 
 @pytest.mark.parametrize("fn,old,new,what,pins", MUTATIONS, ids=[m[3] for m in MUTATIONS])
 def test_planted_mistake_fails_a_pin(fn, old, new, what, pins, monkeypatch):
+    # every pin runs without arguments (a call that fails for want of them
+    # would count as a catch)
+    for pin in pins:
+        assert not any(p.default is inspect.Parameter.empty
+                       for p in inspect.signature(pin).parameters.values()), pin.__name__
     monkeypatch.setattr(_module(fn), fn, _broken(fn, old, new))
     failed = []
     for pin in pins:
