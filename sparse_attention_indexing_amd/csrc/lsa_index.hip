@@ -1453,7 +1453,8 @@ __device__ __forceinline__ int block_scan_excl(int v, int* wsum, int* total) {
 
 // Exact top-B of one query, for a workgroup whose candidate list is unusable
 // (more than `cap` candidates, or fewer than k far keys in them while more
-// buckets are eligible) or when exact selection is forced: the B-th largest score by 4 radix passes of 8 bits over the
+// buckets are eligible) or when exact selection is forced: the B-th largest
+// score by 4 radix passes of 8 bits over the
 // order-preserving integer image of the fp32 score, then every bucket above
 // it and, among buckets equal to it, the lowest.  Writes raw score bits to
 // skey[] and buckets to sbkt[] (LDS) and returns the count (min(B, ne)).
