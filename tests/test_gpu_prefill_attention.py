@@ -218,3 +218,33 @@ def test_prefill_attention_row_layout():
     del K, V
     out = _run(Q, Kr, Vr, idx[None], cnt[None], q_start, p)
     _check(out, qs, ks, vs, idx[None], cnt[None], q_start, prm, np.arange(Tq), "row layout")
+
+
+@pytest.mark.parametrize("n_sink,window", [(4, 512), (3, 100)])
+def test_prefill_attention_row_layout_early_rows(n_sink, window):
+    """One workgroup per row, where the gather appends the row's near keys
+    itself: rows from position 0 on, so that for the first rows the sinks and
+    the window overlap and the near set is every key up to the row, with odd
+    lists; two sequences."""
+    say(f"case: prefill attention, one workgroup per row, rows from 0, n_sink={n_sink} window={window}")
+    w = S.WORKLOADS[2]
+    B, T, q_start, Tq = 2, 900, 0, 700
+    p = lsa.Params(k=256, n_sink=n_sink, window=window)
+    prm = oracle_params(p)
+    idx = np.full((B, Tq, 800), -1, np.int32)
+    cnt = np.zeros((B, Tq), np.int32)
+    for b in range(B):
+        idx[b], cnt[b] = _odd_lists(np.random.default_rng(100 * b + window), T, q_start, Tq, 800, prm)
+    idx[idx >= T] = -1            # past T the larger cache's zero rows would count
+    qs, ks, vs, Q, K, V = _qkv(w, B, T, np.arange(q_start, q_start + Tq))
+    Tmax = (256 << 20) // (w.Hkv * w.D * 2) + 1
+    assert not lsa.attention_head_major(B, Tmax, w.Hkv, w.D, lsa.LSA_BF16)
+    Kr = torch.zeros((B, Tmax, w.Hkv, w.D), dtype=torch.bfloat16, device="cuda")
+    Vr = torch.zeros_like(Kr)
+    Kr[:, :T] = K
+    Vr[:, :T] = V
+    del K, V
+    out = _run(Q, Kr, Vr, idx, cnt, q_start, p)
+    rows = np.unique(np.concatenate([np.arange(0, 12), np.arange(95, 110), np.arange(500, 530),
+                                     np.arange(Tq - 8, Tq)]))
+    _check(out, qs, ks, vs, idx, cnt, q_start, prm, rows, "row layout, early rows")
