@@ -154,6 +154,43 @@ def test_index_last_chunk_and_determinism():
     compare_lists(a[0].cpu().numpy()[rows], a[1].cpu().numpy()[rows], T - Tq + rows, Y[rows], oc)
 
 
+@pytest.mark.parametrize("dtype,n_queries,k", [(lsa.LSA_BF16, 8192, 2048), (lsa.LSA_BF16, 40, 2048),
+                                                 (lsa.LSA_F32, 8192, 2048), (lsa.LSA_BF16, 8192, 256)])
+def test_index_identical_keys_every_score_tied(dtype, n_queries, k):
+    """Every latent key the same vector: Ward merges at zero cost (the tie rule
+    alone shapes the buckets), every centroid is the same, so every bucket
+    scores the same for a query and the walk takes buckets in ascending order.
+    The one-pass range select then finds all candidates in one bin and takes
+    the radix passes, and the cut bucket is chosen among tied scores by bucket
+    index.  Exact equality with the oracle is required here (the tie rule is
+    the method's, not a rounding accident); many queries (256-thread groups)
+    and a few (1,024-thread groups).  With k = 256 the later queries' candidates
+    (every eligible bucket passes tau) overflow their slots, and the exact
+    top-B selection breaks the ties."""
+    say(f"case: identical keys, all scores tied, dtype={dtype} queries={n_queries} k={k}")
+    T = 8192
+    rng = np.random.default_rng(23)
+    v = rng.standard_normal(64)
+    X = np.tile(v.astype(np.float32), (T, 1))
+    Y = rng.standard_normal((T, 64)).astype(np.float32)
+    p = lsa.Params(k=k, index_dtype=dtype)
+    c = gpu_cache(X, p)
+    q_start = T - n_queries
+    Yq = Y[q_start:]
+    idx, cnt = lsa.index_prefill(c, torch.from_numpy(Yq).cuda(), q_start, p, stats=FB)
+    torch.cuda.synchronize()
+    oc = O.build_cache(X, oracle_params(p))
+    idx_h, cnt_h = idx.cpu().numpy(), cnt.cpu().numpy()
+    rows = np.unique(np.concatenate([np.arange(0, n_queries, max(1, n_queries // 300)),
+                                     np.arange(n_queries - 8, n_queries)]))
+    for r in rows:
+        pos = q_start + int(r)
+        ref = O.index_query(Yq[r], pos, oc)
+        assert int(cnt_h[r]) == ref.count, f"position {pos}: count"
+        assert np.array_equal(idx_h[r, :ref.count], ref.idx[:ref.count]), f"position {pos}: list"
+    say(f"identical keys: {len(rows)} lists equal to the oracle's")
+
+
 def test_index_lowpass_last_chunk():
     """T=65536, last 2048 queries, k=16: every query has ~8K eligible buckets
     and keeps 69, so the scoring kernel stages its few candidates in LDS
