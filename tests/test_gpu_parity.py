@@ -177,7 +177,10 @@ def test_index_identical_keys_every_score_tied(dtype, n_queries, k):
     c = gpu_cache(X, p)
     q_start = T - n_queries
     Yq = Y[q_start:]
+    fb0 = FB.total
     idx, cnt = lsa.index_prefill(c, torch.from_numpy(Yq).cuda(), q_start, p, stats=FB)
+    # k = 256: the later queries' candidates overflow, the exact top-B runs
+    assert (FB.total > fb0) if k == 256 else (FB.total == fb0)
     torch.cuda.synchronize()
     oc = O.build_cache(X, oracle_params(p))
     idx_h, cnt_h = idx.cpu().numpy(), cnt.cpu().numpy()
@@ -681,3 +684,38 @@ def test_decode_steps(mode, window, n_sink):
     X, Y, _ = seqs[0]
     oc = O.build_cache(X[:lens[0] + 4], oracle_params(p))
     compare_cache(cache_to_host(caches[0]), oc, X)
+
+
+@pytest.mark.parametrize("k", [2048, 256])
+def test_decode_identical_keys_every_score_tied(k):
+    """Decode over caches whose latent keys are all the same vector (every
+    bucket score tied, buckets taken in ascending order): three sequences,
+    four steps, the first completing a block (clustered at zero cost, the tie
+    rule alone) on its third step; lists equal the oracle's exactly.  With
+    k = 256 the sequences hold more eligible buckets than candidate slots, so
+    the candidates above the sampled threshold (all of them) overflow and the
+    exact top-B breaks the ties."""
+    say(f"case: decode, identical keys, k={k}")
+    lens = [4 * 512 + 509, 3000, 1500] if k == 2048 else [9 * 512 + 509, 6000, 5000]
+    p = lsa.Params(k=k, index_dtype=lsa.LSA_BF16)
+    rng = np.random.default_rng(29)
+    seqs = []
+    for n in lens:
+        v = rng.standard_normal(64).astype(np.float32)
+        seqs.append((np.tile(v, (n + 4, 1)), rng.standard_normal((n + 4, 64)).astype(np.float32)))
+    caches = [gpu_cache(X[:n], p, max_tokens=n + 4) for (X, Y), n in zip(seqs, lens)]
+    fb0 = FB.total
+    for step in range(4):
+        q = torch.from_numpy(np.stack([Y[n + step] for (X, Y), n in zip(seqs, lens)])).cuda()
+        kn = torch.from_numpy(np.stack([X[n + step] for (X, Y), n in zip(seqs, lens)])).cuda()
+        idx, cnt = lsa.index_decode(caches, q, kn, p, stats=FB)
+        torch.cuda.synchronize()
+        idx_h, cnt_h = idx.cpu().numpy(), cnt.cpu().numpy()
+        for b, ((X, Y), n) in enumerate(zip(seqs, lens)):
+            pos = n + step
+            ref = O.index_query(Y[pos], pos, O.build_cache(X[:pos + 1], oracle_params(p)))
+            assert int(cnt_h[b]) == ref.count, f"sequence {b} step {step}: count"
+            assert np.array_equal(idx_h[b, :ref.count], ref.idx[:ref.count]), f"sequence {b} step {step}"
+    # with k = 256 every query took the exact top-B (the case this exercises)
+    assert (FB.total - fb0 == 12) if k == 256 else (FB.total == fb0)
+    say("decode with identical keys: every list equal to the oracle's")
