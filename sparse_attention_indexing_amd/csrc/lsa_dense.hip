@@ -205,7 +205,8 @@ __global__ __launch_bounds__(kDenseNT) void k_dense_attn(DenseArgs a) {
 // that partial attention per (row, head): O relative to the reference max m
 // (base 2, scaled), m, and the sum l; the gather kernel starts from it and
 // adds the list's remaining (far) keys.
-constexpr int kNearRing = 6;                 // K/V tiles in flight per near workgroup
+constexpr int kNearTile = 32;               // keys per near tile
+constexpr int kNearRing = 4;                // K/V tiles in flight per near workgroup
 
 struct NearArgs {
   const uint16_t* q;        // [B * Tq, Hq, 128]
@@ -233,7 +234,8 @@ __global__ __launch_bounds__(kDenseNT) void k_near_attn(NearArgs a) {
   constexpr int PW = 16 / G;                  // positions per 16-column group
   constexpr int CG = kNearGroups;
   constexpr int P = kDenseWaves * CG * PW;    // positions per workgroup
-  __shared__ __attribute__((aligned(16))) char lds[2][2][kKTile];   // [buffer][K, V]
+  constexpr int KT = kNearTile;
+  __shared__ __attribute__((aligned(16))) char lds[2][2][KT * 256];   // [buffer][K, V]
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kvh = blockIdx.y;
@@ -266,9 +268,9 @@ __global__ __launch_bounds__(kDenseNT) void k_near_attn(NearArgs a) {
   const int64_t p_first = a.q_start + t0, p_last = a.q_start + t_end - 1;
   const int64_t sk_end = p_last + 1 < a.n_sink ? p_last + 1 : a.n_sink;
   const int64_t wk_lo = p_first - a.window + 1 > 0 ? p_first - a.window + 1 : 0;
-  const int64_t ts_end = (sk_end + 15) >> 4;                    // sink tiles [0, ts_end)
-  const int64_t tw0 = (wk_lo >> 4) > ts_end ? (wk_lo >> 4) : ts_end;
-  const int64_t n_tiles = ts_end + ((p_last >> 4) >= tw0 ? (p_last >> 4) - tw0 + 1 : 0);
+  const int64_t ts_end = (sk_end + KT - 1) / KT;                // sink tiles [0, ts_end)
+  const int64_t tw0 = wk_lo / KT > ts_end ? wk_lo / KT : ts_end;
+  const int64_t n_tiles = ts_end + (p_last / KT >= tw0 ? p_last / KT - tw0 + 1 : 0);
   auto tile_of = [&](int64_t i) -> int64_t { return i < ts_end ? i : tw0 + (i - ts_end); };
   // the wave's keys, to skip tiles that none of its columns reads
   const bool wave_live = wt0 < t_end;
@@ -314,24 +316,39 @@ __global__ __launch_bounds__(kDenseNT) void k_near_attn(NearArgs a) {
   const bool wave_full = __builtin_amdgcn_readfirstlane(__ballot(!all_ok) == 0 ? 1 : 0) != 0;
   const int64_t full_lo = wp_last - a.window + 1, full_hi = wp_first;
 
+  // tile loads: threads 0..255 take K, 256..511 V; thread t: 16-byte chunk
+  // t % 16 of keys (t & 255) / 16 and that + 16
   const int ld_v = tid >> 8, ld_key = (tid & 255) >> 4, ld_ch = tid & 15;
   const uint16_t* src = (ld_v ? a.v : a.k) + b * a.Tmax * a.Hkv * kHeadDim;
-  auto fetch = [&](int64_t i) -> u32x4_t {
-    int64_t key = tile_of(i) * 16 + ld_key;
-    key = key < a.Tmax ? key : a.Tmax - 1;
-    return *reinterpret_cast<const u32x4_t*>(src + (key * a.Hkv + kvh) * kHeadDim + 8 * ld_ch);
+  struct Chunk { u32x4_t x[2]; };
+  auto fetch = [&](int64_t i) -> Chunk {
+    Chunk c;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      int64_t key = tile_of(i) * KT + 16 * hh + ld_key;
+      key = key < a.Tmax ? key : a.Tmax - 1;
+      c.x[hh] = *reinterpret_cast<const u32x4_t*>(src + (key * a.Hkv + kvh) * kHeadDim + 8 * ld_ch);
+    }
+    return c;
   };
-  auto put = [&](int buf, u32x4_t x) {
-    const int rr = ld_key;
-    const int sw = ld_v ? (ld_ch ^ (2 * (rr & 7))) : (ld_ch ^ rr);
-    *reinterpret_cast<u32x4_t*>(&lds[buf][ld_v][256 * rr + 16 * sw]) = x;
+  // chunks XOR swizzled by row: K by (row & 15), V by 2 (row & 7)
+  auto put = [&](int buf, const Chunk& c) {
+    const int sw = ld_v ? (ld_ch ^ (2 * (ld_key & 7))) : (ld_ch ^ ld_key);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+      *reinterpret_cast<u32x4_t*>(&lds[buf][ld_v][256 * (16 * hh + ld_key) + 16 * sw]) = c.x[hh];
   };
   const int sk = 4 * u + (r16 >> 2), cv = (r16 & 3) >> 1, vsw = 2 * (sk & 7);
 
   // kNearRing tiles are requested ahead of the one computed (each thread
-  // holds its 16 bytes of each in registers); one barrier per tile, the LDS
-  // tiles double buffered
-  u32x4_t ring[kNearRing];
+  // holds its 32 bytes of each in registers); one barrier per tile, the LDS
+  // tiles double buffered.  A tile is two halves of 16 keys: the scores of
+  // half hh come from 16x16x32 products S^T = K Q^T (lane (column, u) gets
+  // keys 16 hh + 4 u .. + 3), and O^T += V^T P^T is one 16x16x32 product per
+  // 16 dims whose k index 8 u + e stands for key 4 u + e (e < 4) or
+  // 16 + 4 u + e - 4 (e >= 4), so each lane's eight probabilities are its own
+  // scores of the two halves and V^T takes one transposing read per half.
+  Chunk ring[kNearRing];
   // Q first: with only ring loads pending in the loop, each tile's wait is
   // kNearRing - 1 later loads
   __builtin_amdgcn_s_waitcnt(0x0F70);          // vmcnt(0)
@@ -352,44 +369,60 @@ __global__ __launch_bounds__(kDenseNT) void k_near_attn(NearArgs a) {
       put(buf, ring[j]);
       __syncthreads();
       ring[j] = fetch(i + kNearRing < n_tiles ? i + kNearRing : n_tiles - 1);
-      const int64_t kb = tile_of(i < n_tiles ? i : n_tiles - 1) * 16;
-      if (i < n_tiles && wave_live && (kb < ws_end || (kb + 15 >= ww_lo && kb <= wp_last))) {
+      const int64_t kb = tile_of(i < n_tiles ? i : n_tiles - 1) * KT;
+      if (i < n_tiles && wave_live && (kb < ws_end || (kb + KT - 1 >= ww_lo && kb <= wp_last))) {
         const char* kt = lds[buf][0];
         const char* vt = lds[buf][1];
-        u32x4_t kf[4];
+        f32x4 sacc[CG][2];
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-          kf[jj] = *reinterpret_cast<const u32x4_t*>(kt + 256 * r16 + 16 * ((4 * jj + u) ^ r16));
-        f32x4 sacc[CG];
-#pragma unroll
-        for (int c = 0; c < CG; ++c) {
-          sacc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int hh = 0; hh < 2; ++hh) {
+          u32x4_t kf[4];
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj)
-            sacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[jj]),
-                                                              qf[c][jj], sacc[c], 0, 0, 0);
+            kf[jj] = *reinterpret_cast<const u32x4_t*>(kt + 256 * (16 * hh + r16) +
+                                                       16 * ((4 * jj + u) ^ r16));
+#pragma unroll
+          for (int c = 0; c < CG; ++c) {
+            sacc[c][hh] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+              sacc[c][hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  __builtin_bit_cast(bf16x8, kf[jj]), qf[c][jj], sacc[c][hh], 0, 0, 0);
+          }
         }
-        const bool full = wave_full && kb >= full_lo && kb + 15 <= full_hi;
+        const bool full = wave_full && kb >= full_lo && kb + KT - 1 <= full_hi;
         const int32_t kq = (int32_t)kb + 4 * u;            // this lane's first key
-        v4s_t pb4[CG];
+        bf16x8 pb8[CG];
 #pragma unroll
         for (int c = 0; c < CG; ++c) {
-          // scaled scores of keys 4 u + e (base 2); keys outside the column's
-          // near set get -inf
-          float xs[4];
+          // scaled scores of keys 16 hh + 4 u + e (base 2); keys outside the
+          // column's near set get -inf
+          float xs[8];
+          if (full) {                            // uniform: no key of the tile is masked
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) xs[4 * hh + e] = sacc[c][hh][e] * sl;
+          } else {
+            // non-short-circuit operators: lane masks, no branches
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int32_t key = kq + 16 * hh + e;
+                const bool ok = (key <= p32[c]) & ((key < se32[c]) | (key >= ws32[c]));
+                xs[4 * hh + e] = ok ? sacc[c][hh][e] * sl : -__builtin_inff();
+              }
+          }
           bool up = false;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int32_t key = kq + e;
-            const bool ok = full || (key <= p32[c] && (key < se32[c] || key >= ws32[c]));
-            xs[e] = ok ? sacc[c][e] * sl : -__builtin_inff();
-            up |= xs[e] > m[c] + kNearLazy;
-          }
+          for (int e = 0; e < 8; ++e) up |= xs[e] > m[c] + kNearLazy;
           // lazy reference max: O and l are rescaled only when a score
           // exceeds it by more than 2^kNearLazy (they always share it, so the
           // result does not depend on when that happens)
           if (__ballot(up)) {
-            float x = fmaxf(fmaxf(xs[0], xs[1]), fmaxf(xs[2], xs[3]));
+            float x = fmaxf(fmaxf(fmaxf(xs[0], xs[1]), fmaxf(xs[2], xs[3])),
+                            fmaxf(fmaxf(xs[4], xs[5]), fmaxf(xs[6], xs[7])));
             x = fmaxf(x, __shfl_xor(x, 16, 64));
             x = fmaxf(x, __shfl_xor(x, 32, 64));
             const float mn = fmaxf(m[c], x);
@@ -401,25 +434,29 @@ __global__ __launch_bounds__(kDenseNT) void k_near_attn(NearArgs a) {
 #pragma unroll
               for (int e = 0; e < 4; ++e) o[c][jj][e] *= alpha;
           }
-          float pv[4];
+          float pv[8];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
+          for (int e = 0; e < 8; ++e) {
             pv[e] = __builtin_amdgcn_exp2f(xs[e] - m[c]);
             lp[c] += pv[e];
           }
-          uint2 w2;
-          w2.x = pack2(pv[0], pv[1]);
-          w2.y = pack2(pv[2], pv[3]);
-          pb4[c] = __builtin_bit_cast(v4s_t, w2);
+          u32x4_t w4;
+          w4.x = pack2(pv[0], pv[1]);
+          w4.y = pack2(pv[2], pv[3]);
+          w4.z = pack2(pv[4], pv[5]);
+          w4.w = pack2(pv[6], pv[7]);
+          pb8[c] = __builtin_bit_cast(bf16x8, w4);
         }
         const char* vrd = vt + 256 * sk + 8 * (r16 & 1);
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
-          const v4s_t va4 = __builtin_bit_cast(
-              v4s_t, tr16(reinterpret_cast<const uint16_t*>(vrd + 16 * ((2 * jj + cv) ^ vsw))));
+          const int off = 16 * ((2 * jj + cv) ^ vsw);
+          const uint2 v0 = tr16(reinterpret_cast<const uint16_t*>(vrd + off));
+          const uint2 v1 = tr16(reinterpret_cast<const uint16_t*>(vrd + 16 * 256 + off));
+          const bf16x8 va8 = __builtin_bit_cast(bf16x8, u32x4_t{v0.x, v0.y, v1.x, v1.y});
 #pragma unroll
           for (int c = 0; c < CG; ++c)
-            o[c][jj] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va4, pb4[c], o[c][jj], 0, 0, 0);
+            o[c][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va8, pb8[c], o[c][jj], 0, 0, 0);
         }
       }
     }
