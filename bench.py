@@ -218,7 +218,14 @@ def attention_roofline(lsa, torch, w, idx, cnt, L: int, t_attn_ms: float, kname:
     row's bytes, cache hits included) is reported beside it; where the caches
     serve the gather, its rate can exceed HBM peak and is not a roofline
     fraction.  `traffic` is the counter-measured bytes that cross the L2 per
-    launch when the committed counter summary matches this kernel."""
+    launch when the committed counter summary matches this kernel.
+
+    The roof that binds: the gather's rows reach the CUs from L2, the
+    Infinity Cache or HBM, and only the bytes that leave the L2 load the
+    memory side.  When the counters match this kernel, `achieved` is those
+    bytes per launch over the launch time against HBM peak (basis
+    "traffic"); otherwise the compulsory bytes are used (basis
+    "compulsory").  Both rates, and the MFMA share, are reported beside it."""
     esz = 2 if w.dtype == "bf16" else 4
     Tq = idx.shape[0]
     launch_rows = min(lsa.attention_launch_rows(), Tq) if w.dtype == "bf16" else Tq
@@ -241,22 +248,27 @@ def attention_roofline(lsa, torch, w, idx, cnt, L: int, t_attn_ms: float, kname:
     mfma_peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
     ridge = mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9)
     sec = t_launch * 1e-3
-    if intensity >= ridge:
-        achieved, peak, unit, bound = flop / launches / sec / 1e12, mfma_peak, "TFLOP/s", "mfma"
-    else:
-        achieved, peak, unit, bound = compulsory / launches / sec / 1e9, HBM_PEAK_GBS, "GB/s", "hbm"
     traffic = measured_traffic(kname, workload, launch_rows)
+    mfma_tflops = flop / launches / sec / 1e12
+    compulsory_gbs = compulsory / launches / sec / 1e9
+    if traffic is not None:
+        achieved, peak, unit, bound, basis = traffic / sec / 1e9, HBM_PEAK_GBS, "GB/s", "hbm", "traffic"
+    elif intensity >= ridge:
+        achieved, peak, unit, bound, basis = mfma_tflops, mfma_peak, "TFLOP/s", "mfma", "flop"
+    else:
+        achieved, peak, unit, bound, basis = compulsory_gbs, HBM_PEAK_GBS, "GB/s", "hbm", "compulsory"
     roof = dict(bound=bound, achieved=round(achieved, 2), peak=peak, unit=unit,
                 frac=round(achieved / peak, 4), traffic=None if traffic is None else round(traffic),
-                kernel=kname, launches_per_step=launches, kernel_ms=round(float(t_launch), 4),
+                basis=basis, kernel=kname, launches_per_step=launches,
+                kernel_ms=round(float(t_launch), 4),
                 algorithmic_flop=round(flop / launches),
+                mfma_tflops=round(mfma_tflops, 1), mfma_frac=round(mfma_tflops / mfma_peak, 4),
                 compulsory_bytes=round(compulsory / launches),
+                compulsory_gbs=round(compulsory_gbs, 1),
+                compulsory_frac=round(compulsory_gbs / HBM_PEAK_GBS, 4),
                 intensity_flop_per_byte=round(intensity, 1), ridge_flop_per_byte=round(ridge, 1),
                 logical_bytes=round(logical / launches),
                 logical_gbs=round(logical / launches / sec / 1e9, 1))
-    if traffic is not None:
-        roof["traffic_gbs"] = round(traffic / sec / 1e9, 1)
-        roof["traffic_frac"] = round(traffic / sec / 1e9 / HBM_PEAK_GBS, 4)
     return roof
 
 
