@@ -879,12 +879,17 @@ def main():
                       else args.cpu_seconds, scan_keys=args.scan)
     if headline:
         # the metric's other ends, on the same GPU in the same run: the 10M
-        # last prefill chunk (flat) and one step of the 16 x 1M decode batch
+        # last prefill chunk (flat), one step of the 16 x 1M decode batch and
+        # one step of a single 10M-token sequence's decode
         res["extra"] = {}
         r10 = run_prefill(S.WORKLOADS[5], dev, "flat", min(args.steps, 3), 1)
         res["extra"][r10["config"]["workload"]] = _extra_summary(r10)
+        torch.cuda.empty_cache()
         rdec = run_decode(S.WORKLOADS[3], dev, "flat")
         res["extra"][rdec["config"]["workload"]] = _extra_summary(rdec)
+        torch.cuda.empty_cache()
+        rdec10 = run_decode(S.WORKLOADS[5], dev, "flat", batch=1)
+        res["extra"][rdec10["config"]["workload"]] = _extra_summary(rdec10)
     print(json.dumps(res), flush=True)
 
 
