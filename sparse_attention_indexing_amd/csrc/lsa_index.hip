@@ -2149,10 +2149,15 @@ __global__ __launch_bounds__(NT) void k_select_expand(IndexCtx ctx, IndexWs ws, 
   uint32_t* skey = reinterpret_cast<uint32_t*>(sm);           // [cap] orderable scores
   uint32_t* sbkt = skey + cap;                                // [cap] bucket ids
   uint8_t* contrib = reinterpret_cast<uint8_t*>(sbkt + cap);  // [cap]
-  int32_t* far = reinterpret_cast<int32_t*>(contrib + cap);   // [kf]
-  // radix-sort buffer for the far keys: reuses skey/sbkt, which are dead once
-  // the far keys are emitted (kf <= 2 cap since cap >= 3 B > 3 k / 4)
-  int32_t* far2 = reinterpret_cast<int32_t*>(sm);
+  // the far items and the radix sort's second buffer: where skey/sbkt were
+  // when both fit there (kf <= cap: every thread holds its candidates' bucket
+  // ids in registers before the items are written), else far after contrib
+  // and the second buffer over skey/sbkt (kf <= 2 cap since cap >= 3 B >
+  // 3 k / 4).  The launcher sizes the dynamic LDS by the same rule.
+  const bool far_low = kf <= cap;
+  int32_t* far = far_low ? reinterpret_cast<int32_t*>(sm)
+                         : reinterpret_cast<int32_t*>(contrib + cap);   // [kf]
+  int32_t* far2 = far_low ? far + kf : reinterpret_cast<int32_t*>(sm);
   __shared__ uint32_t hist[NT / 64][256];
   __shared__ int wsum[NT / 64];
   __shared__ uint32_t s_prefix, s_want;
@@ -2330,12 +2335,13 @@ __global__ __launch_bounds__(NT) void k_select_expand(IndexCtx ctx, IndexWs ws, 
   const uint32_t gstar = 0xFFFFFFFFu - gstar_key;
   const int n_far = cut ? k : total;
   static_assert(kPool == 4, "items are packed as (position / 4) << 4 | 4-bit key mask");
-  // the items of candidate i taking `take` far keys, in member (= key) order
-  auto for_items = [&](int i, uint32_t m, int take, auto&& f) {
+  // the items of candidate i (bucket or run g) taking `take` far keys, in
+  // member (= key) order
+  auto for_items = [&](int i, uint32_t g, uint32_t m, int take, auto&& f) {
     if (run_keys) {
       // a scan's run of b keys (b = 1, 4 or 8, aligned to b): its first
       // `take` keys that are not sinks, as items of 4 keys
-      const int64_t r0 = (int64_t)sbkt[i] * run_keys;
+      const int64_t r0 = (int64_t)g * run_keys;
       if (run_keys == 1) {
         if (take > 0 && r0 >= s_end) f((int32_t)(((r0 >> 2) << 4) | (1 << (r0 & 3))));
         return;
@@ -2350,7 +2356,7 @@ __global__ __launch_bounds__(NT) void k_select_expand(IndexCtx ctx, IndexWs ws, 
       }
       return;
     }
-    const int64_t kb = (int64_t)(sbkt[i] / kBuckets) * kBlock;
+    const int64_t kb = (int64_t)(g / kBuckets) * kBlock;
     const bool clean = kb >= s_end && kb + kBlock <= w_start;   // no sink or window key
     if (clean && take == (int)contrib[i]) {
       // the whole bucket: every member item with all of its keys
@@ -2383,17 +2389,21 @@ __global__ __launch_bounds__(NT) void k_select_expand(IndexCtx ctx, IndexWs ws, 
       return 0;
     };
     int tk[PER];
+    uint32_t gb[PER];
     int mine = 0;
 #pragma unroll
     for (int jj = 0; jj < PER; ++jj) {
       const int i = tid + NT * jj;
       tk[jj] = i < c ? take_of(i) : 0;
-      if (tk[jj] > 0) for_items(i, mw[jj], tk[jj], [&](int32_t) { ++mine; });
+      gb[jj] = i < c ? sbkt[i] : 0u;
+      if (tk[jj] > 0) for_items(i, gb[jj], mw[jj], tk[jj], [&](int32_t) { ++mine; });
     }
+    // the scan's barriers also end every read of skey/sbkt, which far may overwrite
     int o = block_scan_nt<NT>(mine, wsum, &n_items);
 #pragma unroll
     for (int jj = 0; jj < PER; ++jj)
-      if (tk[jj] > 0) for_items(tid + NT * jj, mw[jj], tk[jj], [&](int32_t it) { far[o++] = it; });
+      if (tk[jj] > 0)
+        for_items(tid + NT * jj, gb[jj], mw[jj], tk[jj], [&](int32_t it) { far[o++] = it; });
   }
   __syncthreads();
   // sort by position (bits 4 and up); positions are below p.  A token scan
@@ -2650,7 +2660,8 @@ hipError_t launch_select_expand(const IndexCtx& ctx, const IndexWs& ws, int32_t*
   if (ctx.n <= 0) return hipSuccess;
   const int64_t kf = ctx.k > 1 ? ctx.k : 1;
   if (kf > 2 * (int64_t)ctx.cap) return hipErrorInvalidValue;   // the far-key sort reuses 8 cap bytes
-  const size_t smem = (size_t)ctx.cap * 9 + (size_t)kf * 4;
+  // far items over the candidates' keys and buckets when they fit there
+  const size_t smem = (size_t)ctx.cap * 9 + (kf <= ctx.cap ? 0 : (size_t)kf * 4);
   auto launch = [&](auto kern, int nt) {
     allow_large_lds(reinterpret_cast<const void*>(kern), smem > 128 * 1024 ? smem : 128 * 1024);
     hipLaunchKernelGGL(kern, dim3((unsigned)ctx.n), dim3(nt), smem, s, ctx, ws, idx, count, ranked,
