@@ -788,12 +788,15 @@ __global__ __launch_bounds__(256, 2) void k_score_lowpass(IndexCtx ctx, IndexWs 
 // histograms are added in global memory and finished by k_thresh_tau.
 __global__ __launch_bounds__(512, 1) void k_thresh_q128(IndexCtx ctx, IndexWs ws, int seg_tiles,
                                                         int split) {
-  __shared__ uint32_t hist[kQueriesPerWg][kBins];
+  // one row per query, padded by a word: lanes of different queries whose
+  // scores fall in the same bin then add into different LDS banks
+  constexpr int kRow = kBins + 1;
+  __shared__ uint32_t hist[kQueriesPerWg][kRow];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
   const int64_t q0 = (int64_t)blockIdx.x * kQueriesPerWg;
-  for (int i = tid; i < kQueriesPerWg * kBins; i += 512) (&hist[0][0])[i] = 0;
+  for (int i = tid; i < kQueriesPerWg * kRow; i += 512) (&hist[0][0])[i] = 0;
   QCols qc;
   const int32_t nmax = load_qcols(qc, ctx, nullptr, q0, col);
   const int32_t n_samp = nmax / kSampleStride;            // samples of the widest query
@@ -810,17 +813,30 @@ __global__ __launch_bounds__(512, 1) void k_thresh_q128(IndexCtx ctx, IndexWs ws
       const int32_t j = t * kTile + col;
       return sample_bucket(j < jlast ? j : jlast);
     };
+    // bin of a score: (s + 1) * 128 truncated, clamped to [0, 255] (the
+    // clamp taken on the float first: the same bin for every finite s)
+    auto bin_of = [](float sc) {
+      return (int)__builtin_amdgcn_fmed3f((sc + 1.0f) * (kBins / 2), 0.f, (float)(kBins - 1));
+    };
     auto epilogue = [&](const f32x16 (&acc)[4], int32_t t) {
+      // sample jj's bucket 16 jj + (7 jj & 15) grows with jj, so a tile whose
+      // last sample is eligible for a query is eligible in every row
+      const int32_t jl = t * kTile + kTile - 1;
+      const bool in_samp = jl < n_samp;
+      const int32_t gl = 16 * jl + ((7 * jl) & 15);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         if (qc.all[j]) continue;
+        uint32_t* hrow = hist[32 * j + col];
+        if (in_samp && gl < qc.ne[j]) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int32_t jj = t * kTile + tile_row(r, lane);
-          if (jj < n_samp && 16 * jj + ((7 * jj) & 15) < qc.ne[j]) {
-            int bin = (int)((acc[j][r] + 1.0f) * (kBins / 2));
-            bin = bin < 0 ? 0 : (bin >= kBins ? kBins - 1 : bin);
-            atomicAdd(&hist[32 * j + col][bin], 1u);
+          for (int r = 0; r < 16; ++r) atomicAdd(&hrow[bin_of(acc[j][r])], 1u);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int32_t jj = t * kTile + tile_row(r, lane);
+            if (jj < n_samp && 16 * jj + ((7 * jj) & 15) < qc.ne[j])
+              atomicAdd(&hrow[bin_of(acc[j][r])], 1u);
           }
         }
       }
@@ -845,7 +861,7 @@ __global__ __launch_bounds__(512, 1) void k_thresh_q128(IndexCtx ctx, IndexWs ws
   __syncthreads();
   if (split) {
     for (int i = tid; i < kQueriesPerWg * kBins; i += 512) {
-      const uint32_t v = (&hist[0][0])[i];
+      const uint32_t v = hist[i / kBins][i % kBins];
       const int64_t qj = q0 + i / kBins;
       if (v && qj < ctx.n) atomicAdd(&ws.hist[qj * kBins + (i % kBins)], v);
     }
