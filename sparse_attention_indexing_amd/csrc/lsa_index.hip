@@ -658,16 +658,18 @@ __device__ __forceinline__ void highpass_tile(const f32x16 (&acc)[4], int32_t t,
     int base = 0;
     if (!qc.all[j] && half == 0 && nl + np > 0) base = atomicAdd(&ws.cand_cnt[qc.qi[j]], nl + np);
     base = __shfl(base, col, 64);
+    // one predicated store per row: bucket g goes to slot g (every bucket
+    // kept) or to the next appended slot while the list has room
     int slot = base + (half ? np : 0);
+    const bool all = qc.all[j];
+    const int lim = all ? 0x7fffffff : cap;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      if ((bits >> r) & 1u) {
-        const int32_t g = t * kTile + tile_row(r, lane);
-        const uint2 e = make_uint2(__float_as_uint(acc[j][r]), (uint32_t)g);
-        if (qc.all[j]) dst[g] = e;
-        else if (slot < cap) dst[slot] = e;
-        ++slot;
-      }
+      const bool pr = ((bits >> r) & 1u) != 0;
+      const uint32_t g = (uint32_t)(t * kTile + tile_row(r, lane));
+      const uint32_t d = all ? g : (uint32_t)slot;
+      if (pr & (slot < lim)) dst[d] = make_uint2(__float_as_uint(acc[j][r]), g);
+      slot += pr ? 1 : 0;
     }
   }
 }
