@@ -1936,16 +1936,13 @@ __device__ int32_t* radix_sort_i32(int32_t* keys, int32_t* tmp, int n, int max_k
     for (int i = tid; i < NW * NB; i += NT) cnt[i] = 0;
     __syncthreads();
     uint32_t* my = cnt + wave * NB;
-    // histogram with one atomic per distinct digit and wave (sorted runs of
-    // keys share their high digits, which would serialise per-lane atomics)
+    // histogram: one LDS atomic per key into its wave's counters.  Lanes with
+    // the same digit (sorted runs share their high digits) serialise in the
+    // LDS unit, which this kernel leaves mostly idle, instead of costing the
+    // eight ballots and per-lane selects of match_digit in VALU, which bound it
     for (int e0 = c0; e0 < c1; e0 += 64) {
       const int e = e0 + lane;
-      const bool ok = e < c1;
-      const uint64_t active = __ballot(ok);
-      const uint32_t d = ok ? ((uint32_t)keys[e] >> shift) & (NB - 1) : 0u;
-      const uint64_t peers = match_digit<DB>(d, active);
-      if (ok && (peers & ((1ull << lane) - 1ull)) == 0)
-        atomicAdd(&my[d], (uint32_t)__popcll(peers));
+      if (e < c1) atomicAdd(&my[((uint32_t)keys[e] >> shift) & (NB - 1)], 1u);
     }
     __syncthreads();
     {
