@@ -638,10 +638,21 @@ __device__ __forceinline__ void ring_drain(LL& L, const IndexCtx& ctx, const Ind
 
 // High-pass epilogue (many candidates, or every eligible bucket kept): per
 // query and tile one atomic reserves the slots of both lanes that hold the
-// query's 32 rows; queries with ne <= cap store bucket g at slot g.
-__device__ __forceinline__ void highpass_tile(const f32x16 (&acc)[4], int32_t t, const QCols& qc,
-                                              int lane, int col, int half, const IndexWs& ws,
-                                              int cap) {
+// query's 32 rows; queries with ne <= cap store bucket g at slot g.  It runs in
+// two halves around the next tile's loads: the passing rows and the four slot
+// reservations first, the stores after.  The wait for a returning atomic
+// covers every memory operation issued before it, so reservations issued
+// after the next tile's loads would wait for those loads too.
+struct HpRes {
+  uint32_t bits01, bits23;          // passing rows of query groups 0..3, 16 bits each
+  int base[4];                      // reserved slot (lanes of the first half)
+};
+
+__device__ __forceinline__ HpRes highpass_reserve(const f32x16 (&acc)[4], int32_t t,
+                                                  const QCols& qc, int lane, int half,
+                                                  const IndexWs& ws) {
+  HpRes h;
+  h.bits01 = h.bits23 = 0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     uint32_t bits = 0;
@@ -651,16 +662,29 @@ __device__ __forceinline__ void highpass_tile(const f32x16 (&acc)[4], int32_t t,
       const bool p = (qc.all[j] || acc[j][r] >= qc.tau[j]) && g < qc.ne[j];
       bits |= (uint32_t)p << r;
     }
-    if (__ballot(bits != 0) == 0) continue;
-    uint2* dst = ws.cand + (int64_t)qc.qi[j] * cap;
+    if (j < 2) h.bits01 |= bits << (16 * j);
+    else h.bits23 |= bits << (16 * (j - 2));
     const int nl = __popc(bits);
     const int np = __shfl_xor(nl, 32, 64);
-    int base = 0;
-    if (!qc.all[j] && half == 0 && nl + np > 0) base = atomicAdd(&ws.cand_cnt[qc.qi[j]], nl + np);
-    base = __shfl(base, col, 64);
+    h.base[j] = 0;
+    if (!qc.all[j] && half == 0 && nl + np > 0)
+      h.base[j] = atomicAdd(&ws.cand_cnt[qc.qi[j]], nl + np);
+  }
+  return h;
+}
+
+__device__ __forceinline__ void highpass_store(const f32x16 (&acc)[4], int32_t t, const QCols& qc,
+                                               const HpRes& h, int lane, int col, int half,
+                                               const IndexWs& ws, int cap) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t bits = ((j < 2 ? h.bits01 : h.bits23) >> (16 * (j & 1))) & 0xFFFFu;
+    if (__ballot(bits != 0) == 0) continue;
+    uint2* dst = ws.cand + (int64_t)qc.qi[j] * cap;
+    const int np = __shfl_xor(__popc(bits), 32, 64);
     // one predicated store per row: bucket g goes to slot g (every bucket
     // kept) or to the next appended slot while the list has room
-    int slot = base + (half ? np : 0);
+    int slot = __shfl(h.base[j], col, 64) + (half ? np : 0);
     const bool all = qc.all[j];
     const int lim = all ? 0x7fffffff : cap;
 #pragma unroll
@@ -705,11 +729,14 @@ __global__ __launch_bounds__(256, 2) void k_score_highpass(IndexCtx ctx, IndexWs
   for (; t < t1; t += 8) {
     f32x16 acc[4];
     mfma_q128(acc, ra, q);
+    HpRes h = highpass_reserve(acc, t, qc, lane, half, ws);
     load_atile(ra, cent, (int64_t)(t + 8 < tl ? t + 8 : tl) * kTile + col, half);
-    highpass_tile(acc, t, qc, lane, col, half, ws, ctx.cap);
+    highpass_store(acc, t, qc, h, lane, col, half, ws, ctx.cap);
     mfma_q128(acc, rb, q);
+    const bool more = t + 4 < t1;
+    if (more) h = highpass_reserve(acc, t + 4, qc, lane, half, ws);
     load_atile(rb, cent, (int64_t)(t + 12 < tl ? t + 12 : tl) * kTile + col, half);
-    if (t + 4 < t1) highpass_tile(acc, t + 4, qc, lane, col, half, ws, ctx.cap);
+    if (more) highpass_store(acc, t + 4, qc, h, lane, col, half, ws, ctx.cap);
   }
 }
 
@@ -1903,14 +1930,14 @@ __device__ __forceinline__ uint64_t match_digit(uint32_t d, uint64_t active) {
   return peers;
 }
 
-// Stable LSD radix sort (DB-bit digits) of n non-negative int32 keys in LDS,
-// ascending by their bits lo and up (the bits below lo keep their input
-// order), by a workgroup of NT threads of which the first NW waves hold the
-// keys (4, or 8 when NT >= 1024; at most NT / 64 x 256 / 2^DB).  Wave w owns
-// the contiguous chunk [w*ch, (w+1)*ch); `tmp` is a second buffer of n ints,
-// `cnt` NW x 2^DB counters (one row per wave); the scatter ranks lanes with
-// equal digits by ballots, which keeps it stable.  Returns the buffer that
-// holds the result.
+// LSD radix sort (DB-bit digits) of n non-negative int32 keys in LDS that are
+// distinct in their bits lo and up, ascending by those bits, by a workgroup of
+// NT threads of which the first NW waves hold the keys (4, or 8 when NT >=
+// 1024; at most NT / 64 x 256 / 2^DB).  Wave w owns the contiguous chunk
+// [w*ch, (w+1)*ch); `tmp` is a second buffer of n ints, `cnt` NW x 2^DB
+// counters (one row per wave).  After the first pass the scatter ranks lanes
+// with equal digits by ballots, which keeps those passes stable.  Returns the
+// buffer that holds the result.
 template <int DB, int NT = 256>
 __device__ int32_t* radix_sort_i32(int32_t* keys, int32_t* tmp, int n, int max_key, int lo,
                                    uint32_t* cnt) {
@@ -1965,18 +1992,31 @@ __device__ int32_t* radix_sort_i32(int32_t* keys, int32_t* tmp, int n, int max_k
       }
     }
     __syncthreads();
-    for (int e0 = c0; e0 < c1; e0 += 64) {
-      const int e = e0 + lane;
-      const bool ok = e < c1;
-      const uint64_t active = __ballot(ok);
-      const int32_t key = ok ? keys[e] : 0;
-      const uint32_t d = ((uint32_t)key >> shift) & (NB - 1);
-      const uint64_t peers = match_digit<DB>(d, active);
-      if (ok) {
-        const int rank = __popcll(peers & ((1ull << lane) - 1ull));
-        const uint32_t base = my[d];
-        tmp[base + rank] = key;
-        if (rank == 0) my[d] = base + (uint32_t)__popcll(peers);
+    if (shift == lo) {
+      // first pass: the input order carries nothing to keep, so equal digits
+      // may land in any order (the keys are distinct in the sorted bits, so
+      // later passes still order them fully): slots straight from the atomics
+      for (int e0 = c0; e0 < c1; e0 += 64) {
+        const int e = e0 + lane;
+        if (e < c1) {
+          const int32_t key = keys[e];
+          tmp[atomicAdd(&my[((uint32_t)key >> shift) & (NB - 1)], 1u)] = key;
+        }
+      }
+    } else {
+      for (int e0 = c0; e0 < c1; e0 += 64) {
+        const int e = e0 + lane;
+        const bool ok = e < c1;
+        const uint64_t active = __ballot(ok);
+        const int32_t key = ok ? keys[e] : 0;
+        const uint32_t d = ((uint32_t)key >> shift) & (NB - 1);
+        const uint64_t peers = match_digit<DB>(d, active);
+        if (ok) {
+          const int rank = __popcll(peers & ((1ull << lane) - 1ull));
+          const uint32_t base = my[d];
+          tmp[base + rank] = key;
+          if (rank == 0) my[d] = base + (uint32_t)__popcll(peers);
+        }
       }
     }
     __syncthreads();
