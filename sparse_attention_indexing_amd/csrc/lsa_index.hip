@@ -1171,6 +1171,7 @@ __device__ __forceinline__ void load_rows8(uint4 (&u)[8], const uint4* cent, int
 }
 
 constexpr int kDecStage = 64;           // LDS candidate slots per wave
+constexpr int kDecStageAll = 512;       // ... when they hold every row of the wave
 
 // tau of query qi from its sampled histogram, computed by one wave: lane l
 // sums the 4 bins 4 (63 - l) .. 4 (63 - l) + 3, so an inclusive prefix over
@@ -1215,8 +1216,14 @@ __device__ __forceinline__ float dec_tau_wave(const IndexCtx& ctx, const IndexWs
 // once per workgroup, not once per wave, so the same-address atomics that
 // end every workgroup stay few).  The candidate count starts at zero
 // (k_dec_prep).  Each wave keeps two batches of 8 row loads in flight.
+// S: LDS candidate slots per wave.  With S = kDecStageAll the launcher
+// guarantees that a wave's rows (rows_per_wg / 4) fit, so the loop holds no
+// global memory operation besides its loads: with a store or an atomic that
+// may be in flight beside them, the compiler waits for every load before
+// using any (the batches then stop overlapping).
+template <int S>
 __global__ __launch_bounds__(256) void k_dec_filter(IndexCtx ctx, IndexWs ws, int rows_per_wg) {
-  __shared__ uint2 s_buf[4][kDecStage];
+  __shared__ uint2 s_buf[4][S];
   __shared__ int s_cnt[4];
   __shared__ int s_base;
   const int64_t qi = blockIdx.y;
@@ -1262,14 +1269,17 @@ __global__ __launch_bounds__(256) void k_dec_filter(IndexCtx ctx, IndexWs ws, in
     }
     npass = __builtin_amdgcn_readfirstlane(npass);
     if (npass == 0) return;
-    if (cnt + npass > kDecStage) flush_wave();
     int base = cnt;
     uint2* dst = stage;
-    if (npass > kDecStage) {                               // only when every row passes
-      int g = 0;
-      if (lane == 0) g = atomicAdd(&ws.cand_cnt[qi], npass);
-      base = __shfl(g, 0, 64);
-      dst = cand;
+    if constexpr (S == kDecStage) {
+      if (cnt + npass > S) flush_wave();
+      base = cnt;
+      if (npass > S) {                                     // only when every row passes
+        int g = 0;
+        if (lane == 0) g = atomicAdd(&ws.cand_cnt[qi], npass);
+        base = __shfl(g, 0, 64);
+        dst = cand;
+      }
     }
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -1308,7 +1318,8 @@ __global__ __launch_bounds__(256) void k_dec_filter(IndexCtx ctx, IndexWs ws, in
   __syncthreads();
   int off = s_base;
   for (int w = 0; w < wave; ++w) off += s_cnt[w];
-  if (lane < cnt && off + lane < ctx.cap) cand[off + lane] = stage[lane];
+  for (int i = lane; i < cnt; i += 64)
+    if (off + i < ctx.cap) cand[off + i] = stage[i];
 }
 
 // Sampled histogram for the decode threshold: grid.x = chunks of
@@ -2653,8 +2664,12 @@ hipError_t launch_score_filter(const IndexCtx& ctx, const IndexWs& ws, int dtype
     if (steps < kDecMinRowsPerWg / 256) steps = kDecMinRowsPerWg / 256;
     const int64_t per = 256 * steps;
     const int64_t gx = (rows + per - 1) / per;
-    hipLaunchKernelGGL(k_dec_filter, dim3((unsigned)gx, (unsigned)ctx.n), dim3(256), 0, s, ctx, ws,
-                       (int)per);
+    if (per / 4 <= kDecStageAll)
+      hipLaunchKernelGGL(k_dec_filter<kDecStageAll>, dim3((unsigned)gx, (unsigned)ctx.n), dim3(256),
+                         0, s, ctx, ws, (int)per);
+    else
+      hipLaunchKernelGGL(k_dec_filter<kDecStage>, dim3((unsigned)gx, (unsigned)ctx.n), dim3(256), 0,
+                         s, ctx, ws, (int)per);
     return hipGetLastError();
   }
   // decode has few queries: shorter segments give enough workgroups to stream HBM
